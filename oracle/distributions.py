@@ -1,0 +1,160 @@
+"""Processed distributions and the discrete decisions of a round.
+
+Every decision here is taken in float32, the precision the GPU takes it in:
+the logits arrive as float32, probabilities leave as float32, and sampling
+and acceptance use float32 sums, products, quotients and compares.
+
+Definitions (TensorRT-Edge-LLM guide "CodePredictor Speculative Decoding",
+"How a round works"; lab-artifacts "Lesson 8: Speculative Decoding, Beyond
+Text", section 02 "Two exact algorithms"):
+
+* TopKSoftmax(z; T, k): the k largest logits form the support (total order:
+  larger logit first, lower code id first among equal logits); on it
+  p_i = exp((z_i - max z) / T) / sum_j exp((z_j - max z) / T); p = 0 elsewhere.
+  Temperature and top-k are applied to draft and target alike, as the exact
+  stochastic algorithm requires both to be taken after every processor.
+* Sample(w, u): inverse CDF over the entries with w_i > 0 in ascending code
+  order, with a sequential float32 running sum: t = u * sum(w), return the
+  first i whose running sum exceeds t.
+* Acceptance of draft d: accept iff u < p(d) / q(d) (float32 quotient), which
+  is "accept with probability min(1, p/q)" for u uniform in [0, 1).
+* Residual: w = max(0, p - q) elementwise in float32, sampled with Sample; if
+  every entry is zero (possible only through rounding) p itself is sampled.
+* Greedy: argmax over the raw logits, ties to the lowest code id; the draft is
+  accepted left to right while it equals the target argmax, the first mismatch
+  emits the target argmax, a full match emits the bonus argmax.
+
+Near-tie flags mark decisions whose outcome could flip under a different but
+equally valid float32 rounding of the same quantities:
+  accept  |u - p(d)/q(d)| < 1e-5
+  argmax  top-2 logit gap < 1e-4
+  topk    k-th minus (k+1)-th largest logit < 1e-4  (only when k < V)
+  cdf     t within 1e-5 * sum(w) of an interior boundary of the chosen entry
+
+Pins: tests/test_oracle_distributions.py (torch.topk/torch.softmax,
+np.cumsum + np.searchsorted inverse CDF, the closed form 1 - TV(p, q) for the
+acceptance rate, hand-built tie and degenerate cases, and the greedy
+verifier tuples of tests/golden/greedy_verifier.json).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+EPS_ACCEPT = 1e-5
+EPS_GAP = 1e-4
+EPS_CDF = 1e-5
+
+
+def topk_support(z: np.ndarray, k: int):
+    """Top-k set of float32 logits ``z`` as ascending code ids, plus the
+    near-tie flag of its boundary."""
+    z = np.asarray(z, dtype=np.float32)
+    V = z.shape[0]
+    if k >= V:
+        return np.arange(V), False
+    # primary key: logit descending; secondary: code id ascending
+    order = np.lexsort((np.arange(V), -z))
+    gap = float(z[order[k - 1]]) - float(z[order[k]])
+    return np.sort(order[:k]), gap < EPS_GAP
+
+
+def topk_softmax(z: np.ndarray, temperature, k: int):
+    """TopKSoftmax(z; T, k) -> (dense float32 probabilities [V], topk flag)."""
+    z = np.asarray(z, dtype=np.float32)
+    support, flag = topk_support(z, k)
+    zs = z[support].astype(np.float64)
+    m = zs.max()
+    e = np.exp((zs - m) / float(np.float32(temperature)))
+    p = np.zeros(z.shape[0], dtype=np.float32)
+    p[support] = (e / e.sum()).astype(np.float32)
+    return p, flag
+
+
+def argmax_with_gap(z: np.ndarray):
+    """Greedy choice: (argmax with ties to the lowest id, top-2 near-tie flag)."""
+    z = np.asarray(z, dtype=np.float32)
+    i = int(np.argmax(z))
+    if z.shape[0] == 1:
+        return i, False
+    rest = np.delete(z, i)
+    gap = float(z[i]) - float(rest.max())
+    return i, gap < EPS_GAP
+
+
+def sample(w: np.ndarray, u) -> tuple[int, bool]:
+    """Sample(w, u): sequential float32 inverse CDF over the positive entries
+    of ``w`` in ascending code order.  Returns (code, cdf near-tie flag)."""
+    w = np.asarray(w, dtype=np.float32)
+    u = np.float32(u)
+    ids = np.flatnonzero(w > 0)
+    if ids.size == 0:
+        raise ValueError("sample(): no positive weight")
+    tot = np.float32(0.0)
+    for i in ids:
+        tot = np.float32(tot + w[i])
+    t = np.float32(u * tot)
+    eps = float(tot) * EPS_CDF
+    run = np.float32(0.0)
+    for pos, i in enumerate(ids):
+        before = run
+        run = np.float32(run + w[i])
+        if t < run:
+            near_lo = pos > 0 and abs(float(t) - float(before)) < eps
+            near_hi = pos + 1 < ids.size and abs(float(run) - float(t)) < eps
+            return int(i), bool(near_lo or near_hi)
+    # t == tot after rounding: the last positive entry owns the top end
+    last = ids.size - 1
+    near = last > 0 and abs(float(t) - float(run - w[ids[last]])) < eps
+    return int(ids[last]), bool(near)
+
+
+def accept_test(p_d, q_d, u) -> tuple[bool, bool]:
+    """min(1, p/q) acceptance: (accepted, accept near-tie flag)."""
+    p_d, q_d, u = np.float32(p_d), np.float32(q_d), np.float32(u)
+    ratio = np.float32(p_d / q_d)
+    return bool(u < ratio), abs(float(u) - float(ratio)) < EPS_ACCEPT
+
+
+def residual(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Unnormalised residual max(0, p - q) in float32 (Sample normalises)."""
+    d = np.asarray(p, np.float32) - np.asarray(q, np.float32)
+    return np.maximum(d, np.float32(0.0)).astype(np.float32)
+
+
+def residual_or_target(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """The weights a rejected position is resampled from."""
+    r = residual(p, q)
+    return r if np.any(r > 0) else np.asarray(p, np.float32)
+
+
+@dataclass(frozen=True)
+class GreedyRound:
+    """Decision of one greedy verification block: the accepted draft prefix,
+    the codes emitted this round, and the first rejected draft offset."""
+    accepted: tuple
+    emitted: tuple
+    rejected_at: int | None
+
+
+def verify_greedy(draft, target_argmax) -> GreedyRound:
+    """Greedy argmax-equality verification of one block.
+
+    ``target_argmax`` scores every drafted position plus the one after it, so
+    it must be exactly one longer than ``draft``.  The matching prefix of the
+    draft is kept; the first mismatch is replaced by the target's choice and
+    ends the round; a full match is followed by the target's bonus choice.
+    Pure function: no cache is touched here.
+    """
+    draft, target_argmax = tuple(draft), tuple(target_argmax)
+    if len(target_argmax) != len(draft) + 1:
+        raise ValueError("target_argmax must have one entry per drafted "
+                         "position plus one for the bonus position")
+    n_match = 0
+    while n_match < len(draft) and draft[n_match] == target_argmax[n_match]:
+        n_match += 1
+    accepted = draft[:n_match]
+    emitted = accepted + (target_argmax[n_match],)
+    rejected = n_match if n_match < len(draft) else None
+    return GreedyRound(accepted, emitted, rejected)

@@ -1,0 +1,207 @@
+"""Per-frame decode: prefill, then speculative rounds until the frame is full.
+
+Frame state between rounds (plainest reading of the TensorRT-Edge-LLM guide,
+"How a round works", and Lesson 8, sections 03 and 07): codes c_0..c_s are
+committed, the KV holds positions 0..s, h_s is held, and c_s was drawn from
+head_s(h_s) but has not been fed yet.
+
+Prefill ("RVQ Position Aware ...", Figure 1 caption; SGLang-Omni note, MTP):
+rows [h_frame, E_0[c_0]] at positions 0, 1 -> h_1; c_1 ~ TopKSoftmax(head_1
+h_1) with U(1, target); s = 1.
+
+Round, while s < G - 1, with gamma = min(N - 1, G - 2 - s) (0 when
+speculation is off, which is exactly the autoregressive loop):
+  draft   t = 1..gamma: q_t = TopKSoftmax(head_{s+t} h_s),
+          d_t = Sample(q_t, U(s+t, draft))                  [greedy: argmax]
+  verify  one causal pass over rows r = 0..gamma at positions s+1+r with
+          inputs E_s[c_s] (r = 0) and E_{s+r}[d_r] (r >= 1); row r is scored
+          by head_{s+1+r}, so row t-1 scores draft d_t (the logit shift of
+          Lesson 8, section 07) and row gamma scores the bonus position.
+  accept  t = 1..gamma: keep d_t iff U(s+t, accept) < p_{t-1}(d_t)/q_t(d_t);
+          at the first rejection c_{s+t} = Sample(max(0, p_{t-1} - q_t),
+          U(s+t, target)) and stop; if every draft is kept,
+          c_{s+gamma+1} = Sample(p_gamma, U(s+gamma+1, target)).
+          [greedy: Lesson 8's argmax-equality rule, verify_greedy]
+  commit  n codes; KV truncated to positions 0..s+n; h_{s+n} = row n-1's
+          output; s += n.
+
+Uniforms are indexed by absolute depth, so a depth that was drafted and
+discarded is redrafted in the next round with the same draft uniform; no
+committed code ever depended on it, so the reuse is statistically safe.
+
+Pins: tests/test_oracle_spec.py -- greedy speculative output equals greedy
+autoregressive output exactly for N = 2..8; brute-force enumeration of every
+draft outcome equals the autoregressive joint to 1e-12; chi-square of
+speculative code sequences against the exact autoregressive joint; special
+cases p == q (all accepted) and k = 1 (deterministic chain equals greedy).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import distributions as dist
+from .philox import PURPOSE_ACCEPT, PURPOSE_DRAFT, PURPOSE_TARGET, uniform
+
+MAX_OFFSETS = 8
+
+
+def new_stats() -> dict:
+    return {
+        "frames": 0, "codes": 0, "prefill_passes": 0, "rounds": 0,
+        "proposed": [0] * MAX_OFFSETS, "accepted": [0] * MAX_OFFSETS,
+        "bonus": 0, "near_tie_accept": 0, "near_tie_argmax": 0,
+        "near_tie_cdf": 0, "near_tie_topk": 0,
+    }
+
+
+class _Frame:
+    """Book-keeping of one frame: codes, near-tie flags (bit j = a flagged
+    decision at depth j) and counters."""
+
+    def __init__(self, G, c0, stats):
+        self.codes = np.full(G, -1, dtype=np.int32)
+        self.codes[0] = c0
+        self.flags = 0
+        self.stats = stats
+
+    def flag(self, kind: str, depth: int, hit: bool):
+        if hit:
+            self.flags |= 1 << depth
+            self.stats["near_tie_" + kind] += 1
+
+
+def _dist(model, fr, j, h, dp):
+    """Processed distribution for depth j from hidden h (stochastic mode)."""
+    p, f_topk = dist.topk_softmax(model.logits(j, h), dp["temperature"],
+                                  dp["top_k"])
+    if dp["top_k"] < model.V:
+        fr.flag("topk", j, f_topk)
+    return p
+
+
+def _greedy(model, fr, j, h):
+    code, f_arg = dist.argmax_with_gap(model.logits(j, h))
+    fr.flag("argmax", j, f_arg)
+    return code
+
+
+def _draw(fr, w, seed, depth, purpose):
+    code, f_cdf = dist.sample(w, uniform(seed, depth, purpose))
+    fr.flag("cdf", depth, f_cdf)
+    return code
+
+
+def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
+                 stats: dict | None = None):
+    """Decode one frame.  ``dp`` = {verify_size, greedy, temperature, top_k}.
+
+    Returns (codes [G] int32 with codes[0] = c0, near-tie flag bitmask).
+    """
+    stats = new_stats() if stats is None else stats
+    G = model.G
+    N = int(dp["verify_size"])
+    greedy = bool(dp["greedy"])
+    fr = _Frame(G, c0, stats)
+    kv = model.new_kv()
+
+    # prefill: positions 0 (talker hidden state) and 1 (E_0[c_0])
+    outs = model.forward_rows([np.asarray(h_frame, np.float64),
+                               model.embed_row(0, c0)], [0, 1], kv)
+    stats["prefill_passes"] += 1
+    h = outs[1]
+    if G > 1:
+        if greedy:
+            fr.codes[1] = _greedy(model, fr, 1, h)
+        else:
+            fr.codes[1] = _draw(fr, _dist(model, fr, 1, h, dp), seed, 1,
+                                PURPOSE_TARGET)
+    s = 1
+
+    while s < G - 1:
+        gamma = 0 if N == 0 else min(N - 1, G - 2 - s)
+        # (1) draft from h_s with the later heads
+        drafts, qs = [], []
+        for t in range(1, gamma + 1):
+            if greedy:
+                drafts.append(_greedy(model, fr, s + t, h))
+            else:
+                q = _dist(model, fr, s + t, h, dp)
+                qs.append(q)
+                drafts.append(_draw(fr, q, seed, s + t, PURPOSE_DRAFT))
+        # (2) verify: one causal block over the committed depth + drafts
+        rows = [model.embed_row(s, int(fr.codes[s]))]
+        rows += [model.embed_row(s + t, d) for t, d in enumerate(drafts, 1)]
+        outs = model.forward_rows(rows, [s + 1 + r for r in range(gamma + 1)],
+                                  kv)
+        # (3) accept
+        if greedy:
+            target = [_greedy(model, fr, s + 1 + r, outs[r])
+                      for r in range(gamma + 1)]
+            rnd = dist.verify_greedy(drafts, target)
+            emitted = list(rnd.emitted)
+            n_acc = len(rnd.accepted)
+        else:
+            ps = [_dist(model, fr, s + 1 + r, outs[r], dp)
+                  for r in range(gamma + 1)]
+            emitted = []
+            rejected = False
+            for t in range(1, gamma + 1):
+                d = drafts[t - 1]
+                ok, f_acc = dist.accept_test(ps[t - 1][d], qs[t - 1][d],
+                                             uniform(seed, s + t,
+                                                     PURPOSE_ACCEPT))
+                fr.flag("accept", s + t, f_acc)
+                if ok:
+                    emitted.append(d)
+                    continue
+                w = dist.residual_or_target(ps[t - 1], qs[t - 1])
+                emitted.append(_draw(fr, w, seed, s + t, PURPOSE_TARGET))
+                rejected = True
+                break
+            if rejected:
+                n_acc = len(emitted) - 1    # the last code is the correction
+            else:
+                n_acc = gamma
+                emitted.append(_draw(fr, ps[gamma], seed, s + gamma + 1,
+                                     PURPOSE_TARGET))
+        # (4) commit and truncate
+        n = len(emitted)
+        fr.codes[s + 1: s + 1 + n] = emitted
+        kv.truncate(s + n + 1)
+        h = outs[n - 1]
+        stats["rounds"] += 1
+        for t in range(1, gamma + 1):
+            stats["proposed"][t - 1] += 1
+            if t <= n_acc:
+                stats["accepted"][t - 1] += 1
+        if n_acc == gamma:
+            stats["bonus"] += 1
+        s += n
+
+    stats["frames"] += 1
+    stats["codes"] += G - 1
+    return fr.codes, fr.flags
+
+
+def decode(model, dp: dict, h_frame, c0, seeds, frames=None, streams=None,
+           stats: dict | None = None):
+    """Decode frames/streams of [F][B] inputs; returns codes [F][B][G] and
+    flags [F][B].  ``frames``/``streams`` select a subset (index lists)."""
+    F, B = c0.shape
+    fsel = range(F) if frames is None else frames
+    bsel = range(B) if streams is None else streams
+    codes = np.full((F, B, model.G), -1, dtype=np.int32)
+    flags = np.zeros((F, B), dtype=np.uint32)
+    for f in fsel:
+        for b in bsel:
+            codes[f, b], flags[f, b] = decode_frame(
+                model, dp, h_frame[f, b], int(c0[f, b]), int(seeds[f, b]),
+                stats)
+    return codes, flags
+
+
+def codes_per_round(stats: dict) -> float:
+    """Committed codes per verify pass (a round commits 1 + accepted drafts;
+    the autoregressive loop scores 1.0)."""
+    return (stats["codes"] - stats["frames"]) / max(stats["rounds"], 1) \
+        if stats["rounds"] else 0.0

@@ -1,0 +1,215 @@
+/*
+ * cp_spec.h -- C ABI of the MI355X CodePredictor speculative-decoding library.
+ *
+ * One round of in-frame RVQ speculative decoding, as the TensorRT-Edge-LLM
+ * user guide "CodePredictor Speculative Decoding" describes it (sections "Why
+ * the draft is free" and "How a round works"):
+ *   draft   apply head_{s+t} to the held hidden state h_s, t = 1..N-1, as one
+ *           batched GEMV over the stacked later-depth lm_heads, and sample a
+ *           proposal from each temperature/top-k distribution;
+ *   verify  one causal decoder pass over the committed depth plus the drafts;
+ *   accept  exact speculative sampling (min(1, p/q), residual norm(p - q)+,
+ *           bonus from the trailing distribution), or argmax equality when
+ *           decoding greedily (Lesson 8, "Two exact algorithms");
+ *   commit  the accepted codes and truncate the per-frame KV (Lesson 8,
+ *           section 07, "treat each round as a transaction").
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers named d_* are device pointers on the current HIP device;
+ *     the caller owns all device memory (weights, inputs, outputs, workspace,
+ *     statistics).  The library never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void*; every call is asynchronous on
+ *     it unless stated otherwise.  Results are valid after the stream syncs.
+ *   - Matrices are row-major [out][in].  Weights are float32 or bfloat16 bit
+ *     patterns (uint16) as cfg.weight_dtype says; norm gains are float32.
+ *   - Return value: CP_SPEC_OK, a positive warning, or a negative error.  On
+ *     a negative return nothing was launched; cp_spec_last_error() gives a
+ *     message (thread-local, valid until the next call on the same thread).
+ */
+#ifndef CP_SPEC_H
+#define CP_SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define CP_SPEC_OK 0
+/* Speculation disabled for this model, the autoregressive loop is used:
+ * fewer than three RVQ depths (guide, "Limitations": automatic fallback). */
+#define CP_SPEC_WARN_AR_FALLBACK 1
+#define CP_SPEC_EINVAL (-1)       /* bad argument (e.g. verify_size 1 or > 8) */
+#define CP_SPEC_EUNSUPPORTED (-2) /* shape outside the kernels' bounds        */
+#define CP_SPEC_EHIP (-3)         /* a HIP runtime call failed                */
+#define CP_SPEC_EWORKSPACE (-4)   /* workspace too small / misaligned         */
+
+#define CP_SPEC_F32 0
+#define CP_SPEC_BF16 1
+
+/* Kernel bounds.  The vocabulary bound is the "small-vocabulary" bound of the
+ * guide's "Kernels" section: a whole row of logits is held on chip. */
+#define CP_SPEC_MAX_VOCAB 4096
+#define CP_SPEC_MAX_GROUPS 32
+#define CP_SPEC_MAX_WINDOW 8
+#define CP_SPEC_MAX_OFFSETS 8
+
+/* Near-tie flag bits reported per decision by the component entry points. */
+#define CP_SPEC_FLAG_TOPK 1u   /* k-th minus (k+1)-th largest logit < 1e-4    */
+#define CP_SPEC_FLAG_ARGMAX 2u /* top-2 logit gap < 1e-4 (greedy)             */
+#define CP_SPEC_FLAG_CDF 4u    /* sample point within 1e-5*sum of a boundary  */
+#define CP_SPEC_FLAG_ACCEPT 8u /* |u - p(d)/q(d)| < 1e-5                      */
+
+typedef struct cp_spec cp_spec; /* opaque handle */
+
+typedef struct cp_spec_cfg {
+  int32_t layers;       /* decoder layers L                                  */
+  int32_t hidden;       /* H                                                 */
+  int32_t q_heads;      /* query heads                                       */
+  int32_t kv_heads;     /* key/value heads (grouped-query when < q_heads)    */
+  int32_t head_dim;     /* d (even)                                          */
+  int32_t ffn;          /* SwiGLU intermediate width                         */
+  int32_t code_groups;  /* G: RVQ depths per frame (c_0 .. c_{G-1})          */
+  int32_t vocab;        /* V: codebook size of every depth                   */
+  int32_t weight_dtype; /* CP_SPEC_F32 or CP_SPEC_BF16                       */
+  float rope_theta;     /* RoPE base                                         */
+  float rms_eps;        /* RMSNorm epsilon                                   */
+  int32_t verify_size;  /* N: 0 = off (autoregressive loop), else 2..8: the  */
+                        /* committed depth plus N-1 drafted depths (guide,   */
+                        /* "Options", --cpSpecVerifySize; 1 is rejected)     */
+  int32_t greedy;       /* 1 = argmax decoding (exact greedy verification)   */
+  float temperature;    /* > 0 unless greedy                                 */
+  int32_t top_k;        /* 1..V unless greedy                                */
+  int32_t max_streams;  /* largest n_streams any call will pass              */
+} cp_spec_cfg;
+
+typedef struct cp_spec_weights {
+  const void* embed;       /* [G][V][H]: table j embeds code c_j             */
+  const void* heads;       /* [G-1][V][H]: lm_head j (scores c_j) at j-1      */
+  const float* final_norm; /* [H]                                            */
+  /* Host array of layers*9 device pointers, per layer in this order:
+   * attn_norm[H] (f32), wq[nq*d][H], wk[nkv*d][H], wv[nkv*d][H], wo[H][nq*d],
+   * ffn_norm[H] (f32), w_gate[F][H], w_up[F][H], w_down[H][F].
+   * Read during cp_spec_create only; the device pointers are borrowed. */
+  const void* const* layer;
+} cp_spec_weights;
+
+/* Device-side statistics, accumulated (never cleared) by decode calls. */
+typedef struct cp_spec_stats {
+  int64_t frames;          /* frames completed                               */
+  int64_t codes;           /* codes committed (G-1 per frame)                */
+  int64_t prefill_passes;  /* frame bootstrap passes                         */
+  int64_t rounds;          /* verify passes after the prefill                */
+  int64_t proposed[CP_SPEC_MAX_OFFSETS]; /* drafts proposed at offset t=i+1  */
+  int64_t accepted[CP_SPEC_MAX_OFFSETS]; /* drafts accepted at offset t=i+1  */
+  int64_t bonus;           /* rounds whose drafts were all accepted          */
+  int64_t near_tie_accept, near_tie_argmax, near_tie_cdf, near_tie_topk;
+} cp_spec_stats;
+
+/* Bytes of device workspace cp_spec_create needs for `cfg` (256-byte
+ * aligned base required).  0 if cfg is invalid (see cp_spec_last_error). */
+size_t cp_spec_workspace_bytes(const cp_spec_cfg* cfg);
+
+/* Validate cfg, borrow the weights, carve the caller's workspace and upload
+ * the RoPE table (synchronous: the device must be idle with respect to the
+ * workspace).  Errors: EINVAL for verify_size 1 or > 8, non-positive shapes,
+ * q_heads not a multiple of kv_heads, odd head_dim, temperature <= 0 or
+ * top_k outside 1..V when sampling; EUNSUPPORTED for V > 4096, G > 32, or
+ * matrix widths the kernels do not tile; EWORKSPACE when bytes is short.
+ * Returns CP_SPEC_WARN_AR_FALLBACK (handle still created) when G < 3 with
+ * verify_size > 0: every frame then runs the autoregressive loop. */
+int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg,
+                   void* d_workspace, size_t workspace_bytes, cp_spec** out);
+
+void cp_spec_destroy(cp_spec* h);
+const char* cp_spec_last_error(void);
+
+/* Decode n_frames frames for each of n_streams independent streams.
+ *   d_h_frame   [F][B][H] f32  talker hidden state of each frame (position 0)
+ *   d_c0        [F][B]    i32  the frame's first code (from the talker)
+ *   d_seeds     [F][B]    u64  Philox4x32-10 key of each frame
+ *   d_out_codes [F][B][G] i32  out: c_0..c_{G-1} ([..][0] = c0)
+ *   d_out_flags [F][B]    u32  out, nullable: bit j set when a decision at
+ *                              depth j was a near tie (see CP_SPEC_FLAG_*)
+ *   d_stats     cp_spec_stats  device, nullable: counters are added to it
+ * A frame is a pure function of (weights, h_frame, c0, seed): frames of one
+ * stream run in order, streams advance independently (ragged acceptance).
+ * Host-synchronising: returns after the last frame has been decoded.
+ * Errors: EINVAL for n_streams outside 1..max_streams or n_frames < 0. */
+int cp_spec_decode_frames(cp_spec* h, void* stream, int32_t n_streams,
+                          int32_t n_frames, const float* d_h_frame,
+                          const int32_t* d_c0, const uint64_t* d_seeds,
+                          int32_t* d_out_codes, uint32_t* d_out_flags,
+                          cp_spec_stats* d_stats);
+
+/* Copy device statistics to the host (synchronises `stream`). */
+int cp_spec_get_stats(const cp_spec_stats* d_stats, void* stream,
+                      cp_spec_stats* host_out);
+
+/* ---- component entry points: one step of the round each ----------------
+ * They run exactly the kernels cp_spec_decode_frames runs, on caller data,
+ * so each step can be checked on its own.  They use the handle's workspace
+ * as scratch: calls on one handle must not overlap. */
+
+/* Stacked-head logits (draft GEMV, guide "Why the draft is free"; per-row
+ * verify heads, guide "Limitations"):
+ *   logits[r][:] = head_{d_head[r]} . (apply_final_norm ? RMSNorm_final(x[r])
+ *                                                        : x[r])
+ * d_x [n_rows][H] f32, d_head [n_rows] i32 in 1..G-1 (0 = skip the row),
+ * d_logits [n_rows][V] f32.  n_rows <= max_streams * max(N, 2). */
+int cp_spec_head_logits(cp_spec* h, void* stream, int32_t n_rows,
+                        const float* d_x, const int32_t* d_head,
+                        int32_t apply_final_norm, float* d_logits);
+
+/* Temperature/top-k softmax and inverse-CDF sampling of each row (guide,
+ * "Kernels"; Lesson 8, "Exact stochastic decoding"):
+ *   probs[r] = TopKSoftmax(logits[r]; T, k)  (zero off the top-k support,
+ *              ties at the k-th logit go to the lower code id)
+ *   codes[r] = Sample(probs[r], u[r]): sequential float32 inverse CDF over
+ *              the positive entries in ascending code order
+ * Greedy handles: codes[r] = argmax (ties to the lower id), probs untouched.
+ * d_u nullable (no sampling: codes[r] = -1 when not greedy); d_probs
+ * nullable; d_flags [n_rows] u32 nullable (CP_SPEC_FLAG_* bits). */
+int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows,
+                        const float* d_logits, const float* d_u,
+                        float* d_probs, int32_t* d_codes, uint32_t* d_flags);
+
+/* Accept scan of one round per stream (guide, "How a round works", step 3):
+ *   for t = 1..gamma[b]: accept d_t iff u_accept[b][t-1] < p[t-1](d_t) /
+ *   q[t-1](d_t) (float32); at the first rejection emit
+ *   Sample(max(0, p[t-1] - q[t-1]), u_target[b][t-1]) and stop; if all are
+ *   accepted emit Sample(p[gamma], u_target[b][gamma]).
+ * Greedy handles: d_q and the uniforms are ignored, d_p holds target logits
+ * rows and the argmax-equality rule applies.
+ *   d_gamma [B] i32 in 0..width; d_draft [B][width] i32;
+ *   d_q [B][width][V] f32; d_p [B][width+1][V] f32;
+ *   d_u_accept [B][width] f32; d_u_target [B][width+1] f32;
+ *   d_n out [B] i32 (codes committed, 1..gamma+1);
+ *   d_codes out [B][width+1] i32 (the committed codes, in depth order);
+ *   d_flags out [B] u32 nullable (bit t-1: near tie at offset t). */
+int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width,
+                   const int32_t* d_gamma, const int32_t* d_draft,
+                   const float* d_q, const float* d_p,
+                   const float* d_u_accept, const float* d_u_target,
+                   int32_t* d_n, int32_t* d_codes, uint32_t* d_flags);
+
+/* One causal decoder pass over rows_per_stream rows of each stream (the
+ * verify pass, guide "How a round works", step 2):
+ *   d_x [B][R][H] f32   in: input rows; out: final-RMSNormed hidden states
+ *   d_pos [B][R] i32    position of each row (-1 = inactive row); a stream's
+ *                       active rows must be consecutive positions, and every
+ *                       position below its first row must already be in KV
+ *   d_kv  [B][L][2][G][n_kv][d] f32  per-frame cache: K (before RoPE) at
+ *                       [..][0], V at [..][1]; rows write their position and
+ *                       attend to positions <= their own.
+ * n_streams <= max_streams, rows_per_stream <= max(N, 2). */
+int cp_spec_decoder_forward(cp_spec* h, void* stream, int32_t n_streams,
+                            int32_t rows_per_stream, float* d_x,
+                            const int32_t* d_pos, float* d_kv);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CP_SPEC_H */

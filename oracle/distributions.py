@@ -97,6 +97,7 @@ def sample(w: np.ndarray, u) -> tuple[int, bool]:
     t = np.float32(u * tot)
     eps = float(tot) * EPS_CDF
     run = np.float32(0.0)
+    before = run
     for pos, i in enumerate(ids):
         before = run
         run = np.float32(run + w[i])
@@ -104,10 +105,9 @@ def sample(w: np.ndarray, u) -> tuple[int, bool]:
             near_lo = pos > 0 and abs(float(t) - float(before)) < eps
             near_hi = pos + 1 < ids.size and abs(float(run) - float(t)) < eps
             return int(i), bool(near_lo or near_hi)
-    # t == tot after rounding: the last positive entry owns the top end
-    last = ids.size - 1
-    near = last > 0 and abs(float(t) - float(run - w[ids[last]])) < eps
-    return int(ids[last]), bool(near)
+    # t == sum after rounding: the last positive entry owns the top end
+    near = ids.size > 1 and abs(float(t) - float(before)) < eps
+    return int(ids[-1]), bool(near)
 
 
 def accept_test(p_d, q_d, u) -> tuple[bool, bool]:
@@ -127,6 +127,36 @@ def residual_or_target(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     """The weights a rejected position is resampled from."""
     r = residual(p, q)
     return r if np.any(r > 0) else np.asarray(p, np.float32)
+
+
+def accept_scan(drafts, qs, ps, u_accept, u_target):
+    """Stochastic accept scan of one round (guide, "How a round works",
+    step 3).  ``drafts[t-1]`` was drawn from ``qs[t-1]``; ``ps[r]`` is the
+    verified distribution of row r (row t-1 scores draft t, row gamma the
+    bonus position).  ``u_accept(t)`` and ``u_target(t)`` give the uniforms
+    of offset t.  Returns (emitted codes, drafts accepted, [(offset, kind)]
+    near ties) where kind is 'accept' or 'cdf'."""
+    gamma = len(drafts)
+    emitted, near = [], []
+    for t in range(1, gamma + 1):
+        d = drafts[t - 1]
+        ok, f_acc = accept_test(ps[t - 1][d], qs[t - 1][d], u_accept(t))
+        if f_acc:
+            near.append((t, "accept"))
+        if ok:
+            emitted.append(d)
+            continue
+        code, f_cdf = sample(residual_or_target(ps[t - 1], qs[t - 1]),
+                             u_target(t))
+        if f_cdf:
+            near.append((t, "cdf"))
+        emitted.append(code)
+        return emitted, t - 1, near
+    code, f_cdf = sample(ps[gamma], u_target(gamma + 1))
+    if f_cdf:
+        near.append((gamma + 1, "cdf"))
+    emitted.append(code)
+    return emitted, gamma, near
 
 
 @dataclass(frozen=True)

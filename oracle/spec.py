@@ -143,27 +143,12 @@ def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
         else:
             ps = [_dist(model, fr, s + 1 + r, outs[r], dp)
                   for r in range(gamma + 1)]
-            emitted = []
-            rejected = False
-            for t in range(1, gamma + 1):
-                d = drafts[t - 1]
-                ok, f_acc = dist.accept_test(ps[t - 1][d], qs[t - 1][d],
-                                             uniform(seed, s + t,
-                                                     PURPOSE_ACCEPT))
-                fr.flag("accept", s + t, f_acc)
-                if ok:
-                    emitted.append(d)
-                    continue
-                w = dist.residual_or_target(ps[t - 1], qs[t - 1])
-                emitted.append(_draw(fr, w, seed, s + t, PURPOSE_TARGET))
-                rejected = True
-                break
-            if rejected:
-                n_acc = len(emitted) - 1    # the last code is the correction
-            else:
-                n_acc = gamma
-                emitted.append(_draw(fr, ps[gamma], seed, s + gamma + 1,
-                                     PURPOSE_TARGET))
+            emitted, n_acc, near = dist.accept_scan(
+                drafts, qs, ps,
+                lambda t: uniform(seed, s + t, PURPOSE_ACCEPT),
+                lambda t: uniform(seed, s + t, PURPOSE_TARGET))
+            for t, kind in near:
+                fr.flag(kind, s + t, True)
         # (4) commit and truncate
         n = len(emitted)
         fr.codes[s + 1: s + 1 + n] = emitted

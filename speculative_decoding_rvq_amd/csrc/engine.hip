@@ -1,0 +1,500 @@
+// Host side of the CodePredictor speculative-decoding library: validation,
+// workspace carving, the round sequence (captured once into a hipGraph per
+// stream count and replayed), the frame loop, and the C ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace cps;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define CPS_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(CP_SPEC_EHIP, std::string(#call) + ": " + hipGetErrorString(e_));    \
+  } while (0)
+
+struct Shape {
+  int L, H, nq, nkv, d, F, G, V, wdt, N, greedy, top_k, maxB;
+  float theta, eps, T;
+  int R, W, qdim, kvdim;
+  int vec;  // weight elements per 16-byte chunk
+};
+
+struct Layout {
+  size_t st, call, dhead, thead, pos, hstate, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
+      tlogits, p, tcode, tflags, rope, total;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int choose_kt(int K, int vec) {
+  if (K % vec) return 0;
+  const int segs = K / vec;
+  for (int kt : {256, 128, 64})
+    if (segs % kt == 0 && segs / kt <= 4) return kt;
+  return 0;
+}
+
+int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
+  if (!c) return fail(CP_SPEC_EINVAL, "cfg is null");
+  *warn_ar = false;
+  if (c->layers < 1 || c->hidden < 1 || c->q_heads < 1 || c->kv_heads < 1 || c->head_dim < 2 ||
+      c->ffn < 1 || c->vocab < 1 || c->max_streams < 1)
+    return fail(CP_SPEC_EINVAL, "non-positive shape in cfg");
+  if (c->code_groups < 2) return fail(CP_SPEC_EINVAL, "code_groups must be >= 2");
+  if (c->q_heads % c->kv_heads) return fail(CP_SPEC_EINVAL, "q_heads must be a multiple of kv_heads");
+  if (c->head_dim % 2) return fail(CP_SPEC_EINVAL, "head_dim must be even");
+  if (c->weight_dtype != CP_SPEC_F32 && c->weight_dtype != CP_SPEC_BF16)
+    return fail(CP_SPEC_EINVAL, "weight_dtype must be CP_SPEC_F32 or CP_SPEC_BF16");
+  if (c->verify_size == 1)
+    return fail(CP_SPEC_EINVAL, "verify_size 1 leaves no draft slot (valid: 0 = off, 2..8)");
+  if (c->verify_size < 0 || c->verify_size > CP_SPEC_MAX_WINDOW)
+    return fail(CP_SPEC_EINVAL, "verify_size must be 0 (off) or 2..8");
+  if (!c->greedy) {
+    if (!(c->temperature > 0.0f)) return fail(CP_SPEC_EINVAL, "temperature must be > 0");
+    if (c->top_k < 1 || c->top_k > c->vocab) return fail(CP_SPEC_EINVAL, "top_k must be in 1..vocab");
+  }
+  if (c->vocab > CP_SPEC_MAX_VOCAB)
+    return fail(CP_SPEC_EUNSUPPORTED, "vocab above the small-vocabulary bound (4096)");
+  const int vpt = c->vocab / 256;
+  if (c->vocab % 256 || (vpt & (vpt - 1)))
+    return fail(CP_SPEC_EUNSUPPORTED, "vocab must be 256 * 2^i (256..4096)");
+  if (c->code_groups > CP_SPEC_MAX_GROUPS) return fail(CP_SPEC_EUNSUPPORTED, "code_groups > 32");
+  if (c->head_dim > 128) return fail(CP_SPEC_EUNSUPPORTED, "head_dim > 128");
+  Shape& s_ = *s;
+  s_.L = c->layers; s_.H = c->hidden; s_.nq = c->q_heads; s_.nkv = c->kv_heads; s_.d = c->head_dim;
+  s_.F = c->ffn; s_.G = c->code_groups; s_.V = c->vocab; s_.wdt = c->weight_dtype;
+  s_.N = c->verify_size; s_.greedy = c->greedy ? 1 : 0;
+  s_.top_k = c->greedy ? 1 : c->top_k; s_.maxB = c->max_streams;
+  s_.theta = c->rope_theta; s_.eps = c->rms_eps; s_.T = c->greedy ? 1.0f : c->temperature;
+  s_.qdim = s_.nq * s_.d; s_.kvdim = s_.nkv * s_.d;
+  s_.vec = s_.wdt == CP_SPEC_BF16 ? 8 : 4;
+  if (s_.N > 0 && s_.G < 3) {
+    *warn_ar = true;  // no depth to draft: the autoregressive loop
+    s_.N = 0;
+  }
+  s_.R = std::max(s_.N, 2);
+  s_.W = std::max(s_.N - 1, 1);
+  for (int K : {s_.H, s_.qdim, s_.F})
+    if (!choose_kt(K, s_.vec))
+      return fail(CP_SPEC_EUNSUPPORTED, "matrix width " + std::to_string(K) +
+                                            " not tileable (multiple of 256 fp32 / 512 bf16 "
+                                            "elements, at most 4 chunks per lane)");
+  for (int N_ : {s_.qdim + 2 * s_.kvdim, s_.H, s_.V, s_.kvdim, s_.qdim})
+    if (N_ % kRPGHost) return fail(CP_SPEC_EUNSUPPORTED, "output width must be a multiple of 4");
+  if (s_.F % 2) return fail(CP_SPEC_EUNSUPPORTED, "ffn must be even");
+  return CP_SPEC_OK;
+}
+
+Layout make_layout(const Shape& s) {
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t B = s.maxB, R = s.R, W = s.W, f4 = sizeof(float), i4 = sizeof(int);
+  l.st = take(B * sizeof(StreamState));
+  l.call = take(sizeof(CallDesc));
+  l.dhead = take(B * W * i4);
+  l.thead = take(B * R * i4);
+  l.pos = take(B * R * i4);
+  l.hstate = take(B * s.H * f4);
+  l.X = take(B * R * s.H * f4);
+  l.Hout = take(B * R * s.H * f4);
+  l.Q = take(B * R * s.qdim * f4);
+  l.attn = take(B * R * s.qdim * f4);
+  l.act = take(B * R * s.F * f4);
+  l.kv = take(B * static_cast<size_t>(s.L) * 2 * s.G * s.kvdim * f4);
+  l.dlogits = take(B * W * s.V * f4);
+  l.q = take(B * W * s.V * f4);
+  l.dcode = take(B * W * i4);
+  l.dflags = take(B * W * i4);
+  l.tlogits = take(B * R * s.V * f4);
+  l.p = take(B * R * s.V * f4);
+  l.tcode = take(B * R * i4);
+  l.tflags = take(B * R * i4);
+  l.rope = take(static_cast<size_t>(s.G) * (s.d / 2) * sizeof(float2));
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+struct cp_spec {
+  Shape sh;
+  Layout lo;
+  char* ws;
+  const void* embed;
+  const void* heads;
+  const float* fnorm;
+  std::vector<std::array<const void*, 9>> layers;
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t graph = nullptr;
+  int graph_B = -1;
+  bool use_graph = true;
+
+  template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  long long kv_sb() const { return static_cast<long long>(sh.L) * 2 * sh.G * sh.kvdim; }
+
+  RoundArgs round_args(int B) const {
+    RoundArgs r{};
+    r.B = B; r.R = sh.R; r.W = sh.W; r.G = sh.G; r.V = sh.V; r.H = sh.H; r.N = sh.N;
+    r.greedy = sh.greedy; r.top_k = sh.top_k; r.L = sh.L; r.T = sh.T;
+    r.wbf16 = sh.wdt == CP_SPEC_BF16;
+    r.embed = embed;
+    r.st = at<StreamState>(lo.st);
+    r.call = at<CallDesc>(lo.call);
+    r.dhead = at<int>(lo.dhead);
+    r.thead = at<int>(lo.thead);
+    r.pos = at<int>(lo.pos);
+    r.hstate = at<float>(lo.hstate);
+    r.X = at<float>(lo.X);
+    r.Hout = at<float>(lo.Hout);
+    r.dlogits = at<float>(lo.dlogits);
+    r.q = at<float>(lo.q);
+    r.dcode = at<int>(lo.dcode);
+    r.dflags = at<uint32_t>(lo.dflags);
+    r.tlogits = at<float>(lo.tlogits);
+    r.p = at<float>(lo.p);
+    r.tcode = at<int>(lo.tcode);
+    r.tflags = at<uint32_t>(lo.tflags);
+    return r;
+  }
+};
+
+namespace {
+
+int mt_for(int M) { return M <= 2 ? 2 : (M <= 4 ? 4 : 8); }
+
+// One skinny projection: Y (op) W . rows(X).
+int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
+  a.kt = choose_kt(a.K, h->sh.vec);
+  if (!a.kt) return fail(CP_SPEC_EUNSUPPORTED, "untileable K");
+  const int rg = 256 / a.kt;
+  a.units = mode == kSwiGLU ? a.N / 2 : a.N / 4;
+  int gx = (a.units + rg - 1) / rg;
+  gx = std::min(gx, 4096);
+  int mt, gy;
+  if (mode == kHead) {
+    mt = 1;
+    gy = a.M;
+  } else {
+    mt = mt_for(a.M);
+    gy = (a.M + mt - 1) / mt;
+  }
+  if (a.M <= 0) return CP_SPEC_OK;
+  CPS_HIP(launch_gemv(h->sh.wdt, mode, mt, a, gx, gy, s));
+  return CP_SPEC_OK;
+}
+
+// All decoder layers over B*R rows of X at positions `pos`, cache `kv`.
+int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const int* pos, float* kv) {
+  const Shape& sh = h->sh;
+  const int M = B * R;
+  float* Q = h->at<float>(h->lo.Q);
+  float* attn = h->at<float>(h->lo.attn);
+  float* act = h->at<float>(h->lo.act);
+  const long long layer_kv = 2LL * sh.G * sh.kvdim;
+  for (int l = 0; l < sh.L; ++l) {
+    const auto& w = h->layers[l];
+    float* kvl = kv + l * layer_kv;
+    GemvArgs a{};
+    a.W0 = w[1]; a.W1 = w[2]; a.W2 = w[3];
+    a.N = sh.qdim + 2 * sh.kvdim; a.K = sh.H;
+    a.X = X; a.ldx = sh.H; a.xdiv = 1; a.M = M;
+    a.norm_g = static_cast<const float*>(w[0]); a.eps = sh.eps;
+    a.Y = Q; a.ldy = sh.qdim;
+    a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
+    a.kv_vo = static_cast<long long>(sh.G) * sh.kvdim; a.rows_per_stream = R; a.pos = pos;
+    a.kv_positions = sh.G;
+    int rc = gemv(h, s, kQKV, a);
+    if (rc) return rc;
+
+    AttnArgs at{};
+    at.Q = Q; at.out = attn; at.kv = kvl; at.kv_sb = h->kv_sb(); at.kv_vo = a.kv_vo; at.pos = pos;
+    at.rope = h->at<float2>(h->lo.rope); at.R = R; at.nq = sh.nq; at.nkv = sh.nkv; at.d = sh.d;
+    at.G = sh.G; at.scale = 1.0f / std::sqrt(static_cast<float>(sh.d));
+    CPS_HIP(launch_attention(at, B, s));
+
+    GemvArgs o{};
+    o.W0 = w[4]; o.N = sh.H; o.K = sh.qdim; o.X = attn; o.ldx = sh.qdim; o.xdiv = 1; o.M = M;
+    o.Y = X; o.ldy = sh.H;
+    if ((rc = gemv(h, s, kAdd, o))) return rc;
+
+    GemvArgs g{};
+    g.W0 = w[6]; g.W1 = w[7]; g.N = sh.F; g.K = sh.H; g.X = X; g.ldx = sh.H; g.xdiv = 1; g.M = M;
+    g.norm_g = static_cast<const float*>(w[5]); g.eps = sh.eps; g.Y = act; g.ldy = sh.F;
+    if ((rc = gemv(h, s, kSwiGLU, g))) return rc;
+
+    GemvArgs dn{};
+    dn.W0 = w[8]; dn.N = sh.H; dn.K = sh.F; dn.X = act; dn.ldx = sh.F; dn.xdiv = 1; dn.M = M;
+    dn.Y = X; dn.ldy = sh.H;
+    if ((rc = gemv(h, s, kAdd, dn))) return rc;
+  }
+  return CP_SPEC_OK;
+}
+
+int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv, const int* head,
+                const float* norm_g, float* xnorm_out, float* logits) {
+  GemvArgs a{};
+  a.W0 = h->heads; a.N = h->sh.V; a.K = h->sh.H; a.X = X; a.ldx = h->sh.H; a.xdiv = xdiv; a.M = M;
+  a.norm_g = norm_g; a.eps = h->sh.eps; a.Y = logits; a.ldy = h->sh.V; a.head = head;
+  a.head_stride = static_cast<long long>(h->sh.V) * h->sh.H; a.xnorm_out = xnorm_out;
+  a.n_heads = h->sh.G - 1;
+  return gemv(h, s, kHead, a);
+}
+
+// The whole round for B streams: draft GEMV -> draft sample -> verify pass ->
+// per-row heads -> target softmax -> accept/commit/truncate.
+int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
+  const Shape& sh = h->sh;
+  const RoundArgs r = h->round_args(B);
+  int rc;
+  if (sh.N >= 2) {
+    if ((rc = head_logits(h, s, B * sh.W, r.hstate, sh.W, r.dhead, nullptr, nullptr, r.dlogits)))
+      return rc;
+    CPS_HIP(launch_draft_topk(r, s));
+  }
+  if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv)))) return rc;
+  if ((rc = head_logits(h, s, B * sh.R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits))) return rc;
+  CPS_HIP(launch_target_topk(r, s));
+  CPS_HIP(launch_round_accept(r, s));
+  return CP_SPEC_OK;
+}
+
+int ensure_graph(cp_spec* h, int B) {
+  if (h->graph && h->graph_B == B) return CP_SPEC_OK;
+  if (h->graph) {
+    hipGraphExecDestroy(h->graph);
+    h->graph = nullptr;
+    h->graph_B = -1;
+  }
+  hipGraph_t g = nullptr;
+  CPS_HIP(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  const int rc = enqueue_round(h, h->cap_stream, B);
+  const hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
+  if (rc) {
+    if (g) hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(CP_SPEC_EHIP, std::string("graph capture: ") + hipGetErrorString(e));
+  const hipError_t ei = hipGraphInstantiate(&h->graph, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (ei != hipSuccess) return fail(CP_SPEC_EHIP, std::string("graph instantiate: ") + hipGetErrorString(ei));
+  h->graph_B = B;
+  return CP_SPEC_OK;
+}
+
+// Rounds a stream still needs at the least: every round commits at most
+// max(N, 1) codes and every frame starts with its prefill pass.
+long long rounds_lower_bound(const Shape& sh, const StreamState& st, int F) {
+  const int nw = std::max(sh.N, 1);
+  const long long per_frame = 1 + (sh.G - 2 + nw - 1) / nw;
+  if (st.mode == kModeDone) return 0;
+  if (st.mode == kModePrefill) return static_cast<long long>(F - st.f) * per_frame;
+  return (sh.G - 1 - st.s + nw - 1) / nw + static_cast<long long>(F - st.f - 1) * per_frame;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cp_spec_last_error(void) { return g_err.c_str(); }
+
+size_t cp_spec_workspace_bytes(const cp_spec_cfg* cfg) {
+  Shape s{};
+  bool warn = false;
+  if (validate(cfg, &s, &warn) < 0) return 0;
+  return make_layout(s).total;
+}
+
+int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_workspace,
+                   size_t workspace_bytes, cp_spec** out) {
+  if (!out) return fail(CP_SPEC_EINVAL, "out is null");
+  *out = nullptr;
+  Shape s{};
+  bool warn = false;
+  const int rc = validate(cfg, &s, &warn);
+  if (rc < 0) return rc;
+  if (!w || !w->embed || !w->heads || !w->final_norm || !w->layer)
+    return fail(CP_SPEC_EINVAL, "weights incomplete");
+  const Layout lo = make_layout(s);
+  if (!d_workspace || workspace_bytes < lo.total)
+    return fail(CP_SPEC_EWORKSPACE, "workspace smaller than cp_spec_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256)
+    return fail(CP_SPEC_EWORKSPACE, "workspace must be 256-byte aligned");
+  for (int i = 0; i < 9 * s.L; ++i)
+    if (!w->layer[i]) return fail(CP_SPEC_EINVAL, "null layer weight pointer");
+
+  cp_spec* h = new cp_spec();
+  h->sh = s;
+  h->lo = lo;
+  h->ws = static_cast<char*>(d_workspace);
+  h->embed = w->embed;
+  h->heads = w->heads;
+  h->fnorm = w->final_norm;
+  h->layers.resize(s.L);
+  for (int l = 0; l < s.L; ++l)
+    for (int j = 0; j < 9; ++j) h->layers[l][j] = w->layer[9 * l + j];
+
+  // RoPE table, angle = position * theta^(-2i/d), evaluated in double.
+  std::vector<float2> rope(static_cast<size_t>(s.G) * (s.d / 2));
+  for (int p = 0; p < s.G; ++p)
+    for (int i = 0; i < s.d / 2; ++i) {
+      const double ang = p * std::pow(static_cast<double>(s.theta), -2.0 * i / s.d);
+      rope[static_cast<size_t>(p) * (s.d / 2) + i] =
+          make_float2(static_cast<float>(std::cos(ang)), static_cast<float>(std::sin(ang)));
+    }
+  hipError_t e = hipMemset(d_workspace, 0, lo.total);
+  if (e == hipSuccess)
+    e = hipMemcpy(h->at<char>(lo.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(CP_SPEC_EHIP, std::string("create: ") + hipGetErrorString(e));
+  }
+  *out = h;
+  if (warn) {
+    g_err = "fewer than two drafted depths available: autoregressive loop";
+    return CP_SPEC_WARN_AR_FALLBACK;
+  }
+  return CP_SPEC_OK;
+}
+
+void cp_spec_destroy(cp_spec* h) {
+  if (!h) return;
+  if (h->graph) hipGraphExecDestroy(h->graph);
+  if (h->cap_stream) hipStreamDestroy(h->cap_stream);
+  delete h;
+}
+
+int cp_spec_decode_frames(cp_spec* h, void* stream, int32_t n_streams, int32_t n_frames,
+                          const float* d_h_frame, const int32_t* d_c0, const uint64_t* d_seeds,
+                          int32_t* d_out_codes, uint32_t* d_out_flags, cp_spec_stats* d_stats) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (n_streams < 1 || n_streams > h->sh.maxB)
+    return fail(CP_SPEC_EINVAL, "n_streams outside 1..max_streams");
+  if (n_frames < 0) return fail(CP_SPEC_EINVAL, "n_frames < 0");
+  if (n_frames == 0) return CP_SPEC_OK;
+  if (!d_h_frame || !d_c0 || !d_seeds || !d_out_codes)
+    return fail(CP_SPEC_EINVAL, "null input/output pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int B = n_streams;
+  const RoundArgs r = h->round_args(B);
+  CallDesc c{};
+  c.h_frame = d_h_frame; c.c0 = d_c0; c.seeds = d_seeds; c.out_codes = d_out_codes;
+  c.out_flags = d_out_flags; c.stats = d_stats; c.F = n_frames; c.B = B;
+  if (h->use_graph) {
+    const int rc = ensure_graph(h, B);
+    if (rc) return rc;
+  }
+  CPS_HIP(launch_round_init(r, c, s));
+  std::vector<StreamState> st(B);
+  const int nw = std::max(h->sh.N, 1);
+  long long chunk = static_cast<long long>(n_frames) * (1 + (h->sh.G - 2 + nw - 1) / nw);
+  const long long cap = static_cast<long long>(n_frames) * h->sh.G + 16;
+  long long launched = 0;
+  for (;;) {
+    for (long long i = 0; i < chunk; ++i) {
+      if (h->use_graph) {
+        CPS_HIP(hipGraphLaunch(h->graph, s));
+      } else {
+        const int rc = enqueue_round(h, s, B);
+        if (rc) return rc;
+      }
+    }
+    launched += chunk;
+    CPS_HIP(hipMemcpyAsync(st.data(), r.st, B * sizeof(StreamState), hipMemcpyDeviceToHost, s));
+    CPS_HIP(hipStreamSynchronize(s));
+    long long need = 0;
+    for (int b = 0; b < B; ++b) need = std::max(need, rounds_lower_bound(h->sh, st[b], n_frames));
+    if (need == 0) break;
+    if (launched > cap) return fail(CP_SPEC_EHIP, "round loop did not terminate");
+    chunk = need;
+  }
+  return CP_SPEC_OK;
+}
+
+int cp_spec_get_stats(const cp_spec_stats* d_stats, void* stream, cp_spec_stats* host_out) {
+  if (!d_stats || !host_out) return fail(CP_SPEC_EINVAL, "null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CPS_HIP(hipMemcpyAsync(host_out, d_stats, sizeof(cp_spec_stats), hipMemcpyDeviceToHost, s));
+  CPS_HIP(hipStreamSynchronize(s));
+  return CP_SPEC_OK;
+}
+
+int cp_spec_head_logits(cp_spec* h, void* stream, int32_t n_rows, const float* d_x,
+                        const int32_t* d_head, int32_t apply_final_norm, float* d_logits) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (n_rows < 0 || n_rows > h->sh.maxB * h->sh.R) return fail(CP_SPEC_EINVAL, "n_rows out of range");
+  if (n_rows == 0) return CP_SPEC_OK;
+  if (!d_x || !d_head || !d_logits) return fail(CP_SPEC_EINVAL, "null pointer");
+  return head_logits(h, static_cast<hipStream_t>(stream), n_rows, d_x, 1, d_head,
+                     apply_final_norm ? h->fnorm : nullptr, nullptr, d_logits);
+}
+
+int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows, const float* d_logits,
+                        const float* d_u, float* d_probs, int32_t* d_codes, uint32_t* d_flags) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (n_rows < 0) return fail(CP_SPEC_EINVAL, "n_rows < 0");
+  if (n_rows == 0) return CP_SPEC_OK;
+  if (!d_logits) return fail(CP_SPEC_EINVAL, "null logits");
+  TopkArgs a{};
+  a.logits = d_logits; a.probs = d_probs; a.codes = d_codes; a.flags = d_flags; a.u = d_u;
+  a.V = h->sh.V; a.k = h->sh.top_k; a.greedy = h->sh.greedy; a.T = h->sh.T; a.n_rows = n_rows;
+  CPS_HIP(launch_topk_rows(a, static_cast<hipStream_t>(stream)));
+  return CP_SPEC_OK;
+}
+
+int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width, const int32_t* d_gamma,
+                   const int32_t* d_draft, const float* d_q, const float* d_p,
+                   const float* d_u_accept, const float* d_u_target, int32_t* d_n, int32_t* d_codes,
+                   uint32_t* d_flags) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (n_streams < 0 || width < 0 || width > CP_SPEC_MAX_WINDOW - 1)
+    return fail(CP_SPEC_EINVAL, "n_streams/width out of range");
+  if (n_streams == 0) return CP_SPEC_OK;
+  if (!d_gamma || !d_draft || !d_p || !d_n || !d_codes || (!h->sh.greedy && (!d_q || !d_u_accept || !d_u_target)))
+    return fail(CP_SPEC_EINVAL, "null pointer");
+  AcceptArgs a{};
+  a.B = n_streams; a.W = width; a.V = h->sh.V; a.greedy = h->sh.greedy; a.gamma = d_gamma;
+  a.draft = d_draft; a.q = d_q; a.p = d_p; a.u_acc = d_u_accept; a.u_tgt = d_u_target; a.n_out = d_n;
+  a.codes_out = d_codes; a.flags_out = d_flags;
+  CPS_HIP(launch_accept_rows(a, static_cast<hipStream_t>(stream)));
+  return CP_SPEC_OK;
+}
+
+int cp_spec_decoder_forward(cp_spec* h, void* stream, int32_t n_streams, int32_t rows_per_stream,
+                            float* d_x, const int32_t* d_pos, float* d_kv) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (n_streams < 0 || n_streams > h->sh.maxB || rows_per_stream < 1 || rows_per_stream > h->sh.R)
+    return fail(CP_SPEC_EINVAL, "n_streams/rows_per_stream out of range");
+  if (n_streams == 0) return CP_SPEC_OK;
+  if (!d_x || !d_pos || !d_kv) return fail(CP_SPEC_EINVAL, "null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rc = run_layers(h, s, n_streams, rows_per_stream, d_x, d_pos, d_kv);
+  if (rc) return rc;
+  CPS_HIP(launch_rmsnorm_rows(d_x, d_x, h->fnorm, n_streams * rows_per_stream, h->sh.H, h->sh.eps, s));
+  return CP_SPEC_OK;
+}
+
+}  // extern "C"

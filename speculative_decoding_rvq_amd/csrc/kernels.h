@@ -1,0 +1,154 @@
+// Kernel argument blocks and launchers of the CodePredictor round.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/cp_spec.h"
+
+namespace cps {
+
+constexpr int kRPG = 4;       // GEMV output rows per row group per pass
+constexpr int kRPGHost = kRPG;
+
+enum GemvMode : int {
+  kStore = 0,   // Y[m][o] = acc
+  kAdd = 1,     // Y[m][o] += acc             (residual add)
+  kSwiGLU = 2,  // Y[m][o] = silu(gate) * up  (W0 = gate, W1 = up)
+  kQKV = 3,     // q -> Y, k/v -> KV cache at the row's position
+  kHead = 4,    // per-row lm_head: W = heads[head[m] - 1]
+};
+
+struct GemvArgs {
+  const void* W0;
+  const void* W1;
+  const void* W2;
+  int N;          // output rows (kQKV: qdim + 2*kvdim; kSwiGLU: ffn)
+  int K;          // reduction length
+  const float* X; // activation rows
+  int ldx;
+  int xdiv;       // activation row of output row m is m / xdiv
+  int M;          // activation rows
+  const float* norm_g;  // nullable: RMSNorm(x) * g applied to X rows first
+  float eps;
+  float* Y;
+  int ldy;
+  // kQKV
+  int qdim, kvdim;
+  float* kv;            // [B][L][2][G][nkv][d] base of this layer: + b*kv_sb
+  long long kv_sb;      // floats per stream in the cache
+  long long kv_vo;      // offset of V from K inside a layer
+  int rows_per_stream;  // R
+  int kv_positions;     // G: positions per stream in the cache
+  const int* pos;       // [M] position of each row, -1 = inactive
+  // kHead
+  const int* head;      // [M] head index 1..n_heads, 0 = skip
+  int n_heads;          // G-1
+  long long head_stride;  // elements per head matrix (V*H)
+  float* xnorm_out;     // nullable: normalised rows written here ([M][K])
+  // tiling (host-chosen)
+  int kt;     // threads covering one row's K (64/128/256)
+  int units;  // number of RPG-row output units
+};
+
+struct AttnArgs {
+  const float* Q;     // [B*R][qdim]
+  float* out;         // [B*R][qdim]
+  const float* kv;    // layer base, + b*kv_sb
+  long long kv_sb;
+  long long kv_vo;
+  const int* pos;     // [B*R]
+  const float2* rope; // [G][d/2] (cos, sin)
+  int R, nq, nkv, d, G;
+  float scale;
+};
+
+struct TopkArgs {
+  const float* logits;  // row r at logits + r*V
+  float* probs;         // nullable
+  int* codes;           // nullable
+  uint32_t* flags;      // nullable
+  const float* u;       // nullable (component call: uniforms per row)
+  int V, k, greedy;
+  float T;
+  int n_rows;
+};
+
+struct AcceptArgs {  // component accept
+  int B, W, V, greedy;
+  const int* gamma;
+  const int* draft;
+  const float* q;
+  const float* p;
+  const float* u_acc;
+  const float* u_tgt;
+  int* n_out;
+  int* codes_out;
+  uint32_t* flags_out;
+};
+
+// Per-stream state of the round engine.
+struct StreamState {
+  int f;       // frame being decoded
+  int s;       // committed depth (c_0..c_s committed, c_s not yet fed)
+  int gamma;   // drafts in the coming round
+  int mode;    // kModePrefill / kModeSpec / kModeDone
+  uint32_t flags;
+  int pad[3];
+};
+enum { kModePrefill = 0, kModeSpec = 1, kModeDone = 2 };
+
+// Arguments of one decode call, written on device by the init kernel so the
+// captured round graph can be replayed for any call.
+struct CallDesc {
+  const float* h_frame;
+  const int* c0;
+  const uint64_t* seeds;
+  int* out_codes;
+  uint32_t* out_flags;
+  cp_spec_stats* stats;
+  int F, B;
+  int active;   // streams with frames left
+  int pad;
+};
+
+struct RoundArgs {
+  // shapes
+  int B, R, W, G, V, H, N, greedy, top_k, L;
+  float T;
+  int wbf16;
+  // weights
+  const void* embed;
+  // state and buffers
+  StreamState* st;
+  CallDesc* call;
+  int* dhead;   // [B][W]
+  int* thead;   // [B][R]
+  int* pos;     // [B][R]
+  float* hstate;   // [B][H]
+  float* X;        // [B][R][H]
+  float* Hout;     // [B][R][H]
+  float* dlogits;  // [B][W][V]
+  float* q;        // [B][W][V]
+  int* dcode;      // [B][W]
+  uint32_t* dflags;  // [B][W]
+  float* tlogits;  // [B][R][V]
+  float* p;        // [B][R][V]
+  int* tcode;      // [B][R]
+  uint32_t* tflags;  // [B][R]
+};
+
+// Launchers (kernels.hip).  All asynchronous on `s`.
+hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid_x, int grid_y,
+                       hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int rows, int H, float eps,
+                               hipStream_t s);
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s);
+hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s);
+hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t s);
+hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s);
+hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s);
+hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s);
+
+}  // namespace cps

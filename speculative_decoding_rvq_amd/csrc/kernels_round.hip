@@ -1,0 +1,704 @@
+// Attention, top-k softmax + sampling, acceptance and the round control
+// kernels of CodePredictor speculative decoding.
+#include <type_traits>
+
+#include "dev_common.h"
+#include "kernels.h"
+
+namespace cps {
+
+hipError_t launch_gemv_f32(int mode, int mt, const GemvArgs& a, int gx, int gy, hipStream_t s);
+hipError_t launch_gemv_bf16(int mode, int mt, const GemvArgs& a, int gx, int gy, hipStream_t s);
+
+hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid_x, int grid_y,
+                       hipStream_t s) {
+  return wdtype == CP_SPEC_BF16 ? launch_gemv_bf16(mode, mt, a, grid_x, grid_y, s)
+                                : launch_gemv_f32(mode, mt, a, grid_x, grid_y, s);
+}
+
+// ---------------------------------------------------------------------------
+// Causal attention over the in-frame positions of one stream and one KV head.
+// The stream's K (rotated here) and V for positions 0..max row position are
+// staged in LDS; each wave takes (row, query head) pairs of the group.
+__global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int R = a.R, d = a.d, half = d / 2;
+  const int kvdim = a.nkv * d;
+  const int qdim = a.nq * d;
+  int maxp = -1;
+  for (int r = 0; r < R; ++r) maxp = max(maxp, a.pos[b * R + r]);
+  if (maxp < 0 || maxp >= a.G) return;  // positions outside the frame: no-op
+  const int np = maxp + 1;
+  float* Ks = smem;                 // [np][d]
+  float* Vs = smem + np * d;        // [np][d]
+  const float* kb = a.kv + static_cast<size_t>(b) * a.kv_sb + g * d;
+  const float* vb = kb + a.kv_vo;
+  for (int idx = threadIdx.x; idx < np * half; idx += kBlock) {
+    const int p = idx / half, i = idx % half;
+    const float k1 = kb[p * kvdim + i], k2 = kb[p * kvdim + i + half];
+    const float2 cs = a.rope[p * half + i];
+    Ks[p * d + i] = k1 * cs.x - k2 * cs.y;
+    Ks[p * d + i + half] = k2 * cs.x + k1 * cs.y;
+    Vs[p * d + i] = vb[p * kvdim + i];
+    Vs[p * d + i + half] = vb[p * kvdim + i + half];
+  }
+  __syncthreads();
+  const int group = a.nq / a.nkv;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int pair = wave; pair < R * group; pair += kBlock / kWave) {
+    const int r = pair / group, j = pair % group;
+    const int row = b * R + r;
+    const int pr = a.pos[row];
+    if (pr < 0) continue;
+    const int h = g * group + j;
+    const float* qrow = a.Q + static_cast<size_t>(row) * qdim + h * d;
+    float q1[4], q2[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = lane + kWave * c;
+      q1[c] = 0.0f;
+      q2[c] = 0.0f;
+      if (i < half) {
+        const float x1 = qrow[i], x2 = qrow[i + half];
+        const float2 cs = a.rope[pr * half + i];
+        q1[c] = x1 * cs.x - x2 * cs.y;
+        q2[c] = x2 * cs.x + x1 * cs.y;
+      }
+    }
+    // online softmax over positions 0..pr (running max and rescaled sums)
+    float mx = -INFINITY, sum = 0.0f;
+    float o1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, o2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p <= pr; ++p) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = lane + kWave * c;
+        if (i < half) dot += q1[c] * Ks[p * d + i] + q2[c] * Ks[p * d + i + half];
+      }
+      dot = wave_sum(dot) * a.scale;
+      const float mn = fmaxf(mx, dot);
+      const float corr = expf(mx - mn);
+      const float e = expf(dot - mn);
+      sum = sum * corr + e;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = lane + kWave * c;
+        if (i < half) {
+          o1[c] = o1[c] * corr + e * Vs[p * d + i];
+          o2[c] = o2[c] * corr + e * Vs[p * d + i + half];
+        }
+      }
+      mx = mn;
+    }
+    const float inv = 1.0f / sum;
+    float* orow = a.out + static_cast<size_t>(row) * qdim + h * d;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = lane + kWave * c;
+      if (i < half) {
+        orow[i] = o1[c] * inv;
+        orow[i + half] = o2[c] * inv;
+      }
+    }
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s) {
+  const size_t shm = 2 * static_cast<size_t>(a.G) * a.d * sizeof(float);
+  hipLaunchKernelGGL(attention_kernel, dim3(B, a.nkv), dim3(kBlock), shm, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void rmsnorm_rows_kernel(const float* x, float* y,
+                                                              const float* g, int H, float eps) {
+  __shared__ float red[8];
+  const float* xr = x + static_cast<size_t>(blockIdx.x) * H;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < H; i += kBlock) ss += xr[i] * xr[i];
+  const float tot = block_sum(ss, red);
+  const float rinv = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+  float* yr = y + static_cast<size_t>(blockIdx.x) * H;
+  for (int i = threadIdx.x; i < H; i += kBlock) yr[i] = xr[i] * rinv * g[i];
+}
+
+hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int rows, int H, float eps,
+                               hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(kBlock), 0, s, x, y, g, H, eps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Temperature/top-k softmax of one row of logits, and optional sampling.
+//
+// The top-k set is found by an MSB-first radix select on order-preserving
+// 32-bit keys (4 passes of 8 bits, a 256-bin LDS histogram each), which
+// yields the exact k-th largest key; entries above it are in, entries equal
+// to it are admitted in ascending code order until k are taken.  One pass
+// over the row whatever k is.  Probabilities are exp((z - max)/T) / sum on
+// the set, zero elsewhere.  Thread t owns codes [t*VPT, (t+1)*VPT).
+struct TopkSmem {
+  uint32_t hist[256];
+  int sel[2];
+  uint64_t red64[4];
+  uint32_t red32[4];
+  float redf[4];
+  int redi[8];
+  float prow[4096];
+  SampleSmem samp;
+};
+
+struct TopkResult {
+  int code;
+  uint32_t flags;
+};
+
+template <int VPT>
+__device__ TopkResult topk_row(const float* __restrict__ z, int k, float T, bool greedy,
+                               bool do_sample, float u, float* probs, TopkSmem& sm) {
+  constexpr int V = VPT * kBlock;
+  const int tid = threadIdx.x;
+  const int base = tid * VPT;
+  float zv[VPT];
+  uint32_t key[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    zv[j] = z[base + j];
+    key[j] = float_key(zv[j]);
+  }
+  TopkResult res{-1, 0u};
+  if (greedy) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const uint64_t c = (static_cast<uint64_t>(key[j]) << 32) |
+                         static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(base + j));
+      best = c > best ? c : best;
+    }
+    best = block_max_u64(best, sm.red64);
+    const int arg = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    uint32_t second = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      if (base + j != arg) second = key[j] > second ? key[j] : second;
+    second = block_max_u32(second, sm.red32);
+    res.code = arg;
+    if (V > 1) {
+      const double gap = static_cast<double>(key_float(static_cast<uint32_t>(best >> 32))) -
+                         static_cast<double>(key_float(second));
+      if (gap < kEpsGap) res.flags |= kFlagArgmax;
+    }
+    return res;
+  }
+
+  // ---- radix select of the k-th largest key ----
+  bool member[VPT];
+  if (k >= V) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) member[j] = true;
+  } else {
+    uint32_t prefix = 0, pmask = 0;
+    int rem = k;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      sm.hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if ((key[j] & pmask) == prefix) atomicAdd(&sm.hist[(key[j] >> shift) & 255u], 1u);
+      __syncthreads();
+      // thread t looks at digit 255 - t: inclusive count of digits >= it
+      const int c = static_cast<int>(sm.hist[255 - tid]);
+      int total;
+      const int excl = block_exclusive_scan(c, sm.redi, &total);
+      if (excl < rem && excl + c >= rem) {
+        sm.sel[0] = 255 - tid;
+        sm.sel[1] = rem - excl;
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(sm.sel[0]) << shift;
+      pmask |= 255u << shift;
+      rem = sm.sel[1];
+      __syncthreads();
+    }
+    const uint32_t kth = prefix;
+    // ties at the k-th key: the `rem` lowest codes among them are admitted
+    int eq = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) eq += key[j] == kth ? 1 : 0;
+    int eq_total;
+    int rank = block_exclusive_scan(eq, sm.redi, &eq_total);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      if (key[j] > kth) {
+        member[j] = true;
+      } else if (key[j] == kth) {
+        member[j] = rank < rem;
+        ++rank;
+      } else {
+        member[j] = false;
+      }
+    }
+    // boundary gap: k-th largest minus the largest logit left out
+    uint32_t out_best = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      if (!member[j]) out_best = key[j] > out_best ? key[j] : out_best;
+    out_best = block_max_u32(out_best, sm.red32);
+    const double gap = static_cast<double>(key_float(kth)) - static_cast<double>(key_float(out_best));
+    if (gap < kEpsGap) res.flags |= kFlagTopk;
+  }
+
+  // ---- softmax on the set ----
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) kmax = key[j] > kmax ? key[j] : kmax;
+  kmax = block_max_u32(kmax, sm.red32);
+  const float zmax = key_float(kmax);
+  float e[VPT];
+  float part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    e[j] = member[j] ? expf((zv[j] - zmax) / T) : 0.0f;
+    part += e[j];
+  }
+  const float Z = block_sum(part, sm.redf);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const float pj = e[j] / Z;
+    sm.prow[base + j] = pj;
+    if (probs != nullptr) probs[base + j] = pj;
+  }
+  __syncthreads();
+  if (do_sample) {
+    bool near = false;
+    res.code = block_sample([&](int i) { return sm.prow[i]; }, V, u, sm.samp, &near);
+    if (near) res.flags |= kFlagCdf;
+  }
+  return res;
+}
+
+template <typename F>
+__device__ __forceinline__ void dispatch_vpt(int V, F&& f) {
+  switch (V / kBlock) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    case 16: f(std::integral_constant<int, 16>{}); break;
+    default: break;
+  }
+}
+
+// Component: n_rows independent rows.
+__global__ __launch_bounds__(kBlock) void topk_rows_kernel(const TopkArgs a) {
+  __shared__ TopkSmem sm;
+  const int r = blockIdx.x;
+  const float* z = a.logits + static_cast<size_t>(r) * a.V;
+  float* pr = a.probs ? a.probs + static_cast<size_t>(r) * a.V : nullptr;
+  const bool samp = a.u != nullptr && !a.greedy;
+  const float u = samp ? a.u[r] : 0.0f;
+  TopkResult res{-1, 0u};
+  dispatch_vpt(a.V, [&](auto vpt) {
+    res = topk_row<decltype(vpt)::value>(z, a.k, a.T, a.greedy != 0, samp, u, pr, sm);
+  });
+  if (threadIdx.x == 0) {
+    if (a.codes) a.codes[r] = res.code;
+    if (a.flags) a.flags[r] = res.flags;
+  }
+}
+
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(a.n_rows), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Accept scan of one stream's round.  Decisions are taken by thread 0 in
+// float32 and broadcast; sampling uses the block sampler.  Callbacks give
+// the uniforms (acceptance at offset t, target draw at offset t) and, when
+// greedy, the target argmax of verify row r.  Returns the number of codes
+// committed; codes[0..n) are the committed codes; accept_near[t-1] and
+// cdf_near[t-1] report near ties at offset t.
+
+template <typename UA, typename UT, typename TA>
+__device__ int accept_scan(int gamma, const int* draft, const float* q, const float* p, int V,
+                           bool greedy, UA uacc, UT utgt, TA targmax, int* codes,
+                           uint32_t* accept_near, uint32_t* cdf_near, int* n_acc_out,
+                           SampleSmem& samp, int* dec) {
+  if (greedy) {
+    int t = 0;
+    while (t < gamma && draft[t] == targmax(t)) {
+      codes[t] = draft[t];
+      ++t;
+    }
+    codes[t] = targmax(t);
+    *n_acc_out = t;
+    return t + 1;
+  }
+  for (int t = 1; t <= gamma; ++t) {
+    const int d = draft[t - 1];
+    const bool inr = d >= 0 && d < V;
+    if (threadIdx.x == 0) {
+      const float pd = inr ? p[static_cast<size_t>(t - 1) * V + d] : 0.0f;
+      const float qd = inr ? q[static_cast<size_t>(t - 1) * V + d] : 1.0f;
+      const float ratio = pd / qd;
+      const float uu = uacc(t);
+      dec[0] = uu < ratio ? 1 : 0;
+      dec[1] = fabs(static_cast<double>(uu) - static_cast<double>(ratio)) < kEpsAccept ? 1 : 0;
+    }
+    __syncthreads();
+    const int ok = dec[0];
+    accept_near[t - 1] = dec[1];
+    __syncthreads();
+    if (ok) {
+      codes[t - 1] = d;
+      continue;
+    }
+    const float* pr = p + static_cast<size_t>(t - 1) * V;
+    const float* qr = q + static_cast<size_t>(t - 1) * V;
+    bool near = false;
+    const float ut = utgt(t);
+    int c = block_sample([&](int i) { return fmaxf(pr[i] - qr[i], 0.0f); }, V, ut, samp, &near);
+    if (c < 0) c = block_sample([&](int i) { return pr[i]; }, V, ut, samp, &near);
+    codes[t - 1] = c;
+    cdf_near[t - 1] = near ? 1u : 0u;
+    *n_acc_out = t - 1;
+    return t;
+  }
+  const float* pr = p + static_cast<size_t>(gamma) * V;
+  bool near = false;
+  codes[gamma] = block_sample([&](int i) { return pr[i]; }, V, utgt(gamma + 1), samp, &near);
+  cdf_near[gamma] = near ? 1u : 0u;
+  *n_acc_out = gamma;
+  return gamma + 1;
+}
+
+// Component accept: one block per stream, uniforms and drafts from memory.
+__global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a) {
+  __shared__ int dec[2];
+  __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
+  __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
+  __shared__ int targ[CP_SPEC_MAX_WINDOW + 1];
+  __shared__ TopkSmem tsm;
+  const int b = blockIdx.x;
+  const int W = a.W, V = a.V;
+  const int gamma = min(max(a.gamma[b], 0), W);
+  if (threadIdx.x <= CP_SPEC_MAX_WINDOW) {
+    anear[threadIdx.x] = 0;
+    cnear[threadIdx.x] = 0;
+  }
+  const float* q = a.q + static_cast<size_t>(b) * W * V;
+  const float* p = a.p + static_cast<size_t>(b) * (W + 1) * V;
+  if (a.greedy) {
+    for (int r = 0; r <= gamma; ++r) {
+      TopkResult res{-1, 0u};
+      dispatch_vpt(V, [&](auto vpt) {
+        res = topk_row<decltype(vpt)::value>(p + static_cast<size_t>(r) * V, 1, 1.0f, true, false,
+                                             0.0f, nullptr, tsm);
+      });
+      if (threadIdx.x == 0) targ[r] = res.code;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  const int* draft = a.draft + static_cast<size_t>(b) * W;
+  const float* ua = a.u_acc + static_cast<size_t>(b) * W;
+  const float* ut = a.u_tgt + static_cast<size_t>(b) * (W + 1);
+  int n_acc = 0;
+  const int n = accept_scan(
+      gamma, draft, q, p, V, a.greedy != 0, [&](int t) { return ua[t - 1]; },
+      [&](int t) { return ut[t - 1]; }, [&](int r) { return targ[r]; }, codes, anear, cnear,
+      &n_acc, tsm.samp, dec);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.n_out[b] = n;
+    for (int i = 0; i <= W; ++i) a.codes_out[static_cast<size_t>(b) * (W + 1) + i] = i < n ? codes[i] : -1;
+    if (a.flags_out) {
+      uint32_t f = 0;
+      for (int t = 1; t <= gamma + 1; ++t)
+        if (anear[t - 1] || cnear[t - 1]) f |= 1u << (t - 1);
+      a.flags_out[b] = f;
+    }
+  }
+}
+
+hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(accept_rows_kernel, dim3(a.B), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Round control.
+
+// Copy one input row into the verify rows: E_table[code] (fp32 or bf16).
+__device__ __forceinline__ void embed_row(const RoundArgs& r, int table, int code, float* dst) {
+  code = min(max(code, 0), r.V - 1);  // codes come from [0, V); never index outside
+  const size_t off = (static_cast<size_t>(table) * r.V + code) * r.H;
+  if (r.wbf16) {
+    const uint16_t* e = static_cast<const uint16_t*>(r.embed) + off;
+    for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = bf16_to_f32(e[i]);
+  } else {
+    const float* e = static_cast<const float*>(r.embed) + off;
+    for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = e[i];
+  }
+}
+
+// Prefill of frame f for stream b: rows [h_frame, E_0[c_0]] at positions 0, 1
+// and head 1 on row 1.
+__device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int f) {
+  float* x = r.X + static_cast<size_t>(b) * r.R * r.H;
+  const float* hf = c.h_frame + (static_cast<size_t>(f) * c.B + b) * r.H;
+  for (int i = threadIdx.x; i < r.H; i += kBlock) x[i] = hf[i];
+  const int c0 = c.c0[static_cast<size_t>(f) * c.B + b];
+  embed_row(r, 0, c0, x + r.H);
+  if (threadIdx.x == 0) {
+    c.out_codes[(static_cast<size_t>(f) * c.B + b) * r.G] = c0;
+    for (int i = 0; i < r.R; ++i) {
+      r.pos[b * r.R + i] = i < 2 ? i : -1;
+      r.thead[b * r.R + i] = i == 1 ? 1 : 0;
+    }
+    for (int t = 0; t < r.W; ++t) r.dhead[b * r.W + t] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, const CallDesc c) {
+  const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) {
+    *r.call = c;
+    r.call->active = c.F > 0 ? c.B : 0;
+  }
+  StreamState st{};
+  if (c.F > 0) {
+    setup_prefill(r, c, b, 0);
+    st.mode = kModePrefill;
+  } else {
+    st.mode = kModeDone;
+    if (threadIdx.x == 0) {
+      for (int i = 0; i < r.R; ++i) {
+        r.pos[b * r.R + i] = -1;
+        r.thead[b * r.R + i] = 0;
+      }
+      for (int t = 0; t < r.W; ++t) r.dhead[b * r.W + t] = 0;
+    }
+  }
+  if (threadIdx.x == 0) r.st[b] = st;
+}
+
+hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t s) {
+  hipLaunchKernelGGL(round_init_kernel, dim3(c.B), dim3(kBlock), 0, s, r, c);
+  return hipGetLastError();
+}
+
+// Draft distributions q_t and proposals d_t of every stream (block (t-1, b)),
+// plus the verify input row E_{s+t}[d_t].
+__global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
+  __shared__ TopkSmem sm;
+  const int t = blockIdx.x + 1, b = blockIdx.y;
+  const StreamState st = r.st[b];
+  if (st.mode != kModeSpec || t > st.gamma) return;
+  const uint64_t seed = r.call->seeds[static_cast<size_t>(st.f) * r.call->B + b];
+  const size_t row = static_cast<size_t>(b) * r.W + (t - 1);
+  const float u = frame_uniform(seed, st.s + t, kDraft);
+  TopkResult res{-1, 0u};
+  dispatch_vpt(r.V, [&](auto vpt) {
+    res = topk_row<decltype(vpt)::value>(r.dlogits + row * r.V, r.top_k, r.T, r.greedy != 0,
+                                         r.greedy == 0, u, r.q + row * r.V, sm);
+  });
+  if (threadIdx.x == 0) {
+    r.dcode[row] = res.code;
+    r.dflags[row] = res.flags;
+  }
+  embed_row(r, st.s + t, res.code, r.X + (static_cast<size_t>(b) * r.R + t) * r.H);
+}
+
+hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
+  if (r.W <= 0 || r.N < 2) return hipSuccess;
+  hipLaunchKernelGGL(draft_topk_kernel, dim3(r.W, r.B), dim3(kBlock), 0, s, r);
+  return hipGetLastError();
+}
+
+// Target distributions p_r of every verify row that has a head.
+__global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) {
+  __shared__ TopkSmem sm;
+  const int rr = blockIdx.x, b = blockIdx.y;
+  const size_t row = static_cast<size_t>(b) * r.R + rr;
+  if (r.thead[row] <= 0) return;
+  TopkResult res{-1, 0u};
+  dispatch_vpt(r.V, [&](auto vpt) {
+    res = topk_row<decltype(vpt)::value>(r.tlogits + row * r.V, r.top_k, r.T, r.greedy != 0, false,
+                                         0.0f, r.greedy ? nullptr : r.p + row * r.V, sm);
+  });
+  if (threadIdx.x == 0) {
+    r.tcode[row] = res.code;
+    r.tflags[row] = res.flags;
+  }
+}
+
+hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s) {
+  hipLaunchKernelGGL(target_topk_kernel, dim3(r.R, r.B), dim3(kBlock), 0, s, r);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ void count_flags(uint32_t f, long long* cnt) {
+  if (f & kFlagTopk) ++cnt[0];
+  if (f & kFlagArgmax) ++cnt[1];
+  if (f & kFlagCdf) ++cnt[2];
+  if (f & kFlagAccept) ++cnt[3];
+}
+
+// Accept, commit, truncate, and set up the stream's next round (or frame).
+__global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) {
+  __shared__ SampleSmem samp;
+  __shared__ int dec[2];
+  __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
+  __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
+  const int b = blockIdx.x;
+  StreamState st = r.st[b];
+  if (st.mode == kModeDone) return;
+  const CallDesc c = *r.call;
+  const size_t fb = static_cast<size_t>(st.f) * c.B + b;
+  const uint64_t seed = c.seeds[fb];
+  int* out = c.out_codes + fb * r.G;
+  long long nt[4] = {0, 0, 0, 0};  // topk, argmax, cdf, accept near ties
+  if (threadIdx.x <= CP_SPEC_MAX_WINDOW) {
+    anear[threadIdx.x] = 0;
+    cnear[threadIdx.x] = 0;
+  }
+  __syncthreads();
+
+  if (st.mode == kModePrefill) {
+    const size_t row = static_cast<size_t>(b) * r.R + 1;
+    int c1;
+    uint32_t f = r.tflags[row];
+    if (r.greedy) {
+      c1 = r.tcode[row];
+    } else {
+      bool near = false;
+      const float* pr = r.p + row * r.V;
+      c1 = block_sample([&](int i) { return pr[i]; }, r.V, frame_uniform(seed, 1, kTarget), samp,
+                        &near);
+      if (near) f |= kFlagCdf;
+    }
+    count_flags(f, nt);
+    if (f) st.flags |= 1u << 1;
+    if (threadIdx.x == 0) out[1] = c1;
+    const float* src = r.Hout + row * r.H;
+    float* dst = r.hstate + static_cast<size_t>(b) * r.H;
+    for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = src[i];
+    st.s = 1;
+    if (threadIdx.x == 0 && c.stats) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->prefill_passes), 1ull);
+  } else {
+    const int s = st.s, gamma = st.gamma;
+    for (int t = 1; t <= gamma; ++t) {
+      const uint32_t f = r.dflags[static_cast<size_t>(b) * r.W + t - 1];
+      count_flags(f, nt);
+      if (f) st.flags |= 1u << (s + t);
+    }
+    for (int rr = 0; rr <= gamma; ++rr) {
+      const uint32_t f = r.tflags[static_cast<size_t>(b) * r.R + rr];
+      count_flags(f, nt);
+      if (f) st.flags |= 1u << (s + 1 + rr);
+    }
+    const int* draft = r.dcode + static_cast<size_t>(b) * r.W;
+    const float* q = r.q + static_cast<size_t>(b) * r.W * r.V;
+    const float* p = r.p + static_cast<size_t>(b) * r.R * r.V;
+    const int* tc = r.tcode + static_cast<size_t>(b) * r.R;
+    int n_acc = 0;
+    const int n = accept_scan(
+        gamma, draft, q, p, r.V, r.greedy != 0,
+        [&](int t) { return frame_uniform(seed, s + t, kAccept); },
+        [&](int t) { return frame_uniform(seed, s + t, kTarget); }, [&](int rr) { return tc[rr]; },
+        codes, anear, cnear, &n_acc, samp, dec);
+    __syncthreads();
+    for (int t = 1; t <= n; ++t) {
+      if (anear[t - 1]) {
+        ++nt[3];
+        st.flags |= 1u << (s + t);
+      }
+      if (cnear[t - 1]) {
+        ++nt[2];
+        st.flags |= 1u << (s + t);
+      }
+    }
+    if (threadIdx.x == 0) {
+      for (int t = 0; t < n; ++t) out[s + 1 + t] = codes[t];
+      if (c.stats) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->rounds), 1ull);
+        for (int t = 1; t <= gamma; ++t) {
+          atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->proposed[t - 1]), 1ull);
+          if (t <= n_acc) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->accepted[t - 1]), 1ull);
+        }
+        if (n_acc == gamma) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->bonus), 1ull);
+      }
+    }
+    const float* src = r.Hout + (static_cast<size_t>(b) * r.R + (n - 1)) * r.H;
+    float* dst = r.hstate + static_cast<size_t>(b) * r.H;
+    for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = src[i];
+    st.s = s + n;
+  }
+  if (threadIdx.x == 0 && c.stats) {
+    if (nt[0]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_topk), static_cast<unsigned long long>(nt[0]));
+    if (nt[1]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_argmax), static_cast<unsigned long long>(nt[1]));
+    if (nt[2]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_cdf), static_cast<unsigned long long>(nt[2]));
+    if (nt[3]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_accept), static_cast<unsigned long long>(nt[3]));
+  }
+  __syncthreads();
+
+  // ---- next round of this stream ----
+  if (st.s >= r.G - 1) {
+    if (threadIdx.x == 0) {
+      if (c.out_flags) c.out_flags[fb] = st.flags;
+      if (c.stats) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->frames), 1ull);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->codes), static_cast<unsigned long long>(r.G - 1));
+      }
+    }
+    st.f += 1;
+    st.s = 0;
+    st.flags = 0;
+    st.gamma = 0;
+    if (st.f >= c.F) {
+      st.mode = kModeDone;
+      if (threadIdx.x == 0) {
+        atomicSub(&r.call->active, 1);
+        for (int i = 0; i < r.R; ++i) {
+          r.pos[b * r.R + i] = -1;
+          r.thead[b * r.R + i] = 0;
+        }
+        for (int t = 0; t < r.W; ++t) r.dhead[b * r.W + t] = 0;
+      }
+    } else {
+      st.mode = kModePrefill;
+      setup_prefill(r, c, b, st.f);
+    }
+  } else {
+    const int s = st.s;
+    const int gamma = r.N == 0 ? 0 : min(r.N - 1, r.G - 2 - s);
+    st.gamma = gamma;
+    st.mode = kModeSpec;
+    const int cs = out[s];
+    __syncthreads();
+    embed_row(r, s, cs, r.X + static_cast<size_t>(b) * r.R * r.H);
+    if (threadIdx.x == 0) {
+      for (int i = 0; i < r.R; ++i) {
+        r.pos[b * r.R + i] = i <= gamma ? s + 1 + i : -1;
+        r.thead[b * r.R + i] = i <= gamma ? s + 1 + i : 0;
+      }
+      for (int t = 1; t <= r.W; ++t) r.dhead[b * r.W + t - 1] = t <= gamma ? s + t : 0;
+    }
+  }
+  if (threadIdx.x == 0) r.st[b] = st;
+}
+
+hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s) {
+  hipLaunchKernelGGL(round_accept_kernel, dim3(r.B), dim3(kBlock), 0, s, r);
+  return hipGetLastError();
+}
+
+}  // namespace cps

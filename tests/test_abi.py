@@ -1,0 +1,97 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and its validation returns the documented codes (no GPU needed:
+nothing here reaches a HIP call)."""
+import ctypes as C
+
+import pytest
+
+import synth
+from speculative_decoding_rvq_amd import binding
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_every_header_symbol_is_exported(L):
+    syms = binding.header_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(binding._SIGS)
+
+
+def test_workspace_sizes():
+    for cid in (1, 2, 3, 4, 5):
+        n = binding.workspace_bytes(binding.make_cfg(synth.config(cid)))
+        assert n > 0 and n % 256 == 0, cid
+    n1 = binding.workspace_bytes(binding.make_cfg(synth.config(4),
+                                                  max_streams=1))
+    n64 = binding.workspace_bytes(binding.make_cfg(synth.config(4)))
+    assert n64 > n1
+
+
+def _create(cfg):
+    h = C.c_void_p()
+    w = binding.Weights(1, 1, 1, C.cast((C.c_void_p * 18)(*([1] * 18)),
+                                        C.POINTER(C.c_void_p)))
+    rc = binding.lib().cp_spec_create(C.byref(w), C.byref(cfg), None, 0,
+                                      C.byref(h))
+    return rc, binding.last_error()
+
+
+@pytest.mark.parametrize("field,value,code,msg", [
+    ("verify_size", 1, binding.EINVAL, "no draft slot"),
+    ("verify_size", 9, binding.EINVAL, "0 (off) or 2..8"),
+    ("verify_size", -1, binding.EINVAL, "0 (off) or 2..8"),
+    ("vocab", 8192, binding.EUNSUPPORTED, "small-vocabulary"),
+    ("vocab", 300, binding.EUNSUPPORTED, "256 * 2^i"),
+    ("top_k", 0, binding.EINVAL, "top_k"),
+    ("top_k", 257, binding.EINVAL, "top_k"),
+    ("temperature", 0.0, binding.EINVAL, "temperature"),
+    ("q_heads", 3, binding.EINVAL, "multiple of kv_heads"),
+    ("code_groups", 1, binding.EINVAL, "code_groups"),
+    ("code_groups", 33, binding.EUNSUPPORTED, "code_groups"),
+    ("hidden", 100, binding.EUNSUPPORTED, "not tileable"),
+    ("max_streams", 0, binding.EINVAL, "non-positive"),
+    ("head_dim", 256, binding.EUNSUPPORTED, "head_dim"),
+])
+def test_create_validation(field, value, code, msg):
+    cfg = binding.make_cfg(synth.config(1))
+    setattr(cfg, field, value)
+    rc, err = _create(cfg)
+    assert rc == code and msg in err, (rc, err)
+    assert binding.lib().cp_spec_workspace_bytes(C.byref(cfg)) == 0
+
+
+def test_greedy_ignores_sampling_fields():
+    cfg = binding.make_cfg(synth.config(3))
+    cfg.top_k = 0
+    cfg.temperature = 0.0
+    assert binding.workspace_bytes(cfg) > 0
+
+
+def test_workspace_checks_before_any_device_work():
+    cfg = binding.make_cfg(synth.config(1))
+    rc, err = _create(cfg)                     # null workspace
+    assert rc == binding.EWORKSPACE and "workspace" in err
+    h = C.c_void_p()
+    w = binding.Weights(1, 1, 1, C.cast((C.c_void_p * 18)(*([1] * 18)),
+                                        C.POINTER(C.c_void_p)))
+    n = binding.workspace_bytes(cfg)
+    rc = binding.lib().cp_spec_create(C.byref(w), C.byref(cfg),
+                                      C.c_void_p(0x1000 + 3), n, C.byref(h))
+    assert rc == binding.EWORKSPACE and "aligned" in binding.last_error()
+    rc = binding.lib().cp_spec_create(C.byref(w), C.byref(cfg),
+                                      C.c_void_p(0x1000), n - 1, C.byref(h))
+    assert rc == binding.EWORKSPACE
+
+
+def test_null_handle_calls_are_rejected():
+    Lb = binding.lib()
+    assert Lb.cp_spec_decode_frames(None, None, 1, 1, None, None, None, None,
+                                    None, None) == binding.EINVAL
+    assert Lb.cp_spec_topk_sample(None, None, 1, None, None, None, None,
+                                  None) == binding.EINVAL
+    Lb.cp_spec_destroy(None)

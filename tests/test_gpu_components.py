@@ -1,0 +1,256 @@
+"""GPU parity of each step of the round, through the C ABI, against the oracle.
+
+* stacked-head logits: rel 1e-3 / abs 2e-3 (same bf16 weights, fp32 sums);
+* top-k softmax: identical support (unless the boundary is a flagged near
+  tie), probabilities to float32 rounding; sampling bit-exact against the
+  oracle's inverse CDF fed the GPU's own float32 probabilities;
+* accept scan: bit-exact codes, counts and flags on fed p, q and uniforms;
+* decoder pass: ragged multi-stream blocks, transactional truncation.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import device_weights, handle, log, oracle_model, weights
+from oracle import decoder as odec
+from oracle import distributions as odist
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _t(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a)
+    return (t if dtype is None else t.to(dtype)).cuda()
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+@pytest.mark.parametrize("norm", [0, 1])
+def test_head_logits(cid, norm):
+    log(f"head_logits cfg{cid} norm={norm}")
+    c = synth.config(cid)
+    m = oracle_model(cid)
+    h = handle(cid, max_streams=2)
+    rng = np.random.default_rng(10 + cid)
+    rows = 2 * max(c["verify_size"], 2)
+    x = rng.standard_normal((rows, c["hidden"])).astype(np.float32)
+    heads = rng.integers(1, c["groups"], size=rows).astype(np.int32)
+    heads[1] = 0                                   # a skipped row
+    out = torch.full((rows, c["vocab"]), 123.0, device="cuda")
+    h.head_logits(_t(x), _t(heads), norm, out)
+    got = out.cpu().numpy()
+    for r in range(rows):
+        if heads[r] == 0:
+            assert np.all(got[r] == 123.0)
+            continue
+        xr = x[r].astype(np.float64)
+        if norm:
+            xr = odec.rmsnorm(xr, m.final_norm, m.eps)
+        ref = m.logits(int(heads[r]), xr)
+        np.testing.assert_allclose(got[r], ref, rtol=1e-3, atol=2e-3)
+        # the achieved error is far inside the stated tolerance
+        assert np.max(np.abs(got[r] - ref)) < 1e-4
+
+
+def _logit_rows(V, n, rng, ties=False):
+    z = (rng.standard_normal((n, V)) * 0.4).astype(np.float32)
+    if ties:
+        # exact ties straddling the top-k boundary and the maximum
+        for r in range(n):
+            order = np.argsort(-z[r])
+            z[r, order[45:55]] = z[r, order[49]]
+            z[r, order[1]] = z[r, order[0]]
+    return z
+
+
+@pytest.mark.parametrize("cid,over", [
+    (1, {}), (2, {}), (5, {}),
+    (1, {"top_k": 256}),                  # k = V: full softmax
+    (2, {"top_k": 1}),                    # k = 1: a point mass
+    (2, {"temperature": 1.7, "top_k": 333}),
+])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_sample(cid, over, ties):
+    log(f"topk_sample cfg{cid} {over} ties={ties}")
+    c = synth.config(cid)
+    h = handle(cid, max_streams=1, **over)
+    k = h.cfg.top_k
+    T = h.cfg.temperature
+    V = c["vocab"]
+    rng = np.random.default_rng(20 + cid + k)
+    n = 24
+    z = _logit_rows(V, n, rng, ties)
+    u = (rng.integers(0, 2**24, size=n) / 2**24).astype(np.float32)
+    u[0], u[1] = 0.0, 1 - 2**-24
+    probs = torch.zeros((n, V), device="cuda")
+    codes = torch.zeros(n, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda")
+    h.topk_sample(_t(z), _t(u), probs, codes, flags)
+    P = probs.cpu().numpy()
+    C = codes.cpu().numpy()
+    Fl = flags.cpu().numpy().view(np.uint32)
+    for r in range(n):
+        ref, ftopk = odist.topk_softmax(z[r], T, k)
+        assert bool(Fl[r] & 1) == (ftopk and k < V), r
+        if not ftopk:
+            assert np.array_equal(P[r] > 0, ref > 0), r
+        np.testing.assert_allclose(P[r], ref, rtol=3e-6, atol=1e-8)
+        # sampling: bit-exact on the same float32 probabilities
+        code, fcdf = odist.sample(P[r], u[r])
+        assert C[r] == code, (r, C[r], code)
+        assert bool(Fl[r] & 4) == fcdf
+
+
+@pytest.mark.parametrize("cid", [1, 5])
+def test_topk_greedy_argmax(cid):
+    log(f"greedy argmax cfg{cid}")
+    c = synth.config(cid)
+    h = handle(cid, max_streams=1, greedy=1)
+    rng = np.random.default_rng(30)
+    z = _logit_rows(c["vocab"], 16, rng, ties=True)
+    z[3, :] = 0.25                                 # all equal: id 0 wins
+    z[4, 7] = z[4].max() + 5e-5                    # near tie
+    codes = torch.zeros(16, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(16, dtype=torch.int32, device="cuda")
+    h.topk_sample(_t(z), None, None, codes, flags)
+    C = codes.cpu().numpy()
+    Fl = flags.cpu().numpy().view(np.uint32)
+    for r in range(16):
+        ref, near = odist.argmax_with_gap(z[r])
+        assert C[r] == ref and bool(Fl[r] & 2) == near
+
+
+def _dist_rows(V, n, k, rng, T=0.9):
+    out = []
+    for _ in range(n):
+        z = (rng.standard_normal(V) * 0.8).astype(np.float32)
+        out.append(odist.topk_softmax(z, T, k)[0])
+    return np.array(out, dtype=np.float32)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 5])
+def test_accept_bit_exact(cid):
+    log(f"accept cfg{cid}")
+    c = synth.config(cid)
+    V, k = c["vocab"], c["top_k"]
+    W = 3
+    B = 64
+    h = handle(cid, max_streams=B)
+    rng = np.random.default_rng(40 + cid)
+    gamma = rng.integers(0, W + 1, size=B).astype(np.int32)
+    q = _dist_rows(V, B * W, k, rng).reshape(B, W, V)
+    p = _dist_rows(V, B * (W + 1), k, rng).reshape(B, W + 1, V)
+    # special streams: p == q (accept all), disjoint supports (reject all),
+    # draft outside p's support (p(d) = 0), and an exact ratio tie
+    p[0, :W] = q[0]
+    gamma[0] = W
+    q[1] = 0
+    q[1, :, :3] = np.float32(1 / 3)
+    p[1, :, :3] = 0
+    gamma[1] = W
+    draft = np.zeros((B, W), np.int32)
+    for b in range(B):
+        for t in range(W):
+            draft[b, t] = odist.sample(q[b, t], rng.random())[0]
+    ua = (rng.integers(0, 2**24, size=(B, W)) / 2**24).astype(np.float32)
+    ut = (rng.integers(0, 2**24, size=(B, W + 1)) / 2**24).astype(np.float32)
+    d2 = draft[2, 0]
+    ua[2, 0] = np.float32(p[2, 0, d2] / q[2, 0, d2]) if p[2, 0, d2] > 0 else 0
+    gamma[2] = max(gamma[2], 1)
+    n_out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    codes = torch.zeros((B, W + 1), dtype=torch.int32, device="cuda")
+    flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+    h.accept(_t(gamma), _t(draft), _t(q), _t(p), _t(ua), _t(ut), n_out, codes,
+             flags)
+    N = n_out.cpu().numpy()
+    Cd = codes.cpu().numpy()
+    Fl = flags.cpu().numpy().view(np.uint32)
+    for b in range(B):
+        g = int(gamma[b])
+        em, n_acc, near = odist.accept_scan(
+            list(draft[b, :g]), list(q[b, :g]), list(p[b, :g + 1]),
+            lambda t: ua[b, t - 1], lambda t: ut[b, t - 1])
+        assert N[b] == len(em), b
+        assert list(Cd[b, :N[b]]) == em, b
+        assert np.all(Cd[b, N[b]:] == -1)
+        want = 0
+        for t, _ in near:
+            want |= 1 << (t - 1)
+        assert Fl[b] == want, (b, Fl[b], want)
+    assert N[0] == W + 1                      # p == q: everything accepted
+    assert N[1] == 1                          # disjoint: first draft rejected
+
+
+def test_accept_greedy():
+    log("accept greedy")
+    c = synth.config(1)
+    V, W, B = c["vocab"], 4, 16
+    h = handle(3, max_streams=B, verify_size=5)
+    rng = np.random.default_rng(50)
+    logits = (rng.standard_normal((B, W + 1, V)) * 0.4).astype(np.float32)
+    amax = logits.argmax(-1)
+    gamma = rng.integers(0, W + 1, size=B).astype(np.int32)
+    draft = amax[:, :W].copy().astype(np.int32)
+    for b in range(B):                         # a mismatch at a random offset
+        t = rng.integers(0, W + 1)
+        if t < W:
+            draft[b, t] = (draft[b, t] + 1) % V
+    n_out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    codes = torch.zeros((B, W + 1), dtype=torch.int32, device="cuda")
+    h.accept(_t(gamma), _t(draft), None, _t(logits), None, None, n_out, codes)
+    N = n_out.cpu().numpy()
+    Cd = codes.cpu().numpy()
+    for b in range(B):
+        g = int(gamma[b])
+        rnd = odist.verify_greedy(tuple(draft[b, :g]), tuple(amax[b, :g + 1]))
+        assert tuple(Cd[b, :N[b]]) == rnd.emitted
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_decoder_ragged_blocks_and_truncation(cid):
+    """A prefill block, a ragged verify block, then a block that overwrites
+    rejected positions after truncation, for three streams."""
+    log(f"decoder_forward cfg{cid}")
+    c = synth.config(cid)
+    m = oracle_model(cid)
+    B = 3
+    R = max(c["verify_size"], 2)
+    h = handle(cid, max_streams=B)
+    L, G, nkv, d, H = c["layers"], c["groups"], c["kv_heads"], c["head_dim"], \
+        c["hidden"]
+    kv = torch.zeros((B, L, 2, G, nkv, d), device="cuda")
+    okv = [m.new_kv() for _ in range(B)]
+    rng = np.random.default_rng(60 + cid)
+
+    def emb(j):
+        return m.embed_row(j % G, int(rng.integers(0, c["vocab"])))
+
+    def step(pos_rows, trunc=None):
+        if trunc is not None:
+            for b in range(B):
+                okv[b].truncate(trunc[b])
+        x = np.zeros((B, R, H), np.float32)
+        pos = np.full((B, R), -1, np.int32)
+        for b, plist in enumerate(pos_rows):
+            for r, p_ in enumerate(plist):
+                x[b, r] = rng.standard_normal(H) if p_ == 0 else emb(p_ - 1)
+                pos[b, r] = p_
+        xt = _t(x)
+        h.decoder_forward(xt, _t(pos), kv)
+        got = xt.cpu().numpy()
+        for b, plist in enumerate(pos_rows):
+            if not plist:
+                continue
+            ref = m.forward_rows([x[b, r].astype(np.float64)
+                                  for r in range(len(plist))], plist, okv[b])
+            for r in range(len(plist)):
+                np.testing.assert_allclose(got[b, r], ref[r], rtol=1e-3,
+                                           atol=2e-3)
+                assert np.max(np.abs(got[b, r] - ref[r])) < 1e-4
+
+    step([[0, 1], [0, 1], [0, 1]])
+    step([list(range(2, 2 + R)), [2, 3], [2]])
+    # stream 0 keeps positions 0..3, stream 1 keeps 0..3, stream 2 keeps 0..2
+    step([[4, 5], list(range(4, 4 + R)), [3]], trunc=[4, 4, 3])

@@ -30,7 +30,36 @@ def _inputs(c, torch, np):
             torch.from_numpy(seeds.view(np.int64)).cuda(), hf, c0, seeds)
 
 
-def run_workload(cid, steps, warmup, verify_size=None, frames=None):
+def kernel_table(h, c, B, iters=200):
+    """Live per-kernel timing (HIP events on the decode stream) of every
+    kernel kind of the round, in its decode launch configuration."""
+    from speculative_decoding_rvq_amd import binding
+    per_round = {"draft_heads": 1, "target_heads": 1}
+    out = {}
+    for kind in binding.KERNEL_KINDS:
+        if kind == "draft_heads" and c["verify_size"] < 2:
+            continue
+        t = h.time_kernel(kind, B, iters)
+        t["launches_per_round"] = per_round.get(kind, c["layers"])
+        t["us_per_round"] = t["avg_us"] * t["launches_per_round"]
+        t["achieved_GBps"] = t["bytes_per_launch"] / (t["avg_us"] * 1e3)
+        t["achieved_TFLOPs"] = t["flops_per_launch"] / (t["avg_us"] * 1e6)
+        out[kind] = t
+    return out
+
+
+def roofline(table):
+    """Roofline object of the kernel with the largest share of a round."""
+    kind = max(table, key=lambda k: table[k]["us_per_round"])
+    t = table[kind]
+    return {"bound": "hbm", "kernel": kind, "achieved": t["achieved_GBps"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": t["achieved_GBps"] / HBM_PEAK_GBS, "traffic": None,
+            "avg_us": t["avg_us"], "bytes_per_launch": t["bytes_per_launch"]}
+
+
+def run_workload(cid, steps, warmup, verify_size=None, frames=None,
+                 kernels=False):
     import numpy as np
     import torch
 
@@ -67,7 +96,7 @@ def run_workload(cid, steps, warmup, verify_size=None, frames=None):
     s = binding.get_stats(st)
     codes = F * B * (G - 1)
     res = {
-        "config": cid, "name": c["name"], "streams": B, "frames": F,
+        "workload": cid, "name": c["name"], "streams": B, "frames": F,
         "verify_size": c["verify_size"], "ms_per_step": ms,
         "wall_ms_per_step": 1e3 * wall / steps,
         "codes_per_s": codes / (ms / 1e3),
@@ -78,6 +107,9 @@ def run_workload(cid, steps, warmup, verify_size=None, frames=None):
         "acceptance_by_offset": [a / p for a, p in zip(s["accepted"], s["proposed"]) if p],
         "stats": s,
     }
+    if kernels:
+        torch.cuda.synchronize()
+        res["kernels"] = kernel_table(h, c, B)
     h.close()
     del wdev
     torch.cuda.empty_cache()
@@ -125,7 +157,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3tts",
+                    help="one of synth.WORKLOADS")
     ap.add_argument("--frames", type=int, default=None)
     ap.add_argument("--cpu-frames", type=int, default=24)
     ap.add_argument("--no-extra", action="store_true",
@@ -139,8 +172,8 @@ def main():
     import torch
     torch.cuda.set_device(0)
 
-    main_res, c = run_workload(args.config, args.steps, args.warmup,
-                               frames=args.frames)
+    main_res, c = run_workload(args.workload, args.steps, args.warmup,
+                               frames=args.frames, kernels=True)
     line = {
         "metric": METRIC,
         "value": main_res["codes_per_s"],
@@ -155,7 +188,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{c['name']} (config {args.config}): {c['streams']} "
+            "workload": f"{c['name']}: {c['streams']} "
                         f"stream(s) x {c['frames']} frames, G{c['groups']} "
                         f"V{c['vocab']} H{c['hidden']} L{c['layers']}, "
                         f"N={c['verify_size']}, T={c['temperature']}, "
@@ -168,18 +201,23 @@ def main():
         "frames_per_s": main_res["frames_per_s"],
         "realtime_factor_vs_12.5fps": main_res["frames_per_s_per_stream"] / REALTIME_FPS,
         "acceptance_by_offset": main_res["acceptance_by_offset"],
+        "roofline": roofline(main_res["kernels"]),
+        "kernels": {k: {kk: round(v, 3) if isinstance(v, float) else v
+                        for kk, v in t.items()}
+                    for k, t in main_res["kernels"].items()},
     }
     if not args.no_extra:
-        ar, _ = run_workload(args.config, 1, 1, verify_size=0, frames=args.frames)
+        ar, _ = run_workload(args.workload, 1, 1, verify_size=0, frames=args.frames)
         line["ar_baseline"] = {"codes_per_s": ar["codes_per_s"],
                                "ms_per_step": ar["ms_per_step"],
                                "speedup": main_res["codes_per_s"] / ar["codes_per_s"]}
-        s64, _ = run_workload(4, 1, 1)
+        s64, _ = run_workload("tiny-64", 1, 1, kernels=True)
         line["streams64"] = {k: s64[k] for k in (
             "codes_per_s", "frames_per_s", "ms_per_step",
             "codes_per_verify_pass", "codes_per_decoder_pass",
             "acceptance_by_offset")}
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_frames)
+        line["streams64"]["roofline"] = roofline(s64["kernels"])
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 
 

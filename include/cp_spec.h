@@ -209,6 +209,36 @@ int cp_spec_decoder_forward(cp_spec* h, void* stream, int32_t n_streams,
                             int32_t rows_per_stream, float* d_x,
                             const int32_t* d_pos, float* d_kv);
 
+/* ---- measurement --------------------------------------------------------
+ * Kernel kinds of the round, for cp_spec_time_kernel. */
+#define CP_SPEC_KERNEL_DRAFT_HEADS 0  /* stacked-head draft GEMV            */
+#define CP_SPEC_KERNEL_QKV 1          /* RMSNorm + Q/K/V GEMV + KV append   */
+#define CP_SPEC_KERNEL_ATTENTION 2    /* in-frame causal attention          */
+#define CP_SPEC_KERNEL_O_PROJ 3       /* output projection + residual       */
+#define CP_SPEC_KERNEL_GATE_UP 4      /* RMSNorm + gate/up GEMV + SwiGLU    */
+#define CP_SPEC_KERNEL_DOWN 5         /* down projection + residual         */
+#define CP_SPEC_KERNEL_TARGET_HEADS 6 /* final RMSNorm + per-row heads      */
+#define CP_SPEC_KERNEL_KINDS 7
+
+typedef struct cp_spec_kernel_timing {
+  double avg_us;           /* mean device time per launch                   */
+  double bytes_per_launch; /* algorithmic bytes: weights read once plus the */
+                           /* activation rows read and written              */
+  double flops_per_launch; /* 2 * rows * weight elements                    */
+  int32_t launches;
+  int32_t rows;            /* activation rows per launch                    */
+} cp_spec_kernel_timing;
+
+/* Time one kernel of the round in its decode launch configuration for
+ * n_streams streams: `iters` back-to-back launches between two HIP events
+ * recorded on `stream`, cycling through the layers (or through distinct
+ * heads) so consecutive launches read different weights.  Rows sit at
+ * mid-frame positions with one distinct head each.  Overwrites the handle's
+ * workspace (decode state included); synchronises `stream`. */
+int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams,
+                        int32_t kind, int32_t iters,
+                        cp_spec_kernel_timing* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,15 @@ class Stats(C.Structure):
 
 STATS_WORDS = C.sizeof(Stats) // 8
 
+KERNEL_KINDS = ("draft_heads", "qkv", "attention", "o_proj", "gate_up",
+                "down", "target_heads")
+
+
+class KernelTiming(C.Structure):
+    _fields_ = [("avg_us", C.c_double), ("bytes_per_launch", C.c_double),
+                ("flops_per_launch", C.c_double), ("launches", C.c_int32),
+                ("rows", C.c_int32)]
+
 _P = C.c_void_p
 _SIGS = {
     "cp_spec_workspace_bytes": (C.c_size_t, [C.POINTER(Cfg)]),
@@ -76,6 +85,8 @@ _SIGS = {
                                  _P, _P, _P, _P, _P]),
     "cp_spec_decoder_forward": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P,
                                           _P, _P]),
+    "cp_spec_time_kernel": (C.c_int, [_P, _P, C.c_int32, C.c_int32,
+                                      C.c_int32, C.POINTER(KernelTiming)]),
 }
 
 _lib = None
@@ -230,6 +241,17 @@ class Handle:
             self.h, _stream(stream), B, W, _ptr(gamma), _ptr(draft), _ptr(q),
             _ptr(p), _ptr(u_accept), _ptr(u_target), _ptr(n_out),
             _ptr(codes_out), _ptr(flags_out)))
+
+    def time_kernel(self, kind: str, n_streams: int, iters: int,
+                    stream=None) -> dict:
+        out = KernelTiming()
+        _check(lib().cp_spec_time_kernel(
+            self.h, _stream(stream), n_streams, KERNEL_KINDS.index(kind),
+            iters, C.byref(out)))
+        return {"kind": kind, "avg_us": out.avg_us,
+                "bytes_per_launch": out.bytes_per_launch,
+                "flops_per_launch": out.flops_per_launch,
+                "launches": out.launches, "rows": out.rows}
 
     def decoder_forward(self, x, pos, kv, stream=None):
         B, R = int(pos.shape[0]), int(pos.shape[1])

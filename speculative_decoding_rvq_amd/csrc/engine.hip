@@ -206,50 +206,63 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
   return CP_SPEC_OK;
 }
 
-// All decoder layers over B*R rows of X at positions `pos`, cache `kv`.
-int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const int* pos, float* kv) {
+// One decoder kernel of layer l over B*R rows of X at positions `pos`.
+int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R, float* X,
+                 const int* pos, float* kv) {
   const Shape& sh = h->sh;
   const int M = B * R;
   float* Q = h->at<float>(h->lo.Q);
   float* attn = h->at<float>(h->lo.attn);
   float* act = h->at<float>(h->lo.act);
-  const long long layer_kv = 2LL * sh.G * sh.kvdim;
-  for (int l = 0; l < sh.L; ++l) {
-    const auto& w = h->layers[l];
-    float* kvl = kv + l * layer_kv;
-    GemvArgs a{};
-    a.W0 = w[1]; a.W1 = w[2]; a.W2 = w[3];
-    a.N = sh.qdim + 2 * sh.kvdim; a.K = sh.H;
-    a.X = X; a.ldx = sh.H; a.xdiv = 1; a.M = M;
-    a.norm_g = static_cast<const float*>(w[0]); a.eps = sh.eps;
-    a.Y = Q; a.ldy = sh.qdim;
-    a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
-    a.kv_vo = static_cast<long long>(sh.G) * sh.kvdim; a.rows_per_stream = R; a.pos = pos;
-    a.kv_positions = sh.G;
-    int rc = gemv(h, s, kQKV, a);
-    if (rc) return rc;
-
-    AttnArgs at{};
-    at.Q = Q; at.out = attn; at.kv = kvl; at.kv_sb = h->kv_sb(); at.kv_vo = a.kv_vo; at.pos = pos;
-    at.rope = h->at<float2>(h->lo.rope); at.R = R; at.nq = sh.nq; at.nkv = sh.nkv; at.d = sh.d;
-    at.G = sh.G; at.scale = 1.0f / std::sqrt(static_cast<float>(sh.d));
-    CPS_HIP(launch_attention(at, B, s));
-
-    GemvArgs o{};
-    o.W0 = w[4]; o.N = sh.H; o.K = sh.qdim; o.X = attn; o.ldx = sh.qdim; o.xdiv = 1; o.M = M;
-    o.Y = X; o.ldy = sh.H;
-    if ((rc = gemv(h, s, kAdd, o))) return rc;
-
-    GemvArgs g{};
-    g.W0 = w[6]; g.W1 = w[7]; g.N = sh.F; g.K = sh.H; g.X = X; g.ldx = sh.H; g.xdiv = 1; g.M = M;
-    g.norm_g = static_cast<const float*>(w[5]); g.eps = sh.eps; g.Y = act; g.ldy = sh.F;
-    if ((rc = gemv(h, s, kSwiGLU, g))) return rc;
-
-    GemvArgs dn{};
-    dn.W0 = w[8]; dn.N = sh.H; dn.K = sh.F; dn.X = act; dn.ldx = sh.F; dn.xdiv = 1; dn.M = M;
-    dn.Y = X; dn.ldy = sh.H;
-    if ((rc = gemv(h, s, kAdd, dn))) return rc;
+  const auto& w = h->layers[l];
+  float* kvl = kv + l * 2LL * sh.G * sh.kvdim;
+  const long long kv_vo = static_cast<long long>(sh.G) * sh.kvdim;
+  GemvArgs a{};
+  a.xdiv = 1;
+  a.M = M;
+  a.eps = sh.eps;
+  switch (kind) {
+    case CP_SPEC_KERNEL_QKV:
+      a.W0 = w[1]; a.W1 = w[2]; a.W2 = w[3];
+      a.N = sh.qdim + 2 * sh.kvdim; a.K = sh.H;
+      a.X = X; a.ldx = sh.H; a.norm_g = static_cast<const float*>(w[0]);
+      a.Y = Q; a.ldy = sh.qdim;
+      a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
+      a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.G;
+      return gemv(h, s, kQKV, a);
+    case CP_SPEC_KERNEL_ATTENTION: {
+      AttnArgs at{};
+      at.Q = Q; at.out = attn; at.kv = kvl; at.kv_sb = h->kv_sb(); at.kv_vo = kv_vo; at.pos = pos;
+      at.rope = h->at<float2>(h->lo.rope); at.R = R; at.nq = sh.nq; at.nkv = sh.nkv; at.d = sh.d;
+      at.G = sh.G; at.scale = 1.0f / std::sqrt(static_cast<float>(sh.d));
+      CPS_HIP(launch_attention(at, B, s));
+      return CP_SPEC_OK;
+    }
+    case CP_SPEC_KERNEL_O_PROJ:
+      a.W0 = w[4]; a.N = sh.H; a.K = sh.qdim; a.X = attn; a.ldx = sh.qdim; a.Y = X; a.ldy = sh.H;
+      return gemv(h, s, kAdd, a);
+    case CP_SPEC_KERNEL_GATE_UP:
+      a.W0 = w[6]; a.W1 = w[7]; a.N = sh.F; a.K = sh.H; a.X = X; a.ldx = sh.H;
+      a.norm_g = static_cast<const float*>(w[5]); a.Y = act; a.ldy = sh.F;
+      return gemv(h, s, kSwiGLU, a);
+    case CP_SPEC_KERNEL_DOWN:
+      a.W0 = w[8]; a.N = sh.H; a.K = sh.F; a.X = act; a.ldx = sh.F; a.Y = X; a.ldy = sh.H;
+      return gemv(h, s, kAdd, a);
+    default:
+      return fail(CP_SPEC_EINVAL, "not a decoder kernel kind");
   }
+}
+
+const int kLayerKinds[5] = {CP_SPEC_KERNEL_QKV, CP_SPEC_KERNEL_ATTENTION, CP_SPEC_KERNEL_O_PROJ,
+                            CP_SPEC_KERNEL_GATE_UP, CP_SPEC_KERNEL_DOWN};
+
+// All decoder layers over B*R rows of X at positions `pos`, cache `kv`.
+int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const int* pos, float* kv) {
+  for (int l = 0; l < h->sh.L; ++l)
+    for (int kind : kLayerKinds) {
+      const int rc = layer_kernel(h, s, kind, l, B, R, X, pos, kv);
+      if (rc) return rc;
+    }
   return CP_SPEC_OK;
 }
 
@@ -494,6 +507,103 @@ int cp_spec_decoder_forward(cp_spec* h, void* stream, int32_t n_streams, int32_t
   const int rc = run_layers(h, s, n_streams, rows_per_stream, d_x, d_pos, d_kv);
   if (rc) return rc;
   CPS_HIP(launch_rmsnorm_rows(d_x, d_x, h->fnorm, n_streams * rows_per_stream, h->sh.H, h->sh.eps, s));
+  return CP_SPEC_OK;
+}
+
+int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kind, int32_t iters,
+                        cp_spec_kernel_timing* out) {
+  if (!h || !out) return fail(CP_SPEC_EINVAL, "null pointer");
+  if (n_streams < 1 || n_streams > h->sh.maxB) return fail(CP_SPEC_EINVAL, "n_streams out of range");
+  if (kind < 0 || kind >= CP_SPEC_KERNEL_KINDS) return fail(CP_SPEC_EINVAL, "unknown kernel kind");
+  if (iters < 1) return fail(CP_SPEC_EINVAL, "iters < 1");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Shape& sh = h->sh;
+  const int B = n_streams, R = sh.R, W = sh.W, G = sh.G;
+  const RoundArgs r = h->round_args(B);
+  // rows at mid-frame positions s0+1.., one distinct head per row
+  const int s0 = std::max(0, G - 1 - R);
+  std::vector<int> pos(static_cast<size_t>(B) * R), thead(static_cast<size_t>(B) * R);
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < R; ++i) {
+      pos[b * R + i] = s0 + 1 + i;
+      thead[b * R + i] = std::min(s0 + 1 + i, G - 1);
+    }
+  // head tables for the draft GEMV: variant v uses heads 1 + (v*W + t) % (G-1)
+  const int nvar = G - 1;
+  std::vector<int> dvar(static_cast<size_t>(nvar) * B * W);
+  for (int v = 0; v < nvar; ++v)
+    for (int b = 0; b < B; ++b)
+      for (int t = 0; t < W; ++t) dvar[(static_cast<size_t>(v) * B + b) * W + t] = 1 + (v * W + t) % (G - 1);
+  int* d_dvar = reinterpret_cast<int*>(r.q);  // scratch: the draft-distribution buffer
+  CPS_HIP(hipMemcpyAsync(r.pos, pos.data(), pos.size() * sizeof(int), hipMemcpyHostToDevice, s));
+  CPS_HIP(hipMemcpyAsync(r.thead, thead.data(), thead.size() * sizeof(int), hipMemcpyHostToDevice, s));
+  CPS_HIP(hipMemcpyAsync(d_dvar, dvar.data(), dvar.size() * sizeof(int), hipMemcpyHostToDevice, s));
+  CPS_HIP(hipStreamSynchronize(s));
+
+  const double ws = sh.wdt == CP_SPEC_BF16 ? 2.0 : 4.0;
+  const double M = static_cast<double>(B) * R, H = sh.H, F = sh.F, V = sh.V;
+  const double qd = sh.qdim, kvd = sh.kvdim;
+  double bytes = 0, flops = 0, rows = M;
+  switch (kind) {
+    case CP_SPEC_KERNEL_DRAFT_HEADS:
+      rows = static_cast<double>(B) * W;
+      bytes = std::min(W, G - 1) * V * H * ws + rows * (H + V) * 4;
+      flops = 2 * rows * V * H;
+      break;
+    case CP_SPEC_KERNEL_QKV:
+      bytes = (qd + 2 * kvd) * H * ws + M * (H + qd + 2 * kvd) * 4;
+      flops = 2 * M * (qd + 2 * kvd) * H;
+      break;
+    case CP_SPEC_KERNEL_ATTENTION: {
+      const double np = s0 + R;
+      bytes = B * np * 2 * kvd * 4 + M * 2 * qd * 4;
+      flops = 4 * M * np * qd;
+      break;
+    }
+    case CP_SPEC_KERNEL_O_PROJ:
+      bytes = H * qd * ws + M * (qd + 2 * H) * 4;
+      flops = 2 * M * H * qd;
+      break;
+    case CP_SPEC_KERNEL_GATE_UP:
+      bytes = 2 * F * H * ws + M * (H + F) * 4;
+      flops = 4 * M * F * H;
+      break;
+    case CP_SPEC_KERNEL_DOWN:
+      bytes = H * F * ws + M * (F + 2 * H) * 4;
+      flops = 2 * M * H * F;
+      break;
+    case CP_SPEC_KERNEL_TARGET_HEADS:
+      bytes = std::min(R, G - 1) * V * H * ws + M * (2 * H + V) * 4;
+      flops = 2 * M * V * H;
+      break;
+  }
+  auto launch = [&](int i) -> int {
+    if (kind == CP_SPEC_KERNEL_DRAFT_HEADS)
+      return head_logits(h, s, B * W, r.hstate, W, d_dvar + static_cast<size_t>(i % nvar) * B * W,
+                         nullptr, nullptr, r.dlogits);
+    if (kind == CP_SPEC_KERNEL_TARGET_HEADS)
+      return head_logits(h, s, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits);
+    return layer_kernel(h, s, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv));
+  };
+  int rc = launch(0);  // warm the launch path
+  if (rc) return rc;
+  hipEvent_t e0, e1;
+  CPS_HIP(hipEventCreate(&e0));
+  CPS_HIP(hipEventCreate(&e1));
+  CPS_HIP(hipEventRecord(e0, s));
+  for (int i = 0; i < iters && !rc; ++i) rc = launch(i);
+  CPS_HIP(hipEventRecord(e1, s));
+  CPS_HIP(hipEventSynchronize(e1));
+  float ms = 0.0f;
+  CPS_HIP(hipEventElapsedTime(&ms, e0, e1));
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  if (rc) return rc;
+  out->avg_us = 1e3 * ms / iters;
+  out->bytes_per_launch = bytes;
+  out->flops_per_launch = flops;
+  out->launches = iters;
+  out->rows = static_cast<int32_t>(rows);
   return CP_SPEC_OK;
 }
 

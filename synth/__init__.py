@@ -5,30 +5,32 @@ draws numbers: model shapes, weights, per-frame inputs and per-frame Philox
 seeds.  It holds none of the decoding method's arithmetic (no forward pass, no
 softmax, no sampling, no acceptance rule).
 
-Workloads (shapes follow the five configurations the speculative-decoding
-target is quoted on; the real Qwen3-TTS CodePredictor is 5 layers, hidden
-1024, 16 code groups of vocabulary 2048, per "RVQ Position Aware Speculative
-Decoding for On Device TTS", section 2 and Figure 1):
+Workloads (the real Qwen3-TTS CodePredictor is 5 layers, hidden 1024, 16
+code groups of vocabulary 2048, per "RVQ Position Aware Speculative Decoding
+for On Device TTS", section 2 and Figure 1):
 
-  1  tiny, fp32:   2 layers, H 256, 4/4 heads of 64, FFN 768, G 8, V 256
-  2  Qwen3-TTS-0.6B-shaped, bf16: 5 layers, H 1024, 16/8 heads of 128,
-     FFN 3072, G 16, V 2048
-  3  config 1's decoder, greedy, verify window swept 2..8
-  4  config 1's decoder, 64 streams, top-k 50, N 4
-  5  wide Omni-talker-like, bf16: 8 layers, H 2048, 16/4 heads of 128,
-     FFN 6144, G 16, V 4096, heads correlated across depths
+  tiny         fp32: 2 layers, H 256, 4/4 heads of 64, FFN 768, G 8, V 256,
+               1 stream x 100 frames, N 3
+  qwen3tts     Qwen3-TTS-0.6B-shaped, bf16: 5 layers, H 1024, 16/8 heads of
+               128, FFN 3072, G 16, V 2048, 1 stream x 1000 frames, N 4
+  tiny-greedy  the tiny decoder, greedy, verify window swept 2..8
+  tiny-64      the tiny decoder, 64 streams x 500 frames, top-k 50, N 4
+  wide-256     wide Omni-talker-like, bf16: 8 layers, H 2048, 16/4 heads of
+               128, FFN 6144, G 16, V 4096, heads correlated across depths,
+               256 streams x 200 frames, N 4
 
 Value recipe:
   * every weight matrix (projections, embedding tables, lm_heads) is drawn
-    N(0, 0.02) in float32 from numpy's PCG64 seeded with ``1000 + config``;
+    N(0, 0.02) in float32 from numpy's PCG64 seeded with ``1000 + n``, n the
+    workload's number in WORKLOADS (1-based);
     bf16 configurations round each value to bfloat16 with round-to-nearest-
     even and hand the bit patterns over as uint16;
   * RMSNorm gains are 1 (float32);
-  * config 5's heads are W_j = B + 0.3 * N_j with B, N_j iid N(0, 0.02);
+  * wide-256's heads are W_j = B + 0.3 * N_j with B, N_j iid N(0, 0.02);
   * h_frame ~ N(0, 1) float32 and c0 ~ U{0..V-1}, from PCG64 seeded with
-    ``2000 + config``;
+    ``2000 + n``;
   * the Philox key of frame f, stream b is SplitMix64(seed_base + f*B + b)
-    with seed_base = ``3000 + config`` shifted left by 32 bits.
+    with seed_base = ``3000 + n`` shifted left by 32 bits.
 """
 from __future__ import annotations
 
@@ -38,27 +40,29 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-# Decoder/codebook shapes and decoding parameters of the five workloads.
+# Decoder/codebook shapes and decoding parameters of the workloads.
+WORKLOADS = ("tiny", "qwen3tts", "tiny-greedy", "tiny-64", "wide-256")
+
 _BASE = {
-    1: dict(name="tiny-fp32", layers=2, hidden=256, q_heads=4, kv_heads=4,
+    "tiny": dict(name="tiny-fp32", layers=2, hidden=256, q_heads=4, kv_heads=4,
             head_dim=64, ffn=768, groups=8, vocab=256, dtype=F32,
             rope_theta=1e4, rms_eps=1e-6, greedy=False, temperature=0.9,
             top_k=50, verify_size=3, streams=1, frames=100, heads_corr=None),
-    2: dict(name="qwen3-tts-0.6b-codepredictor", layers=5, hidden=1024,
+    "qwen3tts": dict(name="qwen3-tts-0.6b-codepredictor", layers=5, hidden=1024,
             q_heads=16, kv_heads=8, head_dim=128, ffn=3072, groups=16,
             vocab=2048, dtype=BF16, rope_theta=1e4, rms_eps=1e-6,
             greedy=False, temperature=0.9, top_k=50, verify_size=4,
             streams=1, frames=1000, heads_corr=None),
-    3: dict(name="tiny-fp32-greedy", layers=2, hidden=256, q_heads=4,
+    "tiny-greedy": dict(name="tiny-fp32-greedy", layers=2, hidden=256, q_heads=4,
             kv_heads=4, head_dim=64, ffn=768, groups=8, vocab=256, dtype=F32,
             rope_theta=1e4, rms_eps=1e-6, greedy=True, temperature=1.0,
             top_k=1, verify_size=4, verify_sweep=(2, 3, 4, 5, 6, 7, 8),
             streams=1, frames=1000, heads_corr=None),
-    4: dict(name="tiny-fp32-64streams", layers=2, hidden=256, q_heads=4,
+    "tiny-64": dict(name="tiny-fp32-64streams", layers=2, hidden=256, q_heads=4,
             kv_heads=4, head_dim=64, ffn=768, groups=8, vocab=256, dtype=F32,
             rope_theta=1e4, rms_eps=1e-6, greedy=False, temperature=0.9,
             top_k=50, verify_size=4, streams=64, frames=500, heads_corr=None),
-    5: dict(name="omni-talker-wide-codepredictor", layers=8, hidden=2048,
+    "wide-256": dict(name="omni-talker-wide-codepredictor", layers=8, hidden=2048,
             q_heads=16, kv_heads=4, head_dim=128, ffn=6144, groups=16,
             vocab=4096, dtype=BF16, rope_theta=1e4, rms_eps=1e-6,
             greedy=False, temperature=0.8, top_k=100, verify_size=4,
@@ -66,8 +70,9 @@ _BASE = {
 }
 
 
-def config(cid: int, **overrides) -> dict:
-    """Return a copy of workload ``cid`` with ``overrides`` applied.
+def config(wl: str, **overrides) -> dict:
+    """Return a copy of workload ``wl`` (a name in WORKLOADS) with
+    ``overrides`` applied.
 
     Keys: layers, hidden, q_heads, kv_heads, head_dim, ffn, groups (G),
     vocab (V), dtype ('f32'|'bf16'), rope_theta, rms_eps, greedy,
@@ -75,11 +80,12 @@ def config(cid: int, **overrides) -> dict:
     frames (F), heads_corr (None or the noise scale of correlated heads),
     plus 'id', 'weight_seed', 'input_seed', 'philox_base'.
     """
-    c = copy.deepcopy(_BASE[cid])
-    c["id"] = cid
-    c["weight_seed"] = 1000 + cid
-    c["input_seed"] = 2000 + cid
-    c["philox_base"] = (3000 + cid) << 32
+    n = WORKLOADS.index(wl) + 1
+    c = copy.deepcopy(_BASE[wl])
+    c["id"] = wl
+    c["weight_seed"] = 1000 + n
+    c["input_seed"] = 2000 + n
+    c["philox_base"] = (3000 + n) << 32
     c.update(overrides)
     return c
 

@@ -23,12 +23,12 @@ def test_every_header_symbol_is_exported(L):
 
 
 def test_workspace_sizes():
-    for cid in (1, 2, 3, 4, 5):
+    for cid in synth.WORKLOADS:
         n = binding.workspace_bytes(binding.make_cfg(synth.config(cid)))
         assert n > 0 and n % 256 == 0, cid
-    n1 = binding.workspace_bytes(binding.make_cfg(synth.config(4),
+    n1 = binding.workspace_bytes(binding.make_cfg(synth.config("tiny-64"),
                                                   max_streams=1))
-    n64 = binding.workspace_bytes(binding.make_cfg(synth.config(4)))
+    n64 = binding.workspace_bytes(binding.make_cfg(synth.config("tiny-64")))
     assert n64 > n1
 
 
@@ -58,7 +58,7 @@ def _create(cfg):
     ("head_dim", 256, binding.EUNSUPPORTED, "head_dim"),
 ])
 def test_create_validation(field, value, code, msg):
-    cfg = binding.make_cfg(synth.config(1))
+    cfg = binding.make_cfg(synth.config("tiny"))
     setattr(cfg, field, value)
     rc, err = _create(cfg)
     assert rc == code and msg in err, (rc, err)
@@ -66,14 +66,14 @@ def test_create_validation(field, value, code, msg):
 
 
 def test_greedy_ignores_sampling_fields():
-    cfg = binding.make_cfg(synth.config(3))
+    cfg = binding.make_cfg(synth.config("tiny-greedy"))
     cfg.top_k = 0
     cfg.temperature = 0.0
     assert binding.workspace_bytes(cfg) > 0
 
 
 def test_workspace_checks_before_any_device_work():
-    cfg = binding.make_cfg(synth.config(1))
+    cfg = binding.make_cfg(synth.config("tiny"))
     rc, err = _create(cfg)                     # null workspace
     assert rc == binding.EWORKSPACE and "workspace" in err
     h = C.c_void_p()

@@ -21,7 +21,7 @@ def _check(cid, c, hf, c0, seeds, pairs, gc, gf, gst, dp, exact_stats):
     sel_c = np.array([gc[f, b] for f, b in pairs])
     sel_f = np.array([gf[f, b] for f, b in pairs])
     res = compare_frames(sel_c, sel_f, oc, of)
-    log(f"cfg{cid} N={dp['verify_size']}: {res['frames']} frames, "
+    log(f"{cid} N={dp['verify_size']}: {res['frames']} frames, "
         f"{res['exact']} exact, {res['flagged_mismatch']} flagged mismatches, "
         f"{res['flagged_frames']} flagged frames, "
         f"{len(res['unflagged'])} unflagged")
@@ -36,99 +36,99 @@ def _check(cid, c, hf, c0, seeds, pairs, gc, gf, gst, dp, exact_stats):
     return res
 
 
-def test_config1_full():
-    c = synth.config(1)
+def test_tiny_full():
+    c = synth.config("tiny")
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(1)
-    log("decode cfg1 F=100 B=1")
+    h = handle("tiny")
+    log("decode tiny F=100 B=1")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     pairs = [(f, 0) for f in range(c["frames"])]
-    _check(1, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), True)
+    _check("tiny", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), True)
     assert gst["frames"] == 100 and gst["codes"] == 100 * 7
     assert gst["prefill_passes"] == 100
 
 
-def test_config1_autoregressive_mode():
-    c = synth.config(1, verify_size=0, frames=30)
+def test_tiny_autoregressive_mode():
+    c = synth.config("tiny", verify_size=0, frames=30)
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(1, verify_size=0)
-    log("decode cfg1 AR F=30")
+    h = handle("tiny", verify_size=0)
+    log("decode tiny AR F=30")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     pairs = [(f, 0) for f in range(30)]
-    _check(1, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c, verify_size=0),
+    _check("tiny", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c, verify_size=0),
            True)
     assert gst["rounds"] == 30 * 6 and sum(gst["proposed"]) == 0
 
 
 @pytest.mark.parametrize("N", [2, 3, 4, 5, 6, 7, 8])
-def test_config3_greedy_sweep(N):
-    c = synth.config(3, verify_size=N, frames=150)
+def test_tiny_greedy_window_sweep(N):
+    c = synth.config("tiny-greedy", verify_size=N, frames=150)
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(3, verify_size=N)
-    log(f"decode cfg3 greedy N={N} F=150")
+    h = handle("tiny-greedy", verify_size=N)
+    log(f"decode tiny-greedy N={N} F=150")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     pairs = [(f, 0) for f in range(150)]
-    _check(3, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c, verify_size=N),
+    _check("tiny-greedy", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c, verify_size=N),
            True)
     # greedy speculation reproduces greedy autoregressive decoding on GPU too
-    har = handle(3, verify_size=0)
+    har = handle("tiny-greedy", verify_size=0)
     ac, af, _ = decode_gpu(har, hf, c0, seeds)
     res = compare_frames(gc, gf, ac, af)
     assert not res["unflagged"]
 
 
-def test_config4_small_all_frames():
-    c = synth.config(4, frames=5)
+def test_tiny_64_streams_all_frames():
+    c = synth.config("tiny-64", frames=5)
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(4)
-    log("decode cfg4 B=64 F=5")
+    h = handle("tiny-64")
+    log("decode tiny-64 B=64 F=5")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     pairs = [(f, b) for f in range(5) for b in range(64)]
-    _check(4, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), True)
+    _check("tiny-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), True)
 
 
-def test_config4_full_sampled():
-    c = synth.config(4)
+def test_tiny_64_streams_full_sampled():
+    c = synth.config("tiny-64")
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(4)
-    log("decode cfg4 B=64 F=500 (full)")
+    h = handle("tiny-64")
+    log("decode tiny-64 B=64 F=500 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 64 * 500
     rng = np.random.default_rng(4)
     pairs = [(int(rng.integers(0, 500)), int(rng.integers(0, 64)))
              for _ in range(24)]
-    _check(4, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+    _check("tiny-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
-def test_config2_full_sampled():
-    c = synth.config(2)
+def test_qwen3tts_full_sampled():
+    c = synth.config("qwen3tts")
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(2)
-    log("decode cfg2 B=1 F=1000 (full)")
+    h = handle("qwen3tts")
+    log("decode qwen3tts B=1 F=1000 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 1000 and gst["codes"] == 15000
     pairs = [(f, 0) for f in (0, 1, 333, 777, 999)]
-    _check(2, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+    _check("qwen3tts", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
-def test_config5_sampled():
-    c = synth.config(5, frames=2)
+def test_wide_256_streams_sampled():
+    c = synth.config("wide-256", frames=2)
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(5)
-    log("decode cfg5 B=256 F=2")
+    h = handle("wide-256")
+    log("decode wide-256 B=256 F=2")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 512
     pairs = [(0, 0), (1, 255), (0, 128)]
-    _check(5, c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+    _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
 def test_determinism_and_stream_independence():
     """Two runs are bit-identical; stream 0 of a 64-stream run equals the
     same frames decoded alone (up to flagged near ties)."""
-    c = synth.config(4, frames=4)
+    c = synth.config("tiny-64", frames=4)
     hf, c0, seeds = synth.make_inputs(c)
-    h = handle(4)
-    log("determinism cfg4")
+    h = handle("tiny-64")
+    log("determinism tiny-64")
     a = decode_gpu(h, hf, c0, seeds)
     b = decode_gpu(h, hf, c0, seeds)
     np.testing.assert_array_equal(a[0], b[0])
@@ -141,13 +141,13 @@ def test_determinism_and_stream_independence():
 
 def test_zero_frames_and_bad_stream_count():
     from speculative_decoding_rvq_amd import binding
-    c = synth.config(1)
-    h = handle(1)
+    c = synth.config("tiny")
+    h = handle("tiny")
     hf, c0, seeds = synth.make_inputs(c, frames=1)
     gc, _, st = decode_gpu(h, hf[:0], c0[:0], seeds[:0])
     assert gc.shape[0] == 0 and st["frames"] == 0
     with pytest.raises(binding.CpSpecError):
-        h2 = handle(1)
+        h2 = handle("tiny")
         bad = np.zeros((1, 2), np.int32)
         decode_gpu(h2, np.zeros((1, 2, 256), np.float32), bad,
                    np.zeros((1, 2), np.uint64))

@@ -73,7 +73,7 @@ def _hf_model(c, w):
     synth.custom(layers=1, hidden=64, q_heads=4, kv_heads=1, head_dim=16,
                  ffn=96, groups=5, vocab=8, dtype=synth.BF16,
                  weight_scale=0.2, rope_theta=500.0, rms_eps=1e-5),
-    synth.config(1),
+    synth.config("tiny"),
 ], ids=["gqa2", "mqa-bf16", "config1"])
 def test_frame_matches_hf_llama(c):
     """All G positions of a frame, fed one at a time through the KV cache,

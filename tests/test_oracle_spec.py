@@ -34,7 +34,7 @@ def _tiny(**kw):
 
 
 @pytest.mark.parametrize("c", [
-    synth.config(1),
+    synth.config("tiny"),
     synth.custom(layers=2, hidden=32, q_heads=4, kv_heads=2, head_dim=8,
                  ffn=48, groups=16, vocab=32, weight_scale=0.3),
 ], ids=["config1", "G16"])
@@ -259,7 +259,7 @@ def test_disjoint_supports_reject_everything_and_match_ar():
 
 
 def test_top1_sampling_is_the_greedy_chain():
-    c = synth.config(1)
+    c = synth.config("tiny")
     m = dec.Model(c, synth.make_weights(c))
     h, c0, seeds = synth.make_inputs(c, frames=3, streams=1)
     a, _ = spec.decode(m, _dp(3, T=0.9, k=1), h, c0, seeds)
@@ -268,7 +268,7 @@ def test_top1_sampling_is_the_greedy_chain():
 
 
 def test_round_bounds_and_first_code_matches_ar():
-    c = synth.config(1)
+    c = synth.config("tiny")
     m = dec.Model(c, synth.make_weights(c))
     h, c0, seeds = synth.make_inputs(c, frames=8, streams=1)
     st = spec.new_stats()

@@ -42,40 +42,88 @@ template <> __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t*
 }
 
 // ----------------------------------------------------------- reductions ----
+// Cross-lane steps use DPP (row rotations / shifts / broadcasts inside the
+// VALU) and readlane, not LDS permutes.  Fixed association order:
+// deterministic.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ uint32_t lane_u(uint32_t v, int l) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+
+// row_ror:n control words (rotate within each row of 16 lanes)
+constexpr int kRor8 = 0x128, kRor4 = 0x124, kRor2 = 0x122, kRor1 = 0x121;
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<kRor8>(v);
+  v += dpp_f<kRor4>(v);
+  v += dpp_f<kRor2>(v);
+  v += dpp_f<kRor1>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kRor8>(v));
+  v = fmaxf(v, dpp_f<kRor4>(v));
+  v = fmaxf(v, dpp_f<kRor2>(v));
+  v = fmaxf(v, dpp_f<kRor1>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
-}
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  v = umax32(v, static_cast<uint32_t>(dpp_i<kRor8>(static_cast<int>(v))));
+  v = umax32(v, static_cast<uint32_t>(dpp_i<kRor4>(static_cast<int>(v))));
+  v = umax32(v, static_cast<uint32_t>(dpp_i<kRor2>(static_cast<int>(v))));
+  v = umax32(v, static_cast<uint32_t>(dpp_i<kRor1>(static_cast<int>(v))));
+  return umax32(umax32(lane_u(v, 0), lane_u(v, 16)), umax32(lane_u(v, 32), lane_u(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  v = mn(v, static_cast<uint32_t>(dpp_i<kRor8>(static_cast<int>(v))));
+  v = mn(v, static_cast<uint32_t>(dpp_i<kRor4>(static_cast<int>(v))));
+  v = mn(v, static_cast<uint32_t>(dpp_i<kRor2>(static_cast<int>(v))));
+  v = mn(v, static_cast<uint32_t>(dpp_i<kRor1>(static_cast<int>(v))));
+  return mn(mn(lane_u(v, 0), lane_u(v, 16)), mn(lane_u(v, 32), lane_u(v, 48)));
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v += dpp_i<kRor8>(v);
+  v += dpp_i<kRor4>(v);
+  v += dpp_i<kRor2>(v);
+  v += dpp_i<kRor1>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+// Largest 64-bit key of the wave (compared as unsigned).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = static_cast<uint32_t>(v >> 32);
+  const uint32_t mhi = wave_max_u32(hi);
+  const uint32_t lo = hi == mhi ? static_cast<uint32_t>(v) : 0u;
+  return (static_cast<uint64_t>(mhi) << 32) | wave_max_u32(lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each
+// row of 16 (row_shr 1, 2, 4, 8 with zero fill), then the row totals carried
+// across rows with row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
   return v;
 }
 
 // Block-wide reductions over 256 threads; `red` is 4+ words of LDS.  Every
-// thread gets the result.  Fixed tree order: deterministic.
+// thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
@@ -100,9 +148,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   __syncthreads();
   if (l == 0) red[w] = v;
   __syncthreads();
-  uint32_t a = red[0] > red[1] ? red[0] : red[1];
-  uint32_t b = red[2] > red[3] ? red[2] : red[3];
-  return a > b ? a : b;
+  return umax32(umax32(red[0], red[1]), umax32(red[2], red[3]));
 }
 __device__ __forceinline__ int block_sum_i(int v, int* red) {
   v = wave_sum_i(v);
@@ -117,12 +163,7 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
 // `red` needs 4 words of LDS.  Returns the exclusive prefix; *total = sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int n = __shfl_up(inc, o, kWave);
-    if (l >= o) inc += n;
-  }
+  const int inc = wave_incl_scan(v);
   __syncthreads();
   if (l == kWave - 1) red[w] = inc;
   __syncthreads();
@@ -210,34 +251,51 @@ __device__ int block_sample(WF weight, int V, float u, SampleSmem& sm, bool* fla
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < kWave) {
+    // wave 0: the running sum is sequential in code order (float32 adds in
+    // one lane); entries are brought in 64 at a time and read with readlane
+    const int lane = threadIdx.x;
     int code = -1, near = 0;
     if (total > 0) {
 #pragma clang fp contract(off)
       float tot = 0.0f;
-      for (int i = 0; i < total; ++i) tot = tot + sm.w[i];
+      for (int base = 0; base < total; base += kWave) {
+        const float wl = base + lane < total ? sm.w[base + lane] : 0.0f;
+        const int n = min(kWave, total - base);
+#pragma unroll 16
+        for (int i = 0; i < n; ++i) tot = tot + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+      }
       const float t = u * tot;
       const double eps = static_cast<double>(tot) * kEpsCdf;
-      float run = 0.0f;
+      float run = 0.0f, before = 0.0f;
       int pos = total - 1;
-      for (int i = 0; i < total; ++i) {
-        const float before = run;
-        run = run + sm.w[i];
-        if (t < run) {
-          pos = i;
-          const bool lo = i > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps;
-          const bool hi = i + 1 < total && fabs(static_cast<double>(run) - static_cast<double>(t)) < eps;
-          near = (lo || hi) ? 1 : 0;
-          break;
+      bool found = false;
+      for (int base = 0; base < total && !found; base += kWave) {
+        const float wl = base + lane < total ? sm.w[base + lane] : 0.0f;
+        const int n = min(kWave, total - base);
+        for (int i = 0; i < n; ++i) {
+          before = run;
+          run = run + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+          if (t < run) {
+            pos = base + i;
+            found = true;
+            break;
+          }
         }
-        if (i == total - 1) {  // t == sum after rounding: the last entry
-          near = (i > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps) ? 1 : 0;
-        }
+      }
+      if (found) {
+        const bool lo = pos > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps;
+        const bool hi = pos + 1 < total && fabs(static_cast<double>(run) - static_cast<double>(t)) < eps;
+        near = (lo || hi) ? 1 : 0;
+      } else {  // t == sum after rounding: the last entry owns the top end
+        near = (total > 1 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps) ? 1 : 0;
       }
       code = sm.idx[pos];
     }
-    sm.result[0] = code;
-    sm.result[1] = near;
+    if (lane == 0) {
+      sm.result[0] = code;
+      sm.result[1] = near;
+    }
   }
   __syncthreads();
   *flag = sm.result[1] != 0;

@@ -44,6 +44,8 @@ struct Layout {
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Threads covering one weight row's K in the GEMV: the largest of 256, 128,
+// 64 that divides the row's 16-byte chunks with at most 4 chunks per thread.
 int choose_kt(int K, int vec) {
   if (K % vec) return 0;
   const int segs = K / vec;
@@ -77,7 +79,9 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   if (c->vocab % 256 || (vpt & (vpt - 1)))
     return fail(CP_SPEC_EUNSUPPORTED, "vocab must be 256 * 2^i (256..4096)");
   if (c->code_groups > CP_SPEC_MAX_GROUPS) return fail(CP_SPEC_EUNSUPPORTED, "code_groups > 32");
-  if (c->head_dim > 128) return fail(CP_SPEC_EUNSUPPORTED, "head_dim > 128");
+  if (c->head_dim != 8 && c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 &&
+      c->head_dim != 128)
+    return fail(CP_SPEC_EUNSUPPORTED, "head_dim must be 8, 16, 32, 64 or 128");
   Shape& s_ = *s;
   s_.L = c->layers; s_.H = c->hidden; s_.nq = c->q_heads; s_.nkv = c->kv_heads; s_.d = c->head_dim;
   s_.F = c->ffn; s_.G = c->code_groups; s_.V = c->vocab; s_.wdt = c->weight_dtype;
@@ -96,7 +100,7 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
     if (!choose_kt(K, s_.vec))
       return fail(CP_SPEC_EUNSUPPORTED, "matrix width " + std::to_string(K) +
                                             " not tileable (multiple of 256 fp32 / 512 bf16 "
-                                            "elements, at most 4 chunks per lane)");
+                                            "elements, at most 4 chunks per thread)");
   for (int N_ : {s_.qdim + 2 * s_.kvdim, s_.H, s_.V, s_.kvdim, s_.qdim})
     if (N_ % kRPGHost) return fail(CP_SPEC_EUNSUPPORTED, "output width must be a multiple of 4");
   if (s_.F % 2) return fail(CP_SPEC_EUNSUPPORTED, "ffn must be even");
@@ -183,25 +187,34 @@ struct cp_spec {
 
 namespace {
 
-int mt_for(int M) { return M <= 2 ? 2 : (M <= 4 ? 4 : 8); }
+// Activation rows per GEMV tile: enough for M when it is small, bounded so
+// that the activation slices a thread keeps (rows x chunks x 16 bytes) stay
+// within 96 registers.
+int mt_for(int M, int spt, int vec) {
+  int mt = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
+  while (mt > 1 && mt * spt * vec > 96) mt >>= 1;
+  return mt;
+}
 
 // One skinny projection: Y (op) W . rows(X).
 int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
-  a.kt = choose_kt(a.K, h->sh.vec);
+  if (a.M <= 0) return CP_SPEC_OK;
+  const int vec = h->sh.vec;
+  a.kt = choose_kt(a.K, vec);
   if (!a.kt) return fail(CP_SPEC_EUNSUPPORTED, "untileable K");
+  const int spt = a.K / (vec * a.kt);
   const int rg = 256 / a.kt;
-  a.units = mode == kSwiGLU ? a.N / 2 : a.N / 4;
-  int gx = (a.units + rg - 1) / rg;
-  gx = std::min(gx, 4096);
+  const int rpg = gemv_rpg(spt);
+  a.units = mode == kSwiGLU ? a.N / (rpg / 2) : a.N / rpg;
+  const int gx = std::min((a.units + rg - 1) / rg, 4096);
   int mt, gy;
   if (mode == kHead) {
     mt = 1;
     gy = a.M;
   } else {
-    mt = mt_for(a.M);
+    mt = mt_for(a.M, spt, vec);
     gy = (a.M + mt - 1) / mt;
   }
-  if (a.M <= 0) return CP_SPEC_OK;
   CPS_HIP(launch_gemv(h->sh.wdt, mode, mt, a, gx, gy, s));
   return CP_SPEC_OK;
 }

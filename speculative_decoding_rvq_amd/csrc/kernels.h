@@ -8,8 +8,11 @@
 
 namespace cps {
 
-constexpr int kRPG = 4;       // GEMV output rows per row group per pass
-constexpr int kRPGHost = kRPG;
+constexpr int kRPGHost = 4;   // output widths must be multiples of this
+
+// GEMV weight rows per row group per unit: 4, or 2 when a thread holds three
+// or more 16-byte chunks of each row.
+__host__ __device__ constexpr int gemv_rpg(int spt) { return spt >= 3 ? 2 : 4; }
 
 enum GemvMode : int {
   kStore = 0,   // Y[m][o] = acc

@@ -18,95 +18,138 @@ hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid
 
 // ---------------------------------------------------------------------------
 // Causal attention over the in-frame positions of one stream and one KV head.
-// The stream's K (rotated here) and V for positions 0..max row position are
-// staged in LDS; each wave takes (row, query head) pairs of the group.
+//
+// Phase 1 issues every global load at once (float4): K of positions
+// 0..max row position, rotated by RoPE on the way into LDS, V, and the rotated
+// queries of the group's (row, query head) pairs.  Phase 2: thread (pair, p)
+// of a 32-lane group computes one score; the group's max and sum give the
+// softmax weights (positions above the row's own are masked).  Phase 3: each
+// thread produces four consecutive output dimensions of one pair.
+template <int D>
 __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   extern __shared__ float smem[];
+  constexpr int half = D / 2;
+  constexpr int H4 = half / 4;  // float4s per half row
+  constexpr int KS = D + 4;     // padded K row stride (rows on different banks)
   const int b = blockIdx.x, g = blockIdx.y;
-  const int R = a.R, d = a.d, half = d / 2;
-  const int kvdim = a.nkv * d;
-  const int qdim = a.nq * d;
+  const int R = a.R;
+  const int kvdim = a.nkv * D;
+  const int qdim = a.nq * D;
+  const int group = a.nq / a.nkv;
+  const int npair = R * group;
+  __shared__ int pos_s[CP_SPEC_MAX_WINDOW];
+  if (threadIdx.x < R) pos_s[threadIdx.x] = a.pos[b * R + threadIdx.x];
+  __syncthreads();
   int maxp = -1;
-  for (int r = 0; r < R; ++r) maxp = max(maxp, a.pos[b * R + r]);
-  if (maxp < 0 || maxp >= a.G) return;  // positions outside the frame: no-op
+  for (int r = 0; r < R; ++r) maxp = max(maxp, pos_s[r]);
+  if (maxp < 0 || maxp >= a.G) return;  // no active row, or outside the frame
   const int np = maxp + 1;
-  float* Ks = smem;                 // [np][d]
-  float* Vs = smem + np * d;        // [np][d]
-  const float* kb = a.kv + static_cast<size_t>(b) * a.kv_sb + g * d;
+  float* Ks = smem;                  // [np][KS]
+  float* Vs = Ks + a.G * KS;         // [np][D]
+  float* Qs = Vs + a.G * D;          // [npair][D]
+  float* S = Qs + npair * D;         // [npair][32]
+  const float* kb = a.kv + static_cast<size_t>(b) * a.kv_sb + g * D;
   const float* vb = kb + a.kv_vo;
-  for (int idx = threadIdx.x; idx < np * half; idx += kBlock) {
-    const int p = idx / half, i = idx % half;
-    const float k1 = kb[p * kvdim + i], k2 = kb[p * kvdim + i + half];
-    const float2 cs = a.rope[p * half + i];
-    Ks[p * d + i] = k1 * cs.x - k2 * cs.y;
-    Ks[p * d + i + half] = k2 * cs.x + k1 * cs.y;
-    Vs[p * d + i] = vb[p * kvdim + i];
-    Vs[p * d + i + half] = vb[p * kvdim + i + half];
+
+  // ---- phase 1: K (rotated), V, Q (rotated) into LDS ----
+  const int nk = np * H4, nq = npair * H4;
+  for (int it = threadIdx.x; it < nk + nq; it += kBlock) {
+    if (it < nk) {
+      const int p = it / H4, i4 = (it % H4) * 4;
+      const float4 k1 = *reinterpret_cast<const float4*>(kb + p * kvdim + i4);
+      const float4 k2 = *reinterpret_cast<const float4*>(kb + p * kvdim + i4 + half);
+      const float4 v1 = *reinterpret_cast<const float4*>(vb + p * kvdim + i4);
+      const float4 v2 = *reinterpret_cast<const float4*>(vb + p * kvdim + i4 + half);
+      const float4 c01 = *reinterpret_cast<const float4*>(a.rope + p * half + i4);      // cos,sin x2
+      const float4 c23 = *reinterpret_cast<const float4*>(a.rope + p * half + i4 + 2);
+      float* kr = Ks + p * KS;
+      kr[i4 + 0] = k1.x * c01.x - k2.x * c01.y;  kr[i4 + half + 0] = k2.x * c01.x + k1.x * c01.y;
+      kr[i4 + 1] = k1.y * c01.z - k2.y * c01.w;  kr[i4 + half + 1] = k2.y * c01.z + k1.y * c01.w;
+      kr[i4 + 2] = k1.z * c23.x - k2.z * c23.y;  kr[i4 + half + 2] = k2.z * c23.x + k1.z * c23.y;
+      kr[i4 + 3] = k1.w * c23.z - k2.w * c23.w;  kr[i4 + half + 3] = k2.w * c23.z + k1.w * c23.w;
+      *reinterpret_cast<float4*>(Vs + p * D + i4) = v1;
+      *reinterpret_cast<float4*>(Vs + p * D + i4 + half) = v2;
+    } else {
+      const int jt = it - nk;
+      const int pr = jt / H4, i4 = (jt % H4) * 4;
+      const int r = pr / group, j = pr % group;
+      const float* qrow = a.Q + static_cast<size_t>(b * R + r) * qdim + (g * group + j) * D;
+      const int pq = max(pos_s[r], 0);
+      const float4 q1 = *reinterpret_cast<const float4*>(qrow + i4);
+      const float4 q2 = *reinterpret_cast<const float4*>(qrow + i4 + half);
+      const float4 c01 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4);
+      const float4 c23 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4 + 2);
+      float* qr = Qs + pr * D;
+      qr[i4 + 0] = q1.x * c01.x - q2.x * c01.y;  qr[i4 + half + 0] = q2.x * c01.x + q1.x * c01.y;
+      qr[i4 + 1] = q1.y * c01.z - q2.y * c01.w;  qr[i4 + half + 1] = q2.y * c01.z + q1.y * c01.w;
+      qr[i4 + 2] = q1.z * c23.x - q2.z * c23.y;  qr[i4 + half + 2] = q2.z * c23.x + q1.z * c23.y;
+      qr[i4 + 3] = q1.w * c23.z - q2.w * c23.w;  qr[i4 + half + 3] = q2.w * c23.z + q1.w * c23.w;
+    }
   }
   __syncthreads();
-  const int group = a.nq / a.nkv;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int pair = wave; pair < R * group; pair += kBlock / kWave) {
-    const int r = pair / group, j = pair % group;
-    const int row = b * R + r;
-    const int pr = a.pos[row];
-    if (pr < 0) continue;
-    const int h = g * group + j;
-    const float* qrow = a.Q + static_cast<size_t>(row) * qdim + h * d;
-    float q1[4], q2[4];
+
+  // ---- phase 2: scores and softmax, 32 lanes per pair ----
+  for (int base = 0; base < npair * 32; base += kBlock) {
+    const int idx = base + threadIdx.x;
+    const int pr = idx >> 5, p = idx & 31;
+    const bool live_pair = pr < npair;
+    const int pp = live_pair ? pos_s[pr / group] : -1;
+    float s = -INFINITY;
+    if (live_pair && p <= pp) {
+      const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
+      const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
+      float acc = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = lane + kWave * c;
-      q1[c] = 0.0f;
-      q2[c] = 0.0f;
-      if (i < half) {
-        const float x1 = qrow[i], x2 = qrow[i + half];
-        const float2 cs = a.rope[pr * half + i];
-        q1[c] = x1 * cs.x - x2 * cs.y;
-        q2[c] = x2 * cs.x + x1 * cs.y;
+      for (int i = 0; i < D / 4; ++i) {
+        const float4 x = q4[i], y = k4[i];
+        acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
       }
+      s = acc * a.scale;
     }
-    // online softmax over positions 0..pr (running max and rescaled sums)
-    float mx = -INFINITY, sum = 0.0f;
-    float o1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, o2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p = 0; p <= pr; ++p) {
-      float dot = 0.0f;
+    // max and sum over the 32 lanes of the pair (xor within 32)
+    float mx = s;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = lane + kWave * c;
-        if (i < half) dot += q1[c] * Ks[p * d + i] + q2[c] * Ks[p * d + i + half];
-      }
-      dot = wave_sum(dot) * a.scale;
-      const float mn = fmaxf(mx, dot);
-      const float corr = expf(mx - mn);
-      const float e = expf(dot - mn);
-      sum = sum * corr + e;
+    for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+    const float e = (live_pair && p <= pp) ? expf(s - mx) : 0.0f;
+    float sum = e;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = lane + kWave * c;
-        if (i < half) {
-          o1[c] = o1[c] * corr + e * Vs[p * d + i];
-          o2[c] = o2[c] * corr + e * Vs[p * d + i + half];
-        }
-      }
-      mx = mn;
+    for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
+    if (live_pair) S[pr * 32 + p] = (p <= pp) ? e / sum : 0.0f;
+  }
+  __syncthreads();
+
+  // ---- phase 3: four output dimensions of one pair per thread ----
+  constexpr int D4 = D / 4;
+  for (int idx = threadIdx.x; idx < npair * D4; idx += kBlock) {
+    const int pr = idx / D4, i4 = (idx % D4) * 4;
+    const int r = pr / group, j = pr % group;
+    const int pp = pos_s[r];
+    if (pp < 0) continue;
+    const float* srow = S + pr * 32;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int p = 0; p <= pp; ++p) {
+      const float w = srow[p];
+      const float4 v = *reinterpret_cast<const float4*>(Vs + p * D + i4);
+      o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
     }
-    const float inv = 1.0f / sum;
-    float* orow = a.out + static_cast<size_t>(row) * qdim + h * d;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = lane + kWave * c;
-      if (i < half) {
-        orow[i] = o1[c] * inv;
-        orow[i + half] = o2[c] * inv;
-      }
-    }
+    *reinterpret_cast<float4*>(a.out + static_cast<size_t>(b * R + r) * qdim + (g * group + j) * D + i4) = o;
   }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s) {
-  const size_t shm = 2 * static_cast<size_t>(a.G) * a.d * sizeof(float);
-  hipLaunchKernelGGL(attention_kernel, dim3(B, a.nkv), dim3(kBlock), shm, s, a);
+  const size_t npair = static_cast<size_t>(a.R) * (a.nq / a.nkv);
+  const size_t shm =
+      (static_cast<size_t>(a.G) * (2 * a.d + 4) + npair * a.d + npair * 32) * sizeof(float);
+  switch (a.d) {
+#define CPS_ATT(D_)                                                                     \
+  case D_:                                                                              \
+    hipLaunchKernelGGL(attention_kernel<D_>, dim3(B, a.nkv), dim3(kBlock), shm, s, a); \
+    break;
+    CPS_ATT(8) CPS_ATT(16) CPS_ATT(32) CPS_ATT(64) CPS_ATT(128)
+#undef CPS_ATT
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -319,17 +362,17 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Accept scan of one stream's round.  Decisions are taken by thread 0 in
-// float32 and broadcast; sampling uses the block sampler.  Callbacks give
-// the uniforms (acceptance at offset t, target draw at offset t) and, when
-// greedy, the target argmax of verify row r.  Returns the number of codes
+// float32 and broadcast; sampling uses the block sampler.  uacc[t-1] and
+// utgt[t-1] are the uniforms of offset t (acceptance test, target draw); a
+// callback gives the target argmax of verify row r when greedy.  Returns the number of codes
 // committed; codes[0..n) are the committed codes; accept_near[t-1] and
 // cdf_near[t-1] report near ties at offset t.
 
-template <typename UA, typename UT, typename TA>
+template <typename TA>
 __device__ int accept_scan(int gamma, const int* draft, const float* q, const float* p, int V,
-                           bool greedy, UA uacc, UT utgt, TA targmax, int* codes,
+                           bool greedy, const float* uacc, const float* utgt, TA targmax, int* codes,
                            uint32_t* accept_near, uint32_t* cdf_near, int* n_acc_out,
-                           SampleSmem& samp, int* dec) {
+                           SampleSmem& samp, int* dec, float* pq) {
   if (greedy) {
     int t = 0;
     while (t < gamma && draft[t] == targmax(t)) {
@@ -340,14 +383,22 @@ __device__ int accept_scan(int gamma, const int* draft, const float* q, const fl
     *n_acc_out = t;
     return t + 1;
   }
-  for (int t = 1; t <= gamma; ++t) {
+  // p(d_t) and q(d_t) of every offset in one round trip
+  if (threadIdx.x < gamma) {
+    const int t = threadIdx.x + 1;
     const int d = draft[t - 1];
     const bool inr = d >= 0 && d < V;
+    pq[2 * threadIdx.x] = inr ? p[static_cast<size_t>(t - 1) * V + d] : 0.0f;
+    pq[2 * threadIdx.x + 1] = inr ? q[static_cast<size_t>(t - 1) * V + d] : 1.0f;
+  }
+  __syncthreads();
+  for (int t = 1; t <= gamma; ++t) {
+    const int d = draft[t - 1];
     if (threadIdx.x == 0) {
-      const float pd = inr ? p[static_cast<size_t>(t - 1) * V + d] : 0.0f;
-      const float qd = inr ? q[static_cast<size_t>(t - 1) * V + d] : 1.0f;
+      const float pd = pq[2 * (t - 1)];
+      const float qd = pq[2 * (t - 1) + 1];
       const float ratio = pd / qd;
-      const float uu = uacc(t);
+      const float uu = uacc[t - 1];
       dec[0] = uu < ratio ? 1 : 0;
       dec[1] = fabs(static_cast<double>(uu) - static_cast<double>(ratio)) < kEpsAccept ? 1 : 0;
     }
@@ -362,7 +413,7 @@ __device__ int accept_scan(int gamma, const int* draft, const float* q, const fl
     const float* pr = p + static_cast<size_t>(t - 1) * V;
     const float* qr = q + static_cast<size_t>(t - 1) * V;
     bool near = false;
-    const float ut = utgt(t);
+    const float ut = utgt[t - 1];
     int c = block_sample([&](int i) { return fmaxf(pr[i] - qr[i], 0.0f); }, V, ut, samp, &near);
     if (c < 0) c = block_sample([&](int i) { return pr[i]; }, V, ut, samp, &near);
     codes[t - 1] = c;
@@ -372,7 +423,7 @@ __device__ int accept_scan(int gamma, const int* draft, const float* q, const fl
   }
   const float* pr = p + static_cast<size_t>(gamma) * V;
   bool near = false;
-  codes[gamma] = block_sample([&](int i) { return pr[i]; }, V, utgt(gamma + 1), samp, &near);
+  codes[gamma] = block_sample([&](int i) { return pr[i]; }, V, utgt[gamma], samp, &near);
   cdf_near[gamma] = near ? 1u : 0u;
   *n_acc_out = gamma;
   return gamma + 1;
@@ -381,6 +432,7 @@ __device__ int accept_scan(int gamma, const int* draft, const float* q, const fl
 // Component accept: one block per stream, uniforms and drafts from memory.
 __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a) {
   __shared__ int dec[2];
+  __shared__ float pq[2 * CP_SPEC_MAX_WINDOW];
   __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
   __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
   __shared__ int targ[CP_SPEC_MAX_WINDOW + 1];
@@ -407,13 +459,17 @@ __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a)
   }
   __syncthreads();
   const int* draft = a.draft + static_cast<size_t>(b) * W;
-  const float* ua = a.u_acc + static_cast<size_t>(b) * W;
-  const float* ut = a.u_tgt + static_cast<size_t>(b) * (W + 1);
+  __shared__ float ua[CP_SPEC_MAX_WINDOW], ut[CP_SPEC_MAX_WINDOW + 1];
+  if (!a.greedy) {
+    if (threadIdx.x < gamma) ua[threadIdx.x] = a.u_acc[static_cast<size_t>(b) * W + threadIdx.x];
+    if (threadIdx.x >= 16 && threadIdx.x - 16 <= gamma)
+      ut[threadIdx.x - 16] = a.u_tgt[static_cast<size_t>(b) * (W + 1) + threadIdx.x - 16];
+  }
+  __syncthreads();
   int n_acc = 0;
-  const int n = accept_scan(
-      gamma, draft, q, p, V, a.greedy != 0, [&](int t) { return ua[t - 1]; },
-      [&](int t) { return ut[t - 1]; }, [&](int r) { return targ[r]; }, codes, anear, cnear,
-      &n_acc, tsm.samp, dec);
+  const int n = accept_scan(gamma, draft, q, p, V, a.greedy != 0, ua, ut,
+                            [&](int r) { return targ[r]; }, codes, anear, cnear, &n_acc, tsm.samp,
+                            dec, pq);
   __syncthreads();
   if (threadIdx.x == 0) {
     a.n_out[b] = n;
@@ -556,6 +612,8 @@ __device__ __forceinline__ void count_flags(uint32_t f, long long* cnt) {
 __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) {
   __shared__ SampleSmem samp;
   __shared__ int dec[2];
+  __shared__ float pq[2 * CP_SPEC_MAX_WINDOW];
+  __shared__ float ua[CP_SPEC_MAX_WINDOW], ut[CP_SPEC_MAX_WINDOW + 1];
   __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
   __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
   const int b = blockIdx.x;
@@ -609,12 +667,15 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
     const float* q = r.q + static_cast<size_t>(b) * r.W * r.V;
     const float* p = r.p + static_cast<size_t>(b) * r.R * r.V;
     const int* tc = r.tcode + static_cast<size_t>(b) * r.R;
+    // the round's uniforms, one thread each
+    if (threadIdx.x < gamma) ua[threadIdx.x] = frame_uniform(seed, s + 1 + threadIdx.x, kAccept);
+    if (threadIdx.x >= 16 && threadIdx.x - 16 <= gamma)
+      ut[threadIdx.x - 16] = frame_uniform(seed, s + 1 + (threadIdx.x - 16), kTarget);
+    __syncthreads();
     int n_acc = 0;
-    const int n = accept_scan(
-        gamma, draft, q, p, r.V, r.greedy != 0,
-        [&](int t) { return frame_uniform(seed, s + t, kAccept); },
-        [&](int t) { return frame_uniform(seed, s + t, kTarget); }, [&](int rr) { return tc[rr]; },
-        codes, anear, cnear, &n_acc, samp, dec);
+    const int n = accept_scan(gamma, draft, q, p, r.V, r.greedy != 0, ua, ut,
+                              [&](int rr) { return tc[rr]; }, codes, anear, cnear, &n_acc, samp,
+                              dec, pq);
     __syncthreads();
     for (int t = 1; t <= n; ++t) {
       if (anear[t - 1]) {

@@ -56,6 +56,7 @@ def _create(cfg):
     ("hidden", 100, binding.EUNSUPPORTED, "not tileable"),
     ("max_streams", 0, binding.EINVAL, "non-positive"),
     ("head_dim", 256, binding.EUNSUPPORTED, "head_dim"),
+    ("head_dim", 48, binding.EUNSUPPORTED, "head_dim"),
 ])
 def test_create_validation(field, value, code, msg):
     cfg = binding.make_cfg(synth.config("tiny"))

@@ -14,6 +14,9 @@ constexpr int kRPGHost = 4;   // output widths must be multiples of this
 // or more 16-byte chunks of each row.
 __host__ __device__ constexpr int gemv_rpg(int spt) { return spt >= 3 ? 2 : 4; }
 
+// Matrix-core tiles: 64 activation rows x 64 outputs, K steps of 32.
+constexpr int kMfmaTM = 64, kMfmaTN = 64, kMfmaTK = 32;
+
 enum GemvMode : int {
   kStore = 0,   // Y[m][o] = acc
   kAdd = 1,     // Y[m][o] += acc             (residual add)
@@ -49,6 +52,10 @@ struct GemvArgs {
   int n_heads;          // G-1
   long long head_stride;  // elements per head matrix (V*H)
   float* xnorm_out;     // nullable: normalised rows written here ([M][K])
+  // kHead on the matrix cores: rows grouped by head
+  const int* head_count;  // [n_heads] rows using each head
+  const int* head_rows;   // [n_heads][rows_cap] row indices, stream order
+  int rows_cap;
   // tiling (host-chosen)
   int kt;     // threads covering one row's K (64/128/256)
   int units;  // number of RPG-row output units
@@ -141,9 +148,13 @@ struct RoundArgs {
   uint32_t* tflags;  // [B][R]
 };
 
-// Launchers (kernels.hip).  All asynchronous on `s`.
+// Launchers.  All asynchronous on `s`.
 hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid_x, int grid_y,
                        hipStream_t s);
+hipError_t launch_mfma(int wdtype, int mode, const GemvArgs& a, dim3 grid, hipStream_t s);
+// Per-head row lists of the coming round (draft rows and verify rows).
+hipError_t launch_head_plan(const int* dhead, const int* thead, int B, int W, int R, int n_heads,
+                            int* dcount, int* drows, int* tcount, int* trows, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int rows, int H, float eps,
                                hipStream_t s);

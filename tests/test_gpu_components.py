@@ -26,18 +26,25 @@ def _t(a, dtype=None):
     return (t if dtype is None else t.to(dtype)).cuda()
 
 
-@pytest.mark.parametrize("cid", ["tiny", "qwen3tts"])
+@pytest.mark.parametrize("cid,rows", [("tiny", 6), ("qwen3tts", 8),
+                                      ("tiny", 77), ("qwen3tts", 133),
+                                      ("wide-256", 70)])
 @pytest.mark.parametrize("norm", [0, 1])
-def test_head_logits(cid, norm):
-    log(f"head_logits {cid} norm={norm}")
+def test_head_logits(cid, rows, norm):
+    """Few rows run one GEMV block per row; 32 or more rows are grouped by
+    head into 64-row matrix-core tiles (ragged last tile per head)."""
+    log(f"head_logits {cid} rows={rows} norm={norm}")
     c = synth.config(cid)
     m = oracle_model(cid)
-    h = handle(cid, max_streams=2)
-    rng = np.random.default_rng(10 + len(cid))
-    rows = 2 * max(c["verify_size"], 2)
+    R = max(c["verify_size"], 2)
+    h = handle(cid, max_streams=(rows + R - 1) // R)
+    rng = np.random.default_rng(10 + len(cid) + rows)
     x = rng.standard_normal((rows, c["hidden"])).astype(np.float32)
     heads = rng.integers(1, c["groups"], size=rows).astype(np.int32)
     heads[1] = 0                                   # a skipped row
+    if rows > 64:
+        heads[:70 if rows > 70 else 66] = 2        # one head spans two tiles
+        heads[1] = 0
     out = torch.full((rows, c["vocab"]), 123.0, device="cuda")
     h.head_logits(_t(x), _t(heads), norm, out)
     got = out.cpu().numpy()
@@ -208,14 +215,15 @@ def test_accept_greedy():
         assert tuple(Cd[b, :N[b]]) == rnd.emitted
 
 
-@pytest.mark.parametrize("cid", ["tiny", "qwen3tts"])
-def test_decoder_ragged_blocks_and_truncation(cid):
+@pytest.mark.parametrize("cid,B", [("tiny", 3), ("qwen3tts", 3),
+                                   ("tiny", 24), ("qwen3tts", 24)])
+def test_decoder_ragged_blocks_and_truncation(cid, B):
     """A prefill block, a ragged verify block, then a block that overwrites
-    rejected positions after truncation, for three streams."""
-    log(f"decoder_forward {cid}")
+    rejected positions after truncation, for B streams (stream b follows
+    pattern b % 3).  24 streams put the projections on the matrix cores."""
+    log(f"decoder_forward {cid} B={B}")
     c = synth.config(cid)
     m = oracle_model(cid)
-    B = 3
     R = max(c["verify_size"], 2)
     h = handle(cid, max_streams=B)
     L, G, nkv, d, H = c["layers"], c["groups"], c["kv_heads"], c["head_dim"], \
@@ -250,7 +258,11 @@ def test_decoder_ragged_blocks_and_truncation(cid):
                                            atol=2e-3)
                 assert np.max(np.abs(got[b, r] - ref[r])) < 1e-4
 
-    step([[0, 1], [0, 1], [0, 1]])
-    step([list(range(2, 2 + R)), [2, 3], [2]])
-    # stream 0 keeps positions 0..3, stream 1 keeps 0..3, stream 2 keeps 0..2
-    step([[4, 5], list(range(4, 4 + R)), [3]], trunc=[4, 4, 3])
+    def pattern(rows):
+        return [rows[b % 3] for b in range(B)]
+
+    step(pattern([[0, 1], [0, 1], [0, 1]]))
+    step(pattern([list(range(2, 2 + R)), [2, 3], [2]]))
+    # pattern 0 keeps positions 0..3, pattern 1 keeps 0..3, pattern 2 0..2
+    step(pattern([[4, 5], list(range(4, 4 + R)), [3]]),
+         trunc=pattern([4, 4, 3]))

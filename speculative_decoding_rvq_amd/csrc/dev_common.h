@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace cps {
@@ -122,22 +124,30 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Block barrier ordering LDS accesses only: global stores still in flight
+// are not waited for (the workgroup-scope fence of a full barrier would).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Block-wide reductions over 256 threads; `red` is 4+ words of LDS.  Every
 // thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  __syncthreads();
+  lds_sync();
   if (l == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   v = wave_max_u64(v);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  __syncthreads();
+  lds_sync();
   if (l == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   uint64_t a = red[0] > red[1] ? red[0] : red[1];
   uint64_t b = red[2] > red[3] ? red[2] : red[3];
   return a > b ? a : b;
@@ -145,17 +155,17 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  __syncthreads();
+  lds_sync();
   if (l == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   return umax32(umax32(red[0], red[1]), umax32(red[2], red[3]));
 }
 __device__ __forceinline__ int block_sum_i(int v, int* red) {
   v = wave_sum_i(v);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  __syncthreads();
+  lds_sync();
   if (l == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   return red[0] + red[1] + red[2] + red[3];
 }
 
@@ -164,9 +174,9 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int inc = wave_incl_scan(v);
-  __syncthreads();
+  lds_sync();
   if (l == kWave - 1) red[w] = inc;
-  __syncthreads();
+  lds_sync();
   int base = 0;
   for (int i = 0; i < w; ++i) base += red[i];
   *total = red[0] + red[1] + red[2] + red[3];
@@ -221,87 +231,130 @@ constexpr double kEpsGap = 1e-4;
 constexpr double kEpsCdf = 1e-5;
 constexpr uint32_t kFlagTopk = 1u, kFlagArgmax = 2u, kFlagCdf = 4u, kFlagAccept = 8u;
 
-// LDS scratch the block sampler needs: compacted support of up to V entries.
+// LDS scratch the block sampler needs: compacted support of up to 4096
+// entries (weights, then their running sums).
 struct SampleSmem {
   int idx[4096];
   float w[4096];
-  int red[8];
+  int red[4];
   int result[2];
 };
 
-// Sample(w, u) over a row whose weights are produced by `weight(i)`,
-// i in [0, V), V a multiple of 256: the entries with w_i > 0 in ascending
-// code order, a sequential float32 running sum, t = u * sum, first entry
-// whose running sum exceeds t.  Result for every thread: the code, and the
-// CDF near-tie flag through *flag.  Returns -1 if no weight is positive.
-template <typename WF>
-__device__ int block_sample(WF weight, int V, float u, SampleSmem& sm, bool* flag) {
-  const int per = V / kBlock;
-  const int base = threadIdx.x * per;
+// Wave 0: Sample over the `total` compacted entries of sm (ascending code
+// order).  The running sum is formed once, sequentially in float32 (every
+// lane adds the same values in the same order, 32 entries in registers at a
+// time) and stored over the weights; the first running sum above t = u * sum
+// is then found 64 entries at a time with a ballot.
+__device__ __forceinline__ void wave0_walk(SampleSmem& sm, int total, float u) {
+  const int lane = threadIdx.x;
+  int code = -1, near = 0;
+  if (total > 0) {
+    float carry = 0.0f;
+    for (int c0 = 0; c0 < total; c0 += 32) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(&sm.w[c0 + i]);
+        v[i] = q.x;
+        v[i + 1] = q.y;
+        v[i + 2] = q.z;
+        v[i + 3] = q.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        carry = carry + (c0 + i < total ? v[i] : 0.0f);
+        v[i] = carry;
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < 32; i += 4)
+          *reinterpret_cast<float4*>(&sm.w[c0 + i]) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+      }
+    }
+    const float tot = carry;
+    const float t = u * tot;
+    int pos = -1;
+    for (int c0 = 0; c0 < total; c0 += kWave) {
+      const int i = c0 + lane;
+      const uint64_t m = __ballot(i < total && t < sm.w[i]);
+      if (m != 0) {
+        pos = c0 + __ffsll(static_cast<unsigned long long>(m)) - 1;
+        break;
+      }
+    }
+    const bool found = pos >= 0;
+    if (!found) pos = total - 1;  // t == sum after rounding: the last entry owns the top end
+    const float run = sm.w[pos];
+    const float before = pos > 0 ? sm.w[pos - 1] : 0.0f;
+    const double eps = static_cast<double>(tot) * kEpsCdf;
+    if (found) {
+      const bool lo = pos > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps;
+      const bool hi = pos + 1 < total && fabs(static_cast<double>(run) - static_cast<double>(t)) < eps;
+      near = (lo || hi) ? 1 : 0;
+    } else {
+      near = (total > 1 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps) ? 1 : 0;
+    }
+    code = sm.idx[pos];
+  }
+  if (lane == 0) {
+    sm.result[0] = code;
+    sm.result[1] = near;
+  }
+}
+
+// Sample(w, u) over a row held in registers, thread t owning codes
+// [t*VPT, (t+1)*VPT): the entries with w_i > 0 in ascending code order, a
+// sequential float32 running sum, t = u * sum, the first entry whose running
+// sum exceeds t.  Every thread gets the code (-1 if no weight is positive)
+// and the CDF near-tie flag through *flag.  sm.red must not be read by the
+// caller between two calls; the rest of sm is free once this returns.
+template <int VPT>
+__device__ int sample_regs(const float (&wv)[VPT], float u, SampleSmem& sm, bool* flag) {
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int base = tid * VPT;
   int cnt = 0;
-  for (int j = 0; j < per; ++j) cnt += weight(base + j) > 0.0f ? 1 : 0;
-  int total;
-  int off = block_exclusive_scan(cnt, sm.red, &total);
-  for (int j = 0; j < per; ++j) {
-    const float wv = weight(base + j);
-    if (wv > 0.0f) {
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) cnt += wv[j] > 0.0f ? 1 : 0;
+  const int inc = wave_incl_scan(cnt);
+  if (lane == kWave - 1) sm.red[w] = inc;
+  lds_sync();
+  int off = inc - cnt;
+  for (int i = 0; i < w; ++i) off += sm.red[i];
+  const int total = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    if (wv[j] > 0.0f) {
       sm.idx[off] = base + j;
-      sm.w[off] = wv;
+      sm.w[off] = wv[j];
       ++off;
     }
   }
-  __syncthreads();
-  if (threadIdx.x < kWave) {
-    // wave 0: the running sum is sequential in code order (float32 adds in
-    // one lane); entries are brought in 64 at a time and read with readlane
-    const int lane = threadIdx.x;
-    int code = -1, near = 0;
-    if (total > 0) {
-#pragma clang fp contract(off)
-      float tot = 0.0f;
-      for (int base = 0; base < total; base += kWave) {
-        const float wl = base + lane < total ? sm.w[base + lane] : 0.0f;
-        const int n = min(kWave, total - base);
-#pragma unroll 16
-        for (int i = 0; i < n; ++i) tot = tot + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-      }
-      const float t = u * tot;
-      const double eps = static_cast<double>(tot) * kEpsCdf;
-      float run = 0.0f, before = 0.0f;
-      int pos = total - 1;
-      bool found = false;
-      for (int base = 0; base < total && !found; base += kWave) {
-        const float wl = base + lane < total ? sm.w[base + lane] : 0.0f;
-        const int n = min(kWave, total - base);
-        for (int i = 0; i < n; ++i) {
-          before = run;
-          run = run + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-          if (t < run) {
-            pos = base + i;
-            found = true;
-            break;
-          }
-        }
-      }
-      if (found) {
-        const bool lo = pos > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps;
-        const bool hi = pos + 1 < total && fabs(static_cast<double>(run) - static_cast<double>(t)) < eps;
-        near = (lo || hi) ? 1 : 0;
-      } else {  // t == sum after rounding: the last entry owns the top end
-        near = (total > 1 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps) ? 1 : 0;
-      }
-      code = sm.idx[pos];
-    }
-    if (lane == 0) {
-      sm.result[0] = code;
-      sm.result[1] = near;
-    }
-  }
-  __syncthreads();
+  lds_sync();
+  if (tid < kWave) wave0_walk(sm, total, u);
+  lds_sync();
   *flag = sm.result[1] != 0;
-  const int code = sm.result[0];
-  __syncthreads();
-  return code;
+  return sm.result[0];
+}
+
+// The same over weights produced by `weight(i)`, i in [0, V), V = 256 * 2^i
+// up to 4096.
+template <typename WF>
+__device__ int block_sample(WF weight, int V, float u, SampleSmem& sm, bool* flag) {
+  auto run = [&](auto vpt) {
+    constexpr int VPT = decltype(vpt)::value;
+    float wv[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) wv[j] = weight(threadIdx.x * VPT + j);
+    return sample_regs<VPT>(wv, u, sm, flag);
+  };
+  switch (V / kBlock) {
+    case 1: return run(std::integral_constant<int, 1>{});
+    case 2: return run(std::integral_constant<int, 2>{});
+    case 4: return run(std::integral_constant<int, 4>{});
+    case 8: return run(std::integral_constant<int, 8>{});
+    case 16: return run(std::integral_constant<int, 16>{});
+    default: return -1;
+  }
 }
 
 }  // namespace cps

@@ -117,6 +117,7 @@ size_t plan_ints(const Shape& s) { return 2 * static_cast<size_t>(s.G - 1) * (1 
 // cores (64-row tiles); below it the GEMV streams each weight once per few rows.
 constexpr int kMfmaMinStreams = 8;
 constexpr int kMfmaMinRows = 32;
+constexpr int kFillBlocks = 256;  // one block per compute unit
 
 Layout make_layout(const Shape& s) {
   Layout l{};
@@ -217,8 +218,16 @@ bool mfma_fits(int mode, const GemvArgs& a) {
 int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
   if (a.M <= 0) return CP_SPEC_OK;
   if (mode != kHead && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
-    const int gx = mode == kSwiGLU ? a.N / (kMfmaTN / 2) : a.N / kMfmaTN;
-    CPS_HIP(launch_mfma(h->sh.wdt, mode, a, dim3(gx, (a.M + kMfmaTM - 1) / kMfmaTM), s));
+    // the largest tile that still gives the chip enough blocks
+    const int cols = mode == kSwiGLU ? a.N * 2 : a.N;  // tile columns (gate and up side by side)
+    int tile = kTile64, t = 64;
+    if (a.K % (4 * kMfmaTK) == 0) {
+      if (cols / 64 * ((a.M + 63) / 64) < kFillBlocks) {
+        tile = kTile32, t = 32;
+        if (cols / 32 * ((a.M + 31) / 32) < kFillBlocks) tile = kTile16, t = 16;
+      }
+    }
+    CPS_HIP(launch_mfma(h->sh.wdt, mode, tile, a, dim3(cols / t, (a.M + t - 1) / t), s));
     return CP_SPEC_OK;
   }
   const int vec = h->sh.vec;
@@ -319,8 +328,12 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
   a.n_heads = h->sh.G - 1;
   if (plan && mfma_fits(kHead, a)) {
     a.head_count = plan->count; a.head_rows = plan->rows; a.rows_cap = plan->cap;
-    const dim3 grid(a.N / kMfmaTN, (plan->cap + kMfmaTM - 1) / kMfmaTM, a.n_heads);
-    CPS_HIP(launch_mfma(h->sh.wdt, kHead, a, grid, s));
+    // tiles by the average rows per head
+    const int avg = (M + a.n_heads - 1) / a.n_heads;
+    const bool big = a.N / 64 * ((avg + 63) / 64) * a.n_heads >= kFillBlocks || a.K % (4 * kMfmaTK);
+    const int t = big ? 64 : 32;
+    const dim3 grid(a.N / t, (plan->cap + t - 1) / t, a.n_heads);
+    CPS_HIP(launch_mfma(h->sh.wdt, kHead, big ? kTile64 : kTile32, a, grid, s));
     return CP_SPEC_OK;
   }
   return gemv(h, s, kHead, a);

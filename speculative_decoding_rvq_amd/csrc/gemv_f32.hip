@@ -6,7 +6,7 @@ namespace cps {
 hipError_t launch_gemv_f32(int mode, int mt, const GemvArgs& a, int gx, int gy, hipStream_t s) {
   return launch_gemv_t<float>(mode, mt, a, gx, gy, s);
 }
-hipError_t launch_mfma_f32(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
-  return launch_mfma_t<float>(mode, a, grid, s);
+hipError_t launch_mfma_f32(int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  return launch_mfma_t<float>(mode, tile, a, grid, s);
 }
 }  // namespace cps

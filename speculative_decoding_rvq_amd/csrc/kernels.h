@@ -151,7 +151,10 @@ struct RoundArgs {
 // Launchers.  All asynchronous on `s`.
 hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid_x, int grid_y,
                        hipStream_t s);
-hipError_t launch_mfma(int wdtype, int mode, const GemvArgs& a, dim3 grid, hipStream_t s);
+// tile: kTile64 (64 x 64, LDS-staged), kTile32 / kTile16 (split-K over the
+// block's four waves; K a multiple of 128).
+enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };
+hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
 // Per-head row lists of the coming round (draft rows and verify rows).
 hipError_t launch_head_plan(const int* dhead, const int* thead, int B, int W, int R, int n_heads,
                             int* dcount, int* drows, int* tcount, int* trows, hipStream_t s);

@@ -4,6 +4,7 @@
 
 #include "dev_common.h"
 #include "kernels.h"
+#include "topk_impl.h"
 
 namespace cps {
 
@@ -16,11 +17,12 @@ hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid
                                 : launch_gemv_f32(mode, mt, a, grid_x, grid_y, s);
 }
 
-hipError_t launch_mfma_f32(int mode, const GemvArgs& a, dim3 grid, hipStream_t s);
-hipError_t launch_mfma_bf16(int mode, const GemvArgs& a, dim3 grid, hipStream_t s);
+hipError_t launch_mfma_f32(int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
+hipError_t launch_mfma_bf16(int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
 
-hipError_t launch_mfma(int wdtype, int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
-  return wdtype == CP_SPEC_BF16 ? launch_mfma_bf16(mode, a, grid, s) : launch_mfma_f32(mode, a, grid, s);
+hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  return wdtype == CP_SPEC_BF16 ? launch_mfma_bf16(mode, tile, a, grid, s)
+                                : launch_mfma_f32(mode, tile, a, grid, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -223,168 +225,6 @@ hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int row
 }
 
 // ---------------------------------------------------------------------------
-// Temperature/top-k softmax of one row of logits, and optional sampling.
-//
-// The top-k set is found by an MSB-first radix select on order-preserving
-// 32-bit keys (4 passes of 8 bits, a 256-bin LDS histogram each), which
-// yields the exact k-th largest key; entries above it are in, entries equal
-// to it are admitted in ascending code order until k are taken.  One pass
-// over the row whatever k is.  Probabilities are exp((z - max)/T) / sum on
-// the set, zero elsewhere.  Thread t owns codes [t*VPT, (t+1)*VPT).
-struct TopkSmem {
-  uint32_t hist[256];
-  int sel[2];
-  uint64_t red64[4];
-  uint32_t red32[4];
-  float redf[4];
-  int redi[8];
-  float prow[4096];
-  SampleSmem samp;
-};
-
-struct TopkResult {
-  int code;
-  uint32_t flags;
-};
-
-template <int VPT>
-__device__ TopkResult topk_row(const float* __restrict__ z, int k, float T, bool greedy,
-                               bool do_sample, float u, float* probs, TopkSmem& sm) {
-  constexpr int V = VPT * kBlock;
-  const int tid = threadIdx.x;
-  const int base = tid * VPT;
-  float zv[VPT];
-  uint32_t key[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    zv[j] = z[base + j];
-    key[j] = float_key(zv[j]);
-  }
-  TopkResult res{-1, 0u};
-  if (greedy) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const uint64_t c = (static_cast<uint64_t>(key[j]) << 32) |
-                         static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(base + j));
-      best = c > best ? c : best;
-    }
-    best = block_max_u64(best, sm.red64);
-    const int arg = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
-    uint32_t second = 0;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-      if (base + j != arg) second = key[j] > second ? key[j] : second;
-    second = block_max_u32(second, sm.red32);
-    res.code = arg;
-    if (V > 1) {
-      const double gap = static_cast<double>(key_float(static_cast<uint32_t>(best >> 32))) -
-                         static_cast<double>(key_float(second));
-      if (gap < kEpsGap) res.flags |= kFlagArgmax;
-    }
-    return res;
-  }
-
-  // ---- radix select of the k-th largest key ----
-  bool member[VPT];
-  if (k >= V) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) member[j] = true;
-  } else {
-    uint32_t prefix = 0, pmask = 0;
-    int rem = k;
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      sm.hist[tid] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < VPT; ++j)
-        if ((key[j] & pmask) == prefix) atomicAdd(&sm.hist[(key[j] >> shift) & 255u], 1u);
-      __syncthreads();
-      // thread t looks at digit 255 - t: inclusive count of digits >= it
-      const int c = static_cast<int>(sm.hist[255 - tid]);
-      int total;
-      const int excl = block_exclusive_scan(c, sm.redi, &total);
-      if (excl < rem && excl + c >= rem) {
-        sm.sel[0] = 255 - tid;
-        sm.sel[1] = rem - excl;
-      }
-      __syncthreads();
-      prefix |= static_cast<uint32_t>(sm.sel[0]) << shift;
-      pmask |= 255u << shift;
-      rem = sm.sel[1];
-      __syncthreads();
-    }
-    const uint32_t kth = prefix;
-    // ties at the k-th key: the `rem` lowest codes among them are admitted
-    int eq = 0;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) eq += key[j] == kth ? 1 : 0;
-    int eq_total;
-    int rank = block_exclusive_scan(eq, sm.redi, &eq_total);
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      if (key[j] > kth) {
-        member[j] = true;
-      } else if (key[j] == kth) {
-        member[j] = rank < rem;
-        ++rank;
-      } else {
-        member[j] = false;
-      }
-    }
-    // boundary gap: k-th largest minus the largest logit left out
-    uint32_t out_best = 0;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-      if (!member[j]) out_best = key[j] > out_best ? key[j] : out_best;
-    out_best = block_max_u32(out_best, sm.red32);
-    const double gap = static_cast<double>(key_float(kth)) - static_cast<double>(key_float(out_best));
-    if (gap < kEpsGap) res.flags |= kFlagTopk;
-  }
-
-  // ---- softmax on the set ----
-  uint32_t kmax = 0;
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) kmax = key[j] > kmax ? key[j] : kmax;
-  kmax = block_max_u32(kmax, sm.red32);
-  const float zmax = key_float(kmax);
-  float e[VPT];
-  float part = 0.0f;
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    e[j] = member[j] ? expf((zv[j] - zmax) / T) : 0.0f;
-    part += e[j];
-  }
-  const float Z = block_sum(part, sm.redf);
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const float pj = e[j] / Z;
-    sm.prow[base + j] = pj;
-    if (probs != nullptr) probs[base + j] = pj;
-  }
-  __syncthreads();
-  if (do_sample) {
-    bool near = false;
-    res.code = block_sample([&](int i) { return sm.prow[i]; }, V, u, sm.samp, &near);
-    if (near) res.flags |= kFlagCdf;
-  }
-  return res;
-}
-
-template <typename F>
-__device__ __forceinline__ void dispatch_vpt(int V, F&& f) {
-  switch (V / kBlock) {
-    case 1: f(std::integral_constant<int, 1>{}); break;
-    case 2: f(std::integral_constant<int, 2>{}); break;
-    case 4: f(std::integral_constant<int, 4>{}); break;
-    case 8: f(std::integral_constant<int, 8>{}); break;
-    case 16: f(std::integral_constant<int, 16>{}); break;
-    default: break;
-  }
-}
-
 // Component: n_rows independent rows.
 __global__ __launch_bounds__(kBlock) void topk_rows_kernel(const TopkArgs a) {
   __shared__ TopkSmem sm;

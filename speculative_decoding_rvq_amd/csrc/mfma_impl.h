@@ -38,8 +38,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return u >> 16;
 }
 
-// Output slot n of the launch -> weight row (mode dependent).
-template <typename WT, int MODE>
+// Output slot n of the launch -> weight row (mode dependent).  SwiGLU tiles of
+// TN columns hold TN/2 gate rows then the TN/2 matching up rows.
+template <typename WT, int MODE, int TN = kMfmaTN>
 __device__ __forceinline__ const WT* gemm_weight_row(const GemvArgs& a, const WT* W0, int n) {
   if (MODE == kQKV) {
     const WT* W1 = static_cast<const WT*>(a.W1);
@@ -50,9 +51,9 @@ __device__ __forceinline__ const WT* gemm_weight_row(const GemvArgs& a, const WT
   }
   if (MODE == kSwiGLU) {
     const WT* W1 = static_cast<const WT*>(a.W1);
-    const int tile = n / kTN, c = n % kTN;
-    const int f = tile * (kTN / 2) + (c % (kTN / 2));
-    return (c < kTN / 2 ? W0 : W1) + static_cast<size_t>(f) * a.K;
+    const int tile = n / TN, c = n % TN;
+    const int f = tile * (TN / 2) + (c % (TN / 2));
+    return (c < TN / 2 ? W0 : W1) + static_cast<size_t>(f) * a.K;
   }
   return W0 + static_cast<size_t>(n) * a.K;
 }
@@ -293,6 +294,257 @@ hipError_t launch_mfma_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) 
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K variant for problems with few output tiles (small hidden sizes, few
+// rows per head): a block owns a (16 FM) x (16 FN) tile and its four waves
+// take a quarter of K each, reading their fragments straight from global
+// memory (lane l: row l % 16, k = 8 (l / 16) .. +7 of each 32-wide chunk, the
+// same k assignment as above) with up to U chunks in flight.  The partial
+// tiles and the rows' partial sums of squares meet in LDS and are added in a
+// fixed order, so the result does not depend on timing.
+template <typename WT, int MODE, int FM, int FN>
+__global__ __launch_bounds__(kBlock) void mfma_splitk_kernel(const GemvArgs a) {
+  constexpr bool kBf16 = sizeof(WT) == 2;
+  constexpr int TM = 16 * FM, TN = 16 * FN;
+  constexpr int U = FM + FN >= 3 ? 2 : 4;
+  constexpr int kWaves = kBlock / kWave;
+  __shared__ float part[kWaves][TM][TN + 1];
+  __shared__ float ssq_s[kWaves][TM];
+  __shared__ float rinv_s[TM];
+  __shared__ int rows_s[TM];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * TN;
+
+  const WT* W0 = static_cast<const WT*>(a.W0);
+  int count;
+  if (MODE == kHead) {
+    const int j = blockIdx.z;
+    count = a.head_count[j] - blockIdx.y * TM;
+    if (count <= 0) return;
+    count = min(count, TM);
+    if (tid < TM)
+      rows_s[tid] = tid < count ? a.head_rows[static_cast<size_t>(j) * a.rows_cap + blockIdx.y * TM + tid] : -1;
+    W0 = W0 + static_cast<size_t>(j) * static_cast<size_t>(a.head_stride);
+  } else {
+    const int m0 = blockIdx.y * TM;
+    count = min(TM, a.M - m0);
+    if (tid < TM) rows_s[tid] = tid < count ? m0 + tid : -1;
+  }
+  __syncthreads();
+
+  const float* xr[FM];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    const int row = rows_s[16 * f + li];
+    xr[f] = row >= 0 ? a.X + static_cast<size_t>(row / a.xdiv) * a.ldx : nullptr;
+  }
+  const WT* wr[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) wr[f] = gemm_weight_row<WT, MODE, TN>(a, W0, n0 + 16 * f + li);
+  const bool norm = a.norm_g != nullptr;
+
+  const int kw = a.K / kWaves;            // this wave's K range
+  const int kbeg = wave * kw + 8 * lg;    // lane's first k
+  const int nch = kw / kTK;
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float ss[FM];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) ss[f] = 0.0f;
+
+  using WV = typename std::conditional<kBf16, uint4, float4>::type;
+  constexpr int kWV = kBf16 ? 1 : 2;  // 16-byte weight loads per chunk and fragment
+  for (int c0 = 0; c0 < nch; c0 += U) {
+    float4 xa[U][FM][2];
+    WV wb[U][FN][kWV];
+    float4 ga[U][2];
+    // ---- issue every load of the group ----
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u >= nch) break;
+      const int k = kbeg + (c0 + u) * kTK;
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int v = 0; v < kWV; ++v) wb[u][f][v] = *reinterpret_cast<const WV*>(wr[f] + k + v * (8 / kWV));
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        if (xr[f]) {
+          xa[u][f][0] = *reinterpret_cast<const float4*>(xr[f] + k);
+          xa[u][f][1] = *reinterpret_cast<const float4*>(xr[f] + k + 4);
+        } else {
+          xa[u][f][0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          xa[u][f][1] = xa[u][f][0];
+        }
+      }
+      if (norm) {
+        ga[u][0] = *reinterpret_cast<const float4*>(a.norm_g + k);
+        ga[u][1] = *reinterpret_cast<const float4*>(a.norm_g + k + 4);
+      }
+    }
+    // ---- MFMAs of the group ----
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u >= nch) break;
+      const float g[8] = {ga[u][0].x, ga[u][0].y, ga[u][0].z, ga[u][0].w,
+                          ga[u][1].x, ga[u][1].y, ga[u][1].z, ga[u][1].w};
+      float x[FM][8];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const float4 p0 = xa[u][f][0], p1 = xa[u][f][1];
+        x[f][0] = p0.x; x[f][1] = p0.y; x[f][2] = p0.z; x[f][3] = p0.w;
+        x[f][4] = p1.x; x[f][5] = p1.y; x[f][6] = p1.z; x[f][7] = p1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ss[f] += x[f][e] * x[f][e];
+          if (norm) x[f][e] *= g[e];
+        }
+      }
+      if constexpr (kBf16) {
+        bf16x8 ap[FM][3];
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t h = bf16_rne_bits(x[f][e]);
+            const float r1 = x[f][e] - __uint_as_float(h << 16);
+            const uint32_t mm = bf16_rne_bits(r1);
+            const float r2 = r1 - __uint_as_float(mm << 16);
+            ap[f][0][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(h));
+            ap[f][1][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(mm));
+            ap[f][2][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(__float_as_uint(r2) >> 16));
+          }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const bf16x8 bw = __builtin_bit_cast(bf16x8, wb[u][fn][0]);
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[fm][pc], bw, acc[fm][fn], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const float4 q0 = wb[u][fn][0], q1 = wb[u][fn][1];
+          const float w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[fm][s], w[s], acc[fm][fn], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- partial tiles and sums of squares -> LDS ----
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave][16 * fm + 4 * lg + i][16 * fn + li] = acc[fm][fn][i];
+  if (norm) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      float t = ss[f];
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      if (lg == 0) ssq_s[wave][16 * f + li] = t;
+    }
+  }
+  __syncthreads();
+  if (norm && tid < TM) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += ssq_s[w][tid];
+    rinv_s[tid] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+  }
+  __syncthreads();
+
+  if (MODE == kHead && norm && a.xnorm_out != nullptr && blockIdx.x == 0) {
+    for (int idx = tid; idx < count * a.K; idx += kBlock) {
+      const int r = idx / a.K, k = idx % a.K;
+      const int row = rows_s[r];
+      a.xnorm_out[static_cast<size_t>(row) * a.K + k] =
+          a.X[static_cast<size_t>(row / a.xdiv) * a.ldx + k] * a.norm_g[k] * rinv_s[r];
+    }
+  }
+  auto tile_val = [&](int r, int c) {
+    float v = part[0][r][c];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += part[w][r][c];
+    return norm ? v * rinv_s[r] : v;
+  };
+  if (MODE == kSwiGLU) {
+    for (int idx = tid; idx < TM * (TN / 2); idx += kBlock) {
+      const int r = idx / (TN / 2), c = idx % (TN / 2);
+      const int row = rows_s[r];
+      if (row < 0) continue;
+      const float g = tile_val(r, c), u = tile_val(r, c + TN / 2);
+      const float sg = g / (1.0f + expf(-g));
+      a.Y[static_cast<size_t>(row) * a.ldy + blockIdx.x * (TN / 2) + c] = sg * u;
+    }
+    return;
+  }
+  for (int idx = tid; idx < TM * TN; idx += kBlock) {
+    const int r = idx / TN, c = idx % TN;
+    const int row = rows_s[r];
+    if (row < 0) continue;
+    const float val = tile_val(r, c);
+    const int o = n0 + c;
+    if (MODE == kAdd) {
+      a.Y[static_cast<size_t>(row) * a.ldy + o] += val;
+    } else if (MODE == kHead) {
+      a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+    } else if (MODE == kQKV) {
+      if (o < a.qdim) {
+        a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+      } else {
+        const int pp = a.pos[row];
+        if (pp >= 0 && pp < a.kv_positions) {
+          const int b = row / a.rows_per_stream;
+          float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
+          const int oo = o - a.qdim;
+          if (oo < a.kvdim) base[oo] = val;
+          else base[a.kv_vo + (oo - a.kvdim)] = val;
+        }
+      }
+    }
+  }
+}
+
+template <typename WT, int FM, int FN>
+hipError_t launch_splitk_mode(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  switch (mode) {
+    case kAdd: hipLaunchKernelGGL((mfma_splitk_kernel<WT, kAdd, FM, FN>), grid, dim3(kBlock), 0, s, a); break;
+    case kSwiGLU: hipLaunchKernelGGL((mfma_splitk_kernel<WT, kSwiGLU, FM, FN>), grid, dim3(kBlock), 0, s, a); break;
+    case kQKV: hipLaunchKernelGGL((mfma_splitk_kernel<WT, kQKV, FM, FN>), grid, dim3(kBlock), 0, s, a); break;
+    case kHead: hipLaunchKernelGGL((mfma_splitk_kernel<WT, kHead, FM, FN>), grid, dim3(kBlock), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// tile: 0 = 64 x 64 LDS-staged, 1 = 32 x 32 split-K, 2 = 16 x 16 split-K
+template <typename WT>
+hipError_t launch_mfma_t(int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  switch (tile) {
+    case 0: return launch_mfma_t<WT>(mode, a, grid, s);
+    case 1: return launch_splitk_mode<WT, 2, 2>(mode, a, grid, s);
+    case 2: return launch_splitk_mode<WT, 1, 1>(mode, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace cps

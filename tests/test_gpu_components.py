@@ -28,11 +28,12 @@ def _t(a, dtype=None):
 
 @pytest.mark.parametrize("cid,rows", [("tiny", 6), ("qwen3tts", 8),
                                       ("tiny", 77), ("qwen3tts", 133),
-                                      ("wide-256", 70)])
+                                      ("wide-256", 70), ("tiny", 4100)])
 @pytest.mark.parametrize("norm", [0, 1])
 def test_head_logits(cid, rows, norm):
     """Few rows run one GEMV block per row; 32 or more rows are grouped by
-    head into 64-row matrix-core tiles (ragged last tile per head)."""
+    head into matrix-core tiles (ragged last tile per head): 32 x 32
+    split-K tiles for few rows per head, 64 x 64 tiles for many."""
     log(f"head_logits {cid} rows={rows} norm={norm}")
     c = synth.config(cid)
     m = oracle_model(cid)
@@ -62,13 +63,24 @@ def test_head_logits(cid, rows, norm):
 
 
 def _logit_rows(V, n, rng, ties=False):
+    """Rows of N(0, 0.4) logits.  ties=True / "ties": exact ties straddling
+    the top-k boundary and the maximum; "mass": a third of the row tied at
+    the boundary value; "outlier": one logit far above the rest, so that the
+    rest crowd into one value bin; both of the last two exceed the 256
+    entries the boundary bin is ranked by directly (for V >= 1024)."""
     z = (rng.standard_normal((n, V)) * 0.4).astype(np.float32)
-    if ties:
-        # exact ties straddling the top-k boundary and the maximum
+    if ties is True or ties == "ties":
         for r in range(n):
             order = np.argsort(-z[r])
             z[r, order[45:55]] = z[r, order[49]]
             z[r, order[1]] = z[r, order[0]]
+    elif ties == "mass":
+        for r in range(n):
+            order = np.argsort(-z[r])
+            z[r, order[30:30 + V // 3]] = z[r, order[40]]
+    elif ties == "outlier":
+        z[:, 5] = 3.0e4
+        z[1, :] = 1.0                              # one value everywhere
     return z
 
 
@@ -78,7 +90,7 @@ def _logit_rows(V, n, rng, ties=False):
     ("qwen3tts", {"top_k": 1}),           # k = 1: a point mass
     ("qwen3tts", {"temperature": 1.7, "top_k": 333}),
 ])
-@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("ties", [False, True, "mass", "outlier"])
 def test_topk_sample(cid, over, ties):
     log(f"topk_sample {cid} {over} ties={ties}")
     c = synth.config(cid)
@@ -216,11 +228,13 @@ def test_accept_greedy():
 
 
 @pytest.mark.parametrize("cid,B", [("tiny", 3), ("qwen3tts", 3),
-                                   ("tiny", 24), ("qwen3tts", 24)])
+                                   ("tiny", 24), ("qwen3tts", 24),
+                                   ("tiny", 400)])
 def test_decoder_ragged_blocks_and_truncation(cid, B):
     """A prefill block, a ragged verify block, then a block that overwrites
     rejected positions after truncation, for B streams (stream b follows
-    pattern b % 3).  24 streams put the projections on the matrix cores."""
+    pattern b % 3).  24 streams put the projections on the split-K matrix-core
+    tiles, 400 tiny streams on the 64 x 64 tiles."""
     log(f"decoder_forward {cid} B={B}")
     c = synth.config(cid)
     m = oracle_model(cid)

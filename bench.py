@@ -160,7 +160,7 @@ def main():
     ap.add_argument("--workload", default="qwen3tts",
                     help="one of synth.WORKLOADS")
     ap.add_argument("--frames", type=int, default=None)
-    ap.add_argument("--cpu-frames", type=int, default=24)
+    ap.add_argument("--cpu-frames", type=int, default=160)
     ap.add_argument("--no-extra", action="store_true",
                     help="only the main workload (no AR / 64-stream / CPU legs)")
     args = ap.parse_args()

@@ -309,7 +309,7 @@ __device__ __forceinline__ void wave0_walk(SampleSmem& sm, int total, float u) {
 // and the CDF near-tie flag through *flag.  sm.red must not be read by the
 // caller between two calls; the rest of sm is free once this returns.
 template <int VPT>
-__device__ int sample_regs(const float (&wv)[VPT], float u, SampleSmem& sm, bool* flag) {
+__device__ __forceinline__ int sample_regs(const float (&wv)[VPT], float u, SampleSmem& sm, bool* flag) {
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int base = tid * VPT;
   int cnt = 0;

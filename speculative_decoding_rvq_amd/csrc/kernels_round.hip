@@ -235,7 +235,8 @@ __global__ __launch_bounds__(kBlock) void topk_rows_kernel(const TopkArgs a) {
   const float u = samp ? a.u[r] : 0.0f;
   TopkResult res{-1, 0u};
   dispatch_vpt(a.V, [&](auto vpt) {
-    res = topk_row<decltype(vpt)::value>(z, a.k, a.T, a.greedy != 0, samp, u, pr, sm);
+    float pvd[decltype(vpt)::value];
+    res = topk_row<decltype(vpt)::value>(z, a.k, a.T, a.greedy != 0, samp, u, pr, sm, pvd);
   });
   if (threadIdx.x == 0) {
     if (a.codes) a.codes[r] = res.code;
@@ -339,8 +340,9 @@ __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a)
     for (int r = 0; r <= gamma; ++r) {
       TopkResult res{-1, 0u};
       dispatch_vpt(V, [&](auto vpt) {
-        res = topk_row<decltype(vpt)::value>(p + static_cast<size_t>(r) * V, 1, 1.0f, true, false,
-                                             0.0f, nullptr, tsm);
+        float pvd[decltype(vpt)::value];
+    res = topk_row<decltype(vpt)::value>(p + static_cast<size_t>(r) * V, 1, 1.0f, true, false,
+                                             0.0f, nullptr, tsm, pvd);
       });
       if (threadIdx.x == 0) targ[r] = res.code;
       __syncthreads();
@@ -452,8 +454,9 @@ __global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
   const float u = frame_uniform(seed, st.s + t, kDraft);
   TopkResult res{-1, 0u};
   dispatch_vpt(r.V, [&](auto vpt) {
+    float pvd[decltype(vpt)::value];
     res = topk_row<decltype(vpt)::value>(r.dlogits + row * r.V, r.top_k, r.T, r.greedy != 0,
-                                         r.greedy == 0, u, r.q + row * r.V, sm);
+                                         r.greedy == 0, u, r.q + row * r.V, sm, pvd);
   });
   if (threadIdx.x == 0) {
     r.dcode[row] = res.code;
@@ -468,21 +471,96 @@ hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Target distributions p_r of every verify row that has a head.
+// Target distribution p_r of every verify row that has a head, and the
+// row's share of the acceptance step, all rows of all streams in parallel:
+//   row r < gamma scores draft offset t = r+1: accept d_t iff
+//     U(s+t, accept) < p_r(d_t) / q_t(d_t); if not, the row draws its
+//     residual sample norm(max(0, p_r - q_t)) with U(s+t, target);
+//   row gamma draws the bonus from p_gamma with U(s+gamma+1, target);
+//   prefill row 1 draws c_1 from p_1 with U(1, target).
+// Each row's outcome depends on that row alone, so the sequential scan
+// reduces to "first rejected offset" in the accept kernel.  tcode holds the
+// draft code (accepted) or the row's sample; tflags the row's top-k / argmax
+// flags, its accept-test and CDF near ties, and kRowAccepted.
+constexpr uint32_t kRowAccepted = 1u << 8;
+
 __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) {
   __shared__ TopkSmem sm;
+  __shared__ float pq_s[2];
   const int rr = blockIdx.x, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.R + rr;
   if (r.thead[row] <= 0) return;
-  TopkResult res{-1, 0u};
-  dispatch_vpt(r.V, [&](auto vpt) {
-    res = topk_row<decltype(vpt)::value>(r.tlogits + row * r.V, r.top_k, r.T, r.greedy != 0, false,
-                                         0.0f, r.greedy ? nullptr : r.p + row * r.V, sm);
-  });
-  if (threadIdx.x == 0) {
-    r.tcode[row] = res.code;
-    r.tflags[row] = res.flags;
+  const float* z = r.tlogits + row * r.V;
+  if (r.greedy) {
+    TopkResult res{-1, 0u};
+    dispatch_vpt(r.V, [&](auto vpt) {
+      float pvd[decltype(vpt)::value];
+    res = topk_row<decltype(vpt)::value>(z, 1, 1.0f, true, false, 0.0f, nullptr, sm, pvd);
+    });
+    if (threadIdx.x == 0) {
+      r.tcode[row] = res.code;
+      r.tflags[row] = res.flags;
+    }
+    return;
   }
+  const StreamState st = r.st[b];
+  const bool spec = st.mode == kModeSpec;
+  const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
+  const int depth = spec ? st.s + 1 + rr : 1;
+  dispatch_vpt(r.V, [&](auto vpt) {
+    constexpr int VPT = decltype(vpt)::value;
+    const int base = threadIdx.x * VPT;
+    // loads that do not wait for the softmax
+    float qv[VPT];
+    int d = -1;
+    if (test) {
+      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + rr) * r.V;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
+      d = r.dcode[static_cast<size_t>(b) * r.W + rr];
+    }
+    const uint64_t seed = r.call->seeds[static_cast<size_t>(st.f) * r.call->B + b];
+    float pv[VPT];
+    const TopkResult res = topk_row<VPT>(z, r.top_k, r.T, false, false, 0.0f, nullptr, sm, pv);
+    uint32_t flags = res.flags & (kFlagTopk | kFlagArgmax);
+    int code;
+    bool near = false;
+    if (test) {
+      if (threadIdx.x == 0) {
+        pq_s[0] = 0.0f;  // a code outside [0, V) is rejected
+        pq_s[1] = 1.0f;
+      }
+      lds_sync();
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        if (base + j == d) {
+          pq_s[0] = pv[j];
+          pq_s[1] = qv[j];
+        }
+      }
+      lds_sync();
+      const float ratio = pq_s[0] / pq_s[1];
+      const float ua = frame_uniform(seed, depth, kAccept);
+      if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) flags |= kFlagAccept;
+      if (ua < ratio) {
+        code = d;
+        flags |= kRowAccepted;
+      } else {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) qv[j] = fmaxf(pv[j] - qv[j], 0.0f);  // the residual
+        const float ut = frame_uniform(seed, depth, kTarget);
+        code = sample_regs<VPT>(qv, ut, sm.samp, &near);
+        if (code < 0) code = sample_regs<VPT>(pv, ut, sm.samp, &near);
+      }
+    } else {
+      code = sample_regs<VPT>(pv, frame_uniform(seed, depth, kTarget), sm.samp, &near);
+    }
+    if (near) flags |= kFlagCdf;
+    if (threadIdx.x == 0) {
+      r.tcode[row] = code;
+      r.tflags[row] = flags;
+    }
+  });
 }
 
 hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s) {
@@ -497,87 +575,74 @@ __device__ __forceinline__ void count_flags(uint32_t f, long long* cnt) {
   if (f & kFlagAccept) ++cnt[3];
 }
 
+__device__ __forceinline__ void add_near_ties(cp_spec_stats* s, const long long* nt) {
+  if (nt[0]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_topk), static_cast<unsigned long long>(nt[0]));
+  if (nt[1]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_argmax), static_cast<unsigned long long>(nt[1]));
+  if (nt[2]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_cdf), static_cast<unsigned long long>(nt[2]));
+  if (nt[3]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_accept), static_cast<unsigned long long>(nt[3]));
+}
+
 // Accept, commit, truncate, and set up the stream's next round (or frame).
+// The rows' outcomes come from the target kernel: n = first rejected offset
+// (or gamma + 1), committed codes = the accepted drafts, then row n-1's
+// sample.  Greedy: accept while d_t equals row t-1's argmax.
 __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) {
-  __shared__ SampleSmem samp;
-  __shared__ int dec[2];
-  __shared__ float pq[2 * CP_SPEC_MAX_WINDOW];
-  __shared__ float ua[CP_SPEC_MAX_WINDOW], ut[CP_SPEC_MAX_WINDOW + 1];
-  __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
-  __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
+  __shared__ int sh_n;
   const int b = blockIdx.x;
   StreamState st = r.st[b];
   if (st.mode == kModeDone) return;
   const CallDesc c = *r.call;
   const size_t fb = static_cast<size_t>(st.f) * c.B + b;
-  const uint64_t seed = c.seeds[fb];
   int* out = c.out_codes + fb * r.G;
-  long long nt[4] = {0, 0, 0, 0};  // topk, argmax, cdf, accept near ties
-  if (threadIdx.x <= CP_SPEC_MAX_WINDOW) {
-    anear[threadIdx.x] = 0;
-    cnear[threadIdx.x] = 0;
-  }
-  __syncthreads();
-
+  const size_t rb = static_cast<size_t>(b) * r.R;
   if (st.mode == kModePrefill) {
-    const size_t row = static_cast<size_t>(b) * r.R + 1;
-    int c1;
-    uint32_t f = r.tflags[row];
-    if (r.greedy) {
-      c1 = r.tcode[row];
-    } else {
-      bool near = false;
-      const float* pr = r.p + row * r.V;
-      c1 = block_sample([&](int i) { return pr[i]; }, r.V, frame_uniform(seed, 1, kTarget), samp,
-                        &near);
-      if (near) f |= kFlagCdf;
+    if (threadIdx.x == 0) {
+      long long nt[4] = {0, 0, 0, 0};
+      const uint32_t f = r.tflags[rb + 1] & ~kRowAccepted;
+      count_flags(f, nt);
+      if (f) st.flags |= 1u << 1;
+      out[1] = r.tcode[rb + 1];
+      if (c.stats) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->prefill_passes), 1ull);
+        add_near_ties(c.stats, nt);
+      }
+      sh_n = 1;
     }
-    count_flags(f, nt);
-    if (f) st.flags |= 1u << 1;
-    if (threadIdx.x == 0) out[1] = c1;
-    const float* src = r.Hout + row * r.H;
-    float* dst = r.hstate + static_cast<size_t>(b) * r.H;
-    for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = src[i];
     st.s = 1;
-    if (threadIdx.x == 0 && c.stats) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->prefill_passes), 1ull);
   } else {
     const int s = st.s, gamma = st.gamma;
-    for (int t = 1; t <= gamma; ++t) {
-      const uint32_t f = r.dflags[static_cast<size_t>(b) * r.W + t - 1];
-      count_flags(f, nt);
-      if (f) st.flags |= 1u << (s + t);
-    }
-    for (int rr = 0; rr <= gamma; ++rr) {
-      const uint32_t f = r.tflags[static_cast<size_t>(b) * r.R + rr];
-      count_flags(f, nt);
-      if (f) st.flags |= 1u << (s + 1 + rr);
-    }
-    const int* draft = r.dcode + static_cast<size_t>(b) * r.W;
-    const float* q = r.q + static_cast<size_t>(b) * r.W * r.V;
-    const float* p = r.p + static_cast<size_t>(b) * r.R * r.V;
-    const int* tc = r.tcode + static_cast<size_t>(b) * r.R;
-    // the round's uniforms, one thread each
-    if (threadIdx.x < gamma) ua[threadIdx.x] = frame_uniform(seed, s + 1 + threadIdx.x, kAccept);
-    if (threadIdx.x >= 16 && threadIdx.x - 16 <= gamma)
-      ut[threadIdx.x - 16] = frame_uniform(seed, s + 1 + (threadIdx.x - 16), kTarget);
-    __syncthreads();
-    int n_acc = 0;
-    const int n = accept_scan(gamma, draft, q, p, r.V, r.greedy != 0, ua, ut,
-                              [&](int rr) { return tc[rr]; }, codes, anear, cnear, &n_acc, samp,
-                              dec, pq);
-    __syncthreads();
-    for (int t = 1; t <= n; ++t) {
-      if (anear[t - 1]) {
-        ++nt[3];
-        st.flags |= 1u << (s + t);
-      }
-      if (cnear[t - 1]) {
-        ++nt[2];
-        st.flags |= 1u << (s + t);
-      }
-    }
     if (threadIdx.x == 0) {
-      for (int t = 0; t < n; ++t) out[s + 1 + t] = codes[t];
+      long long nt[4] = {0, 0, 0, 0};
+      const int* draft = r.dcode + static_cast<size_t>(b) * r.W;
+      for (int t = 1; t <= gamma; ++t) {
+        const uint32_t f = r.dflags[static_cast<size_t>(b) * r.W + t - 1];
+        count_flags(f, nt);
+        if (f) st.flags |= 1u << (s + t);
+      }
+      for (int i = 0; i <= gamma; ++i) {
+        const uint32_t f = r.tflags[rb + i] & (kFlagTopk | kFlagArgmax);
+        count_flags(f, nt);
+        if (f) st.flags |= 1u << (s + 1 + i);
+      }
+      int n_acc = 0;
+      if (r.greedy) {
+        while (n_acc < gamma && draft[n_acc] == r.tcode[rb + n_acc]) ++n_acc;
+      } else {
+        while (n_acc < gamma && (r.tflags[rb + n_acc] & kRowAccepted)) ++n_acc;
+        for (int t = 1; t <= min(n_acc + 1, gamma); ++t) {
+          if (r.tflags[rb + t - 1] & kFlagAccept) {
+            ++nt[3];
+            st.flags |= 1u << (s + t);
+          }
+        }
+        if (r.tflags[rb + n_acc] & kFlagCdf) {
+          ++nt[2];
+          st.flags |= 1u << (s + n_acc + 1);
+        }
+      }
+      const int n = n_acc + 1;
+      for (int t = 0; t < n_acc; ++t) out[s + 1 + t] = draft[t];
+      out[s + n] = r.tcode[rb + n_acc];
       if (c.stats) {
         atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->rounds), 1ull);
         for (int t = 1; t <= gamma; ++t) {
@@ -585,18 +650,19 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
           if (t <= n_acc) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->accepted[t - 1]), 1ull);
         }
         if (n_acc == gamma) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->bonus), 1ull);
+        add_near_ties(c.stats, nt);
       }
+      sh_n = n;
     }
-    const float* src = r.Hout + (static_cast<size_t>(b) * r.R + (n - 1)) * r.H;
+    __syncthreads();
+    st.s = s + sh_n;
+  }
+  __syncthreads();
+  {
+    const int n = sh_n;  // h_{s+n} = output row n - 1 (prefill: row 1)
+    const float* src = r.Hout + (rb + n - (st.mode == kModePrefill ? 0 : 1)) * r.H;
     float* dst = r.hstate + static_cast<size_t>(b) * r.H;
     for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = src[i];
-    st.s = s + n;
-  }
-  if (threadIdx.x == 0 && c.stats) {
-    if (nt[0]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_topk), static_cast<unsigned long long>(nt[0]));
-    if (nt[1]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_argmax), static_cast<unsigned long long>(nt[1]));
-    if (nt[2]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_cdf), static_cast<unsigned long long>(nt[2]));
-    if (nt[3]) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->near_tie_accept), static_cast<unsigned long long>(nt[3]));
   }
   __syncthreads();
 

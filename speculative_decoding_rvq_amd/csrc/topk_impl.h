@@ -103,9 +103,11 @@ __device__ void radix_members(const uint32_t* key, int k, bool* member, TopkSmem
   }
 }
 
+// pv receives the thread's VPT probabilities (left unset when greedy).
 template <int VPT>
-__device__ TopkResult topk_row(const float* __restrict__ z, int k, float T, bool greedy,
-                               bool do_sample, float u, float* probs, TopkSmem& sm) {
+__device__ __forceinline__ TopkResult topk_row(const float* __restrict__ z, int k, float T,
+                                               bool greedy, bool do_sample, float u, float* probs,
+                                               TopkSmem& sm, float (&pv)[VPT]) {
   constexpr int V = VPT * kBlock;
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid % kWave;
@@ -285,7 +287,6 @@ __device__ TopkResult topk_row(const float* __restrict__ z, int k, float T, bool
     const double gap = static_cast<double>(key_float(kth)) - static_cast<double>(key_float(out_best));
     if (gap < kEpsGap) res.flags |= kFlagTopk;
   }
-  float pv[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) pv[j] = e[j] / Z;
   if (do_sample) {

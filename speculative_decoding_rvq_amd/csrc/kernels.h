@@ -104,7 +104,8 @@ struct StreamState {
   int gamma;   // drafts in the coming round
   int mode;    // kModePrefill / kModeSpec / kModeDone
   uint32_t flags;
-  int pad[3];
+  int last;                   // c_s, the last committed code
+  uint32_t seed_lo, seed_hi;  // the frame's Philox key
 };
 enum { kModePrefill = 0, kModeSpec = 1, kModeDone = 2 };
 

@@ -396,6 +396,14 @@ __device__ __forceinline__ void embed_row(const RoundArgs& r, int table, int cod
   }
 }
 
+__device__ __forceinline__ uint64_t frame_seed(const StreamState& st) {
+  return (static_cast<uint64_t>(st.seed_hi) << 32) | st.seed_lo;
+}
+__device__ __forceinline__ void set_frame_seed(StreamState& st, uint64_t seed) {
+  st.seed_lo = static_cast<uint32_t>(seed);
+  st.seed_hi = static_cast<uint32_t>(seed >> 32);
+}
+
 // Prefill of frame f for stream b: rows [h_frame, E_0[c_0]] at positions 0, 1
 // and head 1 on row 1.
 __device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int f) {
@@ -424,6 +432,7 @@ __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, c
   if (c.F > 0) {
     setup_prefill(r, c, b, 0);
     st.mode = kModePrefill;
+    set_frame_seed(st, c.seeds[b]);
   } else {
     st.mode = kModeDone;
     if (threadIdx.x == 0) {
@@ -447,22 +456,26 @@ hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t 
 __global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
   __shared__ TopkSmem sm;
   const int t = blockIdx.x + 1, b = blockIdx.y;
-  const StreamState st = r.st[b];
-  if (st.mode != kModeSpec || t > st.gamma) return;
-  const uint64_t seed = r.call->seeds[static_cast<size_t>(st.f) * r.call->B + b];
   const size_t row = static_cast<size_t>(b) * r.W + (t - 1);
-  const float u = frame_uniform(seed, st.s + t, kDraft);
-  TopkResult res{-1, 0u};
   dispatch_vpt(r.V, [&](auto vpt) {
-    float pvd[decltype(vpt)::value];
-    res = topk_row<decltype(vpt)::value>(r.dlogits + row * r.V, r.top_k, r.T, r.greedy != 0,
-                                         r.greedy == 0, u, r.q + row * r.V, sm, pvd);
+    constexpr int VPT = decltype(vpt)::value;
+    float zv[VPT];
+    load_row<VPT>(r.dlogits + row * r.V, zv);  // before the state: the row always exists
+    const StreamState st = r.st[b];
+    if (st.mode != kModeSpec) return;
+    // verify row 0 = E_s[c_s], gathered while the draft rows are sampled
+    if (t == 1) embed_row(r, st.s, st.last, r.X + static_cast<size_t>(b) * r.R * r.H);
+    if (t > st.gamma) return;
+    const float u = frame_uniform(frame_seed(st), st.s + t, kDraft);
+    float pv[VPT];
+    const TopkResult res = topk_regs<VPT>(zv, r.top_k, r.T, r.greedy != 0, r.greedy == 0, u,
+                                          r.q + row * r.V, sm, pv);
+    if (threadIdx.x == 0) {
+      r.dcode[row] = res.code;
+      r.dflags[row] = res.flags;
+    }
+    embed_row(r, st.s + t, res.code, r.X + (static_cast<size_t>(b) * r.R + t) * r.H);
   });
-  if (threadIdx.x == 0) {
-    r.dcode[row] = res.code;
-    r.dflags[row] = res.flags;
-  }
-  embed_row(r, st.s + t, res.code, r.X + (static_cast<size_t>(b) * r.R + t) * r.H);
 }
 
 hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
@@ -489,27 +502,25 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
   __shared__ float pq_s[2];
   const int rr = blockIdx.x, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.R + rr;
-  if (r.thead[row] <= 0) return;
-  const float* z = r.tlogits + row * r.V;
-  if (r.greedy) {
-    TopkResult res{-1, 0u};
-    dispatch_vpt(r.V, [&](auto vpt) {
-      float pvd[decltype(vpt)::value];
-    res = topk_row<decltype(vpt)::value>(z, 1, 1.0f, true, false, 0.0f, nullptr, sm, pvd);
-    });
-    if (threadIdx.x == 0) {
-      r.tcode[row] = res.code;
-      r.tflags[row] = res.flags;
-    }
-    return;
-  }
-  const StreamState st = r.st[b];
-  const bool spec = st.mode == kModeSpec;
-  const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
-  const int depth = spec ? st.s + 1 + rr : 1;
   dispatch_vpt(r.V, [&](auto vpt) {
     constexpr int VPT = decltype(vpt)::value;
     const int base = threadIdx.x * VPT;
+    float zv[VPT];
+    load_row<VPT>(r.tlogits + row * r.V, zv);  // before the row's head: the row always exists
+    if (r.thead[row] <= 0) return;
+    if (r.greedy) {
+      float pvd[VPT];
+      const TopkResult res = topk_regs<VPT>(zv, 1, 1.0f, true, false, 0.0f, nullptr, sm, pvd);
+      if (threadIdx.x == 0) {
+        r.tcode[row] = res.code;
+        r.tflags[row] = res.flags;
+      }
+      return;
+    }
+    const StreamState st = r.st[b];
+    const bool spec = st.mode == kModeSpec;
+    const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
+    const int depth = spec ? st.s + 1 + rr : 1;
     // loads that do not wait for the softmax
     float qv[VPT];
     int d = -1;
@@ -519,9 +530,9 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
       d = r.dcode[static_cast<size_t>(b) * r.W + rr];
     }
-    const uint64_t seed = r.call->seeds[static_cast<size_t>(st.f) * r.call->B + b];
+    const uint64_t seed = frame_seed(st);
     float pv[VPT];
-    const TopkResult res = topk_row<VPT>(z, r.top_k, r.T, false, false, 0.0f, nullptr, sm, pv);
+    const TopkResult res = topk_regs<VPT>(zv, r.top_k, r.T, false, false, 0.0f, nullptr, sm, pv);
     uint32_t flags = res.flags & (kFlagTopk | kFlagArgmax);
     int code;
     bool near = false;
@@ -587,7 +598,7 @@ __device__ __forceinline__ void add_near_ties(cp_spec_stats* s, const long long*
 // (or gamma + 1), committed codes = the accepted drafts, then row n-1's
 // sample.  Greedy: accept while d_t equals row t-1's argmax.
 __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) {
-  __shared__ int sh_n;
+  __shared__ int sh_n, sh_last;
   const int b = blockIdx.x;
   StreamState st = r.st[b];
   if (st.mode == kModeDone) return;
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
       const uint32_t f = r.tflags[rb + 1] & ~kRowAccepted;
       count_flags(f, nt);
       if (f) st.flags |= 1u << 1;
-      out[1] = r.tcode[rb + 1];
+      out[1] = sh_last = r.tcode[rb + 1];
       if (c.stats) {
         atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->prefill_passes), 1ull);
         add_near_ties(c.stats, nt);
@@ -642,7 +653,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
       }
       const int n = n_acc + 1;
       for (int t = 0; t < n_acc; ++t) out[s + 1 + t] = draft[t];
-      out[s + n] = r.tcode[rb + n_acc];
+      out[s + n] = sh_last = r.tcode[rb + n_acc];
       if (c.stats) {
         atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->rounds), 1ull);
         for (int t = 1; t <= gamma; ++t) {
@@ -658,6 +669,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
     st.s = s + sh_n;
   }
   __syncthreads();
+  st.last = sh_last;
   {
     const int n = sh_n;  // h_{s+n} = output row n - 1 (prefill: row 1)
     const float* src = r.Hout + (rb + n - (st.mode == kModePrefill ? 0 : 1)) * r.H;
@@ -691,6 +703,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
       }
     } else {
       st.mode = kModePrefill;
+      set_frame_seed(st, c.seeds[static_cast<size_t>(st.f) * c.B + b]);
       setup_prefill(r, c, b, st.f);
     }
   } else {
@@ -698,9 +711,8 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
     const int gamma = r.N == 0 ? 0 : min(r.N - 1, r.G - 2 - s);
     st.gamma = gamma;
     st.mode = kModeSpec;
-    const int cs = out[s];
-    __syncthreads();
-    embed_row(r, s, cs, r.X + static_cast<size_t>(b) * r.R * r.H);
+    // verify row 0 = E_s[c_s]: the draft kernel gathers it when it runs
+    if (r.N < 2) embed_row(r, s, st.last, r.X + static_cast<size_t>(b) * r.R * r.H);
     if (threadIdx.x == 0) {
       for (int i = 0; i < r.R; ++i) {
         r.pos[b * r.R + i] = i <= gamma ? s + 1 + i : -1;

@@ -103,22 +103,20 @@ __device__ void radix_members(const uint32_t* key, int k, bool* member, TopkSmem
   }
 }
 
+// The row's logits come in registers (zv: codes [t*VPT, (t+1)*VPT) of
+// thread t), so that callers can issue the loads before anything else.
 // pv receives the thread's VPT probabilities (left unset when greedy).
 template <int VPT>
-__device__ __forceinline__ TopkResult topk_row(const float* __restrict__ z, int k, float T,
-                                               bool greedy, bool do_sample, float u, float* probs,
-                                               TopkSmem& sm, float (&pv)[VPT]) {
+__device__ __forceinline__ TopkResult topk_regs(const float (&zv)[VPT], int k, float T,
+                                                bool greedy, bool do_sample, float u, float* probs,
+                                                TopkSmem& sm, float (&pv)[VPT]) {
   constexpr int V = VPT * kBlock;
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid % kWave;
   const int base = tid * VPT;
-  float zv[VPT];
   uint32_t key[VPT];
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    zv[j] = z[base + j];
-    key[j] = float_key(zv[j]);
-  }
+  for (int j = 0; j < VPT; ++j) key[j] = float_key(zv[j]);
   TopkResult res{-1, 0u};
   if (greedy) {
     uint64_t best = 0;
@@ -300,6 +298,22 @@ __device__ __forceinline__ TopkResult topk_row(const float* __restrict__ z, int 
     for (int j = 0; j < VPT; ++j) probs[base + j] = pv[j];
   }
   return res;
+}
+
+// Thread t's VPT logits of a row.
+template <int VPT>
+__device__ __forceinline__ void load_row(const float* __restrict__ z, float (&zv)[VPT]) {
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) zv[j] = z[threadIdx.x * VPT + j];
+}
+
+template <int VPT>
+__device__ __forceinline__ TopkResult topk_row(const float* __restrict__ z, int k, float T,
+                                               bool greedy, bool do_sample, float u, float* probs,
+                                               TopkSmem& sm, float (&pv)[VPT]) {
+  float zv[VPT];
+  load_row<VPT>(z, zv);
+  return topk_regs<VPT>(zv, k, T, greedy, do_sample, u, probs, sm, pv);
 }
 
 template <typename F>

@@ -20,6 +20,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "committed RVQ codes/sec + accepted codes/verify pass, 1 & 64 streams, N=4"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense, MI355X
 REALTIME_FPS = 12.5
 
 
@@ -48,14 +49,23 @@ def kernel_table(h, c, B, iters=200):
     return out
 
 
-def roofline(table):
-    """Roofline object of the kernel with the largest share of a round."""
+def roofline(table, weight_dtype):
+    """Roofline object of the kernel with the largest share of a round:
+    HBM-bound for the GEMV path, MFMA-bound (dense peak of the weights'
+    dtype; the bf16 path issues three MFMAs per product, counted once here)
+    when the launch ran on matrix-core tiles."""
     kind = max(table, key=lambda k: table[k]["us_per_round"])
     t = table[kind]
-    return {"bound": "hbm", "kernel": kind, "achieved": t["achieved_GBps"],
+    common = {"kernel": kind, "traffic": None, "avg_us": t["avg_us"],
+              "bytes_per_launch": t["bytes_per_launch"],
+              "flops_per_launch": t["flops_per_launch"]}
+    if t.get("matrix_cores"):
+        peak = MFMA_PEAK_TFLOPS[weight_dtype]
+        return {"bound": "mfma", "achieved": t["achieved_TFLOPs"], "peak": peak,
+                "unit": "TFLOP/s", "frac": t["achieved_TFLOPs"] / peak, **common}
+    return {"bound": "hbm", "achieved": t["achieved_GBps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": t["achieved_GBps"] / HBM_PEAK_GBS, "traffic": None,
-            "avg_us": t["avg_us"], "bytes_per_launch": t["bytes_per_launch"]}
+            "frac": t["achieved_GBps"] / HBM_PEAK_GBS, **common}
 
 
 def run_workload(cid, steps, warmup, verify_size=None, frames=None,
@@ -201,7 +211,7 @@ def main():
         "frames_per_s": main_res["frames_per_s"],
         "realtime_factor_vs_12.5fps": main_res["frames_per_s_per_stream"] / REALTIME_FPS,
         "acceptance_by_offset": main_res["acceptance_by_offset"],
-        "roofline": roofline(main_res["kernels"]),
+        "roofline": roofline(main_res["kernels"], c["dtype"]),
         "kernels": {k: {kk: round(v, 3) if isinstance(v, float) else v
                         for kk, v in t.items()}
                     for k, t in main_res["kernels"].items()},
@@ -211,12 +221,12 @@ def main():
         line["ar_baseline"] = {"codes_per_s": ar["codes_per_s"],
                                "ms_per_step": ar["ms_per_step"],
                                "speedup": main_res["codes_per_s"] / ar["codes_per_s"]}
-        s64, _ = run_workload("tiny-64", 1, 1, kernels=True)
+        s64, c64 = run_workload("tiny-64", 1, 1, kernels=True)
         line["streams64"] = {k: s64[k] for k in (
             "codes_per_s", "frames_per_s", "ms_per_step",
             "codes_per_verify_pass", "codes_per_decoder_pass",
             "acceptance_by_offset")}
-        line["streams64"]["roofline"] = roofline(s64["kernels"])
+        line["streams64"]["roofline"] = roofline(s64["kernels"], c64["dtype"])
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 

@@ -227,13 +227,17 @@ typedef struct cp_spec_kernel_timing {
   double flops_per_launch; /* 2 * rows * weight elements                    */
   int32_t launches;
   int32_t rows;            /* activation rows per launch                    */
+  int32_t matrix_cores;    /* 1: the launch ran on MFMA tiles, 0: GEMV or   */
+                           /* vector code                                   */
+  int32_t reserved;
 } cp_spec_kernel_timing;
 
 /* Time one kernel of the round in its decode launch configuration for
- * n_streams streams: `iters` back-to-back launches between two HIP events
- * recorded on `stream`, cycling through the layers (or through distinct
- * heads) so consecutive launches read different weights.  Rows sit at
- * mid-frame positions with one distinct head each.  Overwrites the handle's
+ * n_streams streams: `iters` launches, captured into one HIP graph (as the
+ * decode round is) and replayed between two HIP events recorded on
+ * `stream`, cycling through the layers (or through distinct heads) so
+ * consecutive launches read different weights.  Rows sit at mid-frame
+ * positions with one distinct head each.  Overwrites the handle's
  * workspace (decode state included); synchronises `stream`. */
 int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams,
                         int32_t kind, int32_t iters,

@@ -66,7 +66,8 @@ KERNEL_KINDS = ("draft_heads", "qkv", "attention", "o_proj", "gate_up",
 class KernelTiming(C.Structure):
     _fields_ = [("avg_us", C.c_double), ("bytes_per_launch", C.c_double),
                 ("flops_per_launch", C.c_double), ("launches", C.c_int32),
-                ("rows", C.c_int32)]
+                ("rows", C.c_int32), ("matrix_cores", C.c_int32),
+                ("reserved", C.c_int32)]
 
 _P = C.c_void_p
 _SIGS = {
@@ -251,7 +252,8 @@ class Handle:
         return {"kind": kind, "avg_us": out.avg_us,
                 "bytes_per_launch": out.bytes_per_launch,
                 "flops_per_launch": out.flops_per_launch,
-                "launches": out.launches, "rows": out.rows}
+                "launches": out.launches, "rows": out.rows,
+                "matrix_cores": bool(out.matrix_cores)}
 
     def decoder_forward(self, x, pos, kv, stream=None):
         B, R = int(pos.shape[0]), int(pos.shape[1])

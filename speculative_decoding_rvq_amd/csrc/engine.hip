@@ -104,6 +104,8 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   for (int N_ : {s_.qdim + 2 * s_.kvdim, s_.H, s_.V, s_.kvdim, s_.qdim})
     if (N_ % kRPGHost) return fail(CP_SPEC_EUNSUPPORTED, "output width must be a multiple of 4");
   if (s_.F % 2) return fail(CP_SPEC_EUNSUPPORTED, "ffn must be even");
+  if (attention_smem_bytes(s_.G, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024)
+    return fail(CP_SPEC_EUNSUPPORTED, "attention tile (positions x head_dim x query group) exceeds LDS");
   return CP_SPEC_OK;
 }
 
@@ -464,6 +466,7 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
   hipError_t e = hipMemset(d_workspace, 0, lo.total);
   if (e == hipSuccess)
     e = hipMemcpy(h->at<char>(lo.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = attention_allow_smem(s.d, attention_smem_bytes(s.G, s.d, s.R, s.nq / s.nkv));
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
     delete h;
@@ -690,34 +693,65 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
       flops = 2 * M * V * H;
       break;
   }
-  auto launch = [&](int i) -> int {
+  auto launch = [&](hipStream_t ls, int i) -> int {
     if (kind == CP_SPEC_KERNEL_DRAFT_HEADS)
-      return head_logits(h, s, B * W, r.hstate, W, d_dvar + static_cast<size_t>(i % nvar) * B * W,
+      return head_logits(h, ls, B * W, r.hstate, W, d_dvar + static_cast<size_t>(i % nvar) * B * W,
                          nullptr, nullptr, r.dlogits, grouped ? &dplans[i % nvar] : nullptr);
     if (kind == CP_SPEC_KERNEL_TARGET_HEADS)
-      return head_logits(h, s, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits,
+      return head_logits(h, ls, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits,
                          grouped ? &tplan : nullptr);
-    return layer_kernel(h, s, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv));
+    return layer_kernel(h, ls, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv));
   };
-  int rc = launch(0);  // warm the launch path
+  int rc = launch(s, 0);  // warm the launch path
   if (rc) return rc;
-  hipEvent_t e0, e1;
-  CPS_HIP(hipEventCreate(&e0));
-  CPS_HIP(hipEventCreate(&e1));
-  CPS_HIP(hipEventRecord(e0, s));
-  for (int i = 0; i < iters && !rc; ++i) rc = launch(i);
-  CPS_HIP(hipEventRecord(e1, s));
-  CPS_HIP(hipEventSynchronize(e1));
+  CPS_HIP(hipStreamSynchronize(s));
+  // the launches as one graph, like the decode round
+  hipGraph_t g = nullptr;
+  hipGraphExec_t ge = nullptr;
+  CPS_HIP(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  for (int i = 0; i < iters && !rc; ++i) rc = launch(h->cap_stream, i);
+  const hipError_t ec = hipStreamEndCapture(h->cap_stream, &g);
+  if (rc) {
+    if (g) hipGraphDestroy(g);
+    return rc;
+  }
+  if (ec != hipSuccess) return fail(CP_SPEC_EHIP, std::string("timing capture: ") + hipGetErrorString(ec));
+  const hipError_t ei = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (ei != hipSuccess) return fail(CP_SPEC_EHIP, std::string("timing instantiate: ") + hipGetErrorString(ei));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t et = hipGraphLaunch(ge, s);  // warm
+  if (et == hipSuccess) et = hipEventCreate(&e0);
+  if (et == hipSuccess) et = hipEventCreate(&e1);
+  if (et == hipSuccess) et = hipEventRecord(e0, s);
+  if (et == hipSuccess) et = hipGraphLaunch(ge, s);
+  if (et == hipSuccess) et = hipEventRecord(e1, s);
+  if (et == hipSuccess) et = hipEventSynchronize(e1);
   float ms = 0.0f;
-  CPS_HIP(hipEventElapsedTime(&ms, e0, e1));
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
-  if (rc) return rc;
+  if (et == hipSuccess) et = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
+  hipGraphExecDestroy(ge);
+  if (et != hipSuccess) return fail(CP_SPEC_EHIP, std::string("timing: ") + hipGetErrorString(et));
   out->avg_us = 1e3 * ms / iters;
   out->bytes_per_launch = bytes;
   out->flops_per_launch = flops;
   out->launches = iters;
   out->rows = static_cast<int32_t>(rows);
+  out->reserved = 0;
+  if (kind == CP_SPEC_KERNEL_DRAFT_HEADS || kind == CP_SPEC_KERNEL_TARGET_HEADS)
+    out->matrix_cores = grouped && sh.V % kMfmaTN == 0 && sh.H % kMfmaTK == 0;
+  else if (kind == CP_SPEC_KERNEL_ATTENTION)
+    out->matrix_cores = 0;
+  else {
+    GemvArgs t{};
+    int mode = kAdd;
+    t.K = kind == CP_SPEC_KERNEL_O_PROJ ? sh.qdim : kind == CP_SPEC_KERNEL_DOWN ? sh.F : sh.H;
+    t.N = kind == CP_SPEC_KERNEL_QKV ? sh.qdim + 2 * sh.kvdim : kind == CP_SPEC_KERNEL_GATE_UP ? sh.F : sh.H;
+    if (kind == CP_SPEC_KERNEL_QKV) mode = kQKV;
+    if (kind == CP_SPEC_KERNEL_GATE_UP) mode = kSwiGLU;
+    out->matrix_cores = B * R >= kMfmaMinRows && mfma_fits(mode, t);
+  }
   return CP_SPEC_OK;
 }
 

@@ -159,6 +159,10 @@ hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 g
 // Per-head row lists of the coming round (draft rows and verify rows).
 hipError_t launch_head_plan(const int* dhead, const int* thead, int B, int W, int R, int n_heads,
                             int* dcount, int* drows, int* tcount, int* trows, hipStream_t s);
+// LDS the attention kernel needs, and raising its limit above 64 KB (once,
+// before any launch).
+size_t attention_smem_bytes(int G, int d, int R, int group);
+hipError_t attention_allow_smem(int d, size_t bytes);
 hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int rows, int H, float eps,
                                hipStream_t s);

@@ -187,10 +187,27 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   }
 }
 
+size_t attention_smem_bytes(int G, int d, int R, int group) {
+  const size_t npair = static_cast<size_t>(R) * group;
+  return (static_cast<size_t>(G) * (2 * d + 4) + npair * d + npair * 32) * sizeof(float);
+}
+
+hipError_t attention_allow_smem(int d, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  switch (d) {
+#define CPS_ATT_ATTR(D_) \
+  case D_:               \
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel<D_>), \
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+    CPS_ATT_ATTR(8) CPS_ATT_ATTR(16) CPS_ATT_ATTR(32) CPS_ATT_ATTR(64) CPS_ATT_ATTR(128)
+#undef CPS_ATT_ATTR
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s) {
-  const size_t npair = static_cast<size_t>(a.R) * (a.nq / a.nkv);
-  const size_t shm =
-      (static_cast<size_t>(a.G) * (2 * a.d + 4) + npair * a.d + npair * 32) * sizeof(float);
+  const size_t shm = attention_smem_bytes(a.G, a.d, a.R, a.nq / a.nkv);
   switch (a.d) {
 #define CPS_ATT(D_)                                                                     \
   case D_:                                                                              \

@@ -58,6 +58,27 @@ __device__ __forceinline__ const WT* gemm_weight_row(const GemvArgs& a, const WT
   return W0 + static_cast<size_t>(n) * a.K;
 }
 
+// Final-normed activation rows for the heads' caller (x * g * rinv): the
+// column tiles of a row tile split K between them, float4 at a time, so each
+// block writes a short slice.
+__device__ __forceinline__ void write_xnorm(const GemvArgs& a, const int* rows_s, const float* rinv_s,
+                                            int count) {
+  const int k4 = a.K / 4;
+  const int per = (k4 + gridDim.x - 1) / gridDim.x;
+  const int c0 = blockIdx.x * per, c1 = min(k4, c0 + per);
+  const int w = c1 - c0;
+  if (w <= 0) return;
+  for (int idx = threadIdx.x; idx < count * w; idx += kBlock) {
+    const int r = idx / w, c = 4 * (c0 + idx % w);
+    const int row = rows_s[r];
+    const float4 x = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row / a.xdiv) * a.ldx + c);
+    const float4 g = *reinterpret_cast<const float4*>(a.norm_g + c);
+    const float ri = rinv_s[r];
+    *reinterpret_cast<float4*>(a.xnorm_out + static_cast<size_t>(row) * a.K + c) =
+        make_float4(x.x * g.x * ri, x.y * g.y * ri, x.z * g.z * ri, x.w * g.w * ri);
+  }
+}
+
 struct GemmSmemF32 {
   float A[kTM][kTK + 4];
   float B[kTN][kTK + 4];
@@ -231,14 +252,7 @@ __global__ __launch_bounds__(kBlock) void mfma_gemm_kernel(const GemvArgs a) {
   __syncthreads();
 
   // final-normed rows for the heads' caller (once per row, by the first n tile)
-  if (MODE == kHead && norm && a.xnorm_out != nullptr && blockIdx.x == 0) {
-    for (int idx = tid; idx < count * a.K; idx += kBlock) {
-      const int r = idx / a.K, k = idx % a.K;
-      const int row = rows_s[r];
-      a.xnorm_out[static_cast<size_t>(row) * a.K + k] =
-          a.X[static_cast<size_t>(row / a.xdiv) * a.ldx + k] * a.norm_g[k] * rinv_s[r];
-    }
-  }
+  if (MODE == kHead && norm && a.xnorm_out != nullptr) write_xnorm(a, rows_s, rinv_s, count);
 
   // ---- fused epilogue ----
   if (MODE == kSwiGLU) {
@@ -472,14 +486,7 @@ __global__ __launch_bounds__(kBlock) void mfma_splitk_kernel(const GemvArgs a) {
   }
   __syncthreads();
 
-  if (MODE == kHead && norm && a.xnorm_out != nullptr && blockIdx.x == 0) {
-    for (int idx = tid; idx < count * a.K; idx += kBlock) {
-      const int r = idx / a.K, k = idx % a.K;
-      const int row = rows_s[r];
-      a.xnorm_out[static_cast<size_t>(row) * a.K + k] =
-          a.X[static_cast<size_t>(row / a.xdiv) * a.ldx + k] * a.norm_g[k] * rinv_s[r];
-    }
-  }
+  if (MODE == kHead && norm && a.xnorm_out != nullptr) write_xnorm(a, rows_s, rinv_s, count);
   auto tile_val = [&](int r, int c) {
     float v = part[0][r][c];
 #pragma unroll

@@ -49,14 +49,45 @@ def kernel_table(h, c, B, iters=200):
     return out
 
 
-def roofline(table, weight_dtype):
+TRAFFIC_SOURCES = ("speculative_decoding_rvq_amd/csrc/gemv_impl.h",
+                   "speculative_decoding_rvq_amd/csrc/gemv_bf16.hip",
+                   "speculative_decoding_rvq_amd/csrc/kernels.h")
+
+
+def measured_traffic(workload, kind):
+    """HBM-side bytes per launch from the committed counter summary
+    (profiles/<workload>_<kind>_traffic.md), or None when there is none or
+    the kernel's sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_{kind}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", " ", "#")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline(table, weight_dtype, workload=None):
     """Roofline object of the kernel with the largest share of a round:
     HBM-bound for the GEMV path, MFMA-bound (dense peak of the weights'
     dtype; the bf16 path issues three MFMAs per product, counted once here)
     when the launch ran on matrix-core tiles."""
     kind = max(table, key=lambda k: table[k]["us_per_round"])
     t = table[kind]
-    common = {"kernel": kind, "traffic": None, "avg_us": t["avg_us"],
+    traffic = measured_traffic(workload, kind) if workload else None
+    common = {"kernel": kind, "traffic": traffic, "avg_us": t["avg_us"],
               "bytes_per_launch": t["bytes_per_launch"],
               "flops_per_launch": t["flops_per_launch"]}
     if t.get("matrix_cores"):
@@ -173,6 +204,9 @@ def main():
     ap.add_argument("--cpu-frames", type=int, default=160)
     ap.add_argument("--no-extra", action="store_true",
                     help="only the main workload (no AR / 64-stream / CPU legs)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (reference "
+                         "kernel for scaling the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU; streams shard across GPUs "
@@ -181,6 +215,15 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        x = torch.ones(n, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(8):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mb, "launches": 8}), flush=True)
+        return
 
     main_res, c = run_workload(args.workload, args.steps, args.warmup,
                                frames=args.frames, kernels=True)
@@ -211,7 +254,7 @@ def main():
         "frames_per_s": main_res["frames_per_s"],
         "realtime_factor_vs_12.5fps": main_res["frames_per_s_per_stream"] / REALTIME_FPS,
         "acceptance_by_offset": main_res["acceptance_by_offset"],
-        "roofline": roofline(main_res["kernels"], c["dtype"]),
+        "roofline": roofline(main_res["kernels"], c["dtype"], args.workload),
         "kernels": {k: {kk: round(v, 3) if isinstance(v, float) else v
                         for kk, v in t.items()}
                     for k, t in main_res["kernels"].items()},
@@ -226,7 +269,7 @@ def main():
             "codes_per_s", "frames_per_s", "ms_per_step",
             "codes_per_verify_pass", "codes_per_decoder_pass",
             "acceptance_by_offset")}
-        line["streams64"]["roofline"] = roofline(s64["kernels"], c64["dtype"])
+        line["streams64"]["roofline"] = roofline(s64["kernels"], c64["dtype"], "tiny-64")
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 

@@ -270,6 +270,17 @@ def main():
             "codes_per_verify_pass", "codes_per_decoder_pass",
             "acceptance_by_offset")}
         line["streams64"]["roofline"] = roofline(s64["kernels"], c64["dtype"], "tiny-64")
+        # the qwen3tts shape at 64 streams: weights large enough for the
+        # batched projections' roofline to mean something
+        q64, cq64 = run_workload("qwen3tts-64", 1, 1, kernels=True)
+        line["streams64_qwen3tts"] = {k: q64[k] for k in (
+            "codes_per_s", "frames_per_s", "ms_per_step",
+            "codes_per_verify_pass", "codes_per_decoder_pass")}
+        line["streams64_qwen3tts"]["roofline"] = roofline(q64["kernels"], cq64["dtype"],
+                                                          "qwen3tts-64")
+        line["streams64_qwen3tts"]["kernels"] = {
+            k: {kk: round(v, 3) if isinstance(v, float) else v for kk, v in t.items()}
+            for k, t in q64["kernels"].items()}
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 

@@ -18,6 +18,9 @@ for On Device TTS", section 2 and Figure 1):
   wide-256     wide Omni-talker-like, bf16: 8 layers, H 2048, 16/4 heads of
                128, FFN 6144, G 16, V 4096, heads correlated across depths,
                256 streams x 200 frames, N 4
+  qwen3tts-64  the qwen3tts shape with 64 streams x 100 frames (batched rows
+               large enough that the decoder's weights, not launches, set
+               the pace)
 
 Value recipe:
   * every weight matrix (projections, embedding tables, lm_heads) is drawn
@@ -41,7 +44,7 @@ F32 = "f32"
 BF16 = "bf16"
 
 # Decoder/codebook shapes and decoding parameters of the workloads.
-WORKLOADS = ("tiny", "qwen3tts", "tiny-greedy", "tiny-64", "wide-256")
+WORKLOADS = ("tiny", "qwen3tts", "tiny-greedy", "tiny-64", "wide-256", "qwen3tts-64")
 
 _BASE = {
     "tiny": dict(name="tiny-fp32", layers=2, hidden=256, q_heads=4, kv_heads=4,
@@ -67,6 +70,11 @@ _BASE = {
             vocab=4096, dtype=BF16, rope_theta=1e4, rms_eps=1e-6,
             greedy=False, temperature=0.8, top_k=100, verify_size=4,
             streams=256, frames=200, heads_corr=0.3),
+    "qwen3tts-64": dict(name="qwen3-tts-0.6b-codepredictor-64streams", layers=5,
+            hidden=1024, q_heads=16, kv_heads=8, head_dim=128, ffn=3072,
+            groups=16, vocab=2048, dtype=BF16, rope_theta=1e4, rms_eps=1e-6,
+            greedy=False, temperature=0.9, top_k=50, verify_size=4,
+            streams=64, frames=100, heads_corr=None),
 }
 
 

@@ -122,6 +122,19 @@ def test_wide_256_streams_sampled():
     _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
+def test_qwen3tts_64_streams_full_sampled():
+    """The qwen3tts shape at 64 streams in the benchmark's configuration
+    (all 100 frames of every stream, matrix-core projections and heads)."""
+    c = synth.config("qwen3tts-64")
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle("qwen3tts-64")
+    log("decode qwen3tts-64 B=64 F=100 (full)")
+    gc, gf, gst = decode_gpu(h, hf, c0, seeds)
+    assert gst["frames"] == 6400 and gst["codes"] == 6400 * 15
+    pairs = [(0, 0), (0, 63), (37, 11), (99, 40), (99, 63)]
+    _check("qwen3tts-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+
+
 def test_determinism_and_stream_independence():
     """Two runs are bit-identical; stream 0 of a 64-stream run equals the
     same frames decoded alone (up to flagged near ties)."""

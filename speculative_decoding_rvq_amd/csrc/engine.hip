@@ -38,7 +38,7 @@ struct Shape {
 };
 
 struct Layout {
-  size_t st, call, dhead, thead, pos, hstate, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
+  size_t st, call, sstats, dhead, thead, pos, hstate, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
       tlogits, p, tcode, tflags, rope, plan, total;
 };
 
@@ -132,6 +132,7 @@ Layout make_layout(const Shape& s) {
   const size_t B = s.maxB, R = s.R, W = s.W, f4 = sizeof(float), i4 = sizeof(int);
   l.st = take(B * sizeof(StreamState));
   l.call = take(sizeof(CallDesc));
+  l.sstats = take(B * sizeof(cp_spec_stats));
   l.dhead = take(B * W * i4);
   l.thead = take(B * R * i4);
   l.pos = take(B * R * i4);
@@ -182,6 +183,7 @@ struct cp_spec {
     r.embed = embed;
     r.st = at<StreamState>(lo.st);
     r.call = at<CallDesc>(lo.call);
+    r.sstats = at<cp_spec_stats>(lo.sstats);
     r.dhead = at<int>(lo.dhead);
     r.thead = at<int>(lo.thead);
     r.pos = at<int>(lo.pos);
@@ -502,7 +504,7 @@ int cp_spec_decode_frames(cp_spec* h, void* stream, int32_t n_streams, int32_t n
   const RoundArgs r = h->round_args(B);
   CallDesc c{};
   c.h_frame = d_h_frame; c.c0 = d_c0; c.seeds = d_seeds; c.out_codes = d_out_codes;
-  c.out_flags = d_out_flags; c.stats = d_stats; c.F = n_frames; c.B = B;
+  c.out_flags = d_out_flags; c.F = n_frames; c.B = B;
   if (h->use_graph) {
     const int rc = ensure_graph(h, B);
     if (rc) return rc;
@@ -530,6 +532,10 @@ int cp_spec_decode_frames(cp_spec* h, void* stream, int32_t n_streams, int32_t n
     if (need == 0) break;
     if (launched > cap) return fail(CP_SPEC_EHIP, "round loop did not terminate");
     chunk = need;
+  }
+  if (d_stats) {
+    CPS_HIP(launch_stats_flush(r.sstats, B, d_stats, s));
+    CPS_HIP(hipStreamSynchronize(s));
   }
   return CP_SPEC_OK;
 }

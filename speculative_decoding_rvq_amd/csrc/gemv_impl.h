@@ -10,12 +10,13 @@
 // for M fused multiply-adds.
 //
 // Latency: the weight loads of the block's first unit are issued before
-// anything else; activation rows, the RMSNorm sum of squares and its block
-// reduction proceed while they are in flight.  RMSNorm's 1/sqrt(mean+eps) is
-// a per-row scalar applied to the dot products in the epilogue.  Partial sums
+// anything else, then the activation rows.  RMSNorm's 1/sqrt(mean+eps) is a
+// per-row scalar applied to the dot products in the epilogue, so the rows'
+// sums of squares are reduced together with the dot products: partial sums
 // are folded within DPP rows of 16 lanes (four rotations) and across rows and
-// waves through LDS.  The epilogue is fused: residual add, SwiGLU product, Q
-// write plus K/V append at the row's position, per-row lm_head logits (with
+// waves through LDS, behind a single barrier.  The epilogue is fused:
+// residual add, SwiGLU product (gate and up partials summed by one thread),
+// Q write plus K/V append at the row's position, per-row lm_head logits (with
 // the final-normed hidden state written once).
 #pragma once
 
@@ -67,15 +68,15 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   constexpr int VEC = C::N;
   constexpr int RPG = gemv_rpg(SPT);
   constexpr int NV = RPG * MT;
-  __shared__ float part[kBlock / 16][NV];  // per DPP row partial sums
-  __shared__ float red[4][MT];
-  __shared__ float rinv_s[MT];
+  // per DPP row: NV dot-product partials, then MT sums of squares (RMSNorm)
+  __shared__ float part[kBlock / 16][NV + MT];
 
   const int KT = a.kt;
   const int RG = kBlock / KT;
+  const int rows16 = KT / 16;  // DPP rows per row group
   const int tid = threadIdx.x;
   const int rg = tid / KT, kt = tid % KT;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int lane = tid % kWave;
   const int m0 = blockIdx.y * MT;
   const int Mloc = min(MT, a.M - m0);
   if (Mloc <= 0) return;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
     }
   }
 
-  // ---- activation slices (x * g) in registers, sums of squares ----
+  // ---- activation slices (x * g) in registers, partial sums of squares ----
   const bool norm = a.norm_g != nullptr;
   float xr[MT][SPT][VEC];
   float ss[MT];
@@ -126,33 +127,14 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
       }
     }
   }
-  if (norm) {
-    // every row group holds a full copy of each row: reduce row group 0 only
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float w = wave_sum(ss[m]);
-      if (lane == 0) red[wave][m] = w;
-    }
-    __syncthreads();
-    if (tid < MT) {
-      const int wpr = KT / kWave;  // waves of row group 0
-      float t = 0.0f;
-      for (int w = 0; w < wpr; ++w) t += red[w][tid];
-      rinv_s[tid] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
-    }
-    __syncthreads();
-    if (MODE == kHead && a.xnorm_out != nullptr && blockIdx.x == 0 && rg == 0) {
-      const float ri = rinv_s[0];
-#pragma unroll
-      for (int j = 0; j < SPT; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          a.xnorm_out[static_cast<size_t>(m0) * a.K + (kt + KT * j) * VEC + e] = xr[0][j][e] * ri;
-    }
-  }
+
+  // thread (g, idx) of the epilogue owns slot idx / MT of unit g, row idx % MT
+  const bool owner = tid < RG * NV;
+  const int g = owner ? tid / NV : 0, idx = owner ? tid % NV : 0;
+  float ri = 1.0f;  // 1/rms of the owner's row, known after the first reduction
 
   // ---- units ----
-  for (; ubase < a.units; ubase += stride) {
+  for (bool first = true; ubase < a.units; ubase += stride, first = false) {
     float v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = 0.0f;
@@ -178,42 +160,61 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         for (int j = 0; j < SPT; ++j) wv[rp][j] = *reinterpret_cast<const VT*>(wr + (kt + KT * j) * VEC);
       }
     }
-    // fold 16 lanes per DPP row, then the DPP rows of the row group in LDS
+    // fold 16 lanes per DPP row (dot products and, the first time, the sums
+    // of squares), then the DPP rows of the row group in LDS: one barrier
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = row16_sum(v[i]);
+    if (first && norm) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) ss[m] = row16_sum(ss[m]);
+    }
     if ((lane & 15) == 0) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) part[tid >> 4][i] = v[i];
+      if (first && norm) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) part[tid >> 4][NV + m] = ss[m];
+      }
     }
     __syncthreads();
-    const int rows16 = KT / 16;  // DPP rows per row group
-    float val = 0.0f;
-    int g = 0, idx = 0;
-    if (tid < RG * NV) {
-      g = tid / NV;
-      idx = tid % NV;
-      for (int q = 0; q < rows16; ++q) val += part[g * rows16 + q][idx];
-      if (norm) val *= rinv_s[idx % MT];
-    }
-    // ---- fused epilogue: thread (g, idx) owns slot idx / MT, row idx % MT ----
-    if (MODE == kSwiGLU) {
-      // slots below RPG/2 are gate values, the rest the matching up values
-      constexpr int H2 = RPG / 2;
-      __syncthreads();
-      if (tid < RG * NV) part[g][idx] = val;
-      __syncthreads();
-      if (tid < RG * NV) {
-        const int rp = idx / MT, m = idx % MT;
-        const int u = ubase + g;
-        if (rp < H2 && u < a.units && m < Mloc) {
-          const float up = part[g][(rp + H2) * MT + m];
-          a.Y[static_cast<size_t>(m0 + m) * a.ldy + H2 * u + rp] = silu_f(val) * up;
-        }
+    if (first && norm) {
+      // every row group holds a full copy of each row: row group 0's sums
+      if (owner) {
+        float t = 0.0f;
+        for (int q = 0; q < rows16; ++q) t += part[q][NV + idx % MT];
+        ri = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
       }
-    } else if (tid < RG * NV) {
+      if (MODE == kHead && a.xnorm_out != nullptr && blockIdx.x == 0 && rg == 0) {
+        float t = 0.0f;
+        for (int q = 0; q < rows16; ++q) t += part[q][NV];
+        const float r0 = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+#pragma unroll
+        for (int j = 0; j < SPT; ++j)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            a.xnorm_out[static_cast<size_t>(m0) * a.K + (kt + KT * j) * VEC + e] = xr[0][j][e] * r0;
+      }
+    }
+    // ---- fused epilogue ----
+    if (owner) {
       const int rp = idx / MT, m = idx % MT;
       const int u = ubase + g;
-      if (u < a.units && m < Mloc) {
+      if (MODE == kSwiGLU) {
+        // slots below RPG/2 are gate values, the rest the matching up values
+        constexpr int H2 = RPG / 2;
+        if (rp < H2 && u < a.units && m < Mloc) {
+          const int iu = (rp + H2) * MT + m;
+          float gate = 0.0f, up = 0.0f;
+          for (int q = 0; q < rows16; ++q) {
+            gate += part[g * rows16 + q][idx];
+            up += part[g * rows16 + q][iu];
+          }
+          a.Y[static_cast<size_t>(m0 + m) * a.ldy + H2 * u + rp] = silu_f(gate * ri) * (up * ri);
+        }
+      } else if (u < a.units && m < Mloc) {
+        float val = 0.0f;
+        for (int q = 0; q < rows16; ++q) val += part[g * rows16 + q][idx];
+        val *= ri;
         const int o = u * RPG + rp;
         const int row = m0 + m;
         if (MODE == kAdd) {
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         }
       }
     }
-    __syncthreads();
+    if (nb < a.units) __syncthreads();  // part[] is rewritten by the next unit
   }
 }
 

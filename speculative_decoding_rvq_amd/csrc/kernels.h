@@ -117,10 +117,7 @@ struct CallDesc {
   const uint64_t* seeds;
   int* out_codes;
   uint32_t* out_flags;
-  cp_spec_stats* stats;
   int F, B;
-  int active;   // streams with frames left
-  int pad;
 };
 
 struct RoundArgs {
@@ -133,6 +130,7 @@ struct RoundArgs {
   // state and buffers
   StreamState* st;
   CallDesc* call;
+  cp_spec_stats* sstats;  // [B] per-stream counters of the current call
   int* dhead;   // [B][W]
   int* thead;   // [B][R]
   int* pos;     // [B][R]
@@ -172,5 +170,7 @@ hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t 
 hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s);
+// Adds the B per-stream counters to *out (one block; fixed order).
+hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats* out, hipStream_t s);
 
 }  // namespace cps

@@ -209,8 +209,8 @@ hipError_t attention_allow_smem(int d, size_t bytes) {
 hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s) {
   const size_t shm = attention_smem_bytes(a.G, a.d, a.R, a.nq / a.nkv);
   switch (a.d) {
-#define CPS_ATT(D_)                                                                     \
-  case D_:                                                                              \
+#define CPS_ATT(D_)                                                                          \
+  case D_:                                                                                   \
     hipLaunchKernelGGL(attention_kernel<D_>, dim3(B, a.nkv), dim3(kBlock), shm, s, a); \
     break;
     CPS_ATT(8) CPS_ATT(16) CPS_ATT(32) CPS_ATT(64) CPS_ATT(128)
@@ -441,10 +441,9 @@ __device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int 
 
 __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, const CallDesc c) {
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x == 0) {
-    *r.call = c;
-    r.call->active = c.F > 0 ? c.B : 0;
-  }
+  if (b == 0 && threadIdx.x == 0) *r.call = c;
+  constexpr int kStatWords = sizeof(cp_spec_stats) / sizeof(long long);
+  if (threadIdx.x < kStatWords) reinterpret_cast<long long*>(r.sstats + b)[threadIdx.x] = 0;
   StreamState st{};
   if (c.F > 0) {
     setup_prefill(r, c, b, 0);
@@ -596,128 +595,169 @@ hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s) {
   return hipGetLastError();
 }
 
-__device__ __forceinline__ void count_flags(uint32_t f, long long* cnt) {
-  if (f & kFlagTopk) ++cnt[0];
-  if (f & kFlagArgmax) ++cnt[1];
-  if (f & kFlagCdf) ++cnt[2];
-  if (f & kFlagAccept) ++cnt[3];
+// Near-tie flag bits -> the four near-tie counters (stats words).
+__device__ __forceinline__ void count_flags(uint32_t f, cp_spec_stats* cnt) {
+  if (f & kFlagTopk) ++cnt->near_tie_topk;
+  if (f & kFlagArgmax) ++cnt->near_tie_argmax;
+  if (f & kFlagCdf) ++cnt->near_tie_cdf;
+  if (f & kFlagAccept) ++cnt->near_tie_accept;
 }
 
-__device__ __forceinline__ void add_near_ties(cp_spec_stats* s, const long long* nt) {
-  if (nt[0]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_topk), static_cast<unsigned long long>(nt[0]));
-  if (nt[1]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_argmax), static_cast<unsigned long long>(nt[1]));
-  if (nt[2]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_cdf), static_cast<unsigned long long>(nt[2]));
-  if (nt[3]) atomicAdd(reinterpret_cast<unsigned long long*>(&s->near_tie_accept), static_cast<unsigned long long>(nt[3]));
-}
+// Candidate rows of h_{s+n} held in registers while the outcome is decided:
+// up to kHrowF4 float4 per thread, i.e. R * H <= 8192.
+constexpr int kHrowF4 = 8;
 
 // Accept, commit, truncate, and set up the stream's next round (or frame).
 // The rows' outcomes come from the target kernel: n = first rejected offset
 // (or gamma + 1), committed codes = the accepted drafts, then row n-1's
 // sample.  Greedy: accept while d_t equals row t-1's argmax.
+//
+// Latency: every load that depends only on the stream index goes out at once
+// (state, call, the rows' codes and flags, the stream's counters, and all R
+// output rows, one of which becomes h_{s+n}); one thread then decides, and
+// the block writes.  Counters stay per stream (no device-wide atomics inside
+// the round); they are added to the caller's totals once per call.
 __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) {
-  __shared__ int sh_n, sh_last;
-  const int b = blockIdx.x;
-  StreamState st = r.st[b];
+  __shared__ StreamState st_s;
+  __shared__ CallDesc c_s;
+  __shared__ cp_spec_stats cnt_s;
+  __shared__ int tcode_s[CP_SPEC_MAX_WINDOW], dcode_s[CP_SPEC_MAX_WINDOW];
+  __shared__ uint32_t tflags_s[CP_SPEC_MAX_WINDOW], dflags_s[CP_SPEC_MAX_WINDOW];
+  __shared__ int sh_n, sh_hrow;
+  constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
+  constexpr int kCntW = sizeof(cp_spec_stats) / 8;
+  static_assert(kStW <= 32 && kCallW <= 32 && kCntW <= 32, "state words");
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const size_t rb = static_cast<size_t>(b) * r.R;
+
+  // ---- every independent load at once ----
+  if (tid < kStW) {
+    reinterpret_cast<int*>(&st_s)[tid] = reinterpret_cast<const int*>(r.st + b)[tid];
+  } else if (tid >= 32 && tid < 32 + kCallW) {
+    reinterpret_cast<int*>(&c_s)[tid - 32] = reinterpret_cast<const int*>(r.call)[tid - 32];
+  } else if (tid >= 64 && tid < 64 + kCntW) {
+    reinterpret_cast<long long*>(&cnt_s)[tid - 64] = reinterpret_cast<const long long*>(r.sstats + b)[tid - 64];
+  } else if (tid >= 96 && tid < 96 + r.R) {
+    tcode_s[tid - 96] = r.tcode[rb + tid - 96];
+    tflags_s[tid - 96] = r.tflags[rb + tid - 96];
+  } else if (tid >= 112 && tid < 112 + r.W) {
+    dcode_s[tid - 112] = r.dcode[static_cast<size_t>(b) * r.W + tid - 112];
+    dflags_s[tid - 112] = r.dflags[static_cast<size_t>(b) * r.W + tid - 112];
+  }
+  const int H4 = r.H / 4;
+  const int nf4 = r.R * H4;
+  const bool held = nf4 <= kHrowF4 * kBlock;
+  float4 hv[kHrowF4];
+  if (held) {
+    const float4* src = reinterpret_cast<const float4*>(r.Hout + rb * r.H);
+#pragma unroll
+    for (int i = 0; i < kHrowF4; ++i) {
+      const int q = tid + i * kBlock;
+      if (q < nf4) hv[i] = src[q];
+    }
+  }
+  __syncthreads();
+  StreamState st = st_s;
   if (st.mode == kModeDone) return;
-  const CallDesc c = *r.call;
+  const CallDesc& c = c_s;
   const size_t fb = static_cast<size_t>(st.f) * c.B + b;
   int* out = c.out_codes + fb * r.G;
-  const size_t rb = static_cast<size_t>(b) * r.R;
-  if (st.mode == kModePrefill) {
-    if (threadIdx.x == 0) {
-      long long nt[4] = {0, 0, 0, 0};
-      const uint32_t f = r.tflags[rb + 1] & ~kRowAccepted;
-      count_flags(f, nt);
-      if (f) st.flags |= 1u << 1;
-      out[1] = sh_last = r.tcode[rb + 1];
-      if (c.stats) {
-        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->prefill_passes), 1ull);
-        add_near_ties(c.stats, nt);
-      }
+
+  // ---- the decision (one thread) ----
+  if (tid == 0) {
+    cp_spec_stats& cnt = cnt_s;
+    if (st.mode == kModePrefill) {
+      const uint32_t f = tflags_s[1] & ~kRowAccepted;
+      count_flags(f, &cnt);
+      if (f) st_s.flags |= 1u << 1;
+      out[1] = st_s.last = tcode_s[1];
+      ++cnt.prefill_passes;
       sh_n = 1;
-    }
-    st.s = 1;
-  } else {
-    const int s = st.s, gamma = st.gamma;
-    if (threadIdx.x == 0) {
-      long long nt[4] = {0, 0, 0, 0};
-      const int* draft = r.dcode + static_cast<size_t>(b) * r.W;
+      sh_hrow = 1;
+      st_s.s = 1;
+    } else {
+      const int s = st.s, gamma = st.gamma;
+      uint32_t fl = st.flags;
       for (int t = 1; t <= gamma; ++t) {
-        const uint32_t f = r.dflags[static_cast<size_t>(b) * r.W + t - 1];
-        count_flags(f, nt);
-        if (f) st.flags |= 1u << (s + t);
+        const uint32_t f = dflags_s[t - 1];
+        count_flags(f, &cnt);
+        if (f) fl |= 1u << (s + t);
       }
       for (int i = 0; i <= gamma; ++i) {
-        const uint32_t f = r.tflags[rb + i] & (kFlagTopk | kFlagArgmax);
-        count_flags(f, nt);
-        if (f) st.flags |= 1u << (s + 1 + i);
+        const uint32_t f = tflags_s[i] & (kFlagTopk | kFlagArgmax);
+        count_flags(f, &cnt);
+        if (f) fl |= 1u << (s + 1 + i);
       }
       int n_acc = 0;
       if (r.greedy) {
-        while (n_acc < gamma && draft[n_acc] == r.tcode[rb + n_acc]) ++n_acc;
+        while (n_acc < gamma && dcode_s[n_acc] == tcode_s[n_acc]) ++n_acc;
       } else {
-        while (n_acc < gamma && (r.tflags[rb + n_acc] & kRowAccepted)) ++n_acc;
+        while (n_acc < gamma && (tflags_s[n_acc] & kRowAccepted)) ++n_acc;
         for (int t = 1; t <= min(n_acc + 1, gamma); ++t) {
-          if (r.tflags[rb + t - 1] & kFlagAccept) {
-            ++nt[3];
-            st.flags |= 1u << (s + t);
+          if (tflags_s[t - 1] & kFlagAccept) {
+            ++cnt.near_tie_accept;
+            fl |= 1u << (s + t);
           }
         }
-        if (r.tflags[rb + n_acc] & kFlagCdf) {
-          ++nt[2];
-          st.flags |= 1u << (s + n_acc + 1);
+        if (tflags_s[n_acc] & kFlagCdf) {
+          ++cnt.near_tie_cdf;
+          fl |= 1u << (s + n_acc + 1);
         }
       }
       const int n = n_acc + 1;
-      for (int t = 0; t < n_acc; ++t) out[s + 1 + t] = draft[t];
-      out[s + n] = sh_last = r.tcode[rb + n_acc];
-      if (c.stats) {
-        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->rounds), 1ull);
-        for (int t = 1; t <= gamma; ++t) {
-          atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->proposed[t - 1]), 1ull);
-          if (t <= n_acc) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->accepted[t - 1]), 1ull);
-        }
-        if (n_acc == gamma) atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->bonus), 1ull);
-        add_near_ties(c.stats, nt);
+      for (int t = 0; t < n_acc; ++t) out[s + 1 + t] = dcode_s[t];
+      out[s + n] = st_s.last = tcode_s[n_acc];
+      ++cnt.rounds;
+      for (int t = 1; t <= gamma; ++t) {
+        ++cnt.proposed[t - 1];
+        if (t <= n_acc) ++cnt.accepted[t - 1];
       }
+      if (n_acc == gamma) ++cnt.bonus;
+      st_s.flags = fl;
+      st_s.s = s + n;
       sh_n = n;
+      sh_hrow = n - 1;
     }
-    __syncthreads();
-    st.s = s + sh_n;
+    if (st_s.s >= r.G - 1) {  // frame complete
+      if (c.out_flags) c.out_flags[fb] = st_s.flags;
+      ++cnt.frames;
+      cnt.codes += r.G - 1;
+    }
   }
   __syncthreads();
-  st.last = sh_last;
+  st = st_s;
+
+  // ---- h_{s+n} = output row n-1 (prefill: row 1) ----
   {
-    const int n = sh_n;  // h_{s+n} = output row n - 1 (prefill: row 1)
-    const float* src = r.Hout + (rb + n - (st.mode == kModePrefill ? 0 : 1)) * r.H;
-    float* dst = r.hstate + static_cast<size_t>(b) * r.H;
-    for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = src[i];
+    const int hrow = sh_hrow;
+    float4* dst = reinterpret_cast<float4*>(r.hstate + static_cast<size_t>(b) * r.H);
+    if (held) {
+#pragma unroll
+      for (int i = 0; i < kHrowF4; ++i) {
+        const int q = tid + i * kBlock;
+        if (q < nf4 && q / H4 == hrow) dst[q % H4] = hv[i];
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(r.Hout + (rb + hrow) * r.H);
+      for (int i = tid; i < H4; i += kBlock) dst[i] = src[i];
+    }
   }
-  __syncthreads();
+  if (tid < kCntW)
+    reinterpret_cast<long long*>(r.sstats + b)[tid] = reinterpret_cast<const long long*>(&cnt_s)[tid];
 
   // ---- next round of this stream ----
   if (st.s >= r.G - 1) {
-    if (threadIdx.x == 0) {
-      if (c.out_flags) c.out_flags[fb] = st.flags;
-      if (c.stats) {
-        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->frames), 1ull);
-        atomicAdd(reinterpret_cast<unsigned long long*>(&c.stats->codes), static_cast<unsigned long long>(r.G - 1));
-      }
-    }
     st.f += 1;
     st.s = 0;
     st.flags = 0;
     st.gamma = 0;
     if (st.f >= c.F) {
       st.mode = kModeDone;
-      if (threadIdx.x == 0) {
-        atomicSub(&r.call->active, 1);
-        for (int i = 0; i < r.R; ++i) {
-          r.pos[b * r.R + i] = -1;
-          r.thead[b * r.R + i] = 0;
-        }
-        for (int t = 0; t < r.W; ++t) r.dhead[b * r.W + t] = 0;
+      if (tid < r.R) {
+        r.pos[rb + tid] = -1;
+        r.thead[rb + tid] = 0;
       }
+      if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = 0;
     } else {
       st.mode = kModePrefill;
       set_frame_seed(st, c.seeds[static_cast<size_t>(st.f) * c.B + b]);
@@ -729,20 +769,33 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
     st.gamma = gamma;
     st.mode = kModeSpec;
     // verify row 0 = E_s[c_s]: the draft kernel gathers it when it runs
-    if (r.N < 2) embed_row(r, s, st.last, r.X + static_cast<size_t>(b) * r.R * r.H);
-    if (threadIdx.x == 0) {
-      for (int i = 0; i < r.R; ++i) {
-        r.pos[b * r.R + i] = i <= gamma ? s + 1 + i : -1;
-        r.thead[b * r.R + i] = i <= gamma ? s + 1 + i : 0;
-      }
-      for (int t = 1; t <= r.W; ++t) r.dhead[b * r.W + t - 1] = t <= gamma ? s + t : 0;
+    if (r.N < 2) embed_row(r, s, st.last, r.X + rb * r.H);
+    if (tid < r.R) {
+      r.pos[rb + tid] = tid <= gamma ? s + 1 + tid : -1;
+      r.thead[rb + tid] = tid <= gamma ? s + 1 + tid : 0;
     }
+    if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = tid + 1 <= gamma ? s + tid + 1 : 0;
   }
-  if (threadIdx.x == 0) r.st[b] = st;
+  if (tid == 0) r.st[b] = st;
 }
 
 hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s) {
   hipLaunchKernelGGL(round_accept_kernel, dim3(r.B), dim3(kBlock), 0, s, r);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kBlock) void stats_flush_kernel(const cp_spec_stats* sstats, int B,
+                                                             cp_spec_stats* out) {
+  constexpr int kW = sizeof(cp_spec_stats) / sizeof(long long);
+  const int i = threadIdx.x;
+  if (i >= kW) return;
+  long long t = 0;
+  for (int b = 0; b < B; ++b) t += reinterpret_cast<const long long*>(sstats + b)[i];
+  if (t) atomicAdd(reinterpret_cast<unsigned long long*>(out) + i, static_cast<unsigned long long>(t));
+}
+
+hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats* out, hipStream_t s) {
+  hipLaunchKernelGGL(stats_flush_kernel, dim3(1), dim3(kBlock), 0, s, sstats, B, out);
   return hipGetLastError();
 }
 

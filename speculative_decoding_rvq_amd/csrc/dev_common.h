@@ -36,6 +36,19 @@ template <> struct Chunk<uint16_t> {
   }
 };
 
+// x = hi + mid + lo, each a bf16 bit pattern, by truncation: hi keeps the
+// top 8 significant bits of x, mid the top 8 of the exact remainder x - hi,
+// lo the rest (at most 8 significant bits, so bf16 holds it exactly).
+__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hb = __float_as_uint(x) & 0xFFFF0000u;
+  const float r1 = x - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  h = hb >> 16;
+  m = mb >> 16;
+  l = __float_as_uint(r2) >> 16;
+}
+
 // Row `row` of a table stored as WT, converted to fp32 element `i`.
 template <typename WT> __device__ __forceinline__ float load_elem(const WT* p, size_t i);
 template <> __device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }

@@ -218,9 +218,23 @@ bool mfma_fits(int mode, const GemvArgs& a) {
   return mode == kSwiGLU ? a.N % (kMfmaTN / 2) == 0 : a.N % kMfmaTN == 0;
 }
 
+// bf16 matrix-core tiles fit: K an even number of 32-wide chunks per wave
+// (four waves), columns whole 64-wide tiles (SwiGLU: 32 gate + 32 up rows).
+bool bgemm_fits(int mode, const GemvArgs& a) {
+  if (a.K % 256) return false;
+  return mode == kSwiGLU ? a.N % 32 == 0 : a.N % 64 == 0;
+}
+
 // One skinny projection: Y (op) W . rows(X).  Many rows: matrix-core tiles.
 int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
   if (a.M <= 0) return CP_SPEC_OK;
+  if (h->sh.wdt == CP_SPEC_BF16 && mode != kHead && a.M >= kMfmaMinRows && bgemm_fits(mode, a)) {
+    // 32 x 64 tiles (16 x 64 when that still leaves few blocks)
+    const int cols = mode == kSwiGLU ? a.N * 2 : a.N;
+    const int fm = cols / 64 * ((a.M + 31) / 32) < kFillBlocks ? 1 : 2;
+    CPS_HIP(launch_bgemm_bf16(mode, fm, 4, a, dim3(cols / 64, (a.M + 16 * fm - 1) / (16 * fm)), s));
+    return CP_SPEC_OK;
+  }
   if (mode != kHead && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
     // the largest tile that still gives the chip enough blocks
     const int cols = mode == kSwiGLU ? a.N * 2 : a.N;  // tile columns (gate and up side by side)
@@ -330,6 +344,14 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
   a.norm_g = norm_g; a.eps = h->sh.eps; a.Y = logits; a.ldy = h->sh.V; a.head = head;
   a.head_stride = static_cast<long long>(h->sh.V) * h->sh.H; a.xnorm_out = xnorm_out;
   a.n_heads = h->sh.G - 1;
+  if (plan && h->sh.wdt == CP_SPEC_BF16 && bgemm_fits(kHead, a)) {
+    a.head_count = plan->count; a.head_rows = plan->rows; a.rows_cap = plan->cap;
+    // 16-row tiles while the heads' row lists are short, else 32
+    const int avg = (M + a.n_heads - 1) / a.n_heads;
+    const int fm = avg <= 16 ? 1 : 2;
+    CPS_HIP(launch_bgemm_bf16(kHead, fm, 4, a, dim3(a.N / 64, (plan->cap + 16 * fm - 1) / (16 * fm), a.n_heads), s));
+    return CP_SPEC_OK;
+  }
   if (plan && mfma_fits(kHead, a)) {
     a.head_count = plan->count; a.head_rows = plan->rows; a.rows_cap = plan->cap;
     // tiles by the average rows per head

@@ -154,6 +154,10 @@ hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid
 // block's four waves; K a multiple of 128).
 enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };
 hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
+// bf16 weights on the matrix cores: block tile (16 fm) x (16 fn), (fm, fn) in
+// {(1, 4), (2, 4), (2, 2)}, K a multiple of 256; grid (columns / tile, rows /
+// tile) or, lm_heads, (V / tile, row tiles, heads).
+hipError_t launch_bgemm_bf16(int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
 // Per-head row lists of the coming round (draft rows and verify rows).
 hipError_t launch_head_plan(const int* dhead, const int* thead, int B, int W, int R, int n_heads,
                             int* dcount, int* drows, int* tcount, int* trows, hipStream_t s);

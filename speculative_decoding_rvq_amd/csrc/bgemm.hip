@@ -3,11 +3,10 @@
 //
 // C[m][n] = sum_k x_m[k] * W[n][k], W row-major [out][in].
 //
-// Exactness: every fp32 activation is split into three bf16 pieces by
-// truncation, x = hi + mid + lo (split3), and the tile runs
-// v_mfma_f32_16x16x32_bf16 once per piece into one fp32 accumulator.
-// bf16 x bf16 products are exact in fp32, so the result is the fp32 dot
-// product up to summation order.
+// Every fp32 activation is split into three bf16 pieces by truncation,
+// x = hi + mid + lo (split3), and the tile runs v_mfma_f32_16x16x32_bf16
+// once per piece into one fp32 accumulator.  bf16 x bf16 products are exact
+// in fp32, so the result is the fp32 dot product up to summation order.
 //
 // Tiling: a block owns (16 FM) x (16 FN) outputs and its four wave64s split
 // K in quarters: a wave reads its activation and weight fragments straight
@@ -39,17 +38,17 @@ constexpr int kWaves = kBlock / kWave;  // 4: K quarters
 
 // Weight row read for output column n of the launch (SwiGLU tiles of TN
 // columns: TN/2 gate rows, then the matching up rows).
-template <int MODE, int TN>
-__device__ __forceinline__ const uint16_t* bweight_row(const GemvArgs& a, const uint16_t* W0, int n) {
+template <typename WT, int MODE, int TN>
+__device__ __forceinline__ const WT* bweight_row(const GemvArgs& a, const WT* W0, int n) {
   if (MODE == kQKV) {
-    const uint16_t* W1 = static_cast<const uint16_t*>(a.W1);
-    const uint16_t* W2 = static_cast<const uint16_t*>(a.W2);
+    const WT* W1 = static_cast<const WT*>(a.W1);
+    const WT* W2 = static_cast<const WT*>(a.W2);
     if (n < a.qdim) return W0 + static_cast<size_t>(n) * a.K;
     if (n < a.qdim + a.kvdim) return W1 + static_cast<size_t>(n - a.qdim) * a.K;
     return W2 + static_cast<size_t>(n - a.qdim - a.kvdim) * a.K;
   }
   if (MODE == kSwiGLU) {
-    const uint16_t* W1 = static_cast<const uint16_t*>(a.W1);
+    const WT* W1 = static_cast<const WT*>(a.W1);
     const int tile = n / TN, c = n % TN;
     const int f = tile * (TN / 2) + (c % (TN / 2));
     return (c < TN / 2 ? W0 : W1) + static_cast<size_t>(f) * a.K;
@@ -58,7 +57,8 @@ __device__ __forceinline__ const uint16_t* bweight_row(const GemvArgs& a, const 
 }
 
 template <int MODE, int FM, int FN, bool NORM>
-__global__ __launch_bounds__(kBlock) void bgemm_bf16_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
+  using WT = uint16_t;  // bf16 bit patterns
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ float part[kWaves][TM][TN + 1];
   __shared__ float ssq_s[kWaves][TM];
@@ -71,15 +71,13 @@ __global__ __launch_bounds__(kBlock) void bgemm_bf16_kernel(const GemvArgs a) {
   const int n0 = blockIdx.x * TN;
 
   // ---- the block's activation rows ----
-  const uint16_t* W0 = static_cast<const uint16_t*>(a.W0);
+  const WT* W0 = static_cast<const WT*>(a.W0);
   int count;
   if (MODE == kHead) {
-    const int j = blockIdx.z;  // head j+1
-    count = a.head_count[j] - blockIdx.y * TM;
+    const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
+    __shared__ int red_h[4];
+    count = head_rows_slice(a.head, a.M, j + 1, blockIdx.y * TM, TM, rows_s, red_h);
     if (count <= 0) return;
-    count = min(count, TM);
-    if (tid < TM)
-      rows_s[tid] = tid < count ? a.head_rows[static_cast<size_t>(j) * a.rows_cap + blockIdx.y * TM + tid] : -1;
     W0 = W0 + static_cast<size_t>(j) * static_cast<size_t>(a.head_stride);
   } else {
     const int m0 = blockIdx.y * TM;
@@ -97,16 +95,16 @@ __global__ __launch_bounds__(kBlock) void bgemm_bf16_kernel(const GemvArgs a) {
     xv[f] = row >= 0;
     xr[f] = a.X + static_cast<size_t>(row >= 0 ? row / a.xdiv : 0) * a.ldx;
   }
-  const uint16_t* wr[FN];
+  const WT* wr[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) wr[f] = bweight_row<MODE, TN>(a, W0, n0 + 16 * f + li);
+  for (int f = 0; f < FN; ++f) wr[f] = bweight_row<WT, MODE, TN>(a, W0, n0 + 16 * f + li);
   const int cw = a.K / 32 / kWaves;          // chunks of this wave (even)
   const int kbase = wave * cw * 32 + 8 * lg;  // lane's first k
 
   struct Frag {  // one chunk of this lane's operands (native vectors)
     floatx4 x[FM][2];
     floatx4 g[2];
-    u32x4 w[FN];
+    u32x4 w[FN];  // 8 bf16 per weight fragment
   };
   auto fetch = [&](int c) __attribute__((always_inline)) {
     Frag f;
@@ -137,23 +135,24 @@ __global__ __launch_bounds__(kBlock) void bgemm_bf16_kernel(const GemvArgs a) {
   for (int f = 0; f < FM; ++f) ss[f] = 0.0f;
 
   auto compute = [&](const Frag& fr) __attribute__((always_inline)) {
+    float xs[FM][8];  // this lane's x (* g) values of the chunk
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = xv[f] ? fr.x[f][e / 4][e % 4] : 0.0f;
+        ss[f] += x * x;
+        xs[f][e] = NORM ? x * fr.g[e / 4][e % 4] : x;
+      }
     bf16x8 ap[FM][3];
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
       uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        float x0 = xv[f] ? fr.x[f][e / 4][e % 4] : 0.0f;
-        float x1 = xv[f] ? fr.x[f][e / 4][e % 4 + 1] : 0.0f;
-        ss[f] += x0 * x0;
-        ss[f] += x1 * x1;
-        if constexpr (NORM) {
-          x0 *= fr.g[e / 4][e % 4];
-          x1 *= fr.g[e / 4][e % 4 + 1];
-        }
         uint32_t h0, m0, l0, h1, m1, l1;
-        split3(x0, h0, m0, l0);
-        split3(x1, h1, m1, l1);
+        split3(xs[f][e], h0, m0, l0);
+        split3(xs[f][e + 1], h1, m1, l1);
         hp[e / 2] = h0 | (h1 << 16);
         mp[e / 2] = m0 | (m1 << 16);
         lp[e / 2] = l0 | (l1 << 16);
@@ -279,10 +278,10 @@ __global__ __launch_bounds__(kBlock) void bgemm_bf16_kernel(const GemvArgs a) {
 template <int FM, int FN, bool NORM>
 hipError_t launch_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
   switch (mode) {
-    case kAdd: hipLaunchKernelGGL((bgemm_bf16_kernel<kAdd, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
-    case kSwiGLU: hipLaunchKernelGGL((bgemm_bf16_kernel<kSwiGLU, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
-    case kQKV: hipLaunchKernelGGL((bgemm_bf16_kernel<kQKV, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
-    case kHead: hipLaunchKernelGGL((bgemm_bf16_kernel<kHead, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
+    case kAdd: hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
+    case kSwiGLU: hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
+    case kQKV: hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
+    case kHead: hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -296,11 +295,12 @@ hipError_t launch_f(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bgemm_bf16(int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s) {
+// bf16 weights only: fp32 weights keep the fp32 kernels of mfma_impl.h,
+// which measured faster on the small fp32 shapes.
+hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  if (wdtype != CP_SPEC_BF16) return hipErrorInvalidValue;
   if (fm == 1 && fn == 4) return launch_f<1, 4>(mode, a, grid, s);
   if (fm == 2 && fn == 4) return launch_f<2, 4>(mode, a, grid, s);
-  if (fm == 1 && fn == 8) return launch_f<1, 8>(mode, a, grid, s);
-  if (fm == 2 && fn == 8) return launch_f<2, 8>(mode, a, grid, s);
   return hipErrorInvalidValue;
 }
 

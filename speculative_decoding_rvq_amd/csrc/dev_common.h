@@ -196,6 +196,25 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
   return base + inc - v;
 }
 
+// The rows of one lm_head: indices i < n, ascending, with head[i] == h.  The
+// block keeps positions [first, first + cap) of that list in rows[0..cap)
+// (-1 past its end) and returns how many it kept.  `red` is 4 ints of LDS.
+__device__ __forceinline__ int head_rows_slice(const int* head, int n, int h, int first, int cap, int* rows,
+                                               int* red) {
+  for (int i = threadIdx.x; i < cap; i += kBlock) rows[i] = -1;
+  int base = 0;
+  for (int r0 = 0; r0 < n; r0 += kBlock) {
+    const int i = r0 + threadIdx.x;
+    const bool hit = i < n && head[i] == h;
+    int total;
+    const int pos = base + block_exclusive_scan(hit ? 1 : 0, red, &total);  // barriers inside
+    if (hit && pos >= first && pos < first + cap) rows[pos - first] = i;
+    base += total;
+  }
+  __syncthreads();
+  return min(max(base - first, 0), cap);
+}
+
 // ------------------------------------------------------------- Philox ----
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11, section 4): ten rounds of
 // the 4-word multiply/xor S-box with a Weyl-advanced 2-word key.

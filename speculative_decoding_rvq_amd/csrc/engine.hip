@@ -39,7 +39,7 @@ struct Shape {
 
 struct Layout {
   size_t st, call, sstats, dhead, thead, pos, hstate, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
-      tlogits, p, tcode, tflags, rope, plan, total;
+      tlogits, p, tcode, tflags, rope, total;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -109,11 +109,6 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   return CP_SPEC_OK;
 }
 
-// Rows per head list: the draft/verify lists hold one row per stream, the
-// row-list form (head_logits entry point) one per input row.
-size_t plan_cap(const Shape& s) { return static_cast<size_t>(s.maxB) * s.R; }
-// dcount[G-1], tcount[G-1], drows[G-1][cap], trows[G-1][cap]
-size_t plan_ints(const Shape& s) { return 2 * static_cast<size_t>(s.G - 1) * (1 + plan_cap(s)); }
 
 // Streams from which the round's projections and heads run on the matrix
 // cores (64-row tiles); below it the GEMV streams each weight once per few rows.
@@ -152,7 +147,6 @@ Layout make_layout(const Shape& s) {
   l.tcode = take(B * R * i4);
   l.tflags = take(B * R * i4);
   l.rope = take(static_cast<size_t>(s.G) * (s.d / 2) * sizeof(float2));
-  l.plan = take(plan_ints(s) * i4);
   l.total = off;
   return l;
 }
@@ -229,10 +223,10 @@ bool bgemm_fits(int mode, const GemvArgs& a) {
 int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
   if (a.M <= 0) return CP_SPEC_OK;
   if (h->sh.wdt == CP_SPEC_BF16 && mode != kHead && a.M >= kMfmaMinRows && bgemm_fits(mode, a)) {
-    // 32 x 64 tiles (16 x 64 when that still leaves few blocks)
+    // bf16: 32 x 64 tiles (16 x 64 when that still leaves few blocks)
     const int cols = mode == kSwiGLU ? a.N * 2 : a.N;
     const int fm = cols / 64 * ((a.M + 31) / 32) < kFillBlocks ? 1 : 2;
-    CPS_HIP(launch_bgemm_bf16(mode, fm, 4, a, dim3(cols / 64, (a.M + 16 * fm - 1) / (16 * fm)), s));
+    CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, 4, a, dim3(cols / 64, (a.M + 16 * fm - 1) / (16 * fm)), s));
     return CP_SPEC_OK;
   }
   if (mode != kHead && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
@@ -328,54 +322,34 @@ int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const in
   return CP_SPEC_OK;
 }
 
-// Head lists for `plan` (nullptr: per-row GEMV): counts and rows as laid
-// out by the head-plan kernel, `cap` rows per head.
-struct HeadPlan {
-  const int* count;
-  const int* rows;
-  int cap;
-};
-
 // lm_head logits of M rows (row m reads X row m / xdiv, head head[m]).
+// per_head > 0: on the matrix cores, rows grouped by head (each block finds
+// its head's rows itself), at most per_head rows per head; else per-row GEMV.
 int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv, const int* head,
-                const float* norm_g, float* xnorm_out, float* logits, const HeadPlan* plan = nullptr) {
+                const float* norm_g, float* xnorm_out, float* logits, int per_head = 0) {
   GemvArgs a{};
   a.W0 = h->heads; a.N = h->sh.V; a.K = h->sh.H; a.X = X; a.ldx = h->sh.H; a.xdiv = xdiv; a.M = M;
   a.norm_g = norm_g; a.eps = h->sh.eps; a.Y = logits; a.ldy = h->sh.V; a.head = head;
   a.head_stride = static_cast<long long>(h->sh.V) * h->sh.H; a.xnorm_out = xnorm_out;
   a.n_heads = h->sh.G - 1;
-  if (plan && h->sh.wdt == CP_SPEC_BF16 && bgemm_fits(kHead, a)) {
-    a.head_count = plan->count; a.head_rows = plan->rows; a.rows_cap = plan->cap;
-    // 16-row tiles while the heads' row lists are short, else 32
+  if (per_head > 0 && h->sh.wdt == CP_SPEC_BF16 && bgemm_fits(kHead, a)) {
+    // bf16: 16-row tiles while the heads' row lists are short, else 32
     const int avg = (M + a.n_heads - 1) / a.n_heads;
     const int fm = avg <= 16 ? 1 : 2;
-    CPS_HIP(launch_bgemm_bf16(kHead, fm, 4, a, dim3(a.N / 64, (plan->cap + 16 * fm - 1) / (16 * fm), a.n_heads), s));
+    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, fm, 4, a,
+                         dim3(a.N / 64, (per_head + 16 * fm - 1) / (16 * fm), a.n_heads), s));
     return CP_SPEC_OK;
   }
-  if (plan && mfma_fits(kHead, a)) {
-    a.head_count = plan->count; a.head_rows = plan->rows; a.rows_cap = plan->cap;
+  if (per_head > 0 && mfma_fits(kHead, a)) {
     // tiles by the average rows per head
     const int avg = (M + a.n_heads - 1) / a.n_heads;
     const bool big = a.N / 64 * ((avg + 63) / 64) * a.n_heads >= kFillBlocks || a.K % (4 * kMfmaTK);
     const int t = big ? 64 : 32;
-    const dim3 grid(a.N / t, (plan->cap + t - 1) / t, a.n_heads);
+    const dim3 grid(a.N / t, (per_head + t - 1) / t, a.n_heads);
     CPS_HIP(launch_mfma(h->sh.wdt, kHead, big ? kTile64 : kTile32, a, grid, s));
     return CP_SPEC_OK;
   }
   return gemv(h, s, kHead, a);
-}
-
-// Head-plan buffers (dcount, tcount, drows, trows), `cap` rows per head.
-void plan_ptrs(const cp_spec* h, int cap, HeadPlan* d, HeadPlan* t, int** dc, int** dr, int** tc,
-               int** tr) {
-  const size_t nh = h->sh.G - 1;
-  int* base = h->at<int>(h->lo.plan);
-  *dc = base;
-  *tc = base + nh;
-  *dr = base + 2 * nh;
-  *tr = base + 2 * nh + nh * plan_cap(h->sh);
-  *d = HeadPlan{*dc, *dr, cap};
-  *t = HeadPlan{*tc, *tr, cap};
 }
 
 // The whole round for B streams: draft GEMV -> draft sample -> verify pass ->
@@ -384,21 +358,16 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
   const Shape& sh = h->sh;
   const RoundArgs r = h->round_args(B);
   int rc;
-  HeadPlan dp, tp, *dplan = nullptr, *tplan = nullptr;
-  if (B >= kMfmaMinStreams) {
-    int *dc, *dr, *tc, *tr;
-    plan_ptrs(h, B, &dp, &tp, &dc, &dr, &tc, &tr);
-    CPS_HIP(launch_head_plan(r.dhead, r.thead, B, sh.W, sh.R, sh.G - 1, dc, dr, tc, tr, s));
-    dplan = &dp;
-    tplan = &tp;
-  }
+  // many streams: lm_heads on the matrix cores, at most one row per stream
+  // and head in each of the draft and verify row sets
+  const int per_head = B >= kMfmaMinStreams ? B : 0;
   if (sh.N >= 2) {
-    if ((rc = head_logits(h, s, B * sh.W, r.hstate, sh.W, r.dhead, nullptr, nullptr, r.dlogits, dplan)))
+    if ((rc = head_logits(h, s, B * sh.W, r.hstate, sh.W, r.dhead, nullptr, nullptr, r.dlogits, per_head)))
       return rc;
     CPS_HIP(launch_draft_topk(r, s));
   }
   if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv)))) return rc;
-  if ((rc = head_logits(h, s, B * sh.R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, tplan))) return rc;
+  if ((rc = head_logits(h, s, B * sh.R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head))) return rc;
   CPS_HIP(launch_target_topk(r, s));
   CPS_HIP(launch_round_accept(r, s));
   return CP_SPEC_OK;
@@ -577,15 +546,9 @@ int cp_spec_head_logits(cp_spec* h, void* stream, int32_t n_rows, const float* d
   if (n_rows == 0) return CP_SPEC_OK;
   if (!d_x || !d_head || !d_logits) return fail(CP_SPEC_EINVAL, "null pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  HeadPlan dp, tp, *plan = nullptr;
-  if (n_rows >= kMfmaMinRows) {  // rows grouped by head for the matrix cores
-    int *dc, *dr, *tc, *tr;
-    plan_ptrs(h, n_rows, &dp, &tp, &dc, &dr, &tc, &tr);
-    CPS_HIP(launch_head_plan(d_head, nullptr, n_rows, 1, 0, h->sh.G - 1, dc, dr, tc, tr, s));
-    plan = &dp;
-  }
+  // many rows: grouped by head on the matrix cores (any number per head)
   return head_logits(h, s, n_rows, d_x, 1, d_head, apply_final_norm ? h->fnorm : nullptr, nullptr,
-                     d_logits, plan);
+                     d_logits, n_rows >= kMfmaMinRows ? n_rows : 0);
 }
 
 int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows, const float* d_logits,
@@ -653,10 +616,8 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
     }
   // head tables for the draft GEMV: variant v uses heads 1 + (v*W + t) % (G-1)
   const bool grouped = B >= kMfmaMinStreams;
-  const size_t var_ints = 2 * static_cast<size_t>(G - 1) * (1 + B);  // one variant's head plan
-  const size_t p_ints = static_cast<size_t>(B) * R * sh.V;            // scratch: target probs
-  const int nvar = grouped ? static_cast<int>(std::max<size_t>(1, std::min<size_t>(G - 1, p_ints / var_ints)))
-                           : G - 1;
+  const int per_head = grouped ? B : 0;
+  const int nvar = G - 1;
   std::vector<int> dvar(static_cast<size_t>(nvar) * B * W);
   for (int v = 0; v < nvar; ++v)
     for (int b = 0; b < B; ++b)
@@ -665,23 +626,6 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
   CPS_HIP(hipMemcpyAsync(r.pos, pos.data(), pos.size() * sizeof(int), hipMemcpyHostToDevice, s));
   CPS_HIP(hipMemcpyAsync(r.thead, thead.data(), thead.size() * sizeof(int), hipMemcpyHostToDevice, s));
   CPS_HIP(hipMemcpyAsync(d_dvar, dvar.data(), dvar.size() * sizeof(int), hipMemcpyHostToDevice, s));
-  // grouped heads: the verify rows' plan in the round's buffer, one plan per
-  // draft variant in the target-probability scratch
-  HeadPlan tplan{}, dummy{};
-  std::vector<HeadPlan> dplans;
-  if (grouped) {
-    int *dc, *dr, *tc, *tr;
-    plan_ptrs(h, B, &dummy, &tplan, &dc, &dr, &tc, &tr);
-    CPS_HIP(launch_head_plan(r.dhead, r.thead, B, W, R, G - 1, dc, dr, tc, tr, s));
-    for (int v = 0; v < nvar; ++v) {
-      int* base = reinterpret_cast<int*>(r.p) + v * var_ints;
-      int* vc = base;
-      int* vr = base + 2 * (G - 1);
-      CPS_HIP(launch_head_plan(d_dvar + static_cast<size_t>(v) * B * W, nullptr, B, W, 0, G - 1, vc, vr,
-                               vc + (G - 1), vr + static_cast<size_t>(G - 1) * B, s));
-      dplans.push_back(HeadPlan{vc, vr, B});
-    }
-  }
   CPS_HIP(hipStreamSynchronize(s));
 
   const double ws = sh.wdt == CP_SPEC_BF16 ? 2.0 : 4.0;
@@ -724,10 +668,9 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
   auto launch = [&](hipStream_t ls, int i) -> int {
     if (kind == CP_SPEC_KERNEL_DRAFT_HEADS)
       return head_logits(h, ls, B * W, r.hstate, W, d_dvar + static_cast<size_t>(i % nvar) * B * W,
-                         nullptr, nullptr, r.dlogits, grouped ? &dplans[i % nvar] : nullptr);
+                         nullptr, nullptr, r.dlogits, per_head);
     if (kind == CP_SPEC_KERNEL_TARGET_HEADS)
-      return head_logits(h, ls, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits,
-                         grouped ? &tplan : nullptr);
+      return head_logits(h, ls, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head);
     return layer_kernel(h, ls, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv));
   };
   int rc = launch(s, 0);  // warm the launch path

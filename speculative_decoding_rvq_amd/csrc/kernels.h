@@ -52,10 +52,6 @@ struct GemvArgs {
   int n_heads;          // G-1
   long long head_stride;  // elements per head matrix (V*H)
   float* xnorm_out;     // nullable: normalised rows written here ([M][K])
-  // kHead on the matrix cores: rows grouped by head
-  const int* head_count;  // [n_heads] rows using each head
-  const int* head_rows;   // [n_heads][rows_cap] row indices, stream order
-  int rows_cap;
   // tiling (host-chosen)
   int kt;     // threads covering one row's K (64/128/256)
   int units;  // number of RPG-row output units
@@ -154,13 +150,11 @@ hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid
 // block's four waves; K a multiple of 128).
 enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };
 hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
-// bf16 weights on the matrix cores: block tile (16 fm) x (16 fn), (fm, fn) in
-// {(1, 4), (2, 4), (2, 2)}, K a multiple of 256; grid (columns / tile, rows /
-// tile) or, lm_heads, (V / tile, row tiles, heads).
-hipError_t launch_bgemm_bf16(int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
-// Per-head row lists of the coming round (draft rows and verify rows).
-hipError_t launch_head_plan(const int* dhead, const int* thead, int B, int W, int R, int n_heads,
-                            int* dcount, int* drows, int* tcount, int* trows, hipStream_t s);
+// Matrix-core projections with in-block split-K (bf16 weights):
+// block tile (16 fm) x (16 fn), (fm, fn) in {(1, 4), (2, 4)}, K a multiple
+// of 256; grid (columns / tile, rows / tile) or, lm_heads, (V / tile, row
+// tiles, heads).
+hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
 // LDS the attention kernel needs, and raising its limit above 64 KB (once,
 // before any launch).
 size_t attention_smem_bytes(int G, int d, int R, int group);

@@ -26,48 +26,6 @@ hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 g
 }
 
 // ---------------------------------------------------------------------------
-// Rows grouped by lm_head: block j lists, in stream order, the draft rows
-// (b*W + t) and verify rows (b*R + r) whose head is j+1 (thead nullable).
-// Within a round a stream has at most one row per head in each list; the
-// lists hold B entries per head (W = 1 turns dhead into a plain row list).
-__global__ __launch_bounds__(kBlock) void head_plan_kernel(const int* dhead, const int* thead, int B,
-                                                           int W, int R, int* dcount, int* drows,
-                                                           int* tcount, int* trows) {
-  __shared__ int red[8];
-  const int j = blockIdx.x, h = j + 1;
-  int dbase = 0, tbase = 0;
-  for (int b0 = 0; b0 < B; b0 += kBlock) {
-    const int b = b0 + threadIdx.x;
-    int drow = -1, trow = -1;
-    if (b < B) {
-      for (int t = 0; t < W; ++t)
-        if (dhead[b * W + t] == h) drow = b * W + t;
-      for (int r = 0; thead && r < R; ++r)
-        if (thead[b * R + r] == h) trow = b * R + r;
-    }
-    int dtot, ttot;
-    const int doff = block_exclusive_scan(drow >= 0 ? 1 : 0, red, &dtot);
-    const int toff = block_exclusive_scan(trow >= 0 ? 1 : 0, red + 4, &ttot);
-    if (drow >= 0) drows[static_cast<size_t>(j) * B + dbase + doff] = drow;
-    if (trow >= 0) trows[static_cast<size_t>(j) * B + tbase + toff] = trow;
-    dbase += dtot;
-    tbase += ttot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    dcount[j] = dbase;
-    tcount[j] = tbase;
-  }
-}
-
-hipError_t launch_head_plan(const int* dhead, const int* thead, int B, int W, int R, int n_heads,
-                            int* dcount, int* drows, int* tcount, int* trows, hipStream_t s) {
-  hipLaunchKernelGGL(head_plan_kernel, dim3(n_heads), dim3(kBlock), 0, s, dhead, thead, B, W, R, dcount,
-                     drows, tcount, trows);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Causal attention over the in-frame positions of one stream and one KV head.
 //
 // Phase 1 issues every global load at once (float4): K of positions

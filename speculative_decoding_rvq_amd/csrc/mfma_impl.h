@@ -110,12 +110,10 @@ __global__ __launch_bounds__(kBlock) void mfma_gemm_kernel(const GemvArgs a) {
   const WT* W0 = static_cast<const WT*>(a.W0);
   int count;
   if (MODE == kHead) {
-    const int j = blockIdx.z;  // head j+1
-    count = a.head_count[j] - blockIdx.y * kTM;
+    const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
+    __shared__ int red_h[4];
+    count = head_rows_slice(a.head, a.M, j + 1, blockIdx.y * kTM, kTM, rows_s, red_h);
     if (count <= 0) return;
-    count = min(count, kTM);
-    if (tid < kTM)
-      rows_s[tid] = tid < count ? a.head_rows[static_cast<size_t>(j) * a.rows_cap + blockIdx.y * kTM + tid] : -1;
     W0 = W0 + static_cast<size_t>(j) * static_cast<size_t>(a.head_stride);
   } else {
     const int m0 = blockIdx.y * kTM;
@@ -337,12 +335,10 @@ __global__ __launch_bounds__(kBlock) void mfma_splitk_kernel(const GemvArgs a) {
   const WT* W0 = static_cast<const WT*>(a.W0);
   int count;
   if (MODE == kHead) {
-    const int j = blockIdx.z;
-    count = a.head_count[j] - blockIdx.y * TM;
+    const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
+    __shared__ int red_h[4];
+    count = head_rows_slice(a.head, a.M, j + 1, blockIdx.y * TM, TM, rows_s, red_h);
     if (count <= 0) return;
-    count = min(count, TM);
-    if (tid < TM)
-      rows_s[tid] = tid < count ? a.head_rows[static_cast<size_t>(j) * a.rows_cap + blockIdx.y * TM + tid] : -1;
     W0 = W0 + static_cast<size_t>(j) * static_cast<size_t>(a.head_stride);
   } else {
     const int m0 = blockIdx.y * TM;

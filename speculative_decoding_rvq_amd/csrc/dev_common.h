@@ -145,6 +145,15 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// LDS written by some lanes of a wave, then read by others of the same wave:
+// a wave's LDS accesses are performed in order, so only the compiler needs
+// holding back.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Block-wide reductions over 256 threads; `red` is 4+ words of LDS.  Every
 // thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -267,26 +276,48 @@ constexpr uint32_t kFlagTopk = 1u, kFlagArgmax = 2u, kFlagCdf = 4u, kFlagAccept 
 // entries (weights, then their running sums).
 struct SampleSmem {
   int idx[4096];
-  float w[4096];
+  alignas(16) float w[4096];
   int red[4];
   int result[2];
 };
 
-// Wave 0: Sample over the `total` compacted entries of sm (ascending code
-// order).  The running sum is formed once, sequentially in float32 (every
-// lane adds the same values in the same order, 32 entries in registers at a
-// time) and stored over the weights; the first running sum above t = u * sum
-// is then found 64 entries at a time with a ballot.
-__device__ __forceinline__ void wave0_walk(SampleSmem& sm, int total, float u) {
-  const int lane = threadIdx.x;
-  int code = -1, near = 0;
-  if (total > 0) {
+// One wave: Sample over the list w[0..total) in list order (entries with
+// w = 0 are skipped, as Sample skips non-positive weights).  Lane 0 turns w
+// into its running sums in place, sequentially in float32; t = u * sum; the
+// first running sum above t is then found 64 entries at a time by ballot.
+// *code = idx of the chosen entry (-1 if no entry is positive); *near = the
+// CDF near-tie flag (t within 1e-5 * sum of a boundary of the chosen entry
+// that has a positive entry on its other side; positions among the positive
+// entries come from per-block positivity masks, lane c holding block c's).
+// Needs: w 16-byte aligned and zero from total up to the next multiple of 32;
+// total <= 4096; all 64 lanes active.
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  return (static_cast<uint64_t>(lane_u(static_cast<uint32_t>(v >> 32), l)) << 32) |
+         lane_u(static_cast<uint32_t>(v), l);
+}
+
+template <typename IT>
+__device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, float u, int* code, int* near) {
+  const int lane = threadIdx.x % kWave;
+  *code = -1;
+  *near = 0;
+  uint64_t mine = 0;  // positivity mask of block `lane`
+  int npos = 0, last = -1;
+  for (int c0 = 0, c = 0; c0 < total; c0 += kWave, ++c) {
+    const int i = c0 + lane;
+    const uint64_t m = __ballot(i < total && w[min(i, total - 1)] > 0.0f);
+    if (lane == c) mine = m;
+    npos += __popcll(m);
+    if (m) last = c0 + 63 - __clzll(static_cast<long long>(m));
+  }
+  if (npos == 0) return;
+  if (lane == 0) {
     float carry = 0.0f;
     for (int c0 = 0; c0 < total; c0 += 32) {
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; i += 4) {
-        const float4 q = *reinterpret_cast<const float4*>(&sm.w[c0 + i]);
+        const float4 q = *reinterpret_cast<const float4*>(&w[c0 + i]);
         v[i] = q.x;
         v[i + 1] = q.y;
         v[i + 2] = q.z;
@@ -294,41 +325,48 @@ __device__ __forceinline__ void wave0_walk(SampleSmem& sm, int total, float u) {
       }
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        carry = carry + (c0 + i < total ? v[i] : 0.0f);
+        carry = carry + v[i];
         v[i] = carry;
       }
-      if (lane == 0) {
 #pragma unroll
-        for (int i = 0; i < 32; i += 4)
-          *reinterpret_cast<float4*>(&sm.w[c0 + i]) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
-      }
+      for (int i = 0; i < 32; i += 4)
+        *reinterpret_cast<float4*>(&w[c0 + i]) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
     }
-    const float tot = carry;
-    const float t = u * tot;
-    int pos = -1;
-    for (int c0 = 0; c0 < total; c0 += kWave) {
-      const int i = c0 + lane;
-      const uint64_t m = __ballot(i < total && t < sm.w[i]);
-      if (m != 0) {
-        pos = c0 + __ffsll(static_cast<unsigned long long>(m)) - 1;
-        break;
-      }
-    }
-    const bool found = pos >= 0;
-    if (!found) pos = total - 1;  // t == sum after rounding: the last entry owns the top end
-    const float run = sm.w[pos];
-    const float before = pos > 0 ? sm.w[pos - 1] : 0.0f;
-    const double eps = static_cast<double>(tot) * kEpsCdf;
-    if (found) {
-      const bool lo = pos > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps;
-      const bool hi = pos + 1 < total && fabs(static_cast<double>(run) - static_cast<double>(t)) < eps;
-      near = (lo || hi) ? 1 : 0;
-    } else {
-      near = (total > 1 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps) ? 1 : 0;
-    }
-    code = sm.idx[pos];
   }
-  if (lane == 0) {
+  wave_lds_sync();
+  const float tot = w[total - 1];
+  const float t = u * tot;
+  const double eps = static_cast<double>(tot) * kEpsCdf;
+  for (int c0 = 0, c = 0; c0 < total; c0 += kWave, ++c) {
+    const int i = c0 + lane;
+    const uint64_t hit = __ballot(i < total && t < w[min(i, total - 1)]);
+    if (hit) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      const int pos = c0 + l;
+      const float run = w[pos];
+      const float before = pos > 0 ? w[pos - 1] : 0.0f;
+      // positive entries before the chosen one
+      const int pb = wave_sum_i(lane < c ? __popcll(mine) : 0) +
+                     __popcll(lane_u64(mine, c) & ((1ull << l) - 1ull));
+      const bool lo = pb > 0 && fabs(static_cast<double>(t) - static_cast<double>(before)) < eps;
+      const bool hi = pb + 1 < npos && fabs(static_cast<double>(run) - static_cast<double>(t)) < eps;
+      *code = static_cast<int>(idx[pos]);
+      *near = (lo || hi) ? 1 : 0;
+      return;
+    }
+  }
+  // t == sum after rounding: the last positive entry owns the top end
+  const float before_last = last > 0 ? w[last - 1] : 0.0f;
+  *code = static_cast<int>(idx[last]);
+  *near = (npos > 1 && fabs(static_cast<double>(t) - static_cast<double>(before_last)) < eps) ? 1 : 0;
+}
+
+// Wave 0: Sample over the `total` compacted entries of sm (ascending code
+// order); the result goes to sm.result.
+__device__ __forceinline__ void wave0_walk(SampleSmem& sm, int total, float u) {
+  int code, near;
+  list_draw(sm.w, sm.idx, total, u, &code, &near);
+  if (threadIdx.x == 0) {
     sm.result[0] = code;
     sm.result[1] = near;
   }
@@ -361,6 +399,7 @@ __device__ __forceinline__ int sample_regs(const float (&wv)[VPT], float u, Samp
       ++off;
     }
   }
+  if (tid < 32 && total + tid < ((total + 31) & ~31)) sm.w[total + tid] = 0.0f;  // pad for the walk
   lds_sync();
   if (tid < kWave) wave0_walk(sm, total, u);
   lds_sync();

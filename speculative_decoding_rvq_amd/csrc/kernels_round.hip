@@ -202,26 +202,45 @@ hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int row
 // ---------------------------------------------------------------------------
 // Component: n_rows independent rows.
 __global__ __launch_bounds__(kBlock) void topk_rows_kernel(const TopkArgs a) {
-  __shared__ TopkSmem sm;
+  extern __shared__ float4 row_dyn[];
+  __shared__ SelSmem S;
+  __shared__ uint64_t red64[4];
+  __shared__ uint32_t red32[4];
   const int r = blockIdx.x;
   const float* z = a.logits + static_cast<size_t>(r) * a.V;
   float* pr = a.probs ? a.probs + static_cast<size_t>(r) * a.V : nullptr;
   const bool samp = a.u != nullptr && !a.greedy;
   const float u = samp ? a.u[r] : 0.0f;
-  TopkResult res{-1, 0u};
   dispatch_vpt(a.V, [&](auto vpt) {
-    float pvd[decltype(vpt)::value];
-    res = topk_row<decltype(vpt)::value>(z, a.k, a.T, a.greedy != 0, samp, u, pr, sm, pvd);
+    constexpr int VPT = decltype(vpt)::value;
+    float zv[VPT];
+    load_row<VPT>(z, zv);
+    if (a.greedy) {
+      const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
+      if (threadIdx.x == 0) {
+        if (a.codes) a.codes[r] = res.code;
+        if (a.flags) a.flags[r] = res.flags;
+      }
+      return;
+    }
+    const RowLds L = row_lds(row_dyn, a.V, false);
+    store_row<VPT>(zv, L.z);
+    int total;
+    uint32_t flags = 0;
+    if (!topk_list<VPT>(zv, a.k, a.T, L, S, pr, &total, &flags)) return;
+    int code = -1, near = 0;
+    if (samp) list_draw(L.lw, L.lidx, total, u, &code, &near);
+    if (near) flags |= kFlagCdf;
+    if (threadIdx.x == 0) {
+      if (a.codes) a.codes[r] = code;
+      if (a.flags) a.flags[r] = flags;
+    }
   });
-  if (threadIdx.x == 0) {
-    if (a.codes) a.codes[r] = res.code;
-    if (a.flags) a.flags[r] = res.flags;
-  }
 }
 
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(a.n_rows), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(a.n_rows), dim3(kBlock), row_lds_bytes(a.V, false), s, a);
   return hipGetLastError();
 }
 
@@ -301,7 +320,9 @@ __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a)
   __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
   __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
   __shared__ int targ[CP_SPEC_MAX_WINDOW + 1];
-  __shared__ TopkSmem tsm;
+  __shared__ SampleSmem samp;
+  __shared__ uint64_t red64[4];
+  __shared__ uint32_t red32[4];
   const int b = blockIdx.x;
   const int W = a.W, V = a.V;
   const int gamma = min(max(a.gamma[b], 0), W);
@@ -315,9 +336,9 @@ __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a)
     for (int r = 0; r <= gamma; ++r) {
       TopkResult res{-1, 0u};
       dispatch_vpt(V, [&](auto vpt) {
-        float pvd[decltype(vpt)::value];
-    res = topk_row<decltype(vpt)::value>(p + static_cast<size_t>(r) * V, 1, 1.0f, true, false,
-                                             0.0f, nullptr, tsm, pvd);
+        float zv[decltype(vpt)::value];
+        load_row<decltype(vpt)::value>(p + static_cast<size_t>(r) * V, zv);
+        res = argmax_regs<decltype(vpt)::value>(zv, red64, red32);
       });
       if (threadIdx.x == 0) targ[r] = res.code;
       __syncthreads();
@@ -334,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a)
   __syncthreads();
   int n_acc = 0;
   const int n = accept_scan(gamma, draft, q, p, V, a.greedy != 0, ua, ut,
-                            [&](int r) { return targ[r]; }, codes, anear, cnear, &n_acc, tsm.samp,
+                            [&](int r) { return targ[r]; }, codes, anear, cnear, &n_acc, samp,
                             dec, pq);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -368,6 +389,36 @@ __device__ __forceinline__ void embed_row(const RoundArgs& r, int table, int cod
   } else {
     const float* e = static_cast<const float*>(r.embed) + off;
     for (int i = threadIdx.x; i < r.H; i += kBlock) dst[i] = e[i];
+  }
+}
+
+// The same by threads i = 0..n-1 of a group (8 bf16 or 4 fp32 values per
+// thread per step when the rows are 16-byte aligned).
+__device__ __forceinline__ void embed_row_span(const RoundArgs& r, int table, int code, float* dst, int i0,
+                                               int n) {
+  code = min(max(code, 0), r.V - 1);
+  const size_t off = (static_cast<size_t>(table) * r.V + code) * r.H;
+  const bool dst_al = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+  if (r.wbf16) {
+    const uint16_t* e = static_cast<const uint16_t*>(r.embed) + off;
+    if ((r.H & 7) == 0 && dst_al && (reinterpret_cast<uintptr_t>(e) & 15u) == 0) {
+      for (int i = i0 * 8; i < r.H; i += n * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(e + i);
+        *reinterpret_cast<float4*>(dst + i) = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+        *reinterpret_cast<float4*>(dst + i + 4) =
+            make_float4(bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w));
+      }
+    } else {
+      for (int i = i0; i < r.H; i += n) dst[i] = bf16_to_f32(e[i]);
+    }
+  } else {
+    const float* e = static_cast<const float*>(r.embed) + off;
+    if ((r.H & 3) == 0 && dst_al && (reinterpret_cast<uintptr_t>(e) & 15u) == 0) {
+      for (int i = i0 * 4; i < r.H; i += n * 4)
+        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(e + i);
+    } else {
+      for (int i = i0; i < r.H; i += n) dst[i] = e[i];
+    }
   }
 }
 
@@ -428,7 +479,10 @@ hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t 
 // Draft distributions q_t and proposals d_t of every stream (block (t-1, b)),
 // plus the verify input row E_{s+t}[d_t].
 __global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
-  __shared__ TopkSmem sm;
+  extern __shared__ float4 row_dyn[];
+  __shared__ SelSmem S;
+  __shared__ uint64_t red64[4];
+  __shared__ uint32_t red32[4];
   const int t = blockIdx.x + 1, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.W + (t - 1);
   dispatch_vpt(r.V, [&](auto vpt) {
@@ -437,24 +491,48 @@ __global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
     load_row<VPT>(r.dlogits + row * r.V, zv);  // before the state: the row always exists
     const StreamState st = r.st[b];
     if (st.mode != kModeSpec) return;
-    // verify row 0 = E_s[c_s], gathered while the draft rows are sampled
-    if (t == 1) embed_row(r, st.s, st.last, r.X + static_cast<size_t>(b) * r.R * r.H);
-    if (t > st.gamma) return;
-    const float u = frame_uniform(frame_seed(st), st.s + t, kDraft);
-    float pv[VPT];
-    const TopkResult res = topk_regs<VPT>(zv, r.top_k, r.T, r.greedy != 0, r.greedy == 0, u,
-                                          r.q + row * r.V, sm, pv);
-    if (threadIdx.x == 0) {
-      r.dcode[row] = res.code;
-      r.dflags[row] = res.flags;
+    // verify row 0 = E_s[c_s]: gathered by the block of offset 1, while the
+    // draft rows are sampled
+    float* x0 = r.X + static_cast<size_t>(b) * r.R * r.H;
+    if (t > st.gamma) {  // gamma = 0: only row 0 to fill
+      if (t == 1) embed_row(r, st.s, st.last, x0);
+      return;
     }
-    embed_row(r, st.s + t, res.code, r.X + (static_cast<size_t>(b) * r.R + t) * r.H);
+    float* xrow = r.X + (static_cast<size_t>(b) * r.R + t) * r.H;
+    if (r.greedy) {
+      if (t == 1) embed_row(r, st.s, st.last, x0);
+      const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
+      if (threadIdx.x == 0) {
+        r.dcode[row] = res.code;
+        r.dflags[row] = res.flags;
+      }
+      embed_row(r, st.s + t, res.code, xrow);
+      return;
+    }
+    const RowLds L = row_lds(row_dyn, r.V, false);
+    store_row<VPT>(zv, L.z);
+    const float u = frame_uniform(frame_seed(st), st.s + t, kDraft);
+    int total;
+    uint32_t flags = 0;
+    if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, r.q + row * r.V, &total, &flags)) {
+      if (t == 1) embed_row_span(r, st.s, st.last, x0, threadIdx.x - kWave, kBlock - kWave);
+      return;
+    }
+    // wave 0 finishes the row: the draw, then the next input row
+    int code, near;
+    list_draw(L.lw, L.lidx, total, u, &code, &near);
+    if (near) flags |= kFlagCdf;
+    if (threadIdx.x == 0) {
+      r.dcode[row] = code;
+      r.dflags[row] = flags;
+    }
+    embed_row_span(r, st.s + t, code, xrow, threadIdx.x, kWave);
   });
 }
 
 hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
   if (r.W <= 0 || r.N < 2) return hipSuccess;
-  hipLaunchKernelGGL(draft_topk_kernel, dim3(r.W, r.B), dim3(kBlock), 0, s, r);
+  hipLaunchKernelGGL(draft_topk_kernel, dim3(r.W, r.B), dim3(kBlock), row_lds_bytes(r.V, false), s, r);
   return hipGetLastError();
 }
 
@@ -472,8 +550,10 @@ hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
 constexpr uint32_t kRowAccepted = 1u << 8;
 
 __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) {
-  __shared__ TopkSmem sm;
-  __shared__ float pq_s[2];
+  extern __shared__ float4 row_dyn[];
+  __shared__ SelSmem S;
+  __shared__ uint64_t red64[4];
+  __shared__ uint32_t red32[4];
   const int rr = blockIdx.x, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.R + rr;
   dispatch_vpt(r.V, [&](auto vpt) {
@@ -483,8 +563,7 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     load_row<VPT>(r.tlogits + row * r.V, zv);  // before the row's head: the row always exists
     if (r.thead[row] <= 0) return;
     if (r.greedy) {
-      float pvd[VPT];
-      const TopkResult res = topk_regs<VPT>(zv, 1, 1.0f, true, false, 0.0f, nullptr, sm, pvd);
+      const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
       if (threadIdx.x == 0) {
         r.tcode[row] = res.code;
         r.tflags[row] = res.flags;
@@ -495,50 +574,52 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     const bool spec = st.mode == kModeSpec;
     const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
     const int depth = spec ? st.s + 1 + rr : 1;
-    // loads that do not wait for the softmax
-    float qv[VPT];
+    const RowLds L = row_lds(row_dyn, r.V, true);
+    store_row<VPT>(zv, L.z);
     int d = -1;
     if (test) {
+      // the draft distribution of offset rr + 1, for the test and the residual
       const float* qrow = r.q + (static_cast<size_t>(b) * r.W + rr) * r.V;
+      float qv[VPT];
 #pragma unroll
       for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
+      store_row<VPT>(qv, L.q);
       d = r.dcode[static_cast<size_t>(b) * r.W + rr];
     }
+    int total;
+    uint32_t flags = 0;
+    if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, nullptr, &total, &flags)) return;
+    // wave 0: the row's decision
     const uint64_t seed = frame_seed(st);
-    float pv[VPT];
-    const TopkResult res = topk_regs<VPT>(zv, r.top_k, r.T, false, false, 0.0f, nullptr, sm, pv);
-    uint32_t flags = res.flags & (kFlagTopk | kFlagArgmax);
-    int code;
-    bool near = false;
+    const float ut = frame_uniform(seed, depth, kTarget);
+    int code, near = 0;
     if (test) {
-      if (threadIdx.x == 0) {
-        pq_s[0] = 0.0f;  // a code outside [0, V) is rejected
-        pq_s[1] = 1.0f;
-      }
-      lds_sync();
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        if (base + j == d) {
-          pq_s[0] = pv[j];
-          pq_s[1] = qv[j];
-        }
-      }
-      lds_sync();
-      const float ratio = pq_s[0] / pq_s[1];
+      // p_r(d_t) is zero unless d_t is in the target's top-k set; a code
+      // outside [0, V) is rejected (p = 0, q = 1)
+      const float qd = (d >= 0 && d < r.V) ? L.q[d] : 1.0f;
+      float pd = 0.0f;
+      for (int i = threadIdx.x; i < total; i += kWave)
+        if (L.lidx[i] == d) pd = L.lw[i];
+      pd = wave_max(pd);
+      const float ratio = pd / qd;
       const float ua = frame_uniform(seed, depth, kAccept);
       if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) flags |= kFlagAccept;
       if (ua < ratio) {
         code = d;
         flags |= kRowAccepted;
       } else {
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) qv[j] = fmaxf(pv[j] - qv[j], 0.0f);  // the residual
-        const float ut = frame_uniform(seed, depth, kTarget);
-        code = sample_regs<VPT>(qv, ut, sm.samp, &near);
-        if (code < 0) code = sample_regs<VPT>(pv, ut, sm.samp, &near);
+        // the residual max(0, p - q) lives on the target's set (p is zero
+        // elsewhere); with no positive entry the draw falls back to p
+        bool pos = false;
+        for (int i = threadIdx.x; i < total; i += kWave) pos |= L.lw[i] - L.q[L.lidx[i]] > 0.0f;
+        if (__ballot(pos)) {
+          for (int i = threadIdx.x; i < total; i += kWave) L.lw[i] = fmaxf(L.lw[i] - L.q[L.lidx[i]], 0.0f);
+          wave_lds_sync();
+        }
+        list_draw(L.lw, L.lidx, total, ut, &code, &near);
       }
     } else {
-      code = sample_regs<VPT>(pv, frame_uniform(seed, depth, kTarget), sm.samp, &near);
+      list_draw(L.lw, L.lidx, total, ut, &code, &near);
     }
     if (near) flags |= kFlagCdf;
     if (threadIdx.x == 0) {
@@ -549,7 +630,7 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
 }
 
 hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s) {
-  hipLaunchKernelGGL(target_topk_kernel, dim3(r.R, r.B), dim3(kBlock), 0, s, r);
+  hipLaunchKernelGGL(target_topk_kernel, dim3(r.R, r.B), dim3(kBlock), row_lds_bytes(r.V, true), s, r);
   return hipGetLastError();
 }
 

@@ -18,8 +18,12 @@ OUT = os.path.join(PKG, "libcpspec.so")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 
 ARCH = "gfx950"
+# MFMA accumulators live in ordinary VGPRs: the unified register file holds
+# them, and the allocator no longer shuttles them between AGPRs inside the K
+# loops.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wno-unused-command-line-argument"]
 
 

@@ -1,23 +1,29 @@
 // Batched projections and lm_heads on the matrix cores: bf16 weights, fp32
 // activations (many activation rows: streams x verify rows).
 //
-// C[m][n] = sum_k x_m[k] * W[n][k], W row-major [out][in].
+// C[m][n] = sum_k x_m[k] * W[n][k].
 //
 // Every fp32 activation is split into three bf16 pieces by truncation,
 // x = hi + mid + lo (split3), and the tile runs v_mfma_f32_16x16x32_bf16
 // once per piece into one fp32 accumulator.  bf16 x bf16 products are exact
 // in fp32, so the result is the fp32 dot product up to summation order.
 //
-// Tiling: a block owns (16 FM) x (16 FN) outputs and its four wave64s split
-// K in quarters: a wave reads its activation and weight fragments straight
-// from global memory in the MFMA operand layout (lane l: row l % 16, k =
-// 8 (l / 16) .. +7 of each 32-wide chunk), splits its activation fragments
-// in registers and keeps two chunks of loads in flight.  Loads are
-// unconditional and held in native vectors, so the compiler's waits count
-// exactly the chunk being consumed.  The four partial tiles (and the rows'
-// partial sums of squares) meet in LDS and are added in wave order: the
-// result does not depend on timing.  Many small tiles fill the chip without
-// any cross-block reduction.
+// Memory traffic is what bounds these shapes, so both operands are read in
+// whole cache lines:
+//  * weights are packed once, at create, in MFMA fragment order: for each
+//    16-column tile and 32-wide K chunk, 64 lanes x 8 bf16 (1 KB) with lane
+//    l holding W[16 t + l % 16][32 c + 8 (l / 16) .. +7], chunk-major (the
+//    tiles of one chunk side by side).  A wave reads a B fragment as one
+//    contiguous 1 KB load;
+//  * activations are read row-major, a quad of lanes per 128-byte row
+//    segment, each lane holding the 8 values of one fragment entry; they are
+//    split in registers and written as whole entries to a small XOR-swizzled
+//    LDS stage private to the wave (no block barrier in the K loop, no bank
+//    conflicts on either side).
+// Tiling: a block owns (16 FM) x (16 FN) outputs; its four wave64s split K
+// in quarters and keep the next two chunks' loads in flight.  The partial
+// tiles (and the rows' partial sums of squares) meet in LDS and are added in
+// a fixed order, (w0 + w1) + (w2 + w3): the result does not depend on timing.
 //
 // RMSNorm: x * g is split; the rows' sums of squares are accumulated on the
 // way and 1/sqrt(mean + eps) scales the outputs.  Epilogues: residual add,
@@ -32,99 +38,113 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = kBlock / kWave;  // 4: K quarters
 
-// Weight row read for output column n of the launch (SwiGLU tiles of TN
-// columns: TN/2 gate rows, then the matching up rows).
-template <typename WT, int MODE, int TN>
-__device__ __forceinline__ const WT* bweight_row(const GemvArgs& a, const WT* W0, int n) {
-  if (MODE == kQKV) {
-    const WT* W1 = static_cast<const WT*>(a.W1);
-    const WT* W2 = static_cast<const WT*>(a.W2);
-    if (n < a.qdim) return W0 + static_cast<size_t>(n) * a.K;
-    if (n < a.qdim + a.kvdim) return W1 + static_cast<size_t>(n - a.qdim) * a.K;
-    return W2 + static_cast<size_t>(n - a.qdim - a.kvdim) * a.K;
-  }
-  if (MODE == kSwiGLU) {
-    const WT* W1 = static_cast<const WT*>(a.W1);
-    const int tile = n / TN, c = n % TN;
-    const int f = tile * (TN / 2) + (c % (TN / 2));
-    return (c < TN / 2 ? W0 : W1) + static_cast<size_t>(f) * a.K;
-  }
-  return W0 + static_cast<size_t>(n) * a.K;
+// Packed layouts are chunk-major: fragment (tile t, K chunk c) of a matrix
+// packed with NT tiles per chunk is the 1 KB at (c * NT + t) * 512 bf16, so
+// the fragments that waves load together (neighbouring tiles of one chunk)
+// are neighbours in memory and spread over the cache channels.
+__device__ __forceinline__ size_t frag_at(int t, int c, int NT) {
+  return (static_cast<size_t>(c) * NT + t) * 512;
 }
 
-template <int MODE, int FM, int FN, bool NORM>
+// Packed 16-column tile j of the block's tile: its tile index in W0 (or, for
+// the SwiGLU up half, in W1).
+template <int MODE, int FN>
+__device__ __forceinline__ int btile(int bx, int j) {
+  if (MODE == kSwiGLU) {  // gate tiles, then the matching up tiles
+    constexpr int H = FN / 2;
+    return bx * H + (j % H);
+  }
+  return bx * FN + j;
+}
+
+template <int MODE, int FM, int FN, bool NORM, bool PL>
 __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
-  using WT = uint16_t;  // bf16 bit patterns
   constexpr int TM = 16 * FM, TN = 16 * FN;
-  __shared__ float part[kWaves][TM][TN + 1];
-  __shared__ float ssq_s[kWaves][TM];
+  struct StageT { u32x4 f[kWaves][FM * 3][kWave]; };          // split fragments of one chunk
+  struct PartT { float v[kWaves][TM][TN + 1]; float ssq[kWaves][TM]; };
+  __shared__ union {
+    StageT stage;
+    PartT part;
+  } sm;
   __shared__ float rinv_s[TM];
   __shared__ int rows_s[TM];
+  __shared__ int pos_s[TM];  // Q/K/V: the rows' positions
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * TN;
 
   // ---- the block's activation rows ----
-  const WT* W0 = static_cast<const WT*>(a.W0);
+  const uint16_t* W0 = static_cast<const uint16_t*>(a.W0);
+  int tile0 = 0;  // lm_heads: the head's first tile
   int count;
   if (MODE == kHead) {
     const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
     __shared__ int red_h[4];
     count = head_rows_slice(a.head, a.M, j + 1, blockIdx.y * TM, TM, rows_s, red_h);
     if (count <= 0) return;
-    W0 = W0 + static_cast<size_t>(j) * static_cast<size_t>(a.head_stride);
+    tile0 = j * (a.N / 16);
   } else {
     const int m0 = blockIdx.y * TM;
     count = min(TM, a.M - m0);
     if (tid < TM) rows_s[tid] = tid < count ? m0 + tid : -1;
   }
   __syncthreads();
+  // per-row values the epilogue needs, loaded while the K loop runs (visible
+  // after the barrier that precedes the epilogue)
+  if (tid < TM) {
+    const int row = rows_s[tid];
+    if (MODE == kQKV) pos_s[tid] = row >= 0 ? a.pos[row] : -1;
+    if (PL && NORM) {  // the split pass's partial sums of squares, in order
+      float t = 0.0f;
+      if (row >= 0)
+        for (int j = 0; j < a.K / 256; ++j) t += a.ssp[static_cast<size_t>(row) * (a.K / 256) + j];
+      rinv_s[tid] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+    }
+  }
 
-  // ---- this lane's operand rows; a missing row reads X row 0 (masked) ----
-  const float* xr[FM];
-  bool xv[FM];
+  // ---- operand pointers.  Activations: for row tile f, lane l reads row
+// 16 f + l / 4, k 8 (l % 4) .. +7 of each chunk (a quad covers one 128-byte
+// row segment) and so holds exactly fragment entry (l / 4) + 16 (l % 4).  A
+// missing row reads X row 0: its outputs and sum of squares are never used.
+  const int cw = a.K / 32 / kWaves;  // chunks of this wave
+  const int c0 = wave * cw;
+  // blocks start their K walk at different chunks, so that the blocks that
+  // share a weight tile or an activation tile (on one XCD) do not all miss on
+  // the same lines at once
+  const int rot = (blockIdx.x / 8 + 2 * blockIdx.y + blockIdx.z) % cw;
+  auto rc = [&](int step) { const int c = step + rot; return c >= cw ? c - cw : c; };
+  const int kl = 8 * (lane & 3);
+  const float* xb = a.X + c0 * 32 + kl;
+  int xo[FM];  // row offsets in floats
 #pragma unroll
   for (int f = 0; f < FM; ++f) {
-    const int row = rows_s[16 * f + li];
-    xv[f] = row >= 0;
-    xr[f] = a.X + static_cast<size_t>(row >= 0 ? row / a.xdiv : 0) * a.ldx;
+    const int row = rows_s[16 * f + (lane >> 2)];
+    xo[f] = (row >= 0 ? row / a.xdiv : 0) * a.ldx;
   }
-  const WT* wr[FN];
+  const float* gr = NORM ? a.norm_g + c0 * 32 + kl : nullptr;
+  const uint16_t* wr[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) wr[f] = bweight_row<WT, MODE, TN>(a, W0, n0 + 16 * f + li);
-  const int cw = a.K / 32 / kWaves;          // chunks of this wave (even)
-  const int kbase = wave * cw * 32 + 8 * lg;  // lane's first k
+  for (int j = 0; j < FN; ++j) {
+    const uint16_t* Wm = (MODE == kSwiGLU && j >= FN / 2) ? static_cast<const uint16_t*>(a.W1) : W0;
+    wr[j] = Wm + frag_at(tile0 + btile<MODE, FN>(blockIdx.x, j), c0, a.wtiles) + lane * 8;
+  }
+  const size_t wstep = static_cast<size_t>(a.wtiles) * 512;  // one chunk further
 
-  struct Frag {  // one chunk of this lane's operands (native vectors)
-    floatx4 x[FM][2];
-    floatx4 g[2];
-    u32x4 w[FN];  // 8 bf16 per weight fragment
+  struct BFrag {  // ... and weight fragments
+    u32x4 w[FN];
   };
-  auto fetch = [&](int c) __attribute__((always_inline)) {
-    Frag f;
-    const int k = kbase + c * 32;
+  auto fetch_b = [&](int c) __attribute__((always_inline)) {
+    BFrag f;
 #pragma unroll
-    for (int i = 0; i < FN; ++i) f.w[i] = *reinterpret_cast<const u32x4*>(wr[i] + k);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      f.x[i][0] = *reinterpret_cast<const floatx4*>(xr[i] + k);
-      f.x[i][1] = *reinterpret_cast<const floatx4*>(xr[i] + k + 4);
-    }
-    if constexpr (NORM) {
-      f.g[0] = *reinterpret_cast<const floatx4*>(a.norm_g + k);
-      f.g[1] = *reinterpret_cast<const floatx4*>(a.norm_g + k + 4);
-    } else {
-      f.g[0] = f.g[1] = floatx4{1.0f, 1.0f, 1.0f, 1.0f};
-    }
+    for (int j = 0; j < FN; ++j) f.w[j] = *reinterpret_cast<const u32x4*>(wr[j] + rc(c) * wstep);
     return f;
   };
-
   floatx4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -132,143 +152,277 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float ss[FM];
 #pragma unroll
-  for (int f = 0; f < FM; ++f) ss[f] = 0.0f;
+  for (int i = 0; i < FM; ++i) ss[i] = 0.0f;
+  if constexpr (PL) {
+    // activations pre-split: plane p of row tile t, chunk c is the 1 KB
+    // fragment at ((c * T + t) * 3 + p) * 512 bf16 (T row tiles)
+    const uint16_t* ab = a.planes + (static_cast<size_t>(c0) * a.ptiles + blockIdx.y * FM) * 3 * 512 + lane * 8;
+    const size_t astep = static_cast<size_t>(a.ptiles) * 3 * 512;
+    struct PFrag {
+      u32x4 x[FM][3];
+    };
+    auto fetch_p = [&](int c) __attribute__((always_inline)) {
+      PFrag f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          f.x[i][p] = *reinterpret_cast<const u32x4*>(ab + rc(c) * astep + (i * 3 + p) * 512);
+      return f;
+    };
+    auto mma_p = [&](const PFrag& fa, const BFrag& fb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+          for (int n = 0; n < FN; ++n)
+            acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa.x[f][p]),
+                                                                __builtin_bit_cast(bf16x8, fb.w[n]), acc[f][n], 0, 0, 0);
+    };
+    // two chunks of loads in flight (an even chunk count per wave; the
+    // fetches past the end re-read the last chunk and are not used)
+    // (issued in the loop's order: the wait counts at the loop head then
+    // cover only the chunk being consumed)
+    PFrag pa0 = fetch_p(0);
+    BFrag pb0 = fetch_b(0);
+    __builtin_amdgcn_sched_barrier(0);
+    PFrag pa1 = fetch_p(1);
+    BFrag pb1 = fetch_b(1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c = 0; c < cw; c += 2) {
+      mma_p(pa0, pb0);
+      __builtin_amdgcn_sched_barrier(0);
+      pa0 = fetch_p(min(c + 2, cw - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      pb0 = fetch_b(min(c + 2, cw - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      mma_p(pa1, pb1);
+      __builtin_amdgcn_sched_barrier(0);
+      pa1 = fetch_p(min(c + 3, cw - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      pb1 = fetch_b(min(c + 3, cw - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+  struct AFrag {  // one chunk of this lane's activation loads
+    floatx4 x[FM][2];
+    floatx4 g[2];
+  };
+  auto fetch_a = [&](int step) __attribute__((always_inline)) {
+    const int c = rc(step);
+    AFrag f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      f.x[i][0] = *reinterpret_cast<const floatx4*>(xb + xo[i] + c * 32);
+      f.x[i][1] = *reinterpret_cast<const floatx4*>(xb + xo[i] + c * 32 + 4);
+    }
+    if constexpr (NORM) {
+      f.g[0] = *reinterpret_cast<const floatx4*>(gr + c * 32);
+      f.g[1] = *reinterpret_cast<const floatx4*>(gr + c * 32 + 4);
+    } else {
+      f.g[0] = f.g[1] = floatx4{1.0f, 1.0f, 1.0f, 1.0f};
+    }
+    return f;
+  };
 
-  auto compute = [&](const Frag& fr) __attribute__((always_inline)) {
-    float xs[FM][8];  // this lane's x (* g) values of the chunk
+
+  // Stage slots are XOR-swizzled, entry e at e ^ (((e >> 4) & 3) << 1), so
+  // that both this lane mapping's writes and the fragment reads (lane e reads
+  // entry e) hit eight distinct 16-byte bank groups per eight lanes.
+  auto slot = [](int e) { return e ^ (((e >> 4) & 3) << 1); };
+  const int wslot = slot((lane >> 2) + 16 * (lane & 3));
+  const int rslot = slot(lane);
+  // split x * g of one chunk into the wave's LDS stage: three bf16 pieces,
+  // two values per word (the high halves, gathered by byte permutes)
+  auto split_store = [&](const AFrag& fr) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = xv[f] ? fr.x[f][e / 4][e % 4] : 0.0f;
-        ss[f] += x * x;
-        xs[f][e] = NORM ? x * fr.g[e / 4][e % 4] : x;
-      }
-    bf16x8 ap[FM][3];
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
+    for (int i = 0; i < FM; ++i) {
       uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        uint32_t h0, m0, l0, h1, m1, l1;
-        split3(xs[f][e], h0, m0, l0);
-        split3(xs[f][e + 1], h1, m1, l1);
-        hp[e / 2] = h0 | (h1 << 16);
-        mp[e / 2] = m0 | (m1 << 16);
-        lp[e / 2] = l0 | (l1 << 16);
+        const float x0 = fr.x[i][e / 4][e % 4], x1 = fr.x[i][e / 4][e % 4 + 1];
+        ss[i] = fmaf(x0, x0, ss[i]);
+        ss[i] = fmaf(x1, x1, ss[i]);
+        const float y0 = NORM ? x0 * fr.g[e / 4][e % 4] : x0;
+        const float y1 = NORM ? x1 * fr.g[e / 4][e % 4 + 1] : x1;
+        const float r0 = y0 - __uint_as_float(__float_as_uint(y0) & 0xFFFF0000u);
+        const float r1 = y1 - __uint_as_float(__float_as_uint(y1) & 0xFFFF0000u);
+        const float q0 = r0 - __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
+        const float q1 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+        hp[e / 2] = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
+        mp[e / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+        lp[e / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
       }
-      ap[f][0] = __builtin_bit_cast(bf16x8, u32x4{hp[0], hp[1], hp[2], hp[3]});
-      ap[f][1] = __builtin_bit_cast(bf16x8, u32x4{mp[0], mp[1], mp[2], mp[3]});
-      ap[f][2] = __builtin_bit_cast(bf16x8, u32x4{lp[0], lp[1], lp[2], lp[3]});
+      sm.stage.f[wave][i * 3 + 0][wslot] = u32x4{hp[0], hp[1], hp[2], hp[3]};
+      sm.stage.f[wave][i * 3 + 1][wslot] = u32x4{mp[0], mp[1], mp[2], mp[3]};
+      sm.stage.f[wave][i * 3 + 2][wslot] = u32x4{lp[0], lp[1], lp[2], lp[3]};
     }
+  };
+  auto mma = [&](const BFrag& fb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+    for (int p = 0; p < 3; ++p) {
+      bf16x8 ap[FM];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) ap[f] = __builtin_bit_cast(bf16x8, sm.stage.f[wave][f * 3 + p][rslot]);
 #pragma unroll
       for (int f = 0; f < FM; ++f)
 #pragma unroll
         for (int n = 0; n < FN; ++n)
-          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[f][p], __builtin_bit_cast(bf16x8, fr.w[n]),
+          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[f], __builtin_bit_cast(bf16x8, fb.w[n]),
                                                               acc[f][n], 0, 0, 0);
+    }
   };
 
-  // ---- K loop: two chunks in flight (the chunk count is even; the
-  // fetches past the end re-read the last chunk and are not used) ----
-  Frag f0 = fetch(0);
+  // ---- K loop (an even number of chunks per wave), two chunks of loads in
+// flight per operand: a chunk's
+// activation registers are refilled as soon as they are split, its weight
+// registers once its MFMAs are issued (the fetches past the end re-read the
+// last chunk and are not used) ----
+  // (issued in the loop's order, see above)
+  AFrag fa0 = fetch_a(0);
   __builtin_amdgcn_sched_barrier(0);
-  Frag f1 = fetch(1);
+  BFrag fb0 = fetch_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  AFrag fa1 = fetch_a(1);
+  __builtin_amdgcn_sched_barrier(0);
+  BFrag fb1 = fetch_b(1);
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < cw; c += 2) {
-    compute(f0);
+    wave_lds_sync();  // the previous chunk's fragment reads are done
+    split_store(fa0);
     __builtin_amdgcn_sched_barrier(0);
-    f0 = fetch(min(c + 2, cw - 1));
+    fa0 = fetch_a(min(c + 2, cw - 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute(f1);
+    wave_lds_sync();
+    mma(fb0);
     __builtin_amdgcn_sched_barrier(0);
-    f1 = fetch(min(c + 3, cw - 1));
+    fb0 = fetch_b(min(c + 2, cw - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    wave_lds_sync();
+    split_store(fa1);
+    __builtin_amdgcn_sched_barrier(0);
+    fa1 = fetch_a(min(c + 3, cw - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    wave_lds_sync();
+    mma(fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    fb1 = fetch_b(min(c + 3, cw - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- partial tiles and sums of squares -> LDS, added in wave order ----
+  }
+
+  // ---- the four partial tiles (and the rows' partial sums of squares) to
+  // LDS, one barrier, then every thread finishes TM * TN / 256 outputs,
+  // adding the partials in a fixed order: (w0 + w1) + (w2 + w3) ----
+  __syncthreads();  // every wave is past its last stage read (stage and part share LDS)
+  if (NORM && !PL) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float t = ss[i];
+      t += __shfl_xor(t, 1);
+      t += __shfl_xor(t, 2);
+      if ((lane & 3) == 0) sm.part.ssq[wave][16 * i + (lane >> 2)] = t;
+    }
+  }
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int n = 0; n < FN; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[wave][16 * f + 4 * lg + i][16 * n + li] = acc[f][n][i];
-  if (NORM) {
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-      float t = ss[f];
-      t += __shfl_xor(t, 16);
-      t += __shfl_xor(t, 32);
-      if (lg == 0) ssq_s[wave][16 * f + li] = t;
+      for (int i = 0; i < 4; ++i) sm.part.v[wave][16 * f + 4 * lg + i][16 * n + li] = acc[f][n][i];
+  __syncthreads();
+  auto rinv_of = [&](int r) {
+    if constexpr (PL) {
+      return rinv_s[r];
+    } else {
+      const float t = (sm.part.ssq[0][r] + sm.part.ssq[1][r]) + (sm.part.ssq[2][r] + sm.part.ssq[3][r]);
+      return 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
     }
-  }
-  __syncthreads();
-  if (NORM && tid < TM) {
-    float t = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += ssq_s[w][tid];
-    rinv_s[tid] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
-  }
-  __syncthreads();
+  };
   auto tile_val = [&](int r, int c) {
-    float v = part[0][r][c];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += part[w][r][c];
-    return NORM ? v * rinv_s[r] : v;
+    const float v = (sm.part.v[0][r][c] + sm.part.v[1][r][c]) + (sm.part.v[2][r][c] + sm.part.v[3][r][c]);
+    return NORM ? v * rinv_of(r) : v;
   };
 
   // final-normed rows for the heads' caller (the column tiles split K)
   if (MODE == kHead && NORM && a.xnorm_out != nullptr) {
     const int k4 = a.K / 4;
     const int per = (k4 + gridDim.x - 1) / gridDim.x;
-    const int c0 = blockIdx.x * per, c1 = min(k4, c0 + per);
-    const int w = c1 - c0;
+    const int q0 = blockIdx.x * per, q1 = min(k4, q0 + per);
+    const int w = q1 - q0;
     for (int idx = tid; w > 0 && idx < count * w; idx += kBlock) {
-      const int r = idx / w, c = 4 * (c0 + idx % w);
+      const int r = idx / w, c = 4 * (q0 + idx % w);
       const int row = rows_s[r];
       const float4 x = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row / a.xdiv) * a.ldx + c);
       const float4 g = *reinterpret_cast<const float4*>(a.norm_g + c);
-      const float ri = rinv_s[r];
+      const float ri = rinv_of(r);
       *reinterpret_cast<float4*>(a.xnorm_out + static_cast<size_t>(row) * a.K + c) =
           make_float4(x.x * g.x * ri, x.y * g.y * ri, x.z * g.z * ri, x.w * g.w * ri);
     }
   }
 
-  // ---- fused epilogue ----
+  // ---- fused epilogue: all of the thread's values first, then the stores
+  // (the residual add loads every old value before storing any) ----
+  const int n0 = blockIdx.x * TN;
   if (MODE == kSwiGLU) {
-    for (int idx = tid; idx < TM * (TN / 2); idx += kBlock) {
-      const int r = idx / (TN / 2), c = idx % (TN / 2);
-      const int row = rows_s[r];
-      if (row < 0) continue;
+    constexpr int PER = TM * (TN / 2) / kBlock;
+    float out[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * kBlock, r = idx / (TN / 2), c = idx % (TN / 2);
       const float g = tile_val(r, c), u = tile_val(r, c + TN / 2);
-      const float sg = g / (1.0f + expf(-g));
-      a.Y[static_cast<size_t>(row) * a.ldy + blockIdx.x * (TN / 2) + c] = sg * u;
+      out[k] = g / (1.0f + expf(-g)) * u;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * kBlock, r = idx / (TN / 2), c = idx % (TN / 2);
+      const int row = rows_s[r];
+      if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + blockIdx.x * (TN / 2) + c] = out[k];
     }
     return;
   }
-  for (int idx = tid; idx < TM * TN; idx += kBlock) {
-    const int r = idx / TN, c = idx % TN;
+  constexpr int PER = TM * TN / kBlock;
+  float val[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + k * kBlock;
+    val[k] = tile_val(idx / TN, idx % TN);
+  }
+  if (MODE == kAdd) {
+    float old[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * kBlock, row = rows_s[idx / TN];
+      old[k] = row >= 0 ? a.Y[static_cast<size_t>(row) * a.ldy + n0 + idx % TN] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * kBlock, row = rows_s[idx / TN];
+      if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + n0 + idx % TN] = old[k] + val[k];
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + k * kBlock, r = idx / TN, c = idx % TN;
     const int row = rows_s[r];
     if (row < 0) continue;
-    const float val = tile_val(r, c);
     const int o = n0 + c;
-    if (MODE == kAdd) {
-      a.Y[static_cast<size_t>(row) * a.ldy + o] += val;
-    } else if (MODE == kHead) {
-      a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+    if (MODE == kHead) {
+      a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k];
     } else if (MODE == kQKV) {
       if (o < a.qdim) {
-        a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+        a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k];
       } else {
-        const int pp = a.pos[row];
+        const int pp = pos_s[r];
         if (pp >= 0 && pp < a.kv_positions) {
           const int b = row / a.rows_per_stream;
           float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
           const int oo = o - a.qdim;
-          if (oo < a.kvdim) base[oo] = val;
-          else base[a.kv_vo + (oo - a.kvdim)] = val;
+          if (oo < a.kvdim) base[oo] = val[k];
+          else base[a.kv_vo + (oo - a.kvdim)] = val[k];
         }
       }
     }
@@ -277,11 +431,24 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
 
 template <int FM, int FN, bool NORM>
 hipError_t launch_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  const bool pl = a.planes != nullptr;
   switch (mode) {
-    case kAdd: hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
-    case kSwiGLU: hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
-    case kQKV: hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
-    case kHead: hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM>), grid, dim3(kBlock), 0, s, a); break;
+    case kAdd:
+      if (pl) hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, true>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case kSwiGLU:
+      if (pl) hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, true>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case kQKV:
+      if (pl) hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, true>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case kHead:  // rows gathered per head: always the in-kernel split
+      if (pl) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -293,15 +460,121 @@ hipError_t launch_f(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
                              : launch_t<FM, FN, false>(mode, a, grid, s);
 }
 
+// Split pass: rows [0, M) of X (times g when set) into three bf16 planes in
+// fragment order, rows up to the next multiple of 64 zero; with g, per row
+// the partial sums of squares of x over each 256-wide K block.  Block
+// (row tile, K block): 16 rows x 256 values, two fragment entries a thread,
+// both of row 16 t + tid % 16.
+__global__ __launch_bounds__(kBlock) void split_rows_kernel(const float* X, int ldx, int M, int K, const float* g,
+                                                            uint16_t* planes, float* ssp) {
+  __shared__ float red[kWaves][16];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int mt = blockIdx.x, kb = blockIdx.y;
+  const int row = 16 * mt + tid % 16;
+  float ss = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = tid + h * kBlock;      // entry of the block: chunk e / 64, fragment lane e % 64
+    const int c = 8 * kb + e / 64, L = e % 64;
+    const int k = 32 * c + 8 * (L / 16);
+    float v[8], gv[8];
+    if (g != nullptr) {
+      const floatx4 g0 = *reinterpret_cast<const floatx4*>(g + k);
+      const floatx4 g1 = *reinterpret_cast<const floatx4*>(g + k + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gv[i] = g0[i];
+        gv[i + 4] = g1[i];
+      }
+    }
+    if (row < M) {
+      const floatx4 x0 = *reinterpret_cast<const floatx4*>(X + static_cast<size_t>(row) * ldx + k);
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(X + static_cast<size_t>(row) * ldx + k + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = x0[i];
+        v[i + 4] = x1[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      ss = fmaf(v[i], v[i], ss);
+      ss = fmaf(v[i + 1], v[i + 1], ss);
+      const float y0 = g != nullptr ? v[i] * gv[i] : v[i];
+      const float y1 = g != nullptr ? v[i + 1] * gv[i + 1] : v[i + 1];
+      const float r0 = y0 - __uint_as_float(__float_as_uint(y0) & 0xFFFF0000u);
+      const float r1 = y1 - __uint_as_float(__float_as_uint(y1) & 0xFFFF0000u);
+      const float q0 = r0 - __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
+      const float q1 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+      hp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
+      mp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+      lp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(planes) + (static_cast<size_t>(c) * gridDim.x + mt) * 3 * kWave + L;
+    dst[0] = u32x4{hp[0], hp[1], hp[2], hp[3]};
+    dst[kWave] = u32x4{mp[0], mp[1], mp[2], mp[3]};
+    dst[2 * kWave] = u32x4{lp[0], lp[1], lp[2], lp[3]};
+  }
+  if (g == nullptr) return;
+  // the 16 threads of a row in each wave (lanes l, l+16, l+32, l+48), then the waves
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  if (lane < 16) red[wave][lane] = ss;
+  __syncthreads();
+  if (tid < 16 && row < M)
+    ssp[static_cast<size_t>(row) * (K / 256) + kb] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+}
+
+// Packs one bf16 matrix [N][K] (row-major, N % 16 == 0, K % 32 == 0) into
+// fragment order at tiles t0.. of a chunk-major packed matrix with NT tiles
+// per chunk: thread t writes one fragment entry (8 bf16).
+__global__ __launch_bounds__(kBlock) void pack_frag_kernel(const uint16_t* W, int N, int K, uint16_t* P, int NT,
+                                                           int t0) {
+  const size_t t = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const size_t total = static_cast<size_t>(N / 16) * (K / 32) * kWave;
+  if (t >= total) return;
+  const int l = static_cast<int>(t % kWave);
+  const size_t blk = t / kWave;
+  const int c = static_cast<int>(blk % (K / 32));
+  const int tile = static_cast<int>(blk / (K / 32));
+  const uint16_t* src = W + static_cast<size_t>(tile * 16 + l % 16) * K + c * 32 + 8 * (l / 16);
+  uint16_t* dst = P + frag_at(t0 + tile, c, NT) + l * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = src[e];
+}
+
 }  // namespace
 
-// bf16 weights only: fp32 weights keep the fp32 kernels of mfma_impl.h,
-// which measured faster on the small fp32 shapes.
+// bf16 weights only (packed by pack_fragments); fp32 weights keep the fp32
+// kernels of mfma_impl.h.
 hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s) {
   if (wdtype != CP_SPEC_BF16) return hipErrorInvalidValue;
-  if (fm == 1 && fn == 4) return launch_f<1, 4>(mode, a, grid, s);
+  if (fm == 2 && fn == 2) return launch_f<2, 2>(mode, a, grid, s);
   if (fm == 2 && fn == 4) return launch_f<2, 4>(mode, a, grid, s);
+  if (fm == 4 && fn == 4) return launch_f<4, 4>(mode, a, grid, s);
+  if (fm == 4 && fn == 6) return launch_f<4, 6>(mode, a, grid, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_rows(const float* X, int ldx, int M, int K, const float* g, uint16_t* planes, float* ssp,
+                             hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (K % 256 || ldx % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_rows_kernel, dim3((M + 63) / 64 * 4, K / 256), dim3(kBlock), 0, s, X, ldx, M, K, g,
+                     planes, ssp);
+  return hipGetLastError();
+}
+
+hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, int t0, hipStream_t s) {
+  if (N % 16 || K % 32 || N <= 0 || K <= 0 || t0 < 0 || t0 + N / 16 > NT) return hipErrorInvalidValue;
+  const size_t total = static_cast<size_t>(N / 16) * (K / 32) * kWave;
+  hipLaunchKernelGGL(pack_frag_kernel, dim3(static_cast<unsigned>((total + kBlock - 1) / kBlock)), dim3(kBlock),
+                     0, s, W, N, K, P, NT, t0);
+  return hipGetLastError();
 }
 
 }  // namespace cps

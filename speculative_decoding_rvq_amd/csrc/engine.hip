@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
+#include <utility>
 #include <array>
 #include <cmath>
 #include <cstring>
@@ -39,7 +41,7 @@ struct Shape {
 
 struct Layout {
   size_t st, call, sstats, dhead, thead, pos, hstate, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
-      tlogits, p, tcode, tflags, rope, total;
+      tlogits, p, tcode, tflags, rope, packed, planes, ssp, total;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -116,6 +118,24 @@ constexpr int kMfmaMinStreams = 8;
 constexpr int kMfmaMinRows = 32;
 constexpr int kFillBlocks = 256;  // one block per compute unit
 
+// bf16 weights in MFMA fragment order for the batched path: only when many
+// rows can occur and every matrix tiles (N % 16, K % 128).
+bool packs_weights(const Shape& s) {
+  if (s.wdt != CP_SPEC_BF16) return false;
+  if (s.maxB * s.R < kMfmaMinRows && s.maxB < kMfmaMinStreams) return false;
+  return s.H % 128 == 0 && s.qdim % 128 == 0 && s.F % 128 == 0 && s.kvdim % 16 == 0 && s.V % 16 == 0;
+}
+
+// Per layer: QKV (stacked), O, gate, up, down; then the stacked lm_heads.
+size_t packed_layer_elems(const Shape& s) {
+  const size_t H = s.H, F = s.F;
+  return (s.qdim + 2 * static_cast<size_t>(s.kvdim)) * H + H * s.qdim + 2 * F * H + H * F;
+}
+size_t packed_elems(const Shape& s) {
+  if (!packs_weights(s)) return 0;
+  return packed_layer_elems(s) * s.L + static_cast<size_t>(s.G - 1) * s.V * s.H;
+}
+
 Layout make_layout(const Shape& s) {
   Layout l{};
   size_t off = 0;
@@ -147,6 +167,13 @@ Layout make_layout(const Shape& s) {
   l.tcode = take(B * R * i4);
   l.tflags = take(B * R * i4);
   l.rope = take(static_cast<size_t>(s.G) * (s.d / 2) * sizeof(float2));
+  l.packed = take(packed_elems(s) * sizeof(uint16_t));
+  // pre-split activation planes (three bf16 per value) and partial sums of
+  // squares of the batched projections' input rows
+  const size_t prow = packs_weights(s) ? (B * R + 63) / 64 * 64 : 0;
+  const size_t kmax = std::max({static_cast<size_t>(s.H), static_cast<size_t>(s.qdim), static_cast<size_t>(s.F)});
+  l.planes = take(prow * kmax * 3 * sizeof(uint16_t));
+  l.ssp = take(prow * (kmax / 256) * f4);
   l.total = off;
   return l;
 }
@@ -161,6 +188,10 @@ struct cp_spec {
   const void* heads;
   const float* fnorm;
   std::vector<std::array<const void*, 9>> layers;
+  // fragment-packed bf16 copies (batched path): per layer QKV, O, gate, up,
+  // down; the lm_heads; all null when the weights are not packed
+  std::vector<std::array<const uint16_t*, 5>> packed;
+  const uint16_t* packed_heads = nullptr;
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t graph = nullptr;
   int graph_B = -1;
@@ -212,21 +243,51 @@ bool mfma_fits(int mode, const GemvArgs& a) {
   return mode == kSwiGLU ? a.N % (kMfmaTN / 2) == 0 : a.N % kMfmaTN == 0;
 }
 
-// bf16 matrix-core tiles fit: K an even number of 32-wide chunks per wave
-// (four waves), columns whole 64-wide tiles (SwiGLU: 32 gate + 32 up rows).
-bool bgemm_fits(int mode, const GemvArgs& a) {
-  if (a.K % 256) return false;
-  return mode == kSwiGLU ? a.N % 32 == 0 : a.N % 64 == 0;
+// Block tile (16 fm) x (16 fn) of the packed bf16 kernel for M rows: the
+// largest that still gives every compute unit a block, else the one with the
+// most blocks; false when no tile divides the columns or K is not a
+// multiple of 256 (four waves, each an even number of 32-wide chunks).
+bool bgemm_tile(int mode, int N, int K, int M, int* fm_out, int* fn_out) {
+  static const int kTiles[4][2] = {{4, 6}, {4, 4}, {2, 4}, {2, 2}};
+  if (K % 256) return false;
+  int best = -1, best_blocks = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int fm = kTiles[i][0], fn = kTiles[i][1];
+    const bool fits = mode == kSwiGLU ? N % (8 * fn) == 0 : N % (16 * fn) == 0;
+    if (!fits) continue;
+    const int cols = mode == kSwiGLU ? 2 * N : N;
+    const int blocks = cols / (16 * fn) * ((M + 16 * fm - 1) / (16 * fm));
+    if (blocks >= kFillBlocks) {
+      best = i;
+      break;
+    }
+    if (blocks > best_blocks) best = i, best_blocks = blocks;
+  }
+  if (best < 0) return false;
+  *fm_out = kTiles[best][0];
+  *fn_out = kTiles[best][1];
+  return true;
 }
 
-// One skinny projection: Y (op) W . rows(X).  Many rows: matrix-core tiles.
-int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a) {
+// One skinny projection: Y (op) W . rows(X).  Many rows: matrix-core tiles
+// (bf16: over the fragment-packed copies pk0 / pk1 of W0 / W1).
+int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* pk0 = nullptr,
+         const uint16_t* pk1 = nullptr) {
   if (a.M <= 0) return CP_SPEC_OK;
-  if (h->sh.wdt == CP_SPEC_BF16 && mode != kHead && a.M >= kMfmaMinRows && bgemm_fits(mode, a)) {
-    // bf16: 32 x 64 tiles (16 x 64 when that still leaves few blocks)
+  int fm, fn;
+  if (pk0 != nullptr && mode != kHead && a.M >= kMfmaMinRows && bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn)) {
     const int cols = mode == kSwiGLU ? a.N * 2 : a.N;
-    const int fm = cols / 64 * ((a.M + 31) / 32) < kFillBlocks ? 1 : 2;
-    CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, 4, a, dim3(cols / 64, (a.M + 16 * fm - 1) / (16 * fm)), s));
+    a.W0 = pk0;
+    a.W1 = pk1;
+    // the activation rows split once, then the tiles read the pieces
+    uint16_t* planes = h->at<uint16_t>(h->lo.planes);
+    float* ssp = h->at<float>(h->lo.ssp);
+    CPS_HIP(launch_split_rows(a.X, a.ldx, a.M, a.K, a.norm_g, planes, ssp, s));
+    a.planes = planes;
+    a.ptiles = (a.M + 63) / 64 * 4;
+    a.ssp = ssp;
+    a.wtiles = a.N / 16;  // per packed matrix (SwiGLU: gate and up each)
+    CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, fn, a, dim3(cols / (16 * fn), (a.M + 16 * fm - 1) / (16 * fm)), s));
     return CP_SPEC_OK;
   }
   if (mode != kHead && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
@@ -271,6 +332,8 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
   float* attn = h->at<float>(h->lo.attn);
   float* act = h->at<float>(h->lo.act);
   const auto& w = h->layers[l];
+  const uint16_t* const* pk = h->packed.empty() ? nullptr : h->packed[l].data();
+  auto pw = [&](int i) { return pk ? pk[i] : nullptr; };
   float* kvl = kv + l * 2LL * sh.G * sh.kvdim;
   const long long kv_vo = static_cast<long long>(sh.G) * sh.kvdim;
   GemvArgs a{};
@@ -285,7 +348,7 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       a.Y = Q; a.ldy = sh.qdim;
       a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
       a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.G;
-      return gemv(h, s, kQKV, a);
+      return gemv(h, s, kQKV, a, pw(0));
     case CP_SPEC_KERNEL_ATTENTION: {
       AttnArgs at{};
       at.Q = Q; at.out = attn; at.kv = kvl; at.kv_sb = h->kv_sb(); at.kv_vo = kv_vo; at.pos = pos;
@@ -296,14 +359,14 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
     }
     case CP_SPEC_KERNEL_O_PROJ:
       a.W0 = w[4]; a.N = sh.H; a.K = sh.qdim; a.X = attn; a.ldx = sh.qdim; a.Y = X; a.ldy = sh.H;
-      return gemv(h, s, kAdd, a);
+      return gemv(h, s, kAdd, a, pw(1));
     case CP_SPEC_KERNEL_GATE_UP:
       a.W0 = w[6]; a.W1 = w[7]; a.N = sh.F; a.K = sh.H; a.X = X; a.ldx = sh.H;
       a.norm_g = static_cast<const float*>(w[5]); a.Y = act; a.ldy = sh.F;
-      return gemv(h, s, kSwiGLU, a);
+      return gemv(h, s, kSwiGLU, a, pw(2), pw(3));
     case CP_SPEC_KERNEL_DOWN:
       a.W0 = w[8]; a.N = sh.H; a.K = sh.F; a.X = act; a.ldx = sh.F; a.Y = X; a.ldy = sh.H;
-      return gemv(h, s, kAdd, a);
+      return gemv(h, s, kAdd, a, pw(4));
     default:
       return fail(CP_SPEC_EINVAL, "not a decoder kernel kind");
   }
@@ -332,12 +395,11 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
   a.norm_g = norm_g; a.eps = h->sh.eps; a.Y = logits; a.ldy = h->sh.V; a.head = head;
   a.head_stride = static_cast<long long>(h->sh.V) * h->sh.H; a.xnorm_out = xnorm_out;
   a.n_heads = h->sh.G - 1;
-  if (per_head > 0 && h->sh.wdt == CP_SPEC_BF16 && bgemm_fits(kHead, a)) {
-    // bf16: 16-row tiles while the heads' row lists are short, else 32
-    const int avg = (M + a.n_heads - 1) / a.n_heads;
-    const int fm = avg <= 16 ? 1 : 2;
-    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, fm, 4, a,
-                         dim3(a.N / 64, (per_head + 16 * fm - 1) / (16 * fm), a.n_heads), s));
+  if (per_head > 0 && h->packed_heads != nullptr && a.N % 64 == 0 && a.K % 256 == 0) {
+    // bf16, packed heads: 32 x 64 tiles per head
+    a.W0 = h->packed_heads;
+    a.wtiles = a.n_heads * (a.N / 16);
+    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, 4, a, dim3(a.N / 64, (per_head + 31) / 32, a.n_heads), s));
     return CP_SPEC_OK;
   }
   if (per_head > 0 && mfma_fits(kHead, a)) {
@@ -460,6 +522,36 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
   if (e == hipSuccess)
     e = hipMemcpy(h->at<char>(lo.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = attention_allow_smem(s.d, attention_smem_bytes(s.G, s.d, s.R, s.nq / s.nkv));
+  if (e == hipSuccess && packs_weights(s)) {
+    // fragment-packed copies of every bf16 matrix (read once, here)
+    uint16_t* p = h->at<uint16_t>(lo.packed);
+    // a packed matrix of NT tiles per chunk from row-stacked sources
+    auto pack = [&](std::initializer_list<std::pair<const void*, int>> parts, int K) {
+      int N = 0;
+      for (const auto& pr : parts) N += pr.second;
+      uint16_t* dst = p;
+      int t0 = 0;
+      for (const auto& pr : parts) {
+        if (e == hipSuccess)
+          e = pack_fragments(static_cast<const uint16_t*>(pr.first), pr.second, K, dst, N / 16, t0, nullptr);
+        t0 += pr.second / 16;
+      }
+      p += static_cast<size_t>(N) * K;
+      return dst;
+    };
+    h->packed.resize(s.L);
+    for (int l = 0; l < s.L; ++l) {
+      const auto& wl = h->layers[l];
+      auto& pk = h->packed[l];
+      pk[0] = pack({{wl[1], s.qdim}, {wl[2], s.kvdim}, {wl[3], s.kvdim}}, s.H);  // Q, K, V tiles
+      pk[1] = pack({{wl[4], s.H}}, s.qdim);
+      pk[2] = pack({{wl[6], s.F}}, s.H);
+      pk[3] = pack({{wl[7], s.F}}, s.H);
+      pk[4] = pack({{wl[8], s.H}}, s.F);
+    }
+    h->packed_heads = pack({{h->heads, (s.G - 1) * s.V}}, s.H);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
     delete h;

@@ -55,6 +55,13 @@ struct GemvArgs {
   // tiling (host-chosen)
   int kt;     // threads covering one row's K (64/128/256)
   int units;  // number of RPG-row output units
+  // matrix-core path: W0 / W1 fragment-packed with wtiles tiles per chunk;
+  // activations pre-split by launch_split_rows (nullable) into ptiles row
+  // tiles
+  int wtiles;
+  const uint16_t* planes;
+  int ptiles;
+  const float* ssp;  // [M][K / 256] partial sums of squares (with norm_g)
 };
 
 struct AttnArgs {
@@ -150,11 +157,24 @@ hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid
 // block's four waves; K a multiple of 128).
 enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };
 hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
-// Matrix-core projections with in-block split-K (bf16 weights):
-// block tile (16 fm) x (16 fn), (fm, fn) in {(1, 4), (2, 4)}, K a multiple
-// of 256; grid (columns / tile, rows / tile) or, lm_heads, (V / tile, row
-// tiles, heads).
+// Matrix-core projections with in-block split-K over fragment-packed bf16
+// weights (W0 / W1 packed by pack_fragments): block tile (16 fm) x (16 fn),
+// (fm, fn) in {(2, 2), (2, 4), (4, 4), (4, 6)}, K a multiple of 256; grid
+// (columns / tile, rows / tile) or, lm_heads, (V / tile, row tiles, heads).
 hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
+// One bf16 matrix [N][K] row-major into MFMA fragment order (N % 16 == 0,
+// K % 32 == 0), at tiles t0 .. t0 + N/16 - 1 of a chunk-major packed matrix
+// with NT tiles per chunk: fragment (tile t, K chunk c) is 64 lanes x 8 bf16
+// at ((c * NT + t) * 64 + lane) * 8, lane l holding W[16 t + l % 16][32 c +
+// 8 (l / 16) + 0..7].
+hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, int t0, hipStream_t s);
+// Rows [0, M) of X (times g when set) split into three bf16 planes in
+// fragment order for launch_bgemm (a.planes): with T = ceil(M / 64) * 4 row
+// tiles, row tile t, K chunk c, plane p at ((c * T + t) * 3 + p) * 512 bf16;
+// rows from M up to 64 T are zero.  With g,
+// ssp[m][j] = sum of x^2 over K block j (256 wide).  K % 256 == 0.
+hipError_t launch_split_rows(const float* X, int ldx, int M, int K, const float* g, uint16_t* planes, float* ssp,
+                             hipStream_t s);
 // LDS the attention kernel needs, and raising its limit above 64 KB (once,
 // before any launch).
 size_t attention_smem_bytes(int G, int d, int R, int group);

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
     if (PL && NORM) {  // the split pass's partial sums of squares, in order
       float t = 0.0f;
       if (row >= 0)
-        for (int j = 0; j < a.K / 256; ++j) t += a.ssp[static_cast<size_t>(row) * (a.K / 256) + j];
+        for (int j = 0; j < a.K / 32; ++j) t += a.ssp[static_cast<size_t>(row) * (a.K / 32) + j];
       rinv_s[tid] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
     }
   }
@@ -366,6 +366,23 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
   // ---- fused epilogue: all of the thread's values first, then the stores
   // (the residual add loads every old value before storing any) ----
   const int n0 = blockIdx.x * TN;
+  if (MODE == kSwiGLU && a.out_planes != nullptr) {
+    // the down projection's input: eight activations per thread, split
+    constexpr int W = TN / 2, G = TM * W / 8;
+    for (int q = tid; q < G; q += kBlock) {
+      const int r = q / (W / 8), c8 = (q % (W / 8)) * 8;
+      const int row = rows_s[r];
+      if (row < 0) continue;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = tile_val(r, c8 + e), u = tile_val(r, c8 + e + W);
+        y[e] = g / (1.0f + expf(-g)) * u;
+      }
+      split_store8(a.out_planes, a.out_ptiles, row, blockIdx.x * W + c8, y);
+    }
+    return;
+  }
   if (MODE == kSwiGLU) {
     constexpr int PER = TM * (TN / 2) / kBlock;
     float out[PER];
@@ -389,6 +406,39 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
   for (int k = 0; k < PER; ++k) {
     const int idx = tid + k * kBlock;
     val[k] = tile_val(idx / TN, idx % TN);
+  }
+  if (MODE == kAdd && a.out_planes != nullptr) {
+    // the residual rows, then the next normed projection's input: x * g
+    // split, eight columns per thread, and the rows' sums of squares per 32
+    // columns (four neighbouring lanes)
+    constexpr int G = TM * TN / 8, ITER = (G + kBlock - 1) / kBlock;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int q = tid + it * kBlock;
+      const int r = q < G ? q / (TN / 8) : 0, c8 = q < G ? (q % (TN / 8)) * 8 : 0;
+      const int row = q < G ? rows_s[r] : -1;
+      float ss = 0.0f;
+      if (row >= 0) {
+        float* yp = a.Y + static_cast<size_t>(row) * a.ldy + n0 + c8;
+        const floatx4 o0 = *reinterpret_cast<const floatx4*>(yp);
+        const floatx4 o1 = *reinterpret_cast<const floatx4*>(yp + 4);
+        float xn[8], y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xn[e] = (e < 4 ? o0[e] : o1[e - 4]) + tile_val(r, c8 + e);
+        *reinterpret_cast<floatx4*>(yp) = floatx4{xn[0], xn[1], xn[2], xn[3]};
+        *reinterpret_cast<floatx4*>(yp + 4) = floatx4{xn[4], xn[5], xn[6], xn[7]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ss = fmaf(xn[e], xn[e], ss);
+          y[e] = a.out_g != nullptr ? xn[e] * a.out_g[n0 + c8 + e] : xn[e];
+        }
+        split_store8(a.out_planes, a.out_ptiles, row, n0 + c8, y);
+      }
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      if (row >= 0 && c8 % 32 == 0) a.out_ssp[static_cast<size_t>(row) * (a.N / 32) + (n0 + c8) / 32] = ss;
+    }
+    return;
   }
   if (MODE == kAdd) {
     float old[PER];
@@ -462,31 +512,20 @@ hipError_t launch_f(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
 
 // Split pass: rows [0, M) of X (times g when set) into three bf16 planes in
 // fragment order, rows up to the next multiple of 64 zero; with g, per row
-// the partial sums of squares of x over each 256-wide K block.  Block
-// (row tile, K block): 16 rows x 256 values, two fragment entries a thread,
-// both of row 16 t + tid % 16.
+// the sums of squares of x over each 32-wide K chunk.  Block (row tile, K
+// block): 16 rows x 256 values; wave w takes fragment entries of chunks
+// w and w + 4 of the block (lane = fragment lane), so the four entries of
+// one row and chunk sit in lanes l, l +- 16, l +- 32 of one wave.
 __global__ __launch_bounds__(kBlock) void split_rows_kernel(const float* X, int ldx, int M, int K, const float* g,
                                                             uint16_t* planes, float* ssp) {
-  __shared__ float red[kWaves][16];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int mt = blockIdx.x, kb = blockIdx.y;
-  const int row = 16 * mt + tid % 16;
-  float ss = 0.0f;
+  const int row = 16 * mt + lane % 16;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int e = tid + h * kBlock;      // entry of the block: chunk e / 64, fragment lane e % 64
-    const int c = 8 * kb + e / 64, L = e % 64;
-    const int k = 32 * c + 8 * (L / 16);
-    float v[8], gv[8];
-    if (g != nullptr) {
-      const floatx4 g0 = *reinterpret_cast<const floatx4*>(g + k);
-      const floatx4 g1 = *reinterpret_cast<const floatx4*>(g + k + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gv[i] = g0[i];
-        gv[i + 4] = g1[i];
-      }
-    }
+    const int c = 8 * kb + wave + 4 * h;
+    const int k = 32 * c + 8 * (lane / 16);
+    float v[8], y[8];
     if (row < M) {
       const floatx4 x0 = *reinterpret_cast<const floatx4*>(X + static_cast<size_t>(row) * ldx + k);
       const floatx4 x1 = *reinterpret_cast<const floatx4*>(X + static_cast<size_t>(row) * ldx + k + 4);
@@ -499,34 +538,28 @@ __global__ __launch_bounds__(kBlock) void split_rows_kernel(const float* X, int 
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    uint32_t hp[4], mp[4], lp[4];
+    float ss = 0.0f;
+    if (g != nullptr) {
+      const floatx4 g0 = *reinterpret_cast<const floatx4*>(g + k);
+      const floatx4 g1 = *reinterpret_cast<const floatx4*>(g + k + 4);
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      ss = fmaf(v[i], v[i], ss);
-      ss = fmaf(v[i + 1], v[i + 1], ss);
-      const float y0 = g != nullptr ? v[i] * gv[i] : v[i];
-      const float y1 = g != nullptr ? v[i + 1] * gv[i + 1] : v[i + 1];
-      const float r0 = y0 - __uint_as_float(__float_as_uint(y0) & 0xFFFF0000u);
-      const float r1 = y1 - __uint_as_float(__float_as_uint(y1) & 0xFFFF0000u);
-      const float q0 = r0 - __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
-      const float q1 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-      hp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
-      mp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
-      lp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
+      for (int i = 0; i < 4; ++i) {
+        y[i] = v[i] * g0[i];
+        y[i + 4] = v[i + 4] * g1[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = v[i];
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(planes) + (static_cast<size_t>(c) * gridDim.x + mt) * 3 * kWave + L;
-    dst[0] = u32x4{hp[0], hp[1], hp[2], hp[3]};
-    dst[kWave] = u32x4{mp[0], mp[1], mp[2], mp[3]};
-    dst[2 * kWave] = u32x4{lp[0], lp[1], lp[2], lp[3]};
+    split_store8(planes, gridDim.x, row, k, y);
+    if (g != nullptr) {
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (lane < 16 && row < M) ssp[static_cast<size_t>(row) * (K / 32) + c] = ss;
+    }
   }
-  if (g == nullptr) return;
-  // the 16 threads of a row in each wave (lanes l, l+16, l+32, l+48), then the waves
-  ss += __shfl_xor(ss, 16);
-  ss += __shfl_xor(ss, 32);
-  if (lane < 16) red[wave][lane] = ss;
-  __syncthreads();
-  if (tid < 16 && row < M)
-    ssp[static_cast<size_t>(row) * (K / 256) + kb] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
 }
 
 // Packs one bf16 matrix [N][K] (row-major, N % 16 == 0, K % 32 == 0) into

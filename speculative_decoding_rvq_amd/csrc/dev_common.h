@@ -49,6 +49,32 @@ __device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32
   l = __float_as_uint(r2) >> 16;
 }
 
+// Eight consecutive values y of row `row`, columns k .. k+7 (k % 8 == 0),
+// split into three bf16 pieces (split3) and stored as one fragment entry
+// per piece in a chunk-major plane buffer with T row tiles: row tile
+// t = row / 16, K chunk c = k / 32, piece p at ((c * T + t) * 3 + p) * 64
+// 16-byte entries, fragment lane (row % 16) + 16 ((k % 32) / 8).
+__device__ __forceinline__ void split_store8(uint16_t* planes, int T, int row, int k, const float (&y)[8]) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const float y0 = y[i], y1 = y[i + 1];
+    const float r0 = y0 - __uint_as_float(__float_as_uint(y0) & 0xFFFF0000u);
+    const float r1 = y1 - __uint_as_float(__float_as_uint(y1) & 0xFFFF0000u);
+    const float q0 = r0 - __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
+    const float q1 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+    hp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
+    mp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+    lp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
+  }
+  const int L = row % 16 + 16 * ((k % 32) / 8);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(planes) + (static_cast<size_t>(k / 32) * T + row / 16) * 3 * 64 + L;
+  dst[0] = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
+  dst[64] = u32x4_t{mp[0], mp[1], mp[2], mp[3]};
+  dst[128] = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
+}
+
 // Row `row` of a table stored as WT, converted to fp32 element `i`.
 template <typename WT> __device__ __forceinline__ float load_elem(const WT* p, size_t i);
 template <> __device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }

@@ -172,8 +172,8 @@ Layout make_layout(const Shape& s) {
   // squares of the batched projections' input rows
   const size_t prow = packs_weights(s) ? (B * R + 63) / 64 * 64 : 0;
   const size_t kmax = std::max({static_cast<size_t>(s.H), static_cast<size_t>(s.qdim), static_cast<size_t>(s.F)});
-  l.planes = take(prow * kmax * 3 * sizeof(uint16_t));
-  l.ssp = take(prow * (kmax / 256) * f4);
+  l.planes = take(2 * prow * kmax * 3 * sizeof(uint16_t));  // two alternating buffers
+  l.ssp = take(prow * (kmax / 32) * f4);
   l.total = off;
   return l;
 }
@@ -275,17 +275,22 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
          const uint16_t* pk1 = nullptr) {
   if (a.M <= 0) return CP_SPEC_OK;
   int fm, fn;
+  if (a.planes != nullptr && !bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn))
+    return fail(CP_SPEC_EINVAL, "pre-split rows without a matrix-core tile");
   if (pk0 != nullptr && mode != kHead && a.M >= kMfmaMinRows && bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn)) {
     const int cols = mode == kSwiGLU ? a.N * 2 : a.N;
     a.W0 = pk0;
     a.W1 = pk1;
-    // the activation rows split once, then the tiles read the pieces
-    uint16_t* planes = h->at<uint16_t>(h->lo.planes);
-    float* ssp = h->at<float>(h->lo.ssp);
-    CPS_HIP(launch_split_rows(a.X, a.ldx, a.M, a.K, a.norm_g, planes, ssp, s));
-    a.planes = planes;
-    a.ptiles = (a.M + 63) / 64 * 4;
-    a.ssp = ssp;
+    if (a.planes == nullptr) {
+      // the activation rows split once, then the tiles read the pieces (the
+      // decoder layers' own path has them split by the producing kernel)
+      uint16_t* planes = h->at<uint16_t>(h->lo.planes);
+      float* ssp = h->at<float>(h->lo.ssp);
+      CPS_HIP(launch_split_rows(a.X, a.ldx, a.M, a.K, a.norm_g, planes, ssp, s));
+      a.planes = planes;
+      a.ptiles = (a.M + 63) / 64 * 4;
+      a.ssp = ssp;
+    }
     a.wtiles = a.N / 16;  // per packed matrix (SwiGLU: gate and up each)
     CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, fn, a, dim3(cols / (16 * fn), (a.M + 16 * fm - 1) / (16 * fm)), s));
     return CP_SPEC_OK;
@@ -323,9 +328,25 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
   return CP_SPEC_OK;
 }
 
-// One decoder kernel of layer l over B*R rows of X at positions `pos`.
+// Whether the decoder layers over M rows run on the matrix cores with the
+// activation split folded into the producing kernels: the attention kernel
+// writes the O projection's input pieces, the SwiGLU epilogue the down
+// projection's, the residual-add epilogues the next normed projection's (x *
+// gain, plus the rows' partial sums of squares).  Two plane buffers
+// alternate: every kernel reads one and writes the other.
+bool fused_planes(const cp_spec* h, int M) {
+  if (h->packed.empty() || M < kMfmaMinRows) return false;
+  const Shape& s = h->sh;
+  int fm, fn;
+  return s.d % 8 == 0 && bgemm_tile(kQKV, s.qdim + 2 * s.kvdim, s.H, M, &fm, &fn) &&
+         bgemm_tile(kAdd, s.H, s.qdim, M, &fm, &fn) && bgemm_tile(kSwiGLU, s.F, s.H, M, &fm, &fn) &&
+         bgemm_tile(kAdd, s.H, s.F, M, &fm, &fn);
+}
+
+// One decoder kernel of layer l over B*R rows of X at positions `pos`
+// (fused: see fused_planes; layer 0's Q/K/V input is split by the caller).
 int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R, float* X,
-                 const int* pos, float* kv) {
+                 const int* pos, float* kv, bool fused = false) {
   const Shape& sh = h->sh;
   const int M = B * R;
   float* Q = h->at<float>(h->lo.Q);
@@ -340,6 +361,11 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
   a.xdiv = 1;
   a.M = M;
   a.eps = sh.eps;
+  uint16_t* P0 = h->at<uint16_t>(h->lo.planes);
+  uint16_t* P1 = P0 + static_cast<size_t>((M + 63) / 64 * 64) *
+                          std::max({sh.H, sh.qdim, sh.F}) * 3;  // within the second buffer
+  float* S = h->at<float>(h->lo.ssp);
+  const int T = (M + 63) / 64 * 4;
   switch (kind) {
     case CP_SPEC_KERNEL_QKV:
       a.W0 = w[1]; a.W1 = w[2]; a.W2 = w[3];
@@ -348,24 +374,37 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       a.Y = Q; a.ldy = sh.qdim;
       a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
       a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.G;
+      if (fused) a.planes = P0, a.ptiles = T, a.ssp = S;
       return gemv(h, s, kQKV, a, pw(0));
     case CP_SPEC_KERNEL_ATTENTION: {
       AttnArgs at{};
       at.Q = Q; at.out = attn; at.kv = kvl; at.kv_sb = h->kv_sb(); at.kv_vo = kv_vo; at.pos = pos;
       at.rope = h->at<float2>(h->lo.rope); at.R = R; at.nq = sh.nq; at.nkv = sh.nkv; at.d = sh.d;
       at.G = sh.G; at.scale = 1.0f / std::sqrt(static_cast<float>(sh.d));
+      if (fused) at.planes = P1, at.ptiles = T;
       CPS_HIP(launch_attention(at, B, s));
       return CP_SPEC_OK;
     }
     case CP_SPEC_KERNEL_O_PROJ:
       a.W0 = w[4]; a.N = sh.H; a.K = sh.qdim; a.X = attn; a.ldx = sh.qdim; a.Y = X; a.ldy = sh.H;
+      if (fused) {
+        a.planes = P1, a.ptiles = T;
+        a.out_planes = P0, a.out_ptiles = T, a.out_g = static_cast<const float*>(w[5]), a.out_ssp = S;
+      }
       return gemv(h, s, kAdd, a, pw(1));
     case CP_SPEC_KERNEL_GATE_UP:
       a.W0 = w[6]; a.W1 = w[7]; a.N = sh.F; a.K = sh.H; a.X = X; a.ldx = sh.H;
       a.norm_g = static_cast<const float*>(w[5]); a.Y = act; a.ldy = sh.F;
+      if (fused) a.planes = P0, a.ptiles = T, a.ssp = S, a.out_planes = P1, a.out_ptiles = T;
       return gemv(h, s, kSwiGLU, a, pw(2), pw(3));
     case CP_SPEC_KERNEL_DOWN:
       a.W0 = w[8]; a.N = sh.H; a.K = sh.F; a.X = act; a.ldx = sh.F; a.Y = X; a.ldy = sh.H;
+      if (fused) {
+        a.planes = P1, a.ptiles = T;
+        if (l + 1 < sh.L)  // the next layer's Q/K/V input
+          a.out_planes = P0, a.out_ptiles = T, a.out_g = static_cast<const float*>(h->layers[l + 1][0]),
+          a.out_ssp = S;
+      }
       return gemv(h, s, kAdd, a, pw(4));
     default:
       return fail(CP_SPEC_EINVAL, "not a decoder kernel kind");
@@ -377,9 +416,13 @@ const int kLayerKinds[5] = {CP_SPEC_KERNEL_QKV, CP_SPEC_KERNEL_ATTENTION, CP_SPE
 
 // All decoder layers over B*R rows of X at positions `pos`, cache `kv`.
 int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const int* pos, float* kv) {
+  const bool fused = fused_planes(h, B * R);
+  if (fused)  // layer 0's Q/K/V input: the rows as the round left them
+    CPS_HIP(launch_split_rows(X, h->sh.H, B * R, h->sh.H, static_cast<const float*>(h->layers[0][0]),
+                              h->at<uint16_t>(h->lo.planes), h->at<float>(h->lo.ssp), s));
   for (int l = 0; l < h->sh.L; ++l)
     for (int kind : kLayerKinds) {
-      const int rc = layer_kernel(h, s, kind, l, B, R, X, pos, kv);
+      const int rc = layer_kernel(h, s, kind, l, B, R, X, pos, kv, fused);
       if (rc) return rc;
     }
   return CP_SPEC_OK;
@@ -708,6 +751,7 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
     }
   // head tables for the draft GEMV: variant v uses heads 1 + (v*W + t) % (G-1)
   const bool grouped = B >= kMfmaMinStreams;
+  const bool fused = fused_planes(h, B * R);
   const int per_head = grouped ? B : 0;
   const int nvar = G - 1;
   std::vector<int> dvar(static_cast<size_t>(nvar) * B * W);
@@ -763,8 +807,14 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
                          nullptr, nullptr, r.dlogits, per_head);
     if (kind == CP_SPEC_KERNEL_TARGET_HEADS)
       return head_logits(h, ls, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head);
-    return layer_kernel(h, ls, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv));
+    return layer_kernel(h, ls, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv), fused);
   };
+  // the layers as the round runs them; one pass first fills every buffer
+  // a kind reads
+  if (fused) {
+    const int rc0 = run_layers(h, s, B, R, r.X, r.pos, h->at<float>(h->lo.kv));
+    if (rc0) return rc0;
+  }
   int rc = launch(s, 0);  // warm the launch path
   if (rc) return rc;
   CPS_HIP(hipStreamSynchronize(s));

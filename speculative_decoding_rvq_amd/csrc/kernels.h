@@ -61,12 +61,21 @@ struct GemvArgs {
   int wtiles;
   const uint16_t* planes;
   int ptiles;
-  const float* ssp;  // [M][K / 256] partial sums of squares (with norm_g)
+  const float* ssp;  // [M][K / 32] partial sums of squares (with norm_g)
+  // ... and the next projection's input, written by this one's epilogue
+  // (SwiGLU: the activations; residual add: the new rows times out_g, with
+  // their partial sums of squares in out_ssp [M][N / 32]); nullable
+  uint16_t* out_planes;
+  int out_ptiles;
+  const float* out_g;
+  float* out_ssp;
 };
 
 struct AttnArgs {
   const float* Q;     // [B*R][qdim]
   float* out;         // [B*R][qdim]
+  uint16_t* planes;   // nullable: out split for the O projection instead
+  int ptiles;         // (planes) row tiles
   const float* kv;    // layer base, + b*kv_sb
   long long kv_sb;
   long long kv_vo;
@@ -172,7 +181,7 @@ hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, 
 // fragment order for launch_bgemm (a.planes): with T = ceil(M / 64) * 4 row
 // tiles, row tile t, K chunk c, plane p at ((c * T + t) * 3 + p) * 512 bf16;
 // rows from M up to 64 T are zero.  With g,
-// ssp[m][j] = sum of x^2 over K block j (256 wide).  K % 256 == 0.
+// ssp[m][j] = sum of x^2 over K chunk j (32 wide).  K % 256 == 0.
 hipError_t launch_split_rows(const float* X, int ldx, int M, int K, const float* g, uint16_t* planes, float* ssp,
                              hipStream_t s);
 // LDS the attention kernel needs, and raising its limit above 64 KB (once,

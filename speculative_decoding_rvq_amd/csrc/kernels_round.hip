@@ -127,21 +127,33 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 3: four output dimensions of one pair per thread ----
-  constexpr int D4 = D / 4;
-  for (int idx = threadIdx.x; idx < npair * D4; idx += kBlock) {
-    const int pr = idx / D4, i4 = (idx % D4) * 4;
+  // ---- phase 3: eight output dimensions of one pair per thread (fp32
+  // rows, or their split pieces for the O projection) ----
+  constexpr int D8 = D / 8;
+  for (int idx = threadIdx.x; idx < npair * D8; idx += kBlock) {
+    const int pr = idx / D8, i8 = (idx % D8) * 8;
     const int r = pr / group, j = pr % group;
     const int pp = pos_s[r];
     if (pp < 0) continue;
     const float* srow = S + pr * 32;
-    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
     for (int p = 0; p <= pp; ++p) {
       const float w = srow[p];
-      const float4 v = *reinterpret_cast<const float4*>(Vs + p * D + i4);
-      o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
+      const float4 v0 = *reinterpret_cast<const float4*>(Vs + p * D + i8);
+      const float4 v1 = *reinterpret_cast<const float4*>(Vs + p * D + i8 + 4);
+      o[0] += w * v0.x; o[1] += w * v0.y; o[2] += w * v0.z; o[3] += w * v0.w;
+      o[4] += w * v1.x; o[5] += w * v1.y; o[6] += w * v1.z; o[7] += w * v1.w;
     }
-    *reinterpret_cast<float4*>(a.out + static_cast<size_t>(b * R + r) * qdim + (g * group + j) * D + i4) = o;
+    const int row = b * R + r, k = (g * group + j) * D + i8;
+    if (a.planes != nullptr) {
+      split_store8(a.planes, a.ptiles, row, k, o);
+    } else {
+      float* dst = a.out + static_cast<size_t>(row) * qdim + k;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
   }
 }
 

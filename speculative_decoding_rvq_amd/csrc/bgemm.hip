@@ -20,10 +20,11 @@
 //    split in registers and written as whole entries to a small XOR-swizzled
 //    LDS stage private to the wave (no block barrier in the K loop, no bank
 //    conflicts on either side).
-// Tiling: a block owns (16 FM) x (16 FN) outputs; its four wave64s split K
-// in quarters and keep the next two chunks' loads in flight.  The partial
-// tiles (and the rows' partial sums of squares) meet in LDS and are added in
-// a fixed order, (w0 + w1) + (w2 + w3): the result does not depend on timing.
+// Tiling: a block owns (16 FM) x (16 FN) outputs; its eight wave64s (two a
+// SIMD, so one's MFMAs cover the other's waits) split K in eighths and keep
+// the next two chunks' loads in flight.  The partial tiles (and the rows'
+// partial sums of squares) meet in LDS and are added in a fixed order: the
+// result does not depend on timing.
 //
 // RMSNorm: x * g is split; the rows' sums of squares are accumulated on the
 // way and 1/sqrt(mean + eps) scales the outputs.  Epilogues: residual add,
@@ -41,7 +42,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = kBlock / kWave;  // 4: K quarters
+constexpr int kGW = 8;               // waves of a block: K eighths
+constexpr int kGT = kGW * kWave;     // 512 threads
 
 // Packed layouts are chunk-major: fragment (tile t, K chunk c) of a matrix
 // packed with NT tiles per chunk is the 1 KB at (c * NT + t) * 512 bf16, so
@@ -63,10 +65,11 @@ __device__ __forceinline__ int btile(int bx, int j) {
 }
 
 template <int MODE, int FM, int FN, bool NORM, bool PL>
-__global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
-  struct StageT { u32x4 f[kWaves][FM * 3][kWave]; };          // split fragments of one chunk
-  struct PartT { float v[kWaves][TM][TN + 1]; float ssq[kWaves][TM]; };
+  constexpr int SW = PL ? 1 : kGW;  // stage: only the in-kernel split uses it
+  struct StageT { u32x4 f[SW][FM * 3][kWave]; };  // split fragments of one chunk
+  struct PartT { float v[4][TM][TN + 1]; float ssq[kGW][TM]; };
   __shared__ union {
     StageT stage;
     PartT part;
@@ -85,8 +88,8 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
   int count;
   if (MODE == kHead) {
     const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
-    __shared__ int red_h[4];
-    count = head_rows_slice(a.head, a.M, j + 1, blockIdx.y * TM, TM, rows_s, red_h);
+    __shared__ int red_h[kGW];
+    count = head_rows_slice<kGT>(a.head, a.M, j + 1, blockIdx.y * TM, TM, rows_s, red_h);
     if (count <= 0) return;
     tile0 = j * (a.N / 16);
   } else {
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
 // 16 f + l / 4, k 8 (l % 4) .. +7 of each chunk (a quad covers one 128-byte
 // row segment) and so holds exactly fragment entry (l / 4) + 16 (l % 4).  A
 // missing row reads X row 0: its outputs and sum of squares are never used.
-  const int cw = a.K / 32 / kWaves;  // chunks of this wave
+  const int cw = a.K / 32 / kGW;  // chunks of this wave
   const int c0 = wave * cw;
   // blocks start their K walk at different chunks, so that the blocks that
   // share a weight tile or an activation tile (on one XCD) do not all miss on
@@ -313,9 +316,10 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
 
   }
 
-  // ---- the four partial tiles (and the rows' partial sums of squares) to
-  // LDS, one barrier, then every thread finishes TM * TN / 256 outputs,
-  // adding the partials in a fixed order: (w0 + w1) + (w2 + w3) ----
+  // ---- the eight partial tiles meet in LDS in a fixed order: waves 4-7
+  // hand theirs to waves 0-3 (w + w+4), which store the four sums; one more
+  // barrier and every thread finishes TM * TN / 512 outputs as
+  // (s0 + s1) + (s2 + s3).  The rows' partial sums of squares go along. ----
   __syncthreads();  // every wave is past its last stage read (stage and part share LDS)
   if (NORM && !PL) {
 #pragma unroll
@@ -326,18 +330,33 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
       if ((lane & 3) == 0) sm.part.ssq[wave][16 * i + (lane >> 2)] = t;
     }
   }
+  auto store_acc = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-  for (int f = 0; f < FM; ++f)
+    for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int n = 0; n < FN; ++n)
+      for (int n = 0; n < FN; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.part.v[wave][16 * f + 4 * lg + i][16 * n + li] = acc[f][n][i];
+        for (int i = 0; i < 4; ++i) sm.part.v[slot][16 * f + 4 * lg + i][16 * n + li] = acc[f][n][i];
+  };
+  if (wave >= 4) store_acc(wave - 4);
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int n = 0; n < FN; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[f][n][i] += sm.part.v[wave][16 * f + 4 * lg + i][16 * n + li];
+  }
+  __syncthreads();
+  if (wave < 4) store_acc(wave);
   __syncthreads();
   auto rinv_of = [&](int r) {
     if constexpr (PL) {
       return rinv_s[r];
     } else {
-      const float t = (sm.part.ssq[0][r] + sm.part.ssq[1][r]) + (sm.part.ssq[2][r] + sm.part.ssq[3][r]);
+      const float t = ((sm.part.ssq[0][r] + sm.part.ssq[4][r]) + (sm.part.ssq[1][r] + sm.part.ssq[5][r])) +
+                      ((sm.part.ssq[2][r] + sm.part.ssq[6][r]) + (sm.part.ssq[3][r] + sm.part.ssq[7][r]));
       return 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
     }
   };
@@ -352,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
     const int per = (k4 + gridDim.x - 1) / gridDim.x;
     const int q0 = blockIdx.x * per, q1 = min(k4, q0 + per);
     const int w = q1 - q0;
-    for (int idx = tid; w > 0 && idx < count * w; idx += kBlock) {
+    for (int idx = tid; w > 0 && idx < count * w; idx += kGT) {
       const int r = idx / w, c = 4 * (q0 + idx % w);
       const int row = rows_s[r];
       const float4 x = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row / a.xdiv) * a.ldx + c);
@@ -369,7 +388,7 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
   if (MODE == kSwiGLU && a.out_planes != nullptr) {
     // the down projection's input: eight activations per thread, split
     constexpr int W = TN / 2, G = TM * W / 8;
-    for (int q = tid; q < G; q += kBlock) {
+    for (int q = tid; q < G; q += kGT) {
       const int r = q / (W / 8), c8 = (q % (W / 8)) * 8;
       const int row = rows_s[r];
       if (row < 0) continue;
@@ -384,37 +403,37 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
     return;
   }
   if (MODE == kSwiGLU) {
-    constexpr int PER = TM * (TN / 2) / kBlock;
+    constexpr int PER = TM * (TN / 2) / kGT;
     float out[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kBlock, r = idx / (TN / 2), c = idx % (TN / 2);
+      const int idx = tid + k * kGT, r = idx / (TN / 2), c = idx % (TN / 2);
       const float g = tile_val(r, c), u = tile_val(r, c + TN / 2);
       out[k] = g / (1.0f + expf(-g)) * u;
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kBlock, r = idx / (TN / 2), c = idx % (TN / 2);
+      const int idx = tid + k * kGT, r = idx / (TN / 2), c = idx % (TN / 2);
       const int row = rows_s[r];
       if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + blockIdx.x * (TN / 2) + c] = out[k];
     }
     return;
   }
-  constexpr int PER = TM * TN / kBlock;
+  constexpr int PER = TM * TN / kGT;
   float val[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int idx = tid + k * kBlock;
+    const int idx = tid + k * kGT;
     val[k] = tile_val(idx / TN, idx % TN);
   }
   if (MODE == kAdd && a.out_planes != nullptr) {
     // the residual rows, then the next normed projection's input: x * g
     // split, eight columns per thread, and the rows' sums of squares per 32
     // columns (four neighbouring lanes)
-    constexpr int G = TM * TN / 8, ITER = (G + kBlock - 1) / kBlock;
+    constexpr int G = TM * TN / 8, ITER = (G + kGT - 1) / kGT;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      const int q = tid + it * kBlock;
+      const int q = tid + it * kGT;
       const int r = q < G ? q / (TN / 8) : 0, c8 = q < G ? (q % (TN / 8)) * 8 : 0;
       const int row = q < G ? rows_s[r] : -1;
       float ss = 0.0f;
@@ -444,19 +463,19 @@ __global__ __launch_bounds__(kBlock) void bgemm_kernel(const GemvArgs a) {
     float old[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kBlock, row = rows_s[idx / TN];
+      const int idx = tid + k * kGT, row = rows_s[idx / TN];
       old[k] = row >= 0 ? a.Y[static_cast<size_t>(row) * a.ldy + n0 + idx % TN] : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kBlock, row = rows_s[idx / TN];
+      const int idx = tid + k * kGT, row = rows_s[idx / TN];
       if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + n0 + idx % TN] = old[k] + val[k];
     }
     return;
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int idx = tid + k * kBlock, r = idx / TN, c = idx % TN;
+    const int idx = tid + k * kGT, r = idx / TN, c = idx % TN;
     const int row = rows_s[r];
     if (row < 0) continue;
     const int o = n0 + c;
@@ -483,21 +502,23 @@ template <int FM, int FN, bool NORM>
 hipError_t launch_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
   const bool pl = a.planes != nullptr;
   switch (mode) {
+    // projections read pre-split rows; the lm_heads (rows gathered per head)
+    // split in the kernel
     case kAdd:
-      if (pl) hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, true>), grid, dim3(kBlock), 0, s, a);
-      else hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      if (!pl) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, true>), grid, dim3(kGT), 0, s, a);
       break;
     case kSwiGLU:
-      if (pl) hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, true>), grid, dim3(kBlock), 0, s, a);
-      else hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      if (!pl) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, true>), grid, dim3(kGT), 0, s, a);
       break;
     case kQKV:
-      if (pl) hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, true>), grid, dim3(kBlock), 0, s, a);
-      else hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      if (!pl) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, true>), grid, dim3(kGT), 0, s, a);
       break;
-    case kHead:  // rows gathered per head: always the in-kernel split
+    case kHead:
       if (pl) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false>), grid, dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false>), grid, dim3(kGT), 0, s, a);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -219,30 +219,37 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
 
 // Exclusive prefix sum of one int per thread over the block (thread order).
 // `red` needs 4 words of LDS.  Returns the exclusive prefix; *total = sum.
+template <int NW = kBlock / kWave>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int inc = wave_incl_scan(v);
   lds_sync();
   if (l == kWave - 1) red[w] = inc;
   lds_sync();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += red[i];
-  *total = red[0] + red[1] + red[2] + red[3];
+  int base = 0, t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    base += i < w ? red[i] : 0;
+    t += red[i];
+  }
+  *total = t;
   return base + inc - v;
 }
 
 // The rows of one lm_head: indices i < n, ascending, with head[i] == h.  The
 // block keeps positions [first, first + cap) of that list in rows[0..cap)
-// (-1 past its end) and returns how many it kept.  `red` is 4 ints of LDS.
+// (-1 past its end) and returns how many it kept; NT threads in the block,
+// `red` is NT / 64 ints of LDS.
+template <int NT = kBlock>
 __device__ __forceinline__ int head_rows_slice(const int* head, int n, int h, int first, int cap, int* rows,
                                                int* red) {
-  for (int i = threadIdx.x; i < cap; i += kBlock) rows[i] = -1;
+  for (int i = threadIdx.x; i < cap; i += NT) rows[i] = -1;
   int base = 0;
-  for (int r0 = 0; r0 < n; r0 += kBlock) {
+  for (int r0 = 0; r0 < n; r0 += NT) {
     const int i = r0 + threadIdx.x;
     const bool hit = i < n && head[i] == h;
     int total;
-    const int pos = base + block_exclusive_scan(hit ? 1 : 0, red, &total);  // barriers inside
+    const int pos = base + block_exclusive_scan<NT / kWave>(hit ? 1 : 0, red, &total);  // barriers inside
     if (hit && pos >= first && pos < first + cap) rows[pos - first] = i;
     base += total;
   }

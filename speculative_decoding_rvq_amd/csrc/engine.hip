@@ -246,10 +246,10 @@ bool mfma_fits(int mode, const GemvArgs& a) {
 // Block tile (16 fm) x (16 fn) of the packed bf16 kernel for M rows: the
 // largest that still gives every compute unit a block, else the one with the
 // most blocks; false when no tile divides the columns or K is not a
-// multiple of 256 (four waves, each an even number of 32-wide chunks).
+// multiple of 512 (eight waves, each an even number of 32-wide chunks).
 bool bgemm_tile(int mode, int N, int K, int M, int* fm_out, int* fn_out) {
   static const int kTiles[4][2] = {{4, 6}, {4, 4}, {2, 4}, {2, 2}};
-  if (K % 256) return false;
+  if (K % 512) return false;
   int best = -1, best_blocks = 0;
   for (int i = 0; i < 4; ++i) {
     const int fm = kTiles[i][0], fn = kTiles[i][1];
@@ -438,7 +438,7 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
   a.norm_g = norm_g; a.eps = h->sh.eps; a.Y = logits; a.ldy = h->sh.V; a.head = head;
   a.head_stride = static_cast<long long>(h->sh.V) * h->sh.H; a.xnorm_out = xnorm_out;
   a.n_heads = h->sh.G - 1;
-  if (per_head > 0 && h->packed_heads != nullptr && a.N % 64 == 0 && a.K % 256 == 0) {
+  if (per_head > 0 && h->packed_heads != nullptr && a.N % 64 == 0 && a.K % 512 == 0) {
     // bf16, packed heads: 32 x 64 tiles per head
     a.W0 = h->packed_heads;
     a.wtiles = a.n_heads * (a.N / 16);

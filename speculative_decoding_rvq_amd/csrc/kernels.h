@@ -168,7 +168,7 @@ enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };
 hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
 // Matrix-core projections with in-block split-K over fragment-packed bf16
 // weights (W0 / W1 packed by pack_fragments): block tile (16 fm) x (16 fn),
-// (fm, fn) in {(2, 2), (2, 4), (4, 4), (4, 6)}, K a multiple of 256; grid
+// (fm, fn) in {(2, 2), (2, 4), (4, 4), (4, 6)}, K a multiple of 512; grid
 // (columns / tile, rows / tile) or, lm_heads, (V / tile, row tiles, heads).
 hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
 // One bf16 matrix [N][K] row-major into MFMA fragment order (N % 16 == 0,

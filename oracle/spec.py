@@ -185,6 +185,22 @@ def decode(model, dp: dict, h_frame, c0, seeds, frames=None, streams=None,
     return codes, flags
 
 
+def talker_feedback(model, codes) -> np.ndarray:
+    """The codec part of the Talker's next input for a finished frame
+    (SGLang-Omni note, the Talker/CodePredictor hand-off paragraph; "RVQ
+    Position Aware ...", section 2.1): the sum over the frame's code groups
+    g = 0..G-1 of that group's embedding row E_g[c_g], in float64.  The text
+    projection the Talker adds is not part of the CodePredictor.
+
+    Pins: tests/test_oracle_feedback.py -- one-hot matrix products give the
+    same vector, replacing one code changes it by the difference of the two
+    rows, and a hand-sized table model."""
+    acc = np.zeros(model.H, dtype=np.float64)
+    for g in range(model.G):
+        acc = acc + model.embed_row(g, int(codes[g]))
+    return acc
+
+
 def codes_per_round(stats: dict) -> float:
     """Committed codes per verify pass (a round commits 1 + accepted drafts;
     the autoregressive loop scores 1.0)."""

@@ -151,10 +151,34 @@ def run_workload(cid, steps, warmup, verify_size=None, frames=None,
     if kernels:
         torch.cuda.synchronize()
         res["kernels"] = kernel_table(h, c, B)
+        res["talker_feedback"] = feedback_timing(h, c, out, torch)
     h.close()
     del wdev
     torch.cuda.empty_cache()
     return res, c
+
+
+def feedback_timing(h, c, out, torch, iters=50):
+    """The Talker hand-off (sum of each finished frame's embedding rows) over
+    every frame the timed decode produced, HIP events around `iters`
+    launches on the current stream."""
+    F, B, G = out.shape
+    codes = out.reshape(F * B, G).contiguous()
+    fb = torch.empty((F * B, c["hidden"]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    h.talker_feedback(codes, fb)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        h.talker_feedback(codes, fb)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / iters
+    ws = 2 if c["dtype"] == "bf16" else 4
+    nbytes = F * B * (G * c["hidden"] * ws + c["hidden"] * 4 + G * 4)
+    return {"rows": F * B, "us_per_launch": us, "us_per_frame": us / (F * B),
+            "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / us / 1e3}
 
 
 def cpu_baseline(cid, n_frames):
@@ -258,6 +282,7 @@ def main():
         "kernels": {k: {kk: round(v, 3) if isinstance(v, float) else v
                         for kk, v in t.items()}
                     for k, t in main_res["kernels"].items()},
+        "talker_feedback": main_res["talker_feedback"],
     }
     if not args.no_extra:
         ar, _ = run_workload(args.workload, 1, 1, verify_size=0, frames=args.frames)

@@ -209,6 +209,20 @@ int cp_spec_decoder_forward(cp_spec* h, void* stream, int32_t n_streams,
                             int32_t rows_per_stream, float* d_x,
                             const int32_t* d_pos, float* d_kv);
 
+/* The codec part of the Talker's next input for finished frames (SGLang-Omni
+ * note, the Talker / CodePredictor hand-off paragraph; "RVQ Position Aware
+ * ...", section 2.1): for each row i,
+ *   d_out[i][:] = sum over g = 0..G-1 of E_g[d_codes[i][g]]
+ * added in group order in float32 (the text projection the Talker adds is
+ * not part of the CodePredictor).  d_codes [n_rows][G] i32 device (the
+ * layout of cp_spec_decode_frames' out_codes, n_rows = frames x streams);
+ * d_out [n_rows][H] f32 device, 16-byte aligned, caller-owned.  A row with a
+ * code outside [0, V) is written as NaN.  Asynchronous on `stream`.
+ * Errors: EINVAL for n_rows < 0, null pointers or misaligned buffers;
+ * EUNSUPPORTED for G > 64 or H not a multiple of 4. */
+int cp_spec_talker_feedback(cp_spec* h, void* stream, int32_t n_rows,
+                            const int32_t* d_codes, float* d_out);
+
 /* ---- measurement --------------------------------------------------------
  * Kernel kinds of the round, for cp_spec_time_kernel. */
 #define CP_SPEC_KERNEL_DRAFT_HEADS 0  /* stacked-head draft GEMV            */

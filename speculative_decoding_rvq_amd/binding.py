@@ -82,6 +82,7 @@ _SIGS = {
     "cp_spec_head_logits": (C.c_int, [_P, _P, C.c_int32, _P, _P, C.c_int32,
                                       _P]),
     "cp_spec_topk_sample": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P]),
+    "cp_spec_talker_feedback": (C.c_int, [_P, _P, C.c_int32, _P, _P]),
     "cp_spec_accept": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _P]),
     "cp_spec_decoder_forward": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P,
@@ -234,6 +235,11 @@ class Handle:
         return _check(lib().cp_spec_topk_sample(
             self.h, _stream(stream), int(logits.shape[0]), _ptr(logits),
             _ptr(u), _ptr(probs), _ptr(codes), _ptr(flags)))
+
+    def talker_feedback(self, codes, out, stream=None):
+        """codes [n][G] int32 -> out [n][H] float32 (sum of E_g[c_g])."""
+        return _check(lib().cp_spec_talker_feedback(
+            self.h, _stream(stream), int(codes.shape[0]), _ptr(codes), _ptr(out)))
 
     def accept(self, gamma, draft, q, p, u_accept, u_target, n_out, codes_out,
                flags_out=None, stream=None):

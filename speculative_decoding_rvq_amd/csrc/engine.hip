@@ -699,6 +699,21 @@ int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows, const float* d
   return CP_SPEC_OK;
 }
 
+int cp_spec_talker_feedback(cp_spec* h, void* stream, int32_t n_rows, const int32_t* d_codes, float* d_out) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (n_rows < 0) return fail(CP_SPEC_EINVAL, "n_rows < 0");
+  if (n_rows == 0) return CP_SPEC_OK;
+  if (!d_codes || !d_out) return fail(CP_SPEC_EINVAL, "null pointer");
+  const Shape& sh = h->sh;
+  if (sh.G > 64 || sh.H % 4) return fail(CP_SPEC_EUNSUPPORTED, "feedback needs G <= 64 and H % 4 == 0");
+  if (reinterpret_cast<uintptr_t>(d_out) % 16 ||
+      reinterpret_cast<uintptr_t>(h->embed) % (sh.wdt == CP_SPEC_BF16 ? 8 : 16))
+    return fail(CP_SPEC_EINVAL, "misaligned embedding tables or output");
+  CPS_HIP(launch_talker_feedback(h->embed, sh.wdt == CP_SPEC_BF16, sh.G, sh.V, sh.H, d_codes, n_rows, d_out,
+                                 static_cast<hipStream_t>(stream)));
+  return CP_SPEC_OK;
+}
+
 int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width, const int32_t* d_gamma,
                    const int32_t* d_draft, const float* d_q, const float* d_p,
                    const float* d_u_accept, const float* d_u_target, int32_t* d_n, int32_t* d_codes,

@@ -199,5 +199,10 @@ hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s);
 // Adds the B per-stream counters to *out (one block; fixed order).
 hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats* out, hipStream_t s);
+// out[i][:] = sum over g < G of E_g[codes[i * G + g]] (float32, group
+// order); G <= 64, H % 4 == 0, the embedding rows 8-byte (bf16) or 16-byte
+// (fp32) aligned.
+hipError_t launch_talker_feedback(const void* embed, int wbf16, int G, int V, int H, const int* codes, int n,
+                                  float* out, hipStream_t s);
 
 }  // namespace cps

@@ -835,6 +835,52 @@ hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// The codec part of the Talker's next input for finished frames: row i is
+// the sum over groups g = 0..G-1 of E_g[codes[i][g]], added in group order
+// in float32.  A code outside [0, V) makes the row NaN.  One block per row,
+// four channels per thread per step.
+__global__ __launch_bounds__(kBlock) void talker_feedback_kernel(const void* embed, int wbf16, int G, int V, int H,
+                                                                 const int* codes, float* out) {
+  __shared__ int code_s[64];
+  __shared__ int bad_s;
+  const int row = blockIdx.x;
+  if (threadIdx.x == 0) bad_s = 0;
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += kBlock) {
+    const int c = codes[static_cast<size_t>(row) * G + g];
+    const bool ok = c >= 0 && c < V;
+    code_s[g] = ok ? c : 0;
+    if (!ok) bad_s = 1;
+  }
+  __syncthreads();
+  const float nan = __uint_as_float(0x7FC00000u);
+  float* dst = out + static_cast<size_t>(row) * H;
+  for (int i = threadIdx.x * 4; i < H; i += kBlock * 4) {
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    for (int g = 0; g < G; ++g) {
+      const size_t off = (static_cast<size_t>(g) * V + code_s[g]) * H + i;
+      if (wbf16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(embed) + off);
+        a0 += bf16lo(v.x); a1 += bf16hi(v.x); a2 += bf16lo(v.y); a3 += bf16hi(v.y);
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(embed) + off);
+        a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
+      }
+    }
+    if (bad_s) a0 = a1 = a2 = a3 = nan;
+    *reinterpret_cast<float4*>(dst + i) = make_float4(a0, a1, a2, a3);
+  }
+}
+
+hipError_t launch_talker_feedback(const void* embed, int wbf16, int G, int V, int H, const int* codes, int n,
+                                  float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (G > 64 || H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(talker_feedback_kernel, dim3(n), dim3(kBlock), 0, s, embed, wbf16, G, V, H, codes, out);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kBlock) void stats_flush_kernel(const cp_spec_stats* sstats, int B,
                                                              cp_spec_stats* out) {
   constexpr int kW = sizeof(cp_spec_stats) / sizeof(long long);

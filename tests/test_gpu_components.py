@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import device_weights, handle, log, oracle_model, weights
+from gpu_util import decode_gpu, device_weights, handle, log, oracle_model, weights
 from oracle import decoder as odec
 from oracle import distributions as odist
 
@@ -280,3 +280,27 @@ def test_decoder_ragged_blocks_and_truncation(cid, B):
     # pattern 0 keeps positions 0..3, pattern 1 keeps 0..3, pattern 2 0..2
     step(pattern([[4, 5], list(range(4, 4 + R)), [3]]),
          trunc=pattern([4, 4, 3]))
+
+
+@pytest.mark.parametrize("cid", ["tiny", "qwen3tts"])
+def test_talker_feedback(cid):
+    """Sum of the frame's embedding rows (Talker hand-off) against the oracle,
+    on codes the GPU decoded; a row with an out-of-range code is NaN."""
+    from oracle import spec as ospec
+    log(f"talker feedback {cid}")
+    c = synth.config(cid, frames=6)
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle(cid)
+    gc, _, _ = decode_gpu(h, hf, c0, seeds)
+    F, B, G = gc.shape
+    codes = np.ascontiguousarray(gc.reshape(F * B, G)).astype(np.int32)
+    codes = np.concatenate([codes, codes[:1]])
+    codes[-1, G // 2] = c["vocab"]                  # out of range: NaN row
+    out = torch.empty((codes.shape[0], c["hidden"]), dtype=torch.float32, device="cuda")
+    h.talker_feedback(_t(codes), out)
+    got = out.cpu().numpy()
+    m = oracle_model(cid)
+    for i in range(F * B):
+        ref = ospec.talker_feedback(m, codes[i])
+        np.testing.assert_allclose(got[i], ref, rtol=2e-6, atol=2e-6 * np.abs(ref).max())
+    assert np.all(np.isnan(got[-1]))

@@ -98,6 +98,10 @@ class Model:
         self._embed = w["embed"]           # converted one row at a time
         self.heads = _f64(w["heads"], self.dtype)
         self.final_norm = np.asarray(w["final_norm"], np.float64)
+        # position-aware draft offsets b_1..b_K (float32 vectors), or None
+        off = w.get("draft_offsets")
+        self.draft_offsets = (None if off is None or len(off) == 0 else
+                              np.asarray(off, np.float32).astype(np.float64))
         self.layers = []
         for lw in w["layers"]:
             cv = {}

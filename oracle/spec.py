@@ -11,8 +11,12 @@ h_1) with U(1, target); s = 1.
 
 Round, while s < G - 1, with gamma = min(N - 1, G - 2 - s) (0 when
 speculation is off, which is exactly the autoregressive loop):
-  draft   t = 1..gamma: q_t = TopKSoftmax(head_{s+t} h_s),
+  draft   t = 1..gamma: q_t = TopKSoftmax(head_{s+t} (h_s + b_t)),
           d_t = Sample(q_t, U(s+t, draft))                  [greedy: argmax]
+          b_t is the position-aware offset of draft offset t ("RVQ Position
+          Aware ...", section 2.2 and Figure 3): K vectors shared by every
+          starting depth s, none (b_t = 0) when the model has no offsets or
+          t > K.  Only q depends on b, so the output distribution does not.
   verify  one causal pass over rows r = 0..gamma at positions s+1+r with
           inputs E_s[c_s] (r = 0) and E_{s+r}[d_r] (r >= 1); row r is scored
           by head_{s+1+r}, so row t-1 scores draft d_t (the logit shift of
@@ -34,6 +38,10 @@ autoregressive output exactly for N = 2..8; brute-force enumeration of every
 draft outcome equals the autoregressive joint to 1e-12; chi-square of
 speculative code sequences against the exact autoregressive joint; special
 cases p == q (all accepted) and k = 1 (deterministic chain equals greedy).
+tests/test_oracle_offsets.py -- draft logits of an offset that moves h_s onto
+a scaled unit vector equal the scaled head column; with large one-hot offsets
+every draft is the argmax of its head's column at offset t; greedy output and
+the chi-square of stochastic output are unchanged by offsets.
 """
 from __future__ import annotations
 
@@ -70,17 +78,26 @@ class _Frame:
             self.stats["near_tie_" + kind] += 1
 
 
-def _dist(model, fr, j, h, dp):
-    """Processed distribution for depth j from hidden h (stochastic mode)."""
-    p, f_topk = dist.topk_softmax(model.logits(j, h), dp["temperature"],
-                                  dp["top_k"])
+def draft_logits(model, j: int, t: int, h) -> np.ndarray:
+    """Draft logits of offset t from h_s for depth j = s + t: head_j applied
+    to h_s + b_t ("RVQ Position Aware ...", section 2.2, Figure 3), or to
+    h_s alone when there is no b_t."""
+    b = getattr(model, "draft_offsets", None)
+    if b is not None and t <= len(b):
+        h = h + b[t - 1]
+    return model.logits(j, h)
+
+
+def _dist(model, fr, j, z, dp):
+    """Processed distribution for depth j from logits z (stochastic mode)."""
+    p, f_topk = dist.topk_softmax(z, dp["temperature"], dp["top_k"])
     if dp["top_k"] < model.V:
         fr.flag("topk", j, f_topk)
     return p
 
 
-def _greedy(model, fr, j, h):
-    code, f_arg = dist.argmax_with_gap(model.logits(j, h))
+def _greedy(fr, j, z):
+    code, f_arg = dist.argmax_with_gap(z)
     fr.flag("argmax", j, f_arg)
     return code
 
@@ -92,10 +109,11 @@ def _draw(fr, w, seed, depth, purpose):
 
 
 def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
-                 stats: dict | None = None):
+                 stats: dict | None = None, trace: list | None = None):
     """Decode one frame.  ``dp`` = {verify_size, greedy, temperature, top_k}.
 
     Returns (codes [G] int32 with codes[0] = c0, near-tie flag bitmask).
+    ``trace``, if given, receives (s, h_s, drafts, n) for every round.
     """
     stats = new_stats() if stats is None else stats
     G = model.G
@@ -111,21 +129,23 @@ def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
     h = outs[1]
     if G > 1:
         if greedy:
-            fr.codes[1] = _greedy(model, fr, 1, h)
+            fr.codes[1] = _greedy(fr, 1, model.logits(1, h))
         else:
-            fr.codes[1] = _draw(fr, _dist(model, fr, 1, h, dp), seed, 1,
-                                PURPOSE_TARGET)
+            fr.codes[1] = _draw(fr, _dist(model, fr, 1, model.logits(1, h),
+                                          dp), seed, 1, PURPOSE_TARGET)
     s = 1
 
     while s < G - 1:
         gamma = 0 if N == 0 else min(N - 1, G - 2 - s)
-        # (1) draft from h_s with the later heads
+        # (1) draft from h_s (+ b_t) with the later heads
+        h_s = h
         drafts, qs = [], []
         for t in range(1, gamma + 1):
+            z = draft_logits(model, s + t, t, h)
             if greedy:
-                drafts.append(_greedy(model, fr, s + t, h))
+                drafts.append(_greedy(fr, s + t, z))
             else:
-                q = _dist(model, fr, s + t, h, dp)
+                q = _dist(model, fr, s + t, z, dp)
                 qs.append(q)
                 drafts.append(_draw(fr, q, seed, s + t, PURPOSE_DRAFT))
         # (2) verify: one causal block over the committed depth + drafts
@@ -135,13 +155,14 @@ def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
                                   kv)
         # (3) accept
         if greedy:
-            target = [_greedy(model, fr, s + 1 + r, outs[r])
+            target = [_greedy(fr, s + 1 + r, model.logits(s + 1 + r, outs[r]))
                       for r in range(gamma + 1)]
             rnd = dist.verify_greedy(drafts, target)
             emitted = list(rnd.emitted)
             n_acc = len(rnd.accepted)
         else:
-            ps = [_dist(model, fr, s + 1 + r, outs[r], dp)
+            ps = [_dist(model, fr, s + 1 + r, model.logits(s + 1 + r, outs[r]),
+                        dp)
                   for r in range(gamma + 1)]
             emitted, n_acc, near = dist.accept_scan(
                 drafts, qs, ps,
@@ -154,6 +175,8 @@ def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
         fr.codes[s + 1: s + 1 + n] = emitted
         kv.truncate(s + n + 1)
         h = outs[n - 1]
+        if trace is not None:
+            trace.append((s, h_s, tuple(int(d) for d in drafts), n))
         stats["rounds"] += 1
         for t in range(1, gamma + 1):
             stats["proposed"][t - 1] += 1

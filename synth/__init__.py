@@ -86,7 +86,9 @@ def config(wl: str, **overrides) -> dict:
     vocab (V), dtype ('f32'|'bf16'), rope_theta, rms_eps, greedy,
     temperature, top_k, verify_size (N; 0 = autoregressive), streams (B),
     frames (F), heads_corr (None or the noise scale of correlated heads),
-    plus 'id', 'weight_seed', 'input_seed', 'philox_base'.
+    draft_offsets (K position-aware draft offset vectors, default 0),
+    offset_scale (their standard deviation, default 0.1),
+    plus 'id', 'weight_seed', 'input_seed', 'philox_base', 'offset_seed'.
     """
     n = WORKLOADS.index(wl) + 1
     c = copy.deepcopy(_BASE[wl])
@@ -94,6 +96,7 @@ def config(wl: str, **overrides) -> dict:
     c["weight_seed"] = 1000 + n
     c["input_seed"] = 2000 + n
     c["philox_base"] = (3000 + n) << 32
+    c["offset_seed"] = 4000 + n
     c.update(overrides)
     return c
 
@@ -105,7 +108,7 @@ def custom(**kw) -> dict:
              rope_theta=1e4, rms_eps=1e-6, greedy=False, temperature=0.9,
              top_k=4, verify_size=3, streams=1, frames=4, heads_corr=None,
              id=0, weight_seed=7, input_seed=8, philox_base=9 << 32,
-             weight_scale=0.02)
+             offset_seed=10, weight_scale=0.02)
     c.update(kw)
     return c
 
@@ -154,8 +157,11 @@ def make_weights(c: dict) -> dict:
     """Draw the weights of configuration ``c``.
 
     Returns {'embed': [G][V][H], 'heads': [G-1][V][H] (head j at index j-1),
-    'final_norm': [H] f32, 'layers': [ {name: array} ... ]}.  Matrices are
-    float32 for 'f32' configurations and uint16 bf16 bit patterns for 'bf16'.
+    'final_norm': [H] f32, 'layers': [ {name: array} ... ]} and, when the
+    configuration asks for K > 0 draft offsets, 'draft_offsets': [K][H] f32
+    from a generator of their own (so the other weights do not change).
+    Matrices are float32 for 'f32' configurations and uint16 bf16 bit
+    patterns for 'bf16'.
     """
     rng = np.random.Generator(np.random.PCG64(c["weight_seed"]))
     G, V, H, dt = c["groups"], c["vocab"], c["hidden"], c["dtype"]
@@ -184,6 +190,11 @@ def make_weights(c: dict) -> dict:
                 lw[name] = _draw(rng, shape, s, dt)
         layers.append(lw)
     w["layers"] = layers
+    K = int(c.get("draft_offsets", 0))
+    if K > 0:
+        ro = np.random.Generator(np.random.PCG64(c["offset_seed"]))
+        w["draft_offsets"] = (ro.standard_normal((K, H), dtype=np.float32) *
+                              np.float32(c.get("offset_scale", 0.1)))
     return w
 
 

@@ -100,7 +100,7 @@ def roofline(table, weight_dtype, workload=None):
 
 
 def run_workload(cid, steps, warmup, verify_size=None, frames=None,
-                 kernels=False):
+                 kernels=False, offsets=None):
     import numpy as np
     import torch
 
@@ -111,6 +111,8 @@ def run_workload(cid, steps, warmup, verify_size=None, frames=None,
         over["verify_size"] = verify_size
     if frames is not None:
         over["frames"] = frames
+    if offsets is not None:  # (K, scale): seeded position-aware draft offsets
+        over["draft_offsets"], over["offset_scale"] = offsets
     c = synth.config(cid, **over)
     w = synth.make_weights(c)
     wdev = binding.weights_to_device(w)
@@ -306,6 +308,23 @@ def main():
         line["streams64_qwen3tts"]["kernels"] = {
             k: {kk: round(v, 3) if isinstance(v, float) else v for kk, v in t.items()}
             for k, t in q64["kernels"].items()}
+        # position-aware draft offsets (3 seeded vectors): same decode, the
+        # draft heads reading h_s + b_t; untrained offsets, so only the cost
+        # and the changed acceptance are meaningful
+        line["draft_offsets"] = {}
+        for wl, steps in ((args.workload, args.steps), ("qwen3tts-64", 1)):
+            ref = main_res if wl == args.workload else q64
+            o, co = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
+                                 offsets=(3, 0.1))
+            line["draft_offsets"][wl] = {
+                "K": co["draft_offsets"], "scale": co["offset_scale"],
+                "codes_per_s": o["codes_per_s"], "ms_per_step": o["ms_per_step"],
+                "codes_per_verify_pass": o["codes_per_verify_pass"],
+                "acceptance_by_offset": o["acceptance_by_offset"],
+                "throughput_vs_no_offsets": o["codes_per_s"] / ref["codes_per_s"],
+                "round_time_vs_no_offsets": (o["ms_per_step"] / o["stats"]["rounds"]) /
+                                                    (ref["ms_per_step"] / ref["stats"]["rounds"]),
+            }
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 

@@ -83,6 +83,11 @@ typedef struct cp_spec_cfg {
   float temperature;    /* > 0 unless greedy                                 */
   int32_t top_k;        /* 1..V unless greedy                                */
   int32_t max_streams;  /* largest n_streams any call will pass              */
+  int32_t draft_offsets;/* K: position-aware draft offsets b_1..b_K, 0..8    */
+                        /* ("RVQ Position Aware ...", section 2.2, Fig. 3):  */
+                        /* draft offset t <= K scores with head_{s+t} the    */
+                        /* state h_s + b_t, t > K the state h_s; only the    */
+                        /* draft distributions q change. 0 = no offsets.     */
 } cp_spec_cfg;
 
 typedef struct cp_spec_weights {
@@ -94,6 +99,9 @@ typedef struct cp_spec_weights {
    * ffn_norm[H] (f32), w_gate[F][H], w_up[F][H], w_down[H][F].
    * Read during cp_spec_create only; the device pointers are borrowed. */
   const void* const* layer;
+  /* [K][H] f32 device, b_t at row t-1, 16-byte aligned; borrowed and read by
+   * every decode call; required when cfg.draft_offsets > 0, else ignored. */
+  const float* draft_offsets;
 } cp_spec_weights;
 
 /* Device-side statistics, accumulated (never cleared) by decode calls. */

@@ -32,12 +32,14 @@ class Cfg(C.Structure):
                 ("weight_dtype", C.c_int32), ("rope_theta", C.c_float),
                 ("rms_eps", C.c_float), ("verify_size", C.c_int32),
                 ("greedy", C.c_int32), ("temperature", C.c_float),
-                ("top_k", C.c_int32), ("max_streams", C.c_int32)]
+                ("top_k", C.c_int32), ("max_streams", C.c_int32),
+                ("draft_offsets", C.c_int32)]
 
 
 class Weights(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("heads", C.c_void_p),
-                ("final_norm", C.c_void_p), ("layer", C.POINTER(C.c_void_p))]
+                ("final_norm", C.c_void_p), ("layer", C.POINTER(C.c_void_p)),
+                ("draft_offsets", C.c_void_p)]
 
 
 class Stats(C.Structure):
@@ -138,7 +140,8 @@ def make_cfg(c: dict, max_streams: int | None = None) -> Cfg:
                rope_theta=c["rope_theta"], rms_eps=c["rms_eps"],
                verify_size=c["verify_size"], greedy=int(bool(c["greedy"])),
                temperature=c["temperature"], top_k=c["top_k"],
-               max_streams=max_streams or c["streams"])
+               max_streams=max_streams or c["streams"],
+               draft_offsets=int(c.get("draft_offsets", 0)))
 
 
 def workspace_bytes(cfg: Cfg) -> int:
@@ -170,9 +173,12 @@ def weights_to_device(w: dict, device="cuda") -> dict:
             a = a.view(np.int16)
         return torch.from_numpy(a).to(device)
 
-    return {"embed": dev(w["embed"]), "heads": dev(w["heads"]),
-            "final_norm": dev(w["final_norm"]),
-            "layers": [{k: dev(v) for k, v in lw.items()} for lw in w["layers"]]}
+    out = {"embed": dev(w["embed"]), "heads": dev(w["heads"]),
+           "final_norm": dev(w["final_norm"]),
+           "layers": [{k: dev(v) for k, v in lw.items()} for lw in w["layers"]]}
+    if w.get("draft_offsets") is not None:
+        out["draft_offsets"] = dev(np.asarray(w["draft_offsets"], np.float32))
+    return out
 
 
 LAYER_ORDER = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate",
@@ -200,7 +206,9 @@ class Handle:
         self.weights = Weights(wdev["embed"].data_ptr(),
                                wdev["heads"].data_ptr(),
                                wdev["final_norm"].data_ptr(),
-                               C.cast(self._layer_ptrs, C.POINTER(C.c_void_p)))
+                               C.cast(self._layer_ptrs, C.POINTER(C.c_void_p)),
+                               wdev["draft_offsets"].data_ptr()
+                               if wdev.get("draft_offsets") is not None else None)
         h = C.c_void_p()
         self.status = _check(lib().cp_spec_create(
             C.byref(self.weights), C.byref(self.cfg),

@@ -37,10 +37,11 @@ struct Shape {
   float theta, eps, T;
   int R, W, qdim, kvdim;
   int vec;  // weight elements per 16-byte chunk
+  int K;    // position-aware draft offsets (0 = none)
 };
 
 struct Layout {
-  size_t st, call, sstats, dhead, thead, pos, hstate, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
+  size_t st, call, sstats, dhead, thead, pos, hstate, dX, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
       tlogits, p, tcode, tflags, rope, packed, planes, ssp, total;
 };
 
@@ -75,6 +76,8 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
     if (!(c->temperature > 0.0f)) return fail(CP_SPEC_EINVAL, "temperature must be > 0");
     if (c->top_k < 1 || c->top_k > c->vocab) return fail(CP_SPEC_EINVAL, "top_k must be in 1..vocab");
   }
+  if (c->draft_offsets < 0 || c->draft_offsets > CP_SPEC_MAX_OFFSETS)
+    return fail(CP_SPEC_EINVAL, "draft_offsets must be in 0..8");
   if (c->vocab > CP_SPEC_MAX_VOCAB)
     return fail(CP_SPEC_EUNSUPPORTED, "vocab above the small-vocabulary bound (4096)");
   const int vpt = c->vocab / 256;
@@ -98,6 +101,7 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   }
   s_.R = std::max(s_.N, 2);
   s_.W = std::max(s_.N - 1, 1);
+  s_.K = s_.N >= 2 ? c->draft_offsets : 0;  // no drafts, no offsets
   for (int K : {s_.H, s_.qdim, s_.F})
     if (!choose_kt(K, s_.vec))
       return fail(CP_SPEC_EUNSUPPORTED, "matrix width " + std::to_string(K) +
@@ -152,6 +156,7 @@ Layout make_layout(const Shape& s) {
   l.thead = take(B * R * i4);
   l.pos = take(B * R * i4);
   l.hstate = take(B * s.H * f4);
+  l.dX = take(s.K > 0 ? B * W * s.H * f4 : 0);  // draft inputs h_s + b_t
   l.X = take(B * R * s.H * f4);
   l.Hout = take(B * R * s.H * f4);
   l.Q = take(B * R * s.qdim * f4);
@@ -187,6 +192,7 @@ struct cp_spec {
   const void* embed;
   const void* heads;
   const float* fnorm;
+  const float* doff = nullptr;  // [K][H] draft offsets (borrowed)
   std::vector<std::array<const void*, 9>> layers;
   // fragment-packed bf16 copies (batched path): per layer QKV, O, gate, up,
   // down; the lm_heads; all null when the weights are not packed
@@ -213,6 +219,9 @@ struct cp_spec {
     r.thead = at<int>(lo.thead);
     r.pos = at<int>(lo.pos);
     r.hstate = at<float>(lo.hstate);
+    r.K = sh.K;
+    r.doff = doff;
+    r.dX = sh.K > 0 ? at<float>(lo.dX) : nullptr;
     r.X = at<float>(lo.X);
     r.Hout = at<float>(lo.Hout);
     r.dlogits = at<float>(lo.dlogits);
@@ -467,7 +476,10 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
   // and head in each of the draft and verify row sets
   const int per_head = B >= kMfmaMinStreams ? B : 0;
   if (sh.N >= 2) {
-    if ((rc = head_logits(h, s, B * sh.W, r.hstate, sh.W, r.dhead, nullptr, nullptr, r.dlogits, per_head)))
+    // draft rows read h_s, or h_s + b_t when the drafter has offsets
+    const float* dx = r.K > 0 ? r.dX : r.hstate;
+    if ((rc = head_logits(h, s, B * sh.W, dx, r.K > 0 ? 1 : sh.W, r.dhead, nullptr, nullptr, r.dlogits,
+                          per_head)))
       return rc;
     CPS_HIP(launch_draft_topk(r, s));
   }
@@ -541,6 +553,9 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
     return fail(CP_SPEC_EWORKSPACE, "workspace must be 256-byte aligned");
   for (int i = 0; i < 9 * s.L; ++i)
     if (!w->layer[i]) return fail(CP_SPEC_EINVAL, "null layer weight pointer");
+  if (cfg->draft_offsets > 0 &&
+      (!w->draft_offsets || reinterpret_cast<uintptr_t>(w->draft_offsets) % 16))
+    return fail(CP_SPEC_EINVAL, "draft_offsets > 0 needs a 16-byte aligned offset array");
 
   cp_spec* h = new cp_spec();
   h->sh = s;
@@ -549,6 +564,7 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
   h->embed = w->embed;
   h->heads = w->heads;
   h->fnorm = w->final_norm;
+  h->doff = s.K > 0 ? w->draft_offsets : nullptr;
   h->layers.resize(s.L);
   for (int l = 0; l < s.L; ++l)
     for (int j = 0; j < 9; ++j) h->layers[l][j] = w->layer[9 * l + j];
@@ -818,8 +834,8 @@ int cp_spec_time_kernel(cp_spec* h, void* stream, int32_t n_streams, int32_t kin
   }
   auto launch = [&](hipStream_t ls, int i) -> int {
     if (kind == CP_SPEC_KERNEL_DRAFT_HEADS)
-      return head_logits(h, ls, B * W, r.hstate, W, d_dvar + static_cast<size_t>(i % nvar) * B * W,
-                         nullptr, nullptr, r.dlogits, per_head);
+      return head_logits(h, ls, B * W, r.K > 0 ? r.dX : r.hstate, r.K > 0 ? 1 : W,
+                         d_dvar + static_cast<size_t>(i % nvar) * B * W, nullptr, nullptr, r.dlogits, per_head);
     if (kind == CP_SPEC_KERNEL_TARGET_HEADS)
       return head_logits(h, ls, B * R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head);
     return layer_kernel(h, ls, kind, i % sh.L, B, R, r.X, r.pos, h->at<float>(h->lo.kv), fused);

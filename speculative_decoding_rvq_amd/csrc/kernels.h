@@ -147,6 +147,9 @@ struct RoundArgs {
   int* thead;   // [B][R]
   int* pos;     // [B][R]
   float* hstate;   // [B][H]
+  int K;              // position-aware draft offsets (0 = none)
+  const float* doff;  // [K][H] b_t at row t-1
+  float* dX;          // [B][W][H] draft inputs h_s + b_t (K > 0)
   float* X;        // [B][R][H]
   float* Hout;     // [B][R][H]
   float* dlogits;  // [B][W][V]

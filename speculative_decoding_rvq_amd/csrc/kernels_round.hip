@@ -778,19 +778,35 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
   __syncthreads();
   st = st_s;
 
-  // ---- h_{s+n} = output row n-1 (prefill: row 1) ----
+  // ---- h_{s+n} = output row n-1 (prefill: row 1), and with position-aware
+  // offsets the next round's draft inputs h_{s+n} + b_t, t = 1..W (b_t = 0
+  // past K) ----
   {
     const int hrow = sh_hrow;
     float4* dst = reinterpret_cast<float4*>(r.hstate + static_cast<size_t>(b) * r.H);
+    float4* dx = r.K > 0 ? reinterpret_cast<float4*>(r.dX + static_cast<size_t>(b) * r.W * r.H) : nullptr;
+    const float4* off = reinterpret_cast<const float4*>(r.doff);
+    auto put = [&](int k4, float4 v) {
+      dst[k4] = v;
+      if (dx != nullptr)
+        for (int t = 0; t < r.W; ++t) {
+          float4 o = v;
+          if (t < r.K) {
+            const float4 bt = off[t * H4 + k4];
+            o.x += bt.x, o.y += bt.y, o.z += bt.z, o.w += bt.w;
+          }
+          dx[t * H4 + k4] = o;
+        }
+    };
     if (held) {
 #pragma unroll
       for (int i = 0; i < kHrowF4; ++i) {
         const int q = tid + i * kBlock;
-        if (q < nf4 && q / H4 == hrow) dst[q % H4] = hv[i];
+        if (q < nf4 && q / H4 == hrow) put(q % H4, hv[i]);
       }
     } else {
       const float4* src = reinterpret_cast<const float4*>(r.Hout + (rb + hrow) * r.H);
-      for (int i = tid; i < H4; i += kBlock) dst[i] = src[i];
+      for (int i = tid; i < H4; i += kBlock) put(i, src[i]);
     }
   }
   if (tid < kCntW)

@@ -190,12 +190,21 @@ def make_weights(c: dict) -> dict:
                 lw[name] = _draw(rng, shape, s, dt)
         layers.append(lw)
     w["layers"] = layers
-    K = int(c.get("draft_offsets", 0))
-    if K > 0:
-        ro = np.random.Generator(np.random.PCG64(c["offset_seed"]))
-        w["draft_offsets"] = (ro.standard_normal((K, H), dtype=np.float32) *
-                              np.float32(c.get("offset_scale", 0.1)))
+    off = make_offsets(c)
+    if off is not None:
+        w["draft_offsets"] = off
     return w
+
+
+def make_offsets(c: dict):
+    """The K position-aware draft offsets of ``c`` ([K][H] f32), or None:
+    N(0, offset_scale^2) from a generator of their own."""
+    K = int(c.get("draft_offsets", 0))
+    if K <= 0:
+        return None
+    ro = np.random.Generator(np.random.PCG64(c["offset_seed"]))
+    return (ro.standard_normal((K, c["hidden"]), dtype=np.float32) *
+            np.float32(c.get("offset_scale", 0.1)))
 
 
 def splitmix64(x: np.ndarray) -> np.ndarray:

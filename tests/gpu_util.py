@@ -80,10 +80,25 @@ def compare_frames(gc, gf, oc, of):
     return res
 
 
-def oracle_frames(cid, dp, hf, c0, seeds, pairs):
+def offsets_setup(cid: str, K: int, scale: float, **cfg):
+    """Workload ``cid`` with K seeded position-aware draft offsets: (config,
+    library handle, oracle model); the other weights are the cached ones."""
+    import copy
+    import torch
+    from speculative_decoding_rvq_amd import binding
+    c = synth.config(cid, draft_offsets=K, offset_scale=scale, **cfg)
+    off = synth.make_offsets(c)
+    wdev = {**device_weights(cid), "draft_offsets": torch.from_numpy(off).cuda()}
+    h = binding.Handle(c, wdev)
+    m = copy.copy(oracle_model(cid))
+    m.draft_offsets = off.astype(np.float64)
+    return c, h, m
+
+
+def oracle_frames(cid, dp, hf, c0, seeds, pairs, model=None):
     """Oracle codes/flags for the selected (frame, stream) pairs."""
     from oracle import spec
-    m = oracle_model(cid)
+    m = oracle_model(cid) if model is None else model
     st = spec.new_stats()
     codes, flags = [], []
     for f, b in pairs:

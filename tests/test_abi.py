@@ -57,6 +57,8 @@ def _create(cfg):
     ("max_streams", 0, binding.EINVAL, "non-positive"),
     ("head_dim", 256, binding.EUNSUPPORTED, "head_dim"),
     ("head_dim", 48, binding.EUNSUPPORTED, "head_dim"),
+    ("draft_offsets", 9, binding.EINVAL, "draft_offsets"),
+    ("draft_offsets", -1, binding.EINVAL, "draft_offsets"),
 ])
 def test_create_validation(field, value, code, msg):
     cfg = binding.make_cfg(synth.config("tiny"))
@@ -96,3 +98,29 @@ def test_null_handle_calls_are_rejected():
     assert Lb.cp_spec_topk_sample(None, None, 1, None, None, None, None,
                                   None) == binding.EINVAL
     Lb.cp_spec_destroy(None)
+
+
+def test_draft_offsets_workspace_and_pointer_checks():
+    c = synth.config("qwen3tts")
+    base = binding.workspace_bytes(binding.make_cfg(c))
+    cfg = binding.make_cfg(c)
+    cfg.draft_offsets = 3
+    n = binding.workspace_bytes(cfg)
+    # one [B][N-1][H] float32 buffer of draft input rows
+    W = c["verify_size"] - 1
+    assert n - base == (W * c["hidden"] * 4 + 255) // 256 * 256
+    # speculation off: no drafts, no buffer
+    cfg0 = binding.make_cfg(c)
+    cfg0.verify_size = 0
+    cfg0.draft_offsets = 3
+    cfg1 = binding.make_cfg(c)
+    cfg1.verify_size = 0
+    assert binding.workspace_bytes(cfg0) == binding.workspace_bytes(cfg1)
+    layer = C.cast((C.c_void_p * (9 * c["layers"]))(*([1] * 9 * c["layers"])),
+                   C.POINTER(C.c_void_p))
+    h = C.c_void_p()
+    for ptr in (None, 0x1004):  # missing, misaligned
+        w = binding.Weights(1, 1, 1, layer, ptr)
+        rc = binding.lib().cp_spec_create(C.byref(w), C.byref(cfg),
+                                          C.c_void_p(0x1000), n, C.byref(h))
+        assert rc == binding.EINVAL and "draft_offsets" in binding.last_error()

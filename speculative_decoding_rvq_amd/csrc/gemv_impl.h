@@ -133,6 +133,20 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   const int g = owner ? tid / NV : 0, idx = owner ? tid % NV : 0;
   float ri = 1.0f;  // 1/rms of the owner's row, known after the first reduction
 
+  // epilogue operands that do not depend on the dot products (the residual
+  // value of a residual add, the row's position of a K/V append), loaded
+  // with the unit's weights rather than after the reduction
+  float yold = 0.0f, yold_n = 0.0f;
+  int ppos = -1, ppos_n = -1;
+  auto epi_load = [&](int ub, float& y, int& pp) {
+    const int rp = idx / MT, m = idx % MT, u = ub + g;
+    if (!owner || u >= a.units || m >= Mloc) return;
+    const int row = m0 + m;
+    if (MODE == kAdd) y = a.Y[static_cast<size_t>(row) * a.ldy + u * RPG + rp];
+    if (MODE == kQKV) pp = a.pos[row];
+  };
+  epi_load(ubase, yold, ppos);
+
   // ---- units ----
   for (bool first = true; ubase < a.units; ubase += stride, first = false) {
     float v[NV];
@@ -159,6 +173,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
         for (int j = 0; j < SPT; ++j) wv[rp][j] = *reinterpret_cast<const VT*>(wr + (kt + KT * j) * VEC);
       }
+      epi_load(nb, yold_n, ppos_n);
     }
     // fold 16 lanes per DPP row (dot products and, the first time, the sums
     // of squares), then the DPP rows of the row group in LDS: one barrier
@@ -218,14 +233,14 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         const int o = u * RPG + rp;
         const int row = m0 + m;
         if (MODE == kAdd) {
-          a.Y[static_cast<size_t>(row) * a.ldy + o] += val;
+          a.Y[static_cast<size_t>(row) * a.ldy + o] = yold + val;
         } else if (MODE == kHead || MODE == kStore) {
           a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
         } else if (MODE == kQKV) {
           if (o < a.qdim) {
             a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
           } else {
-            const int pp = a.pos[row];
+            const int pp = ppos;
             if (pp >= 0 && pp < a.kv_positions) {
               const int b = row / a.rows_per_stream;
               float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
@@ -237,6 +252,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         }
       }
     }
+    yold = yold_n, ppos = ppos_n;
     if (nb < a.units) __syncthreads();  // part[] is rewritten by the next unit
   }
 }

@@ -111,6 +111,32 @@ def test_qwen3tts_full_sampled():
     _check("qwen3tts", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
+@pytest.mark.parametrize("N", [2, 6, 8])
+def test_qwen3tts_window_sweep_sampled(N):
+    """Stochastic windows other than the default on the bf16 1-stream path
+    (the windows the per-device sweep compares)."""
+    c = synth.config("qwen3tts", verify_size=N, frames=40)
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle("qwen3tts", verify_size=N)
+    log(f"decode qwen3tts N={N} F=40")
+    gc, gf, gst = decode_gpu(h, hf, c0, seeds)
+    assert gst["frames"] == 40
+    pairs = [(f, 0) for f in (0, 21, 39)]
+    _check("qwen3tts", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+
+
+@pytest.mark.parametrize("N", [2, 8])
+def test_qwen3tts_64_streams_window_sampled(N):
+    c = synth.config("qwen3tts-64", verify_size=N, frames=6)
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle("qwen3tts-64", verify_size=N)
+    log(f"decode qwen3tts-64 N={N} B=64 F=6")
+    gc, gf, gst = decode_gpu(h, hf, c0, seeds)
+    assert gst["frames"] == 6 * 64
+    pairs = [(0, 0), (3, 33), (5, 63)]
+    _check("qwen3tts-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+
+
 def test_wide_256_streams_sampled():
     c = synth.config("wide-256", frames=2)
     hf, c0, seeds = synth.make_inputs(c)

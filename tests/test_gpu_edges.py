@@ -1,0 +1,109 @@
+"""GPU parity at the edges of the method: the fewest code groups (G = 3: every
+round is a single target draw; G = 2: the autoregressive fallback), the full
+vocabulary as top-k set, top-k 1 (the deterministic chain), very low and very
+high temperature, and one handle decoding different stream counts in turn
+(GEMV and matrix-core paths, a new graph per count).  Same frame rule as the
+other decode tests: equal codes, or a near-tie flag at or before the first
+differing depth.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import compare_frames, decode_gpu, dparams, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+_SHAPE = dict(layers=1, hidden=256, q_heads=4, kv_heads=2, head_dim=64,
+              ffn=512, vocab=256, weight_scale=0.05)
+
+
+def _setup(max_streams=None, **kw):
+    from oracle import decoder
+    from speculative_decoding_rvq_amd import binding
+    c = synth.custom(**{**_SHAPE, **kw})
+    w = synth.make_weights(c)
+    h = binding.Handle(c, binding.weights_to_device(w), max_streams=max_streams)
+    return c, h, decoder.Model(c, w)
+
+
+def _oracle(m, dp, hf, c0, seeds, pairs):
+    from oracle import spec
+    st = spec.new_stats()
+    out = [spec.decode_frame(m, dp, hf[f, b], int(c0[f, b]), int(seeds[f, b]), st)
+           for f, b in pairs]
+    return (np.array([o[0] for o in out]), np.array([o[1] for o in out], np.uint32), st)
+
+
+def _check(name, c, m, got, hf, c0, seeds, pairs, dp=None):
+    gc, gf, gst = got
+    oc, of, ost = _oracle(m, dp or dparams(c), hf, c0, seeds, pairs)
+    res = compare_frames(np.array([gc[f, b] for f, b in pairs]),
+                         np.array([gf[f, b] for f, b in pairs]), oc, of)
+    log(f"{name}: {res['frames']} frames, {res['exact']} exact, "
+        f"{res['flagged_mismatch']} flagged, {len(res['unflagged'])} unflagged")
+    assert not res["unflagged"], res["unflagged"][:3]
+    return res, ost
+
+
+def test_three_groups_single_draw_rounds():
+    c, h, m = _setup(groups=3, verify_size=4, top_k=50, frames=30)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode G=3 F=30")
+    got = decode_gpu(h, hf, c0, seeds)
+    res, ost = _check("G3", c, m, got, hf, c0, seeds, [(f, 0) for f in range(30)])
+    st = got[2]
+    assert st["frames"] == 30 and st["codes"] == 60
+    assert st["rounds"] == 30 and sum(st["proposed"]) == 0  # gamma is 0 at s = 1
+
+
+def test_two_groups_autoregressive_fallback():
+    c, h, m = _setup(groups=2, verify_size=4, top_k=50, frames=20)
+    assert h.status == 1  # CP_SPEC_WARN_AR_FALLBACK: created, runs the AR loop
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode G=2 (fallback) F=20")
+    got = decode_gpu(h, hf, c0, seeds)
+    _check("G2", c, m, got, hf, c0, seeds, [(f, 0) for f in range(20)])
+    assert got[2]["rounds"] == 0 and got[2]["prefill_passes"] == 20
+
+
+def test_full_vocabulary_top_k():
+    c, h, m = _setup(groups=8, verify_size=4, top_k=256, temperature=0.9, frames=40)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode top-k = V F=40")
+    got = decode_gpu(h, hf, c0, seeds)
+    _check("topk=V", c, m, got, hf, c0, seeds, [(f, 0) for f in range(40)])
+
+
+def test_top1_sampling_equals_greedy_on_gpu():
+    c, h, m = _setup(groups=8, verify_size=4, top_k=1, frames=30)
+    cg, hg, _ = _setup(groups=8, verify_size=4, greedy=True, top_k=1, frames=30)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode top-k 1 vs greedy F=30")
+    a = decode_gpu(h, hf, c0, seeds)
+    b = decode_gpu(hg, hf, c0, seeds)
+    assert not compare_frames(a[0], a[1], b[0], b[1])["unflagged"]
+    _check("topk=1", c, m, a, hf, c0, seeds, [(f, 0) for f in range(0, 30, 3)])
+
+
+@pytest.mark.parametrize("T", [0.05, 5.0])
+def test_temperature_extremes(T):
+    c, h, m = _setup(groups=8, verify_size=4, top_k=50, temperature=T, frames=30)
+    hf, c0, seeds = synth.make_inputs(c)
+    log(f"decode T={T} F=30")
+    got = decode_gpu(h, hf, c0, seeds)
+    _check(f"T={T}", c, m, got, hf, c0, seeds, [(f, 0) for f in range(30)])
+
+
+def test_one_handle_different_stream_counts():
+    """B = 3 (GEMV path), 8 (matrix-core path) and 1 on one handle."""
+    c, h, m = _setup(max_streams=8, groups=8, verify_size=4, top_k=50, frames=3, streams=8)
+    hf, c0, seeds = synth.make_inputs(c)
+    for B in (3, 8, 1):
+        log(f"decode B={B} of max 8, F=3")
+        got = decode_gpu(h, hf[:, :B], c0[:, :B], seeds[:, :B])
+        assert got[2]["frames"] == 3 * B
+        pairs = [(f, b) for f in range(3) for b in range(B)]
+        _check(f"B={B}", c, m, got, hf[:, :B], c0[:, :B], seeds[:, :B], pairs)

@@ -103,7 +103,16 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   }
 
   // ---- activation slices (x * g) in registers, partial sums of squares ----
+  // (the gain is read once per chunk, not once per row: every vector memory
+  // instruction counts at one stream, more than the bytes it moves)
   const bool norm = a.norm_g != nullptr;
+  float4 gv[SPT][VEC / 4];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      gv[j][e / 4] = norm ? *reinterpret_cast<const float4*>(a.norm_g + (kt + KT * j) * VEC + e)
+                          : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
   float xr[MT][SPT][VEC];
   float ss[MT];
 #pragma unroll
@@ -117,8 +126,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (m < Mloc)
           v = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>((m0 + m) / a.xdiv) * a.ldx + k0 + e);
-        float4 g = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        if (norm) g = *reinterpret_cast<const float4*>(a.norm_g + k0 + e);
+        const float4 g = gv[j][e / 4];
         ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         xr[m][j][e] = v.x * g.x;
         xr[m][j][e + 1] = v.y * g.y;

@@ -573,7 +573,23 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     const int base = threadIdx.x * VPT;
     float zv[VPT];
     load_row<VPT>(r.tlogits + row * r.V, zv);  // before the row's head: the row always exists
-    if (r.thead[row] <= 0) return;
+    // every other load that depends only on the block goes out with it (one
+    // memory round trip, not three): the row's head, the stream's state, and
+    // the draft row this row may test (offset rr + 1 exists for rr < W)
+    const int head = r.thead[row];
+    const StreamState st = r.st[b];
+    const bool has_q = !r.greedy && rr < r.W;
+    float qv[VPT];
+    int dd = -1;
+    if (has_q) {
+      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + rr) * r.V;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
+      dd = r.dcode[static_cast<size_t>(b) * r.W + rr];
+    }
+    // (a finished stream's heads are zero already; testing its mode here keeps
+    // the state load ahead of this branch)
+    if (head <= 0 || st.mode == kModeDone) return;
     if (r.greedy) {
       const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
       if (threadIdx.x == 0) {
@@ -582,7 +598,6 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       }
       return;
     }
-    const StreamState st = r.st[b];
     const bool spec = st.mode == kModeSpec;
     const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
     const int depth = spec ? st.s + 1 + rr : 1;
@@ -591,12 +606,8 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     int d = -1;
     if (test) {
       // the draft distribution of offset rr + 1, for the test and the residual
-      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + rr) * r.V;
-      float qv[VPT];
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
       store_row<VPT>(qv, L.q);
-      d = r.dcode[static_cast<size_t>(b) * r.W + rr];
+      d = dd;
     }
     int total;
     uint32_t flags = 0;

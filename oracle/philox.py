@@ -7,9 +7,11 @@ advanced by the Weyl constants between rounds.  The pages only say "a Philox
 seed per frame"; the counter layout below is this library's choice.
 
 Uniform of a frame decision:
-    U(seed, depth, purpose) = (word0 >> 8) * 2**-24, a float32 in [0, 1),
-    word0 = Philox4x32-10(counter=(depth, purpose, 0, 0),
+    U(seed, depth, purpose, i) = (word0 >> 8) * 2**-24, a float32 in [0, 1),
+    word0 = Philox4x32-10(counter=(depth, purpose, i, 0),
                           key=(seed & 0xffffffff, seed >> 32))[0]
+    i = 0 for the chain window; a tree window numbers the draws and trials
+    that share a depth and purpose.
     purpose 0 = draft sample, 1 = acceptance test, 2 = target sample
     (residual, bonus, prefill and every autoregressive draw).
 
@@ -49,13 +51,14 @@ def philox4x32_10(counter, key):
     return x0, x1, x2, x3
 
 
-def word(seed: int, depth: int, purpose: int) -> int:
+def word(seed: int, depth: int, purpose: int, index: int = 0) -> int:
     """First output word of Philox4x32-10 for one decision of a frame."""
     seed = int(seed)
-    return philox4x32_10((depth, purpose, 0, 0),
+    return philox4x32_10((depth, purpose, index, 0),
                          (seed & MASK32, (seed >> 32) & MASK32))[0]
 
 
-def uniform(seed: int, depth: int, purpose: int) -> np.float32:
-    """U(seed, depth, purpose) as a float32 in [0, 1) with 24 random bits."""
-    return np.float32((word(seed, depth, purpose) >> 8) * (1.0 / (1 << 24)))
+def uniform(seed: int, depth: int, purpose: int, index: int = 0) -> np.float32:
+    """U(seed, depth, purpose, index) as a float32 in [0, 1) with 24 random
+    bits."""
+    return np.float32((word(seed, depth, purpose, index) >> 8) * (1.0 / (1 << 24)))

@@ -148,6 +148,34 @@ def test_wide_256_streams_sampled():
     _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
+def test_wide_256_streams_full_sampled():
+    """The wide workload at full size: 256 streams x 200 frames (8 layers,
+    H 2048, V 4096, correlated heads, top-k 100), sampled frames."""
+    c = synth.config("wide-256")
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle("wide-256")
+    log("decode wide-256 B=256 F=200 (full)")
+    gc, gf, gst = decode_gpu(h, hf, c0, seeds)
+    assert gst["frames"] == 256 * 200 and gst["codes"] == 256 * 200 * 15
+    pairs = [(0, 7), (117, 200), (199, 255)]
+    _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+
+
+def test_tiny_greedy_full_sampled():
+    """The greedy workload at full size (1000 frames, N = 4): sampled frames
+    against the oracle, every frame against the GPU's autoregressive loop."""
+    c = synth.config("tiny-greedy")
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle("tiny-greedy")
+    log("decode tiny-greedy B=1 F=1000 (full)")
+    gc, gf, gst = decode_gpu(h, hf, c0, seeds)
+    assert gst["frames"] == 1000
+    pairs = [(f, 0) for f in range(0, 1000, 50)]
+    _check("tiny-greedy", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
+    ac, af, _ = decode_gpu(handle("tiny-greedy", verify_size=0), hf, c0, seeds)
+    assert not compare_frames(gc, gf, ac, af)["unflagged"]
+
+
 def test_qwen3tts_64_streams_full_sampled():
     """The qwen3tts shape at 64 streams in the benchmark's configuration
     (all 100 frames of every stream, matrix-core projections and heads)."""

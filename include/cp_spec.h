@@ -88,6 +88,18 @@ typedef struct cp_spec_cfg {
                         /* draft offset t <= K scores with head_{s+t} the    */
                         /* state h_s + b_t, t > K the state h_s; only the    */
                         /* draft distributions q change. 0 = no offsets.     */
+  /* Tree-shaped verify window ("RVQ Position Aware ...", section 2.2 and
+   * Figure 2).  tree_nodes = T in 1..7 replaces the chain window (verify_size
+   * is then ignored; the verify block has T + 1 rows); 0 = the chain.
+   * tree_parent[i - 1] is the parent of node i (0 = the root, the committed
+   * code; a parent precedes its children).  A node at depth d draws the code
+   * of depth s + d from that depth's draft distribution; the round walks
+   * down from the root testing a node's children in order with min(1, p'/q)
+   * and replacing p' by norm(max(0, p' - q)) after each rejection, and draws
+   * from p' when no child is accepted.  Stochastic decoding only, at most 7
+   * streams, code_groups + T <= 32 (CP_SPEC_EUNSUPPORTED otherwise). */
+  int32_t tree_nodes;
+  int32_t tree_parent[8];
 } cp_spec_cfg;
 
 typedef struct cp_spec_weights {

@@ -260,8 +260,8 @@ __device__ __forceinline__ int head_rows_slice(const int* head, int n, int h, in
 // ------------------------------------------------------------- Philox ----
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11, section 4): ten rounds of
 // the 4-word multiply/xor S-box with a Weyl-advanced 2-word key.
-__device__ __forceinline__ uint32_t philox_word0(uint64_t seed, uint32_t c0, uint32_t c1) {
-  uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+__device__ __forceinline__ uint32_t philox_word0(uint64_t seed, uint32_t c0, uint32_t c1, uint32_t c2 = 0u) {
+  uint32_t x0 = c0, x1 = c1, x2 = c2, x3 = 0u;
   uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
@@ -282,9 +282,11 @@ __device__ __forceinline__ uint32_t philox_word0(uint64_t seed, uint32_t c0, uin
 enum Purpose : uint32_t { kDraft = 0, kAccept = 1, kTarget = 2 };
 
 // Uniform of one frame decision: 24 random bits of word 0 of
-// Philox4x32-10(counter = (depth, purpose, 0, 0), key = seed), in [0, 1).
-__device__ __forceinline__ float frame_uniform(uint64_t seed, int depth, uint32_t purpose) {
-  return static_cast<float>(philox_word0(seed, static_cast<uint32_t>(depth), purpose) >> 8) *
+// Philox4x32-10(counter = (depth, purpose, index, 0), key = seed), in [0, 1).
+// index 0 for the chain window; a tree window numbers the draws of a depth
+// and the children tested at a node.
+__device__ __forceinline__ float frame_uniform(uint64_t seed, int depth, uint32_t purpose, uint32_t index = 0u) {
+  return static_cast<float>(philox_word0(seed, static_cast<uint32_t>(depth), purpose, index) >> 8) *
          (1.0f / 16777216.0f);
 }
 
@@ -329,11 +331,16 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
          lane_u(static_cast<uint32_t>(v), l);
 }
 
-template <typename IT>
-__device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, float u, int* code, int* near) {
+// The first half of list_draw: the positivity masks of w[0..total) and lane
+// 0's running sums in place.  Several list_search calls with different u can
+// then share one prefix.
+struct ListSums {
+  uint64_t mine;  // positivity mask of block `lane`
+  int npos, last;
+};
+
+__device__ __forceinline__ ListSums list_prefix(float* w, int total) {
   const int lane = threadIdx.x % kWave;
-  *code = -1;
-  *near = 0;
   uint64_t mine = 0;  // positivity mask of block `lane`
   int npos = 0, last = -1;
   for (int c0 = 0, c = 0; c0 < total; c0 += kWave, ++c) {
@@ -343,7 +350,7 @@ __device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, fl
     npos += __popcll(m);
     if (m) last = c0 + 63 - __clzll(static_cast<long long>(m));
   }
-  if (npos == 0) return;
+  if (npos == 0) return ListSums{mine, 0, last};
   if (lane == 0) {
     float carry = 0.0f;
     for (int c0 = 0; c0 < total; c0 += 32) {
@@ -367,6 +374,19 @@ __device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, fl
     }
   }
   wave_lds_sync();
+  return ListSums{mine, npos, last};
+}
+
+// The second half: the entry whose running sum first exceeds u * sum.
+template <typename IT>
+__device__ __forceinline__ void list_search(const float* w, const IT* idx, int total, const ListSums& ls, float u,
+                                            int* code, int* near) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t mine = ls.mine;
+  const int npos = ls.npos, last = ls.last;
+  *code = -1;
+  *near = 0;
+  if (npos == 0) return;
   const float tot = w[total - 1];
   const float t = u * tot;
   const double eps = static_cast<double>(tot) * kEpsCdf;
@@ -392,6 +412,12 @@ __device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, fl
   const float before_last = last > 0 ? w[last - 1] : 0.0f;
   *code = static_cast<int>(idx[last]);
   *near = (npos > 1 && fabs(static_cast<double>(t) - static_cast<double>(before_last)) < eps) ? 1 : 0;
+}
+
+template <typename IT>
+__device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, float u, int* code, int* near) {
+  const ListSums ls = list_prefix(w, total);
+  list_search(w, idx, total, ls, u, code, near);
 }
 
 // Wave 0: Sample over the `total` compacted entries of sm (ascending code
@@ -439,6 +465,38 @@ __device__ __forceinline__ int sample_regs(const float (&wv)[VPT], float u, Samp
   *flag = sm.result[1] != 0;
   return sm.result[0];
 }
+
+// The sequential float32 sum, in ascending code order, of the positive
+// entries of a row held in registers (thread t owning [t*VPT, (t+1)*VPT)).
+// Every thread gets it.  sm is free again once this returns.
+template <int VPT>
+__device__ __forceinline__ float positive_sum_regs(const float (&wv)[VPT], SampleSmem& sm) {
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) cnt += wv[j] > 0.0f ? 1 : 0;
+  const int inc = wave_incl_scan(cnt);
+  if (lane == kWave - 1) sm.red[w] = inc;
+  lds_sync();
+  int off = inc - cnt;
+  for (int i = 0; i < w; ++i) off += sm.red[i];
+  const int total = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    if (wv[j] > 0.0f) sm.w[off++] = wv[j];
+  }
+  lds_sync();
+  if (tid == 0) {
+    float tot = 0.0f;
+    for (int i = 0; i < total; ++i) tot = tot + sm.w[i];
+    sm.result[0] = __float_as_int(tot);
+  }
+  lds_sync();
+  const float tot = __int_as_float(sm.result[0]);
+  lds_sync();  // sm.result and sm.red are reused by the caller's next call
+  return tot;
+}
+
 
 // The same over weights produced by `weight(i)`, i in [0, V), V = 256 * 2^i
 // up to 4096.

@@ -38,10 +38,15 @@ struct Shape {
   int R, W, qdim, kvdim;
   int vec;  // weight elements per 16-byte chunk
   int K;    // position-aware draft offsets (0 = none)
+  // tree window (T = 0: the chain): nodes, depth, parent and depth of node
+  // i (node 0 = the root), K/V positions per stream (the frame's G plus one
+  // slot per node)
+  int tn, td, Gk;
+  int par[8], dep[8];
 };
 
 struct Layout {
-  size_t st, call, sstats, dhead, thead, pos, hstate, dX, X, Hout, Q, attn, act, kv, dlogits, q, dcode, dflags,
+  size_t st, call, sstats, dhead, thead, pos, hstate, dX, X, Hout, ncode, Q, attn, act, kv, dlogits, q, dcode, dflags,
       tlogits, p, tcode, tflags, rope, packed, planes, ssp, total;
 };
 
@@ -78,6 +83,17 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   }
   if (c->draft_offsets < 0 || c->draft_offsets > CP_SPEC_MAX_OFFSETS)
     return fail(CP_SPEC_EINVAL, "draft_offsets must be in 0..8");
+  if (c->tree_nodes < 0 || c->tree_nodes > CP_SPEC_MAX_WINDOW - 1)
+    return fail(CP_SPEC_EINVAL, "tree_nodes must be in 0..7");
+  for (int i = 1; i <= c->tree_nodes; ++i)
+    if (c->tree_parent[i - 1] < 0 || c->tree_parent[i - 1] >= i)
+      return fail(CP_SPEC_EINVAL, "tree_parent[i-1] must be in 0..i-1");
+  if (c->tree_nodes > 0) {
+    if (c->greedy) return fail(CP_SPEC_EUNSUPPORTED, "tree windows decode stochastically only");
+    if (c->max_streams > 7) return fail(CP_SPEC_EUNSUPPORTED, "tree windows run on at most 7 streams");
+    if (c->code_groups + c->tree_nodes > 32)
+      return fail(CP_SPEC_EUNSUPPORTED, "code_groups + tree_nodes must be at most 32");
+  }
   if (c->vocab > CP_SPEC_MAX_VOCAB)
     return fail(CP_SPEC_EUNSUPPORTED, "vocab above the small-vocabulary bound (4096)");
   const int vpt = c->vocab / 256;
@@ -99,8 +115,23 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
     *warn_ar = true;  // no depth to draft: the autoregressive loop
     s_.N = 0;
   }
-  s_.R = std::max(s_.N, 2);
-  s_.W = std::max(s_.N - 1, 1);
+  if (c->tree_nodes > 0 && s_.G < 3) *warn_ar = true;  // nothing to draft: the autoregressive loop
+  s_.tn = s_.td = 0;
+  s_.par[0] = -1;
+  s_.dep[0] = 0;
+  if (c->tree_nodes > 0 && !*warn_ar) {
+    s_.tn = c->tree_nodes;
+    for (int i = 1; i <= s_.tn; ++i) {
+      s_.par[i] = c->tree_parent[i - 1];
+      s_.dep[i] = s_.dep[s_.par[i]] + 1;
+      s_.td = std::max(s_.td, s_.dep[i]);
+    }
+    s_.N = s_.td + 1;  // codes a round commits at most
+  }
+  for (int i = s_.tn + 1; i < 8; ++i) s_.par[i] = -1, s_.dep[i] = 0;
+  s_.Gk = s_.G + s_.tn;
+  s_.R = s_.tn > 0 ? s_.tn + 1 : std::max(s_.N, 2);
+  s_.W = s_.tn > 0 ? s_.td : std::max(s_.N - 1, 1);
   s_.K = s_.N >= 2 ? c->draft_offsets : 0;  // no drafts, no offsets
   for (int K : {s_.H, s_.qdim, s_.F})
     if (!choose_kt(K, s_.vec))
@@ -110,7 +141,8 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   for (int N_ : {s_.qdim + 2 * s_.kvdim, s_.H, s_.V, s_.kvdim, s_.qdim})
     if (N_ % kRPGHost) return fail(CP_SPEC_EUNSUPPORTED, "output width must be a multiple of 4");
   if (s_.F % 2) return fail(CP_SPEC_EUNSUPPORTED, "ffn must be even");
-  if (attention_smem_bytes(s_.G, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024)
+  if (attention_smem_bytes(s_.G, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024 ||
+      tree_attention_smem_bytes(s_.Gk, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024)
     return fail(CP_SPEC_EUNSUPPORTED, "attention tile (positions x head_dim x query group) exceeds LDS");
   return CP_SPEC_OK;
 }
@@ -162,7 +194,8 @@ Layout make_layout(const Shape& s) {
   l.Q = take(B * R * s.qdim * f4);
   l.attn = take(B * R * s.qdim * f4);
   l.act = take(B * R * s.F * f4);
-  l.kv = take(B * static_cast<size_t>(s.L) * 2 * s.G * s.kvdim * f4);
+  l.kv = take(B * static_cast<size_t>(s.L) * 2 * s.Gk * s.kvdim * f4);
+  l.ncode = take(B * 8 * i4);  // tree window: the code of every node
   l.dlogits = take(B * W * s.V * f4);
   l.q = take(B * W * s.V * f4);
   l.dcode = take(B * W * i4);
@@ -204,12 +237,17 @@ struct cp_spec {
   bool use_graph = true;
 
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
-  long long kv_sb() const { return static_cast<long long>(sh.L) * 2 * sh.G * sh.kvdim; }
+  long long kv_sb() const { return static_cast<long long>(sh.L) * 2 * sh.Gk * sh.kvdim; }
 
   RoundArgs round_args(int B) const {
     RoundArgs r{};
     r.B = B; r.R = sh.R; r.W = sh.W; r.G = sh.G; r.V = sh.V; r.H = sh.H; r.N = sh.N;
     r.greedy = sh.greedy; r.top_k = sh.top_k; r.L = sh.L; r.T = sh.T;
+    r.tnodes = sh.tn; r.tdepth = sh.td; r.Gk = sh.Gk; r.kvdim = sh.kvdim;
+    for (int i = 0; i < 8; ++i) r.par[i] = sh.par[i], r.dep[i] = sh.dep[i];
+    r.kv = at<float>(lo.kv);
+    r.kv_sb = kv_sb();
+    r.ncode = at<int>(lo.ncode);
     r.wbf16 = sh.wdt == CP_SPEC_BF16;
     r.embed = embed;
     r.st = at<StreamState>(lo.st);
@@ -364,8 +402,8 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
   const auto& w = h->layers[l];
   const uint16_t* const* pk = h->packed.empty() ? nullptr : h->packed[l].data();
   auto pw = [&](int i) { return pk ? pk[i] : nullptr; };
-  float* kvl = kv + l * 2LL * sh.G * sh.kvdim;
-  const long long kv_vo = static_cast<long long>(sh.G) * sh.kvdim;
+  float* kvl = kv + l * 2LL * sh.Gk * sh.kvdim;
+  const long long kv_vo = static_cast<long long>(sh.Gk) * sh.kvdim;
   GemvArgs a{};
   a.xdiv = 1;
   a.M = M;
@@ -382,7 +420,7 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       a.X = X; a.ldx = sh.H; a.norm_g = static_cast<const float*>(w[0]);
       a.Y = Q; a.ldy = sh.qdim;
       a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
-      a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.G;
+      a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.Gk;
       if (fused) a.planes = P0, a.ptiles = T, a.ssp = S;
       return gemv(h, s, kQKV, a, pw(0));
     case CP_SPEC_KERNEL_ATTENTION: {
@@ -391,6 +429,15 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       at.rope = h->at<float2>(h->lo.rope); at.R = R; at.nq = sh.nq; at.nkv = sh.nkv; at.d = sh.d;
       at.G = sh.G; at.scale = 1.0f / std::sqrt(static_cast<float>(sh.d));
       if (fused) at.planes = P1, at.ptiles = T;
+      if (sh.tn > 0) {  // tree window: node slots and ancestor masks
+        at.Gk = sh.Gk;
+        for (int i = 0; i < 8; ++i) {
+          at.dep[i] = sh.dep[i];
+          at.anc[i] = (i >= 1 && i <= sh.tn) ? (1u << i) | at.anc[sh.par[i]] : 0u;
+        }
+        CPS_HIP(launch_tree_attention(at, B, s));
+        return CP_SPEC_OK;
+      }
       CPS_HIP(launch_attention(at, B, s));
       return CP_SPEC_OK;
     }
@@ -481,12 +528,12 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
     if ((rc = head_logits(h, s, B * sh.W, dx, r.K > 0 ? 1 : sh.W, r.dhead, nullptr, nullptr, r.dlogits,
                           per_head)))
       return rc;
-    CPS_HIP(launch_draft_topk(r, s));
+    CPS_HIP(sh.tn > 0 ? launch_tree_draft(r, s) : launch_draft_topk(r, s));
   }
   if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv)))) return rc;
   if ((rc = head_logits(h, s, B * sh.R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head))) return rc;
   CPS_HIP(launch_target_topk(r, s));
-  CPS_HIP(launch_round_accept(r, s));
+  CPS_HIP(sh.tn > 0 ? launch_tree_accept(r, s) : launch_round_accept(r, s));
   return CP_SPEC_OK;
 }
 
@@ -581,6 +628,8 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
   if (e == hipSuccess)
     e = hipMemcpy(h->at<char>(lo.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = attention_allow_smem(s.d, attention_smem_bytes(s.G, s.d, s.R, s.nq / s.nkv));
+  if (e == hipSuccess && s.tn > 0)
+    e = tree_attention_allow_smem(s.d, tree_attention_smem_bytes(s.Gk, s.d, s.R, s.nq / s.nkv));
   if (e == hipSuccess && packs_weights(s)) {
     // fragment-packed copies of every bf16 matrix (read once, here)
     uint16_t* p = h->at<uint16_t>(lo.packed);

@@ -83,6 +83,11 @@ struct AttnArgs {
   const float2* rope; // [G][d/2] (cos, sin)
   int R, nq, nkv, d, G;
   float scale;
+  // tree window: K/V positions per stream (G + nodes), node depths, and per
+  // row the nodes it attends to (bit i = node i, itself included)
+  int Gk;
+  int dep[8];
+  uint32_t anc[8];
 };
 
 struct TopkArgs {
@@ -150,6 +155,13 @@ struct RoundArgs {
   int K;              // position-aware draft offsets (0 = none)
   const float* doff;  // [K][H] b_t at row t-1
   float* dX;          // [B][W][H] draft inputs h_s + b_t (K > 0)
+  // tree window (T > 0): nodes, depth, node parents and depths, the K/V
+  // cache of the round's streams, every node's code
+  int tnodes, tdepth, Gk, kvdim;
+  int par[8], dep[8];
+  float* kv;          // [B][L][2][Gk][kvdim]
+  long long kv_sb;
+  int* ncode;         // [B][8]
   float* X;        // [B][R][H]
   float* Hout;     // [B][R][H]
   float* dlogits;  // [B][W][V]
@@ -200,6 +212,12 @@ hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t 
 hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s);
+// Tree window: node draws, ancestor-masked attention, the walk and commit.
+hipError_t launch_tree_draft(const RoundArgs& r, hipStream_t s);
+size_t tree_attention_smem_bytes(int Gk, int d, int R, int group);
+hipError_t tree_attention_allow_smem(int d, size_t bytes);
+hipError_t launch_tree_attention(const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_tree_accept(const RoundArgs& r, hipStream_t s);
 // Adds the B per-stream counters to *out (one block; fixed order).
 hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats* out, hipStream_t s);
 // out[i][:] = sum over g < G of E_g[codes[i * G + g]] (float32, group

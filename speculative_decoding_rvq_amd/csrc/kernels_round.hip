@@ -598,6 +598,16 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       }
       return;
     }
+    if (r.tnodes > 0) {
+      // tree window: the row's p (dense, for the walk) and its top-k flag
+      const RowLds L = row_lds(row_dyn, r.V, true);
+      store_row<VPT>(zv, L.z);
+      int total;
+      uint32_t flags = 0;
+      if (topk_list<VPT>(zv, r.top_k, r.T, L, S, r.p + row * r.V, &total, &flags) && threadIdx.x == 0)
+        r.tflags[row] = flags;
+      return;
+    }
     const bool spec = st.mode == kModeSpec;
     const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
     const int depth = spec ? st.s + 1 + rr : 1;
@@ -920,6 +930,493 @@ __global__ __launch_bounds__(kBlock) void stats_flush_kernel(const cp_spec_stats
 
 hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats* out, hipStream_t s) {
   hipLaunchKernelGGL(stats_flush_kernel, dim3(1), dim3(kBlock), 0, s, sstats, B, out);
+  return hipGetLastError();
+}
+
+
+// ===========================================================================
+// Tree-shaped verify window ("RVQ Position Aware Speculative Decoding ...",
+// section 2.2 and Figure 2).  Node 0 is the root (row 0, the committed code
+// c_s); node i = row i sits at depth dep[i], proposes the code of depth
+// s + dep[i] and keeps its K/V in slot G + i - 1 of the stream's cache (the
+// frame's G positions come first) until the round commits it.  Every node draws its code from its depth's draft
+// distribution; the walk tests a node's children in order with min(1, p'/q)
+// and replaces p' by norm(max(0, p' - q)) after each rejection.
+// ===========================================================================
+
+// Draft side: block (d-1, b) forms q_d (dense, for the walk) and draws the
+// code of every node of depth d from it (draw index j = the node's number
+// among the nodes of depth d, node order), then gathers each node's verify
+// input E_{s+d}[code]; the block of depth 1 also gathers row 0 = E_s[c_s].
+// Per-depth flags (top-k boundary, any draw's CDF near tie) go to dflags.
+__global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
+  extern __shared__ float4 row_dyn[];
+  __shared__ SelSmem S;
+  const int d = blockIdx.x + 1, b = blockIdx.y;
+  const size_t row = static_cast<size_t>(b) * r.W + (d - 1);
+  dispatch_vpt(r.V, [&](auto vpt) {
+    constexpr int VPT = decltype(vpt)::value;
+    float zv[VPT];
+    load_row<VPT>(r.dlogits + row * r.V, zv);  // before the state: the row always exists
+    const StreamState st = r.st[b];
+    if (st.mode != kModeSpec) return;
+    float* x0 = r.X + static_cast<size_t>(b) * r.R * r.H;
+    if (d > st.gamma) {  // no node this round at this depth: only row 0 to fill
+      if (d == 1) embed_row(r, st.s, st.last, x0);
+      return;
+    }
+    const RowLds L = row_lds(row_dyn, r.V, false);
+    store_row<VPT>(zv, L.z);
+    int total;
+    uint32_t flags = 0;
+    if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, r.q + row * r.V, &total, &flags)) {
+      if (d == 1) embed_row_span(r, st.s, st.last, x0, threadIdx.x - kWave, kBlock - kWave);
+      return;
+    }
+    // wave 0: every draw of the depth from one set of running sums
+    const ListSums ls = list_prefix(L.lw, total);
+    const uint64_t seed = frame_seed(st);
+    for (int i = 1, j = 0; i <= r.tnodes; ++i) {
+      if (r.dep[i] != d) continue;
+      int code, near;
+      list_search(L.lw, L.lidx, total, ls, frame_uniform(seed, st.s + d, kDraft, j), &code, &near);
+      ++j;
+      if (near) flags |= kFlagCdf;
+      if (threadIdx.x == 0) r.ncode[static_cast<size_t>(b) * 8 + i] = code;
+      embed_row_span(r, st.s + d, code, r.X + (static_cast<size_t>(b) * r.R + i) * r.H, threadIdx.x, kWave);
+    }
+    if (threadIdx.x == 0) r.dflags[row] = flags;
+  });
+}
+
+hipError_t launch_tree_draft(const RoundArgs& r, hipStream_t s) {
+  hipLaunchKernelGGL(tree_draft_kernel, dim3(r.W, r.B), dim3(kBlock), row_lds_bytes(r.V, false), s, r);
+  return hipGetLastError();
+}
+
+// Attention of the tree window over one stream and one KV head.  Keys: the
+// cache positions 0..P-1 (P = 1 + the largest row position below G: the
+// committed prefix and the root) and the node slots G + i - 1 of the active
+// node rows.  A row at a position below G (the root, or a prefill row) is causal
+// over the prefix; node row i sits at logical position pos[0] + dep[i] and
+// sees the whole prefix plus the nodes in anc[i] (itself and its ancestors).
+// K is rotated by its logical position, Q by its row's.  Phases as in
+// attention_kernel.
+template <int D>
+__global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a) {
+  extern __shared__ float smem[];
+  constexpr int half = D / 2;
+  constexpr int H4 = half / 4;
+  constexpr int KS = D + 4;
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int R = a.R;
+  const int kvdim = a.nkv * D;
+  const int qdim = a.nq * D;
+  const int group = a.nq / a.nkv;
+  const int npair = R * group;
+  __shared__ int pos_s[CP_SPEC_MAX_WINDOW], qp_s[CP_SPEC_MAX_WINDOW];
+  __shared__ int kslot_s[64], klp_s[64], knode_s[64];
+  __shared__ int np_s, P_s;
+  if (threadIdx.x < R) pos_s[threadIdx.x] = a.pos[b * R + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int P = 0;
+    for (int r = 0; r < R; ++r)
+      if (pos_s[r] >= 0 && pos_s[r] < a.G) P = max(P, pos_s[r] + 1);
+    const int p0 = pos_s[0];
+    int n = 0;
+    for (int k = 0; k < P; ++k) kslot_s[n] = k, klp_s[n] = k, knode_s[n] = 0, ++n;
+    for (int r = 1; r < R; ++r)
+      if (pos_s[r] >= a.G && pos_s[r] < a.Gk) kslot_s[n] = pos_s[r], klp_s[n] = p0 + a.dep[r], knode_s[n] = r, ++n;
+    for (int r = 0; r < R; ++r)
+      qp_s[r] = pos_s[r] < 0 ? -1 : (pos_s[r] < a.G ? pos_s[r] : (pos_s[r] < a.Gk ? p0 + a.dep[r] : -1));
+    np_s = n;
+    P_s = P;
+  }
+  __syncthreads();
+  const int np = np_s, P = P_s;
+  if (P == 0 || np > 32) return;  // no active row (np <= G + nodes <= 32 by construction)
+  float* Ks = smem;                  // [np][KS]
+  float* Vs = Ks + a.Gk * KS;        // [np][D]
+  float* Qs = Vs + a.Gk * D;         // [npair][D]
+  float* S = Qs + npair * D;         // [npair][32]
+  const float* kb = a.kv + static_cast<size_t>(b) * a.kv_sb + g * D;
+  const float* vb = kb + a.kv_vo;
+
+  // ---- phase 1: K (rotated), V, Q (rotated) into LDS ----
+  const int nk = np * H4, nq = npair * H4;
+  for (int it = threadIdx.x; it < nk + nq; it += kBlock) {
+    if (it < nk) {
+      const int p = it / H4, i4 = (it % H4) * 4;
+      const int sl = kslot_s[p], lp = klp_s[p];
+      const float4 k1 = *reinterpret_cast<const float4*>(kb + sl * kvdim + i4);
+      const float4 k2 = *reinterpret_cast<const float4*>(kb + sl * kvdim + i4 + half);
+      const float4 v1 = *reinterpret_cast<const float4*>(vb + sl * kvdim + i4);
+      const float4 v2 = *reinterpret_cast<const float4*>(vb + sl * kvdim + i4 + half);
+      const float4 c01 = *reinterpret_cast<const float4*>(a.rope + lp * half + i4);
+      const float4 c23 = *reinterpret_cast<const float4*>(a.rope + lp * half + i4 + 2);
+      float* kr = Ks + p * KS;
+      kr[i4 + 0] = k1.x * c01.x - k2.x * c01.y;  kr[i4 + half + 0] = k2.x * c01.x + k1.x * c01.y;
+      kr[i4 + 1] = k1.y * c01.z - k2.y * c01.w;  kr[i4 + half + 1] = k2.y * c01.z + k1.y * c01.w;
+      kr[i4 + 2] = k1.z * c23.x - k2.z * c23.y;  kr[i4 + half + 2] = k2.z * c23.x + k1.z * c23.y;
+      kr[i4 + 3] = k1.w * c23.z - k2.w * c23.w;  kr[i4 + half + 3] = k2.w * c23.z + k1.w * c23.w;
+      *reinterpret_cast<float4*>(Vs + p * D + i4) = v1;
+      *reinterpret_cast<float4*>(Vs + p * D + i4 + half) = v2;
+    } else {
+      const int jt = it - nk;
+      const int pr = jt / H4, i4 = (jt % H4) * 4;
+      const int r = pr / group, j = pr % group;
+      const float* qrow = a.Q + static_cast<size_t>(b * R + r) * qdim + (g * group + j) * D;
+      const int pq = max(qp_s[r], 0);
+      const float4 q1 = *reinterpret_cast<const float4*>(qrow + i4);
+      const float4 q2 = *reinterpret_cast<const float4*>(qrow + i4 + half);
+      const float4 c01 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4);
+      const float4 c23 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4 + 2);
+      float* qr = Qs + pr * D;
+      qr[i4 + 0] = q1.x * c01.x - q2.x * c01.y;  qr[i4 + half + 0] = q2.x * c01.x + q1.x * c01.y;
+      qr[i4 + 1] = q1.y * c01.z - q2.y * c01.w;  qr[i4 + half + 1] = q2.y * c01.z + q1.y * c01.w;
+      qr[i4 + 2] = q1.z * c23.x - q2.z * c23.y;  qr[i4 + half + 2] = q2.z * c23.x + q1.z * c23.y;
+      qr[i4 + 3] = q1.w * c23.z - q2.w * c23.w;  qr[i4 + half + 3] = q2.w * c23.z + q1.w * c23.w;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: scores and softmax, 32 lanes per pair (lane = key) ----
+  for (int base = 0; base < npair * 32; base += kBlock) {
+    const int idx = base + threadIdx.x;
+    const int pr = idx >> 5, p = idx & 31;
+    const bool live_pair = pr < npair;
+    const int r = live_pair ? pr / group : 0;
+    const int qp = live_pair ? qp_s[r] : -1;
+    bool ok = live_pair && qp >= 0 && p < np;
+    if (ok) ok = p < P ? kslot_s[p] <= qp : ((a.anc[r] >> knode_s[p]) & 1u) != 0u;
+    float s = -INFINITY;
+    if (ok) {
+      const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
+      const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) {
+        const float4 x = q4[i], y = k4[i];
+        acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+      }
+      s = acc * a.scale;
+    }
+    float mx = s;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+    const float e = ok ? expf(s - mx) : 0.0f;
+    float sum = e;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
+    if (live_pair) S[pr * 32 + p] = ok ? e / sum : 0.0f;
+  }
+  __syncthreads();
+
+  // ---- phase 3: eight output dimensions of one pair per thread ----
+  constexpr int D8 = D / 8;
+  for (int idx = threadIdx.x; idx < npair * D8; idx += kBlock) {
+    const int pr = idx / D8, i8 = (idx % D8) * 8;
+    const int r = pr / group, j = pr % group;
+    if (qp_s[r] < 0) continue;
+    const float* srow = S + pr * 32;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+    for (int p = 0; p < np; ++p) {
+      const float w = srow[p];
+      const float4 v0 = *reinterpret_cast<const float4*>(Vs + p * D + i8);
+      const float4 v1 = *reinterpret_cast<const float4*>(Vs + p * D + i8 + 4);
+      o[0] += w * v0.x; o[1] += w * v0.y; o[2] += w * v0.z; o[3] += w * v0.w;
+      o[4] += w * v1.x; o[5] += w * v1.y; o[6] += w * v1.z; o[7] += w * v1.w;
+    }
+    const int row = b * R + r, k = (g * group + j) * D + i8;
+    if (a.planes != nullptr) {
+      split_store8(a.planes, a.ptiles, row, k, o);
+    } else {
+      float* dst = a.out + static_cast<size_t>(row) * qdim + k;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+size_t tree_attention_smem_bytes(int Gk, int d, int R, int group) {
+  const size_t npair = static_cast<size_t>(R) * group;
+  return (static_cast<size_t>(Gk) * (2 * d + 4) + npair * d + npair * 32) * sizeof(float);
+}
+
+hipError_t tree_attention_allow_smem(int d, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  switch (d) {
+#define CPS_TATT_ATTR(D_) \
+  case D_:                \
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(tree_attention_kernel<D_>), \
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+    CPS_TATT_ATTR(8) CPS_TATT_ATTR(16) CPS_TATT_ATTR(32) CPS_TATT_ATTR(64) CPS_TATT_ATTR(128)
+#undef CPS_TATT_ATTR
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tree_attention(const AttnArgs& a, int B, hipStream_t s) {
+  const size_t shm = tree_attention_smem_bytes(a.Gk, a.d, a.R, a.nq / a.nkv);
+  switch (a.d) {
+#define CPS_TATT(D_)                                                                              \
+  case D_:                                                                                        \
+    hipLaunchKernelGGL(tree_attention_kernel<D_>, dim3(B, a.nkv), dim3(kBlock), shm, s, a);       \
+    break;
+    CPS_TATT(8) CPS_TATT(16) CPS_TATT(32) CPS_TATT(64) CPS_TATT(128)
+#undef CPS_TATT
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Accept side of the tree window, one block per stream.  Every thread
+// follows the same walk (thread 0 takes each test): at node v (depth d) with
+// p' = the row's p, the active children in node order are tested with
+// U(s+d+1, accept, k) < p'(x)/q_{d+1}(x); after a rejection p' becomes
+// max(0, p' - q_{d+1}) (kept when all zero), normalised by its sequential
+// float32 sum when another child follows; with no child accepted the round
+// draws from p' with U(s+d+1, target).  Then the path is committed, its
+// nodes' K/V move from their slots (G + i - 1) to their positions, h_{s+n} =
+// the last node's output row, and the stream's next round (or frame) is set
+// up.
+__global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) {
+  __shared__ StreamState st_s;
+  __shared__ CallDesc c_s;
+  __shared__ cp_spec_stats cnt_s;
+  __shared__ SampleSmem sm;
+  __shared__ float px_s;
+  __shared__ int ok_s;
+  __shared__ uint32_t fl_s;
+  constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
+  constexpr int kCntW = sizeof(cp_spec_stats) / 8;
+  static_assert(kStW <= 32 && kCallW <= 32 && kCntW <= 32, "state words");
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const size_t rb = static_cast<size_t>(b) * r.R;
+  if (tid < kStW) {
+    reinterpret_cast<int*>(&st_s)[tid] = reinterpret_cast<const int*>(r.st + b)[tid];
+  } else if (tid >= 32 && tid < 32 + kCallW) {
+    reinterpret_cast<int*>(&c_s)[tid - 32] = reinterpret_cast<const int*>(r.call)[tid - 32];
+  } else if (tid >= 64 && tid < 64 + kCntW) {
+    reinterpret_cast<long long*>(&cnt_s)[tid - 64] = reinterpret_cast<const long long*>(r.sstats + b)[tid - 64];
+  }
+  if (tid == 0) fl_s = 0u;
+  __syncthreads();
+  StreamState st = st_s;
+  if (st.mode == kModeDone) return;
+  const CallDesc& c = c_s;
+  const size_t fb = static_cast<size_t>(st.f) * c.B + b;
+  int* out = c.out_codes + fb * r.G;
+  const uint64_t seed = frame_seed(st);
+  const bool spec = st.mode == kModeSpec;
+  const int s = st.s, gamma = st.gamma;
+  int v = 0, n = 0;  // the walk's node and codes committed (the same in every thread)
+  dispatch_vpt(r.V, [&](auto vpt) {
+    constexpr int VPT = decltype(vpt)::value;
+    const int base = tid * VPT;
+    float pv[VPT];
+    if (!spec) {  // prefill: c_1 ~ p of row 1
+      const float* prow = r.p + (rb + 1) * r.V;
+#pragma unroll
+      for (int jj = 0; jj < VPT; ++jj) pv[jj] = prow[base + jj];
+      bool nf = false;
+      const int code = sample_regs<VPT>(pv, frame_uniform(seed, 1, kTarget), sm, &nf);
+      if (tid == 0) {
+        const uint32_t f = (r.tflags[rb + 1] & kFlagTopk) | (nf ? kFlagCdf : 0u);
+        count_flags(f, &cnt_s);
+        if (f) st_s.flags |= 1u << 1;
+        out[1] = st_s.last = code;
+        ++cnt_s.prefill_passes;
+        st_s.s = 1;
+      }
+      v = 1;
+      n = 1;
+      return;
+    }
+    if (tid == 0) {  // the drafts' flags and every active row's top-k flag
+      uint32_t fl = 0u;
+      for (int d = 1; d <= gamma; ++d) {
+        const uint32_t f = r.dflags[static_cast<size_t>(b) * r.W + d - 1];
+        count_flags(f, &cnt_s);
+        if (f) fl |= 1u << (s + d);
+      }
+      for (int i = 0; i <= r.tnodes; ++i) {
+        if (i > 0 && r.dep[i] > gamma) continue;
+        const uint32_t f = r.tflags[rb + i] & kFlagTopk;
+        count_flags(f, &cnt_s);
+        if (f) fl |= 1u << (s + r.dep[i] + 1);
+      }
+      fl_s = fl;
+    }
+    for (;;) {
+      const int d1 = r.dep[v] + 1, j = s + d1;
+      const float* prow = r.p + (rb + v) * r.V;
+#pragma unroll
+      for (int jj = 0; jj < VPT; ++jj) pv[jj] = prow[base + jj];
+      int kids[CP_SPEC_MAX_WINDOW], nk = 0;
+      for (int ch = 1; ch <= r.tnodes; ++ch)
+        if (r.par[ch] == v && r.dep[ch] <= gamma) kids[nk++] = ch;
+      int acc = -1;
+      for (int k = 0; k < nk; ++k) {
+        // q_{d1} exists: d1 <= gamma <= W
+        const float* qrow = r.q + (static_cast<size_t>(b) * r.W + (d1 - 1)) * r.V;
+        const int x = r.ncode[static_cast<size_t>(b) * 8 + kids[k]];
+#pragma unroll
+        for (int jj = 0; jj < VPT; ++jj)
+          if (base + jj == x) px_s = pv[jj];
+        __syncthreads();
+        if (tid == 0) {
+          const float qx = (x >= 0 && x < r.V) ? qrow[x] : 1.0f;
+          const float ratio = px_s / qx;
+          const float ua = frame_uniform(seed, j, kAccept, k);
+          if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) {
+            ++cnt_s.near_tie_accept;
+            fl_s |= 1u << j;
+          }
+          ok_s = ua < ratio ? 1 : 0;
+        }
+        __syncthreads();
+        if (ok_s) {
+          acc = kids[k];
+          break;
+        }
+        // rejected: p' <- max(0, p' - q), kept when nothing is left
+        float rv[VPT];
+        bool any = false;
+#pragma unroll
+        for (int jj = 0; jj < VPT; ++jj) {
+          rv[jj] = fmaxf(pv[jj] - qrow[base + jj], 0.0f);
+          any |= rv[jj] > 0.0f;
+        }
+        if (__syncthreads_or(any)) {
+#pragma unroll
+          for (int jj = 0; jj < VPT; ++jj) pv[jj] = rv[jj];
+        }
+        if (k + 1 < nk) {  // another child is tested on it: normalise
+          const float tot = positive_sum_regs<VPT>(pv, sm);
+#pragma unroll
+          for (int jj = 0; jj < VPT; ++jj) pv[jj] = pv[jj] / tot;
+        }
+      }
+      if (acc < 0) {
+        bool nf = false;
+        const int code = sample_regs<VPT>(pv, frame_uniform(seed, j, kTarget), sm, &nf);
+        if (tid == 0) {
+          if (nf) {
+            ++cnt_s.near_tie_cdf;
+            fl_s |= 1u << j;
+          }
+          out[s + n + 1] = st_s.last = code;
+        }
+        ++n;
+        break;
+      }
+      if (tid == 0) out[s + n + 1] = r.ncode[static_cast<size_t>(b) * 8 + acc];
+      ++n;
+      v = acc;
+    }
+  });
+  __syncthreads();
+
+  if (spec) {
+    if (tid == 0) {
+      ++cnt_s.rounds;
+      for (int d = 1; d <= gamma; ++d) {
+        ++cnt_s.proposed[d - 1];
+        if (d <= n - 1) ++cnt_s.accepted[d - 1];
+      }
+      bool leaf = true;
+      for (int ch = 1; ch <= r.tnodes; ++ch)
+        if (r.par[ch] == v && r.dep[ch] <= gamma) leaf = false;
+      if (leaf) ++cnt_s.bonus;
+      st_s.flags |= fl_s;
+      st_s.s = s + n;
+    }
+    // the accepted nodes' K/V: slot G + a - 1 -> position s + 1 + dep[a],
+    // every layer, K and V
+    float* kvb = r.kv + static_cast<size_t>(b) * r.kv_sb;
+    for (int a = v; a > 0; a = r.par[a]) {
+      const size_t src = static_cast<size_t>(r.G + a - 1) * r.kvdim;
+      const size_t dst = static_cast<size_t>(s + 1 + r.dep[a]) * r.kvdim;
+      for (int l2 = 0; l2 < 2 * r.L; ++l2) {
+        float* lay = kvb + static_cast<size_t>(l2) * r.Gk * r.kvdim;
+        for (int i = tid; i < r.kvdim; i += kBlock) lay[dst + i] = lay[src + i];
+      }
+    }
+  }
+  if (tid == 0 && st_s.s >= r.G - 1) {  // frame complete
+    if (c.out_flags) c.out_flags[fb] = st_s.flags;
+    ++cnt_s.frames;
+    cnt_s.codes += r.G - 1;
+  }
+  __syncthreads();
+  st = st_s;
+
+  // ---- h_{s+n} = the last path node's output row (prefill: row 1), and
+  // with position-aware offsets the next round's draft inputs ----
+  {
+    const int H4 = r.H / 4;
+    const float4* src = reinterpret_cast<const float4*>(r.Hout + (rb + v) * r.H);
+    float4* dst = reinterpret_cast<float4*>(r.hstate + static_cast<size_t>(b) * r.H);
+    float4* dx = r.K > 0 ? reinterpret_cast<float4*>(r.dX + static_cast<size_t>(b) * r.W * r.H) : nullptr;
+    const float4* off = reinterpret_cast<const float4*>(r.doff);
+    for (int i = tid; i < H4; i += kBlock) {
+      const float4 hv = src[i];
+      dst[i] = hv;
+      if (dx != nullptr)
+        for (int t = 0; t < r.W; ++t) {
+          float4 o = hv;
+          if (t < r.K) {
+            const float4 bt = off[t * H4 + i];
+            o.x += bt.x, o.y += bt.y, o.z += bt.z, o.w += bt.w;
+          }
+          dx[t * H4 + i] = o;
+        }
+    }
+  }
+  if (tid < kCntW)
+    reinterpret_cast<long long*>(r.sstats + b)[tid] = reinterpret_cast<const long long*>(&cnt_s)[tid];
+
+  // ---- next round of this stream ----
+  if (st.s >= r.G - 1) {
+    st.f += 1;
+    st.s = 0;
+    st.flags = 0;
+    st.gamma = 0;
+    if (st.f >= c.F) {
+      st.mode = kModeDone;
+      if (tid < r.R) {
+        r.pos[rb + tid] = -1;
+        r.thead[rb + tid] = 0;
+      }
+      if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = 0;
+    } else {
+      st.mode = kModePrefill;
+      set_frame_seed(st, c.seeds[static_cast<size_t>(st.f) * c.B + b]);
+      setup_prefill(r, c, b, st.f);
+    }
+  } else {
+    const int s2 = st.s;
+    const int g2 = min(r.tdepth, r.G - 2 - s2);
+    st.gamma = g2;
+    st.mode = kModeSpec;
+    if (tid < r.R) {
+      const bool act = tid == 0 || r.dep[tid] <= g2;
+      r.pos[rb + tid] = tid == 0 ? s2 + 1 : (act ? r.G + tid - 1 : -1);  // node i: slot G + i - 1
+      r.thead[rb + tid] = act ? s2 + 1 + r.dep[tid] : 0;
+    }
+    if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = tid + 1 <= g2 ? s2 + tid + 1 : 0;
+  }
+  if (tid == 0) r.st[b] = st;
+}
+
+hipError_t launch_tree_accept(const RoundArgs& r, hipStream_t s) {
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(r.B), dim3(kBlock), 0, s, r);
   return hipGetLastError();
 }
 

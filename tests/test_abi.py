@@ -124,3 +124,31 @@ def test_draft_offsets_workspace_and_pointer_checks():
         rc = binding.lib().cp_spec_create(C.byref(w), C.byref(cfg),
                                           C.c_void_p(0x1000), n, C.byref(h))
         assert rc == binding.EINVAL and "draft_offsets" in binding.last_error()
+
+
+def _tree_cfg(parents, **over):
+    c = synth.config("tiny", **over)
+    cfg = binding.make_cfg(dict(c, tree=parents))
+    return cfg
+
+
+@pytest.mark.parametrize("parents,over,code,msg", [
+    ([0] * 8, {}, binding.EINVAL, "tree_nodes"),
+    ([0, 2], {}, binding.EINVAL, "tree_parent"),
+    ([1], {}, binding.EINVAL, "tree_parent"),
+    ([0, 0], {"greedy": True}, binding.EUNSUPPORTED, "stochastically"),
+    ([0, 0], {"streams": 8}, binding.EUNSUPPORTED, "at most 7 streams"),
+    ([0, 0, 0, 1, 2], {"groups": 30}, binding.EUNSUPPORTED, "code_groups + tree_nodes"),
+])
+def test_tree_validation(parents, over, code, msg):
+    cfg = _tree_cfg(parents, **over)
+    rc, err = _create(cfg)
+    assert rc == code and msg in err, (rc, err)
+    assert binding.lib().cp_spec_workspace_bytes(C.byref(cfg)) == 0
+
+
+def test_tree_workspace_holds_node_slots():
+    c = synth.config("tiny")
+    n0 = binding.workspace_bytes(binding.make_cfg(c))
+    n1 = binding.workspace_bytes(binding.make_cfg(dict(c, tree=[0, 0, 1, 2])))
+    assert n1 > n0  # four more K/V slots per stream, five verify rows

@@ -1,0 +1,102 @@
+"""GPU parity of the tree-shaped verify window ("RVQ Position Aware
+Speculative Decoding ...", section 2.2 and Figure 2) against oracle.tree.
+Frame rule as in the other decode tests: equal codes, or a near-tie flag at
+or before the first differing depth.  A one-child tree runs the tree kernels
+over the chain's computation and must equal the GPU chain window exactly.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import compare_frames, decode_gpu, device_weights, handle, log, oracle_model
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _tree_handle(cid, parents, max_streams=None, wdev=None, **cfg):
+    from speculative_decoding_rvq_amd import binding
+    c = synth.config(cid, tree=list(parents), **cfg)
+    return c, binding.Handle(c, wdev or device_weights(cid), max_streams=max_streams)
+
+
+def _oracle(m, c, parents, hf, c0, seeds, pairs):
+    from oracle import spec, tree
+    dp = dict(greedy=c["greedy"], temperature=c["temperature"], top_k=c["top_k"])
+    t = tree.Tree(parents)
+    st = spec.new_stats()
+    out = [tree.decode_frame_tree(m, dp, t, hf[f, b], int(c0[f, b]), int(seeds[f, b]), st)
+           for f, b in pairs]
+    return np.array([o[0] for o in out]), np.array([o[1] for o in out], np.uint32), st
+
+
+def _check(name, c, m, parents, got, hf, c0, seeds, pairs):
+    gc, gf, gst = got
+    oc, of, ost = _oracle(m, c, parents, hf, c0, seeds, pairs)
+    res = compare_frames(np.array([gc[f, b] for f, b in pairs]),
+                         np.array([gf[f, b] for f, b in pairs]), oc, of)
+    log(f"{name} tree {parents}: {res['frames']} frames, {res['exact']} exact, "
+        f"{res['flagged_mismatch']} flagged, {len(res['unflagged'])} unflagged")
+    assert not res["unflagged"], res["unflagged"][:3]
+    if res["exact"] == res["frames"] == gst["frames"]:  # every frame compared
+        for k in ("frames", "codes", "prefill_passes", "rounds", "bonus"):
+            assert gst[k] == ost[k], k
+        assert gst["proposed"] == ost["proposed"] and gst["accepted"] == ost["accepted"]
+    return res
+
+
+@pytest.mark.parametrize("parents", [[0, 0, 1], [0, 0, 0, 1, 2], [0, 1, 1, 2, 3, 0, 6]])
+def test_tree_tiny_all_frames(parents):
+    c, h = _tree_handle("tiny", parents, frames=60)
+    hf, c0, seeds = synth.make_inputs(c)
+    log(f"decode tiny tree {parents} F=60")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 60
+    _check("tiny", c, oracle_model("tiny"), parents, got, hf, c0, seeds, [(f, 0) for f in range(60)])
+
+
+def test_one_child_tree_equals_gpu_chain():
+    c, h = _tree_handle("tiny", [0, 1, 2], frames=60)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode tiny one-child tree vs chain N=4 F=60")
+    a = decode_gpu(h, hf, c0, seeds)
+    b = decode_gpu(handle("tiny", verify_size=4), hf, c0, seeds)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    for k in ("frames", "codes", "rounds", "bonus", "proposed", "accepted"):
+        assert a[2][k] == b[2][k], k
+
+
+def test_tree_with_offsets():
+    from gpu_util import offsets_setup
+    c, _, m = offsets_setup("tiny", 2, 0.5, frames=40)
+    off = synth.make_offsets(c)
+    wdev = {**device_weights("tiny"), "draft_offsets": torch.from_numpy(off).cuda()}
+    parents = [0, 0, 1]
+    ct, h = _tree_handle("tiny", parents, wdev=wdev, frames=40, draft_offsets=2, offset_scale=0.5)
+    hf, c0, seeds = synth.make_inputs(ct)
+    log("decode tiny tree + offsets F=40")
+    got = decode_gpu(h, hf, c0, seeds)
+    _check("tiny+offsets", ct, m, parents, got, hf, c0, seeds, [(f, 0) for f in range(40)])
+
+
+def test_tree_four_streams():
+    parents = [0, 0, 1, 2]
+    c, h = _tree_handle("tiny", parents, max_streams=4, frames=6, streams=4)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode tiny tree B=4 F=6")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 24
+    pairs = [(f, b) for f in range(6) for b in range(4)]
+    _check("tiny B=4", c, oracle_model("tiny"), parents, got, hf, c0, seeds, pairs)
+
+
+def test_tree_qwen3tts_sampled():
+    parents = [0, 0, 1, 2]
+    c, h = _tree_handle("qwen3tts", parents, frames=40)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode qwen3tts tree F=40")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 40
+    _check("qwen3tts", c, oracle_model("qwen3tts"), parents, got, hf, c0, seeds, [(0, 0), (39, 0)])

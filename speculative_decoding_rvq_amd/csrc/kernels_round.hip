@@ -952,6 +952,7 @@ hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats*
 __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
   extern __shared__ float4 row_dyn[];
   __shared__ SelSmem S;
+  __shared__ int tcode_s[CP_SPEC_MAX_WINDOW], tnode_s[CP_SPEC_MAX_WINDOW], nd_s;
   const int d = blockIdx.x + 1, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.W + (d - 1);
   dispatch_vpt(r.V, [&](auto vpt) {
@@ -969,23 +970,38 @@ __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
     store_row<VPT>(zv, L.z);
     int total;
     uint32_t flags = 0;
-    if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, r.q + row * r.V, &total, &flags)) {
-      if (d == 1) embed_row_span(r, st.s, st.last, x0, threadIdx.x - kWave, kBlock - kWave);
-      return;
+    int nd = 0;  // nodes of depth d
+    if (topk_list<VPT>(zv, r.top_k, r.T, L, S, r.q + row * r.V, &total, &flags)) {
+      // wave 0: every draw of the depth from one set of running sums
+      const ListSums ls = list_prefix(L.lw, total);
+      const uint64_t seed = frame_seed(st);
+      for (int i = 1; i <= r.tnodes; ++i) {
+        if (r.dep[i] != d) continue;
+        int code, near;
+        list_search(L.lw, L.lidx, total, ls, frame_uniform(seed, st.s + d, kDraft, nd), &code, &near);
+        if (near) flags |= kFlagCdf;
+        if (threadIdx.x == 0) {
+          tcode_s[nd] = code;
+          tnode_s[nd] = i;
+          r.ncode[static_cast<size_t>(b) * 8 + i] = code;
+        }
+        ++nd;
+      }
+      if (threadIdx.x == 0) {
+        r.dflags[row] = flags;
+        nd_s = nd;
+      }
+    } else if (d == 1) {  // meanwhile the other waves gather row 0
+      embed_row_span(r, st.s, st.last, x0, threadIdx.x - kWave, kBlock - kWave);
     }
-    // wave 0: every draw of the depth from one set of running sums
-    const ListSums ls = list_prefix(L.lw, total);
-    const uint64_t seed = frame_seed(st);
-    for (int i = 1, j = 0; i <= r.tnodes; ++i) {
-      if (r.dep[i] != d) continue;
-      int code, near;
-      list_search(L.lw, L.lidx, total, ls, frame_uniform(seed, st.s + d, kDraft, j), &code, &near);
-      ++j;
-      if (near) flags |= kFlagCdf;
-      if (threadIdx.x == 0) r.ncode[static_cast<size_t>(b) * 8 + i] = code;
-      embed_row_span(r, st.s + d, code, r.X + (static_cast<size_t>(b) * r.R + i) * r.H, threadIdx.x, kWave);
-    }
-    if (threadIdx.x == 0) r.dflags[row] = flags;
+    __syncthreads();
+    // every node's verify input, the nodes side by side (a group of threads each)
+    nd = nd_s;
+    const int per = kBlock / nd;
+    const int k = threadIdx.x / per;
+    if (k < nd)
+      embed_row_span(r, st.s + d, tcode_s[k], r.X + (static_cast<size_t>(b) * r.R + tnode_s[k]) * r.H,
+                     threadIdx.x - k * per, per);
   });
 }
 
@@ -1014,27 +1030,37 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   const int qdim = a.nq * D;
   const int group = a.nq / a.nkv;
   const int npair = R * group;
-  __shared__ int pos_s[CP_SPEC_MAX_WINDOW], qp_s[CP_SPEC_MAX_WINDOW];
+  __shared__ int pos_s[CP_SPEC_MAX_WINDOW], qp_s[CP_SPEC_MAX_WINDOW], dep_s[CP_SPEC_MAX_WINDOW];
+  __shared__ uint32_t anc_s[CP_SPEC_MAX_WINDOW];
   __shared__ int kslot_s[64], klp_s[64], knode_s[64];
-  __shared__ int np_s, P_s;
+  // the rows' positions, depths and masks in LDS (indexing the argument
+  // block per lane would turn into memory loads)
   if (threadIdx.x < R) pos_s[threadIdx.x] = a.pos[b * R + threadIdx.x];
+  if (threadIdx.x >= 64 && threadIdx.x < 64 + CP_SPEC_MAX_WINDOW)
+    dep_s[threadIdx.x - 64] = a.dep[threadIdx.x - 64], anc_s[threadIdx.x - 64] = a.anc[threadIdx.x - 64];
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int P = 0;
-    for (int r = 0; r < R; ++r)
-      if (pos_s[r] >= 0 && pos_s[r] < a.G) P = max(P, pos_s[r] + 1);
-    const int p0 = pos_s[0];
-    int n = 0;
-    for (int k = 0; k < P; ++k) kslot_s[n] = k, klp_s[n] = k, knode_s[n] = 0, ++n;
-    for (int r = 1; r < R; ++r)
-      if (pos_s[r] >= a.G && pos_s[r] < a.Gk) kslot_s[n] = pos_s[r], klp_s[n] = p0 + a.dep[r], knode_s[n] = r, ++n;
-    for (int r = 0; r < R; ++r)
-      qp_s[r] = pos_s[r] < 0 ? -1 : (pos_s[r] < a.G ? pos_s[r] : (pos_s[r] < a.Gk ? p0 + a.dep[r] : -1));
-    np_s = n;
-    P_s = P;
+  // the key list, every entry by its own thread: prefix slots 0..P-1, then
+  // the active node rows in row order
+  int P = 0, nnode = 0;
+  for (int r = 0; r < R; ++r) {
+    const int pr = pos_s[r];
+    if (pr >= 0 && pr < a.G) P = max(P, pr + 1);
+    if (r > 0 && pr >= a.G && pr < a.Gk) ++nnode;
+  }
+  const int p0 = pos_s[0];
+  const int np = P + nnode;
+  if (threadIdx.x < P) {
+    kslot_s[threadIdx.x] = threadIdx.x, klp_s[threadIdx.x] = threadIdx.x, knode_s[threadIdx.x] = 0;
+  } else if (threadIdx.x >= 64 && threadIdx.x < 64 + R) {
+    const int r = threadIdx.x - 64, pr = pos_s[r];
+    qp_s[r] = pr < 0 ? -1 : (pr < a.G ? pr : (pr < a.Gk ? p0 + dep_s[r] : -1));
+    if (r > 0 && pr >= a.G && pr < a.Gk) {
+      int before = 0;
+      for (int i = 1; i < r; ++i) before += (pos_s[i] >= a.G && pos_s[i] < a.Gk) ? 1 : 0;
+      kslot_s[P + before] = pr, klp_s[P + before] = p0 + dep_s[r], knode_s[P + before] = r;
+    }
   }
   __syncthreads();
-  const int np = np_s, P = P_s;
   if (P == 0 || np > 32) return;  // no active row (np <= G + nodes <= 32 by construction)
   float* Ks = smem;                  // [np][KS]
   float* Vs = Ks + a.Gk * KS;        // [np][D]
@@ -1089,7 +1115,7 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
     const int r = live_pair ? pr / group : 0;
     const int qp = live_pair ? qp_s[r] : -1;
     bool ok = live_pair && qp >= 0 && p < np;
-    if (ok) ok = p < P ? kslot_s[p] <= qp : ((a.anc[r] >> knode_s[p]) & 1u) != 0u;
+    if (ok) ok = p < P ? kslot_s[p] <= qp : ((anc_s[r] >> knode_s[p]) & 1u) != 0u;
     float s = -INFINITY;
     if (ok) {
       const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
@@ -1190,9 +1216,10 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
   __shared__ CallDesc c_s;
   __shared__ cp_spec_stats cnt_s;
   __shared__ SampleSmem sm;
-  __shared__ float px_s;
+  __shared__ float px_s, qx_s;
   __shared__ int ok_s;
   __shared__ uint32_t fl_s;
+  __shared__ int par_s[CP_SPEC_MAX_WINDOW], dep_s[CP_SPEC_MAX_WINDOW];
   constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
   constexpr int kCntW = sizeof(cp_spec_stats) / 8;
   static_assert(kStW <= 32 && kCallW <= 32 && kCntW <= 32, "state words");
@@ -1206,6 +1233,9 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
     reinterpret_cast<long long*>(&cnt_s)[tid - 64] = reinterpret_cast<const long long*>(r.sstats + b)[tid - 64];
   }
   if (tid == 0) fl_s = 0u;
+  // the tree in LDS: indexing the argument block at run time would copy it
+  // to scratch
+  if (tid >= 128 && tid < 128 + CP_SPEC_MAX_WINDOW) par_s[tid - 128] = r.par[tid - 128], dep_s[tid - 128] = r.dep[tid - 128];
   __syncthreads();
   StreamState st = st_s;
   if (st.mode == kModeDone) return;
@@ -1246,32 +1276,39 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
         if (f) fl |= 1u << (s + d);
       }
       for (int i = 0; i <= r.tnodes; ++i) {
-        if (i > 0 && r.dep[i] > gamma) continue;
+        if (i > 0 && dep_s[i] > gamma) continue;
         const uint32_t f = r.tflags[rb + i] & kFlagTopk;
         count_flags(f, &cnt_s);
-        if (f) fl |= 1u << (s + r.dep[i] + 1);
+        if (f) fl |= 1u << (s + dep_s[i] + 1);
       }
       fl_s = fl;
     }
     for (;;) {
-      const int d1 = r.dep[v] + 1, j = s + d1;
+      const int d1 = dep_s[v] + 1, j = s + d1;
       const float* prow = r.p + (rb + v) * r.V;
+      // q_{d1} exists when v has children (d1 <= gamma <= W)
+      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + min(d1, r.W) - 1) * r.V;
+      const bool has_q = d1 <= gamma;
+      float qv[VPT];
 #pragma unroll
-      for (int jj = 0; jj < VPT; ++jj) pv[jj] = prow[base + jj];
-      int kids[CP_SPEC_MAX_WINDOW], nk = 0;
+      for (int jj = 0; jj < VPT; ++jj) {
+        pv[jj] = prow[base + jj];
+        qv[jj] = has_q ? qrow[base + jj] : 0.0f;
+      }
+      uint32_t kmask = 0u;  // v's active children (bit = node)
+      int nk = 0;
       for (int ch = 1; ch <= r.tnodes; ++ch)
-        if (r.par[ch] == v && r.dep[ch] <= gamma) kids[nk++] = ch;
+        if (par_s[ch] == v && dep_s[ch] <= gamma) kmask |= 1u << ch, ++nk;
       int acc = -1;
-      for (int k = 0; k < nk; ++k) {
-        // q_{d1} exists: d1 <= gamma <= W
-        const float* qrow = r.q + (static_cast<size_t>(b) * r.W + (d1 - 1)) * r.V;
-        const int x = r.ncode[static_cast<size_t>(b) * 8 + kids[k]];
+      for (int ch = 1, k = 0; ch <= r.tnodes; ++ch) {
+        if (!((kmask >> ch) & 1u)) continue;
+        const int x = r.ncode[static_cast<size_t>(b) * 8 + ch];
 #pragma unroll
         for (int jj = 0; jj < VPT; ++jj)
-          if (base + jj == x) px_s = pv[jj];
+          if (base + jj == x) px_s = pv[jj], qx_s = qv[jj];
         __syncthreads();
         if (tid == 0) {
-          const float qx = (x >= 0 && x < r.V) ? qrow[x] : 1.0f;
+          const float qx = (x >= 0 && x < r.V) ? qx_s : 1.0f;
           const float ratio = px_s / qx;
           const float ua = frame_uniform(seed, j, kAccept, k);
           if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) {
@@ -1282,7 +1319,7 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
         }
         __syncthreads();
         if (ok_s) {
-          acc = kids[k];
+          acc = ch;
           break;
         }
         // rejected: p' <- max(0, p' - q), kept when nothing is left
@@ -1290,7 +1327,7 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
         bool any = false;
 #pragma unroll
         for (int jj = 0; jj < VPT; ++jj) {
-          rv[jj] = fmaxf(pv[jj] - qrow[base + jj], 0.0f);
+          rv[jj] = fmaxf(pv[jj] - qv[jj], 0.0f);
           any |= rv[jj] > 0.0f;
         }
         if (__syncthreads_or(any)) {
@@ -1302,6 +1339,7 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
 #pragma unroll
           for (int jj = 0; jj < VPT; ++jj) pv[jj] = pv[jj] / tot;
         }
+        ++k;
       }
       if (acc < 0) {
         bool nf = false;
@@ -1332,20 +1370,35 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
       }
       bool leaf = true;
       for (int ch = 1; ch <= r.tnodes; ++ch)
-        if (r.par[ch] == v && r.dep[ch] <= gamma) leaf = false;
+        if (par_s[ch] == v && dep_s[ch] <= gamma) leaf = false;
       if (leaf) ++cnt_s.bonus;
       st_s.flags |= fl_s;
       st_s.s = s + n;
     }
     // the accepted nodes' K/V: slot G + a - 1 -> position s + 1 + dep[a],
     // every layer, K and V
+    // (float4 pieces, every load of a node before its stores)
     float* kvb = r.kv + static_cast<size_t>(b) * r.kv_sb;
-    for (int a = v; a > 0; a = r.par[a]) {
+    const int kv4 = r.kvdim / 4, n4 = 2 * r.L * kv4;
+    for (int a = v; a > 0; a = par_s[a]) {
       const size_t src = static_cast<size_t>(r.G + a - 1) * r.kvdim;
-      const size_t dst = static_cast<size_t>(s + 1 + r.dep[a]) * r.kvdim;
-      for (int l2 = 0; l2 < 2 * r.L; ++l2) {
-        float* lay = kvb + static_cast<size_t>(l2) * r.Gk * r.kvdim;
-        for (int i = tid; i < r.kvdim; i += kBlock) lay[dst + i] = lay[src + i];
+      const size_t dst = static_cast<size_t>(s + 1 + dep_s[a]) * r.kvdim;
+      for (int i0 = tid; i0 < n4; i0 += 8 * kBlock) {
+        float4 t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = min(i0 + q * kBlock, n4 - 1);
+          const float* lay = kvb + static_cast<size_t>(i / kv4) * r.Gk * r.kvdim;
+          t[q] = *reinterpret_cast<const float4*>(lay + src + (i % kv4) * 4);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = i0 + q * kBlock;
+          if (i < n4) {
+            float* lay = kvb + static_cast<size_t>(i / kv4) * r.Gk * r.kvdim;
+            *reinterpret_cast<float4*>(lay + dst + (i % kv4) * 4) = t[q];
+          }
+        }
       }
     }
   }
@@ -1406,9 +1459,9 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
     st.gamma = g2;
     st.mode = kModeSpec;
     if (tid < r.R) {
-      const bool act = tid == 0 || r.dep[tid] <= g2;
+      const bool act = tid == 0 || dep_s[tid] <= g2;
       r.pos[rb + tid] = tid == 0 ? s2 + 1 : (act ? r.G + tid - 1 : -1);  // node i: slot G + i - 1
-      r.thead[rb + tid] = act ? s2 + 1 + r.dep[tid] : 0;
+      r.thead[rb + tid] = act ? s2 + 1 + dep_s[tid] : 0;
     }
     if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = tid + 1 <= g2 ? s2 + tid + 1 : 0;
   }

@@ -233,6 +233,57 @@ def verify_sweep(cid, Ns=(2, 3, 4, 5, 6, 8), frames=None, steps=2):
             "by_verify_size": {str(n): {k: round(v, 4) for k, v in r.items()} for n, r in rows.items()}}
 
 
+def tree_sweep(cid, shapes, frames=300, steps=2, oracle_frames=6):
+    """The tree-shaped verify window on this GPU: for each tree (a parent
+    list), codes/s, committed codes per verify pass and the per-depth share of
+    rounds that accepted a node at that depth, on the same weights and
+    inputs; plus the tree oracle's codes/s on the first frames of the first
+    tree (host cores, as the CPU baseline)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from speculative_decoding_rvq_amd import binding
+    c = synth.config(cid, frames=frames)
+    w = synth.make_weights(c)
+    wdev = binding.weights_to_device(w)
+    dh, dc, ds, hf, c0, seeds = _inputs(c, torch, np)
+    F, G = c["frames"], c["groups"]
+    out = torch.empty((F, 1, G), dtype=torch.int32, device="cuda")
+    rows = []
+    for parents in shapes:
+        h = binding.Handle(dict(c, tree=list(parents)), wdev, max_streams=1)
+        st = binding.new_stats_tensor()
+        h.decode_frames(dh, dc, ds, out, None, None)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            h.decode_frames(dh, dc, ds, out, None, st if i == 0 else None)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        s = binding.get_stats(st)
+        rows.append({"tree": list(parents), "codes_per_s": F * (G - 1) / (ms / 1e3),
+                     "ms_per_step": ms,
+                     "codes_per_verify_pass": (s["codes"] - s["frames"]) / max(s["rounds"], 1),
+                     "accepted_share_by_depth": [a / p for a, p in zip(s["accepted"], s["proposed"]) if p]})
+        h.close()
+    del wdev
+    torch.cuda.empty_cache()
+    from oracle import decoder, spec, tree
+    m = decoder.Model(c, w)
+    dp = dict(greedy=False, temperature=c["temperature"], top_k=c["top_k"])
+    t = tree.Tree(shapes[0])
+    t0 = time.perf_counter()
+    for f in range(oracle_frames):
+        tree.decode_frame_tree(m, dp, t, hf[f, 0], int(c0[f, 0]), int(seeds[f, 0]), spec.new_stats())
+    dt = time.perf_counter() - t0
+    return {"workload": cid, "frames": F, "by_tree": rows,
+            "oracle": {"tree": list(shapes[0]), "codes_per_s": oracle_frames * (G - 1) / dt,
+                       "sample": f"first {oracle_frames} frames"}}
+
+
 def cpu_baseline(cid, n_frames):
     """The oracle, as it stands, on the first n_frames of the workload."""
     import numpy as np
@@ -379,6 +430,13 @@ def main():
         # a wider window costs more rows per pass)
         line["verify_sweep"] = [verify_sweep(args.workload, frames=300),
                                 verify_sweep("qwen3tts-64", frames=40)]
+        # the tree-shaped window (at most 7 nodes, one stream), against the
+        # chain above
+        trees = tree_sweep(args.workload, ([0, 0, 1, 2], [0, 0], [0, 0, 0, 1, 2, 3],
+                                           [0, 0, 1, 2, 3, 4], [0, 1, 2]))
+        for row in trees["by_tree"]:
+            row["throughput_vs_chain_n4"] = row["codes_per_s"] / main_res["codes_per_s"]
+        line["tree_window"] = trees
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 

@@ -578,11 +578,14 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     // the draft row this row may test (offset rr + 1 exists for rr < W)
     const int head = r.thead[row];
     const StreamState st = r.st[b];
-    const bool has_q = !r.greedy && rr < r.W;
+    // (the chain's row rr tests draft offset rr + 1; a tree row tests the
+    // children of its node, drafted at depth dep[rr] + 1)
+    const int qi = r.tnodes > 0 ? r.dep[rr] : rr;
+    const bool has_q = !r.greedy && qi < r.W;
     float qv[VPT];
     int dd = -1;
     if (has_q) {
-      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + rr) * r.V;
+      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + qi) * r.V;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
       dd = r.dcode[static_cast<size_t>(b) * r.W + rr];
@@ -599,13 +602,69 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       return;
     }
     if (r.tnodes > 0) {
-      // tree window: the row's p (dense, for the walk) and its top-k flag
+      // tree window: the row's node decides its own step of the walk (it
+      // depends on the node alone): its active children are tested in order
+      // with U(depth, accept, k) < p'(x)/q(x), p' <- max(0, p' - q) after a
+      // rejection (kept when nothing is left), normalised by its sequential
+      // float32 sum when another child follows; with none accepted the row
+      // draws from p' with U(depth, target).  tflags: top-k flag, accept near
+      // ties of the tests, the draw's CDF near tie, accepted child + 1 in
+      // bits 16..23; tcode: the draw.
       const RowLds L = row_lds(row_dyn, r.V, true);
       store_row<VPT>(zv, L.z);
+      const bool spec_t = st.mode == kModeSpec;
+      const int gamma = spec_t ? st.gamma : 0;
+      uint32_t kmask = 0u;
+      int nk = 0;
+      if (spec_t)
+        for (int ch = 1; ch <= r.tnodes; ++ch)
+          if (r.par[ch] == rr && r.dep[ch] <= gamma) kmask |= 1u << ch, ++nk;
+      if (nk > 0) store_row<VPT>(qv, L.q);
       int total;
       uint32_t flags = 0;
-      if (topk_list<VPT>(zv, r.top_k, r.T, L, S, r.p + row * r.V, &total, &flags) && threadIdx.x == 0)
-        r.tflags[row] = flags;
+      if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, nullptr, &total, &flags)) return;
+      const int lane = threadIdx.x % kWave;
+      const uint64_t seed = frame_seed(st);
+      const int depth = spec_t ? st.s + r.dep[rr] + 1 : 1;
+      int dec = -1;
+      for (int ch = 1, k = 0; ch <= r.tnodes; ++ch) {
+        if (!((kmask >> ch) & 1u)) continue;
+        const int x = r.ncode[static_cast<size_t>(b) * 8 + ch];
+        const float qd = (x >= 0 && x < r.V) ? L.q[x] : 1.0f;
+        float pd = 0.0f;
+        for (int i = lane; i < total; i += kWave)
+          if (L.lidx[i] == x) pd = L.lw[i];
+        pd = wave_max(pd);
+        const float ratio = pd / qd;
+        const float ua = frame_uniform(seed, depth, kAccept, k);
+        if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) flags |= kFlagAccept;
+        if (ua < ratio) {
+          dec = ch;
+          break;
+        }
+        bool pos = false;
+        for (int i = lane; i < total; i += kWave) pos |= L.lw[i] - L.q[L.lidx[i]] > 0.0f;
+        if (__ballot(pos)) {
+          for (int i = lane; i < total; i += kWave) L.lw[i] = fmaxf(L.lw[i] - L.q[L.lidx[i]], 0.0f);
+          wave_lds_sync();
+        }
+        if (k + 1 < nk) {  // another child follows: normalise (the list is in code order)
+          float tot = 0.0f;
+          if (lane == 0)
+            for (int i = 0; i < total; ++i)
+              if (L.lw[i] > 0.0f) tot = tot + L.lw[i];
+          tot = __shfl(tot, 0);
+          for (int i = lane; i < total; i += kWave) L.lw[i] = L.lw[i] / tot;
+          wave_lds_sync();
+        }
+        ++k;
+      }
+      int code = -1, near = 0;
+      if (dec < 0) list_draw(L.lw, L.lidx, total, frame_uniform(seed, depth, kTarget), &code, &near);
+      if (threadIdx.x == 0) {
+        r.tcode[row] = code;
+        r.tflags[row] = flags | (near ? kFlagCdf : 0u) | (static_cast<uint32_t>(dec + 1) << 16);
+      }
       return;
     }
     const bool spec = st.mode == kModeSpec;
@@ -1201,165 +1260,102 @@ hipError_t launch_tree_attention(const AttnArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Accept side of the tree window, one block per stream.  Every thread
-// follows the same walk (thread 0 takes each test): at node v (depth d) with
-// p' = the row's p, the active children in node order are tested with
-// U(s+d+1, accept, k) < p'(x)/q_{d+1}(x); after a rejection p' becomes
-// max(0, p' - q_{d+1}) (kept when all zero), normalised by its sequential
-// float32 sum when another child follows; with no child accepted the round
-// draws from p' with U(s+d+1, target).  Then the path is committed, its
-// nodes' K/V move from their slots (G + i - 1) to their positions, h_{s+n} =
-// the last node's output row, and the stream's next round (or frame) is set
-// up.
+// Accept side of the tree window, one block per stream.  Every node's step
+// of the walk was decided by its row in the target kernel (accepted child,
+// or the row's draw); thread 0 follows the decisions from the root.  Then
+// the path is committed, its nodes' K/V move from their slots (G + i - 1) to
+// their positions, h_{s+n} = the last node's output row, and the stream's
+// next round (or frame) is set up.
 __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) {
   __shared__ StreamState st_s;
   __shared__ CallDesc c_s;
   __shared__ cp_spec_stats cnt_s;
-  __shared__ SampleSmem sm;
-  __shared__ float px_s, qx_s;
-  __shared__ int ok_s;
-  __shared__ uint32_t fl_s;
+  __shared__ uint32_t tfl_s[CP_SPEC_MAX_WINDOW], dfl_s[CP_SPEC_MAX_WINDOW];
+  __shared__ int tcode_s[CP_SPEC_MAX_WINDOW], ncode_s[CP_SPEC_MAX_WINDOW];
   __shared__ int par_s[CP_SPEC_MAX_WINDOW], dep_s[CP_SPEC_MAX_WINDOW];
+  __shared__ int v_s, n_s;
   constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
   constexpr int kCntW = sizeof(cp_spec_stats) / 8;
   static_assert(kStW <= 32 && kCallW <= 32 && kCntW <= 32, "state words");
   const int b = blockIdx.x, tid = threadIdx.x;
   const size_t rb = static_cast<size_t>(b) * r.R;
+  // ---- every independent load at once ----
   if (tid < kStW) {
     reinterpret_cast<int*>(&st_s)[tid] = reinterpret_cast<const int*>(r.st + b)[tid];
   } else if (tid >= 32 && tid < 32 + kCallW) {
     reinterpret_cast<int*>(&c_s)[tid - 32] = reinterpret_cast<const int*>(r.call)[tid - 32];
   } else if (tid >= 64 && tid < 64 + kCntW) {
     reinterpret_cast<long long*>(&cnt_s)[tid - 64] = reinterpret_cast<const long long*>(r.sstats + b)[tid - 64];
+  } else if (tid >= 96 && tid < 96 + CP_SPEC_MAX_WINDOW) {
+    const int i = tid - 96;
+    tfl_s[i] = i < r.R ? r.tflags[rb + i] : 0u;
+    tcode_s[i] = i < r.R ? r.tcode[rb + i] : -1;
+    ncode_s[i] = r.ncode[static_cast<size_t>(b) * 8 + i];
+    dfl_s[i] = i < r.W ? r.dflags[static_cast<size_t>(b) * r.W + i] : 0u;
+    par_s[i] = r.par[i];
+    dep_s[i] = r.dep[i];
   }
-  if (tid == 0) fl_s = 0u;
-  // the tree in LDS: indexing the argument block at run time would copy it
-  // to scratch
-  if (tid >= 128 && tid < 128 + CP_SPEC_MAX_WINDOW) par_s[tid - 128] = r.par[tid - 128], dep_s[tid - 128] = r.dep[tid - 128];
   __syncthreads();
   StreamState st = st_s;
   if (st.mode == kModeDone) return;
   const CallDesc& c = c_s;
   const size_t fb = static_cast<size_t>(st.f) * c.B + b;
   int* out = c.out_codes + fb * r.G;
-  const uint64_t seed = frame_seed(st);
   const bool spec = st.mode == kModeSpec;
   const int s = st.s, gamma = st.gamma;
-  int v = 0, n = 0;  // the walk's node and codes committed (the same in every thread)
-  dispatch_vpt(r.V, [&](auto vpt) {
-    constexpr int VPT = decltype(vpt)::value;
-    const int base = tid * VPT;
-    float pv[VPT];
-    if (!spec) {  // prefill: c_1 ~ p of row 1
-      const float* prow = r.p + (rb + 1) * r.V;
-#pragma unroll
-      for (int jj = 0; jj < VPT; ++jj) pv[jj] = prow[base + jj];
-      bool nf = false;
-      const int code = sample_regs<VPT>(pv, frame_uniform(seed, 1, kTarget), sm, &nf);
-      if (tid == 0) {
-        const uint32_t f = (r.tflags[rb + 1] & kFlagTopk) | (nf ? kFlagCdf : 0u);
-        count_flags(f, &cnt_s);
-        if (f) st_s.flags |= 1u << 1;
-        out[1] = st_s.last = code;
-        ++cnt_s.prefill_passes;
-        st_s.s = 1;
-      }
-      v = 1;
-      n = 1;
-      return;
-    }
-    if (tid == 0) {  // the drafts' flags and every active row's top-k flag
+  if (tid == 0) {
+    cp_spec_stats& cnt = cnt_s;
+    if (!spec) {  // prefill: c_1 is row 1's draw
+      const uint32_t f = tfl_s[1] & (kFlagTopk | kFlagCdf);
+      count_flags(f, &cnt);
+      if (f) st_s.flags |= 1u << 1;
+      out[1] = st_s.last = tcode_s[1];
+      ++cnt.prefill_passes;
+      st_s.s = 1;
+      v_s = 1;
+      n_s = 1;
+    } else {
       uint32_t fl = 0u;
-      for (int d = 1; d <= gamma; ++d) {
-        const uint32_t f = r.dflags[static_cast<size_t>(b) * r.W + d - 1];
-        count_flags(f, &cnt_s);
+      for (int d = 1; d <= gamma; ++d) {  // the drafts' flags
+        const uint32_t f = dfl_s[d - 1];
+        count_flags(f, &cnt);
         if (f) fl |= 1u << (s + d);
       }
-      for (int i = 0; i <= r.tnodes; ++i) {
+      for (int i = 0; i <= r.tnodes; ++i) {  // every active row's top-k flag
         if (i > 0 && dep_s[i] > gamma) continue;
-        const uint32_t f = r.tflags[rb + i] & kFlagTopk;
-        count_flags(f, &cnt_s);
+        const uint32_t f = tfl_s[i] & kFlagTopk;
+        count_flags(f, &cnt);
         if (f) fl |= 1u << (s + dep_s[i] + 1);
       }
-      fl_s = fl;
-    }
-    for (;;) {
-      const int d1 = dep_s[v] + 1, j = s + d1;
-      const float* prow = r.p + (rb + v) * r.V;
-      // q_{d1} exists when v has children (d1 <= gamma <= W)
-      const float* qrow = r.q + (static_cast<size_t>(b) * r.W + min(d1, r.W) - 1) * r.V;
-      const bool has_q = d1 <= gamma;
-      float qv[VPT];
-#pragma unroll
-      for (int jj = 0; jj < VPT; ++jj) {
-        pv[jj] = prow[base + jj];
-        qv[jj] = has_q ? qrow[base + jj] : 0.0f;
-      }
-      uint32_t kmask = 0u;  // v's active children (bit = node)
-      int nk = 0;
-      for (int ch = 1; ch <= r.tnodes; ++ch)
-        if (par_s[ch] == v && dep_s[ch] <= gamma) kmask |= 1u << ch, ++nk;
-      int acc = -1;
-      for (int ch = 1, k = 0; ch <= r.tnodes; ++ch) {
-        if (!((kmask >> ch) & 1u)) continue;
-        const int x = r.ncode[static_cast<size_t>(b) * 8 + ch];
-#pragma unroll
-        for (int jj = 0; jj < VPT; ++jj)
-          if (base + jj == x) px_s = pv[jj], qx_s = qv[jj];
-        __syncthreads();
-        if (tid == 0) {
-          const float qx = (x >= 0 && x < r.V) ? qx_s : 1.0f;
-          const float ratio = px_s / qx;
-          const float ua = frame_uniform(seed, j, kAccept, k);
-          if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) {
-            ++cnt_s.near_tie_accept;
-            fl_s |= 1u << j;
-          }
-          ok_s = ua < ratio ? 1 : 0;
+      int v = 0, n = 0;
+      for (;;) {  // the walk: at most one node per depth
+        const uint32_t tf = tfl_s[v];
+        const int j = s + dep_s[v] + 1;
+        if (tf & kFlagAccept) {
+          ++cnt.near_tie_accept;
+          fl |= 1u << j;
         }
-        __syncthreads();
-        if (ok_s) {
-          acc = ch;
+        const int dec = static_cast<int>((tf >> 16) & 0xFFu) - 1;
+        if (dec < 1 || dec > r.tnodes) {
+          if (tf & kFlagCdf) {
+            ++cnt.near_tie_cdf;
+            fl |= 1u << j;
+          }
+          out[s + n + 1] = st_s.last = tcode_s[v];
+          ++n;
           break;
         }
-        // rejected: p' <- max(0, p' - q), kept when nothing is left
-        float rv[VPT];
-        bool any = false;
-#pragma unroll
-        for (int jj = 0; jj < VPT; ++jj) {
-          rv[jj] = fmaxf(pv[jj] - qv[jj], 0.0f);
-          any |= rv[jj] > 0.0f;
-        }
-        if (__syncthreads_or(any)) {
-#pragma unroll
-          for (int jj = 0; jj < VPT; ++jj) pv[jj] = rv[jj];
-        }
-        if (k + 1 < nk) {  // another child is tested on it: normalise
-          const float tot = positive_sum_regs<VPT>(pv, sm);
-#pragma unroll
-          for (int jj = 0; jj < VPT; ++jj) pv[jj] = pv[jj] / tot;
-        }
-        ++k;
-      }
-      if (acc < 0) {
-        bool nf = false;
-        const int code = sample_regs<VPT>(pv, frame_uniform(seed, j, kTarget), sm, &nf);
-        if (tid == 0) {
-          if (nf) {
-            ++cnt_s.near_tie_cdf;
-            fl_s |= 1u << j;
-          }
-          out[s + n + 1] = st_s.last = code;
-        }
+        out[s + n + 1] = ncode_s[dec];
         ++n;
-        break;
+        v = dec;
       }
-      if (tid == 0) out[s + n + 1] = r.ncode[static_cast<size_t>(b) * 8 + acc];
-      ++n;
-      v = acc;
+      st_s.flags |= fl;
+      v_s = v;
+      n_s = n;
     }
-  });
+  }
   __syncthreads();
+  const int v = v_s, n = n_s;
 
   if (spec) {
     if (tid == 0) {
@@ -1372,7 +1368,6 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
       for (int ch = 1; ch <= r.tnodes; ++ch)
         if (par_s[ch] == v && dep_s[ch] <= gamma) leaf = false;
       if (leaf) ++cnt_s.bonus;
-      st_s.flags |= fl_s;
       st_s.s = s + n;
     }
     // the accepted nodes' K/V: slot G + a - 1 -> position s + 1 + dep[a],

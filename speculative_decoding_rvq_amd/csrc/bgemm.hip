@@ -98,18 +98,6 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     if (tid < TM) rows_s[tid] = tid < count ? m0 + tid : -1;
   }
   __syncthreads();
-  // per-row values the epilogue needs, loaded while the K loop runs (visible
-  // after the barrier that precedes the epilogue)
-  if (tid < TM) {
-    const int row = rows_s[tid];
-    if (MODE == kQKV) pos_s[tid] = row >= 0 ? a.pos[row] : -1;
-    if (PL && NORM) {  // the split pass's partial sums of squares, in order
-      float t = 0.0f;
-      if (row >= 0)
-        for (int j = 0; j < a.K / 32; ++j) t += a.ssp[static_cast<size_t>(row) * (a.K / 32) + j];
-      rinv_s[tid] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
-    }
-  }
 
   // ---- operand pointers.  Activations: for row tile f, lane l reads row
 // 16 f + l / 4, k 8 (l % 4) .. +7 of each chunk (a quad covers one 128-byte
@@ -316,6 +304,25 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 
   }
 
+  // RMSNorm of pre-split rows: the producer left per-row sums of squares per
+  // 32-wide K chunk.  TPR neighbouring threads read a row's, each a
+  // contiguous run, all loads at once (they stay in flight during the tile
+  // exchange below); each run is summed in order and the TPR sums folded by
+  // a butterfly, the same on every run.
+  constexpr int TPR = kGT / TM;
+  constexpr int kRun = 8;
+  const int np = a.K / 32, per = np / TPR;
+  const int srow = rows_s[tid / TPR];
+  const float* sp = (PL && NORM) ? a.ssp + static_cast<size_t>(srow >= 0 ? srow : 0) * np + (tid % TPR) * per
+                                 : nullptr;
+  float sv[kRun];
+  if constexpr (PL && NORM) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) sv[i] = (srow >= 0 && i < per) ? sp[i] : 0.0f;
+  }
+  int pv = -1;  // Q/K/V: the row's position, loaded with them
+  if (MODE == kQKV && tid < TM && rows_s[tid] >= 0) pv = a.pos[rows_s[tid]];
+
   // ---- the eight partial tiles meet in LDS in a fixed order: waves 4-7
   // hand theirs to waves 0-3 (w + w+4), which store the four sums; one more
   // barrier and every thread finishes TM * TN / 512 outputs as
@@ -350,6 +357,17 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   }
   __syncthreads();
   if (wave < 4) store_acc(wave);
+  if constexpr (PL && NORM) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i)
+      if (i < per) t += sv[i];
+    for (int i = kRun; i < per; ++i) t += srow >= 0 ? sp[i] : 0.0f;
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) t += __shfl_xor(t, o);
+    if (tid % TPR == 0) rinv_s[tid / TPR] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+  }
+  if (MODE == kQKV && tid < TM) pos_s[tid] = pv;
   __syncthreads();
   auto rinv_of = [&](int r) {
     if constexpr (PL) {

@@ -405,7 +405,10 @@ __device__ __forceinline__ void embed_row(const RoundArgs& r, int table, int cod
 }
 
 // The same by threads i = 0..n-1 of a group (8 bf16 or 4 fp32 values per
-// thread per step when the rows are 16-byte aligned).
+// thread per step when the rows are 16-byte aligned).  bf16 rows: up to
+// kGatherRun steps' loads are issued before the first store, so a row costs
+// one memory round trip, not one per step.
+constexpr int kGatherRun = 4;
 __device__ __forceinline__ void embed_row_span(const RoundArgs& r, int table, int code, float* dst, int i0,
                                                int n) {
   code = min(max(code, 0), r.V - 1);
@@ -414,11 +417,19 @@ __device__ __forceinline__ void embed_row_span(const RoundArgs& r, int table, in
   if (r.wbf16) {
     const uint16_t* e = static_cast<const uint16_t*>(r.embed) + off;
     if ((r.H & 7) == 0 && dst_al && (reinterpret_cast<uintptr_t>(e) & 15u) == 0) {
-      for (int i = i0 * 8; i < r.H; i += n * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(e + i);
-        *reinterpret_cast<float4*>(dst + i) = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
-        *reinterpret_cast<float4*>(dst + i + 4) =
-            make_float4(bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w));
+      const int step = n * 8;
+      for (int i = i0 * 8; i < r.H; i += kGatherRun * step) {
+        uint4 v[kGatherRun];
+#pragma unroll
+        for (int j = 0; j < kGatherRun; ++j)
+          if (i + j * step < r.H) v[j] = *reinterpret_cast<const uint4*>(e + i + j * step);
+#pragma unroll
+        for (int j = 0; j < kGatherRun; ++j) {
+          if (i + j * step >= r.H) break;
+          float* d = dst + i + j * step;
+          *reinterpret_cast<float4*>(d) = make_float4(bf16lo(v[j].x), bf16hi(v[j].x), bf16lo(v[j].y), bf16hi(v[j].y));
+          *reinterpret_cast<float4*>(d + 4) = make_float4(bf16lo(v[j].z), bf16hi(v[j].z), bf16lo(v[j].w), bf16hi(v[j].w));
+        }
       }
     } else {
       for (int i = i0; i < r.H; i += n) dst[i] = bf16_to_f32(e[i]);
@@ -954,6 +965,7 @@ __global__ __launch_bounds__(kBlock) void talker_feedback_kernel(const void* emb
   float* dst = out + static_cast<size_t>(row) * H;
   for (int i = threadIdx.x * 4; i < H; i += kBlock * 4) {
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll 8
     for (int g = 0; g < G; ++g) {
       const size_t off = (static_cast<size_t>(g) * V + code_s[g]) * H + i;
       if (wbf16) {

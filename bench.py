@@ -184,53 +184,30 @@ def feedback_timing(h, c, out, torch, iters=50):
 
 
 def verify_sweep(cid, Ns=(2, 3, 4, 5, 6, 8), frames=None, steps=2):
-    """Per-device choice of the verify window N: for each N, codes/s and
-    committed codes per verify pass on this GPU (same weights and inputs),
-    and the best N.  Also the codes per round that the widest window's
-    measured acceptance predicts for each N: 1 + sum over t < N of the share
-    of rounds whose first t drafts were all accepted (frame ends, which cut
-    the window short, are ignored by the prediction)."""
+    """Per-device choice of the verify window N (the package's
+    calibrate_window): for each N, codes/s, committed codes per verify pass
+    and one pass's time on this GPU (same weights and inputs); the codes per
+    round that the widest window's measured acceptance predicts for each N;
+    the N chosen from prediction and pass times, and the N with the best
+    measured codes/s."""
     import numpy as np
     import torch
 
     import synth
     from speculative_decoding_rvq_amd import binding
+    from speculative_decoding_rvq_amd.calibrate import calibrate_window
     c = synth.config(cid, **({"frames": frames} if frames else {}))
     wdev = binding.weights_to_device(synth.make_weights(c))
     dh, dc, ds, *_ = _inputs(c, torch, np)
-    F, B, G = c["frames"], c["streams"], c["groups"]
-    out = torch.empty((F, B, G), dtype=torch.int32, device="cuda")
-    rows = {}
-    for N in Ns:
-        h = binding.Handle(dict(c, verify_size=N), wdev)
-        st = binding.new_stats_tensor()
-        h.decode_frames(dh, dc, ds, out, None, None)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            h.decode_frames(dh, dc, ds, out, None, st if i == 0 else None)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        s = binding.get_stats(st)
-        rows[N] = {"codes_per_s": F * B * (G - 1) / (ms / 1e3),
-                   "codes_per_verify_pass": (s["codes"] - s["frames"]) / max(s["rounds"], 1),
-                   # one graph replay advances every stream by one decoder pass
-                   "us_per_pass": 1e3 * ms / max(s["rounds"] + s["prefill_passes"], 1) * B,
-                   "stats": s}
-        h.close()
-    widest = rows[max(Ns)]["stats"]
-    share = [a / p for a, p in zip(widest["accepted"], widest["proposed"]) if p]
-    for N in Ns:
-        rows[N]["predicted_codes_per_round"] = 1.0 + sum(share[: N - 1])
-        del rows[N]["stats"]
-    best = max(Ns, key=lambda n: rows[n]["codes_per_s"])
+    cal = calibrate_window(c, wdev, dh, dc, ds, sizes=Ns, repeats=steps)
     del wdev
     torch.cuda.empty_cache()
-    return {"workload": cid, "frames": F, "streams": B, "best_verify_size": best,
-            "accepted_share_by_offset": share,
-            "by_verify_size": {str(n): {k: round(v, 4) for k, v in r.items()} for n, r in rows.items()}}
+    return {"workload": cid, "frames": c["frames"], "streams": c["streams"],
+            "best_verify_size": cal["measured_best"],
+            "calibrated_verify_size": cal["verify_size"],
+            "accepted_share_by_offset": cal["accepted_share_by_offset"],
+            "by_verify_size": {str(n): {k: round(v, 4) for k, v in r.items()}
+                               for n, r in cal["by_verify_size"].items()}}
 
 
 def tree_sweep(cid, shapes, frames=300, steps=2, oracle_frames=6):

@@ -1,0 +1,48 @@
+"""The per-device verify-window choice on the GPU: calibrate_window profiles
+every window size through cp_spec_decode_frames and returns a consistent
+choice (the code streams at each size are checked against the oracle by the
+window-sweep parity tests)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import device_weights, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def test_calibrate_window_tiny():
+    from speculative_decoding_rvq_amd.calibrate import choose_window, expected_codes_per_round
+    from speculative_decoding_rvq_amd.calibrate import calibrate_window
+    c = synth.config("tiny", frames=40)
+    hf, c0, seeds = synth.make_inputs(c)
+    dh = torch.from_numpy(np.ascontiguousarray(hf)).cuda()
+    dc = torch.from_numpy(np.ascontiguousarray(c0)).cuda()
+    ds = torch.from_numpy(np.ascontiguousarray(seeds).view(np.int64)).cuda()
+    sizes = (2, 3, 4, 5)
+    cal = calibrate_window(c, device_weights("tiny"), dh, dc, ds, sizes=sizes, repeats=1)
+    log(f"calibrated N={cal['verify_size']} (measured best {cal['measured_best']}), "
+        f"shares {[round(x, 3) for x in cal['accepted_share_by_offset']]}")
+    share = cal["accepted_share_by_offset"]
+    assert len(share) == max(sizes) - 1
+    assert all(0.0 <= x <= 1.0 for x in share)
+    rows = cal["by_verify_size"]
+    assert sorted(rows) == list(sizes)
+    for n, r in rows.items():
+        assert r["us_per_pass"] > 0.0 and r["codes_per_s"] > 0.0
+        assert 1.0 <= r["codes_per_verify_pass"] <= n
+        assert r["expected_codes_per_round"] == pytest.approx(expected_codes_per_round(share, n))
+    assert cal["verify_size"] == choose_window(share, {n: r["us_per_pass"] for n, r in rows.items()})
+    assert cal["measured_best"] in sizes
+
+
+def test_calibrate_window_rejects_bad_sizes():
+    from speculative_decoding_rvq_amd.calibrate import calibrate_window
+    c = synth.config("tiny", frames=2)
+    hf, c0, seeds = synth.make_inputs(c)
+    with pytest.raises(ValueError):
+        calibrate_window(c, device_weights("tiny"), hf, c0, seeds, sizes=(1, 2))
+    with pytest.raises(ValueError):
+        calibrate_window(c, device_weights("tiny"), hf, c0, seeds, sizes=())

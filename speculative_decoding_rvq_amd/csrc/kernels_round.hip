@@ -454,13 +454,35 @@ __device__ __forceinline__ void set_frame_seed(StreamState& st, uint64_t seed) {
 }
 
 // Prefill of frame f for stream b: rows [h_frame, E_0[c_0]] at positions 0, 1
-// and head 1 on row 1.
+// and head 1 on row 1.  Rows wider than the block are copied with every load
+// issued before the stores (16-byte pieces when aligned): one memory round
+// trip per row instead of one per H / kBlock step.
 __device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int f) {
   float* x = r.X + static_cast<size_t>(b) * r.R * r.H;
   const float* hf = c.h_frame + (static_cast<size_t>(f) * c.B + b) * r.H;
-  for (int i = threadIdx.x; i < r.H; i += kBlock) x[i] = hf[i];
   const int c0 = c.c0[static_cast<size_t>(f) * c.B + b];
-  embed_row(r, 0, c0, x + r.H);
+  if (r.H > kBlock) {
+    if ((r.H & 3) == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(hf)) & 15u) == 0) {
+      const int step = kBlock * 4;
+      for (int i = threadIdx.x * 4; i < r.H; i += kGatherRun * step) {
+        float4 v[kGatherRun];
+#pragma unroll
+        for (int j = 0; j < kGatherRun; ++j)
+          if (i + j * step < r.H) v[j] = *reinterpret_cast<const float4*>(hf + i + j * step);
+#pragma unroll
+        for (int j = 0; j < kGatherRun; ++j) {
+          if (i + j * step >= r.H) break;
+          *reinterpret_cast<float4*>(x + i + j * step) = v[j];
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < r.H; i += kBlock) x[i] = hf[i];
+    }
+    embed_row_span(r, 0, c0, x + r.H, threadIdx.x, kBlock);
+  } else {
+    for (int i = threadIdx.x; i < r.H; i += kBlock) x[i] = hf[i];
+    embed_row(r, 0, c0, x + r.H);
+  }
   if (threadIdx.x == 0) {
     c.out_codes[(static_cast<size_t>(f) * c.B + b) * r.G] = c0;
     for (int i = 0; i < r.R; ++i) {

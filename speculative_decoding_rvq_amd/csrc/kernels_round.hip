@@ -532,10 +532,13 @@ __global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
   const size_t row = static_cast<size_t>(b) * r.W + (t - 1);
   dispatch_vpt(r.V, [&](auto vpt) {
     constexpr int VPT = decltype(vpt)::value;
-    float zv[VPT];
-    load_row<VPT>(r.dlogits + row * r.V, zv);  // before the state: the row always exists
+    // the state goes out first, then the row (it always exists), so that the
+    // draw's uniform is computed while the row is still in flight
     const StreamState st = r.st[b];
+    float zv[VPT];
+    load_row<VPT>(r.dlogits + row * r.V, zv);
     if (st.mode != kModeSpec) return;
+    const float u = r.greedy ? 0.0f : frame_uniform(frame_seed(st), st.s + t, kDraft);
     // verify row 0 = E_s[c_s]: gathered by the block of offset 1, while the
     // draft rows are sampled
     float* x0 = r.X + static_cast<size_t>(b) * r.R * r.H;
@@ -556,7 +559,6 @@ __global__ __launch_bounds__(kBlock) void draft_topk_kernel(const RoundArgs r) {
     }
     const RowLds L = row_lds(row_dyn, r.V, false);
     store_row<VPT>(zv, L.z);
-    const float u = frame_uniform(frame_seed(st), st.s + t, kDraft);
     int total;
     uint32_t flags = 0;
     if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, r.q + row * r.V, &total, &flags)) {
@@ -604,13 +606,15 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
   dispatch_vpt(r.V, [&](auto vpt) {
     constexpr int VPT = decltype(vpt)::value;
     const int base = threadIdx.x * VPT;
-    float zv[VPT];
-    load_row<VPT>(r.tlogits + row * r.V, zv);  // before the row's head: the row always exists
-    // every other load that depends only on the block goes out with it (one
-    // memory round trip, not three): the row's head, the stream's state, and
-    // the draft row this row may test (offset rr + 1 exists for rr < W)
+    // every load that depends only on the block goes out at once (one memory
+    // round trip, not three): the row's head and the stream's state first, so
+    // that the uniforms are computed while the rest is in flight, then the
+    // logits and the draft row this row may test (offset rr + 1 exists for
+    // rr < W)
     const int head = r.thead[row];
     const StreamState st = r.st[b];
+    float zv[VPT];
+    load_row<VPT>(r.tlogits + row * r.V, zv);
     // (the chain's row rr tests draft offset rr + 1; a tree row tests the
     // children of its node, drafted at depth dep[rr] + 1)
     const int qi = r.tnodes > 0 ? r.dep[rr] : rr;
@@ -626,6 +630,12 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     // (a finished stream's heads are zero already; testing its mode here keeps
     // the state load ahead of this branch)
     if (head <= 0 || st.mode == kModeDone) return;
+    // the chain row's uniforms (depth s + 1 + rr; prefill: depth 1)
+    const bool spec = st.mode == kModeSpec;
+    const int depth = spec ? st.s + 1 + rr : 1;
+    const bool chain_s = !r.greedy && r.tnodes == 0;
+    const float ut = chain_s ? frame_uniform(frame_seed(st), depth, kTarget) : 0.0f;
+    const float ua = chain_s && spec && rr < st.gamma ? frame_uniform(frame_seed(st), depth, kAccept) : 0.0f;
     if (r.greedy) {
       const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
       if (threadIdx.x == 0) {
@@ -700,9 +710,7 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       }
       return;
     }
-    const bool spec = st.mode == kModeSpec;
     const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
-    const int depth = spec ? st.s + 1 + rr : 1;
     const RowLds L = row_lds(row_dyn, r.V, true);
     store_row<VPT>(zv, L.z);
     int d = -1;
@@ -715,8 +723,6 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     uint32_t flags = 0;
     if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, nullptr, &total, &flags)) return;
     // wave 0: the row's decision
-    const uint64_t seed = frame_seed(st);
-    const float ut = frame_uniform(seed, depth, kTarget);
     int code, near = 0;
     if (test) {
       // p_r(d_t) is zero unless d_t is in the target's top-k set; a code
@@ -727,7 +733,6 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
         if (L.lidx[i] == d) pd = L.lw[i];
       pd = wave_max(pd);
       const float ratio = pd / qd;
-      const float ua = frame_uniform(seed, depth, kAccept);
       if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) flags |= kFlagAccept;
       if (ua < ratio) {
         code = d;

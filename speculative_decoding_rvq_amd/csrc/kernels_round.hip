@@ -992,7 +992,6 @@ __global__ __launch_bounds__(kBlock) void talker_feedback_kernel(const void* emb
   float* dst = out + static_cast<size_t>(row) * H;
   for (int i = threadIdx.x * 4; i < H; i += kBlock * 4) {
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-#pragma unroll 8
     for (int g = 0; g < G; ++g) {
       const size_t off = (static_cast<size_t>(g) * V + code_s[g]) * H + i;
       if (wbf16) {

@@ -1187,41 +1187,61 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   const float* kb = a.kv + static_cast<size_t>(b) * a.kv_sb + g * D;
   const float* vb = kb + a.kv_vo;
 
-  // ---- phase 1: K (rotated), V, Q (rotated) into LDS ----
+  // ---- phase 1: K (rotated), V, Q (rotated) into LDS; a thread's items
+  // two at a time, both items' loads issued before either's stores ----
   const int nk = np * H4, nq = npair * H4;
-  for (int it = threadIdx.x; it < nk + nq; it += kBlock) {
+  struct Item {
+    float4 x1, x2, v1, v2, c01, c23;
+  };
+  auto load_item = [&](int it, Item& m) {
     if (it < nk) {
       const int p = it / H4, i4 = (it % H4) * 4;
       const int sl = kslot_s[p], lp = klp_s[p];
-      const float4 k1 = *reinterpret_cast<const float4*>(kb + sl * kvdim + i4);
-      const float4 k2 = *reinterpret_cast<const float4*>(kb + sl * kvdim + i4 + half);
-      const float4 v1 = *reinterpret_cast<const float4*>(vb + sl * kvdim + i4);
-      const float4 v2 = *reinterpret_cast<const float4*>(vb + sl * kvdim + i4 + half);
-      const float4 c01 = *reinterpret_cast<const float4*>(a.rope + lp * half + i4);
-      const float4 c23 = *reinterpret_cast<const float4*>(a.rope + lp * half + i4 + 2);
-      float* kr = Ks + p * KS;
-      kr[i4 + 0] = k1.x * c01.x - k2.x * c01.y;  kr[i4 + half + 0] = k2.x * c01.x + k1.x * c01.y;
-      kr[i4 + 1] = k1.y * c01.z - k2.y * c01.w;  kr[i4 + half + 1] = k2.y * c01.z + k1.y * c01.w;
-      kr[i4 + 2] = k1.z * c23.x - k2.z * c23.y;  kr[i4 + half + 2] = k2.z * c23.x + k1.z * c23.y;
-      kr[i4 + 3] = k1.w * c23.z - k2.w * c23.w;  kr[i4 + half + 3] = k2.w * c23.z + k1.w * c23.w;
-      *reinterpret_cast<float4*>(Vs + p * D + i4) = v1;
-      *reinterpret_cast<float4*>(Vs + p * D + i4 + half) = v2;
-    } else {
+      m.x1 = *reinterpret_cast<const float4*>(kb + sl * kvdim + i4);
+      m.x2 = *reinterpret_cast<const float4*>(kb + sl * kvdim + i4 + half);
+      m.v1 = *reinterpret_cast<const float4*>(vb + sl * kvdim + i4);
+      m.v2 = *reinterpret_cast<const float4*>(vb + sl * kvdim + i4 + half);
+      m.c01 = *reinterpret_cast<const float4*>(a.rope + lp * half + i4);
+      m.c23 = *reinterpret_cast<const float4*>(a.rope + lp * half + i4 + 2);
+    } else if (it < nk + nq) {
       const int jt = it - nk;
       const int pr = jt / H4, i4 = (jt % H4) * 4;
       const int r = pr / group, j = pr % group;
       const float* qrow = a.Q + static_cast<size_t>(b * R + r) * qdim + (g * group + j) * D;
       const int pq = max(qp_s[r], 0);
-      const float4 q1 = *reinterpret_cast<const float4*>(qrow + i4);
-      const float4 q2 = *reinterpret_cast<const float4*>(qrow + i4 + half);
-      const float4 c01 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4);
-      const float4 c23 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4 + 2);
-      float* qr = Qs + pr * D;
-      qr[i4 + 0] = q1.x * c01.x - q2.x * c01.y;  qr[i4 + half + 0] = q2.x * c01.x + q1.x * c01.y;
-      qr[i4 + 1] = q1.y * c01.z - q2.y * c01.w;  qr[i4 + half + 1] = q2.y * c01.z + q1.y * c01.w;
-      qr[i4 + 2] = q1.z * c23.x - q2.z * c23.y;  qr[i4 + half + 2] = q2.z * c23.x + q1.z * c23.y;
-      qr[i4 + 3] = q1.w * c23.z - q2.w * c23.w;  qr[i4 + half + 3] = q2.w * c23.z + q1.w * c23.w;
+      m.x1 = *reinterpret_cast<const float4*>(qrow + i4);
+      m.x2 = *reinterpret_cast<const float4*>(qrow + i4 + half);
+      m.c01 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4);
+      m.c23 = *reinterpret_cast<const float4*>(a.rope + pq * half + i4 + 2);
     }
+  };
+  auto store_item = [&](int it, const Item& m) {
+    if (it >= nk + nq) return;
+    int i4;
+    float* dst;
+    if (it < nk) {
+      const int p = it / H4;
+      i4 = (it % H4) * 4;
+      dst = Ks + p * KS;
+      *reinterpret_cast<float4*>(Vs + p * D + i4) = m.v1;
+      *reinterpret_cast<float4*>(Vs + p * D + i4 + half) = m.v2;
+    } else {
+      const int jt = it - nk;
+      i4 = (jt % H4) * 4;
+      dst = Qs + (jt / H4) * D;
+    }
+    const float4 k1 = m.x1, k2 = m.x2, c01 = m.c01, c23 = m.c23;
+    dst[i4 + 0] = k1.x * c01.x - k2.x * c01.y;  dst[i4 + half + 0] = k2.x * c01.x + k1.x * c01.y;
+    dst[i4 + 1] = k1.y * c01.z - k2.y * c01.w;  dst[i4 + half + 1] = k2.y * c01.z + k1.y * c01.w;
+    dst[i4 + 2] = k1.z * c23.x - k2.z * c23.y;  dst[i4 + half + 2] = k2.z * c23.x + k1.z * c23.y;
+    dst[i4 + 3] = k1.w * c23.z - k2.w * c23.w;  dst[i4 + half + 3] = k2.w * c23.z + k1.w * c23.w;
+  };
+  for (int it = threadIdx.x; it < nk + nq; it += 2 * kBlock) {
+    Item m0, m1;
+    load_item(it, m0);
+    load_item(it + kBlock, m1);
+    store_item(it, m0);
+    store_item(it + kBlock, m1);
   }
   __syncthreads();
 

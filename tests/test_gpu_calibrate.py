@@ -46,3 +46,23 @@ def test_calibrate_window_rejects_bad_sizes():
         calibrate_window(c, device_weights("tiny"), hf, c0, seeds, sizes=(1, 2))
     with pytest.raises(ValueError):
         calibrate_window(c, device_weights("tiny"), hf, c0, seeds, sizes=())
+
+
+def test_calibrate_window_greedy_tiny():
+    """Greedy decoding (argmax-equality verify): the shares come from the same
+    counters, and a window of 2 commits at most 2 codes per pass."""
+    from speculative_decoding_rvq_amd.calibrate import calibrate_window, expected_codes_per_round
+    c = synth.config("tiny", frames=30, greedy=True)
+    hf, c0, seeds = synth.make_inputs(c)
+    dh = torch.from_numpy(np.ascontiguousarray(hf)).cuda()
+    dc = torch.from_numpy(np.ascontiguousarray(c0)).cuda()
+    ds = torch.from_numpy(np.ascontiguousarray(seeds).view(np.int64)).cuda()
+    cal = calibrate_window(c, device_weights("tiny"), dh, dc, ds, sizes=(2, 4, 6), repeats=1)
+    log(f"greedy: calibrated N={cal['verify_size']}, shares "
+        f"{[round(x, 3) for x in cal['accepted_share_by_offset']]}")
+    assert cal["verify_size"] in (2, 4, 6)
+    assert len(cal["accepted_share_by_offset"]) == 5
+    assert cal["by_verify_size"][2]["codes_per_verify_pass"] <= 2.0
+    for n, r in cal["by_verify_size"].items():
+        assert r["expected_codes_per_round"] == pytest.approx(
+            expected_codes_per_round(cal["accepted_share_by_offset"], n))

@@ -535,6 +535,7 @@ __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, c
     }
   }
   if (threadIdx.x == 0) r.st[b] = st;
+  if (r.tnodes > 0 && threadIdx.x == 0) r.ncode[static_cast<size_t>(b) * 8] = 0;  // no K/V move pending
 }
 
 hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t s) {
@@ -1067,6 +1068,40 @@ hipError_t launch_stats_flush(const cp_spec_stats* sstats, int B, cp_spec_stats*
 // among the nodes of depth d, node order), then gathers each node's verify
 // input E_{s+d}[code]; the block of depth 1 also gathers row 0 = E_s[c_s].
 // Per-depth flags (top-k boundary, any draw's CDF near tie) go to dflags.
+// The previous round's accepted tree nodes' K/V: slot G + a - 1 -> position
+// s + 1 + dep[a] for every node a on the path from the root to node v, every
+// layer, K and V.  The round's tree accept kernel leaves (s, v) in
+// ncode[b][0]; the W draft blocks of the stream share the move (block
+// `part`), a node at a time with all of a node's loads before its stores.
+// It runs before the round's projections write new node K/V into the slots.
+__device__ void tree_kv_move(const RoundArgs& r, int b, int s, int v, int part) {
+  float* kvb = r.kv + static_cast<size_t>(b) * r.kv_sb;
+  const int kv4 = r.kvdim / 4, n4 = 2 * r.L * kv4;
+  const int nthr = r.W * kBlock;
+  constexpr int Q = 4;
+  for (int a = v; a > 0 && a <= r.tnodes; a = r.par[a]) {
+    const size_t src = static_cast<size_t>(r.G + a - 1) * r.kvdim;
+    const size_t dst = static_cast<size_t>(s + 1 + r.dep[a]) * r.kvdim;
+    for (int i0 = part * kBlock + threadIdx.x; i0 < n4; i0 += Q * nthr) {
+      float4 t[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int i = min(i0 + q * nthr, n4 - 1);
+        const float* lay = kvb + static_cast<size_t>(i / kv4) * r.Gk * r.kvdim;
+        t[q] = *reinterpret_cast<const float4*>(lay + src + (i % kv4) * 4);
+      }
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int i = i0 + q * nthr;
+        if (i < n4) {
+          float* lay = kvb + static_cast<size_t>(i / kv4) * r.Gk * r.kvdim;
+          *reinterpret_cast<float4*>(lay + dst + (i % kv4) * 4) = t[q];
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
   extern __shared__ float4 row_dyn[];
   __shared__ SelSmem S;
@@ -1078,7 +1113,9 @@ __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
     float zv[VPT];
     load_row<VPT>(r.dlogits + row * r.V, zv);  // before the state: the row always exists
     const StreamState st = r.st[b];
+    const int pend = r.ncode[static_cast<size_t>(b) * 8];
     if (st.mode != kModeSpec) return;
+    if (pend > 0) tree_kv_move(r, b, pend >> 8, pend & 0xFF, d - 1);
     float* x0 = r.X + static_cast<size_t>(b) * r.R * r.H;
     if (d > st.gamma) {  // no node this round at this depth: only row 0 to fill
       if (d == 1) embed_row(r, st.s, st.last, x0);
@@ -1449,32 +1486,13 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
       if (leaf) ++cnt_s.bonus;
       st_s.s = s + n;
     }
-    // the accepted nodes' K/V: slot G + a - 1 -> position s + 1 + dep[a],
-    // every layer, K and V
-    // (float4 pieces, every load of a node before its stores)
-    float* kvb = r.kv + static_cast<size_t>(b) * r.kv_sb;
-    const int kv4 = r.kvdim / 4, n4 = 2 * r.L * kv4;
-    for (int a = v; a > 0; a = par_s[a]) {
-      const size_t src = static_cast<size_t>(r.G + a - 1) * r.kvdim;
-      const size_t dst = static_cast<size_t>(s + 1 + dep_s[a]) * r.kvdim;
-      for (int i0 = tid; i0 < n4; i0 += 8 * kBlock) {
-        float4 t[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int i = min(i0 + q * kBlock, n4 - 1);
-          const float* lay = kvb + static_cast<size_t>(i / kv4) * r.Gk * r.kvdim;
-          t[q] = *reinterpret_cast<const float4*>(lay + src + (i % kv4) * 4);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int i = i0 + q * kBlock;
-          if (i < n4) {
-            float* lay = kvb + static_cast<size_t>(i / kv4) * r.Gk * r.kvdim;
-            *reinterpret_cast<float4*>(lay + dst + (i % kv4) * 4) = t[q];
-          }
-        }
-      }
-    }
+  }
+  // the accepted nodes' K/V move to their positions in the next round's draft
+  // kernel: ncode[b][0] = s << 8 | v, or 0 when nothing moves (no node
+  // accepted, a prefill round, or the frame complete)
+  if (tid == 0) {
+    const bool move = spec && v > 0 && s + n < r.G - 1;
+    r.ncode[static_cast<size_t>(b) * 8] = move ? (s << 8) | v : 0;
   }
   if (tid == 0 && st_s.s >= r.G - 1) {  // frame complete
     if (c.out_flags) c.out_flags[fb] = st_s.flags;

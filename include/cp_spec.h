@@ -169,9 +169,13 @@ int cp_spec_get_stats(const cp_spec_stats* d_stats, void* stream,
                       cp_spec_stats* host_out);
 
 /* ---- component entry points: one step of the round each ----------------
- * They run exactly the kernels cp_spec_decode_frames runs, on caller data,
- * so each step can be checked on its own.  They use the handle's workspace
- * as scratch: calls on one handle must not overlap. */
+ * Each runs the code cp_spec_decode_frames runs for that step, on caller
+ * data, so each step can be checked on its own: head_logits and
+ * decoder_forward launch the round's own projection, attention and head
+ * kernels; topk_sample, accept and walk_step launch thin kernels around the
+ * round's device functions (the top-k softmax and inverse-CDF draw, the
+ * acceptance walk step and the chain outcome scan).  They use the handle's
+ * workspace as scratch: calls on one handle must not overlap. */
 
 /* Stacked-head logits (draft GEMV, guide "Why the draft is free"; per-row
  * verify heads, guide "Limitations"):
@@ -199,8 +203,10 @@ int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows,
 /* Accept scan of one round per stream (guide, "How a round works", step 3):
  *   for t = 1..gamma[b]: accept d_t iff u_accept[b][t-1] < p[t-1](d_t) /
  *   q[t-1](d_t) (float32); at the first rejection emit
- *   Sample(max(0, p[t-1] - q[t-1]), u_target[b][t-1]) and stop; if all are
- *   accepted emit Sample(p[gamma], u_target[b][gamma]).
+ *   Sample(max(0, p[t-1] - q[t-1]), u_target[b][t-1]) (p[t-1] itself when
+ *   that residual is all zero) and stop; if all are accepted emit
+ *   Sample(p[gamma], u_target[b][gamma]).  Sample is the float32 inverse CDF
+ *   over the positive entries in ascending code order.
  * Greedy handles: d_q and the uniforms are ignored, d_p holds target logits
  * rows and the argmax-equality rule applies.
  *   d_gamma [B] i32 in 0..width; d_draft [B][width] i32;
@@ -208,12 +214,44 @@ int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows,
  *   d_u_accept [B][width] f32; d_u_target [B][width+1] f32;
  *   d_n out [B] i32 (codes committed, 1..gamma+1);
  *   d_codes out [B][width+1] i32 (the committed codes, in depth order);
- *   d_flags out [B] u32 nullable (bit t-1: near tie at offset t). */
+ *   d_flags out [B] u32 nullable (bit t-1: near tie at offset t, either the
+ *   accept test of a tested offset or the CDF of the committed draw).
+ * Every row is decided in parallel by the step the decode round's target
+ * kernel takes (one child per row), then the outcome scan of its accept
+ * kernel; the rows' steps go through the workspace.
+ * Errors: EINVAL for n_streams outside 0..max_streams, width outside 0..7,
+ * null pointers. */
 int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width,
                    const int32_t* d_gamma, const int32_t* d_draft,
                    const float* d_q, const float* d_p,
                    const float* d_u_accept, const float* d_u_target,
                    int32_t* d_n, int32_t* d_codes, uint32_t* d_flags);
+
+/* One node's step of the tree walk ("RVQ Position Aware ...", section 2.2,
+ * Figure 2: the standard acceptance rule with residual resampling applied
+ * along the tree), the step the decode round's target kernel takes for every
+ * tree row.  For each row i, with p' = p[i] and q = q[i] (the draft
+ * distribution of the children's depth):
+ *   for k = 0..n_children[i]-1: x = children[i][k]; accept x iff
+ *     u_accept[i][k] < p'(x) / q(x) (float32) and stop; else p' <-
+ *     max(0, p' - q) (kept when nothing stays positive), divided by its
+ *     sequential float32 sum in ascending code order when another child
+ *     follows;
+ *   none accepted: code = Sample(p', u_target[i]).
+ *   d_p, d_q [n][V] f32; d_n_children [n] i32 (clamped to 0..max_children);
+ *   d_children [n][max_children] i32; d_u_accept [n][max_children] f32;
+ *   d_u_target [n] f32;
+ *   d_accepted out [n] i32: index of the accepted child, or -1;
+ *   d_codes out [n] i32: the accepted child's code, or the draw;
+ *   d_flags out [n] u32 nullable (CP_SPEC_FLAG_ACCEPT for any test within
+ *   1e-5 of its uniform, CP_SPEC_FLAG_CDF for the draw).
+ * Errors: EINVAL for n_rows < 0, max_children outside 1..64, null pointers;
+ * EUNSUPPORTED on a greedy handle. */
+int cp_spec_walk_step(cp_spec* h, void* stream, int32_t n_rows,
+                      int32_t max_children, const float* d_p, const float* d_q,
+                      const int32_t* d_n_children, const int32_t* d_children,
+                      const float* d_u_accept, const float* d_u_target,
+                      int32_t* d_accepted, int32_t* d_codes, uint32_t* d_flags);
 
 /* One causal decoder pass over rows_per_stream rows of each stream (the
  * verify pass, guide "How a round works", step 2):

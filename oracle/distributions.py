@@ -60,16 +60,90 @@ def topk_support(z: np.ndarray, k: int):
     return np.sort(order[:k]), gap < EPS_GAP
 
 
-def topk_softmax(z: np.ndarray, temperature, k: int):
-    """TopKSoftmax(z; T, k) -> (dense float32 probabilities [V], topk flag)."""
-    z = np.asarray(z, dtype=np.float32)
-    support, flag = topk_support(z, k)
+def _softmax_on(z: np.ndarray, support, temperature) -> np.ndarray:
+    """exp((z_i - max) / T) normalised over ``support``, zero elsewhere."""
     zs = z[support].astype(np.float64)
     m = zs.max()
     e = np.exp((zs - m) / float(np.float32(temperature)))
     p = np.zeros(z.shape[0], dtype=np.float32)
     p[support] = (e / e.sum()).astype(np.float32)
-    return p, flag
+    return p
+
+
+def topk_softmax(z: np.ndarray, temperature, k: int):
+    """TopKSoftmax(z; T, k) -> (dense float32 probabilities [V], topk flag)."""
+    z = np.asarray(z, dtype=np.float32)
+    support, flag = topk_support(z, k)
+    return _softmax_on(z, support, temperature), flag
+
+
+# ---- the other outcomes of near-tie decisions ----------------------------
+# A decision flagged as a near tie may come out the other way under another,
+# equally valid float32 rounding of its inputs.  These give the outcomes it
+# could have had instead; tests re-run a frame with one of them to check that
+# a code stream differing from this oracle's is such a rounding difference.
+
+def topk_alternatives(z: np.ndarray, temperature, k: int, limit: int = 8):
+    """TopKSoftmax with one set member a swapped for a non-member b, for the
+    pairs whose logits differ by less than EPS_GAP (closest pairs first, at
+    most ``limit``)."""
+    z = np.asarray(z, dtype=np.float32)
+    V = z.shape[0]
+    if k >= V:
+        return []
+    support, _ = topk_support(z, k)
+    inset = np.zeros(V, dtype=bool)
+    inset[support] = True
+    outside = np.flatnonzero(~inset)
+    pairs = []
+    for a in support:
+        gaps = float(z[a]) - z[outside].astype(np.float64)
+        for b in outside[gaps < EPS_GAP]:
+            pairs.append((float(z[a]) - float(z[b]), int(a), int(b)))
+    pairs.sort()
+    out = []
+    for _, a, b in pairs[:limit]:
+        alt = np.sort(np.concatenate([support[support != a], [b]]))
+        out.append(_softmax_on(z, alt, temperature))
+    return out
+
+
+def argmax_alternatives(z: np.ndarray):
+    """Codes other than the argmax whose logit is within EPS_GAP of it."""
+    z = np.asarray(z, dtype=np.float32)
+    i = int(np.argmax(z))
+    close = np.flatnonzero(float(z[i]) - z.astype(np.float64) < EPS_GAP)
+    return [int(c) for c in close if c != i]
+
+
+def sample_alternatives(w: np.ndarray, u):
+    """The neighbours Sample(w, u) could have chosen instead when its CDF
+    near-tie flag is set: the positive entry before the chosen one when t is
+    within EPS_CDF * sum of their shared boundary, the one after it when the
+    chosen entry's upper boundary is that close."""
+    w = np.asarray(w, dtype=np.float32)
+    u = np.float32(u)
+    ids = np.flatnonzero(w > 0)
+    tot = np.float32(0.0)
+    for i in ids:
+        tot = np.float32(tot + w[i])
+    t = np.float32(u * tot)
+    eps = float(tot) * EPS_CDF
+    run = np.float32(0.0)
+    before = run
+    for pos, i in enumerate(ids):
+        before = run
+        run = np.float32(run + w[i])
+        if t < run:
+            out = []
+            if pos > 0 and abs(float(t) - float(before)) < eps:
+                out.append(int(ids[pos - 1]))
+            if pos + 1 < ids.size and abs(float(run) - float(t)) < eps:
+                out.append(int(ids[pos + 1]))
+            return out
+    if ids.size > 1 and abs(float(t) - float(before)) < eps:
+        return [int(ids[-2])]
+    return []
 
 
 def argmax_with_gap(z: np.ndarray):
@@ -129,13 +203,19 @@ def residual_or_target(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     return r if np.any(r > 0) else np.asarray(p, np.float32)
 
 
-def accept_scan(drafts, qs, ps, u_accept, u_target):
+def _keep(kind, t, near, default, alternatives):
+    return default
+
+
+def accept_scan(drafts, qs, ps, u_accept, u_target, choose=_keep):
     """Stochastic accept scan of one round (guide, "How a round works",
     step 3).  ``drafts[t-1]`` was drawn from ``qs[t-1]``; ``ps[r]`` is the
     verified distribution of row r (row t-1 scores draft t, row gamma the
     bonus position).  ``u_accept(t)`` and ``u_target(t)`` give the uniforms
     of offset t.  Returns (emitted codes, drafts accepted, [(offset, kind)]
-    near ties) where kind is 'accept' or 'cdf'."""
+    near ties) where kind is 'accept' or 'cdf'.  ``choose(kind, t, near,
+    outcome, alternatives)`` sees every decision and returns the outcome to
+    use (by default the computed one)."""
     gamma = len(drafts)
     emitted, near = [], []
     for t in range(1, gamma + 1):
@@ -143,18 +223,22 @@ def accept_scan(drafts, qs, ps, u_accept, u_target):
         ok, f_acc = accept_test(ps[t - 1][d], qs[t - 1][d], u_accept(t))
         if f_acc:
             near.append((t, "accept"))
+        ok = choose("accept", t, f_acc, ok, [not ok])
         if ok:
             emitted.append(d)
             continue
-        code, f_cdf = sample(residual_or_target(ps[t - 1], qs[t - 1]),
-                             u_target(t))
+        w = residual_or_target(ps[t - 1], qs[t - 1])
+        code, f_cdf = sample(w, u_target(t))
         if f_cdf:
             near.append((t, "cdf"))
+            code = choose("cdf", t, f_cdf, code, sample_alternatives(w, u_target(t)))
         emitted.append(code)
         return emitted, t - 1, near
     code, f_cdf = sample(ps[gamma], u_target(gamma + 1))
     if f_cdf:
         near.append((gamma + 1, "cdf"))
+        code = choose("cdf", gamma + 1, f_cdf, code,
+                      sample_alternatives(ps[gamma], u_target(gamma + 1)))
     emitted.append(code)
     return emitted, gamma, near
 

@@ -63,19 +63,46 @@ def new_stats() -> dict:
 
 
 class _Frame:
-    """Book-keeping of one frame: codes, near-tie flags (bit j = a flagged
-    decision at depth j) and counters."""
+    """Book-keeping of one frame: codes, near-tie flags, counters, and the
+    log of its near-tie decisions.
 
-    def __init__(self, G, c0, stats):
+    Flags: bit j is set for a near tie at depth j in a decision the frame's
+    outcome used (the prefill's; in a round, drafts 1..n_acc + 1 and target
+    rows 0..n_acc, the accept tests that were made and the committed draw).
+    Decisions of drafts and rows past the first rejection did not shape any
+    committed code, so they are not flagged.
+
+    Log: every decision flagged as a near tie, used or not, in the order the
+    frame takes them, with the outcomes it could have had instead.  A frame
+    re-run with ``force = (i, a)`` takes alternative a at near tie i and is
+    otherwise the same computation; the tests use it to show that a code
+    stream that differs from this oracle's is explained by one such
+    rounding-level flip."""
+
+    def __init__(self, G, c0, stats, force=None):
         self.codes = np.full(G, -1, dtype=np.int32)
         self.codes[0] = c0
         self.flags = 0
         self.stats = stats
+        self.force = force
+        self.log = []
 
     def flag(self, kind: str, depth: int, hit: bool):
         if hit:
             self.flags |= 1 << depth
             self.stats["near_tie_" + kind] += 1
+
+    def choose(self, kind: str, depth: int, near: bool, outcome, alternatives):
+        """The outcome of a decision; ``alternatives`` (a list, or a callable
+        giving one) are its other outcomes when ``near``."""
+        if not near:
+            return outcome
+        alts = alternatives() if callable(alternatives) else alternatives
+        i = len(self.log)
+        self.log.append((depth, kind, len(alts)))
+        if self.force is not None and self.force[0] == i and self.force[1] < len(alts):
+            return alts[self.force[1]]
+        return outcome
 
 
 def draft_logits(model, j: int, t: int, h) -> np.ndarray:
@@ -89,87 +116,120 @@ def draft_logits(model, j: int, t: int, h) -> np.ndarray:
 
 
 def _dist(model, fr, j, z, dp):
-    """Processed distribution for depth j from logits z (stochastic mode)."""
-    p, f_topk = dist.topk_softmax(z, dp["temperature"], dp["top_k"])
-    if dp["top_k"] < model.V:
-        fr.flag("topk", j, f_topk)
-    return p
+    """Processed distribution for depth j from logits z (stochastic mode):
+    (p, top-k near-tie flag)."""
+    T, k = dp["temperature"], dp["top_k"]
+    p, f = dist.topk_softmax(z, T, k)
+    f = bool(f and k < model.V)
+    p = fr.choose("topk", j, f, p, lambda: dist.topk_alternatives(z, T, k))
+    return p, f
 
 
 def _greedy(fr, j, z):
-    code, f_arg = dist.argmax_with_gap(z)
-    fr.flag("argmax", j, f_arg)
-    return code
+    code, f = dist.argmax_with_gap(z)
+    code = fr.choose("argmax", j, f, code, lambda: dist.argmax_alternatives(z))
+    return code, f
 
 
-def _draw(fr, w, seed, depth, purpose):
-    code, f_cdf = dist.sample(w, uniform(seed, depth, purpose))
-    fr.flag("cdf", depth, f_cdf)
-    return code
+def _draw(fr, w, seed, depth, purpose, index=0):
+    u = uniform(seed, depth, purpose, index)
+    code, f = dist.sample(w, u)
+    code = fr.choose("cdf", depth, f, code, lambda: dist.sample_alternatives(w, u))
+    return code, f
+
+
+def _prefill(model, fr, dp, h_frame, c0, seed, stats):
+    """Positions 0 (talker hidden state) and 1 (E_0[c_0]); c_1 from head_1."""
+    kv = model.new_kv()
+    outs = model.forward_rows([np.asarray(h_frame, np.float64),
+                               model.embed_row(0, c0)], [0, 1], kv)
+    stats["prefill_passes"] += 1
+    h = outs[1]
+    if model.G > 1:
+        z = model.logits(1, h)
+        if dp["greedy"]:
+            fr.codes[1], f = _greedy(fr, 1, z)
+            fr.flag("argmax", 1, f)
+        else:
+            p, f = _dist(model, fr, 1, z, dp)
+            fr.flag("topk", 1, f)
+            fr.codes[1], f = _draw(fr, p, seed, 1, PURPOSE_TARGET)
+            fr.flag("cdf", 1, f)
+    return kv, h
 
 
 def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
-                 stats: dict | None = None, trace: list | None = None):
+                 stats: dict | None = None, trace: list | None = None,
+                 force=None, log: list | None = None):
     """Decode one frame.  ``dp`` = {verify_size, greedy, temperature, top_k}.
 
     Returns (codes [G] int32 with codes[0] = c0, near-tie flag bitmask).
-    ``trace``, if given, receives (s, h_s, drafts, n) for every round.
+    ``trace``, if given, receives (s, h_s, drafts, n) for every round;
+    ``log``, if given, receives the frame's near-tie decisions (depth, kind,
+    number of alternatives); ``force`` = (i, a) takes alternative a at near
+    tie i (see _Frame).
     """
     stats = new_stats() if stats is None else stats
     G = model.G
     N = int(dp["verify_size"])
     greedy = bool(dp["greedy"])
-    fr = _Frame(G, c0, stats)
-    kv = model.new_kv()
-
-    # prefill: positions 0 (talker hidden state) and 1 (E_0[c_0])
-    outs = model.forward_rows([np.asarray(h_frame, np.float64),
-                               model.embed_row(0, c0)], [0, 1], kv)
-    stats["prefill_passes"] += 1
-    h = outs[1]
-    if G > 1:
-        if greedy:
-            fr.codes[1] = _greedy(fr, 1, model.logits(1, h))
-        else:
-            fr.codes[1] = _draw(fr, _dist(model, fr, 1, model.logits(1, h),
-                                          dp), seed, 1, PURPOSE_TARGET)
+    fr = _Frame(G, c0, stats, force)
+    kv, h = _prefill(model, fr, dp, h_frame, c0, seed, stats)
     s = 1
 
     while s < G - 1:
         gamma = 0 if N == 0 else min(N - 1, G - 2 - s)
-        # (1) draft from h_s (+ b_t) with the later heads
+        # (1) draft from h_s (+ b_t) with the later heads; flags wait for the
+        # outcome (only the drafts it used are flagged)
         h_s = h
-        drafts, qs = [], []
+        drafts, qs, dflags = [], [], []
         for t in range(1, gamma + 1):
             z = draft_logits(model, s + t, t, h)
             if greedy:
-                drafts.append(_greedy(fr, s + t, z))
+                d, f = _greedy(fr, s + t, z)
+                dflags.append(["argmax"] if f else [])
             else:
-                q = _dist(model, fr, s + t, z, dp)
+                q, f1 = _dist(model, fr, s + t, z, dp)
                 qs.append(q)
-                drafts.append(_draw(fr, q, seed, s + t, PURPOSE_DRAFT))
+                d, f2 = _draw(fr, q, seed, s + t, PURPOSE_DRAFT)
+                dflags.append(["topk"] * f1 + ["cdf"] * f2)
+            drafts.append(d)
         # (2) verify: one causal block over the committed depth + drafts
         rows = [model.embed_row(s, int(fr.codes[s]))]
         rows += [model.embed_row(s + t, d) for t, d in enumerate(drafts, 1)]
         outs = model.forward_rows(rows, [s + 1 + r for r in range(gamma + 1)],
                                   kv)
         # (3) accept
+        rflags = []
         if greedy:
-            target = [_greedy(fr, s + 1 + r, model.logits(s + 1 + r, outs[r]))
-                      for r in range(gamma + 1)]
+            target = []
+            for r in range(gamma + 1):
+                a, f = _greedy(fr, s + 1 + r, model.logits(s + 1 + r, outs[r]))
+                target.append(a)
+                rflags.append(["argmax"] if f else [])
             rnd = dist.verify_greedy(drafts, target)
             emitted = list(rnd.emitted)
             n_acc = len(rnd.accepted)
         else:
-            ps = [_dist(model, fr, s + 1 + r, model.logits(s + 1 + r, outs[r]),
-                        dp)
-                  for r in range(gamma + 1)]
+            ps = []
+            for r in range(gamma + 1):
+                p, f = _dist(model, fr, s + 1 + r,
+                             model.logits(s + 1 + r, outs[r]), dp)
+                ps.append(p)
+                rflags.append(["topk"] if f else [])
             emitted, n_acc, near = dist.accept_scan(
                 drafts, qs, ps,
                 lambda t: uniform(seed, s + t, PURPOSE_ACCEPT),
-                lambda t: uniform(seed, s + t, PURPOSE_TARGET))
+                lambda t: uniform(seed, s + t, PURPOSE_TARGET),
+                lambda kind, t, nr, out, alts: fr.choose(kind, s + t, nr, out, alts))
             for t, kind in near:
                 fr.flag(kind, s + t, True)
+        for t in range(1, min(n_acc + 1, gamma) + 1):
+            for kind in dflags[t - 1]:
+                fr.flag(kind, s + t, True)
+        for r in range(n_acc + 1):
+            for kind in rflags[r]:
+                fr.flag(kind, s + 1 + r, True)
         # (4) commit and truncate
         n = len(emitted)
         fr.codes[s + 1: s + 1 + n] = emitted
@@ -188,6 +248,8 @@ def decode_frame(model, dp: dict, h_frame, c0: int, seed: int,
 
     stats["frames"] += 1
     stats["codes"] += G - 1
+    if log is not None:
+        log.extend(fr.log)
     return fr.codes, fr.flags
 
 

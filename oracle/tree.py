@@ -58,7 +58,7 @@ import numpy as np
 
 from . import distributions as dist
 from .philox import PURPOSE_ACCEPT, PURPOSE_DRAFT, PURPOSE_TARGET, uniform
-from .spec import _Frame, _dist, _draw, _greedy, draft_logits, new_stats
+from .spec import _Frame, _dist, _draw, _greedy, _prefill, draft_logits, new_stats
 
 
 class Tree:
@@ -95,37 +95,68 @@ def normalise(r) -> np.ndarray:
 
 def _ranked(fr, depth, z, m):
     """The m highest draft logits' codes (logit descending, code ascending),
-    flagging a gap under EPS_GAP among the first m + 1 at ``depth``."""
+    and whether a gap under EPS_GAP separates two of the first m + 1 (then
+    the ranking could come out with those two swapped)."""
     z = np.asarray(z, dtype=np.float32)
     order = np.lexsort((np.arange(z.shape[0]), -z))
     top = z[order[: m + 1]].astype(np.float64)
-    fr.flag("argmax", depth, bool(np.any(np.abs(np.diff(top)) < dist.EPS_GAP)))
-    return [int(c) for c in order[:m]]
+    near_at = [i for i in range(len(top) - 1) if top[i] - top[i + 1] < dist.EPS_GAP]
+    ranked = [int(c) for c in order[: m + 1]]
+
+    def alts():
+        out = []
+        for i in near_at:
+            r = list(ranked)
+            r[i], r[i + 1] = r[i + 1], r[i]
+            out.append(r[:m])
+        return out
+
+    return fr.choose("argmax", depth, bool(near_at), ranked[:m], alts), bool(near_at)
+
+
+def walk_step(p, q, children, u_accept, u_target, choose=None):
+    """One node's step of the walk: the node's children (codes
+    ``children[k]``, drawn from ``q``) are tested in order against the node's
+    target distribution ``p``: child k is accepted iff u_accept(k) <
+    p'(x)/q(x) (float32), p' = p for the first child; after a rejection p'
+    becomes max(0, p' - q) (p' kept when that is all zero), divided by its
+    sequential float32 sum when another child follows.  With none accepted
+    the node draws Sample(p', u_target).  Returns (index of the accepted
+    child or None, its code or the draw, [near-tie kinds]).  ``choose`` (as in
+    accept_scan) sees every decision."""
+    choose = choose or (lambda kind, k, near, out, alts: out)
+    near = []
+    p = np.asarray(p, np.float32)
+    for k, x in enumerate(children):
+        ok, f = dist.accept_test(p[x], q[x], u_accept(k))
+        if f:
+            near.append("accept")
+        ok = choose("accept", k, f, ok, [not ok])
+        if ok:
+            return k, int(x), near
+        p = dist.residual_or_target(p, q)
+        if k + 1 < len(children):
+            p = normalise(p)
+    code, f = dist.sample(p, u_target)
+    if f:
+        near.append("cdf")
+        code = choose("cdf", len(children), f, code, dist.sample_alternatives(p, u_target))
+    return None, int(code), near
 
 
 def decode_frame_tree(model, dp: dict, tree: Tree, h_frame, c0: int, seed: int,
-                      stats: dict | None = None, trace: list | None = None):
+                      stats: dict | None = None, trace: list | None = None,
+                      force=None, log: list | None = None):
     """Decode one frame with a tree window.  ``dp`` = {greedy, temperature,
     top_k} (the tree replaces verify_size).  Returns (codes [G] int32,
-    near-tie flag bitmask).  ``trace``, if given, receives (s, {node: code},
-    n) for every round."""
+    near-tie flag bitmask: the decisions of the walk's rows and of the draft
+    depths it tested).  ``trace``, if given, receives (s, {node: code}, n)
+    for every round; ``log`` and ``force`` as in spec.decode_frame."""
     stats = new_stats() if stats is None else stats
     G = model.G
     greedy = bool(dp["greedy"])
-    fr = _Frame(G, c0, stats)
-    kv = model.new_kv()
-
-    # prefill: positions 0 (talker hidden state) and 1 (E_0[c_0])
-    outs = model.forward_rows([np.asarray(h_frame, np.float64),
-                               model.embed_row(0, c0)], [0, 1], kv)
-    stats["prefill_passes"] += 1
-    h = outs[1]
-    if G > 1:
-        if greedy:
-            fr.codes[1] = _greedy(fr, 1, model.logits(1, h))
-        else:
-            fr.codes[1] = _draw(fr, _dist(model, fr, 1, model.logits(1, h), dp), seed, 1,
-                                PURPOSE_TARGET)
+    fr = _Frame(G, c0, stats, force)
+    kv, h = _prefill(model, fr, dp, h_frame, c0, seed, stats)
     s = 1
 
     while s < G - 1:
@@ -134,21 +165,26 @@ def decode_frame_tree(model, dp: dict, tree: Tree, h_frame, c0: int, seed: int,
         live = set(nodes)
         kids = {v: [c for c in tree.children[v] if c in live] for v in [0] + nodes}
         D = max([tree.depth[i] for i in nodes], default=0)
-        # (1) candidates of every node from h_s (+ b_d)
-        q, code = {}, {}
+        # (1) candidates of every node from h_s (+ b_d); each depth's flags
+        # wait for the walk
+        q, code, dflags = {}, {}, {}
         for d in range(1, D + 1):
             z = draft_logits(model, s + d, d, h)
             at_d = [i for i in nodes if tree.depth[i] == d]
             if greedy:
                 m = max(len(kids[tree.parent[i]]) for i in at_d)
-                ranked = _ranked(fr, s + d, z, m)
+                ranked, f = _ranked(fr, s + d, z, m)
+                dflags[d] = ["argmax"] * f
                 for i in at_d:
                     code[i] = ranked[kids[tree.parent[i]].index(i)]
             else:
-                q[d] = _dist(model, fr, s + d, z, dp)
+                q[d], f = _dist(model, fr, s + d, z, dp)
+                dflags[d] = ["topk"] * f
+                fcdf = False
                 for j, i in enumerate(at_d):
-                    code[i], f = dist.sample(q[d], uniform(seed, s + d, PURPOSE_DRAFT, j))
-                    fr.flag("cdf", s + d, f)
+                    code[i], f = _draw(fr, q[d], seed, s + d, PURPOSE_DRAFT, j)
+                    fcdf |= f
+                dflags[d] += ["cdf"] * fcdf
         # (2) verify: the root row and every node, each over its root path
         hid, kvs = {}, {}
         kv0 = copy.deepcopy(kv)
@@ -162,20 +198,19 @@ def decode_frame_tree(model, dp: dict, tree: Tree, h_frame, c0: int, seed: int,
         stats["rounds"] += 1
         # (3) every row's target decision (argmax, or p with its top-k
         # flag), then the walk down the tree
-        target = {}
+        target, rflag = {}, {}
         for v in [0] + nodes:
             j = s + tree.depth[v] + 1
             z = model.logits(j, hid[v])
             if greedy:
-                t, f = dist.argmax_with_gap(z)
-                fr.flag("argmax", j, f)
-                target[v] = t
+                target[v], rflag[v] = _greedy(fr, j, z)
             else:
-                target[v] = _dist(model, fr, j, z, dp)
+                target[v], rflag[v] = _dist(model, fr, j, z, dp)
         v, emitted = 0, []
         while True:
             d1 = tree.depth[v] + 1
             j = s + d1
+            fr.flag("argmax" if greedy else "topk", j, rflag[v])
             if greedy:
                 t = target[v]
                 nxt = next((c for c in kids[v] if code[c] == t), None)
@@ -184,29 +219,22 @@ def decode_frame_tree(model, dp: dict, tree: Tree, h_frame, c0: int, seed: int,
                     break
                 v = nxt
                 continue
-            p = target[v]
-            nxt = None
-            for k, c in enumerate(kids[v]):
-                x = code[c]
-                ok, f = dist.accept_test(p[x], q[d1][x], uniform(seed, j, PURPOSE_ACCEPT, k))
-                fr.flag("accept", j, f)
-                if ok:
-                    nxt = c
-                    break
-                # the residual: normalised when another child is tested on
-                # it, sampled as it is otherwise (as the chain does)
-                p = dist.residual_or_target(p, q[d1])
-                if k + 1 < len(kids[v]):
-                    p = normalise(p)
-            if nxt is None:
-                c_new, f = dist.sample(p, uniform(seed, j, PURPOSE_TARGET, 0))
-                fr.flag("cdf", j, f)
-                emitted.append(c_new)
+            k, x, near = walk_step(
+                target[v], q.get(d1), [code[c] for c in kids[v]],
+                lambda k: uniform(seed, j, PURPOSE_ACCEPT, k),
+                uniform(seed, j, PURPOSE_TARGET, 0),
+                lambda kind, k, nr, out, alts: fr.choose(kind, j, nr, out, alts))
+            for kind in near:
+                fr.flag(kind, j, True)
+            emitted.append(x)
+            if k is None:
                 break
-            emitted.append(code[nxt])
-            v = nxt
+            v = kids[v][k]
         # (4) commit the path: codes, its K/V, h of its last node
         n = len(emitted)
+        for d in range(1, min(n, D) + 1):
+            for kind in dflags[d]:
+                fr.flag(kind, s + d, True)
         fr.codes[s + 1: s + 1 + n] = emitted
         kv = kvs[v]
         kv.truncate(s + n + 1)
@@ -223,4 +251,6 @@ def decode_frame_tree(model, dp: dict, tree: Tree, h_frame, c0: int, seed: int,
 
     stats["frames"] += 1
     stats["codes"] += G - 1
+    if log is not None:
+        log.extend(fr.log)
     return fr.codes, fr.flags

@@ -88,6 +88,8 @@ _SIGS = {
     "cp_spec_talker_feedback": (C.c_int, [_P, _P, C.c_int32, _P, _P]),
     "cp_spec_accept": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _P]),
+    "cp_spec_walk_step": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P]),
     "cp_spec_decoder_forward": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P,
                                           _P, _P]),
     "cp_spec_time_kernel": (C.c_int, [_P, _P, C.c_int32, C.c_int32,
@@ -259,6 +261,14 @@ class Handle:
             self.h, _stream(stream), B, W, _ptr(gamma), _ptr(draft), _ptr(q),
             _ptr(p), _ptr(u_accept), _ptr(u_target), _ptr(n_out),
             _ptr(codes_out), _ptr(flags_out)))
+
+    def walk_step(self, p, q, n_children, children, u_accept, u_target,
+                  accepted, codes, flags=None, stream=None):
+        n, maxc = int(children.shape[0]), int(children.shape[1])
+        return _check(lib().cp_spec_walk_step(
+            self.h, _stream(stream), n, maxc, _ptr(p), _ptr(q),
+            _ptr(n_children), _ptr(children), _ptr(u_accept), _ptr(u_target),
+            _ptr(accepted), _ptr(codes), _ptr(flags)))
 
     def time_kernel(self, kind: str, n_streams: int, iters: int,
                     stream=None) -> dict:

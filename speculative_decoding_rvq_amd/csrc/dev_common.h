@@ -307,15 +307,6 @@ constexpr double kEpsGap = 1e-4;
 constexpr double kEpsCdf = 1e-5;
 constexpr uint32_t kFlagTopk = 1u, kFlagArgmax = 2u, kFlagCdf = 4u, kFlagAccept = 8u;
 
-// LDS scratch the block sampler needs: compacted support of up to 4096
-// entries (weights, then their running sums).
-struct SampleSmem {
-  int idx[4096];
-  alignas(16) float w[4096];
-  int red[4];
-  int result[2];
-};
-
 // One wave: Sample over the list w[0..total) in list order (entries with
 // w = 0 are skipped, as Sample skips non-positive weights).  Lane 0 turns w
 // into its running sums in place, sequentially in float32; t = u * sum; the
@@ -418,105 +409,6 @@ template <typename IT>
 __device__ __forceinline__ void list_draw(float* w, const IT* idx, int total, float u, int* code, int* near) {
   const ListSums ls = list_prefix(w, total);
   list_search(w, idx, total, ls, u, code, near);
-}
-
-// Wave 0: Sample over the `total` compacted entries of sm (ascending code
-// order); the result goes to sm.result.
-__device__ __forceinline__ void wave0_walk(SampleSmem& sm, int total, float u) {
-  int code, near;
-  list_draw(sm.w, sm.idx, total, u, &code, &near);
-  if (threadIdx.x == 0) {
-    sm.result[0] = code;
-    sm.result[1] = near;
-  }
-}
-
-// Sample(w, u) over a row held in registers, thread t owning codes
-// [t*VPT, (t+1)*VPT): the entries with w_i > 0 in ascending code order, a
-// sequential float32 running sum, t = u * sum, the first entry whose running
-// sum exceeds t.  Every thread gets the code (-1 if no weight is positive)
-// and the CDF near-tie flag through *flag.  sm.red must not be read by the
-// caller between two calls; the rest of sm is free once this returns.
-template <int VPT>
-__device__ __forceinline__ int sample_regs(const float (&wv)[VPT], float u, SampleSmem& sm, bool* flag) {
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  const int base = tid * VPT;
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) cnt += wv[j] > 0.0f ? 1 : 0;
-  const int inc = wave_incl_scan(cnt);
-  if (lane == kWave - 1) sm.red[w] = inc;
-  lds_sync();
-  int off = inc - cnt;
-  for (int i = 0; i < w; ++i) off += sm.red[i];
-  const int total = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    if (wv[j] > 0.0f) {
-      sm.idx[off] = base + j;
-      sm.w[off] = wv[j];
-      ++off;
-    }
-  }
-  if (tid < 32 && total + tid < ((total + 31) & ~31)) sm.w[total + tid] = 0.0f;  // pad for the walk
-  lds_sync();
-  if (tid < kWave) wave0_walk(sm, total, u);
-  lds_sync();
-  *flag = sm.result[1] != 0;
-  return sm.result[0];
-}
-
-// The sequential float32 sum, in ascending code order, of the positive
-// entries of a row held in registers (thread t owning [t*VPT, (t+1)*VPT)).
-// Every thread gets it.  sm is free again once this returns.
-template <int VPT>
-__device__ __forceinline__ float positive_sum_regs(const float (&wv)[VPT], SampleSmem& sm) {
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) cnt += wv[j] > 0.0f ? 1 : 0;
-  const int inc = wave_incl_scan(cnt);
-  if (lane == kWave - 1) sm.red[w] = inc;
-  lds_sync();
-  int off = inc - cnt;
-  for (int i = 0; i < w; ++i) off += sm.red[i];
-  const int total = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    if (wv[j] > 0.0f) sm.w[off++] = wv[j];
-  }
-  lds_sync();
-  if (tid == 0) {
-    float tot = 0.0f;
-    for (int i = 0; i < total; ++i) tot = tot + sm.w[i];
-    sm.result[0] = __float_as_int(tot);
-  }
-  lds_sync();
-  const float tot = __int_as_float(sm.result[0]);
-  lds_sync();  // sm.result and sm.red are reused by the caller's next call
-  return tot;
-}
-
-
-// The same over weights produced by `weight(i)`, i in [0, V), V = 256 * 2^i
-// up to 4096.
-template <typename WF>
-__device__ int block_sample(WF weight, int V, float u, SampleSmem& sm, bool* flag) {
-  auto run = [&](auto vpt) {
-    constexpr int VPT = decltype(vpt)::value;
-    float wv[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) wv[j] = weight(threadIdx.x * VPT + j);
-    return sample_regs<VPT>(wv, u, sm, flag);
-  };
-  switch (V / kBlock) {
-    case 1: return run(std::integral_constant<int, 1>{});
-    case 2: return run(std::integral_constant<int, 2>{});
-    case 4: return run(std::integral_constant<int, 4>{});
-    case 8: return run(std::integral_constant<int, 8>{});
-    case 16: return run(std::integral_constant<int, 16>{});
-    default: return -1;
-  }
 }
 
 }  // namespace cps

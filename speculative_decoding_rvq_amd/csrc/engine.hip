@@ -202,8 +202,10 @@ Layout make_layout(const Shape& s) {
   l.dflags = take(B * W * i4);
   l.tlogits = take(B * R * s.V * f4);
   l.p = take(B * R * s.V * f4);
-  l.tcode = take(B * R * i4);
-  l.tflags = take(B * R * i4);
+  // (also the component accept's per-row scratch, [B][width + 1])
+  const size_t Rt = std::max<size_t>(R, CP_SPEC_MAX_WINDOW);
+  l.tcode = take(B * Rt * i4);
+  l.tflags = take(B * Rt * i4);
   l.rope = take(static_cast<size_t>(s.G) * (s.d / 2) * sizeof(float2));
   l.packed = take(packed_elems(s) * sizeof(uint16_t));
   // pre-split activation planes (three bf16 per value) and partial sums of
@@ -784,7 +786,7 @@ int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width, c
                    const float* d_u_accept, const float* d_u_target, int32_t* d_n, int32_t* d_codes,
                    uint32_t* d_flags) {
   if (!h) return fail(CP_SPEC_EINVAL, "null handle");
-  if (n_streams < 0 || width < 0 || width > CP_SPEC_MAX_WINDOW - 1)
+  if (n_streams < 0 || n_streams > h->sh.maxB || width < 0 || width > CP_SPEC_MAX_WINDOW - 1)
     return fail(CP_SPEC_EINVAL, "n_streams/width out of range");
   if (n_streams == 0) return CP_SPEC_OK;
   if (!d_gamma || !d_draft || !d_p || !d_n || !d_codes || (!h->sh.greedy && (!d_q || !d_u_accept || !d_u_target)))
@@ -793,7 +795,28 @@ int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width, c
   a.B = n_streams; a.W = width; a.V = h->sh.V; a.greedy = h->sh.greedy; a.gamma = d_gamma;
   a.draft = d_draft; a.q = d_q; a.p = d_p; a.u_acc = d_u_accept; a.u_tgt = d_u_target; a.n_out = d_n;
   a.codes_out = d_codes; a.flags_out = d_flags;
+  a.tcode = h->at<int>(h->lo.tcode);  // the round's own per-row outcome buffers
+  a.tflags = h->at<uint32_t>(h->lo.tflags);
   CPS_HIP(launch_accept_rows(a, static_cast<hipStream_t>(stream)));
+  return CP_SPEC_OK;
+}
+
+int cp_spec_walk_step(cp_spec* h, void* stream, int32_t n_rows, int32_t max_children, const float* d_p,
+                      const float* d_q, const int32_t* d_n_children, const int32_t* d_children,
+                      const float* d_u_accept, const float* d_u_target, int32_t* d_accepted, int32_t* d_codes,
+                      uint32_t* d_flags) {
+  if (!h) return fail(CP_SPEC_EINVAL, "null handle");
+  if (h->sh.greedy) return fail(CP_SPEC_EUNSUPPORTED, "walk_step decodes stochastically only");
+  if (n_rows < 0 || max_children < 1 || max_children > 64)
+    return fail(CP_SPEC_EINVAL, "n_rows < 0 or max_children outside 1..64");
+  if (n_rows == 0) return CP_SPEC_OK;
+  if (!d_p || !d_q || !d_n_children || !d_children || !d_u_accept || !d_u_target || !d_accepted || !d_codes)
+    return fail(CP_SPEC_EINVAL, "null pointer");
+  WalkArgs a{};
+  a.n = n_rows; a.V = h->sh.V; a.maxc = max_children; a.p = d_p; a.q = d_q; a.nchild = d_n_children;
+  a.child = d_children; a.u_acc = d_u_accept; a.u_tgt = d_u_target; a.acc_out = d_accepted;
+  a.code_out = d_codes; a.flags_out = d_flags;
+  CPS_HIP(launch_walk_rows(a, static_cast<hipStream_t>(stream)));
   return CP_SPEC_OK;
 }
 

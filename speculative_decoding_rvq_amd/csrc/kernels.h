@@ -101,7 +101,7 @@ struct TopkArgs {
   int n_rows;
 };
 
-struct AcceptArgs {  // component accept
+struct AcceptArgs {  // component accept of a chain round
   int B, W, V, greedy;
   const int* gamma;
   const int* draft;
@@ -112,6 +112,21 @@ struct AcceptArgs {  // component accept
   int* n_out;
   int* codes_out;
   uint32_t* flags_out;
+  int* tcode;         // scratch [B][W + 1]: each row's step
+  uint32_t* tflags;   // scratch [B][W + 1]
+};
+
+struct WalkArgs {  // component walk step: one node row each
+  int n, V, maxc;
+  const float* p;       // [n][V]
+  const float* q;       // [n][V]
+  const int* nchild;    // [n]
+  const int* child;     // [n][maxc]
+  const float* u_acc;   // [n][maxc]
+  const float* u_tgt;   // [n]
+  int* acc_out;
+  int* code_out;
+  uint32_t* flags_out;  // nullable
 };
 
 // Per-stream state of the round engine.
@@ -207,7 +222,9 @@ hipError_t launch_attention(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int rows, int H, float eps,
                                hipStream_t s);
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s);
+// Every row's step of the walk, then each stream's outcome (two kernels).
 hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s);
+hipError_t launch_walk_rows(const WalkArgs& a, hipStream_t s);
 hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t s);
 hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s);

@@ -5,6 +5,7 @@
 #include "dev_common.h"
 #include "kernels.h"
 #include "topk_impl.h"
+#include "accept_impl.h"
 
 namespace cps {
 
@@ -278,134 +279,156 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Accept scan of one stream's round.  Decisions are taken by thread 0 in
-// float32 and broadcast; sampling uses the block sampler.  uacc[t-1] and
-// utgt[t-1] are the uniforms of offset t (acceptance test, target draw); a
-// callback gives the target argmax of verify row r when greedy.  Returns the number of codes
-// committed; codes[0..n) are the committed codes; accept_near[t-1] and
-// cdf_near[t-1] report near ties at offset t.
+// Component accept (cp_spec_accept, cp_spec_walk_step): the decode round's
+// acceptance functions on caller data.  The caller hands over dense rows;
+// the positive entries of p become the list walk_step reads (the decode
+// round's target kernel hands it the top-k list, which holds the same
+// positive entries in the same order).
 
-template <typename TA>
-__device__ int accept_scan(int gamma, const int* draft, const float* q, const float* p, int V,
-                           bool greedy, const float* uacc, const float* utgt, TA targmax, int* codes,
-                           uint32_t* accept_near, uint32_t* cdf_near, int* n_acc_out,
-                           SampleSmem& samp, int* dec, float* pq) {
-  if (greedy) {
-    int t = 0;
-    while (t < gamma && draft[t] == targmax(t)) {
-      codes[t] = draft[t];
-      ++t;
+// The positive entries of a dense row held in registers (thread t owning
+// codes [t*VPT, (t+1)*VPT)) as a list in ascending code order: L.lw the
+// weights, L.lidx the codes, zero from the count up to the next multiple of
+// 32.  Every thread gets the count; the list is published by a barrier.
+template <int VPT>
+__device__ int dense_to_list(const float (&pv)[VPT], const RowLds& L, int* red) {
+  const int base = threadIdx.x * VPT;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) cnt += pv[j] > 0.0f ? 1 : 0;
+  int total;
+  int off = block_exclusive_scan(cnt, red, &total);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j)
+    if (pv[j] > 0.0f) {
+      L.lw[off] = pv[j];
+      L.lidx[off] = static_cast<uint16_t>(base + j);
+      ++off;
     }
-    codes[t] = targmax(t);
-    *n_acc_out = t;
-    return t + 1;
-  }
-  // p(d_t) and q(d_t) of every offset in one round trip
-  if (threadIdx.x < gamma) {
-    const int t = threadIdx.x + 1;
-    const int d = draft[t - 1];
-    const bool inr = d >= 0 && d < V;
-    pq[2 * threadIdx.x] = inr ? p[static_cast<size_t>(t - 1) * V + d] : 0.0f;
-    pq[2 * threadIdx.x + 1] = inr ? q[static_cast<size_t>(t - 1) * V + d] : 1.0f;
-  }
-  __syncthreads();
-  for (int t = 1; t <= gamma; ++t) {
-    const int d = draft[t - 1];
-    if (threadIdx.x == 0) {
-      const float pd = pq[2 * (t - 1)];
-      const float qd = pq[2 * (t - 1) + 1];
-      const float ratio = pd / qd;
-      const float uu = uacc[t - 1];
-      dec[0] = uu < ratio ? 1 : 0;
-      dec[1] = fabs(static_cast<double>(uu) - static_cast<double>(ratio)) < kEpsAccept ? 1 : 0;
-    }
-    __syncthreads();
-    const int ok = dec[0];
-    accept_near[t - 1] = dec[1];
-    __syncthreads();
-    if (ok) {
-      codes[t - 1] = d;
-      continue;
-    }
-    const float* pr = p + static_cast<size_t>(t - 1) * V;
-    const float* qr = q + static_cast<size_t>(t - 1) * V;
-    bool near = false;
-    const float ut = utgt[t - 1];
-    int c = block_sample([&](int i) { return fmaxf(pr[i] - qr[i], 0.0f); }, V, ut, samp, &near);
-    if (c < 0) c = block_sample([&](int i) { return pr[i]; }, V, ut, samp, &near);
-    codes[t - 1] = c;
-    cdf_near[t - 1] = near ? 1u : 0u;
-    *n_acc_out = t - 1;
-    return t;
-  }
-  const float* pr = p + static_cast<size_t>(gamma) * V;
-  bool near = false;
-  codes[gamma] = block_sample([&](int i) { return pr[i]; }, V, utgt[gamma], samp, &near);
-  cdf_near[gamma] = near ? 1u : 0u;
-  *n_acc_out = gamma;
-  return gamma + 1;
+  if (threadIdx.x < 32 && total + static_cast<int>(threadIdx.x) < ((total + 31) & ~31))
+    L.lw[total + threadIdx.x] = 0.0f;
+  lds_sync();
+  return total;
 }
 
-// Component accept: one block per stream, uniforms and drafts from memory.
+// One block per (offset row r, stream b) of a chain round: row r < gamma
+// tests draft r + 1, row gamma draws the bonus; greedy rows take their
+// argmax.  tcode / tflags [B][W + 1] as the decode round's target kernel
+// writes them.
 __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a) {
-  __shared__ int dec[2];
-  __shared__ float pq[2 * CP_SPEC_MAX_WINDOW];
-  __shared__ int codes[CP_SPEC_MAX_WINDOW + 1];
-  __shared__ uint32_t anear[CP_SPEC_MAX_WINDOW + 1], cnear[CP_SPEC_MAX_WINDOW + 1];
-  __shared__ int targ[CP_SPEC_MAX_WINDOW + 1];
-  __shared__ SampleSmem samp;
+  extern __shared__ float4 row_dyn[];
   __shared__ uint64_t red64[4];
   __shared__ uint32_t red32[4];
-  const int b = blockIdx.x;
+  __shared__ int redi[4];
+  const int r = blockIdx.x, b = blockIdx.y;
   const int W = a.W, V = a.V;
   const int gamma = min(max(a.gamma[b], 0), W);
-  if (threadIdx.x <= CP_SPEC_MAX_WINDOW) {
-    anear[threadIdx.x] = 0;
-    cnear[threadIdx.x] = 0;
-  }
-  const float* q = a.q + static_cast<size_t>(b) * W * V;
-  const float* p = a.p + static_cast<size_t>(b) * (W + 1) * V;
-  if (a.greedy) {
-    for (int r = 0; r <= gamma; ++r) {
-      TopkResult res{-1, 0u};
-      dispatch_vpt(V, [&](auto vpt) {
-        float zv[decltype(vpt)::value];
-        load_row<decltype(vpt)::value>(p + static_cast<size_t>(r) * V, zv);
-        res = argmax_regs<decltype(vpt)::value>(zv, red64, red32);
-      });
-      if (threadIdx.x == 0) targ[r] = res.code;
-      __syncthreads();
+  const size_t orow = static_cast<size_t>(b) * (W + 1) + r;
+  if (r > gamma) {
+    if (threadIdx.x == 0) {
+      a.tcode[orow] = -1;
+      a.tflags[orow] = 0u;
     }
+    return;
   }
-  __syncthreads();
-  const int* draft = a.draft + static_cast<size_t>(b) * W;
-  __shared__ float ua[CP_SPEC_MAX_WINDOW], ut[CP_SPEC_MAX_WINDOW + 1];
-  if (!a.greedy) {
-    if (threadIdx.x < gamma) ua[threadIdx.x] = a.u_acc[static_cast<size_t>(b) * W + threadIdx.x];
-    if (threadIdx.x >= 16 && threadIdx.x - 16 <= gamma)
-      ut[threadIdx.x - 16] = a.u_tgt[static_cast<size_t>(b) * (W + 1) + threadIdx.x - 16];
-  }
-  __syncthreads();
-  int n_acc = 0;
-  const int n = accept_scan(gamma, draft, q, p, V, a.greedy != 0, ua, ut,
-                            [&](int r) { return targ[r]; }, codes, anear, cnear, &n_acc, samp,
-                            dec, pq);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    a.n_out[b] = n;
-    for (int i = 0; i <= W; ++i) a.codes_out[static_cast<size_t>(b) * (W + 1) + i] = i < n ? codes[i] : -1;
-    if (a.flags_out) {
-      uint32_t f = 0;
-      for (int t = 1; t <= gamma + 1; ++t)
-        if (anear[t - 1] || cnear[t - 1]) f |= 1u << (t - 1);
-      a.flags_out[b] = f;
+  dispatch_vpt(V, [&](auto vpt) {
+    constexpr int VPT = decltype(vpt)::value;
+    float pv[VPT];
+    load_row<VPT>(a.p + orow * V, pv);
+    if (a.greedy) {
+      const TopkResult res = argmax_regs<VPT>(pv, red64, red32);
+      if (threadIdx.x == 0) {
+        a.tcode[orow] = res.code;
+        a.tflags[orow] = res.flags;
+      }
+      return;
     }
+    const bool test = r < gamma;
+    const RowLds L = row_lds(row_dyn, V, true);
+    if (test) {
+      float qv[VPT];
+      load_row<VPT>(a.q + (static_cast<size_t>(b) * W + r) * V, qv);
+      store_row<VPT>(qv, L.q);
+    }
+    const int total = dense_to_list<VPT>(pv, L, redi);
+    if (threadIdx.x >= kWave) return;
+    const int d = test ? a.draft[static_cast<size_t>(b) * W + r] : -1;
+    const float ua = test ? a.u_acc[static_cast<size_t>(b) * W + r] : 0.0f;
+    const float ut = a.u_tgt[orow];
+    uint32_t flags = 0;
+    int code = -1;
+    const int acc = walk_step(L, total, V, test ? 1 : 0, [&](int) { return d; }, [&](int) { return ua; }, ut,
+                              &code, &flags);
+    if (acc == 0) flags |= kRowAccepted;
+    if (threadIdx.x == 0) {
+      a.tcode[orow] = code;
+      a.tflags[orow] = flags;
+    }
+  });
+}
+
+// One thread per stream: the round's outcome from its rows (chain_outcome).
+__global__ __launch_bounds__(kBlock) void accept_outcome_kernel(const AcceptArgs a) {
+  const int b = blockIdx.x * kBlock + threadIdx.x;
+  if (b >= a.B) return;
+  const int W = a.W;
+  const int gamma = min(max(a.gamma[b], 0), W);
+  int dc[CP_SPEC_MAX_WINDOW], tc[CP_SPEC_MAX_WINDOW], codes[CP_SPEC_MAX_WINDOW];
+  uint32_t tf[CP_SPEC_MAX_WINDOW];
+  for (int t = 0; t < gamma; ++t) dc[t] = a.draft[static_cast<size_t>(b) * W + t];
+  for (int i = 0; i <= gamma; ++i) {
+    tc[i] = a.tcode[static_cast<size_t>(b) * (W + 1) + i];
+    tf[i] = a.tflags[static_cast<size_t>(b) * (W + 1) + i];
   }
+  const ChainOutcome o = chain_outcome(gamma, a.greedy != 0, dc, tc, tf, codes);
+  const int n = o.n_acc + 1;
+  a.n_out[b] = n;
+  for (int i = 0; i <= W; ++i) a.codes_out[static_cast<size_t>(b) * (W + 1) + i] = i < n ? codes[i] : -1;
+  if (a.flags_out) a.flags_out[b] = o.accept | o.cdf;
 }
 
 hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(accept_rows_kernel, dim3(a.B), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(accept_rows_kernel, dim3(a.W + 1, a.B), dim3(kBlock), row_lds_bytes(a.V, true), s, a);
+  hipLaunchKernelGGL(accept_outcome_kernel, dim3((a.B + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+// One block per row of cp_spec_walk_step: the row's children tested in order
+// against its draft distribution, then the draw (walk_step).
+__global__ __launch_bounds__(kBlock) void walk_rows_kernel(const WalkArgs a) {
+  extern __shared__ float4 row_dyn[];
+  __shared__ int redi[4];
+  const int i = blockIdx.x;
+  const int V = a.V;
+  const int nk = min(max(a.nchild[i], 0), a.maxc);
+  dispatch_vpt(V, [&](auto vpt) {
+    constexpr int VPT = decltype(vpt)::value;
+    float pv[VPT];
+    load_row<VPT>(a.p + static_cast<size_t>(i) * V, pv);
+    const RowLds L = row_lds(row_dyn, V, true);
+    if (nk > 0) {
+      float qv[VPT];
+      load_row<VPT>(a.q + static_cast<size_t>(i) * V, qv);
+      store_row<VPT>(qv, L.q);
+    }
+    const int total = dense_to_list<VPT>(pv, L, redi);
+    if (threadIdx.x >= kWave) return;
+    const size_t cb = static_cast<size_t>(i) * a.maxc;
+    uint32_t flags = 0;
+    int code = -1;
+    const int acc = walk_step(L, total, V, nk, [&](int k) { return a.child[cb + k]; },
+                              [&](int k) { return a.u_acc[cb + k]; }, a.u_tgt[i], &code, &flags);
+    if (threadIdx.x == 0) {
+      a.acc_out[i] = acc;
+      a.code_out[i] = code;
+      if (a.flags_out) a.flags_out[i] = flags;
+    }
+  });
+}
+
+hipError_t launch_walk_rows(const WalkArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(walk_rows_kernel, dim3(a.n), dim3(kBlock), row_lds_bytes(a.V, true), s, a);
   return hipGetLastError();
 }
 
@@ -606,18 +629,22 @@ hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
 }
 
 // Target distribution p_r of every verify row that has a head, and the
-// row's share of the acceptance step, all rows of all streams in parallel:
-//   row r < gamma scores draft offset t = r+1: accept d_t iff
-//     U(s+t, accept) < p_r(d_t) / q_t(d_t); if not, the row draws its
+// row's step of the acceptance walk (walk_step), all rows of all streams in
+// parallel:
+//   chain row r < gamma tests draft offset t = r+1 (one child): accept d_t
+//     iff U(s+t, accept) < p_r(d_t) / q_t(d_t); if not, the row draws its
 //     residual sample norm(max(0, p_r - q_t)) with U(s+t, target);
 //   row gamma draws the bonus from p_gamma with U(s+gamma+1, target);
-//   prefill row 1 draws c_1 from p_1 with U(1, target).
+//   prefill row 1 draws c_1 from p_1 with U(1, target);
+//   tree row v tests its node's active children in node order with
+//     U(depth, accept, k) and draws from the last residual with
+//     U(depth, target) when none is accepted.
 // Each row's outcome depends on that row alone, so the sequential scan
-// reduces to "first rejected offset" in the accept kernel.  tcode holds the
-// draft code (accepted) or the row's sample; tflags the row's top-k / argmax
-// flags, its accept-test and CDF near ties, and kRowAccepted.
-constexpr uint32_t kRowAccepted = 1u << 8;
-
+// reduces to "first rejected offset" (chain) or a walk over the rows'
+// decisions (tree) in the accept kernel.  tcode holds the draft code
+// (accepted) or the row's draw; tflags the row's top-k / argmax flags, its
+// accept-test and CDF near ties, and kRowAccepted (chain) or the accepted
+// child + 1 in bits 16..23 (tree).
 __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) {
   extern __shared__ float4 row_dyn[];
   __shared__ SelSmem S;
@@ -631,14 +658,13 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     // every load that depends only on the block goes out at once (one memory
     // round trip, not three): the row's head and the stream's state first, so
     // that the uniforms are computed while the rest is in flight, then the
-    // logits and the draft row this row may test (offset rr + 1 exists for
-    // rr < W)
+    // logits and the draft distribution this row may test against (the
+    // chain's row rr tests draft offset rr + 1, which exists for rr < W; a
+    // tree row tests the children of its node, drafted at depth dep[rr] + 1)
     const int head = r.thead[row];
     const StreamState st = r.st[b];
     float zv[VPT];
     load_row<VPT>(r.tlogits + row * r.V, zv);
-    // (the chain's row rr tests draft offset rr + 1; a tree row tests the
-    // children of its node, drafted at depth dep[rr] + 1)
     const int qi = r.tnodes > 0 ? r.dep[rr] : rr;
     const bool has_q = !r.greedy && qi < r.W;
     float qv[VPT];
@@ -647,17 +673,12 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       const float* qrow = r.q + (static_cast<size_t>(b) * r.W + qi) * r.V;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
-      dd = r.dcode[static_cast<size_t>(b) * r.W + rr];
+      if (r.tnodes == 0) dd = r.dcode[static_cast<size_t>(b) * r.W + rr];
     }
     // (a finished stream's heads are zero already; testing its mode here keeps
     // the state load ahead of this branch)
     if (head <= 0 || st.mode == kModeDone) return;
-    // the chain row's uniforms (depth s + 1 + rr; prefill: depth 1)
     const bool spec = st.mode == kModeSpec;
-    const int depth = spec ? st.s + 1 + rr : 1;
-    const bool chain_s = !r.greedy && r.tnodes == 0;
-    const float ut = chain_s ? frame_uniform(frame_seed(st), depth, kTarget) : 0.0f;
-    const float ua = chain_s && spec && rr < st.gamma ? frame_uniform(frame_seed(st), depth, kAccept) : 0.0f;
     if (r.greedy) {
       const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
       if (threadIdx.x == 0) {
@@ -666,114 +687,41 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       }
       return;
     }
-    if (r.tnodes > 0) {
-      // tree window: the row's node decides its own step of the walk (it
-      // depends on the node alone): its active children are tested in order
-      // with U(depth, accept, k) < p'(x)/q(x), p' <- max(0, p' - q) after a
-      // rejection (kept when nothing is left), normalised by its sequential
-      // float32 sum when another child follows; with none accepted the row
-      // draws from p' with U(depth, target).  tflags: top-k flag, accept near
-      // ties of the tests, the draw's CDF near tie, accepted child + 1 in
-      // bits 16..23; tcode: the draw.
-      const RowLds L = row_lds(row_dyn, r.V, true);
-      store_row<VPT>(zv, L.z);
-      const bool spec_t = st.mode == kModeSpec;
-      const int gamma = spec_t ? st.gamma : 0;
-      uint32_t kmask = 0u;
-      int nk = 0;
-      if (spec_t)
-        for (int ch = 1; ch <= r.tnodes; ++ch)
-          if (r.par[ch] == rr && r.dep[ch] <= gamma) kmask |= 1u << ch, ++nk;
-      if (nk > 0) store_row<VPT>(qv, L.q);
-      int total;
-      uint32_t flags = 0;
-      if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, nullptr, &total, &flags)) return;
-      const int lane = threadIdx.x % kWave;
-      const uint64_t seed = frame_seed(st);
-      const int depth = spec_t ? st.s + r.dep[rr] + 1 : 1;
-      int dec = -1;
-      for (int ch = 1, k = 0; ch <= r.tnodes; ++ch) {
-        if (!((kmask >> ch) & 1u)) continue;
-        const int x = r.ncode[static_cast<size_t>(b) * 8 + ch];
-        const float qd = (x >= 0 && x < r.V) ? L.q[x] : 1.0f;
-        float pd = 0.0f;
-        for (int i = lane; i < total; i += kWave)
-          if (L.lidx[i] == x) pd = L.lw[i];
-        pd = wave_max(pd);
-        const float ratio = pd / qd;
-        const float ua = frame_uniform(seed, depth, kAccept, k);
-        if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) flags |= kFlagAccept;
-        if (ua < ratio) {
-          dec = ch;
-          break;
-        }
-        bool pos = false;
-        for (int i = lane; i < total; i += kWave) pos |= L.lw[i] - L.q[L.lidx[i]] > 0.0f;
-        if (__ballot(pos)) {
-          for (int i = lane; i < total; i += kWave) L.lw[i] = fmaxf(L.lw[i] - L.q[L.lidx[i]], 0.0f);
-          wave_lds_sync();
-        }
-        if (k + 1 < nk) {  // another child follows: normalise (the list is in code order)
-          float tot = 0.0f;
-          if (lane == 0)
-            for (int i = 0; i < total; ++i)
-              if (L.lw[i] > 0.0f) tot = tot + L.lw[i];
-          tot = __shfl(tot, 0);
-          for (int i = lane; i < total; i += kWave) L.lw[i] = L.lw[i] / tot;
-          wave_lds_sync();
-        }
-        ++k;
-      }
-      int code = -1, near = 0;
-      if (dec < 0) list_draw(L.lw, L.lidx, total, frame_uniform(seed, depth, kTarget), &code, &near);
-      if (threadIdx.x == 0) {
-        r.tcode[row] = code;
-        r.tflags[row] = flags | (near ? kFlagCdf : 0u) | (static_cast<uint32_t>(dec + 1) << 16);
-      }
-      return;
+    // the row's children: chain row rr < gamma tests draft rr + 1; a tree
+    // row its node's children within the round's depth
+    const int gamma = spec ? st.gamma : 0;
+    int nk = 0;
+    int kids[CP_SPEC_MAX_WINDOW];
+    if (r.tnodes == 0) {
+      if (spec && rr < gamma) kids[nk++] = 0;
+    } else if (spec) {
+      for (int ch = 1; ch <= r.tnodes; ++ch)
+        if (r.par[ch] == rr && r.dep[ch] <= gamma) kids[nk++] = ch;
     }
-    const bool test = spec && rr < st.gamma;  // this row scores draft offset rr + 1
+    const uint64_t seed = frame_seed(st);
+    const int depth = spec ? st.s + (r.tnodes > 0 ? r.dep[rr] : rr) + 1 : 1;
+    const float ut = frame_uniform(seed, depth, kTarget);
+    const float ua0 = nk > 0 ? frame_uniform(seed, depth, kAccept) : 0.0f;
     const RowLds L = row_lds(row_dyn, r.V, true);
     store_row<VPT>(zv, L.z);
-    int d = -1;
-    if (test) {
-      // the draft distribution of offset rr + 1, for the test and the residual
-      store_row<VPT>(qv, L.q);
-      d = dd;
-    }
+    if (nk > 0) store_row<VPT>(qv, L.q);
     int total;
     uint32_t flags = 0;
     if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, nullptr, &total, &flags)) return;
-    // wave 0: the row's decision
-    int code, near = 0;
-    if (test) {
-      // p_r(d_t) is zero unless d_t is in the target's top-k set; a code
-      // outside [0, V) is rejected (p = 0, q = 1)
-      const float qd = (d >= 0 && d < r.V) ? L.q[d] : 1.0f;
-      float pd = 0.0f;
-      for (int i = threadIdx.x; i < total; i += kWave)
-        if (L.lidx[i] == d) pd = L.lw[i];
-      pd = wave_max(pd);
-      const float ratio = pd / qd;
-      if (fabs(static_cast<double>(ua) - static_cast<double>(ratio)) < kEpsAccept) flags |= kFlagAccept;
-      if (ua < ratio) {
-        code = d;
-        flags |= kRowAccepted;
-      } else {
-        // the residual max(0, p - q) lives on the target's set (p is zero
-        // elsewhere); with no positive entry the draw falls back to p
-        bool pos = false;
-        for (int i = threadIdx.x; i < total; i += kWave) pos |= L.lw[i] - L.q[L.lidx[i]] > 0.0f;
-        if (__ballot(pos)) {
-          for (int i = threadIdx.x; i < total; i += kWave) L.lw[i] = fmaxf(L.lw[i] - L.q[L.lidx[i]], 0.0f);
-          wave_lds_sync();
-        }
-        list_draw(L.lw, L.lidx, total, ut, &code, &near);
-      }
+    // wave 0: the row's step of the walk
+    int code = -1, acc;
+    if (r.tnodes == 0) {
+      acc = walk_step(L, total, r.V, nk, [&](int) { return dd; }, [&](int) { return ua0; }, ut, &code, &flags);
+      if (acc == 0) flags |= kRowAccepted;
     } else {
-      list_draw(L.lw, L.lidx, total, ut, &code, &near);
+      acc = walk_step(L, total, r.V, nk, [&](int k) { return r.ncode[static_cast<size_t>(b) * 8 + kids[k]]; },
+                      [&](int k) { return k == 0 ? ua0 : frame_uniform(seed, depth, kAccept, k); }, ut, &code,
+                      &flags);
+      if (acc >= 0) {
+        flags |= static_cast<uint32_t>(kids[acc] + 1) << 16;
+        code = -1;
+      }
     }
-    if (near) flags |= kFlagCdf;
     if (threadIdx.x == 0) {
       r.tcode[row] = code;
       r.tflags[row] = flags;
@@ -869,35 +817,32 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
     } else {
       const int s = st.s, gamma = st.gamma;
       uint32_t fl = st.flags;
-      for (int t = 1; t <= gamma; ++t) {
+      int codes[CP_SPEC_MAX_WINDOW];
+      const ChainOutcome o = chain_outcome(gamma, r.greedy != 0, dcode_s, tcode_s, tflags_s, codes);
+      const int n_acc = o.n_acc, n = n_acc + 1;
+      // near ties of the decisions the outcome used: drafts 1..n_acc + 1
+      // (the last one tested), rows 0..n_acc
+      for (int t = 1; t <= min(n_acc + 1, gamma); ++t) {
         const uint32_t f = dflags_s[t - 1];
         count_flags(f, &cnt);
         if (f) fl |= 1u << (s + t);
       }
-      for (int i = 0; i <= gamma; ++i) {
+      for (int i = 0; i <= n_acc; ++i) {
         const uint32_t f = tflags_s[i] & (kFlagTopk | kFlagArgmax);
         count_flags(f, &cnt);
         if (f) fl |= 1u << (s + 1 + i);
       }
-      int n_acc = 0;
-      if (r.greedy) {
-        while (n_acc < gamma && dcode_s[n_acc] == tcode_s[n_acc]) ++n_acc;
-      } else {
-        while (n_acc < gamma && (tflags_s[n_acc] & kRowAccepted)) ++n_acc;
-        for (int t = 1; t <= min(n_acc + 1, gamma); ++t) {
-          if (tflags_s[t - 1] & kFlagAccept) {
-            ++cnt.near_tie_accept;
-            fl |= 1u << (s + t);
-          }
+      for (int t = 1; t <= gamma; ++t)
+        if (o.accept & (1u << (t - 1))) {
+          ++cnt.near_tie_accept;
+          fl |= 1u << (s + t);
         }
-        if (tflags_s[n_acc] & kFlagCdf) {
-          ++cnt.near_tie_cdf;
-          fl |= 1u << (s + n_acc + 1);
-        }
+      if (o.cdf) {
+        ++cnt.near_tie_cdf;
+        fl |= 1u << (s + n);
       }
-      const int n = n_acc + 1;
-      for (int t = 0; t < n_acc; ++t) out[s + 1 + t] = dcode_s[t];
-      out[s + n] = st_s.last = tcode_s[n_acc];
+      for (int t = 0; t < n; ++t) out[s + 1 + t] = codes[t];
+      st_s.last = codes[n_acc];
       ++cnt.rounds;
       for (int t = 1; t <= gamma; ++t) {
         ++cnt.proposed[t - 1];
@@ -1432,21 +1377,15 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
       n_s = 1;
     } else {
       uint32_t fl = 0u;
-      for (int d = 1; d <= gamma; ++d) {  // the drafts' flags
-        const uint32_t f = dfl_s[d - 1];
-        count_flags(f, &cnt);
-        if (f) fl |= 1u << (s + d);
-      }
-      for (int i = 0; i <= r.tnodes; ++i) {  // every active row's top-k flag
-        if (i > 0 && dep_s[i] > gamma) continue;
-        const uint32_t f = tfl_s[i] & kFlagTopk;
-        count_flags(f, &cnt);
-        if (f) fl |= 1u << (s + dep_s[i] + 1);
-      }
       int v = 0, n = 0;
       for (;;) {  // the walk: at most one node per depth
         const uint32_t tf = tfl_s[v];
         const int j = s + dep_s[v] + 1;
+        // the rows the walk visits used their top-k sets
+        if (tf & kFlagTopk) {
+          ++cnt.near_tie_topk;
+          fl |= 1u << j;
+        }
         if (tf & kFlagAccept) {
           ++cnt.near_tie_accept;
           fl |= 1u << j;
@@ -1464,6 +1403,13 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
         out[s + n + 1] = ncode_s[dec];
         ++n;
         v = dec;
+      }
+      // the draft depths whose candidates the walk tested: 1..n (depth n's
+      // children were tested at the last visited node)
+      for (int d = 1; d <= min(n, gamma); ++d) {
+        const uint32_t f = dfl_s[d - 1];
+        count_flags(f, &cnt);
+        if (f) fl |= 1u << (s + d);
       }
       st_s.flags |= fl;
       v_s = v;

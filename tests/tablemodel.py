@@ -6,7 +6,8 @@ It exposes the interface oracle.spec uses (G, V, new_kv, forward_rows,
 embed_row, logits).  The "hidden state" at position j is the tuple of codes
 c_0..c_{j-1} fed so far; head_j applied to the state at depth j gives the
 target logits of c_j, applied to an earlier state (a draft) it gives logits
-from a separate table keyed by (state, j).
+from a separate table keyed by (state, j).  ``edits`` overwrites single
+logits of a table (by its key) to script ties.
 """
 import zlib
 
@@ -29,8 +30,9 @@ class _KV:
 
 class TableModel:
     def __init__(self, G, V, seed=0, scale=1.5, draft_shift=0.0,
-                 target_support=None, draft_support=None):
+                 target_support=None, draft_support=None, edits=None):
         self.G, self.V = G, V
+        self.edits = edits or {}  # table key -> {code: logit}
         self.seed = seed
         self.scale = scale
         self.draft_shift = draft_shift
@@ -48,7 +50,10 @@ class TableModel:
             mask = np.full(self.V, -30.0)
             mask[list(support)] = 0.0
             z = z + mask
-        self._cache[key] = z.astype(np.float32)
+        z = z.astype(np.float32)
+        for code, value in self.edits.get(key, {}).items():
+            z[code] = np.float32(value)
+        self._cache[key] = z
         return self._cache[key]
 
     def new_kv(self):

@@ -178,6 +178,20 @@ def test_accept_bit_exact(cid):
     d2 = draft[2, 0]
     ua[2, 0] = np.float32(p[2, 0, d2] / q[2, 0, d2]) if p[2, 0, d2] > 0 else 0
     gamma[2] = max(gamma[2], 1)
+    # a draft outside p's support (p(d) = 0: always rejected), then the
+    # residual draw
+    gamma[3] = W
+    off = np.flatnonzero(p[3, 0] == 0)[:2]
+    q[3, 0] = 0
+    q[3, 0, off] = np.float32(0.5)
+    draft[3, 0] = off[0]
+    # q >= p everywhere on p's support: the residual is all zero and the
+    # draw falls back to p
+    gamma[4] = 1
+    q[4, 0] = p[4, 0]
+    draft[4, 0] = int(np.flatnonzero(p[4, 0] > 0)[0])
+    ua[4, 0] = np.float32(1.0 - 2**-24)     # ratio 1: u < 1 accepts ...
+    p[4, 0, draft[4, 0]] = np.float32(p[4, 0, draft[4, 0]] * 0.5)  # ... unless p(d) < q(d)
     n_out = torch.zeros(B, dtype=torch.int32, device="cuda")
     codes = torch.zeros((B, W + 1), dtype=torch.int32, device="cuda")
     flags = torch.zeros(B, dtype=torch.int32, device="cuda")
@@ -227,14 +241,34 @@ def test_accept_greedy():
         assert tuple(Cd[b, :N[b]]) == rnd.emitted
 
 
+def _schedule(G, R, rng, steps):
+    """One stream's verify blocks: the prefill [0, 1], then blocks of 1..R
+    consecutive positions, each after truncating 0..2 positions of the block
+    before (never the committed prefix 0..1), until the frame is full; then
+    empty blocks.  Returns [(positions, valid length before the block)]."""
+    out = [([0, 1], 0)]
+    valid, last = 2, 2
+    for _ in range(steps):
+        if valid >= G:
+            out.append(([], valid))
+            continue
+        cut = int(rng.integers(0, min(2, last - 1) + 1)) if last > 1 else 0
+        start = max(2, valid - cut)
+        n = min(int(rng.integers(1, R + 1)), G - start)
+        out.append((list(range(start, start + n)), start))
+        valid, last = start + n, n
+    return out
+
+
 @pytest.mark.parametrize("cid,B", [("tiny", 3), ("qwen3tts", 3),
                                    ("tiny", 24), ("qwen3tts", 24),
                                    ("tiny", 400)])
 def test_decoder_ragged_blocks_and_truncation(cid, B):
-    """A prefill block, a ragged verify block, then a block that overwrites
-    rejected positions after truncation, for B streams (stream b follows
-    pattern b % 3).  24 streams put the projections on the split-K matrix-core
-    tiles, 400 tiny streams on the 64 x 64 tiles."""
+    """Every position of the frame (0..G-1) through ragged verify blocks with
+    transactional truncation between them, for B streams (stream b follows
+    schedule b % 3).  3 streams run the GEMV path; 24 streams the split-K
+    matrix-core tiles (fp32) or the packed bf16 tiles; 400 tiny streams the
+    64 x 64 tiles."""
     log(f"decoder_forward {cid} B={B}")
     c = synth.config(cid)
     m = oracle_model(cid)
@@ -245,24 +279,28 @@ def test_decoder_ragged_blocks_and_truncation(cid, B):
     kv = torch.zeros((B, L, 2, G, nkv, d), device="cuda")
     okv = [m.new_kv() for _ in range(B)]
     rng = np.random.default_rng(60 + len(cid))
-
-    def emb(j):
-        return m.embed_row(j % G, int(rng.integers(0, c["vocab"])))
-
-    def step(pos_rows, trunc=None):
-        if trunc is not None:
-            for b in range(B):
-                okv[b].truncate(trunc[b])
+    scheds = [_schedule(G, R, rng, G) for _ in range(3)]
+    nsteps = max(len(sc) for sc in scheds)
+    top = 0
+    for k in range(nsteps):
         x = np.zeros((B, R, H), np.float32)
         pos = np.full((B, R), -1, np.int32)
-        for b, plist in enumerate(pos_rows):
+        rows = []
+        for b in range(B):
+            sc = scheds[b % 3]
+            plist, valid = sc[k] if k < len(sc) else ([], G)
+            if plist:
+                okv[b].truncate(valid)
             for r, p_ in enumerate(plist):
-                x[b, r] = rng.standard_normal(H) if p_ == 0 else emb(p_ - 1)
+                x[b, r] = (rng.standard_normal(H) if p_ == 0 else
+                           m.embed_row((p_ - 1) % G, int(rng.integers(0, c["vocab"]))))
                 pos[b, r] = p_
+                top = max(top, p_)
+            rows.append(plist)
         xt = _t(x)
         h.decoder_forward(xt, _t(pos), kv)
         got = xt.cpu().numpy()
-        for b, plist in enumerate(pos_rows):
+        for b, plist in enumerate(rows):
             if not plist:
                 continue
             ref = m.forward_rows([x[b, r].astype(np.float64)
@@ -270,16 +308,8 @@ def test_decoder_ragged_blocks_and_truncation(cid, B):
             for r in range(len(plist)):
                 np.testing.assert_allclose(got[b, r], ref[r], rtol=1e-3,
                                            atol=2e-3)
-                assert np.max(np.abs(got[b, r] - ref[r])) < 1e-4
-
-    def pattern(rows):
-        return [rows[b % 3] for b in range(B)]
-
-    step(pattern([[0, 1], [0, 1], [0, 1]]))
-    step(pattern([list(range(2, 2 + R)), [2, 3], [2]]))
-    # pattern 0 keeps positions 0..3, pattern 1 keeps 0..3, pattern 2 0..2
-    step(pattern([[4, 5], list(range(4, 4 + R)), [3]]),
-         trunc=pattern([4, 4, 3]))
+                assert np.max(np.abs(got[b, r] - ref[r])) < 1e-4, (k, b, r)
+    assert top == G - 1  # the last position of the frame was covered
 
 
 @pytest.mark.parametrize("cid", ["tiny", "qwen3tts"])
@@ -304,3 +334,68 @@ def test_talker_feedback(cid):
         ref = ospec.talker_feedback(m, codes[i])
         np.testing.assert_allclose(got[i], ref, rtol=2e-6, atol=2e-6 * np.abs(ref).max())
     assert np.all(np.isnan(got[-1]))
+
+
+def _walk_rows(V, k, n, maxc, rng):
+    """Rows for the tree walk step: p, q (top-k softmax rows), children drawn
+    from q, uniforms; special rows p == q, disjoint supports, children
+    outside p's support, and an exact ratio tie."""
+    z = (rng.standard_normal((n, V)) * 0.8).astype(np.float32)
+    p = np.array([odist.topk_softmax(z[i] + (rng.standard_normal(V) * 0.3).astype(np.float32),
+                                     0.9, k)[0] for i in range(n)], np.float32)
+    q = np.array([odist.topk_softmax(z[i] + (rng.standard_normal(V) * 0.3).astype(np.float32),
+                                     0.9, k)[0] for i in range(n)], np.float32)
+    nch = rng.integers(0, maxc + 1, size=n).astype(np.int32)
+    ch = np.zeros((n, maxc), np.int32)
+    for i in range(n):
+        for j in range(maxc):
+            ch[i, j] = odist.sample(q[i], rng.random())[0]
+    ua = (rng.integers(0, 2**24, size=(n, maxc)) / 2**24).astype(np.float32)
+    ut = (rng.integers(0, 2**24, size=n) / 2**24).astype(np.float32)
+    p[0] = q[0]                                  # p == q: the first child passes
+    nch[0] = maxc
+    p[1] = 0
+    p[1, :5] = np.float32(0.2)                   # disjoint supports: all rejected
+    q[1] = 0
+    q[1, 8:11] = np.float32(1 / 3)
+    ch[1] = 8 + np.arange(maxc) % 3
+    nch[1] = maxc
+    nch[2] = maxc                                # several rejections in a row
+    ua[2] = np.float32(1 - 2**-24)
+    nch[3] = 1                                   # exact tie u == p/q
+    x = ch[3, 0]
+    ua[3, 0] = np.float32(p[3, x] / q[3, x]) if p[3, x] > 0 else 0
+    return p, q, nch, ch, ua, ut
+
+
+@pytest.mark.parametrize("cid", ["tiny", "qwen3tts", "wide-256"])
+def test_walk_step_bit_exact(cid):
+    """cp_spec_walk_step (the tree rows' step in the decode round) against
+    oracle.tree.walk_step: the accepted child, the code and the near-tie
+    flags, bit for bit, for 0..3 children per row."""
+    from oracle import tree as otree
+    log(f"walk step {cid}")
+    c = synth.config(cid)
+    V, k = c["vocab"], c["top_k"]
+    h = handle(cid, max_streams=1)
+    rng = np.random.default_rng(70 + len(cid))
+    n, maxc = 96, 3
+    p, q, nch, ch, ua, ut = _walk_rows(V, k, n, maxc, rng)
+    acc = torch.zeros(n, dtype=torch.int32, device="cuda")
+    codes = torch.zeros(n, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda")
+    h.walk_step(_t(p), _t(q), _t(nch), _t(ch), _t(ua), _t(ut), acc, codes, flags)
+    A = acc.cpu().numpy()
+    Cd = codes.cpu().numpy()
+    Fl = flags.cpu().numpy().view(np.uint32)
+    kinds = {"accept": 8, "cdf": 4}
+    for i in range(n):
+        kk, code, near = otree.walk_step(p[i], q[i], list(ch[i, :nch[i]]),
+                                         lambda j: ua[i, j], ut[i])
+        assert A[i] == (-1 if kk is None else kk), i
+        assert Cd[i] == code, (i, Cd[i], code)
+        want = 0
+        for kind in near:
+            want |= kinds[kind]
+        assert Fl[i] == want, (i, Fl[i], want)
+    assert A[0] == 0 and A[1] == -1

@@ -1,15 +1,16 @@
 """End-to-end GPU parity of cp_spec_decode_frames against the oracle.
 
-Frame rule: the code stream of a frame equals the oracle's, or the first
-differing depth j carries a near-tie flag (GPU or oracle) at a depth <= j;
-zero unflagged mismatches are allowed.  Full-size workloads are decoded in
-the launch configuration the benchmark times and checked on sampled frames.
+Frame rule (gpu_util.compare_frames): the code stream of a frame equals the
+oracle's, or the oracle re-run with one of its near-tie decisions taken the
+other way reproduces it exactly; nothing else passes.  Full-size workloads are
+decoded in the launch configuration the benchmark times and checked on
+sampled frames spread over every stream.
 """
 import numpy as np
 import pytest
 
 import synth
-from gpu_util import compare_frames, decode_gpu, dparams, handle, log, oracle_frames
+from gpu_util import compare_frames, decode_gpu, dparams, handle, log, oracle_frames, spread_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -17,15 +18,16 @@ torch = pytest.importorskip("torch")
 
 
 def _check(cid, c, hf, c0, seeds, pairs, gc, gf, gst, dp, exact_stats):
-    oc, of, ost = oracle_frames(cid, dp, hf, c0, seeds, pairs)
+    oc, of, ost, rerun = oracle_frames(cid, dp, hf, c0, seeds, pairs)
     sel_c = np.array([gc[f, b] for f, b in pairs])
     sel_f = np.array([gf[f, b] for f, b in pairs])
-    res = compare_frames(sel_c, sel_f, oc, of)
+    res = compare_frames(sel_c, sel_f, oc, of, rerun=rerun, tag=cid)
     log(f"{cid} N={dp['verify_size']}: {res['frames']} frames, "
-        f"{res['exact']} exact, {res['flagged_mismatch']} flagged mismatches, "
-        f"{res['flagged_frames']} flagged frames, "
-        f"{len(res['unflagged'])} unflagged")
+        f"{res['exact']} exact, {res['flip_explained']} explained by a "
+        f"near-tie flip, {res['flagged_frames']} flagged frames, "
+        f"{len(res['unflagged'])} unexplained")
     assert not res["unflagged"], res["unflagged"][:3]
+    assert res["flag_diff"] <= 1 + res["exact"] // 50, res["flag_diff"]
     assert np.all(gc[:, :, 0] == c0)
     assert np.all((gc >= 0) & (gc < c["vocab"]))
     if exact_stats and res["exact"] == res["frames"]:
@@ -94,9 +96,7 @@ def test_tiny_64_streams_full_sampled():
     log("decode tiny-64 B=64 F=500 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 64 * 500
-    rng = np.random.default_rng(4)
-    pairs = [(int(rng.integers(0, 500)), int(rng.integers(0, 64)))
-             for _ in range(24)]
+    pairs = spread_pairs(500, 64, 128, seed=4)
     _check("tiny-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
@@ -107,7 +107,7 @@ def test_qwen3tts_full_sampled():
     log("decode qwen3tts B=1 F=1000 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 1000 and gst["codes"] == 15000
-    pairs = [(f, 0) for f in (0, 1, 333, 777, 999)]
+    pairs = spread_pairs(1000, 1, 60, seed=5)
     _check("qwen3tts", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
@@ -121,7 +121,7 @@ def test_qwen3tts_window_sweep_sampled(N):
     log(f"decode qwen3tts N={N} F=40")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 40
-    pairs = [(f, 0) for f in (0, 21, 39)]
+    pairs = spread_pairs(40, 1, 10, seed=N)
     _check("qwen3tts", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
@@ -133,7 +133,7 @@ def test_qwen3tts_64_streams_window_sampled(N):
     log(f"decode qwen3tts-64 N={N} B=64 F=6")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 6 * 64
-    pairs = [(0, 0), (3, 33), (5, 63)]
+    pairs = spread_pairs(6, 64, 16, seed=N)
     _check("qwen3tts-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
@@ -144,7 +144,7 @@ def test_wide_256_streams_sampled():
     log("decode wide-256 B=256 F=2")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 512
-    pairs = [(0, 0), (1, 255), (0, 128)]
+    pairs = spread_pairs(2, 256, 6, seed=2)
     _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
@@ -157,7 +157,7 @@ def test_wide_256_streams_full_sampled():
     log("decode wide-256 B=256 F=200 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 256 * 200 and gst["codes"] == 256 * 200 * 15
-    pairs = [(0, 7), (117, 200), (199, 255)]
+    pairs = spread_pairs(200, 256, 16, seed=7)
     _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
@@ -170,7 +170,7 @@ def test_tiny_greedy_full_sampled():
     log("decode tiny-greedy B=1 F=1000 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 1000
-    pairs = [(f, 0) for f in range(0, 1000, 50)]
+    pairs = [(f, 0) for f in range(0, 1000, 4)]
     _check("tiny-greedy", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
     ac, af, _ = decode_gpu(handle("tiny-greedy", verify_size=0), hf, c0, seeds)
     assert not compare_frames(gc, gf, ac, af)["unflagged"]
@@ -185,7 +185,7 @@ def test_qwen3tts_64_streams_full_sampled():
     log("decode qwen3tts-64 B=64 F=100 (full)")
     gc, gf, gst = decode_gpu(h, hf, c0, seeds)
     assert gst["frames"] == 6400 and gst["codes"] == 6400 * 15
-    pairs = [(0, 0), (0, 63), (37, 11), (99, 40), (99, 63)]
+    pairs = spread_pairs(100, 64, 64, seed=11)
     _check("qwen3tts-64", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 

@@ -1,9 +1,10 @@
 """GPU parity of the position-aware draft offsets ("RVQ Position Aware
 Speculative Decoding ...", section 2.2, Figure 3): draft offset t scores
-head_{s+t} on h_s + b_t.  Same frame rule as the other decode tests (equal
-codes, or a near-tie flag at or before the first differing depth), over the
+head_{s+t} on h_s + b_t, over the
 GEMV (1 stream), fp32 matrix-core (64 streams) and bf16 batched (64 streams)
 head paths, with K equal to the window and K below it (drafts past K see h_s).
+Frame rule of gpu_util.compare_frames (exact, or reproduced by the oracle
+with one near-tie decision taken the other way).
 """
 import numpy as np
 import pytest
@@ -20,13 +21,13 @@ torch = pytest.importorskip("torch")
 def _check(cid, c, m, hf, c0, seeds, pairs, got, exact_stats):
     gc, gf, gst = got
     dp = dparams(c)
-    oc, of, ost = oracle_frames(cid, dp, hf, c0, seeds, pairs, model=m)
+    oc, of, ost, rerun = oracle_frames(cid, dp, hf, c0, seeds, pairs, model=m)
     sel_c = np.array([gc[f, b] for f, b in pairs])
     sel_f = np.array([gf[f, b] for f, b in pairs])
-    res = compare_frames(sel_c, sel_f, oc, of)
+    res = compare_frames(sel_c, sel_f, oc, of, rerun=rerun, tag=f"{cid} offsets")
     log(f"{cid} K={c['draft_offsets']} N={c['verify_size']}: {res['frames']} "
-        f"frames, {res['exact']} exact, {res['flagged_mismatch']} flagged "
-        f"mismatches, {len(res['unflagged'])} unflagged")
+        f"frames, {res['exact']} exact, {res['flip_explained']} explained by "
+        f"a near-tie flip, {len(res['unflagged'])} unexplained")
     assert not res["unflagged"], res["unflagged"][:3]
     if exact_stats and res["exact"] == res["frames"]:
         assert gst["proposed"] == ost["proposed"]
@@ -88,7 +89,7 @@ def test_offsets_qwen3tts_sampled():
     log("decode qwen3tts K=3 F=200")
     got = decode_gpu(h, hf, c0, seeds)
     assert got[2]["frames"] == 200
-    _check("qwen3tts", c, m, hf, c0, seeds, [(f, 0) for f in (0, 57, 199)], got, False)
+    _check("qwen3tts", c, m, hf, c0, seeds, [(f, 0) for f in range(0, 200, 10)], got, False)
 
 
 def test_offsets_qwen3tts_64_streams_sampled():
@@ -97,4 +98,5 @@ def test_offsets_qwen3tts_64_streams_sampled():
     log("decode qwen3tts-64 K=3 B=64 F=12")
     got = decode_gpu(h, hf, c0, seeds)
     assert got[2]["frames"] == 12 * 64
-    _check("qwen3tts-64", c, m, hf, c0, seeds, [(0, 0), (5, 31), (11, 63)], got, False)
+    from gpu_util import spread_pairs
+    _check("qwen3tts-64", c, m, hf, c0, seeds, spread_pairs(12, 64, 24, seed=3), got, False)

@@ -227,6 +227,26 @@ int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width,
                    const float* d_u_accept, const float* d_u_target,
                    int32_t* d_n, int32_t* d_codes, uint32_t* d_flags);
 
+/* cp_spec_accept without a handle and without allocating: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, rule and results
+ * as cp_spec_accept, with the vocabulary size (256 * 2^i, up to 4096) and the
+ * greedy switch given directly.  The rows' steps go through a static
+ * scratch array of 65536 rows (512 KiB) that the library keeps on each GPU
+ * it runs on until the process ends; nothing is allocated, and every row of
+ * the scratch a call reads it has written first.  All calls on one GPU
+ * share that array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ * Errors: EINVAL for a bad vocab, n_streams < 0, width outside 0..7,
+ * n_streams * (width + 1) > 65536, null pointers; EHIP if the scratch
+ * address cannot be looked up. */
+int cp_spec_accept_noalloc(void* stream, int32_t vocab, int32_t greedy,
+                           int32_t n_streams, int32_t width,
+                           const int32_t* d_gamma, const int32_t* d_draft,
+                           const float* d_q, const float* d_p,
+                           const float* d_u_accept, const float* d_u_target,
+                           int32_t* d_n, int32_t* d_codes, uint32_t* d_flags);
+
 /* One node's step of the tree walk ("RVQ Position Aware ...", section 2.2,
  * Figure 2: the standard acceptance rule with residual resampling applied
  * along the tree), the step the decode round's target kernel takes for every

@@ -88,6 +88,9 @@ _SIGS = {
     "cp_spec_talker_feedback": (C.c_int, [_P, _P, C.c_int32, _P, _P]),
     "cp_spec_accept": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _P]),
+    "cp_spec_accept_noalloc": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_int32, _P, _P, _P, _P, _P, _P,
+                                         _P, _P, _P]),
     "cp_spec_walk_step": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P]),
     "cp_spec_decoder_forward": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P,
@@ -286,6 +289,17 @@ class Handle:
         B, R = int(pos.shape[0]), int(pos.shape[1])
         return _check(lib().cp_spec_decoder_forward(
             self.h, _stream(stream), B, R, _ptr(x), _ptr(pos), _ptr(kv)))
+
+
+def accept_noalloc(vocab, greedy, gamma, draft, q, p, u_accept, u_target,
+                   n_out, codes_out, flags_out=None, stream=None):
+    """cp_spec_accept_noalloc: the accept step without a handle, its scratch
+    in the library's static per-GPU array."""
+    B, W = int(draft.shape[0]), int(draft.shape[1])
+    return _check(lib().cp_spec_accept_noalloc(
+        _stream(stream), int(vocab), int(bool(greedy)), B, W, _ptr(gamma),
+        _ptr(draft), _ptr(q), _ptr(p), _ptr(u_accept), _ptr(u_target),
+        _ptr(n_out), _ptr(codes_out), _ptr(flags_out)))
 
 
 def get_stats(stats_tensor, stream=None) -> dict:

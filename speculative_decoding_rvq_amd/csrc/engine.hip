@@ -801,6 +801,29 @@ int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width, c
   return CP_SPEC_OK;
 }
 
+int cp_spec_accept_noalloc(void* stream, int32_t vocab, int32_t greedy, int32_t n_streams, int32_t width,
+                           const int32_t* d_gamma, const int32_t* d_draft, const float* d_q, const float* d_p,
+                           const float* d_u_accept, const float* d_u_target, int32_t* d_n, int32_t* d_codes,
+                           uint32_t* d_flags) {
+  const int vpt = vocab / 256;
+  if (vocab < 256 || vocab > CP_SPEC_MAX_VOCAB || vocab % 256 || (vpt & (vpt - 1)))
+    return fail(CP_SPEC_EINVAL, "vocab must be 256 * 2^i (256..4096)");
+  if (n_streams < 0 || width < 0 || width > CP_SPEC_MAX_WINDOW - 1)
+    return fail(CP_SPEC_EINVAL, "n_streams < 0 or width outside 0..7");
+  if (static_cast<long long>(n_streams) * (width + 1) > kNoAllocRows)
+    return fail(CP_SPEC_EINVAL, "n_streams * (width + 1) exceeds the static scratch (65536 rows)");
+  if (n_streams == 0) return CP_SPEC_OK;
+  if (!d_gamma || !d_draft || !d_p || !d_n || !d_codes || (!greedy && (!d_q || !d_u_accept || !d_u_target)))
+    return fail(CP_SPEC_EINVAL, "null pointer");
+  AcceptArgs a{};
+  a.B = n_streams; a.W = width; a.V = vocab; a.greedy = greedy ? 1 : 0; a.gamma = d_gamma;
+  a.draft = d_draft; a.q = d_q; a.p = d_p; a.u_acc = d_u_accept; a.u_tgt = d_u_target; a.n_out = d_n;
+  a.codes_out = d_codes; a.flags_out = d_flags;
+  CPS_HIP(noalloc_accept_scratch(&a.tcode, &a.tflags));
+  CPS_HIP(launch_accept_rows(a, static_cast<hipStream_t>(stream)));
+  return CP_SPEC_OK;
+}
+
 int cp_spec_walk_step(cp_spec* h, void* stream, int32_t n_rows, int32_t max_children, const float* d_p,
                       const float* d_q, const int32_t* d_n_children, const int32_t* d_children,
                       const float* d_u_accept, const float* d_u_target, int32_t* d_accepted, int32_t* d_codes,

@@ -224,6 +224,11 @@ hipError_t launch_rmsnorm_rows(const float* x, float* y, const float* g, int row
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s);
 // Every row's step of the walk, then each stream's outcome (two kernels).
 hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s);
+// Rows of the allocation-free accept's static scratch, and the device
+// address of the current GPU's copy (looked up once per device).
+constexpr int kNoAllocRows = 65536;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_accept_scratch(int** tcode, uint32_t** tflags);
 hipError_t launch_walk_rows(const WalkArgs& a, hipStream_t s);
 hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t s);
 hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s);

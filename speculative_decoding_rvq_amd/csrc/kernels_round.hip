@@ -1,5 +1,6 @@
 // Attention, top-k softmax + sampling, acceptance and the round control
 // kernels of CodePredictor speculative decoding.
+#include <mutex>
 #include <type_traits>
 
 #include "dev_common.h"
@@ -391,6 +392,37 @@ hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(accept_rows_kernel, dim3(a.W + 1, a.B), dim3(kBlock), row_lds_bytes(a.V, true), s, a);
   hipLaunchKernelGGL(accept_outcome_kernel, dim3((a.B + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free component accept: the rows' steps
+// (tcode, then tflags) of up to kNoAllocRows rows, one copy per GPU, held
+// until the process ends.  Host code takes its device address from
+// hipGetSymbolAddress (noalloc_accept_scratch); the symbol's host-side name
+// is not a device address.
+static __device__ __align__(256) uint32_t scratch[2 * kNoAllocRows];
+
+hipError_t noalloc_accept_scratch(int** tcode, uint32_t** tflags) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+      e = hipGetSymbolAddress(&ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        ptr[dev] = nullptr;
+        return e;
+      }
+    }
+    p = ptr[dev];
+  }
+  *tcode = static_cast<int*>(p);
+  *tflags = static_cast<uint32_t*>(p) + kNoAllocRows;
+  return hipSuccess;
 }
 
 // One block per row of cp_spec_walk_step: the row's children tested in order

@@ -152,3 +152,17 @@ def test_tree_workspace_holds_node_slots():
     n0 = binding.workspace_bytes(binding.make_cfg(c))
     n1 = binding.workspace_bytes(binding.make_cfg(dict(c, tree=[0, 0, 1, 2])))
     assert n1 > n0  # four more K/V slots per stream, five verify rows
+
+
+def test_accept_noalloc_validation(L):
+    """The allocation-free accept rejects bad sizes on the host, before any
+    HIP call."""
+    f = L.cp_spec_accept_noalloc
+    one = C.c_void_p(16)
+    args = [one] * 9
+    assert f(None, 300, 0, 1, 3, *args) == binding.EINVAL
+    assert "vocab" in binding.last_error()
+    assert f(None, 256, 0, 8193, 7, *args) == binding.EINVAL
+    assert "static scratch" in binding.last_error()
+    assert f(None, 256, 0, 1, 8, *args) == binding.EINVAL
+    assert f(None, 256, 0, 0, 3, *args) == binding.OK  # nothing to do

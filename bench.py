@@ -49,12 +49,19 @@ def kernel_table(h, c, B, iters=200):
     return out
 
 
-TRAFFIC_SOURCES = ("speculative_decoding_rvq_amd/csrc/gemv_impl.h",
-                   "speculative_decoding_rvq_amd/csrc/gemv_bf16.hip",
-                   "speculative_decoding_rvq_amd/csrc/kernels.h")
+# the sources of the kernel a traffic summary was taken on: the GEMV (one
+# stream) or the batched matrix-core projections
+TRAFFIC_SOURCES = {
+    False: ("speculative_decoding_rvq_amd/csrc/gemv_impl.h",
+            "speculative_decoding_rvq_amd/csrc/gemv_bf16.hip",
+            "speculative_decoding_rvq_amd/csrc/kernels.h"),
+    True: ("speculative_decoding_rvq_amd/csrc/bgemm.hip",
+           "speculative_decoding_rvq_amd/csrc/dev_common.h",
+           "speculative_decoding_rvq_amd/csrc/kernels.h"),
+}
 
 
-def measured_traffic(workload, kind):
+def measured_traffic(workload, kind, matrix_cores=False):
     """HBM-side bytes per launch from the committed counter summary
     (profiles/<workload>_<kind>_traffic.md), or None when there is none or
     the kernel's sources have changed since the counters were taken."""
@@ -68,7 +75,7 @@ def measured_traffic(workload, kind):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC_SOURCES[bool(matrix_cores)]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     if fields.get("kernel_source_sha256") != h.hexdigest():
@@ -86,7 +93,7 @@ def roofline(table, weight_dtype, workload=None):
     when the launch ran on matrix-core tiles."""
     kind = max(table, key=lambda k: table[k]["us_per_round"])
     t = table[kind]
-    traffic = measured_traffic(workload, kind) if workload else None
+    traffic = measured_traffic(workload, kind, t.get("matrix_cores")) if workload else None
     common = {"kernel": kind, "traffic": traffic, "avg_us": t["avg_us"],
               "bytes_per_launch": t["bytes_per_launch"],
               "flops_per_launch": t["flops_per_launch"]}
@@ -183,7 +190,7 @@ def feedback_timing(h, c, out, torch, iters=50):
             "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / us / 1e3}
 
 
-def verify_sweep(cid, Ns=(2, 3, 4, 5, 6, 8), frames=None, steps=2):
+def verify_sweep(cid, Ns=(2, 3, 4, 5, 6, 7, 8), frames=None, steps=2):
     """Per-device choice of the verify window N (the package's
     calibrate_window): for each N, codes/s, committed codes per verify pass
     and one pass's time on this GPU (same weights and inputs); the codes per
@@ -288,13 +295,83 @@ def cpu_baseline(cid, n_frames):
         if done >= n_frames:
             break
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    host = len(os.sched_getaffinity(0))
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": done * (c["groups"] - 1) / dt, "unit": "codes/s",
-        "cores": int(threads), "kind": "oracle",
+        "cores": int(min(blas, host)), "kind": "oracle",
+        "host_cores": host,
+        "threading": "the frame loop is single-threaded Python; its matrix "
+                     f"products run on numpy's BLAS pool of {blas} threads",
         "sample": f"first {done} frames of the workload (stream 0), "
                   f"{dt:.1f} s after a {t0 - t_build:.1f} s float64 weight copy",
     }
+
+
+def oracle_rate(cid, n_frames, **over):
+    """Oracle codes/s on the first n_frames (stream 0) of a workload."""
+    import synth
+    from oracle import decoder, spec
+    c = synth.config(cid, **over)
+    m = decoder.Model(c, synth.make_weights(c))
+    hf, c0, seeds = synth.make_inputs(c, frames=n_frames)
+    dp = dict(verify_size=c["verify_size"], greedy=c["greedy"],
+              temperature=c["temperature"], top_k=c["top_k"])
+    t0 = time.perf_counter()
+    for f in range(n_frames):
+        spec.decode_frame(m, dp, hf[f, 0], int(c0[f, 0]), int(seeds[f, 0]))
+    return n_frames * (c["groups"] - 1) / (time.perf_counter() - t0)
+
+
+def _leg(r, c, steps, warmup):
+    return {"workload": f"{c['name']}: {c['streams']} stream(s) x {c['frames']} frames, "
+                        f"G{c['groups']} V{c['vocab']} H{c['hidden']} L{c['layers']}, "
+                        f"{c['dtype']} weights, N={c['verify_size']}, "
+                        + ("greedy" if c["greedy"] else f"T={c['temperature']}, top-k {c['top_k']}"),
+            "steps": steps, "warmup": warmup, "ms_per_step": r["ms_per_step"],
+            "codes_per_s": r["codes_per_s"], "frames_per_s": r["frames_per_s"],
+            "realtime_factor_vs_12.5fps": r["frames_per_s_per_stream"] / REALTIME_FPS,
+            "codes_per_verify_pass": r["codes_per_verify_pass"],
+            "codes_per_decoder_pass": r["codes_per_decoder_pass"],
+            "acceptance_by_offset": r["acceptance_by_offset"]}
+
+
+def baseline_configs(main_line, s64, c64):
+    """Every workload the baseline lists, each at its full size: 1 tiny fp32
+    (1 x 100, N 3); 2 the headline line itself; 3 the tiny decoder greedy,
+    N = 2..8 over 1000 frames; 4 tiny at 64 streams (the streams64 leg);
+    5 the wide bf16 decoder at 256 streams x 200 frames with its kernels'
+    roofline (its 1.0 GB of decoder and head weights exceed the 256 MB
+    Infinity Cache, so its weight traffic comes from HBM)."""
+    out = {}
+    r1, c1 = run_workload("tiny", 5, 2)
+    out["1"] = _leg(r1, c1, 5, 2)
+    out["1"]["cpu_oracle_codes_per_s"] = oracle_rate("tiny", 30)
+    out["2"] = {"workload": main_line["config"]["workload"], "see": "value / roofline"}
+    sweep = {}
+    for N in range(2, 9):
+        r3, c3 = run_workload("tiny-greedy", 3, 1, verify_size=N)
+        leg = _leg(r3, c3, 3, 1)
+        sweep[str(N)] = {k: leg[k] for k in ("codes_per_s", "ms_per_step", "codes_per_verify_pass",
+                                               "codes_per_decoder_pass", "acceptance_by_offset")}
+    out["3"] = {"workload": "tiny-fp32-greedy: 1 stream x 1000 frames, G8 V256 H256 L2, f32 "
+                            "weights, greedy, N = 2..8 (N >= 6 commit alike: the window is cut "
+                            "to G - 2 - s drafts)",
+                "by_verify_size": sweep}
+    out["4"] = _leg(s64, c64, 1, 1)
+    r5, c5 = run_workload("wide-256", 1, 1, kernels=True)
+    out["5"] = _leg(r5, c5, 1, 1)
+    k5 = r5["kernels"]
+    out["5"]["roofline"] = roofline(k5, c5["dtype"], "wide-256")
+    # the same launches as weight bytes from HBM per launch time
+    dom = out["5"]["roofline"]["kernel"]
+    ws = 2 if c5["dtype"] == "bf16" else 4
+    out["5"]["roofline"]["hbm_frac_of_weights"] = (
+        k5[dom]["bytes_per_launch"] / (k5[dom]["avg_us"] * 1e3)) / HBM_PEAK_GBS
+    out["5"]["kernels"] = {k: {kk: round(v, 3) if isinstance(v, float) else v for kk, v in t.items()}
+                           for k, t in k5.items()}
+    out["5"]["cpu_oracle_codes_per_s"] = oracle_rate("wide-256", 2)
+    return out
 
 
 def main():
@@ -414,6 +491,7 @@ def main():
         for row in trees["by_tree"]:
             row["throughput_vs_chain_n4"] = row["codes_per_s"] / main_res["codes_per_s"]
         line["tree_window"] = trees
+        line["baseline_configs"] = baseline_configs(line, s64, c64)
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_frames)
     print(json.dumps(line), flush=True)
 

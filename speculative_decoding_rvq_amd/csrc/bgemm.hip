@@ -64,6 +64,31 @@ __device__ __forceinline__ int btile(int bx, int j) {
   return bx * FN + j;
 }
 
+// The output tile of this block.  Blocks are dispatched to the eight XCDs in
+// turn (linear block id modulo 8), and each XCD's L2 serves only its own
+// blocks.  So each XCD takes a contiguous range of column tiles, and its
+// blocks, in dispatch order, sweep that range in groups of 32 tiles (GR row
+// tiles x GC column tiles): the blocks resident on one XCD at a time share
+// their weight and activation tiles through its L2.  Grids of at most one
+// block per compute unit (all resident at once) and grids that do not split
+// that way keep the plain order.
+__device__ __forceinline__ void block_tile(int* bx, int* by) {
+  constexpr int kXcd = 8, kGroup = 32;
+  const int NBX = gridDim.x, NBY = gridDim.y;
+  const int cpx = NBX / kXcd;
+  const int GC = cpx >= 8 ? 8 : cpx, GR = GC > 0 ? kGroup / GC : 0;
+  if (NBX * NBY <= 256 || NBX % kXcd || GC == 0 || kGroup % GC || cpx % GC || NBY % GR) {
+    *bx = blockIdx.x;
+    *by = blockIdx.y;
+    return;
+  }
+  const int L = blockIdx.x + NBX * blockIdx.y;
+  const int x = L % kXcd, i = L / kXcd;
+  const int g = i / kGroup, j = i % kGroup, gpc = cpx / GC;
+  *bx = x * cpx + (g % gpc) * GC + j % GC;
+  *by = (g / gpc) * GR + j / GC;
+}
+
 template <int MODE, int FM, int FN, bool NORM, bool PL>
 __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
@@ -80,6 +105,8 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (MODE != kHead) block_tile(&bx, &by);
   const int li = lane & 15, lg = lane >> 4;
 
   // ---- the block's activation rows ----
@@ -89,11 +116,11 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   if (MODE == kHead) {
     const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
     __shared__ int red_h[kGW];
-    count = head_rows_slice<kGT>(a.head, a.M, j + 1, blockIdx.y * TM, TM, rows_s, red_h);
+    count = head_rows_slice<kGT>(a.head, a.M, j + 1, by * TM, TM, rows_s, red_h);
     if (count <= 0) return;
     tile0 = j * (a.N / 16);
   } else {
-    const int m0 = blockIdx.y * TM;
+    const int m0 = by * TM;
     count = min(TM, a.M - m0);
     if (tid < TM) rows_s[tid] = tid < count ? m0 + tid : -1;
   }
@@ -105,10 +132,13 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 // missing row reads X row 0: its outputs and sum of squares are never used.
   const int cw = a.K / 32 / kGW;  // chunks of this wave
   const int c0 = wave * cw;
-  // blocks start their K walk at different chunks, so that the blocks that
-  // share a weight tile or an activation tile (on one XCD) do not all miss on
-  // the same lines at once
-  const int rot = (blockIdx.x / 8 + 2 * blockIdx.y + blockIdx.z) % cw;
+  // Grids of at most one block per compute unit (every operand stays in the
+  // L2 of its XCD): blocks start their K walk at different chunks, so that
+  // the blocks that share a tile do not all miss on the same lines at once.
+  // Larger grids run in several waves of blocks: there the blocks of a group
+  // walk K together and share each chunk through the L2.
+  const bool stagger = MODE == kHead || gridDim.x * gridDim.y <= 256;
+  const int rot = stagger ? (bx / 8 + 2 * by + blockIdx.z) % cw : 0;
   auto rc = [&](int step) { const int c = step + rot; return c >= cw ? c - cw : c; };
   const int kl = 8 * (lane & 3);
   const float* xb = a.X + c0 * 32 + kl;
@@ -123,7 +153,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const uint16_t* Wm = (MODE == kSwiGLU && j >= FN / 2) ? static_cast<const uint16_t*>(a.W1) : W0;
-    wr[j] = Wm + frag_at(tile0 + btile<MODE, FN>(blockIdx.x, j), c0, a.wtiles) + lane * 8;
+    wr[j] = Wm + frag_at(tile0 + btile<MODE, FN>(bx, j), c0, a.wtiles) + lane * 8;
   }
   const size_t wstep = static_cast<size_t>(a.wtiles) * 512;  // one chunk further
 
@@ -147,7 +177,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   if constexpr (PL) {
     // activations pre-split: plane p of row tile t, chunk c is the 1 KB
     // fragment at ((c * T + t) * 3 + p) * 512 bf16 (T row tiles)
-    const uint16_t* ab = a.planes + (static_cast<size_t>(c0) * a.ptiles + blockIdx.y * FM) * 3 * 512 + lane * 8;
+    const uint16_t* ab = a.planes + (static_cast<size_t>(c0) * a.ptiles + by * FM) * 3 * 512 + lane * 8;
     const size_t astep = static_cast<size_t>(a.ptiles) * 3 * 512;
     struct PFrag {
       u32x4 x[FM][3];
@@ -387,7 +417,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   if (MODE == kHead && NORM && a.xnorm_out != nullptr) {
     const int k4 = a.K / 4;
     const int per = (k4 + gridDim.x - 1) / gridDim.x;
-    const int q0 = blockIdx.x * per, q1 = min(k4, q0 + per);
+    const int q0 = bx * per, q1 = min(k4, q0 + per);
     const int w = q1 - q0;
     for (int idx = tid; w > 0 && idx < count * w; idx += kGT) {
       const int r = idx / w, c = 4 * (q0 + idx % w);
@@ -402,7 +432,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 
   // ---- fused epilogue: all of the thread's values first, then the stores
   // (the residual add loads every old value before storing any) ----
-  const int n0 = blockIdx.x * TN;
+  const int n0 = bx * TN;
   if (MODE == kSwiGLU && a.out_planes != nullptr) {
     // the down projection's input: eight activations per thread, split
     constexpr int W = TN / 2, G = TM * W / 8;
@@ -416,7 +446,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
         const float g = tile_val(r, c8 + e), u = tile_val(r, c8 + e + W);
         y[e] = g / (1.0f + expf(-g)) * u;
       }
-      split_store8(a.out_planes, a.out_ptiles, row, blockIdx.x * W + c8, y);
+      split_store8(a.out_planes, a.out_ptiles, row, bx * W + c8, y);
     }
     return;
   }
@@ -433,7 +463,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     for (int k = 0; k < PER; ++k) {
       const int idx = tid + k * kGT, r = idx / (TN / 2), c = idx % (TN / 2);
       const int row = rows_s[r];
-      if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + blockIdx.x * (TN / 2) + c] = out[k];
+      if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + bx * (TN / 2) + c] = out[k];
     }
     return;
   }

@@ -107,7 +107,7 @@ def roofline(table, weight_dtype, workload=None):
 
 
 def run_workload(cid, steps, warmup, verify_size=None, frames=None,
-                 kernels=False, offsets=None):
+                 kernels=False, offsets=None, **cfg):
     import numpy as np
     import torch
 
@@ -120,6 +120,7 @@ def run_workload(cid, steps, warmup, verify_size=None, frames=None,
         over["frames"] = frames
     if offsets is not None:  # (K, scale): seeded position-aware draft offsets
         over["draft_offsets"], over["offset_scale"] = offsets
+    over.update(cfg)
     c = synth.config(cid, **over)
     w = synth.make_weights(c)
     wdev = binding.weights_to_device(w)
@@ -479,6 +480,26 @@ def main():
                 "throughput_vs_no_offsets": o["codes_per_s"] / ref["codes_per_s"],
                 "round_time_vs_no_offsets": (o["ms_per_step"] / o["stats"]["rounds"]) /
                                                     (ref["ms_per_step"] / ref["stats"]["rounds"]),
+            }
+        # the next round's drafts formed in this round's verify tail (one
+        # heads launch and one softmax launch per round instead of two each)
+        line["fused_draft"] = {}
+        for wl, steps, ref, off in ((args.workload, args.steps, main_res, None),
+                                    ("qwen3tts-64", 1, q64, None),
+                                    (args.workload, args.steps, None, (3, 0.1))):
+            fr, cf = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
+                                  offsets=off, fused_draft=1)
+            if ref is None:
+                ref = run_workload(wl, steps, 1, frames=args.frames, offsets=off)[0]
+            key = wl + (f" K={off[0]}" if off else "")
+            line["fused_draft"][key] = {
+                "codes_per_s": fr["codes_per_s"], "ms_per_step": fr["ms_per_step"],
+                "codes_per_verify_pass": fr["codes_per_verify_pass"],
+                "unfused_codes_per_s": ref["codes_per_s"],
+                "throughput_vs_unfused": fr["codes_per_s"] / ref["codes_per_s"],
+                "us_per_pass": 1e3 * fr["ms_per_step"] / (fr["stats"]["rounds"] + fr["stats"]["prefill_passes"]),
+                "unfused_us_per_pass": 1e3 * ref["ms_per_step"] /
+                                       (ref["stats"]["rounds"] + ref["stats"]["prefill_passes"]),
             }
         # the verify window chosen on this device (acceptance saturates while
         # a wider window costs more rows per pass)

@@ -88,6 +88,18 @@ typedef struct cp_spec_cfg {
                         /* draft offset t <= K scores with head_{s+t} the    */
                         /* state h_s + b_t, t > K the state h_s; only the    */
                         /* draft distributions q change. 0 = no offsets.     */
+  /* 1: the next round's drafts are formed in this round's verify tail ("RVQ
+   * Position Aware ...", section 2.2 and Figure 3: one call verifies and
+   * drafts).  Every verify row that can end the round (and the prefill's
+   * row 1) also scores the heads of the depths after it, with the offsets
+   * when draft_offsets > 0, in the same lm_head launch as the target rows;
+   * their drafts are drawn in the target softmax launch, and the accept
+   * step keeps the set of the row that ends the round.  The drafts and the
+   * committed codes are those of fused_draft 0; the separate draft GEMV and
+   * draft softmax launches are gone, the heads launch scores up to
+   * max(N, 2) x N rows per stream instead of max(N, 2).  Chain windows only
+   * (EUNSUPPORTED with a tree); ignored when verify_size < 2. */
+  int32_t fused_draft;
   /* Tree-shaped verify window ("RVQ Position Aware ...", section 2.2 and
    * Figure 2).  tree_nodes = T in 1..7 replaces the chain window (verify_size
    * is then ignored; the verify block has T + 1 rows); 0 = the chain.

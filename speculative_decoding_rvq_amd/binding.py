@@ -33,7 +33,8 @@ class Cfg(C.Structure):
                 ("rms_eps", C.c_float), ("verify_size", C.c_int32),
                 ("greedy", C.c_int32), ("temperature", C.c_float),
                 ("top_k", C.c_int32), ("max_streams", C.c_int32),
-                ("draft_offsets", C.c_int32), ("tree_nodes", C.c_int32),
+                ("draft_offsets", C.c_int32), ("fused_draft", C.c_int32),
+                ("tree_nodes", C.c_int32),
                 ("tree_parent", C.c_int32 * 8)]
 
 
@@ -148,6 +149,7 @@ def make_cfg(c: dict, max_streams: int | None = None) -> Cfg:
                temperature=c["temperature"], top_k=c["top_k"],
                max_streams=max_streams or c["streams"],
                draft_offsets=int(c.get("draft_offsets", 0)),
+               fused_draft=int(c.get("fused_draft", 0)),
                tree_nodes=len(c.get("tree") or ()),
                tree_parent=(C.c_int32 * 8)(*(list(c.get("tree") or ()) + [0] * 8)[:8]))
 

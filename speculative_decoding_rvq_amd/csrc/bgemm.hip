@@ -422,10 +422,11 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     for (int idx = tid; w > 0 && idx < count * w; idx += kGT) {
       const int r = idx / w, c = 4 * (q0 + idx % w);
       const int row = rows_s[r];
+      if (row % a.xdiv != 0) continue;  // one writer per X row
       const float4 x = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row / a.xdiv) * a.ldx + c);
       const float4 g = *reinterpret_cast<const float4*>(a.norm_g + c);
       const float ri = rinv_of(r);
-      *reinterpret_cast<float4*>(a.xnorm_out + static_cast<size_t>(row) * a.K + c) =
+      *reinterpret_cast<float4*>(a.xnorm_out + static_cast<size_t>(row / a.xdiv) * a.K + c) =
           make_float4(x.x * g.x * ri, x.y * g.y * ri, x.z * g.z * ri, x.w * g.w * ri);
     }
   }
@@ -528,7 +529,12 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     if (row < 0) continue;
     const int o = n0 + c;
     if (MODE == kHead) {
-      a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k];
+      // rows of draft offset k = row % xdiv add head . b_k
+      const int ko = row % a.xdiv;
+      const float bias = (a.hb != nullptr && ko >= 1 && ko <= a.hbK)
+                             ? a.hb[(static_cast<size_t>(blockIdx.z) * a.hbK + (ko - 1)) * a.N + o]
+                             : 0.0f;
+      a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k] + bias;
     } else if (MODE == kQKV) {
       if (o < a.qdim) {
         a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k];

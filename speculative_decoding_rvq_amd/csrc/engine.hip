@@ -38,6 +38,7 @@ struct Shape {
   int R, W, qdim, kvdim;
   int vec;  // weight elements per 16-byte chunk
   int K;    // position-aware draft offsets (0 = none)
+  int fd;   // next round's drafts formed in the verify tail
   // tree window (T = 0: the chain): nodes, depth, parent and depth of node
   // i (node 0 = the root), K/V positions per stream (the frame's G plus one
   // slot per node)
@@ -47,7 +48,7 @@ struct Shape {
 
 struct Layout {
   size_t st, call, sstats, dhead, thead, pos, hstate, dX, X, Hout, ncode, Q, attn, act, kv, dlogits, q, dcode, dflags,
-      tlogits, p, tcode, tflags, rope, packed, planes, ssp, total;
+      tlogits, p, tcode, tflags, rope, packed, planes, ssp, fhead, cq, ccode, cflags, hb, total;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -88,6 +89,9 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   for (int i = 1; i <= c->tree_nodes; ++i)
     if (c->tree_parent[i - 1] < 0 || c->tree_parent[i - 1] >= i)
       return fail(CP_SPEC_EINVAL, "tree_parent[i-1] must be in 0..i-1");
+  if (c->fused_draft != 0 && c->fused_draft != 1) return fail(CP_SPEC_EINVAL, "fused_draft must be 0 or 1");
+  if (c->fused_draft && c->tree_nodes > 0)
+    return fail(CP_SPEC_EUNSUPPORTED, "fused_draft runs chain windows only");
   if (c->tree_nodes > 0) {
     if (c->greedy) return fail(CP_SPEC_EUNSUPPORTED, "tree windows decode stochastically only");
     if (c->max_streams > 7) return fail(CP_SPEC_EUNSUPPORTED, "tree windows run on at most 7 streams");
@@ -133,6 +137,7 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   s_.R = s_.tn > 0 ? s_.tn + 1 : std::max(s_.N, 2);
   s_.W = s_.tn > 0 ? s_.td : std::max(s_.N - 1, 1);
   s_.K = s_.N >= 2 ? c->draft_offsets : 0;  // no drafts, no offsets
+  s_.fd = (c->fused_draft && s_.N >= 2 && s_.tn == 0) ? 1 : 0;
   for (int K : {s_.H, s_.qdim, s_.F})
     if (!choose_kt(K, s_.vec))
       return fail(CP_SPEC_EUNSUPPORTED, "matrix width " + std::to_string(K) +
@@ -184,11 +189,11 @@ Layout make_layout(const Shape& s) {
   l.st = take(B * sizeof(StreamState));
   l.call = take(sizeof(CallDesc));
   l.sstats = take(B * sizeof(cp_spec_stats));
-  l.dhead = take(B * W * i4);
+  l.dhead = take(std::max<size_t>(B * W, CP_SPEC_MAX_OFFSETS) * i4);  // (also create's scratch)
   l.thead = take(B * R * i4);
   l.pos = take(B * R * i4);
   l.hstate = take(B * s.H * f4);
-  l.dX = take(s.K > 0 ? B * W * s.H * f4 : 0);  // draft inputs h_s + b_t
+  l.dX = take(s.K > 0 && !s.fd ? B * W * s.H * f4 : 0);  // draft inputs h_s + b_t
   l.X = take(B * R * s.H * f4);
   l.Hout = take(B * R * s.H * f4);
   l.Q = take(B * R * s.qdim * f4);
@@ -200,7 +205,15 @@ Layout make_layout(const Shape& s) {
   l.q = take(B * W * s.V * f4);
   l.dcode = take(B * W * i4);
   l.dflags = take(B * W * i4);
-  l.tlogits = take(B * R * s.V * f4);
+  // fused drafts: the target rows' logits and every row's candidate drafts'
+  // logits side by side ([B][R][W + 1][V], column 0 the target)
+  const size_t W1 = s.fd ? W + 1 : 1;
+  l.tlogits = take(B * R * W1 * s.V * f4);
+  l.fhead = take(s.fd ? B * R * W1 * i4 : 0);
+  l.cq = take(s.fd ? B * R * W * s.V * f4 : 0);
+  l.ccode = take(s.fd ? B * R * W * i4 : 0);
+  l.cflags = take(s.fd ? B * R * W * i4 : 0);
+  l.hb = take(s.fd && s.K > 0 ? static_cast<size_t>(s.G - 1) * s.K * s.V * f4 : 0);
   l.p = take(B * R * s.V * f4);
   // (also the component accept's per-row scratch, [B][width + 1])
   const size_t Rt = std::max<size_t>(R, CP_SPEC_MAX_WINDOW);
@@ -259,9 +272,14 @@ struct cp_spec {
     r.thead = at<int>(lo.thead);
     r.pos = at<int>(lo.pos);
     r.hstate = at<float>(lo.hstate);
-    r.K = sh.K;
+    r.K = sh.fd ? 0 : sh.K;  // fused drafts: the offsets enter through the heads' table
     r.doff = doff;
-    r.dX = sh.K > 0 ? at<float>(lo.dX) : nullptr;
+    r.dX = sh.K > 0 && !sh.fd ? at<float>(lo.dX) : nullptr;
+    r.fused = sh.fd;
+    r.fhead = sh.fd ? at<int>(lo.fhead) : nullptr;
+    r.cq = sh.fd ? at<float>(lo.cq) : nullptr;
+    r.ccode = sh.fd ? at<int>(lo.ccode) : nullptr;
+    r.cflags = sh.fd ? at<uint32_t>(lo.cflags) : nullptr;
     r.X = at<float>(lo.X);
     r.Hout = at<float>(lo.Hout);
     r.dlogits = at<float>(lo.dlogits);
@@ -326,7 +344,8 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
   int fm, fn;
   if (a.planes != nullptr && !bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn))
     return fail(CP_SPEC_EINVAL, "pre-split rows without a matrix-core tile");
-  if (pk0 != nullptr && mode != kHead && a.M >= kMfmaMinRows && bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn)) {
+  const bool head_mode = mode == kHead || mode == kHeadG;
+  if (pk0 != nullptr && !head_mode && a.M >= kMfmaMinRows && bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn)) {
     const int cols = mode == kSwiGLU ? a.N * 2 : a.N;
     a.W0 = pk0;
     a.W1 = pk1;
@@ -344,7 +363,7 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
     CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, fn, a, dim3(cols / (16 * fn), (a.M + 16 * fm - 1) / (16 * fm)), s));
     return CP_SPEC_OK;
   }
-  if (mode != kHead && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
+  if (!head_mode && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
     // the largest tile that still gives the chip enough blocks
     const int cols = mode == kSwiGLU ? a.N * 2 : a.N;  // tile columns (gate and up side by side)
     int tile = kTile64, t = 64;
@@ -369,6 +388,15 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
   if (mode == kHead) {
     mt = 1;
     gy = a.M;
+  } else if (mode == kHeadG) {
+    // a head's rows share its weights in one block (up to 8, within the
+    // activation registers); a.hslices comes in as the most rows one head
+    // can have and leaves as the slices per head
+    const int rph = std::max(a.hslices, 1);
+    mt = rph <= 2 ? 2 : (rph <= 4 ? 4 : 8);
+    while (mt > 2 && mt * spt * vec > 96) mt >>= 1;
+    a.hslices = (rph + mt - 1) / mt;
+    gy = a.n_heads * a.hslices;
   } else {
     mt = mt_for(a.M, spt, vec);
     gy = (a.M + mt - 1) / mt;
@@ -486,16 +514,23 @@ int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const in
   return CP_SPEC_OK;
 }
 
-// lm_head logits of M rows (row m reads X row m / xdiv, head head[m]).
-// per_head > 0: on the matrix cores, rows grouped by head (each block finds
-// its head's rows itself), at most per_head rows per head; else per-row GEMV.
+// lm_head logits of M rows (row m reads X row m / xdiv, head head[m], 0 =
+// skip).  per_head > 0: on the matrix cores, rows grouped by head (each block
+// finds its head's rows itself), at most per_head rows per head.  Else the
+// GEMV: rows_per_head > 0 groups the rows of a head in one block (at most
+// that many per head), 0 runs one block per row.  hb: per head and draft
+// offset, the head applied to the offset, added to rows m with m % xdiv in
+// 1..K (see GemvArgs).
 int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv, const int* head,
-                const float* norm_g, float* xnorm_out, float* logits, int per_head = 0) {
+                const float* norm_g, float* xnorm_out, float* logits, int per_head = 0, int rows_per_head = 0,
+                const float* hb = nullptr) {
   GemvArgs a{};
   a.W0 = h->heads; a.N = h->sh.V; a.K = h->sh.H; a.X = X; a.ldx = h->sh.H; a.xdiv = xdiv; a.M = M;
   a.norm_g = norm_g; a.eps = h->sh.eps; a.Y = logits; a.ldy = h->sh.V; a.head = head;
   a.head_stride = static_cast<long long>(h->sh.V) * h->sh.H; a.xnorm_out = xnorm_out;
   a.n_heads = h->sh.G - 1;
+  a.hb = hb;
+  a.hbK = hb != nullptr ? h->sh.K : 0;
   if (per_head > 0 && h->packed_heads != nullptr && a.N % 64 == 0 && a.K % 512 == 0) {
     // bf16, packed heads: 32 x 64 tiles per head
     a.W0 = h->packed_heads;
@@ -512,6 +547,10 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
     CPS_HIP(launch_mfma(h->sh.wdt, kHead, big ? kTile64 : kTile32, a, grid, s));
     return CP_SPEC_OK;
   }
+  if (rows_per_head > 0) {
+    a.hslices = rows_per_head;
+    return gemv(h, s, kHeadG, a);
+  }
   return gemv(h, s, kHead, a);
 }
 
@@ -524,6 +563,21 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
   // many streams: lm_heads on the matrix cores, at most one row per stream
   // and head in each of the draft and verify row sets
   const int per_head = B >= kMfmaMinStreams ? B : 0;
+  if (sh.fd) {
+    // drafts were formed last round; this round's verify tail forms the
+    // next ones: rows (stream, verify row r, k) with k = 0 the target head
+    // and k = 1..W row r's candidate drafts (at most R rows of a stream per
+    // head)
+    if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv)))) return rc;
+    const int W1 = sh.W + 1;
+    if ((rc = head_logits(h, s, B * sh.R * W1, r.X, W1, r.fhead, h->fnorm, r.Hout, r.tlogits,
+                          per_head > 0 ? B * sh.R : 0, B * sh.R,
+                          sh.K > 0 ? h->at<float>(h->lo.hb) : nullptr)))
+      return rc;
+    CPS_HIP(launch_target_topk(r, s));
+    CPS_HIP(launch_round_accept(r, s));
+    return CP_SPEC_OK;
+  }
   if (sh.N >= 2) {
     // draft rows read h_s, or h_s + b_t when the drafter has offsets
     const float* dx = r.K > 0 ? r.dX : r.hstate;
@@ -663,6 +717,24 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
     if (e == hipSuccess) e = hipDeviceSynchronize();
   }
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+  if (e == hipSuccess && s.fd && s.K > 0) {
+    // fused drafts with offsets: hb[j-1][t-1][:] = head_j . b_t, added to
+    // the candidate rows' logits (head_j (h + b_t) = head_j h + head_j b_t)
+    int* d_hd = h->at<int>(lo.dhead);  // K head indices, scratch
+    std::vector<int> hd(s.K);
+    for (int j = 1; j <= s.G - 1 && e == hipSuccess; ++j) {
+      std::fill(hd.begin(), hd.end(), j);
+      e = hipMemcpy(d_hd, hd.data(), s.K * sizeof(int), hipMemcpyHostToDevice);
+      if (e != hipSuccess) break;
+      float* dst = h->at<float>(lo.hb) + static_cast<size_t>(j - 1) * s.K * s.V;
+      if (head_logits(h, h->cap_stream, s.K, h->doff, 1, d_hd, nullptr, nullptr, dst) != CP_SPEC_OK) {
+        e = hipErrorLaunchFailure;
+        break;
+      }
+      e = hipStreamSynchronize(h->cap_stream);
+    }
+    if (e == hipSuccess) e = hipMemset(d_hd, 0, s.maxB * s.W * sizeof(int));
+  }
   if (e != hipSuccess) {
     delete h;
     return fail(CP_SPEC_EHIP, std::string("create: ") + hipGetErrorString(e));
@@ -750,7 +822,7 @@ int cp_spec_head_logits(cp_spec* h, void* stream, int32_t n_rows, const float* d
   hipStream_t s = static_cast<hipStream_t>(stream);
   // many rows: grouped by head on the matrix cores (any number per head)
   return head_logits(h, s, n_rows, d_x, 1, d_head, apply_final_norm ? h->fnorm : nullptr, nullptr,
-                     d_logits, n_rows >= kMfmaMinRows ? n_rows : 0);
+                     d_logits, n_rows >= kMfmaMinRows ? n_rows : 0, n_rows);
 }
 
 int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows, const float* d_logits,

@@ -77,16 +77,30 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   const int tid = threadIdx.x;
   const int rg = tid / KT, kt = tid % KT;
   const int lane = tid % kWave;
-  const int m0 = blockIdx.y * MT;
-  const int Mloc = min(MT, a.M - m0);
-  if (Mloc <= 0) return;
+  const int m0 = MODE == kHeadG ? 0 : blockIdx.y * MT;
+  if (MODE != kHeadG && a.M - m0 <= 0) return;
 
   const WT* W0 = static_cast<const WT*>(a.W0);
+  // kHeadG: the block's rows are slice q of the rows of head j + 1
+  __shared__ int rows_s[MODE == kHeadG ? MT : 1];
+  int hsel = 0;  // the block's head (lm_head modes)
   if (MODE == kHead) {
-    const int h = a.head[m0];
-    if (h <= 0 || h > a.n_heads) return;
-    W0 = W0 + static_cast<size_t>(h - 1) * static_cast<size_t>(a.head_stride);
+    hsel = a.head[m0];
+    if (hsel <= 0 || hsel > a.n_heads) return;
   }
+  int Mg = 0;
+  if (MODE == kHeadG) {
+    __shared__ int red_g[kBlock / kWave];
+    const int j = blockIdx.y / a.hslices, q = blockIdx.y % a.hslices;
+    Mg = head_rows_slice(a.head, a.M, j + 1, q * MT, MT, rows_s, red_g);
+    if (Mg <= 0) return;
+    hsel = j + 1;
+  }
+  if (MODE == kHead || MODE == kHeadG)
+    W0 = W0 + static_cast<size_t>(hsel - 1) * static_cast<size_t>(a.head_stride);
+  // activation row m of the block
+  auto row_of = [&](int m) { return MODE == kHeadG ? rows_s[m] : m0 + m; };
+  const int Mloc = MODE == kHeadG ? Mg : min(MT, a.M - m0);
   const int stride = gridDim.x * RG;
   int ubase = blockIdx.x * RG;
 
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
       for (int e = 0; e < VEC; e += 4) {
         float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (m < Mloc)
-          v = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>((m0 + m) / a.xdiv) * a.ldx + k0 + e);
+          v = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row_of(m) / a.xdiv) * a.ldx + k0 + e);
         const float4 g = gv[j][e / 4];
         ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         xr[m][j][e] = v.x * g.x;
@@ -207,15 +221,19 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         for (int q = 0; q < rows16; ++q) t += part[q][NV + idx % MT];
         ri = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
       }
-      if (MODE == kHead && a.xnorm_out != nullptr && blockIdx.x == 0 && rg == 0) {
-        float t = 0.0f;
-        for (int q = 0; q < rows16; ++q) t += part[q][NV];
-        const float r0 = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+      if ((MODE == kHead || MODE == kHeadG) && a.xnorm_out != nullptr && blockIdx.x == 0 && rg == 0) {
 #pragma unroll
-        for (int j = 0; j < SPT; ++j)
+        for (int m = 0; m < MT; ++m) {
+          if (m >= Mloc || row_of(m) % a.xdiv != 0) continue;
+          float t = 0.0f;
+          for (int q = 0; q < rows16; ++q) t += part[q][NV + m];
+          const float r0 = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+          float* dst = a.xnorm_out + static_cast<size_t>(row_of(m) / a.xdiv) * a.K;
 #pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            a.xnorm_out[static_cast<size_t>(m0) * a.K + (kt + KT * j) * VEC + e] = xr[0][j][e] * r0;
+          for (int j = 0; j < SPT; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dst[(kt + KT * j) * VEC + e] = xr[m][j][e] * r0;
+        }
       }
     }
     // ---- fused epilogue ----
@@ -239,10 +257,15 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         for (int q = 0; q < rows16; ++q) val += part[g * rows16 + q][idx];
         val *= ri;
         const int o = u * RPG + rp;
-        const int row = m0 + m;
+        const int row = row_of(m);
         if (MODE == kAdd) {
           a.Y[static_cast<size_t>(row) * a.ldy + o] = yold + val;
-        } else if (MODE == kHead || MODE == kStore) {
+        } else if (MODE == kHead || MODE == kHeadG) {
+          const int k = row % a.xdiv;
+          if (a.hb != nullptr && k >= 1 && k <= a.hbK)
+            val += a.hb[(static_cast<size_t>(hsel - 1) * a.hbK + (k - 1)) * a.N + o];
+          a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+        } else if (MODE == kStore) {
           a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
         } else if (MODE == kQKV) {
           if (o < a.qdim) {
@@ -290,6 +313,9 @@ hipError_t launch_gemv_t(int mode, int mt, const GemvArgs& a, int grid_x, int gr
   CPS_GEMV_MT(kSwiGLU)
   CPS_GEMV_MT(kQKV)
   CPS_GEMV_SPT(kHead, 1)
+  CPS_GEMV_SPT(kHeadG, 2)
+  CPS_GEMV_SPT(kHeadG, 4)
+  CPS_GEMV_SPT(kHeadG, 8)
 #undef CPS_GEMV_MT
 #undef CPS_GEMV_SPT
 #undef CPS_GEMV_CASE

@@ -23,6 +23,9 @@ enum GemvMode : int {
   kSwiGLU = 2,  // Y[m][o] = silu(gate) * up  (W0 = gate, W1 = up)
   kQKV = 3,     // q -> Y, k/v -> KV cache at the row's position
   kHead = 4,    // per-row lm_head: W = heads[head[m] - 1]
+  kHeadG = 5,   // lm_heads, rows grouped by head: each head's weights read
+                // once for all its rows (few rows; the matrix-core paths
+                // group by head themselves)
 };
 
 struct GemvArgs {
@@ -51,7 +54,13 @@ struct GemvArgs {
   const int* head;      // [M] head index 1..n_heads, 0 = skip
   int n_heads;          // G-1
   long long head_stride;  // elements per head matrix (V*H)
-  float* xnorm_out;     // nullable: normalised rows written here ([M][K])
+  float* xnorm_out;     // nullable: normalised X rows written here, by the
+                        // rows m with m % xdiv == 0, at X row m / xdiv
+  // lm_heads: row m with k = m % xdiv in 1..hbK adds hb[(head - 1) * hbK +
+  // k - 1][o] to its logits (the heads applied to the draft offsets b_k)
+  const float* hb;
+  int hbK;
+  int hslices;          // kHeadG: row slices of MT per head (grid y = heads x slices)
   // tiling (host-chosen)
   int kt;     // threads covering one row's K (64/128/256)
   int units;  // number of RPG-row output units
@@ -183,8 +192,17 @@ struct RoundArgs {
   float* q;        // [B][W][V]
   int* dcode;      // [B][W]
   uint32_t* dflags;  // [B][W]
-  float* tlogits;  // [B][R][V]
+  float* tlogits;  // [B][R][V]; fused drafts: [B][R][W + 1][V], column 0
   float* p;        // [B][R][V]
+  // fused drafts: rows (b, r, k) of the heads launch (k = 0 target, k >= 1
+  // row r's candidate draft of offset k), their heads, and every row's
+  // candidate drafts (distributions, codes, flags) until the accept step
+  // keeps the set of the row that ends the round
+  int fused;
+  int* fhead;      // [B][R][W + 1]
+  float* cq;       // [B][R][W][V]
+  int* ccode;      // [B][R][W]
+  uint32_t* cflags;  // [B][R][W]
   int* tcode;      // [B][R]
   uint32_t* tflags;  // [B][R]
 };

@@ -529,6 +529,18 @@ __device__ __forceinline__ void set_frame_seed(StreamState& st, uint64_t seed) {
   st.seed_hi = static_cast<uint32_t>(seed >> 32);
 }
 
+// Fused drafts: the heads of verify row rr of stream b in the next heads
+// launch, given its target head th (0 = inactive row): column 0 the target,
+// column k = 1..W the candidate draft of offset k, head th + k while the
+// round that row rr would end can draft that far (k <= min(N-1, G-2-th)).
+// Called by every thread; thread i < W + 1 writes column i.
+__device__ __forceinline__ void fused_row_heads(const RoundArgs& r, int b, int rr, int th, int i) {
+  if (i > r.W) return;
+  int v = 0;
+  if (th > 0) v = i == 0 ? th : (i <= min(r.N - 1, r.G - 2 - th) ? th + i : 0);
+  r.fhead[(static_cast<size_t>(b) * r.R + rr) * (r.W + 1) + i] = v;
+}
+
 // Prefill of frame f for stream b: rows [h_frame, E_0[c_0]] at positions 0, 1
 // and head 1 on row 1.  Rows wider than the block are copied with every load
 // issued before the stores (16-byte pieces when aligned): one memory round
@@ -567,6 +579,11 @@ __device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int 
     }
     for (int t = 0; t < r.W; ++t) r.dhead[b * r.W + t] = 0;
   }
+  if (r.fused) {  // row 1 scores c_1 and drafts the first round from h_1
+    const int W1 = r.W + 1;
+    if (static_cast<int>(threadIdx.x) < r.R * W1)
+      fused_row_heads(r, b, threadIdx.x / W1, threadIdx.x / W1 == 1 ? 1 : 0, threadIdx.x % W1);
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, const CallDesc c) {
@@ -588,6 +605,8 @@ __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, c
       }
       for (int t = 0; t < r.W; ++t) r.dhead[b * r.W + t] = 0;
     }
+    if (r.fused && static_cast<int>(threadIdx.x) < r.R * (r.W + 1))
+      fused_row_heads(r, b, threadIdx.x / (r.W + 1), 0, threadIdx.x % (r.W + 1));
   }
   if (threadIdx.x == 0) r.st[b] = st;
   if (r.tnodes > 0 && threadIdx.x == 0) r.ncode[static_cast<size_t>(b) * 8] = 0;  // no K/V move pending
@@ -677,15 +696,56 @@ hipError_t launch_draft_topk(const RoundArgs& r, hipStream_t s) {
 // (accepted) or the row's draw; tflags the row's top-k / argmax flags, its
 // accept-test and CDF near ties, and kRowAccepted (chain) or the accepted
 // child + 1 in bits 16..23 (tree).
+// Fused drafts: block (rr, k >= 1) forms row rr's candidate draft of offset
+// k instead: q = TopKSoftmax of its logits (dense, kept for the next round's
+// test), the draw with U(depth, draft) (greedy: the argmax), its flags.
+template <int VPT>
+__device__ void candidate_draft(const RoundArgs& r, int b, int rr, int k, SelSmem& S, float4* row_dyn,
+                                uint64_t* red64, uint32_t* red32) {
+  const size_t frow = (static_cast<size_t>(b) * r.R + rr) * (r.W + 1) + k;
+  const int head = r.fhead[frow];
+  const StreamState st = r.st[b];
+  float zv[VPT];
+  load_row<VPT>(r.tlogits + frow * r.V, zv);
+  if (head <= 0 || st.mode == kModeDone) return;
+  const size_t crow = (static_cast<size_t>(b) * r.R + rr) * r.W + (k - 1);
+  if (r.greedy) {
+    const TopkResult res = argmax_regs<VPT>(zv, red64, red32);
+    if (threadIdx.x == 0) {
+      r.ccode[crow] = res.code;
+      r.cflags[crow] = res.flags;
+    }
+    return;
+  }
+  const float u = frame_uniform(frame_seed(st), head, kDraft);
+  const RowLds L = row_lds(row_dyn, r.V, true);
+  store_row<VPT>(zv, L.z);
+  int total;
+  uint32_t flags = 0;
+  if (!topk_list<VPT>(zv, r.top_k, r.T, L, S, r.cq + crow * r.V, &total, &flags)) return;
+  int code, near;
+  list_draw(L.lw, L.lidx, total, u, &code, &near);
+  if (near) flags |= kFlagCdf;
+  if (threadIdx.x == 0) {
+    r.ccode[crow] = code;
+    r.cflags[crow] = flags;
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) {
   extern __shared__ float4 row_dyn[];
   __shared__ SelSmem S;
   __shared__ uint64_t red64[4];
   __shared__ uint32_t red32[4];
-  const int rr = blockIdx.x, b = blockIdx.y;
+  const int W1 = r.fused ? r.W + 1 : 1;
+  const int rr = blockIdx.x / W1, kc = blockIdx.x % W1, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.R + rr;
   dispatch_vpt(r.V, [&](auto vpt) {
     constexpr int VPT = decltype(vpt)::value;
+    if (kc > 0) {
+      candidate_draft<VPT>(r, b, rr, kc, S, row_dyn, red64, red32);
+      return;
+    }
     const int base = threadIdx.x * VPT;
     // every load that depends only on the block goes out at once (one memory
     // round trip, not three): the row's head and the stream's state first, so
@@ -696,7 +756,7 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     const int head = r.thead[row];
     const StreamState st = r.st[b];
     float zv[VPT];
-    load_row<VPT>(r.tlogits + row * r.V, zv);
+    load_row<VPT>(r.tlogits + row * W1 * r.V, zv);
     const int qi = r.tnodes > 0 ? r.dep[rr] : rr;
     const bool has_q = !r.greedy && qi < r.W;
     float qv[VPT];
@@ -762,7 +822,8 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
 }
 
 hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s) {
-  hipLaunchKernelGGL(target_topk_kernel, dim3(r.R, r.B), dim3(kBlock), row_lds_bytes(r.V, true), s, r);
+  const int W1 = r.fused ? r.W + 1 : 1;
+  hipLaunchKernelGGL(target_topk_kernel, dim3(r.R * W1, r.B), dim3(kBlock), row_lds_bytes(r.V, true), s, r);
   return hipGetLastError();
 }
 
@@ -772,6 +833,37 @@ __device__ __forceinline__ void count_flags(uint32_t f, cp_spec_stats* cnt) {
   if (f & kFlagArgmax) ++cnt->near_tie_argmax;
   if (f & kFlagCdf) ++cnt->near_tie_cdf;
   if (f & kFlagAccept) ++cnt->near_tie_accept;
+}
+
+// Fused drafts, next round of stream b at committed depth s with gamma
+// drafts: the candidate set of the verify row that ended this round (hrow,
+// whose output is h_s) becomes the round's drafts (codes, flags and dense
+// distributions, as the draft kernel leaves them), the verify rows E_s[c_s]
+// and E_{s+t}[d_t] are gathered, and the rows' heads for the next heads
+// launch are set.  Every thread of the block calls it.
+__device__ void fused_next_round(const RoundArgs& r, int b, int s, int gamma, int hrow, int last) {
+  const int tid = threadIdx.x;
+  const size_t cb = (static_cast<size_t>(b) * r.R + hrow) * r.W;
+  const int V4 = r.V / 4;
+  const float4* src = reinterpret_cast<const float4*>(r.cq + cb * r.V);
+  float4* dst = reinterpret_cast<float4*>(r.q + static_cast<size_t>(b) * r.W * r.V);
+  for (int i = tid; i < gamma * V4; i += kBlock) dst[i] = src[i];
+  if (tid < gamma) {
+    r.dcode[static_cast<size_t>(b) * r.W + tid] = r.ccode[cb + tid];
+    r.dflags[static_cast<size_t>(b) * r.W + tid] = r.cflags[cb + tid];
+  }
+  // the gamma + 1 verify rows side by side, a group of threads each
+  const int nrow = gamma + 1, per = kBlock / nrow;
+  const int k = tid / per;
+  if (k < nrow) {
+    const int code = k == 0 ? last : r.ccode[cb + k - 1];
+    embed_row_span(r, s + k, code, r.X + (static_cast<size_t>(b) * r.R + k) * r.H, tid - k * per, per);
+  }
+  const int W1 = r.W + 1;
+  if (tid < r.R * W1) {
+    const int rr = tid / W1;
+    fused_row_heads(r, b, rr, rr <= gamma ? s + 1 + rr : 0, tid % W1);
+  }
 }
 
 // Candidate rows of h_{s+n} held in registers while the outcome is decided:
@@ -942,6 +1034,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
         r.thead[rb + tid] = 0;
       }
       if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = 0;
+      if (r.fused && tid < r.R * (r.W + 1)) fused_row_heads(r, b, tid / (r.W + 1), 0, tid % (r.W + 1));
     } else {
       st.mode = kModePrefill;
       set_frame_seed(st, c.seeds[static_cast<size_t>(st.f) * c.B + b]);
@@ -959,6 +1052,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
       r.thead[rb + tid] = tid <= gamma ? s + 1 + tid : 0;
     }
     if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = tid + 1 <= gamma ? s + tid + 1 : 0;
+    if (r.fused) fused_next_round(r, b, s, gamma, sh_hrow, st.last);
   }
   if (tid == 0) r.st[b] = st;
 }

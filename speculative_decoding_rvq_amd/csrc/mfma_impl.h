@@ -71,12 +71,21 @@ __device__ __forceinline__ void write_xnorm(const GemvArgs& a, const int* rows_s
   for (int idx = threadIdx.x; idx < count * w; idx += kBlock) {
     const int r = idx / w, c = 4 * (c0 + idx % w);
     const int row = rows_s[r];
+    if (row % a.xdiv != 0) continue;  // one writer per X row
     const float4 x = *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row / a.xdiv) * a.ldx + c);
     const float4 g = *reinterpret_cast<const float4*>(a.norm_g + c);
     const float ri = rinv_s[r];
-    *reinterpret_cast<float4*>(a.xnorm_out + static_cast<size_t>(row) * a.K + c) =
+    *reinterpret_cast<float4*>(a.xnorm_out + static_cast<size_t>(row / a.xdiv) * a.K + c) =
         make_float4(x.x * g.x * ri, x.y * g.y * ri, x.z * g.z * ri, x.w * g.w * ri);
   }
+}
+
+// lm_head rows m with k = m % xdiv in 1..hbK: head j+1 applied to draft
+// offset b_k (added to the row's logits); 0 otherwise.
+__device__ __forceinline__ float head_bias(const GemvArgs& a, int j, int row, int o) {
+  const int k = row % a.xdiv;
+  if (a.hb == nullptr || k < 1 || k > a.hbK) return 0.0f;
+  return a.hb[(static_cast<size_t>(j) * a.hbK + (k - 1)) * a.N + o];
 }
 
 struct GemmSmemF32 {
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(kBlock) void mfma_gemm_kernel(const GemvArgs a) {
     if (MODE == kAdd) {
       a.Y[static_cast<size_t>(row) * a.ldy + o] += val;
     } else if (MODE == kHead) {
-      a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+      a.Y[static_cast<size_t>(row) * a.ldy + o] = val + head_bias(a, blockIdx.z, row, o);
     } else if (MODE == kQKV) {
       if (o < a.qdim) {
         a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(kBlock) void mfma_splitk_kernel(const GemvArgs a) {
     if (MODE == kAdd) {
       a.Y[static_cast<size_t>(row) * a.ldy + o] += val;
     } else if (MODE == kHead) {
-      a.Y[static_cast<size_t>(row) * a.ldy + o] = val;
+      a.Y[static_cast<size_t>(row) * a.ldy + o] = val + head_bias(a, blockIdx.z, row, o);
     } else if (MODE == kQKV) {
       if (o < a.qdim) {
         a.Y[static_cast<size_t>(row) * a.ldy + o] = val;

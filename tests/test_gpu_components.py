@@ -27,13 +27,16 @@ def _t(a, dtype=None):
 
 
 @pytest.mark.parametrize("cid,rows", [("tiny", 6), ("qwen3tts", 8),
+                                      ("qwen3tts", 24), ("tiny", 31),
                                       ("tiny", 77), ("qwen3tts", 133),
                                       ("wide-256", 70), ("tiny", 4100)])
 @pytest.mark.parametrize("norm", [0, 1])
 def test_head_logits(cid, rows, norm):
-    """Few rows run one GEMV block per row; 32 or more rows are grouped by
-    head into matrix-core tiles (ragged last tile per head): 32 x 32
-    split-K tiles for few rows per head, 64 x 64 tiles for many."""
+    """Fewer than 32 rows run the GEMV with the rows of a head in one block
+    (24 and 31 rows share three heads: several blocks per head); 32 or more
+    rows are grouped by head into matrix-core tiles (ragged last tile per
+    head): 32 x 32 split-K tiles for few rows per head, 64 x 64 tiles for
+    many."""
     log(f"head_logits {cid} rows={rows} norm={norm}")
     c = synth.config(cid)
     m = oracle_model(cid)
@@ -42,6 +45,8 @@ def test_head_logits(cid, rows, norm):
     rng = np.random.default_rng(10 + len(cid) + rows)
     x = rng.standard_normal((rows, c["hidden"])).astype(np.float32)
     heads = rng.integers(1, c["groups"], size=rows).astype(np.int32)
+    if 16 < rows < 32:
+        heads = rng.integers(1, 4, size=rows).astype(np.int32)
     heads[1] = 0                                   # a skipped row
     if rows > 64:
         heads[:70 if rows > 70 else 66] = 2        # one head spans two tiles

@@ -54,6 +54,7 @@ extern "C" {
 #define CP_SPEC_MAX_VOCAB 4096
 #define CP_SPEC_MAX_GROUPS 32
 #define CP_SPEC_MAX_WINDOW 8
+#define CP_SPEC_MAX_TREE 63   /* tree window nodes (the root not counted) */
 #define CP_SPEC_MAX_OFFSETS 8
 
 /* Near-tie flag bits reported per decision by the component entry points. */
@@ -101,17 +102,23 @@ typedef struct cp_spec_cfg {
    * (EUNSUPPORTED with a tree); ignored when verify_size < 2. */
   int32_t fused_draft;
   /* Tree-shaped verify window ("RVQ Position Aware ...", section 2.2 and
-   * Figure 2).  tree_nodes = T in 1..7 replaces the chain window (verify_size
-   * is then ignored; the verify block has T + 1 rows); 0 = the chain.
-   * tree_parent[i - 1] is the parent of node i (0 = the root, the committed
-   * code; a parent precedes its children).  A node at depth d draws the code
-   * of depth s + d from that depth's draft distribution; the round walks
-   * down from the root testing a node's children in order with min(1, p'/q)
-   * and replacing p' by norm(max(0, p' - q)) after each rejection, and draws
-   * from p' when no child is accepted.  Stochastic decoding only, at most 7
-   * streams, code_groups + T <= 32 (CP_SPEC_EUNSUPPORTED otherwise). */
+   * Figure 2).  tree_nodes = T in 1..63 replaces the chain window
+   * (verify_size is then ignored; the verify block has T + 1 rows); 0 = the
+   * chain.  tree_parent[i - 1] is the parent of node i (0 = the root, the
+   * committed code; a parent precedes its children); depth at most 7.
+   * Sampled: a node at depth d draws the code of depth s + d from that
+   * depth's draft distribution (the j-th node of the depth with uniform
+   * index j); the round walks down from the root testing a node's children
+   * in order with min(1, p'/q) and replacing p' by norm(max(0, p' - q))
+   * after each rejection, and draws from p' when no child is accepted.
+   * Greedy: the k-th child of a node proposes the k-th highest draft logit
+   * of its depth; the walk takes the first child equal to the node's target
+   * argmax, else commits that argmax.  Nodes deeper than the frame allows
+   * are left out of a round.  Sibling rows share their lm_head: the heads
+   * launch reads each head once for all of them.
+   * CP_SPEC_EUNSUPPORTED when the attention tile cannot fit LDS. */
   int32_t tree_nodes;
-  int32_t tree_parent[8];
+  int32_t tree_parent[CP_SPEC_MAX_TREE];
 } cp_spec_cfg;
 
 typedef struct cp_spec_weights {

@@ -22,6 +22,7 @@ EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
 F32, BF16 = 0, 1
 FLAG_TOPK, FLAG_ARGMAX, FLAG_CDF, FLAG_ACCEPT = 1, 2, 4, 8
 MAX_OFFSETS = 8
+MAX_TREE = 63
 
 
 class Cfg(C.Structure):
@@ -35,7 +36,7 @@ class Cfg(C.Structure):
                 ("top_k", C.c_int32), ("max_streams", C.c_int32),
                 ("draft_offsets", C.c_int32), ("fused_draft", C.c_int32),
                 ("tree_nodes", C.c_int32),
-                ("tree_parent", C.c_int32 * 8)]
+                ("tree_parent", C.c_int32 * MAX_TREE)]
 
 
 class Weights(C.Structure):
@@ -151,7 +152,8 @@ def make_cfg(c: dict, max_streams: int | None = None) -> Cfg:
                draft_offsets=int(c.get("draft_offsets", 0)),
                fused_draft=int(c.get("fused_draft", 0)),
                tree_nodes=len(c.get("tree") or ()),
-               tree_parent=(C.c_int32 * 8)(*(list(c.get("tree") or ()) + [0] * 8)[:8]))
+               tree_parent=(C.c_int32 * MAX_TREE)(
+                   *(list(c.get("tree") or ()) + [0] * MAX_TREE)[:MAX_TREE]))
 
 
 def workspace_bytes(cfg: Cfg) -> int:

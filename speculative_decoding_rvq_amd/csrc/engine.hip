@@ -43,7 +43,9 @@ struct Shape {
   // i (node 0 = the root), K/V positions per stream (the frame's G plus one
   // slot per node)
   int tn, td, Gk;
-  int par[8], dep[8];
+  int par[kTreeSlots], dep[kTreeSlots];
+  int tw;   // the most nodes at one depth (rows that share a head)
+  int trb;  // tree attention: rows per block
 };
 
 struct Layout {
@@ -84,8 +86,8 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   }
   if (c->draft_offsets < 0 || c->draft_offsets > CP_SPEC_MAX_OFFSETS)
     return fail(CP_SPEC_EINVAL, "draft_offsets must be in 0..8");
-  if (c->tree_nodes < 0 || c->tree_nodes > CP_SPEC_MAX_WINDOW - 1)
-    return fail(CP_SPEC_EINVAL, "tree_nodes must be in 0..7");
+  if (c->tree_nodes < 0 || c->tree_nodes > CP_SPEC_MAX_TREE)
+    return fail(CP_SPEC_EINVAL, "tree_nodes must be in 0..63");
   for (int i = 1; i <= c->tree_nodes; ++i)
     if (c->tree_parent[i - 1] < 0 || c->tree_parent[i - 1] >= i)
       return fail(CP_SPEC_EINVAL, "tree_parent[i-1] must be in 0..i-1");
@@ -93,10 +95,13 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   if (c->fused_draft && c->tree_nodes > 0)
     return fail(CP_SPEC_EUNSUPPORTED, "fused_draft runs chain windows only");
   if (c->tree_nodes > 0) {
-    if (c->greedy) return fail(CP_SPEC_EUNSUPPORTED, "tree windows decode stochastically only");
-    if (c->max_streams > 7) return fail(CP_SPEC_EUNSUPPORTED, "tree windows run on at most 7 streams");
-    if (c->code_groups + c->tree_nodes > 32)
-      return fail(CP_SPEC_EUNSUPPORTED, "code_groups + tree_nodes must be at most 32");
+    int dep[kTreeSlots] = {0};
+    for (int i = 1; i <= c->tree_nodes; ++i) {
+      dep[i] = dep[c->tree_parent[i - 1]] + 1;
+      if (dep[i] > CP_SPEC_MAX_WINDOW - 1) return fail(CP_SPEC_EINVAL, "tree depth must be at most 7");
+    }
+    if (c->code_groups + c->tree_nodes > kMaxKeys)
+      return fail(CP_SPEC_EUNSUPPORTED, "code_groups + tree_nodes must be at most 128");
   }
   if (c->vocab > CP_SPEC_MAX_VOCAB)
     return fail(CP_SPEC_EUNSUPPORTED, "vocab above the small-vocabulary bound (4096)");
@@ -132,7 +137,13 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
     }
     s_.N = s_.td + 1;  // codes a round commits at most
   }
-  for (int i = s_.tn + 1; i < 8; ++i) s_.par[i] = -1, s_.dep[i] = 0;
+  for (int i = s_.tn + 1; i < kTreeSlots; ++i) s_.par[i] = -1, s_.dep[i] = 0;
+  s_.tw = 1;
+  for (int d = 1; d <= s_.td; ++d) {
+    int n = 0;
+    for (int i = 1; i <= s_.tn; ++i) n += s_.dep[i] == d ? 1 : 0;
+    s_.tw = std::max(s_.tw, n);
+  }
   s_.Gk = s_.G + s_.tn;
   s_.R = s_.tn > 0 ? s_.tn + 1 : std::max(s_.N, 2);
   s_.W = s_.tn > 0 ? s_.td : std::max(s_.N - 1, 1);
@@ -146,8 +157,12 @@ int validate(const cp_spec_cfg* c, Shape* s, bool* warn_ar) {
   for (int N_ : {s_.qdim + 2 * s_.kvdim, s_.H, s_.V, s_.kvdim, s_.qdim})
     if (N_ % kRPGHost) return fail(CP_SPEC_EUNSUPPORTED, "output width must be a multiple of 4");
   if (s_.F % 2) return fail(CP_SPEC_EUNSUPPORTED, "ffn must be even");
-  if (attention_smem_bytes(s_.G, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024 ||
-      tree_attention_smem_bytes(s_.Gk, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024)
+  // tree attention: the most rows per block (a power of two) whose tile fits
+  s_.trb = 0;
+  if (s_.tn > 0)
+    for (int rb = 64; rb >= 1 && !s_.trb; rb /= 2)
+      if (tree_attention_smem_bytes(s_.Gk, s_.d, rb, s_.nq / s_.nkv) <= 160 * 1024) s_.trb = std::min(rb, s_.R);
+  if (attention_smem_bytes(s_.G, s_.d, s_.R, s_.nq / s_.nkv) > 160 * 1024 || (s_.tn > 0 && s_.trb == 0))
     return fail(CP_SPEC_EUNSUPPORTED, "attention tile (positions x head_dim x query group) exceeds LDS");
   return CP_SPEC_OK;
 }
@@ -200,7 +215,7 @@ Layout make_layout(const Shape& s) {
   l.attn = take(B * R * s.qdim * f4);
   l.act = take(B * R * s.F * f4);
   l.kv = take(B * static_cast<size_t>(s.L) * 2 * s.Gk * s.kvdim * f4);
-  l.ncode = take(B * 8 * i4);  // tree window: the code of every node
+  l.ncode = take(B * kTreeSlots * i4);  // tree window: the code of every node
   l.dlogits = take(B * W * s.V * f4);
   l.q = take(B * W * s.V * f4);
   l.dcode = take(B * W * i4);
@@ -259,7 +274,7 @@ struct cp_spec {
     r.B = B; r.R = sh.R; r.W = sh.W; r.G = sh.G; r.V = sh.V; r.H = sh.H; r.N = sh.N;
     r.greedy = sh.greedy; r.top_k = sh.top_k; r.L = sh.L; r.T = sh.T;
     r.tnodes = sh.tn; r.tdepth = sh.td; r.Gk = sh.Gk; r.kvdim = sh.kvdim;
-    for (int i = 0; i < 8; ++i) r.par[i] = sh.par[i], r.dep[i] = sh.dep[i];
+    for (int i = 0; i < kTreeSlots; ++i) r.par[i] = sh.par[i], r.dep[i] = sh.dep[i];
     r.kv = at<float>(lo.kv);
     r.kv_sb = kv_sb();
     r.ncode = at<int>(lo.ncode);
@@ -461,9 +476,10 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       if (fused) at.planes = P1, at.ptiles = T;
       if (sh.tn > 0) {  // tree window: node slots and ancestor masks
         at.Gk = sh.Gk;
-        for (int i = 0; i < 8; ++i) {
+        at.RB = sh.trb;
+        for (int i = 0; i < kTreeSlots; ++i) {
           at.dep[i] = sh.dep[i];
-          at.anc[i] = (i >= 1 && i <= sh.tn) ? (1u << i) | at.anc[sh.par[i]] : 0u;
+          at.anc[i] = (i >= 1 && i <= sh.tn) ? (1ull << i) | at.anc[sh.par[i]] : 0ull;
         }
         CPS_HIP(launch_tree_attention(at, B, s));
         return CP_SPEC_OK;
@@ -561,8 +577,11 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
   const RoundArgs r = h->round_args(B);
   int rc;
   // many streams: lm_heads on the matrix cores, at most one row per stream
-  // and head in each of the draft and verify row sets
+  // and head in the draft row set; in the verify row set a tree's nodes of
+  // one depth share their head (tw of them)
   const int per_head = B >= kMfmaMinStreams ? B : 0;
+  const int per_head_t = per_head * sh.tw;
+  const int rows_head_t = sh.tn > 0 ? B * sh.tw : 0;  // few streams: grouped GEMV
   if (sh.fd) {
     // drafts were formed last round; this round's verify tail forms the
     // next ones: rows (stream, verify row r, k) with k = 0 the target head
@@ -587,7 +606,9 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
     CPS_HIP(sh.tn > 0 ? launch_tree_draft(r, s) : launch_draft_topk(r, s));
   }
   if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv)))) return rc;
-  if ((rc = head_logits(h, s, B * sh.R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head))) return rc;
+  if ((rc = head_logits(h, s, B * sh.R, r.X, 1, r.thead, h->fnorm, r.Hout, r.tlogits, per_head_t,
+                        rows_head_t)))
+    return rc;
   CPS_HIP(launch_target_topk(r, s));
   CPS_HIP(sh.tn > 0 ? launch_tree_accept(r, s) : launch_round_accept(r, s));
   return CP_SPEC_OK;
@@ -685,7 +706,7 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
     e = hipMemcpy(h->at<char>(lo.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = attention_allow_smem(s.d, attention_smem_bytes(s.G, s.d, s.R, s.nq / s.nkv));
   if (e == hipSuccess && s.tn > 0)
-    e = tree_attention_allow_smem(s.d, tree_attention_smem_bytes(s.Gk, s.d, s.R, s.nq / s.nkv));
+    e = tree_attention_allow_smem(s.d, tree_attention_smem_bytes(s.Gk, s.d, s.trb, s.nq / s.nkv));
   if (e == hipSuccess && packs_weights(s)) {
     // fragment-packed copies of every bf16 matrix (read once, here)
     uint16_t* p = h->at<uint16_t>(lo.packed);

@@ -10,6 +10,13 @@ namespace cps {
 
 constexpr int kRPGHost = 4;   // output widths must be multiples of this
 
+// Tree window: nodes (the root not counted), per-stream node slots (slot 0
+// of a stream's node-code array holds the pending K/V move), and the most
+// attention keys of a row (the frame's positions plus the nodes).
+constexpr int kMaxTree = CP_SPEC_MAX_TREE;
+constexpr int kTreeSlots = kMaxTree + 1;
+constexpr int kMaxKeys = 128;
+
 // GEMV weight rows per row group per unit: 4, or 2 when a thread holds three
 // or more 16-byte chunks of each row.
 __host__ __device__ constexpr int gemv_rpg(int spt) { return spt >= 3 ? 2 : 4; }
@@ -92,11 +99,12 @@ struct AttnArgs {
   const float2* rope; // [G][d/2] (cos, sin)
   int R, nq, nkv, d, G;
   float scale;
-  // tree window: K/V positions per stream (G + nodes), node depths, and per
-  // row the nodes it attends to (bit i = node i, itself included)
-  int Gk;
-  int dep[8];
-  uint32_t anc[8];
+  // tree window: K/V positions per stream (G + nodes), rows per block (the
+  // grid's third axis covers the R rows), node depths, and per row the nodes
+  // it attends to (bit i = node i, itself included)
+  int Gk, RB;
+  int dep[kTreeSlots];
+  uint64_t anc[kTreeSlots];
 };
 
 struct TopkArgs {
@@ -182,10 +190,10 @@ struct RoundArgs {
   // tree window (T > 0): nodes, depth, node parents and depths, the K/V
   // cache of the round's streams, every node's code
   int tnodes, tdepth, Gk, kvdim;
-  int par[8], dep[8];
+  int par[kTreeSlots], dep[kTreeSlots];
   float* kv;          // [B][L][2][Gk][kvdim]
   long long kv_sb;
-  int* ncode;         // [B][8]
+  int* ncode;         // [B][kTreeSlots]
   float* X;        // [B][R][H]
   float* Hout;     // [B][R][H]
   float* dlogits;  // [B][W][V]
@@ -254,7 +262,8 @@ hipError_t launch_target_topk(const RoundArgs& r, hipStream_t s);
 hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s);
 // Tree window: node draws, ancestor-masked attention, the walk and commit.
 hipError_t launch_tree_draft(const RoundArgs& r, hipStream_t s);
-size_t tree_attention_smem_bytes(int Gk, int d, int R, int group);
+// LDS of one tree-attention block (RB rows of a stream, one KV head).
+size_t tree_attention_smem_bytes(int Gk, int d, int RB, int group);
 hipError_t tree_attention_allow_smem(int d, size_t bytes);
 hipError_t launch_tree_attention(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_tree_accept(const RoundArgs& r, hipStream_t s);

@@ -609,7 +609,7 @@ __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, c
       fused_row_heads(r, b, threadIdx.x / (r.W + 1), 0, threadIdx.x % (r.W + 1));
   }
   if (threadIdx.x == 0) r.st[b] = st;
-  if (r.tnodes > 0 && threadIdx.x == 0) r.ncode[static_cast<size_t>(b) * 8] = 0;  // no K/V move pending
+  if (r.tnodes > 0 && threadIdx.x == 0) r.ncode[static_cast<size_t>(b) * kTreeSlots] = 0;  // no K/V move pending
 }
 
 hipError_t launch_round_init(const RoundArgs& r, const CallDesc& c, hipStream_t s) {
@@ -782,13 +782,16 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     // the row's children: chain row rr < gamma tests draft rr + 1; a tree
     // row its node's children within the round's depth
     const int gamma = spec ? st.gamma : 0;
+    __shared__ int kids_s[kMaxTree];  // a tree row's active children, node order
     int nk = 0;
-    int kids[CP_SPEC_MAX_WINDOW];
     if (r.tnodes == 0) {
-      if (spec && rr < gamma) kids[nk++] = 0;
+      nk = spec && rr < gamma ? 1 : 0;
     } else if (spec) {
       for (int ch = 1; ch <= r.tnodes; ++ch)
-        if (r.par[ch] == rr && r.dep[ch] <= gamma) kids[nk++] = ch;
+        if (r.par[ch] == rr && r.dep[ch] <= gamma) {
+          if (threadIdx.x == 0) kids_s[nk] = ch;
+          ++nk;
+        }
     }
     const uint64_t seed = frame_seed(st);
     const int depth = spec ? st.s + (r.tnodes > 0 ? r.dep[rr] : rr) + 1 : 1;
@@ -806,11 +809,12 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       acc = walk_step(L, total, r.V, nk, [&](int) { return dd; }, [&](int) { return ua0; }, ut, &code, &flags);
       if (acc == 0) flags |= kRowAccepted;
     } else {
-      acc = walk_step(L, total, r.V, nk, [&](int k) { return r.ncode[static_cast<size_t>(b) * 8 + kids[k]]; },
+      acc = walk_step(L, total, r.V, nk,
+                      [&](int k) { return r.ncode[static_cast<size_t>(b) * kTreeSlots + kids_s[k]]; },
                       [&](int k) { return k == 0 ? ua0 : frame_uniform(seed, depth, kAccept, k); }, ut, &code,
                       &flags);
       if (acc >= 0) {
-        flags |= static_cast<uint32_t>(kids[acc] + 1) << 16;
+        flags |= static_cast<uint32_t>(kids_s[acc] + 1) << 16;
         code = -1;
       }
     }
@@ -1176,7 +1180,8 @@ __device__ void tree_kv_move(const RoundArgs& r, int b, int s, int v, int part) 
 __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
   extern __shared__ float4 row_dyn[];
   __shared__ SelSmem S;
-  __shared__ int tcode_s[CP_SPEC_MAX_WINDOW], tnode_s[CP_SPEC_MAX_WINDOW], nd_s;
+  __shared__ int tcode_s[kMaxTree], tnode_s[kMaxTree], nd_s;
+  __shared__ int rank_s[kTreeSlots];  // greedy: the depth's top m + 1 codes in order
   const int d = blockIdx.x + 1, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.W + (d - 1);
   dispatch_vpt(r.V, [&](auto vpt) {
@@ -1184,7 +1189,7 @@ __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
     float zv[VPT];
     load_row<VPT>(r.dlogits + row * r.V, zv);  // before the state: the row always exists
     const StreamState st = r.st[b];
-    const int pend = r.ncode[static_cast<size_t>(b) * 8];
+    const int pend = r.ncode[static_cast<size_t>(b) * kTreeSlots];
     if (st.mode != kModeSpec) return;
     if (pend > 0) tree_kv_move(r, b, pend >> 8, pend & 0xFF, d - 1);
     float* x0 = r.X + static_cast<size_t>(b) * r.R * r.H;
@@ -1196,33 +1201,87 @@ __global__ __launch_bounds__(kBlock) void tree_draft_kernel(const RoundArgs r) {
     store_row<VPT>(zv, L.z);
     int total;
     uint32_t flags = 0;
-    int nd = 0;  // nodes of depth d
-    if (topk_list<VPT>(zv, r.top_k, r.T, L, S, r.q + row * r.V, &total, &flags)) {
-      // wave 0: every draw of the depth from one set of running sums
-      const ListSums ls = list_prefix(L.lw, total);
-      const uint64_t seed = frame_seed(st);
-      for (int i = 1; i <= r.tnodes; ++i) {
-        if (r.dep[i] != d) continue;
-        int code, near;
-        list_search(L.lw, L.lidx, total, ls, frame_uniform(seed, st.s + d, kDraft, nd), &code, &near);
-        if (near) flags |= kFlagCdf;
-        if (threadIdx.x == 0) {
-          tcode_s[nd] = code;
-          tnode_s[nd] = i;
-          r.ncode[static_cast<size_t>(b) * 8 + i] = code;
-        }
-        ++nd;
+    // greedy: the nodes' codes are the depth's m highest draft logits, the
+    // k-th child of a parent taking the k-th (m = the most children of a
+    // parent at this depth); the top-m + 1 set comes from the top-k
+    // selection, its order from wave 0's ranking
+    int m = 0;
+    if (r.greedy) {
+      for (int p = 0; p <= r.tnodes; ++p) {
+        if (p > 0 && r.dep[p] != d - 1) continue;
+        int n = 0;
+        for (int i = 1; i <= r.tnodes; ++i) n += r.par[i] == p ? 1 : 0;
+        m = max(m, n);
       }
-      if (threadIdx.x == 0) {
-        r.dflags[row] = flags;
-        nd_s = nd;
+    }
+    const int kk = r.greedy ? m + 1 : r.top_k;
+    const float T = r.greedy ? 1.0f : r.T;
+    if (topk_list<VPT>(zv, kk, T, L, S, r.greedy ? nullptr : r.q + row * r.V, &total, &flags)) {
+      const uint64_t seed = frame_seed(st);
+      if (r.greedy) {
+        // wave 0: rank the set by (logit desc, code asc); tcode_s[k] = the
+        // k-th highest; a gap under 1e-4 among the first m + 1 flags the
+        // depth
+        const int lane = threadIdx.x % kWave;
+        if (lane < total) {
+          const int ci = L.lidx[lane];
+          const float zi = L.z[ci];
+          int rank = 0;
+          for (int j = 0; j < total; ++j) {
+            const int cj = L.lidx[j];
+            const float zj = L.z[cj];
+            rank += (zj > zi || (zj == zi && cj < ci)) ? 1 : 0;
+          }
+          rank_s[rank] = ci;
+        }
+        wave_lds_sync();
+        bool near = false;
+        if (lane + 1 < total)
+          near = static_cast<double>(L.z[rank_s[lane]]) - static_cast<double>(L.z[rank_s[lane + 1]]) < kEpsGap;
+        flags = __ballot(near) ? kFlagArgmax : 0u;
+        int nd = 0;
+        for (int i = 1; i <= r.tnodes; ++i) {
+          if (r.dep[i] != d) continue;
+          int rank = 0;  // i's place among its parent's children
+          for (int j = 1; j < i; ++j) rank += r.par[j] == r.par[i] ? 1 : 0;
+          if (threadIdx.x == 0) {
+            tcode_s[nd] = rank_s[rank];
+            tnode_s[nd] = i;
+            r.ncode[static_cast<size_t>(b) * kTreeSlots + i] = rank_s[rank];
+          }
+          ++nd;
+        }
+        if (threadIdx.x == 0) {
+          r.dflags[row] = flags;
+          nd_s = nd;
+        }
+      } else {
+        // wave 0: every draw of the depth from one set of running sums
+        const ListSums ls = list_prefix(L.lw, total);
+        int nd = 0;  // nodes of depth d
+        for (int i = 1; i <= r.tnodes; ++i) {
+          if (r.dep[i] != d) continue;
+          int code, near;
+          list_search(L.lw, L.lidx, total, ls, frame_uniform(seed, st.s + d, kDraft, nd), &code, &near);
+          if (near) flags |= kFlagCdf;
+          if (threadIdx.x == 0) {
+            tcode_s[nd] = code;
+            tnode_s[nd] = i;
+            r.ncode[static_cast<size_t>(b) * kTreeSlots + i] = code;
+          }
+          ++nd;
+        }
+        if (threadIdx.x == 0) {
+          r.dflags[row] = flags;
+          nd_s = nd;
+        }
       }
     } else if (d == 1) {  // meanwhile the other waves gather row 0
       embed_row_span(r, st.s, st.last, x0, threadIdx.x - kWave, kBlock - kWave);
     }
     __syncthreads();
     // every node's verify input, the nodes side by side (a group of threads each)
-    nd = nd_s;
+    const int nd = nd_s;
     const int per = kBlock / nd;
     const int k = threadIdx.x / per;
     if (k < nd)
@@ -1236,14 +1295,16 @@ hipError_t launch_tree_draft(const RoundArgs& r, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Attention of the tree window over one stream and one KV head.  Keys: the
-// cache positions 0..P-1 (P = 1 + the largest row position below G: the
-// committed prefix and the root) and the node slots G + i - 1 of the active
-// node rows.  A row at a position below G (the root, or a prefill row) is causal
-// over the prefix; node row i sits at logical position pos[0] + dep[i] and
-// sees the whole prefix plus the nodes in anc[i] (itself and its ancestors).
-// K is rotated by its logical position, Q by its row's.  Phases as in
-// attention_kernel.
+// Attention of the tree window over rows r0 .. r0 + RB - 1 of one stream
+// and one KV head (grid z: row chunks of RB rows).  Keys: the cache
+// positions 0..P-1 (P = 1 + the largest row position below G: the committed
+// prefix and the root) and the node slots G + i - 1 of the active node rows,
+// at most 128.  A row at a position below G (the root, or a prefill row) is
+// causal over the prefix; node row i sits at logical position pos[0] +
+// dep[i] and sees the whole prefix plus the nodes in anc[i] (itself and its
+// ancestors).  K is rotated by its logical position, Q by its row's.
+// Phases as in attention_kernel; in phase 2 the 32 lanes of a (row, query
+// head) pair take the keys 32 apart.
 template <int D>
 __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a) {
   extern __shared__ float smem[];
@@ -1251,19 +1312,23 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   constexpr int H4 = half / 4;
   constexpr int KS = D + 4;
   const int b = blockIdx.x, g = blockIdx.y;
-  const int R = a.R;
+  const int R = a.R, r0 = blockIdx.z * a.RB;
+  const int nr = min(a.RB, R - r0);
   const int kvdim = a.nkv * D;
   const int qdim = a.nq * D;
   const int group = a.nq / a.nkv;
-  const int npair = R * group;
-  __shared__ int pos_s[CP_SPEC_MAX_WINDOW], qp_s[CP_SPEC_MAX_WINDOW], dep_s[CP_SPEC_MAX_WINDOW];
-  __shared__ uint32_t anc_s[CP_SPEC_MAX_WINDOW];
-  __shared__ int kslot_s[64], klp_s[64], knode_s[64];
+  const int npair = nr * group;
+  const int kstr = (a.Gk + 31) & ~31;  // score row stride
+  __shared__ int pos_s[kTreeSlots], qp_s[kTreeSlots], dep_s[kTreeSlots];
+  __shared__ uint64_t anc_s[kTreeSlots];
+  __shared__ int kslot_s[kMaxKeys], klp_s[kMaxKeys], knode_s[kMaxKeys];
   // the rows' positions, depths and masks in LDS (indexing the argument
   // block per lane would turn into memory loads)
-  if (threadIdx.x < R) pos_s[threadIdx.x] = a.pos[b * R + threadIdx.x];
-  if (threadIdx.x >= 64 && threadIdx.x < 64 + CP_SPEC_MAX_WINDOW)
-    dep_s[threadIdx.x - 64] = a.dep[threadIdx.x - 64], anc_s[threadIdx.x - 64] = a.anc[threadIdx.x - 64];
+  for (int i = threadIdx.x; i < R; i += kBlock) {
+    pos_s[i] = a.pos[b * R + i];
+    dep_s[i] = a.dep[i];
+    anc_s[i] = a.anc[i];
+  }
   __syncthreads();
   // the key list, every entry by its own thread: prefix slots 0..P-1, then
   // the active node rows in row order
@@ -1275,23 +1340,22 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   }
   const int p0 = pos_s[0];
   const int np = P + nnode;
-  if (threadIdx.x < P) {
-    kslot_s[threadIdx.x] = threadIdx.x, klp_s[threadIdx.x] = threadIdx.x, knode_s[threadIdx.x] = 0;
-  } else if (threadIdx.x >= 64 && threadIdx.x < 64 + R) {
-    const int r = threadIdx.x - 64, pr = pos_s[r];
+  for (int i = threadIdx.x; i < P; i += kBlock) kslot_s[i] = i, klp_s[i] = i, knode_s[i] = 0;
+  for (int r = threadIdx.x; r < R; r += kBlock) {
+    const int pr = pos_s[r];
     qp_s[r] = pr < 0 ? -1 : (pr < a.G ? pr : (pr < a.Gk ? p0 + dep_s[r] : -1));
     if (r > 0 && pr >= a.G && pr < a.Gk) {
       int before = 0;
       for (int i = 1; i < r; ++i) before += (pos_s[i] >= a.G && pos_s[i] < a.Gk) ? 1 : 0;
-      kslot_s[P + before] = pr, klp_s[P + before] = p0 + dep_s[r], knode_s[P + before] = r;
+      if (P + before < kMaxKeys) kslot_s[P + before] = pr, klp_s[P + before] = p0 + dep_s[r], knode_s[P + before] = r;
     }
   }
   __syncthreads();
-  if (P == 0 || np > 32) return;  // no active row (np <= G + nodes <= 32 by construction)
+  if (P == 0 || np > kMaxKeys || np > a.Gk || nr <= 0) return;  // no active row (np <= G + nodes)
   float* Ks = smem;                  // [np][KS]
   float* Vs = Ks + a.Gk * KS;        // [np][D]
   float* Qs = Vs + a.Gk * D;         // [npair][D]
-  float* S = Qs + npair * D;         // [npair][32]
+  float* S = Qs + a.RB * group * D;  // [npair][kstr]
   const float* kb = a.kv + static_cast<size_t>(b) * a.kv_sb + g * D;
   const float* vb = kb + a.kv_vo;
 
@@ -1314,7 +1378,7 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
     } else if (it < nk + nq) {
       const int jt = it - nk;
       const int pr = jt / H4, i4 = (jt % H4) * 4;
-      const int r = pr / group, j = pr % group;
+      const int r = r0 + pr / group, j = pr % group;
       const float* qrow = a.Q + static_cast<size_t>(b * R + r) * qdim + (g * group + j) * D;
       const int pq = max(qp_s[r], 0);
       m.x1 = *reinterpret_cast<const float4*>(qrow + i4);
@@ -1353,35 +1417,46 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   }
   __syncthreads();
 
-  // ---- phase 2: scores and softmax, 32 lanes per pair (lane = key) ----
+  // ---- phase 2: scores and softmax, 32 lanes per pair, keys 32 apart ----
   for (int base = 0; base < npair * 32; base += kBlock) {
     const int idx = base + threadIdx.x;
-    const int pr = idx >> 5, p = idx & 31;
+    const int pr = idx >> 5, lane = idx & 31;
     const bool live_pair = pr < npair;
-    const int r = live_pair ? pr / group : 0;
+    const int r = live_pair ? r0 + pr / group : 0;
     const int qp = live_pair ? qp_s[r] : -1;
-    bool ok = live_pair && qp >= 0 && p < np;
-    if (ok) ok = p < P ? kslot_s[p] <= qp : ((anc_s[r] >> knode_s[p]) & 1u) != 0u;
-    float s = -INFINITY;
-    if (ok) {
-      const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
-      const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
-      float acc = 0.0f;
+    float* srow = S + (live_pair ? pr : 0) * kstr;
+    float mx = -INFINITY;
+    for (int p = lane; p < np; p += 32) {
+      bool ok = live_pair && qp >= 0;
+      if (ok) ok = p < P ? kslot_s[p] <= qp : ((anc_s[r] >> knode_s[p]) & 1ull) != 0ull;
+      float sc = -INFINITY;
+      if (ok) {
+        const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
+        const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
+        float acc = 0.0f;
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) {
-        const float4 x = q4[i], y = k4[i];
-        acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+        for (int i = 0; i < D / 4; ++i) {
+          const float4 x = q4[i], y = k4[i];
+          acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+        }
+        sc = acc * a.scale;
       }
-      s = acc * a.scale;
+      if (live_pair) srow[p] = sc;
+      mx = fmaxf(mx, sc);
     }
-    float mx = s;
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-    const float e = ok ? expf(s - mx) : 0.0f;
-    float sum = e;
+    float sum = 0.0f;
+    for (int p = lane; p < np; p += 32) {
+      const float sc = live_pair ? srow[p] : -INFINITY;
+      const float e = sc == -INFINITY ? 0.0f : expf(sc - mx);
+      if (live_pair) srow[p] = e;
+      sum += e;
+    }
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
-    if (live_pair) S[pr * 32 + p] = ok ? e / sum : 0.0f;
+    if (live_pair)
+      for (int p = lane; p < np; p += 32) srow[p] = sum > 0.0f ? srow[p] / sum : 0.0f;
   }
   __syncthreads();
 
@@ -1389,9 +1464,9 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   constexpr int D8 = D / 8;
   for (int idx = threadIdx.x; idx < npair * D8; idx += kBlock) {
     const int pr = idx / D8, i8 = (idx % D8) * 8;
-    const int r = pr / group, j = pr % group;
+    const int r = r0 + pr / group, j = pr % group;
     if (qp_s[r] < 0) continue;
-    const float* srow = S + pr * 32;
+    const float* srow = S + pr * kstr;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.0f;
@@ -1413,9 +1488,10 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
   }
 }
 
-size_t tree_attention_smem_bytes(int Gk, int d, int R, int group) {
-  const size_t npair = static_cast<size_t>(R) * group;
-  return (static_cast<size_t>(Gk) * (2 * d + 4) + npair * d + npair * 32) * sizeof(float);
+size_t tree_attention_smem_bytes(int Gk, int d, int RB, int group) {
+  const size_t npair = static_cast<size_t>(RB) * group;
+  const size_t kstr = (static_cast<size_t>(Gk) + 31) / 32 * 32;
+  return (static_cast<size_t>(Gk) * (2 * d + 4) + npair * d + npair * kstr) * sizeof(float);
 }
 
 hipError_t tree_attention_allow_smem(int d, size_t bytes) {
@@ -1433,11 +1509,13 @@ hipError_t tree_attention_allow_smem(int d, size_t bytes) {
 }
 
 hipError_t launch_tree_attention(const AttnArgs& a, int B, hipStream_t s) {
-  const size_t shm = tree_attention_smem_bytes(a.Gk, a.d, a.R, a.nq / a.nkv);
+  if (a.RB < 1 || a.Gk > kMaxKeys || a.R > kTreeSlots) return hipErrorInvalidValue;
+  const size_t shm = tree_attention_smem_bytes(a.Gk, a.d, a.RB, a.nq / a.nkv);
+  const dim3 grid(B, a.nkv, (a.R + a.RB - 1) / a.RB);
   switch (a.d) {
 #define CPS_TATT(D_)                                                                              \
   case D_:                                                                                        \
-    hipLaunchKernelGGL(tree_attention_kernel<D_>, dim3(B, a.nkv), dim3(kBlock), shm, s, a);       \
+    hipLaunchKernelGGL(tree_attention_kernel<D_>, grid, dim3(kBlock), shm, s, a);                 \
     break;
     CPS_TATT(8) CPS_TATT(16) CPS_TATT(32) CPS_TATT(64) CPS_TATT(128)
 #undef CPS_TATT
@@ -1457,9 +1535,9 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
   __shared__ StreamState st_s;
   __shared__ CallDesc c_s;
   __shared__ cp_spec_stats cnt_s;
-  __shared__ uint32_t tfl_s[CP_SPEC_MAX_WINDOW], dfl_s[CP_SPEC_MAX_WINDOW];
-  __shared__ int tcode_s[CP_SPEC_MAX_WINDOW], ncode_s[CP_SPEC_MAX_WINDOW];
-  __shared__ int par_s[CP_SPEC_MAX_WINDOW], dep_s[CP_SPEC_MAX_WINDOW];
+  __shared__ uint32_t tfl_s[kTreeSlots], dfl_s[CP_SPEC_MAX_WINDOW];
+  __shared__ int tcode_s[kTreeSlots], ncode_s[kTreeSlots];
+  __shared__ int par_s[kTreeSlots], dep_s[kTreeSlots];
   __shared__ int v_s, n_s;
   constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
   constexpr int kCntW = sizeof(cp_spec_stats) / 8;
@@ -1473,12 +1551,12 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
     reinterpret_cast<int*>(&c_s)[tid - 32] = reinterpret_cast<const int*>(r.call)[tid - 32];
   } else if (tid >= 64 && tid < 64 + kCntW) {
     reinterpret_cast<long long*>(&cnt_s)[tid - 64] = reinterpret_cast<const long long*>(r.sstats + b)[tid - 64];
-  } else if (tid >= 96 && tid < 96 + CP_SPEC_MAX_WINDOW) {
-    const int i = tid - 96;
+  } else if (tid >= 128 && tid < 128 + kTreeSlots) {
+    const int i = tid - 128;
     tfl_s[i] = i < r.R ? r.tflags[rb + i] : 0u;
     tcode_s[i] = i < r.R ? r.tcode[rb + i] : -1;
-    ncode_s[i] = r.ncode[static_cast<size_t>(b) * 8 + i];
-    dfl_s[i] = i < r.W ? r.dflags[static_cast<size_t>(b) * r.W + i] : 0u;
+    ncode_s[i] = r.ncode[static_cast<size_t>(b) * kTreeSlots + i];
+    if (i < CP_SPEC_MAX_WINDOW) dfl_s[i] = i < r.W ? r.dflags[static_cast<size_t>(b) * r.W + i] : 0u;
     par_s[i] = r.par[i];
     dep_s[i] = r.dep[i];
   }
@@ -1492,8 +1570,8 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
   const int s = st.s, gamma = st.gamma;
   if (tid == 0) {
     cp_spec_stats& cnt = cnt_s;
-    if (!spec) {  // prefill: c_1 is row 1's draw
-      const uint32_t f = tfl_s[1] & (kFlagTopk | kFlagCdf);
+    if (!spec) {  // prefill: c_1 is row 1's draw (greedy: its argmax)
+      const uint32_t f = tfl_s[1] & (kFlagTopk | kFlagCdf | kFlagArgmax);
       count_flags(f, &cnt);
       if (f) st_s.flags |= 1u << 1;
       out[1] = st_s.last = tcode_s[1];
@@ -1507,24 +1585,37 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
       for (;;) {  // the walk: at most one node per depth
         const uint32_t tf = tfl_s[v];
         const int j = s + dep_s[v] + 1;
-        // the rows the walk visits used their top-k sets
-        if (tf & kFlagTopk) {
-          ++cnt.near_tie_topk;
+        // the rows the walk visits used their top-k set (greedy: argmax)
+        const uint32_t ft = tf & (kFlagTopk | kFlagArgmax);
+        if (ft) {
+          count_flags(ft, &cnt);
           fl |= 1u << j;
         }
-        if (tf & kFlagAccept) {
-          ++cnt.near_tie_accept;
-          fl |= 1u << j;
-        }
-        const int dec = static_cast<int>((tf >> 16) & 0xFFu) - 1;
-        if (dec < 1 || dec > r.tnodes) {
-          if (tf & kFlagCdf) {
-            ++cnt.near_tie_cdf;
+        int dec = -1;  // the accepted child
+        if (r.greedy) {
+          // the first active child whose code equals the row's argmax
+          for (int ch = 1; ch <= r.tnodes && dec < 0; ++ch)
+            if (par_s[ch] == v && dep_s[ch] <= gamma && ncode_s[ch] == tcode_s[v]) dec = ch;
+          if (dec < 0) {
+            out[s + n + 1] = st_s.last = tcode_s[v];
+            ++n;
+            break;
+          }
+        } else {
+          if (tf & kFlagAccept) {
+            ++cnt.near_tie_accept;
             fl |= 1u << j;
           }
-          out[s + n + 1] = st_s.last = tcode_s[v];
-          ++n;
-          break;
+          dec = static_cast<int>((tf >> 16) & 0xFFu) - 1;
+          if (dec < 1 || dec > r.tnodes) {
+            if (tf & kFlagCdf) {
+              ++cnt.near_tie_cdf;
+              fl |= 1u << j;
+            }
+            out[s + n + 1] = st_s.last = tcode_s[v];
+            ++n;
+            break;
+          }
         }
         out[s + n + 1] = ncode_s[dec];
         ++n;
@@ -1537,7 +1628,7 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
         count_flags(f, &cnt);
         if (f) fl |= 1u << (s + d);
       }
-      st_s.flags |= fl;
+    st_s.flags |= fl;
       v_s = v;
       n_s = n;
     }
@@ -1564,7 +1655,7 @@ __global__ __launch_bounds__(kBlock) void tree_accept_kernel(const RoundArgs r) 
   // accepted, a prefill round, or the frame complete)
   if (tid == 0) {
     const bool move = spec && v > 0 && s + n < r.G - 1;
-    r.ncode[static_cast<size_t>(b) * 8] = move ? (s << 8) | v : 0;
+    r.ncode[static_cast<size_t>(b) * kTreeSlots] = move ? (s << 8) | v : 0;
   }
   if (tid == 0 && st_s.s >= r.G - 1) {  // frame complete
     if (c.out_flags) c.out_flags[fb] = st_s.flags;

@@ -40,7 +40,33 @@ def _check(name, c, m, parents, got, hf, c0, seeds, pairs):
     return res
 
 
-@pytest.mark.parametrize("parents", [[0, 0, 1], [0, 0, 0, 1, 2], [0, 1, 1, 2, 3, 0, 6]])
+def widths_tree(widths, extra_root=0):
+    """Parent list of a tree whose nodes at depth d each have widths[d]
+    children (breadth-first numbering), plus extra_root more children of the
+    root without children of their own."""
+    par, level, nid = [], [0], 0
+    for d, w in enumerate(widths):
+        nxt = []
+        for p in level:
+            for _ in range(w):
+                nid += 1
+                par.append(p)
+                nxt.append(nid)
+        if d == 0:
+            for _ in range(extra_root):
+                nid += 1
+                par.append(0)
+        level = nxt
+    return par
+
+
+T15 = widths_tree((3, 2, 1))            # 15 nodes, depth 3
+T31 = widths_tree((2, 2, 2, 2), 1)      # 31 nodes, depth 4
+T63 = widths_tree((2, 2, 2, 2, 2), 1)   # 63 nodes, depth 5
+
+
+@pytest.mark.parametrize("parents", [[0, 0, 1], [0, 0, 0, 1, 2], [0, 1, 1, 2, 3, 0, 6], T15, T31, T63],
+                         ids=["3", "5", "7", "15", "31", "63"])
 def test_tree_tiny_all_frames(parents):
     c, h = _tree_handle("tiny", parents, frames=60)
     hf, c0, seeds = synth.make_inputs(c)
@@ -95,3 +121,54 @@ def test_tree_qwen3tts_sampled():
     assert got[2]["frames"] == 40
     _check("qwen3tts", c, oracle_model("qwen3tts"), parents, got, hf, c0, seeds,
            [(f, 0) for f in range(0, 40, 2)])
+
+
+@pytest.mark.parametrize("parents", [[0, 0, 1, 1], T15, T31], ids=["4", "15", "31"])
+def test_tree_greedy(parents):
+    """Greedy trees: node k of a parent proposes the k-th highest draft
+    logit; the codes equal the oracle's and the GPU's autoregressive greedy
+    codes."""
+    c, h = _tree_handle("tiny-greedy", parents, frames=120)
+    hf, c0, seeds = synth.make_inputs(c)
+    log(f"decode tiny-greedy tree {len(parents)} F=120")
+    got = decode_gpu(h, hf, c0, seeds)
+    _check("tiny-greedy", c, oracle_model("tiny-greedy"), parents, got, hf, c0, seeds,
+           [(f, 0) for f in range(120)])
+    ar = decode_gpu(handle("tiny-greedy", verify_size=0), hf, c0, seeds)
+    assert not compare_frames(got[0], got[1], ar[0], ar[1])["unflagged"]
+
+
+@pytest.mark.parametrize("B,parents", [(8, T15), (64, T31)], ids=["8x15", "64x31"])
+def test_tree_many_streams(B, parents):
+    """Tree windows on the batched path: matrix-core projections and lm_heads
+    with the nodes of one depth sharing their head across streams."""
+    c, h = _tree_handle("tiny-64", parents, max_streams=B, frames=4, streams=B)
+    hf, c0, seeds = synth.make_inputs(c)
+    log(f"decode tiny tree {len(parents)} B={B} F=4")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 4 * B
+    from gpu_util import spread_pairs
+    _check(f"tiny B={B}", c, oracle_model("tiny-64"), parents, got, hf, c0, seeds,
+           spread_pairs(4, B, min(4 * B, 96), seed=B))
+
+
+@pytest.mark.parametrize("parents", [T15, T31], ids=["15", "31"])
+def test_tree_qwen3tts_large_sampled(parents):
+    c, h = _tree_handle("qwen3tts", parents, frames=40)
+    hf, c0, seeds = synth.make_inputs(c)
+    log(f"decode qwen3tts tree {len(parents)} F=40")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 40
+    _check("qwen3tts", c, oracle_model("qwen3tts"), parents, got, hf, c0, seeds,
+           [(f, 0) for f in range(0, 40, 4)])
+
+
+def test_tree_qwen3tts_64_streams_sampled():
+    from gpu_util import spread_pairs
+    c, h = _tree_handle("qwen3tts-64", T15, frames=3)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("decode qwen3tts-64 tree 15 F=3")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 3 * 64
+    _check("qwen3tts-64", c, oracle_model("qwen3tts-64"), T15, got, hf, c0, seeds,
+           spread_pairs(3, 64, 12, seed=5))

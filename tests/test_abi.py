@@ -133,18 +133,28 @@ def _tree_cfg(parents, **over):
 
 
 @pytest.mark.parametrize("parents,over,code,msg", [
-    ([0] * 8, {}, binding.EINVAL, "tree_nodes"),
+    ([0] * 64, {}, binding.EINVAL, "tree_nodes"),
     ([0, 2], {}, binding.EINVAL, "tree_parent"),
     ([1], {}, binding.EINVAL, "tree_parent"),
-    ([0, 0], {"greedy": True}, binding.EUNSUPPORTED, "stochastically"),
-    ([0, 0], {"streams": 8}, binding.EUNSUPPORTED, "at most 7 streams"),
-    ([0, 0, 0, 1, 2], {"groups": 30}, binding.EUNSUPPORTED, "code_groups + tree_nodes"),
+    (list(range(8)), {}, binding.EINVAL, "tree depth"),
+    ([0, 0], {"fused_draft": 1}, binding.EUNSUPPORTED, "chain windows only"),
 ])
 def test_tree_validation(parents, over, code, msg):
     cfg = _tree_cfg(parents, **over)
     rc, err = _create(cfg)
     assert rc == code and msg in err, (rc, err)
     assert binding.lib().cp_spec_workspace_bytes(C.byref(cfg)) == 0
+
+
+@pytest.mark.parametrize("parents,over", [
+    ([0] * 63, {}),                          # 63 children of the root
+    (list(range(7)), {}),                    # depth 7
+    ([0, 0, 1, 1], {"greedy": True}),        # greedy trees
+    ([0, 0, 1, 1], {"streams": 64}),         # any stream count
+])
+def test_tree_shapes_accepted(parents, over):
+    cfg = _tree_cfg(parents, **over)
+    assert binding.lib().cp_spec_workspace_bytes(C.byref(cfg)) > 0, binding.last_error()
 
 
 def test_tree_workspace_holds_node_slots():

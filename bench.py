@@ -505,10 +505,13 @@ def main():
         # a wider window costs more rows per pass)
         line["verify_sweep"] = [verify_sweep(args.workload, frames=300),
                                 verify_sweep("qwen3tts-64", frames=40)]
-        # the tree-shaped window (at most 7 nodes, one stream), against the
-        # chain above
-        trees = tree_sweep(args.workload, ([0, 0, 1, 2], [0, 0], [0, 0, 0, 1, 2, 3],
-                                           [0, 0, 1, 2, 3, 4], [0, 1, 2]))
+        # the tree-shaped window at one stream, against the chain above:
+        # small trees, 15 nodes (3, 2, 1 children per node over three
+        # depths) and 31 (two per node over four depths, a third root child)
+        t15 = [0, 0, 0, 1, 1, 2, 2, 3, 3, 4, 5, 6, 7, 8, 9]
+        t31 = [0, 0, 0, 1, 1, 2, 2, 4, 4, 5, 5, 6, 6, 7, 7, 8, 8, 9, 9, 10, 10, 11, 11,
+               12, 12, 13, 13, 14, 14, 15, 15]
+        trees = tree_sweep(args.workload, ([0, 0, 1, 2], [0, 0], [0, 1, 2], t15, t31))
         for row in trees["by_tree"]:
             row["throughput_vs_chain_n4"] = row["codes_per_s"] / main_res["codes_per_s"]
         line["tree_window"] = trees

@@ -77,7 +77,18 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   const int tid = threadIdx.x;
   const int rg = tid / KT, kt = tid % KT;
   const int lane = tid % kWave;
-  const int m0 = MODE == kHeadG ? 0 : blockIdx.y * MT;
+  // Several row tiles read the same weight rows.  Blocks go to the eight
+  // XCDs in turn (linear id modulo 8): the row tiles of one weight slice are
+  // given to consecutive blocks of one XCD, so all but the first read the
+  // slice from that XCD's L2.
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (MODE != kHeadG && gridDim.y > 1 && gridDim.x % 8 == 0) {
+    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    const int i = L / 8;
+    by = i % gridDim.y;
+    bx = (i / gridDim.y) * 8 + L % 8;
+  }
+  const int m0 = MODE == kHeadG ? 0 : by * MT;
   if (MODE != kHeadG && a.M - m0 <= 0) return;
 
   const WT* W0 = static_cast<const WT*>(a.W0);
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   auto row_of = [&](int m) { return MODE == kHeadG ? rows_s[m] : m0 + m; };
   const int Mloc = MODE == kHeadG ? Mg : min(MT, a.M - m0);
   const int stride = gridDim.x * RG;
-  int ubase = blockIdx.x * RG;
+  int ubase = bx * RG;
 
   // ---- the first unit's weights, before anything else ----
   VT wv[RPG][SPT];
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
         for (int q = 0; q < rows16; ++q) t += part[q][NV + idx % MT];
         ri = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
       }
-      if ((MODE == kHead || MODE == kHeadG) && a.xnorm_out != nullptr && blockIdx.x == 0 && rg == 0) {
+      if ((MODE == kHead || MODE == kHeadG) && a.xnorm_out != nullptr && bx == 0 && rg == 0) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m >= Mloc || row_of(m) % a.xdiv != 0) continue;

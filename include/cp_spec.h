@@ -176,7 +176,11 @@ const char* cp_spec_last_error(void);
  * A frame is a pure function of (weights, h_frame, c0, seed): frames of one
  * stream run in order, streams advance independently (ragged acceptance).
  * Host-synchronising: returns after the last frame has been decoded.
- * Errors: EINVAL for n_streams outside 1..max_streams or n_frames < 0. */
+ * Errors: EINVAL for n_streams outside 1..max_streams or n_frames < 0;
+ * EUNSUPPORTED, after the call has run, when an activation entering a
+ * matrix-core projection (bf16 weights, 32 or more rows in a pass) reached
+ * |x| >= 65504: those projections carry activations as two fp16 pieces, and
+ * the call's codes are then not valid. */
 int cp_spec_decode_frames(cp_spec* h, void* stream, int32_t n_streams,
                           int32_t n_frames, const float* d_h_frame,
                           const int32_t* d_c0, const uint64_t* d_seeds,
@@ -194,7 +198,12 @@ int cp_spec_get_stats(const cp_spec_stats* d_stats, void* stream,
  * kernels; topk_sample, accept and walk_step launch thin kernels around the
  * round's device functions (the top-k softmax and inverse-CDF draw, the
  * acceptance walk step and the chain outcome scan).  They use the handle's
- * workspace as scratch: calls on one handle must not overlap. */
+ * workspace as scratch: calls on one handle must not overlap.  With bf16
+ * weights and 32 or more rows, head_logits and decoder_forward run their
+ * projections on the matrix cores with activations carried as two fp16
+ * pieces: an activation of magnitude 65504 or more (or NaN) there is
+ * carried as +-65504, so the outputs it feeds are finite but wrong, and
+ * these two calls do not report it (decode_frames does, as EUNSUPPORTED). */
 
 /* Stacked-head logits (draft GEMV, guide "Why the draft is free"; per-row
  * verify heads, guide "Limitations"):

@@ -3,23 +3,27 @@
 //
 // C[m][n] = sum_k x_m[k] * W[n][k].
 //
-// Every fp32 activation is split into three bf16 pieces by truncation,
-// x = hi + mid + lo (split3), and the tile runs v_mfma_f32_16x16x32_bf16
-// once per piece into one fp32 accumulator.  bf16 x bf16 products are exact
-// in fp32, so the result is the fp32 dot product up to summation order.
+// Every fp32 activation is carried as two fp16 pieces, x ~ hi + lo
+// (split2_pair: 22 significant bits), and the weights as fp16 copies of the
+// bf16 values times 2^S, one S per packed matrix (exact: a bf16 value has 8
+// significant bits, and S puts the matrix's largest value just below 2^15).
+// The tile runs v_mfma_f32_16x16x32_f16 once per piece into one fp32
+// accumulator; fp16 x fp16 products are exact in fp32, so the result is the
+// fp32 dot product of W and hi + lo up to summation order, then times 2^-S.
 //
 // Memory traffic is what bounds these shapes, so both operands are read in
 // whole cache lines:
 //  * weights are packed once, at create, in MFMA fragment order: for each
-//    16-column tile and 32-wide K chunk, 64 lanes x 8 bf16 (1 KB) with lane
+//    16-column tile and 32-wide K chunk, 64 lanes x 8 fp16 (1 KB) with lane
 //    l holding W[16 t + l % 16][32 c + 8 (l / 16) .. +7], chunk-major (the
 //    tiles of one chunk side by side).  A wave reads a B fragment as one
 //    contiguous 1 KB load;
-//  * activations are read row-major, a quad of lanes per 128-byte row
-//    segment, each lane holding the 8 values of one fragment entry; they are
-//    split in registers and written as whole entries to a small XOR-swizzled
-//    LDS stage private to the wave (no block barrier in the K loop, no bank
-//    conflicts on either side).
+//  * projection inputs arrive pre-split by the producing kernel (two planes
+//    in fragment order); the lm_heads' rows are read row-major, a quad of
+//    lanes per 128-byte row segment, each lane holding the 8 values of one
+//    fragment entry, split in registers and written as whole entries to a
+//    small XOR-swizzled LDS stage private to the wave (no block barrier in
+//    the K loop, no bank conflicts on either side).
 // Tiling: a block owns (16 FM) x (16 FN) outputs; its eight wave64s (two a
 // SIMD, so one's MFMAs cover the other's waits) split K in eighths and keep
 // the next two chunks' loads in flight.  The partial tiles (and the rows'
@@ -31,6 +35,8 @@
 // SwiGLU (columns 0..TN/2-1 of a tile are gate rows, TN/2..TN-1 the matching
 // up rows), Q write plus K/V append at the row's position, lm_head logits for
 // rows grouped by head (final-normed rows written once).
+#include <algorithm>
+
 #include "dev_common.h"
 #include "kernels.h"
 
@@ -40,7 +46,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16x8_t h8;
 
 constexpr int kGW = 8;               // waves of a block: K eighths
 constexpr int kGT = kGW * kWave;     // 512 threads
@@ -93,7 +99,7 @@ template <int MODE, int FM, int FN, bool NORM, bool PL>
 __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   constexpr int SW = PL ? 1 : kGW;  // stage: only the in-kernel split uses it
-  struct StageT { u32x4 f[SW][FM * 3][kWave]; };  // split fragments of one chunk
+  struct StageT { u32x4 f[SW][FM * kPieces][kWave]; };  // split fragments of one chunk
   struct PartT { float v[4][TM][TN + 1]; float ssq[kGW][TM]; };
   __shared__ union {
     StageT stage;
@@ -176,30 +182,30 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   for (int i = 0; i < FM; ++i) ss[i] = 0.0f;
   if constexpr (PL) {
     // activations pre-split: plane p of row tile t, chunk c is the 1 KB
-    // fragment at ((c * T + t) * 3 + p) * 512 bf16 (T row tiles)
-    const uint16_t* ab = a.planes + (static_cast<size_t>(c0) * a.ptiles + by * FM) * 3 * 512 + lane * 8;
-    const size_t astep = static_cast<size_t>(a.ptiles) * 3 * 512;
+    // fragment at ((c * T + t) * 2 + p) * 512 fp16 (T row tiles)
+    const uint16_t* ab = a.planes + (static_cast<size_t>(c0) * a.ptiles + by * FM) * kPieces * 512 + lane * 8;
+    const size_t astep = static_cast<size_t>(a.ptiles) * kPieces * 512;
     struct PFrag {
-      u32x4 x[FM][3];
+      u32x4 x[FM][kPieces];
     };
     auto fetch_p = [&](int c) __attribute__((always_inline)) {
       PFrag f;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          f.x[i][p] = *reinterpret_cast<const u32x4*>(ab + rc(c) * astep + (i * 3 + p) * 512);
+        for (int p = 0; p < kPieces; ++p)
+          f.x[i][p] = *reinterpret_cast<const u32x4*>(ab + rc(c) * astep + (i * kPieces + p) * 512);
       return f;
     };
     auto mma_p = [&](const PFrag& fa, const BFrag& fb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
+      for (int p = 0; p < kPieces; ++p)
 #pragma unroll
         for (int f = 0; f < FM; ++f)
 #pragma unroll
           for (int n = 0; n < FN; ++n)
-            acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa.x[f][p]),
-                                                                __builtin_bit_cast(bf16x8, fb.w[n]), acc[f][n], 0, 0, 0);
+            acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, fa.x[f][p]),
+                                                               __builtin_bit_cast(h8, fb.w[n]), acc[f][n], 0, 0, 0);
     };
     // two chunks of loads in flight (an even chunk count per wave; the
     // fetches past the end re-read the last chunk and are not used)
@@ -254,12 +260,13 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   auto slot = [](int e) { return e ^ (((e >> 4) & 3) << 1); };
   const int wslot = slot((lane >> 2) + 16 * (lane & 3));
   const int rslot = slot(lane);
-  // split x * g of one chunk into the wave's LDS stage: three bf16 pieces,
-  // two values per word (the high halves, gathered by byte permutes)
+  // split x * g of one chunk into the wave's LDS stage: two fp16 pieces,
+  // two values per word
+  bool bad = false;
   auto split_store = [&](const AFrag& fr) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      uint32_t hp[4], mp[4], lp[4];
+      uint32_t hp[4], lp[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float x0 = fr.x[i][e / 4][e % 4], x1 = fr.x[i][e / 4][e % 4 + 1];
@@ -267,31 +274,24 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
         ss[i] = fmaf(x1, x1, ss[i]);
         const float y0 = NORM ? x0 * fr.g[e / 4][e % 4] : x0;
         const float y1 = NORM ? x1 * fr.g[e / 4][e % 4 + 1] : x1;
-        const float r0 = y0 - __uint_as_float(__float_as_uint(y0) & 0xFFFF0000u);
-        const float r1 = y1 - __uint_as_float(__float_as_uint(y1) & 0xFFFF0000u);
-        const float q0 = r0 - __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
-        const float q1 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-        hp[e / 2] = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
-        mp[e / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
-        lp[e / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
+        split2_pair(y0, y1, hp[e / 2], lp[e / 2], bad);
       }
-      sm.stage.f[wave][i * 3 + 0][wslot] = u32x4{hp[0], hp[1], hp[2], hp[3]};
-      sm.stage.f[wave][i * 3 + 1][wslot] = u32x4{mp[0], mp[1], mp[2], mp[3]};
-      sm.stage.f[wave][i * 3 + 2][wslot] = u32x4{lp[0], lp[1], lp[2], lp[3]};
+      sm.stage.f[wave][i * kPieces + 0][wslot] = u32x4{hp[0], hp[1], hp[2], hp[3]};
+      sm.stage.f[wave][i * kPieces + 1][wslot] = u32x4{lp[0], lp[1], lp[2], lp[3]};
     }
   };
   auto mma = [&](const BFrag& fb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      bf16x8 ap[FM];
+    for (int p = 0; p < kPieces; ++p) {
+      h8 ap[FM];
 #pragma unroll
-      for (int f = 0; f < FM; ++f) ap[f] = __builtin_bit_cast(bf16x8, sm.stage.f[wave][f * 3 + p][rslot]);
+      for (int f = 0; f < FM; ++f) ap[f] = __builtin_bit_cast(h8, sm.stage.f[wave][f * kPieces + p][rslot]);
 #pragma unroll
       for (int f = 0; f < FM; ++f)
 #pragma unroll
         for (int n = 0; n < FN; ++n)
-          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[f], __builtin_bit_cast(bf16x8, fb.w[n]),
-                                                              acc[f][n], 0, 0, 0);
+          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[f], __builtin_bit_cast(h8, fb.w[n]), acc[f][n], 0,
+                                                             0, 0);
     }
   };
 
@@ -331,6 +331,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     fb1 = fetch_b(min(c + 3, cw - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (bad) flag_overflow(a.ovf, nullptr, 0);  // the heads' rows are all in use
 
   }
 
@@ -410,7 +411,8 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   };
   auto tile_val = [&](int r, int c) {
     const float v = (sm.part.v[0][r][c] + sm.part.v[1][r][c]) + (sm.part.v[2][r][c] + sm.part.v[3][r][c]);
-    return NORM ? v * rinv_of(r) : v;
+    const float ws = (MODE == kSwiGLU && c >= TN / 2) ? a.wscale1 : a.wscale0;  // 2^-S, exact
+    return NORM ? v * ws * rinv_of(r) : v * ws;
   };
 
   // final-normed rows for the heads' caller (the column tiles split K)
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
         const float g = tile_val(r, c8 + e), u = tile_val(r, c8 + e + W);
         y[e] = g / (1.0f + expf(-g)) * u;
       }
-      split_store8(a.out_planes, a.out_ptiles, row, bx * W + c8, y);
+      if (split_store8(a.out_planes, a.out_ptiles, row, bx * W + c8, y)) flag_overflow(a.ovf, a.pos, row);
     }
     return;
   }
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
           ss = fmaf(xn[e], xn[e], ss);
           y[e] = a.out_g != nullptr ? xn[e] * a.out_g[n0 + c8 + e] : xn[e];
         }
-        split_store8(a.out_planes, a.out_ptiles, row, n0 + c8, y);
+        if (split_store8(a.out_planes, a.out_ptiles, row, n0 + c8, y)) flag_overflow(a.ovf, a.pos, row);
       }
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
@@ -585,14 +587,15 @@ hipError_t launch_f(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
                              : launch_t<FM, FN, false>(mode, a, grid, s);
 }
 
-// Split pass: rows [0, M) of X (times g when set) into three bf16 planes in
+// Split pass: rows [0, M) of X (times g when set) into two fp16 planes in
 // fragment order, rows up to the next multiple of 64 zero; with g, per row
 // the sums of squares of x over each 32-wide K chunk.  Block (row tile, K
 // block): 16 rows x 256 values; wave w takes fragment entries of chunks
 // w and w + 4 of the block (lane = fragment lane), so the four entries of
 // one row and chunk sit in lanes l, l +- 16, l +- 32 of one wave.
 __global__ __launch_bounds__(kBlock) void split_rows_kernel(const float* X, int ldx, int M, int K, const float* g,
-                                                            uint16_t* planes, float* ssp) {
+                                                            uint16_t* planes, float* ssp, int* ovf,
+                                                            const int* pos) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int mt = blockIdx.x, kb = blockIdx.y;
   const int row = 16 * mt + lane % 16;
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(kBlock) void split_rows_kernel(const float* X, int 
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = v[i];
     }
-    split_store8(planes, gridDim.x, row, k, y);
+    if (split_store8(planes, gridDim.x, row, k, y)) flag_overflow(ovf, pos, row);
     if (g != nullptr) {
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
@@ -637,11 +640,12 @@ __global__ __launch_bounds__(kBlock) void split_rows_kernel(const float* X, int 
   }
 }
 
-// Packs one bf16 matrix [N][K] (row-major, N % 16 == 0, K % 32 == 0) into
-// fragment order at tiles t0.. of a chunk-major packed matrix with NT tiles
-// per chunk: thread t writes one fragment entry (8 bf16).
+// Packs one bf16 matrix [N][K] (row-major, N % 16 == 0, K % 32 == 0), times
+// `scale` (a power of two), as fp16 into fragment order at tiles t0.. of a
+// chunk-major packed matrix with NT tiles per chunk: thread t writes one
+// fragment entry (8 values).
 __global__ __launch_bounds__(kBlock) void pack_frag_kernel(const uint16_t* W, int N, int K, uint16_t* P, int NT,
-                                                           int t0) {
+                                                           int t0, float scale) {
   const size_t t = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x;
   const size_t total = static_cast<size_t>(N / 16) * (K / 32) * kWave;
   if (t >= total) return;
@@ -652,7 +656,19 @@ __global__ __launch_bounds__(kBlock) void pack_frag_kernel(const uint16_t* W, in
   const uint16_t* src = W + static_cast<size_t>(tile * 16 + l % 16) * K + c * 32 + 8 * (l / 16);
   uint16_t* dst = P + frag_at(t0 + tile, c, NT) + l * 8;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = src[e];
+  for (int e = 0; e < 8; ++e)
+    dst[e] = static_cast<uint16_t>(f16_bits(static_cast<_Float16>(bf16_to_f32(src[e]) * scale)));
+}
+
+// *out = max |W| over n bf16 values, as float bits (non-negative floats
+// order like their bit patterns).
+__global__ __launch_bounds__(kBlock) void absmax_bf16_kernel(const uint16_t* W, size_t n, uint32_t* out) {
+  float m = 0.0f;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * kBlock)
+    m = fmaxf(m, fabsf(bf16_to_f32(W[i])));
+  m = wave_max(m);
+  if (threadIdx.x % kWave == 0) atomicMax(out, __float_as_uint(m));
 }
 
 }  // namespace
@@ -669,19 +685,27 @@ hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a,
 }
 
 hipError_t launch_split_rows(const float* X, int ldx, int M, int K, const float* g, uint16_t* planes, float* ssp,
-                             hipStream_t s) {
+                             int* ovf, const int* pos, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (K % 256 || ldx % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_rows_kernel, dim3((M + 63) / 64 * 4, K / 256), dim3(kBlock), 0, s, X, ldx, M, K, g,
-                     planes, ssp);
+                     planes, ssp, ovf, pos);
   return hipGetLastError();
 }
 
-hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, int t0, hipStream_t s) {
-  if (N % 16 || K % 32 || N <= 0 || K <= 0 || t0 < 0 || t0 + N / 16 > NT) return hipErrorInvalidValue;
+hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, int t0, int S, hipStream_t s) {
+  if (N % 16 || K % 32 || N <= 0 || K <= 0 || t0 < 0 || t0 + N / 16 > NT || S < -100 || S > 100)
+    return hipErrorInvalidValue;
   const size_t total = static_cast<size_t>(N / 16) * (K / 32) * kWave;
   hipLaunchKernelGGL(pack_frag_kernel, dim3(static_cast<unsigned>((total + kBlock - 1) / kBlock)), dim3(kBlock),
-                     0, s, W, N, K, P, NT, t0);
+                     0, s, W, N, K, P, NT, t0, ldexpf(1.0f, S));
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax_bf16(const uint16_t* W, size_t n, uint32_t* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + kBlock - 1) / kBlock, 4096);
+  hipLaunchKernelGGL(absmax_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, W, n, out);
   return hipGetLastError();
 }
 

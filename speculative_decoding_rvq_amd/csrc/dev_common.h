@@ -6,6 +6,8 @@
 #include <type_traits>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace cps {
 
 constexpr int kBlock = 256;  // every kernel runs 4 wave64s per workgroup
@@ -36,43 +38,57 @@ template <> struct Chunk<uint16_t> {
   }
 };
 
-// x = hi + mid + lo, each a bf16 bit pattern, by truncation: hi keeps the
-// top 8 significant bits of x, mid the top 8 of the exact remainder x - hi,
-// lo the rest (at most 8 significant bits, so bf16 holds it exactly).
-__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
-  const uint32_t hb = __float_as_uint(x) & 0xFFFF0000u;
-  const float r1 = x - __uint_as_float(hb);
-  const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
-  const float r2 = r1 - __uint_as_float(mb);
-  h = hb >> 16;
-  m = mb >> 16;
-  l = __float_as_uint(r2) >> 16;
+// Activation rows that feed the packed matrix-core projections are carried
+// as two fp16 pieces, x ~ hi + lo: hi = fp16(x) and lo = fp16(x - hi), both
+// rounded to nearest even (x - hi is exact in fp32).  hi + lo holds x to 22
+// significant bits, or to 2^-25 in absolute terms when lo is subnormal;
+// fp16 x fp16 products are exact in fp32.  A value outside fp16's range
+// (|x| >= 65504, or NaN) sets the caller's overflow flag and is carried as
+// +-65504, so what it feeds stays finite (and wrong: the caller reports the
+// flag).  kPieces (two) in kernels.h.
+constexpr float kF16Max = 65504.0f;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+// The two pieces of x0, x1, packed two values per word (x0 in the low half).
+__device__ __forceinline__ void split2_pair(float x0, float x1, uint32_t& hi, uint32_t& lo, bool& bad) {
+  bad |= !(fabsf(x0) < kF16Max) || !(fabsf(x1) < kF16Max);
+  x0 = fminf(fmaxf(x0, -kF16Max), kF16Max);  // NaN -> -65504
+  x1 = fminf(fmaxf(x1, -kF16Max), kF16Max);
+  const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+  const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
+  const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
+  hi = f16_bits(h0) | (f16_bits(h1) << 16);
+  lo = f16_bits(l0) | (f16_bits(l1) << 16);
 }
 
 // Eight consecutive values y of row `row`, columns k .. k+7 (k % 8 == 0),
-// split into three bf16 pieces (split3) and stored as one fragment entry
-// per piece in a chunk-major plane buffer with T row tiles: row tile
-// t = row / 16, K chunk c = k / 32, piece p at ((c * T + t) * 3 + p) * 64
-// 16-byte entries, fragment lane (row % 16) + 16 ((k % 32) / 8).
-__device__ __forceinline__ void split_store8(uint16_t* planes, int T, int row, int k, const float (&y)[8]) {
+// split into their two pieces and stored as one fragment entry per piece in
+// a chunk-major plane buffer with T row tiles: row tile t = row / 16, K
+// chunk c = k / 32, piece p at ((c * T + t) * 2 + p) * 64 16-byte entries,
+// fragment lane (row % 16) + 16 ((k % 32) / 8).  Returns whether a value
+// was outside fp16's range (the caller raises the overflow flag for rows
+// whose outputs are used).
+__device__ __forceinline__ bool split_store8(uint16_t* planes, int T, int row, int k, const float (&y)[8]) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  uint32_t hp[4], mp[4], lp[4];
+  uint32_t hp[4], lp[4];
+  bool bad = false;
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const float y0 = y[i], y1 = y[i + 1];
-    const float r0 = y0 - __uint_as_float(__float_as_uint(y0) & 0xFFFF0000u);
-    const float r1 = y1 - __uint_as_float(__float_as_uint(y1) & 0xFFFF0000u);
-    const float q0 = r0 - __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
-    const float q1 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-    hp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
-    mp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
-    lp[i / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
-  }
+  for (int i = 0; i < 8; i += 2) split2_pair(y[i], y[i + 1], hp[i / 2], lp[i / 2], bad);
   const int L = row % 16 + 16 * ((k % 32) / 8);
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(planes) + (static_cast<size_t>(k / 32) * T + row / 16) * 3 * 64 + L;
+  u32x4_t* dst =
+      reinterpret_cast<u32x4_t*>(planes) + (static_cast<size_t>(k / 32) * T + row / 16) * kPieces * 64 + L;
   dst[0] = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
-  dst[64] = u32x4_t{mp[0], mp[1], mp[2], mp[3]};
-  dst[128] = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
+  dst[64] = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
+  return bad;
+}
+
+// The overflow flag of a split row: raised for rows at a position (pos
+// nullable: every row).  Inactive rows run through the projections with
+// whatever their buffers hold, and their outputs are never used.
+__device__ __forceinline__ void flag_overflow(int* ovf, const int* pos, int row) {
+  if (ovf != nullptr && (pos == nullptr || pos[row] >= 0)) *ovf = 1;
 }
 
 // Row `row` of a table stored as WT, converted to fp32 element `i`.

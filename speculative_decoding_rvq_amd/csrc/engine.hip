@@ -50,7 +50,7 @@ struct Shape {
 
 struct Layout {
   size_t st, call, sstats, dhead, thead, pos, hstate, dX, X, Hout, ncode, Q, attn, act, kv, dlogits, q, dcode, dflags,
-      tlogits, p, tcode, tflags, rope, packed, planes, ssp, fhead, cq, ccode, cflags, hb, total;
+      tlogits, p, tcode, tflags, rope, packed, planes, ssp, fhead, cq, ccode, cflags, hb, ovf, total;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -236,12 +236,13 @@ Layout make_layout(const Shape& s) {
   l.tflags = take(B * Rt * i4);
   l.rope = take(static_cast<size_t>(s.G) * (s.d / 2) * sizeof(float2));
   l.packed = take(packed_elems(s) * sizeof(uint16_t));
-  // pre-split activation planes (three bf16 per value) and partial sums of
+  // pre-split activation planes (two fp16 per value) and partial sums of
   // squares of the batched projections' input rows
   const size_t prow = packs_weights(s) ? (B * R + 63) / 64 * 64 : 0;
   const size_t kmax = std::max({static_cast<size_t>(s.H), static_cast<size_t>(s.qdim), static_cast<size_t>(s.F)});
-  l.planes = take(2 * prow * kmax * 3 * sizeof(uint16_t));  // two alternating buffers
+  l.planes = take(2 * prow * kmax * kPieces * sizeof(uint16_t));  // two alternating buffers
   l.ssp = take(prow * (kmax / 32) * f4);
+  l.ovf = take(2 * sizeof(uint32_t));  // activation outside fp16's range; create's scratch word
   l.total = off;
   return l;
 }
@@ -261,6 +262,9 @@ struct cp_spec {
   // down; the lm_heads; all null when the weights are not packed
   std::vector<std::array<const uint16_t*, 5>> packed;
   const uint16_t* packed_heads = nullptr;
+  // 2^-S of each packed matrix (the packed fp16 copy holds W * 2^S)
+  std::vector<std::array<float, 5>> pscale;
+  float hscale = 1.0f;
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t graph = nullptr;
   int graph_B = -1;
@@ -291,6 +295,7 @@ struct cp_spec {
     r.doff = doff;
     r.dX = sh.K > 0 && !sh.fd ? at<float>(lo.dX) : nullptr;
     r.fused = sh.fd;
+    r.ovf = at<int>(lo.ovf);
     r.fhead = sh.fd ? at<int>(lo.fhead) : nullptr;
     r.cq = sh.fd ? at<float>(lo.cq) : nullptr;
     r.ccode = sh.fd ? at<int>(lo.ccode) : nullptr;
@@ -369,7 +374,7 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
       // decoder layers' own path has them split by the producing kernel)
       uint16_t* planes = h->at<uint16_t>(h->lo.planes);
       float* ssp = h->at<float>(h->lo.ssp);
-      CPS_HIP(launch_split_rows(a.X, a.ldx, a.M, a.K, a.norm_g, planes, ssp, s));
+      CPS_HIP(launch_split_rows(a.X, a.ldx, a.M, a.K, a.norm_g, planes, ssp, a.ovf, a.pos, s));
       a.planes = planes;
       a.ptiles = (a.M + 63) / 64 * 4;
       a.ssp = ssp;
@@ -453,9 +458,14 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
   a.xdiv = 1;
   a.M = M;
   a.eps = sh.eps;
+  a.ovf = h->at<int>(h->lo.ovf);
+  a.pos = pos;  // the overflow flag ignores inactive rows
+  a.wscale0 = a.wscale1 = 1.0f;
+  const float* psc = h->pscale.empty() ? nullptr : h->pscale[l].data();
+  auto sc = [&](int i) { return psc ? psc[i] : 1.0f; };
   uint16_t* P0 = h->at<uint16_t>(h->lo.planes);
   uint16_t* P1 = P0 + static_cast<size_t>((M + 63) / 64 * 64) *
-                          std::max({sh.H, sh.qdim, sh.F}) * 3;  // within the second buffer
+                          std::max({sh.H, sh.qdim, sh.F}) * kPieces;  // within the second buffer
   float* S = h->at<float>(h->lo.ssp);
   const int T = (M + 63) / 64 * 4;
   switch (kind) {
@@ -467,6 +477,7 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       a.qdim = sh.qdim; a.kvdim = sh.kvdim; a.kv = kvl; a.kv_sb = h->kv_sb();
       a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.Gk;
       if (fused) a.planes = P0, a.ptiles = T, a.ssp = S;
+      a.wscale0 = sc(0);
       return gemv(h, s, kQKV, a, pw(0));
     case CP_SPEC_KERNEL_ATTENTION: {
       AttnArgs at{};
@@ -474,6 +485,7 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       at.rope = h->at<float2>(h->lo.rope); at.R = R; at.nq = sh.nq; at.nkv = sh.nkv; at.d = sh.d;
       at.G = sh.G; at.scale = 1.0f / std::sqrt(static_cast<float>(sh.d));
       if (fused) at.planes = P1, at.ptiles = T;
+      at.ovf = h->at<int>(h->lo.ovf);
       if (sh.tn > 0) {  // tree window: node slots and ancestor masks
         at.Gk = sh.Gk;
         at.RB = sh.trb;
@@ -493,11 +505,14 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
         a.planes = P1, a.ptiles = T;
         a.out_planes = P0, a.out_ptiles = T, a.out_g = static_cast<const float*>(w[5]), a.out_ssp = S;
       }
+      a.wscale0 = sc(1);
       return gemv(h, s, kAdd, a, pw(1));
     case CP_SPEC_KERNEL_GATE_UP:
       a.W0 = w[6]; a.W1 = w[7]; a.N = sh.F; a.K = sh.H; a.X = X; a.ldx = sh.H;
       a.norm_g = static_cast<const float*>(w[5]); a.Y = act; a.ldy = sh.F;
       if (fused) a.planes = P0, a.ptiles = T, a.ssp = S, a.out_planes = P1, a.out_ptiles = T;
+      a.wscale0 = sc(2);
+      a.wscale1 = sc(3);
       return gemv(h, s, kSwiGLU, a, pw(2), pw(3));
     case CP_SPEC_KERNEL_DOWN:
       a.W0 = w[8]; a.N = sh.H; a.K = sh.F; a.X = act; a.ldx = sh.F; a.Y = X; a.ldy = sh.H;
@@ -507,6 +522,7 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
           a.out_planes = P0, a.out_ptiles = T, a.out_g = static_cast<const float*>(h->layers[l + 1][0]),
           a.out_ssp = S;
       }
+      a.wscale0 = sc(4);
       return gemv(h, s, kAdd, a, pw(4));
     default:
       return fail(CP_SPEC_EINVAL, "not a decoder kernel kind");
@@ -521,7 +537,7 @@ int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const in
   const bool fused = fused_planes(h, B * R);
   if (fused)  // layer 0's Q/K/V input: the rows as the round left them
     CPS_HIP(launch_split_rows(X, h->sh.H, B * R, h->sh.H, static_cast<const float*>(h->layers[0][0]),
-                              h->at<uint16_t>(h->lo.planes), h->at<float>(h->lo.ssp), s));
+                              h->at<uint16_t>(h->lo.planes), h->at<float>(h->lo.ssp), h->at<int>(h->lo.ovf), pos, s));
   for (int l = 0; l < h->sh.L; ++l)
     for (int kind : kLayerKinds) {
       const int rc = layer_kernel(h, s, kind, l, B, R, X, pos, kv, fused);
@@ -547,6 +563,8 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
   a.n_heads = h->sh.G - 1;
   a.hb = hb;
   a.hbK = hb != nullptr ? h->sh.K : 0;
+  a.wscale0 = a.wscale1 = h->hscale;
+  a.ovf = h->at<int>(h->lo.ovf);
   if (per_head > 0 && h->packed_heads != nullptr && a.N % 64 == 0 && a.K % 512 == 0) {
     // bf16, packed heads: 32 x 64 tiles per head
     a.W0 = h->packed_heads;
@@ -711,31 +729,51 @@ int cp_spec_create(const cp_spec_weights* w, const cp_spec_cfg* cfg, void* d_wor
     // fragment-packed copies of every bf16 matrix (read once, here)
     uint16_t* p = h->at<uint16_t>(lo.packed);
     // a packed matrix of NT tiles per chunk from row-stacked sources
-    auto pack = [&](std::initializer_list<std::pair<const void*, int>> parts, int K) {
+    // as fp16 times 2^S, S putting the matrix's largest |w| just below 2^15
+    // (every bf16 value of magnitude 2^(-S-17) or more is then exact); the
+    // kernels multiply their sums by 2^-S
+    uint32_t* d_max = h->at<uint32_t>(lo.ovf);  // scratch word
+    auto pack = [&](std::initializer_list<std::pair<const void*, int>> parts, int K, float* wscale) {
       int N = 0;
       for (const auto& pr : parts) N += pr.second;
       uint16_t* dst = p;
+      uint32_t mbits = 0;
+      if (e == hipSuccess) e = hipMemset(d_max, 0, sizeof(uint32_t));
+      for (const auto& pr : parts)
+        if (e == hipSuccess)
+          e = launch_absmax_bf16(static_cast<const uint16_t*>(pr.first), static_cast<size_t>(pr.second) * K, d_max,
+                                 nullptr);
+      if (e == hipSuccess) e = hipMemcpy(&mbits, d_max, sizeof(uint32_t), hipMemcpyDeviceToHost);
+      float mx = 0.0f;
+      std::memcpy(&mx, &mbits, sizeof(float));
+      int ex = 0;
+      if (mx > 0.0f) std::frexp(mx, &ex);  // mx < 2^ex
+      const int S = mx > 0.0f ? 15 - ex : 0;
+      *wscale = std::ldexp(1.0f, -S);
       int t0 = 0;
       for (const auto& pr : parts) {
         if (e == hipSuccess)
-          e = pack_fragments(static_cast<const uint16_t*>(pr.first), pr.second, K, dst, N / 16, t0, nullptr);
+          e = pack_fragments(static_cast<const uint16_t*>(pr.first), pr.second, K, dst, N / 16, t0, S, nullptr);
         t0 += pr.second / 16;
       }
       p += static_cast<size_t>(N) * K;
       return dst;
     };
     h->packed.resize(s.L);
+    h->pscale.resize(s.L);
     for (int l = 0; l < s.L; ++l) {
       const auto& wl = h->layers[l];
       auto& pk = h->packed[l];
-      pk[0] = pack({{wl[1], s.qdim}, {wl[2], s.kvdim}, {wl[3], s.kvdim}}, s.H);  // Q, K, V tiles
-      pk[1] = pack({{wl[4], s.H}}, s.qdim);
-      pk[2] = pack({{wl[6], s.F}}, s.H);
-      pk[3] = pack({{wl[7], s.F}}, s.H);
-      pk[4] = pack({{wl[8], s.H}}, s.F);
+      auto& ps = h->pscale[l];
+      pk[0] = pack({{wl[1], s.qdim}, {wl[2], s.kvdim}, {wl[3], s.kvdim}}, s.H, &ps[0]);  // Q, K, V tiles
+      pk[1] = pack({{wl[4], s.H}}, s.qdim, &ps[1]);
+      pk[2] = pack({{wl[6], s.F}}, s.H, &ps[2]);
+      pk[3] = pack({{wl[7], s.F}}, s.H, &ps[3]);
+      pk[4] = pack({{wl[8], s.H}}, s.F, &ps[4]);
     }
-    h->packed_heads = pack({{h->heads, (s.G - 1) * s.V}}, s.H);
+    h->packed_heads = pack({{h->heads, (s.G - 1) * s.V}}, s.H, &h->hscale);
     if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemset(d_max, 0, sizeof(uint32_t));
   }
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
   if (e == hipSuccess && s.fd && s.K > 0) {
@@ -819,10 +857,14 @@ int cp_spec_decode_frames(cp_spec* h, void* stream, int32_t n_streams, int32_t n
     if (launched > cap) return fail(CP_SPEC_EHIP, "round loop did not terminate");
     chunk = need;
   }
-  if (d_stats) {
-    CPS_HIP(launch_stats_flush(r.sstats, B, d_stats, s));
-    CPS_HIP(hipStreamSynchronize(s));
-  }
+  if (d_stats) CPS_HIP(launch_stats_flush(r.sstats, B, d_stats, s));
+  int ovf = 0;
+  CPS_HIP(hipMemcpyAsync(&ovf, r.ovf, sizeof(int), hipMemcpyDeviceToHost, s));
+  CPS_HIP(hipStreamSynchronize(s));
+  if (ovf)
+    return fail(CP_SPEC_EUNSUPPORTED,
+                "an activation reached |x| >= 65504, outside the fp16 range of the matrix-core projections: "
+                "this call's codes are not valid");
   return CP_SPEC_OK;
 }
 

@@ -85,6 +85,10 @@ struct GemvArgs {
   int out_ptiles;
   const float* out_g;
   float* out_ssp;
+  // packed fp16 weights hold W * 2^S (one S per packed matrix): the tile's
+  // sums are multiplied by wscale0 (W0) / wscale1 (W1, the SwiGLU up half)
+  float wscale0, wscale1;
+  int* ovf;  // set when an activation of a row in use (pos null or pos[row] >= 0) split for the matrix cores leaves fp16's range
 };
 
 struct AttnArgs {
@@ -92,6 +96,7 @@ struct AttnArgs {
   float* out;         // [B*R][qdim]
   uint16_t* planes;   // nullable: out split for the O projection instead
   int ptiles;         // (planes) row tiles
+  int* ovf;           // (planes) see GemvArgs
   const float* kv;    // layer base, + b*kv_sb
   long long kv_sb;
   long long kv_vo;
@@ -202,6 +207,7 @@ struct RoundArgs {
   uint32_t* dflags;  // [B][W]
   float* tlogits;  // [B][R][V]; fused drafts: [B][R][W + 1][V], column 0
   float* p;        // [B][R][V]
+  int* ovf;        // activation outside fp16's range (cleared by the init kernel)
   // fused drafts: rows (b, r, k) of the heads launch (k = 0 target, k >= 1
   // row r's candidate draft of offset k), their heads, and every row's
   // candidate drafts (distributions, codes, flags) until the accept step
@@ -227,19 +233,26 @@ hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 g
 // (fm, fn) in {(2, 2), (2, 4), (4, 4), (4, 6)}, K a multiple of 512; grid
 // (columns / tile, rows / tile) or, lm_heads, (V / tile, row tiles, heads).
 hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
-// One bf16 matrix [N][K] row-major into MFMA fragment order (N % 16 == 0,
-// K % 32 == 0), at tiles t0 .. t0 + N/16 - 1 of a chunk-major packed matrix
-// with NT tiles per chunk: fragment (tile t, K chunk c) is 64 lanes x 8 bf16
-// at ((c * NT + t) * 64 + lane) * 8, lane l holding W[16 t + l % 16][32 c +
-// 8 (l / 16) + 0..7].
-hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, int t0, hipStream_t s);
-// Rows [0, M) of X (times g when set) split into three bf16 planes in
+// One bf16 matrix [N][K] row-major, times 2^S, as fp16 in MFMA fragment
+// order (N % 16 == 0, K % 32 == 0), at tiles t0 .. t0 + N/16 - 1 of a
+// chunk-major packed matrix with NT tiles per chunk: fragment (tile t, K
+// chunk c) is 64 lanes x 8 fp16 at ((c * NT + t) * 64 + lane) * 8, lane l
+// holding W[16 t + l % 16][32 c + 8 (l / 16) + 0..7] * 2^S.
+hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, int t0, int S, hipStream_t s);
+// *out = the largest |W| of n bf16 values, as float bits (*out must be 0
+// before).
+hipError_t launch_absmax_bf16(const uint16_t* W, size_t n, uint32_t* out, hipStream_t s);
+// Activation pieces per value in the planes of the batched projections.
+constexpr int kPieces = 2;
+// Rows [0, M) of X (times g when set) split into two fp16 planes in
 // fragment order for launch_bgemm (a.planes): with T = ceil(M / 64) * 4 row
-// tiles, row tile t, K chunk c, plane p at ((c * T + t) * 3 + p) * 512 bf16;
+// tiles, row tile t, K chunk c, plane p at ((c * T + t) * 2 + p) * 512 fp16;
 // rows from M up to 64 T are zero.  With g,
-// ssp[m][j] = sum of x^2 over K chunk j (32 wide).  K % 256 == 0.
+// ssp[m][j] = sum of x^2 over K chunk j (32 wide).  K % 256 == 0.  A value
+// outside fp16's range in row m sets *ovf (nullable) when pos (nullable) is
+// null or pos[m] >= 0.
 hipError_t launch_split_rows(const float* X, int ldx, int M, int K, const float* g, uint16_t* planes, float* ssp,
-                             hipStream_t s);
+                             int* ovf, const int* pos, hipStream_t s);
 // LDS the attention kernel needs, and raising its limit above 64 KB (once,
 // before any launch).
 size_t attention_smem_bytes(int G, int d, int R, int group);

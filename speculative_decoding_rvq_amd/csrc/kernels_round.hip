@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
     }
     const int row = b * R + r, k = (g * group + j) * D + i8;
     if (a.planes != nullptr) {
-      split_store8(a.planes, a.ptiles, row, k, o);
+      if (split_store8(a.planes, a.ptiles, row, k, o)) flag_overflow(a.ovf, nullptr, row);  // active rows only
     } else {
       float* dst = a.out + static_cast<size_t>(row) * qdim + k;
       *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
@@ -588,7 +588,10 @@ __device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int 
 
 __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, const CallDesc c) {
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x == 0) *r.call = c;
+  if (b == 0 && threadIdx.x == 0) {
+    *r.call = c;
+    *r.ovf = 0;  // no activation has left fp16's range in this call yet
+  }
   constexpr int kStatWords = sizeof(cp_spec_stats) / sizeof(long long);
   if (threadIdx.x < kStatWords) reinterpret_cast<long long*>(r.sstats + b)[threadIdx.x] = 0;
   StreamState st{};
@@ -1479,7 +1482,7 @@ __global__ __launch_bounds__(kBlock) void tree_attention_kernel(const AttnArgs a
     }
     const int row = b * R + r, k = (g * group + j) * D + i8;
     if (a.planes != nullptr) {
-      split_store8(a.planes, a.ptiles, row, k, o);
+      if (split_store8(a.planes, a.ptiles, row, k, o)) flag_overflow(a.ovf, nullptr, row);  // active rows only
     } else {
       float* dst = a.out + static_cast<size_t>(row) * qdim + k;
       *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);

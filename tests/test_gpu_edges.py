@@ -101,3 +101,34 @@ def test_one_handle_different_stream_counts():
         assert got[2]["frames"] == 3 * B
         pairs = [(f, b) for f in range(3) for b in range(B)]
         _check(f"B={B}", c, m, got, hf[:, :B], c0[:, :B], seeds[:, :B], pairs)
+
+
+def test_activation_outside_fp16_range_is_reported():
+    """The matrix-core projections (bf16 weights, 32 or more rows) carry
+    activations as two fp16 pieces.  A layer-0 norm gain of 1e5 pushes the
+    normed inputs past fp16's range: the call must fail with EUNSUPPORTED,
+    and the same handle must decode normally, code for code, once the gain
+    is back to 1 (the flag starts clear in every call)."""
+    from speculative_decoding_rvq_amd import binding
+    c = synth.custom(**{**_SHAPE, "hidden": 512, "q_heads": 8, "ffn": 1024},
+                     dtype=synth.BF16, groups=8, verify_size=4, top_k=50, frames=2,
+                     streams=16)
+    assert binding.workspace_bytes(binding.make_cfg(c, 16)) > 0  # a valid bf16 shape
+    w = synth.make_weights(c)
+    wd = binding.weights_to_device(w)
+    h = binding.Handle(c, wd, max_streams=16)
+    hf, c0, seeds = synth.make_inputs(c)
+    log("bf16 B=16 N=4: reference call")
+    ref = decode_gpu(h, hf, c0, seeds)
+    gain = wd["layers"][0]["attn_norm"]
+    gain.fill_(1e5)
+    torch.cuda.synchronize()
+    log("bf16 B=16 N=4: layer-0 gain 1e5")
+    with pytest.raises(binding.CpSpecError) as err:
+        decode_gpu(h, hf, c0, seeds)
+    assert err.value.rc == binding.EUNSUPPORTED and "65504" in str(err.value)
+    gain.fill_(1.0)
+    torch.cuda.synchronize()
+    log("bf16 B=16 N=4: gain back to 1")
+    again = decode_gpu(h, hf, c0, seeds)
+    assert np.array_equal(again[0], ref[0]) and np.array_equal(again[1], ref[1])

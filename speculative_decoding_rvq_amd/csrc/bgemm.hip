@@ -100,7 +100,9 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   constexpr int SW = PL ? 1 : kGW;  // stage: only the in-kernel split uses it
   struct StageT { u32x4 f[SW][FM * kPieces][kWave]; };  // split fragments of one chunk
-  struct PartT { float v[4][TM][TN + 1]; float ssq[kGW][TM]; };
+  // partial tiles in fragment order (lane l's four values of fragment
+  // (f, n) as one 16-byte entry), four slots
+  struct PartT { floatx4 v[4][FM * FN][kWave]; float ssq[kGW][TM]; };
   __shared__ union {
     StageT stage;
     PartT part;
@@ -204,8 +206,8 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
         for (int f = 0; f < FM; ++f)
 #pragma unroll
           for (int n = 0; n < FN; ++n)
-            acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, fa.x[f][p]),
-                                                               __builtin_bit_cast(h8, fb.w[n]), acc[f][n], 0, 0, 0);
+            acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, fb.w[n]),
+                                                               __builtin_bit_cast(h8, fa.x[f][p]), acc[f][n], 0, 0, 0);
     };
     // two chunks of loads in flight (an even chunk count per wave; the
     // fetches past the end re-read the last chunk and are not used)
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
       for (int f = 0; f < FM; ++f)
 #pragma unroll
         for (int n = 0; n < FN; ++n)
-          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[f], __builtin_bit_cast(h8, fb.w[n]), acc[f][n], 0,
+          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, fb.w[n]), ap[f], acc[f][n], 0,
                                                              0, 0);
     }
   };
@@ -356,8 +358,10 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 
   // ---- the eight partial tiles meet in LDS in a fixed order: waves 4-7
   // hand theirs to waves 0-3 (w + w+4), which store the four sums; one more
-  // barrier and every thread finishes TM * TN / 512 outputs as
-  // (s0 + s1) + (s2 + s3).  The rows' partial sums of squares go along. ----
+  // barrier and every wave reads the four sums of the fragments it finishes
+  // as (s0 + s1) + (s2 + s3).  Entries are 16 bytes per lane, in lane
+  // order: no bank conflicts.  The rows' partial sums of squares go
+  // along. ----
   __syncthreads();  // every wave is past its last stage read (stage and part share LDS)
   if (NORM && !PL) {
 #pragma unroll
@@ -368,26 +372,22 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
       if ((lane & 3) == 0) sm.part.ssq[wave][16 * i + (lane >> 2)] = t;
     }
   }
-  auto store_acc = [&](int slot) __attribute__((always_inline)) {
+  if (wave >= 4) {
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int n = 0; n < FN; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.part.v[slot][16 * f + 4 * lg + i][16 * n + li] = acc[f][n][i];
-  };
-  if (wave >= 4) store_acc(wave - 4);
-  __syncthreads();
-  if (wave < 4) {
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int n = 0; n < FN; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[f][n][i] += sm.part.v[wave][16 * f + 4 * lg + i][16 * n + li];
+      for (int n = 0; n < FN; ++n) sm.part.v[wave - 4][f * FN + n][lane] = acc[f][n];
   }
   __syncthreads();
-  if (wave < 4) store_acc(wave);
+  if (wave < 4) {  // slot `wave` is this wave's alone from here on
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        acc[f][n] += sm.part.v[wave][f * FN + n][lane];
+        sm.part.v[wave][f * FN + n][lane] = acc[f][n];
+      }
+  }
   if constexpr (PL && NORM) {
     float t = 0.0f;
 #pragma unroll
@@ -409,11 +409,6 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
       return 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
     }
   };
-  auto tile_val = [&](int r, int c) {
-    const float v = (sm.part.v[0][r][c] + sm.part.v[1][r][c]) + (sm.part.v[2][r][c] + sm.part.v[3][r][c]);
-    const float ws = (MODE == kSwiGLU && c >= TN / 2) ? a.wscale1 : a.wscale0;  // 2^-S, exact
-    return NORM ? v * ws * rinv_of(r) : v * ws;
-  };
 
   // final-normed rows for the heads' caller (the column tiles split K)
   if (MODE == kHead && NORM && a.xnorm_out != nullptr) {
@@ -433,121 +428,117 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     }
   }
 
-  // ---- fused epilogue: all of the thread's values first, then the stores
-  // (the residual add loads every old value before storing any) ----
-  const int n0 = bx * TN;
-  if (MODE == kSwiGLU && a.out_planes != nullptr) {
-    // the down projection's input: eight activations per thread, split
-    constexpr int W = TN / 2, G = TM * W / 8;
-    for (int q = tid; q < G; q += kGT) {
-      const int r = q / (W / 8), c8 = (q % (W / 8)) * 8;
-      const int row = rows_s[r];
-      if (row < 0) continue;
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float g = tile_val(r, c8 + e), u = tile_val(r, c8 + e + W);
-        y[e] = g / (1.0f + expf(-g)) * u;
-      }
-      if (split_store8(a.out_planes, a.out_ptiles, row, bx * W + c8, y)) flag_overflow(a.ovf, a.pos, row);
-    }
-    return;
-  }
-  if (MODE == kSwiGLU) {
-    constexpr int PER = TM * (TN / 2) / kGT;
-    float out[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kGT, r = idx / (TN / 2), c = idx % (TN / 2);
-      const float g = tile_val(r, c), u = tile_val(r, c + TN / 2);
-      out[k] = g / (1.0f + expf(-g)) * u;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kGT, r = idx / (TN / 2), c = idx % (TN / 2);
-      const int row = rows_s[r];
-      if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + bx * (TN / 2) + c] = out[k];
-    }
-    return;
-  }
-  constexpr int PER = TM * TN / kGT;
-  float val[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int idx = tid + k * kGT;
-    val[k] = tile_val(idx / TN, idx % TN);
-  }
-  if (MODE == kAdd && a.out_planes != nullptr) {
-    // the residual rows, then the next normed projection's input: x * g
-    // split, eight columns per thread, and the rows' sums of squares per 32
-    // columns (four neighbouring lanes)
-    constexpr int G = TM * TN / 8, ITER = (G + kGT - 1) / kGT;
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int q = tid + it * kGT;
-      const int r = q < G ? q / (TN / 8) : 0, c8 = q < G ? (q % (TN / 8)) * 8 : 0;
-      const int row = q < G ? rows_s[r] : -1;
-      float ss = 0.0f;
-      if (row >= 0) {
-        float* yp = a.Y + static_cast<size_t>(row) * a.ldy + n0 + c8;
-        const floatx4 o0 = *reinterpret_cast<const floatx4*>(yp);
-        const floatx4 o1 = *reinterpret_cast<const floatx4*>(yp + 4);
-        float xn[8], y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xn[e] = (e < 4 ? o0[e] : o1[e - 4]) + tile_val(r, c8 + e);
-        *reinterpret_cast<floatx4*>(yp) = floatx4{xn[0], xn[1], xn[2], xn[3]};
-        *reinterpret_cast<floatx4*>(yp + 4) = floatx4{xn[4], xn[5], xn[6], xn[7]};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ss = fmaf(xn[e], xn[e], ss);
-          y[e] = a.out_g != nullptr ? xn[e] * a.out_g[n0 + c8 + e] : xn[e];
-        }
-        if (split_store8(a.out_planes, a.out_ptiles, row, n0 + c8, y)) flag_overflow(a.ovf, a.pos, row);
-      }
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      if (row >= 0 && c8 % 32 == 0) a.out_ssp[static_cast<size_t>(row) * (a.N / 32) + (n0 + c8) / 32] = ss;
-    }
-    return;
-  }
-  if (MODE == kAdd) {
-    float old[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kGT, row = rows_s[idx / TN];
-      old[k] = row >= 0 ? a.Y[static_cast<size_t>(row) * a.ldy + n0 + idx % TN] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = tid + k * kGT, row = rows_s[idx / TN];
-      if (row >= 0) a.Y[static_cast<size_t>(row) * a.ldy + n0 + idx % TN] = old[k] + val[k];
-    }
-    return;
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int idx = tid + k * kGT, r = idx / TN, c = idx % TN;
+  // ---- each wave finishes fragment pairs u = wave, wave + 8, ...: (f, n0)
+  // and (f, n1), n0 = j and n1 = j + FN / 2 for SwiGLU (a gate tile and its
+  // up tile), n0 = 2 j and n1 = 2 j + 1 otherwise (32 adjacent columns).
+  // Lane l holds row 16 f + l % 16 and, of each fragment, the four columns
+  // 4 (l / 16) .. +3, so every store writes 16 (fp32) or 8 (fp16) bytes. ----
+  const int n0col = bx * TN;
+  constexpr int U = FM * (FN / 2);
+  const int c4 = 4 * lg;
+  for (int u = wave; u < U; u += kGW) {
+    const int f = u / (FN / 2), j = u % (FN / 2);
+    const int na = MODE == kSwiGLU ? j : 2 * j, nb = MODE == kSwiGLU ? j + FN / 2 : 2 * j + 1;
+    const int r = 16 * f + li;
     const int row = rows_s[r];
+    const float rs = NORM ? rinv_of(r) : 1.0f;
+    float va[4], vb[4];
+    {
+      const floatx4 a0 = sm.part.v[0][f * FN + na][lane], a1 = sm.part.v[1][f * FN + na][lane];
+      const floatx4 a2 = sm.part.v[2][f * FN + na][lane], a3 = sm.part.v[3][f * FN + na][lane];
+      const floatx4 b0 = sm.part.v[0][f * FN + nb][lane], b1 = sm.part.v[1][f * FN + nb][lane];
+      const floatx4 b2 = sm.part.v[2][f * FN + nb][lane], b3 = sm.part.v[3][f * FN + nb][lane];
+      const float wa = a.wscale0, wb = MODE == kSwiGLU ? a.wscale1 : a.wscale0;  // 2^-S, exact
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        va[i] = ((a0[i] + a1[i]) + (a2[i] + a3[i])) * wa * rs;
+        vb[i] = ((b0[i] + b1[i]) + (b2[i] + b3[i])) * wb * rs;
+      }
+    }
     if (row < 0) continue;
-    const int o = n0 + c;
-    if (MODE == kHead) {
-      // rows of draft offset k = row % xdiv add head . b_k
-      const int ko = row % a.xdiv;
-      const float bias = (a.hb != nullptr && ko >= 1 && ko <= a.hbK)
-                             ? a.hb[(static_cast<size_t>(blockIdx.z) * a.hbK + (ko - 1)) * a.N + o]
-                             : 0.0f;
-      a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k] + bias;
-    } else if (MODE == kQKV) {
-      if (o < a.qdim) {
-        a.Y[static_cast<size_t>(row) * a.ldy + o] = val[k];
+    if (MODE == kSwiGLU) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = va[i] / (1.0f + expf(-va[i])) * vb[i];
+      const int col = bx * (TN / 2) + 16 * j + c4;  // column of the activations
+      if (a.out_planes != nullptr) {
+        if (split_store4(a.out_planes, a.out_ptiles, row, col, y)) flag_overflow(a.ovf, a.pos, row);
       } else {
-        const int pp = pos_s[r];
-        if (pp >= 0 && pp < a.kv_positions) {
-          const int b = row / a.rows_per_stream;
-          float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
-          const int oo = o - a.qdim;
-          if (oo < a.kvdim) base[oo] = val[k];
-          else base[a.kv_vo + (oo - a.kvdim)] = val[k];
+        *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + col) = floatx4{y[0], y[1], y[2], y[3]};
+      }
+      continue;
+    }
+    const int oa = n0col + 16 * na + c4, ob = n0col + 16 * nb + c4;
+    if (MODE == kAdd) {
+      float* ya = a.Y + static_cast<size_t>(row) * a.ldy + oa;
+      float* yb = a.Y + static_cast<size_t>(row) * a.ldy + ob;
+      const floatx4 pa = *reinterpret_cast<const floatx4*>(ya), pb = *reinterpret_cast<const floatx4*>(yb);
+      float xa[4], xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[i] = pa[i] + va[i];
+        xb[i] = pb[i] + vb[i];
+      }
+      *reinterpret_cast<floatx4*>(ya) = floatx4{xa[0], xa[1], xa[2], xa[3]};
+      *reinterpret_cast<floatx4*>(yb) = floatx4{xb[0], xb[1], xb[2], xb[3]};
+      if (a.out_planes != nullptr) {
+        // the next normed projection's input: x * g split, and the row's
+        // sum of squares over these 32 columns (four lanes of the row)
+        float ga[4] = {1.0f, 1.0f, 1.0f, 1.0f}, gb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (a.out_g != nullptr) {
+          const floatx4 g0 = *reinterpret_cast<const floatx4*>(a.out_g + oa);
+          const floatx4 g1 = *reinterpret_cast<const floatx4*>(a.out_g + ob);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ga[i] = g0[i], gb[i] = g1[i];
+        }
+        float ya4[4], yb4[4], ssr = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ssr = fmaf(xa[i], xa[i], ssr);
+          ya4[i] = xa[i] * ga[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ssr = fmaf(xb[i], xb[i], ssr);
+          yb4[i] = xb[i] * gb[i];
+        }
+        bool bad2 = split_store4(a.out_planes, a.out_ptiles, row, oa, ya4);
+        bad2 |= split_store4(a.out_planes, a.out_ptiles, row, ob, yb4);
+        if (bad2) flag_overflow(a.ovf, a.pos, row);
+        ssr += __shfl_xor(ssr, 16);
+        ssr += __shfl_xor(ssr, 32);
+        if (lg == 0) a.out_ssp[static_cast<size_t>(row) * (a.N / 32) + oa / 32] = ssr;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = h ? ob : oa;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = h ? vb[i] : va[i];
+      if (MODE == kHead) {
+        // rows of draft offset k = row % xdiv add head . b_k
+        const int ko = row % a.xdiv;
+        if (a.hb != nullptr && ko >= 1 && ko <= a.hbK) {
+          const floatx4 bias = *reinterpret_cast<const floatx4*>(
+              a.hb + (static_cast<size_t>(blockIdx.z) * a.hbK + (ko - 1)) * a.N + o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += bias[i];
+        }
+        *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + o) = floatx4{v[0], v[1], v[2], v[3]};
+      } else if (MODE == kQKV) {
+        if (o < a.qdim) {
+          *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + o) = floatx4{v[0], v[1], v[2], v[3]};
+        } else {
+          const int pp = pos_s[r];
+          if (pp >= 0 && pp < a.kv_positions) {
+            const int b = row / a.rows_per_stream;
+            float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
+            const int oo = o - a.qdim;
+            float* dst = oo < a.kvdim ? base + oo : base + a.kv_vo + (oo - a.kvdim);
+            *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
+          }
         }
       }
     }

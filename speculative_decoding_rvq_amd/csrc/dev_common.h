@@ -84,6 +84,21 @@ __device__ __forceinline__ bool split_store8(uint16_t* planes, int T, int row, i
   return bad;
 }
 
+// Four consecutive values y of row `row`, columns k .. k+3 (k % 4 == 0):
+// half of a fragment entry per piece (8 bytes), same layout as split_store8.
+__device__ __forceinline__ bool split_store4(uint16_t* planes, int T, int row, int k, const float (&y)[4]) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t h0, h1, l0, l1;
+  bool bad = false;
+  split2_pair(y[0], y[1], h0, l0, bad);
+  split2_pair(y[2], y[3], h1, l1, bad);
+  const int L = row % 16 + 16 * ((k % 32) / 8);
+  uint16_t* dst = planes + ((static_cast<size_t>(k / 32) * T + row / 16) * kPieces * 64 + L) * 8 + (k % 8);
+  *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h0, h1};
+  *reinterpret_cast<u32x2_t*>(dst + 64 * 8) = u32x2_t{l0, l1};
+  return bad;
+}
+
 // The overflow flag of a split row: raised for rows at a position (pos
 // nullable: every row).  Inactive rows run through the projections with
 // whatever their buffers hold, and their outputs are never used.

@@ -95,6 +95,98 @@ __device__ __forceinline__ void block_tile(int* bx, int* by) {
   *by = (g / gpc) * GR + j / GC;
 }
 
+// Finishes a lane's share of one fragment pair: va / vb are the scaled sums
+// of four consecutive columns of row `row` in fragments a and b.  SwiGLU: a
+// gate and its up values, oa the column of the activations; otherwise oa /
+// ob are the output columns of the two fragments (32 adjacent columns for
+// the residual add).  pp: the row's position (Q/K/V).  Lanes 16 apart hold
+// the same row (the residual add's sums of squares fold over them).
+template <int MODE>
+__device__ __forceinline__ void finish_pair(const GemvArgs& a, int row, int pp, int lg, const float (&va)[4],
+                                            const float (&vb)[4], int oa, int ob) {
+  if (MODE == kSwiGLU) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = va[i] / (1.0f + expf(-va[i])) * vb[i];
+    if (a.out_planes != nullptr) {
+      if (split_store4(a.out_planes, a.out_ptiles, row, oa, y)) flag_overflow(a.ovf, a.pos, row);
+    } else {
+      *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + oa) = floatx4{y[0], y[1], y[2], y[3]};
+    }
+    return;
+  }
+  if (MODE == kAdd) {
+    float* ya = a.Y + static_cast<size_t>(row) * a.ldy + oa;
+    float* yb = a.Y + static_cast<size_t>(row) * a.ldy + ob;
+    const floatx4 pa = *reinterpret_cast<const floatx4*>(ya), pb = *reinterpret_cast<const floatx4*>(yb);
+    float xa[4], xb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xa[i] = pa[i] + va[i];
+      xb[i] = pb[i] + vb[i];
+    }
+    *reinterpret_cast<floatx4*>(ya) = floatx4{xa[0], xa[1], xa[2], xa[3]};
+    *reinterpret_cast<floatx4*>(yb) = floatx4{xb[0], xb[1], xb[2], xb[3]};
+    if (a.out_planes != nullptr) {
+      // the next normed projection's input: x * g split, and the row's sum
+      // of squares over these 32 columns (four lanes of the row)
+      float ga[4] = {1.0f, 1.0f, 1.0f, 1.0f}, gb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (a.out_g != nullptr) {
+        const floatx4 g0 = *reinterpret_cast<const floatx4*>(a.out_g + oa);
+        const floatx4 g1 = *reinterpret_cast<const floatx4*>(a.out_g + ob);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ga[i] = g0[i], gb[i] = g1[i];
+      }
+      float ya4[4], yb4[4], ssr = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ssr = fmaf(xa[i], xa[i], ssr);
+        ya4[i] = xa[i] * ga[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ssr = fmaf(xb[i], xb[i], ssr);
+        yb4[i] = xb[i] * gb[i];
+      }
+      bool bad = split_store4(a.out_planes, a.out_ptiles, row, oa, ya4);
+      bad |= split_store4(a.out_planes, a.out_ptiles, row, ob, yb4);
+      if (bad) flag_overflow(a.ovf, a.pos, row);
+      ssr += __shfl_xor(ssr, 16);
+      ssr += __shfl_xor(ssr, 32);
+      if (lg == 0) a.out_ssp[static_cast<size_t>(row) * (a.N / 32) + oa / 32] = ssr;
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int o = h ? ob : oa;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = h ? vb[i] : va[i];
+    if (MODE == kHead) {
+      // rows of draft offset k = row % xdiv add head . b_k
+      const int ko = row % a.xdiv;
+      if (a.hb != nullptr && ko >= 1 && ko <= a.hbK) {
+        const floatx4 bias =
+            *reinterpret_cast<const floatx4*>(a.hb + (static_cast<size_t>(blockIdx.z) * a.hbK + (ko - 1)) * a.N + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += bias[i];
+      }
+      *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + o) = floatx4{v[0], v[1], v[2], v[3]};
+    } else if (MODE == kQKV) {
+      if (o < a.qdim) {
+        *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + o) = floatx4{v[0], v[1], v[2], v[3]};
+      } else if (pp >= 0 && pp < a.kv_positions) {
+        const int b = row / a.rows_per_stream;
+        float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
+        const int oo = o - a.qdim;
+        float* dst = oo < a.kvdim ? base + oo : base + a.kv_vo + (oo - a.kvdim);
+        *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
+      }
+    }
+  }
+}
+
 template <int MODE, int FM, int FN, bool NORM, bool PL>
 __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
@@ -456,93 +548,199 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
       }
     }
     if (row < 0) continue;
-    if (MODE == kSwiGLU) {
-      float y[4];
+    if (MODE == kSwiGLU)
+      finish_pair<MODE>(a, row, -1, lg, va, vb, bx * (TN / 2) + 16 * j + c4, 0);
+    else
+      finish_pair<MODE>(a, row, MODE == kQKV ? pos_s[r] : -1, lg, va, vb, n0col + 16 * na + c4,
+                        n0col + 16 * nb + c4);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large batches: 128 x 192 block tiles whose operand chunks are staged in LDS
+// and shared by the block's four waves.  Each wave owns a 64 x 96 sub-tile
+// over the whole K, so there are no partial tiles to exchange; the epilogue
+// runs from its registers (finish_pair).  A chunk (32 of K) is 16 KB of
+// activation pieces (eight row tiles, two planes) and 12 KB of weight
+// fragments, copied global -> registers -> LDS by all 256 threads (seven
+// 16-byte entries each, consecutive threads on consecutive entries), two
+// chunks ahead of the MFMAs; one barrier per chunk.  Two blocks fit a
+// compute unit.  SwiGLU: wave column wn takes gate tiles 3 wn .. 3 wn + 2 and
+// the matching up tiles, so its gate and up values meet in its registers.
+constexpr int kLW = 4;            // waves of a staged block
+constexpr int kLT = kLW * kWave;  // 256 threads
+
+// FM x FN fragments per wave, waves 2 x 2 (launched with 4 x 6).
+template <int MODE, bool NORM, int FM, int FN>
+__global__ __launch_bounds__(kLT, 2) void bgemm_lds_kernel(const GemvArgs a) {
+  constexpr int BM = 2 * FM, BN = 2 * FN;
+  constexpr int TM = 16 * BM, TN = 16 * BN;
+  constexpr int AE = BM * kPieces * kWave;  // activation entries of a chunk
+  constexpr int SE = AE + BN * kWave;       // + weight entries
+  constexpr int PT = SE / kLT, PA = AE / kLT;
+  static_assert(SE % kLT == 0 && AE % kLT == 0, "stage entries per thread");
+  __shared__ u32x4 stg[2][SE];
+  __shared__ float rinv_s[TM];
+  __shared__ int rows_s[TM];
+  __shared__ int pos_s[TM];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int li = lane & 15, lg = lane >> 4;
+  int bx = blockIdx.x, by = blockIdx.y;
+  block_tile(&bx, &by);
+  const int m0 = by * TM;
+  if (tid < TM) {
+    const bool in = m0 + tid < a.M;
+    rows_s[tid] = in ? m0 + tid : -1;
+    pos_s[tid] = (MODE == kQKV && in) ? a.pos[m0 + tid] : -1;
+  }
+
+  // ---- the thread's stage entries: PA of activations, then weights.
+  // Sources as a wave-uniform byte base (scalar registers) plus the lane's
+  // 32-bit offset: entry i of thread t is activation entry t + 256 i, or
+  // lane t % 64 of weight tile j = wave + 4 (i - PA) of the block. ----
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const char* abase = reinterpret_cast<const char*>(a.planes) + static_cast<size_t>(by) * BM * kPieces * 1024;
+  const char* bbase[PT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = va[i] / (1.0f + expf(-va[i])) * vb[i];
-      const int col = bx * (TN / 2) + 16 * j + c4;  // column of the activations
-      if (a.out_planes != nullptr) {
-        if (split_store4(a.out_planes, a.out_ptiles, row, col, y)) flag_overflow(a.ovf, a.pos, row);
-      } else {
-        *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + col) = floatx4{y[0], y[1], y[2], y[3]};
-      }
-      continue;
-    }
-    const int oa = n0col + 16 * na + c4, ob = n0col + 16 * nb + c4;
-    if (MODE == kAdd) {
-      float* ya = a.Y + static_cast<size_t>(row) * a.ldy + oa;
-      float* yb = a.Y + static_cast<size_t>(row) * a.ldy + ob;
-      const floatx4 pa = *reinterpret_cast<const floatx4*>(ya), pb = *reinterpret_cast<const floatx4*>(yb);
-      float xa[4], xb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[i] = pa[i] + va[i];
-        xb[i] = pb[i] + vb[i];
-      }
-      *reinterpret_cast<floatx4*>(ya) = floatx4{xa[0], xa[1], xa[2], xa[3]};
-      *reinterpret_cast<floatx4*>(yb) = floatx4{xb[0], xb[1], xb[2], xb[3]};
-      if (a.out_planes != nullptr) {
-        // the next normed projection's input: x * g split, and the row's
-        // sum of squares over these 32 columns (four lanes of the row)
-        float ga[4] = {1.0f, 1.0f, 1.0f, 1.0f}, gb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (a.out_g != nullptr) {
-          const floatx4 g0 = *reinterpret_cast<const floatx4*>(a.out_g + oa);
-          const floatx4 g1 = *reinterpret_cast<const floatx4*>(a.out_g + ob);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ga[i] = g0[i], gb[i] = g1[i];
-        }
-        float ya4[4], yb4[4], ssr = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ssr = fmaf(xa[i], xa[i], ssr);
-          ya4[i] = xa[i] * ga[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ssr = fmaf(xb[i], xb[i], ssr);
-          yb4[i] = xb[i] * gb[i];
-        }
-        bool bad2 = split_store4(a.out_planes, a.out_ptiles, row, oa, ya4);
-        bad2 |= split_store4(a.out_planes, a.out_ptiles, row, ob, yb4);
-        if (bad2) flag_overflow(a.ovf, a.pos, row);
-        ssr += __shfl_xor(ssr, 16);
-        ssr += __shfl_xor(ssr, 32);
-        if (lg == 0) a.out_ssp[static_cast<size_t>(row) * (a.N / 32) + oa / 32] = ssr;
-      }
-      continue;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int o = h ? ob : oa;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = h ? vb[i] : va[i];
-      if (MODE == kHead) {
-        // rows of draft offset k = row % xdiv add head . b_k
-        const int ko = row % a.xdiv;
-        if (a.hb != nullptr && ko >= 1 && ko <= a.hbK) {
-          const floatx4 bias = *reinterpret_cast<const floatx4*>(
-              a.hb + (static_cast<size_t>(blockIdx.z) * a.hbK + (ko - 1)) * a.N + o);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] += bias[i];
-        }
-        *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + o) = floatx4{v[0], v[1], v[2], v[3]};
-      } else if (MODE == kQKV) {
-        if (o < a.qdim) {
-          *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + o) = floatx4{v[0], v[1], v[2], v[3]};
-        } else {
-          const int pp = pos_s[r];
-          if (pp >= 0 && pp < a.kv_positions) {
-            const int b = row / a.rows_per_stream;
-            float* base = a.kv + static_cast<size_t>(b) * a.kv_sb + static_cast<size_t>(pp) * a.kvdim;
-            const int oo = o - a.qdim;
-            float* dst = oo < a.kvdim ? base + oo : base + a.kv_vo + (oo - a.kvdim);
-            *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
-          }
-        }
-      }
+  for (int i = 0; i < PT; ++i) {
+    bbase[i] = nullptr;
+    if (i >= PA) {
+      const int j = wave_u + kLW * (i - PA);
+      const bool up = MODE == kSwiGLU && j >= BN / 2;
+      const int t = MODE == kSwiGLU ? bx * (BN / 2) + (up ? j - BN / 2 : j) : bx * BN + j;
+      bbase[i] = reinterpret_cast<const char*>((up ? a.W1 : a.W0)) + frag_at(t, 0, a.wtiles) * 2;
     }
   }
+  const uint32_t avo = static_cast<uint32_t>(tid) * 16, bvo = static_cast<uint32_t>(lane) * 16;
+  const size_t astep = static_cast<size_t>(a.ptiles) * kPieces * 1024;  // bytes per chunk
+  const size_t wstep = static_cast<size_t>(a.wtiles) * 1024;
+  struct Pre {
+    u32x4 v[PT];
+  };
+  auto load = [&](int c) __attribute__((always_inline)) {
+    Pre q;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const char* src = i < PA ? abase + static_cast<size_t>(c) * astep + i * kLT * 16 + avo
+                               : bbase[i] + static_cast<size_t>(c) * wstep + bvo;
+      q.v[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+    return q;
+  };
+  auto store = [&](int sidx, const Pre& q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) stg[sidx][tid + i * kLT] = q.v[i];
+  };
+  // the wave's B tiles in the stage
+  int bt[FN];
+#pragma unroll
+  for (int n = 0; n < FN; ++n)
+    bt[n] = MODE == kSwiGLU ? (n < FN / 2 ? wn * (FN / 2) + n : BN / 2 + wn * (FN / 2) + n - FN / 2) : wn * FN + n;
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int n = 0; n < FN; ++n) acc[f][n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  // the wave's fragments of a chunk, all read before its MFMAs
+  struct Frags {
+    u32x4 w[FN];
+    u32x4 x[FM][kPieces];
+  };
+  auto frags = [&](int sidx) __attribute__((always_inline)) {
+    Frags g;
+#pragma unroll
+    for (int n = 0; n < FN; ++n) g.w[n] = stg[sidx][AE + bt[n] * kWave + lane];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) g.x[f][p] = stg[sidx][((wm * FM + f) * kPieces + p) * kWave + lane];
+    return g;
+  };
+  auto mma = [&](const Frags& g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p)
+#pragma unroll
+        for (int n = 0; n < FN; ++n)
+          acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, g.w[n]),
+                                                             __builtin_bit_cast(h8, g.x[f][p]), acc[f][n], 0, 0, 0);
+  };
+
+  // ---- prologue: chunks 0 and 1 in flight, the rows' RMSNorm scales ----
+  const int nc = a.K / 32;
+  Pre P0 = load(0);
+  Pre P1 = load(min(1, nc - 1));
+  if constexpr (NORM) {
+    // TPR threads per row, each summing its share of the row's per-chunk
+    // sums of squares in order, then folded by a butterfly
+    constexpr int TPR = kLT / TM;
+    const int r = tid / TPR, per = nc / TPR;
+    const int row = m0 + r < a.M ? m0 + r : 0;
+    const float* sp = a.ssp + static_cast<size_t>(row) * nc + (tid % TPR) * per;
+    float t = 0.0f;
+    for (int i = 0; i < per; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sp + i);
+      t += v.x;
+      t += v.y;
+      t += v.z;
+      t += v.w;
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) t += __shfl_xor(t, o);
+    if (tid % TPR == 0) rinv_s[r] = 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
+  }
+  store(0, P0);
+  if (nc > 2) P0 = load(2);
+  __syncthreads();
+  // chunk c: the wave's fragments out of stage c % 2; chunk c + 1 (register
+  // buffer (c + 1) % 2) into the other stage, read by no wave since the last
+  // barrier, and that buffer reloaded with chunk c + 3; then the MFMAs and
+  // one barrier
+  auto step = [&](int c, int sidx, Pre& nxt) __attribute__((always_inline)) {
+    const Frags g = frags(sidx);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < nc) {
+      store(sidx ^ 1, nxt);
+      if (c + 3 < nc) nxt = load(c + 3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(g);
+    __syncthreads();
+  };
+  for (int c = 0; c < nc; c += 2) {
+    step(c, 0, P1);
+    if (c + 1 < nc) step(c + 1, 1, P0);
+  }
+
+  // ---- epilogue from registers: pairs (f, na) and (f, nb) as in
+  // bgemm_kernel ----
+  const int c4 = 4 * lg;
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int j = 0; j < FN / 2; ++j) {
+      const int na = MODE == kSwiGLU ? j : 2 * j, nb = MODE == kSwiGLU ? j + FN / 2 : 2 * j + 1;
+      const int r = 16 * (wm * FM + f) + li;
+      const int row = rows_s[r];
+      const float rs = NORM ? rinv_s[r] : 1.0f;
+      const float wa = a.wscale0, wbs = MODE == kSwiGLU ? a.wscale1 : a.wscale0;  // 2^-S, exact
+      float va[4], vb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        va[i] = acc[f][na][i] * wa * rs;
+        vb[i] = acc[f][nb][i] * wbs * rs;
+      }
+      if (row < 0) continue;
+      if (MODE == kSwiGLU)
+        finish_pair<MODE>(a, row, -1, lg, va, vb, bx * (TN / 2) + 16 * (wn * (FN / 2) + j) + c4, 0);
+      else
+        finish_pair<MODE>(a, row, MODE == kQKV ? pos_s[r] : -1, lg, va, vb, bx * TN + 16 * (wn * FN + na) + c4,
+                          bx * TN + 16 * (wn * FN + nb) + c4);
+    }
 }
 
 template <int FM, int FN, bool NORM>
@@ -672,6 +870,44 @@ hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a,
   if (fm == 2 && fn == 4) return launch_f<2, 4>(mode, a, grid, s);
   if (fm == 4 && fn == 4) return launch_f<4, 4>(mode, a, grid, s);
   if (fm == 4 && fn == 6) return launch_f<4, 6>(mode, a, grid, s);
+  return hipErrorInvalidValue;
+}
+
+// The staged tile for a shape, as 10 fm + fn, or 0: 128 x 192 (wave tiles
+// of 4 x 6 fragments) where it gives every compute unit a block.  (Measured
+// at wide-256: 128 x 128 tiles on half the compute units, and 64 x 128 tiles
+// for the O and down projections, ran slower than bgemm_kernel.)
+int bgemm_lds_tile(int mode, int N, int K, int M, int ptiles) {
+  if (mode != kSwiGLU && mode != kQKV && mode != kAdd) return 0;
+  if (M < kLdsMinRows || K % 512 || ptiles * 16 < M) return 0;
+  const int cols = mode == kSwiGLU ? 2 * N : N;
+  static const int kTiles[1][2] = {{4, 6}};
+  for (const auto& t : kTiles) {
+    const int bm = 2 * t[0], tn = 32 * t[1];
+    if (ptiles % bm || cols % tn || (mode == kSwiGLU && N % (tn / 2))) continue;
+    if (cols / tn * (ptiles / bm) >= kLdsMinBlocks) return 10 * t[0] + t[1];
+  }
+  return 0;
+}
+
+hipError_t launch_bgemm_lds(int mode, bool norm, const GemvArgs& a, hipStream_t s) {
+  const int tile = a.planes == nullptr ? 0 : bgemm_lds_tile(mode, a.N, a.K, a.M, a.ptiles);
+  if (tile == 0) return hipErrorInvalidValue;
+  const int fm = tile / 10, fn = tile % 10;
+  const int cols = mode == kSwiGLU ? 2 * a.N : a.N;
+  const dim3 grid(cols / (32 * fn), a.ptiles / (2 * fm));
+#define CPS_LDS_CASE(MODE_, FM_, FN_)                                                                   \
+  if (mode == MODE_ && fm == FM_ && fn == FN_) {                                                       \
+    if (norm) hipLaunchKernelGGL((bgemm_lds_kernel<MODE_, true, FM_, FN_>), grid, dim3(kLT), 0, s, a);   \
+    else hipLaunchKernelGGL((bgemm_lds_kernel<MODE_, false, FM_, FN_>), grid, dim3(kLT), 0, s, a);       \
+    return hipGetLastError();                                                                          \
+  }
+#define CPS_LDS_MODE(MODE_) CPS_LDS_CASE(MODE_, 4, 6)
+  CPS_LDS_MODE(kSwiGLU)
+  CPS_LDS_MODE(kQKV)
+  CPS_LDS_MODE(kAdd)
+#undef CPS_LDS_MODE
+#undef CPS_LDS_CASE
   return hipErrorInvalidValue;
 }
 

@@ -380,6 +380,10 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
       a.ssp = ssp;
     }
     a.wtiles = a.N / 16;  // per packed matrix (SwiGLU: gate and up each)
+    if (bgemm_lds_tile(mode, a.N, a.K, a.M, a.ptiles) != 0) {
+      CPS_HIP(launch_bgemm_lds(mode, a.norm_g != nullptr, a, s));
+      return CP_SPEC_OK;
+    }
     CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, fn, a, dim3(cols / (16 * fn), (a.M + 16 * fm - 1) / (16 * fm)), s));
     return CP_SPEC_OK;
   }

@@ -233,6 +233,14 @@ hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 g
 // (fm, fn) in {(2, 2), (2, 4), (4, 4), (4, 6)}, K a multiple of 512; grid
 // (columns / tile, rows / tile) or, lm_heads, (V / tile, row tiles, heads).
 hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s);
+// Large batches (kLdsMinRows rows or more): 128 x 192 block tiles staged in
+// LDS, four waves of 64 x 96 over the whole K; bgemm_lds_tile gives the
+// tile (10 fm + fn) or 0 when the shape does not yield kLdsMinBlocks blocks
+// of it.  Pre-split rows only (a.planes); kSwiGLU, kQKV and kAdd.
+constexpr int kLdsMinRows = 512;
+constexpr int kLdsMinBlocks = 256;
+int bgemm_lds_tile(int mode, int N, int K, int M, int ptiles);
+hipError_t launch_bgemm_lds(int mode, bool norm, const GemvArgs& a, hipStream_t s);
 // One bf16 matrix [N][K] row-major, times 2^S, as fp16 in MFMA fragment
 // order (N % 16 == 0, K % 32 == 0), at tiles t0 .. t0 + N/16 - 1 of a
 // chunk-major packed matrix with NT tiles per chunk: fragment (tile t, K

@@ -407,8 +407,13 @@ def main():
         print(json.dumps({"copy_mib": args.copy_mb, "launches": 8}), flush=True)
         return
 
+    # one stream: the next round's drafts formed in this round's verify tail
+    # (RVQ section 2.2, Figure 3; 2-3 % faster there), separate draft
+    # launches for batched streams (faster there)
+    import synth
+    fd = 1 if synth.config(args.workload)["streams"] == 1 else 0
     main_res, c = run_workload(args.workload, args.steps, args.warmup,
-                               frames=args.frames, kernels=True)
+                               frames=args.frames, kernels=True, fused_draft=fd)
     line = {
         "metric": METRIC,
         "value": main_res["codes_per_s"],
@@ -430,6 +435,7 @@ def main():
                         f"top-k {c['top_k']}",
             "weights": c["dtype"], "streams": c["streams"],
             "frames": c["frames"], "verify_size": c["verify_size"],
+            "fused_draft": fd,
         },
         "accepted_codes_per_verify_pass": main_res["codes_per_verify_pass"],
         "codes_per_decoder_pass": main_res["codes_per_decoder_pass"],
@@ -471,7 +477,7 @@ def main():
         for wl, steps in ((args.workload, args.steps), ("qwen3tts-64", 1)):
             ref = main_res if wl == args.workload else q64
             o, co = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
-                                 offsets=(3, 0.1))
+                                 offsets=(3, 0.1), fused_draft=fd if wl == args.workload else 0)
             line["draft_offsets"][wl] = {
                 "K": co["draft_offsets"], "scale": co["offset_scale"],
                 "codes_per_s": o["codes_per_s"], "ms_per_step": o["ms_per_step"],
@@ -484,13 +490,15 @@ def main():
         # the next round's drafts formed in this round's verify tail (one
         # heads launch and one softmax launch per round instead of two each)
         line["fused_draft"] = {}
-        for wl, steps, ref, off in ((args.workload, args.steps, main_res, None),
-                                    ("qwen3tts-64", 1, q64, None),
-                                    (args.workload, args.steps, None, (3, 0.1))):
-            fr, cf = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
-                                  offsets=off, fused_draft=1)
+        for wl, steps, fused, ref, off in ((args.workload, args.steps, main_res if fd else None,
+                                            None if fd else main_res, None),
+                                           ("qwen3tts-64", 1, None, q64, None),
+                                           (args.workload, args.steps, None, None, (3, 0.1))):
+            fr = fused or run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
+                                       offsets=off, fused_draft=1)[0]
             if ref is None:
-                ref = run_workload(wl, steps, 1, frames=args.frames, offsets=off)[0]
+                ref = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
+                                   offsets=off)[0]
             key = wl + (f" K={off[0]}" if off else "")
             line["fused_draft"][key] = {
                 "codes_per_s": fr["codes_per_s"], "ms_per_step": fr["ms_per_step"],

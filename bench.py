@@ -89,8 +89,9 @@ def measured_traffic(workload, kind, matrix_cores=False):
 def roofline(table, weight_dtype, workload=None):
     """Roofline object of the kernel with the largest share of a round:
     HBM-bound for the GEMV path, MFMA-bound (dense peak of the weights'
-    dtype; the bf16 path issues three MFMAs per product, counted once here)
-    when the launch ran on matrix-core tiles."""
+    dtype; the bf16 path issues two fp16 MFMAs per product, one per
+    activation piece, counted once here) when the launch ran on matrix-core
+    tiles."""
     kind = max(table, key=lambda k: table[k]["us_per_round"])
     t = table[kind]
     traffic = measured_traffic(workload, kind, t.get("matrix_cores")) if workload else None

@@ -33,10 +33,11 @@ hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 g
 // Phase 1 loads (float4) K of positions 0..max row position, rotated by RoPE
 // on the way into LDS, V, and the rotated queries of the group's (row, query
 // head) pairs; a thread takes its items two at a time, both items' loads
-// before either's stores, so one memory round trip covers them.  Phase 2: thread (pair, p)
-// of a 32-lane group computes one score; the group's max and sum give the
-// softmax weights (positions above the row's own are masked).  Phase 3: each
-// thread produces four consecutive output dimensions of one pair.
+// before either's stores, so one memory round trip covers them.  Phase 2: a
+// 16-lane DPP row per pair, lane l scoring positions l and l + 16; the row's
+// max and sum (DPP rotations) give the softmax weights (positions above the
+// row's own are masked).  Phase 3: each thread produces four consecutive
+// output dimensions of one pair.
 template <int D>
 __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   extern __shared__ float smem[];
@@ -120,62 +121,75 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 2: scores and softmax, 32 lanes per pair ----
-  for (int base = 0; base < npair * 32; base += kBlock) {
-    const int idx = base + threadIdx.x;
-    const int pr = idx >> 5, p = idx & 31;
-    const bool live_pair = pr < npair;
-    const int pp = live_pair ? pos_s[pr / group] : -1;
-    float s = -INFINITY;
-    if (live_pair && p <= pp) {
-      const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
-      const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
-      float acc = 0.0f;
+  // ---- phase 2: scores and softmax.  A 16-lane row per pair (pairs in
+  // groups of 16 per block); lane l scores positions l and l + 16, the
+  // row's max and sum fold by DPP rotations (no LDS permutes) ----
+  {
+    const int l16 = threadIdx.x & 15, prow = threadIdx.x >> 4;
+    for (int pr0 = 0; pr0 < npair; pr0 += kBlock / 16) {
+      const int pr = pr0 + prow;
+      const bool live_pair = pr < npair;
+      const int pp = live_pair ? pos_s[pr / group] : -1;
+      float sc[2];
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) {
-        const float4 x = q4[i], y = k4[i];
-        acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+      for (int h = 0; h < 2; ++h) {
+        const int p = l16 + 16 * h;
+        sc[h] = -INFINITY;
+        if (p <= pp) {
+          const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
+          const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
+          float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int i = 0; i < D / 4; ++i) {
+            const float4 x = q4[i], y = k4[i];
+            acc[0] = fmaf(x.x, y.x, acc[0]);
+            acc[1] = fmaf(x.y, y.y, acc[1]);
+            acc[2] = fmaf(x.z, y.z, acc[2]);
+            acc[3] = fmaf(x.w, y.w, acc[3]);
+          }
+          sc[h] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale;
+        }
       }
-      s = acc * a.scale;
+      float mx = fmaxf(sc[0], sc[1]);
+      mx = fmaxf(mx, dpp_f<kRor8>(mx));
+      mx = fmaxf(mx, dpp_f<kRor4>(mx));
+      mx = fmaxf(mx, dpp_f<kRor2>(mx));
+      mx = fmaxf(mx, dpp_f<kRor1>(mx));
+      const float e0 = l16 <= pp ? expf(sc[0] - mx) : 0.0f;
+      const float e1 = l16 + 16 <= pp ? expf(sc[1] - mx) : 0.0f;
+      float sum = e0 + e1;
+      sum += dpp_f<kRor8>(sum);
+      sum += dpp_f<kRor4>(sum);
+      sum += dpp_f<kRor2>(sum);
+      sum += dpp_f<kRor1>(sum);
+      if (live_pair && pp >= 0) {
+        S[pr * 32 + l16] = e0 / sum;  // zero past the row's own position
+        S[pr * 32 + l16 + 16] = e1 / sum;
+      }
     }
-    // max and sum over the 32 lanes of the pair (xor within 32)
-    float mx = s;
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-    const float e = (live_pair && p <= pp) ? expf(s - mx) : 0.0f;
-    float sum = e;
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
-    if (live_pair) S[pr * 32 + p] = (p <= pp) ? e / sum : 0.0f;
   }
   __syncthreads();
 
-  // ---- phase 3: eight output dimensions of one pair per thread (fp32
+  // ---- phase 3: four output dimensions of one pair per thread (fp32
   // rows, or their split pieces for the O projection) ----
-  constexpr int D8 = D / 8;
-  for (int idx = threadIdx.x; idx < npair * D8; idx += kBlock) {
-    const int pr = idx / D8, i8 = (idx % D8) * 8;
+  constexpr int D4 = D / 4;
+  for (int idx = threadIdx.x; idx < npair * D4; idx += kBlock) {
+    const int pr = idx / D4, i4 = (idx % D4) * 4;
     const int r = pr / group, j = pr % group;
     const int pp = pos_s[r];
     if (pp < 0) continue;
     const float* srow = S + pr * 32;
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int p = 0; p <= pp; ++p) {
       const float w = srow[p];
-      const float4 v0 = *reinterpret_cast<const float4*>(Vs + p * D + i8);
-      const float4 v1 = *reinterpret_cast<const float4*>(Vs + p * D + i8 + 4);
-      o[0] += w * v0.x; o[1] += w * v0.y; o[2] += w * v0.z; o[3] += w * v0.w;
-      o[4] += w * v1.x; o[5] += w * v1.y; o[6] += w * v1.z; o[7] += w * v1.w;
+      const float4 v = *reinterpret_cast<const float4*>(Vs + p * D + i4);
+      o[0] += w * v.x; o[1] += w * v.y; o[2] += w * v.z; o[3] += w * v.w;
     }
-    const int row = b * R + r, k = (g * group + j) * D + i8;
+    const int row = b * R + r, k = (g * group + j) * D + i4;
     if (a.planes != nullptr) {
-      if (split_store8(a.planes, a.ptiles, row, k, o)) flag_overflow(a.ovf, nullptr, row);  // active rows only
+      if (split_store4(a.planes, a.ptiles, row, k, o)) flag_overflow(a.ovf, nullptr, row);  // active rows only
     } else {
-      float* dst = a.out + static_cast<size_t>(row) * qdim + k;
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      *reinterpret_cast<float4*>(a.out + static_cast<size_t>(row) * qdim + k) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
 }

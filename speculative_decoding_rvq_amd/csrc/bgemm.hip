@@ -852,12 +852,17 @@ __global__ __launch_bounds__(kBlock) void pack_frag_kernel(const uint16_t* W, in
 // *out = max |W| over n bf16 values, as float bits (non-negative floats
 // order like their bit patterns).
 __global__ __launch_bounds__(kBlock) void absmax_bf16_kernel(const uint16_t* W, size_t n, uint32_t* out) {
+  __shared__ float red[kBlock / kWave];
   float m = 0.0f;
   for (size_t i = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * kBlock)
     m = fmaxf(m, fabsf(bf16_to_f32(W[i])));
   m = wave_max(m);
-  if (threadIdx.x % kWave == 0) atomicMax(out, __float_as_uint(m));
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  // one atomic per block (a word that every wave hit serialised them)
+  if (threadIdx.x == 0)
+    atomicMax(out, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 }  // namespace
@@ -931,7 +936,7 @@ hipError_t pack_fragments(const uint16_t* W, int N, int K, uint16_t* P, int NT, 
 
 hipError_t launch_absmax_bf16(const uint16_t* W, size_t n, uint32_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const size_t blocks = std::min<size_t>((n + kBlock - 1) / kBlock, 4096);
+  const size_t blocks = std::min<size_t>((n + kBlock - 1) / kBlock, 1024);
   hipLaunchKernelGGL(absmax_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, W, n, out);
   return hipGetLastError();
 }

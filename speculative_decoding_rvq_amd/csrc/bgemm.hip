@@ -873,6 +873,7 @@ hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a,
   if (wdtype != CP_SPEC_BF16) return hipErrorInvalidValue;
   if (fm == 2 && fn == 2) return launch_f<2, 2>(mode, a, grid, s);
   if (fm == 2 && fn == 4) return launch_f<2, 4>(mode, a, grid, s);
+  if (fm == 2 && fn == 8) return launch_f<2, 8>(mode, a, grid, s);
   if (fm == 4 && fn == 4) return launch_f<4, 4>(mode, a, grid, s);
   if (fm == 4 && fn == 6) return launch_f<4, 6>(mode, a, grid, s);
   return hipErrorInvalidValue;

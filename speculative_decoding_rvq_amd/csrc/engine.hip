@@ -570,10 +570,16 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
   a.wscale0 = a.wscale1 = h->hscale;
   a.ovf = h->at<int>(h->lo.ovf);
   if (per_head > 0 && h->packed_heads != nullptr && a.N % 64 == 0 && a.K % 512 == 0) {
-    // bf16, packed heads: 32 x 64 tiles per head
+    // bf16, packed heads: 32 x 128 tiles per head where, at the average
+    // rows per head, they still give every compute unit a block (each column
+    // tile re-reads and splits its rows' fp32 activations: wide tiles halve
+    // that), else 32 x 64
     a.W0 = h->packed_heads;
     a.wtiles = a.n_heads * (a.N / 16);
-    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, 4, a, dim3(a.N / 64, (per_head + 31) / 32, a.n_heads), s));
+    const int slices = (per_head + 31) / 32;
+    const int avg = (M + a.n_heads - 1) / a.n_heads;
+    const int fn = a.N % 128 == 0 && a.N / 128 * ((avg + 31) / 32) * a.n_heads >= kFillBlocks ? 8 : 4;
+    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, fn, a, dim3(a.N / (16 * fn), slices, a.n_heads), s));
     return CP_SPEC_OK;
   }
   if (per_head > 0 && mfma_fits(kHead, a)) {

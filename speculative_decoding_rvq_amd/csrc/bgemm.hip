@@ -48,8 +48,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef f16x8_t h8;
 
-constexpr int kGW = 8;               // waves of a block: K eighths
-constexpr int kGT = kGW * kWave;     // 512 threads
 
 // Packed layouts are chunk-major: fragment (tile t, K chunk c) of a matrix
 // packed with NT tiles per chunk is the 1 KB at (c * NT + t) * 512 bf16, so
@@ -187,14 +185,19 @@ __device__ __forceinline__ void finish_pair(const GemvArgs& a, int row, int pp, 
   }
 }
 
-template <int MODE, int FM, int FN, bool NORM, bool PL>
-__global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
+// NW waves, each taking 1/NW of K: eight while the grid has fewer blocks
+// than compute units (more loads in flight per block), four from a block per
+// compute unit on (the partial tiles then meet in one exchange, not two).
+template <int MODE, int FM, int FN, bool NORM, bool PL, int NW>
+__global__ __launch_bounds__(NW * kWave) void bgemm_kernel(const GemvArgs a) {
+  static_assert(NW == 4 || NW == 8, "waves of a K-split block");
+  constexpr int kGT = NW * kWave;
   constexpr int TM = 16 * FM, TN = 16 * FN;
-  constexpr int SW = PL ? 1 : kGW;  // stage: only the in-kernel split uses it
+  constexpr int SW = PL ? 1 : NW;  // stage: only the in-kernel split uses it
   struct StageT { u32x4 f[SW][FM * kPieces][kWave]; };  // split fragments of one chunk
   // partial tiles in fragment order (lane l's four values of fragment
   // (f, n) as one 16-byte entry), four slots
-  struct PartT { floatx4 v[4][FM * FN][kWave]; float ssq[kGW][TM]; };
+  struct PartT { floatx4 v[4][FM * FN][kWave]; float ssq[NW][TM]; };
   __shared__ union {
     StageT stage;
     PartT part;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   int count;
   if (MODE == kHead) {
     const int j = blockIdx.z;  // head j+1: its rows, ascending, slice blockIdx.y
-    __shared__ int red_h[kGW];
+    __shared__ int red_h[NW];
     count = head_rows_slice<kGT>(a.head, a.M, j + 1, by * TM, TM, rows_s, red_h);
     if (count <= 0) return;
     tile0 = j * (a.N / 16);
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
 // 16 f + l / 4, k 8 (l % 4) .. +7 of each chunk (a quad covers one 128-byte
 // row segment) and so holds exactly fragment entry (l / 4) + 16 (l % 4).  A
 // missing row reads X row 0: its outputs and sum of squares are never used.
-  const int cw = a.K / 32 / kGW;  // chunks of this wave
+  const int cw = a.K / 32 / NW;  // chunks of this wave (even, >= 2)
   const int c0 = wave * cw;
   // Grids of at most one block per compute unit (every operand stays in the
   // L2 of its XCD): blocks start their K walk at different chunks, so that
@@ -301,30 +304,33 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
             acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, fb.w[n]),
                                                                __builtin_bit_cast(h8, fa.x[f][p]), acc[f][n], 0, 0, 0);
     };
-    // two chunks of loads in flight (an even chunk count per wave; the
-    // fetches past the end re-read the last chunk and are not used)
-    // (issued in the loop's order: the wait counts at the loop head then
-    // cover only the chunk being consumed)
+    // two chunks of loads in flight, issued in the loop's order (the wait
+    // counts before each chunk's MFMAs then cover only that chunk); the
+    // last two chunks' MFMAs follow the loop, with nothing more to fetch
+    // (deeper prefetch, four chunks, measured no faster)
     PFrag pa0 = fetch_p(0);
     BFrag pb0 = fetch_b(0);
     __builtin_amdgcn_sched_barrier(0);
     PFrag pa1 = fetch_p(1);
     BFrag pb1 = fetch_b(1);
     __builtin_amdgcn_sched_barrier(0);
-    for (int c = 0; c < cw; c += 2) {
+    for (int c = 0; c + 2 < cw; c += 2) {
       mma_p(pa0, pb0);
       __builtin_amdgcn_sched_barrier(0);
-      pa0 = fetch_p(min(c + 2, cw - 1));
+      pa0 = fetch_p(c + 2);
       __builtin_amdgcn_sched_barrier(0);
-      pb0 = fetch_b(min(c + 2, cw - 1));
+      pb0 = fetch_b(c + 2);
       __builtin_amdgcn_sched_barrier(0);
       mma_p(pa1, pb1);
       __builtin_amdgcn_sched_barrier(0);
-      pa1 = fetch_p(min(c + 3, cw - 1));
+      pa1 = fetch_p(c + 3);
       __builtin_amdgcn_sched_barrier(0);
-      pb1 = fetch_b(min(c + 3, cw - 1));
+      pb1 = fetch_b(c + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mma_p(pa0, pb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_p(pa1, pb1);
   } else {
   struct AFrag {  // one chunk of this lane's activation loads
     floatx4 x[FM][2];
@@ -390,11 +396,10 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   };
 
   // ---- K loop (an even number of chunks per wave), two chunks of loads in
-// flight per operand: a chunk's
-// activation registers are refilled as soon as they are split, its weight
-// registers once its MFMAs are issued (the fetches past the end re-read the
-// last chunk and are not used) ----
-  // (issued in the loop's order, see above)
+  // flight per operand: a chunk's activation registers are refilled as soon
+  // as they are split, its weight registers once its MFMAs are issued; the
+  // last two chunks follow the loop (issued in the loop's order, see
+  // above) ----
   AFrag fa0 = fetch_a(0);
   __builtin_amdgcn_sched_barrier(0);
   BFrag fb0 = fetch_b(0);
@@ -403,28 +408,36 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   BFrag fb1 = fetch_b(1);
   __builtin_amdgcn_sched_barrier(0);
-  for (int c = 0; c < cw; c += 2) {
+  for (int c = 0; c + 2 < cw; c += 2) {
     wave_lds_sync();  // the previous chunk's fragment reads are done
     split_store(fa0);
     __builtin_amdgcn_sched_barrier(0);
-    fa0 = fetch_a(min(c + 2, cw - 1));
+    fa0 = fetch_a(c + 2);
     __builtin_amdgcn_sched_barrier(0);
     wave_lds_sync();
     mma(fb0);
     __builtin_amdgcn_sched_barrier(0);
-    fb0 = fetch_b(min(c + 2, cw - 1));
+    fb0 = fetch_b(c + 2);
     __builtin_amdgcn_sched_barrier(0);
     wave_lds_sync();
     split_store(fa1);
     __builtin_amdgcn_sched_barrier(0);
-    fa1 = fetch_a(min(c + 3, cw - 1));
+    fa1 = fetch_a(c + 3);
     __builtin_amdgcn_sched_barrier(0);
     wave_lds_sync();
     mma(fb1);
     __builtin_amdgcn_sched_barrier(0);
-    fb1 = fetch_b(min(c + 3, cw - 1));
+    fb1 = fetch_b(c + 3);
     __builtin_amdgcn_sched_barrier(0);
   }
+  wave_lds_sync();
+  split_store(fa0);
+  wave_lds_sync();
+  mma(fb0);
+  wave_lds_sync();
+  split_store(fa1);
+  wave_lds_sync();
+  mma(fb1);
   if (bad) flag_overflow(a.ovf, nullptr, 0);  // the heads' rows are all in use
 
   }
@@ -448,12 +461,12 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   int pv = -1;  // Q/K/V: the row's position, loaded with them
   if (MODE == kQKV && tid < TM && rows_s[tid] >= 0) pv = a.pos[rows_s[tid]];
 
-  // ---- the eight partial tiles meet in LDS in a fixed order: waves 4-7
-  // hand theirs to waves 0-3 (w + w+4), which store the four sums; one more
-  // barrier and every wave reads the four sums of the fragments it finishes
-  // as (s0 + s1) + (s2 + s3).  Entries are 16 bytes per lane, in lane
-  // order: no bank conflicts.  The rows' partial sums of squares go
-  // along. ----
+  // ---- the partial tiles meet in LDS in a fixed order.  Eight waves:
+  // waves 4-7 hand theirs to waves 0-3 (w + w+4), which store the four
+  // sums; four waves store their own.  One more barrier and every wave reads
+  // the four sums of the fragments it finishes as (s0 + s1) + (s2 + s3).
+  // Entries are 16 bytes per lane, in lane order: no bank conflicts.  The
+  // rows' partial sums of squares go along. ----
   __syncthreads();  // every wave is past its last stage read (stage and part share LDS)
   if (NORM && !PL) {
 #pragma unroll
@@ -464,21 +477,28 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
       if ((lane & 3) == 0) sm.part.ssq[wave][16 * i + (lane >> 2)] = t;
     }
   }
-  if (wave >= 4) {
+  if (NW == 8) {
+    if (wave >= 4) {
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int n = 0; n < FN; ++n) sm.part.v[wave - 4][f * FN + n][lane] = acc[f][n];
+    }
+    __syncthreads();
+    if (wave < 4) {  // slot `wave` is this wave's alone from here on
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int n = 0; n < FN; ++n) {
+          acc[f][n] += sm.part.v[wave][f * FN + n][lane];
+          sm.part.v[wave][f * FN + n][lane] = acc[f][n];
+        }
+    }
+  } else {
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int n = 0; n < FN; ++n) sm.part.v[wave - 4][f * FN + n][lane] = acc[f][n];
-  }
-  __syncthreads();
-  if (wave < 4) {  // slot `wave` is this wave's alone from here on
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int n = 0; n < FN; ++n) {
-        acc[f][n] += sm.part.v[wave][f * FN + n][lane];
-        sm.part.v[wave][f * FN + n][lane] = acc[f][n];
-      }
+      for (int n = 0; n < FN; ++n) sm.part.v[wave][f * FN + n][lane] = acc[f][n];
   }
   if constexpr (PL && NORM) {
     float t = 0.0f;
@@ -496,8 +516,10 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
     if constexpr (PL) {
       return rinv_s[r];
     } else {
-      const float t = ((sm.part.ssq[0][r] + sm.part.ssq[4][r]) + (sm.part.ssq[1][r] + sm.part.ssq[5][r])) +
-                      ((sm.part.ssq[2][r] + sm.part.ssq[6][r]) + (sm.part.ssq[3][r] + sm.part.ssq[7][r]));
+      float t = (sm.part.ssq[0][r] + sm.part.ssq[1][r]) + (sm.part.ssq[2][r] + sm.part.ssq[3][r]);
+      if (NW == 8)
+        t = ((sm.part.ssq[0][r] + sm.part.ssq[4][r]) + (sm.part.ssq[1][r] + sm.part.ssq[5][r])) +
+            ((sm.part.ssq[2][r] + sm.part.ssq[6][r]) + (sm.part.ssq[3][r] + sm.part.ssq[7][r]));
       return 1.0f / sqrtf(t / static_cast<float>(a.K) + a.eps);
     }
   };
@@ -528,7 +550,7 @@ __global__ __launch_bounds__(kGT) void bgemm_kernel(const GemvArgs a) {
   const int n0col = bx * TN;
   constexpr int U = FM * (FN / 2);
   const int c4 = 4 * lg;
-  for (int u = wave; u < U; u += kGW) {
+  for (int u = wave; u < U; u += NW) {
     const int f = u / (FN / 2), j = u % (FN / 2);
     const int na = MODE == kSwiGLU ? j : 2 * j, nb = MODE == kSwiGLU ? j + FN / 2 : 2 * j + 1;
     const int r = 16 * f + li;
@@ -743,27 +765,28 @@ __global__ __launch_bounds__(kLT, 2) void bgemm_lds_kernel(const GemvArgs a) {
     }
 }
 
-template <int FM, int FN, bool NORM>
+template <int FM, int FN, bool NORM, int NW>
 hipError_t launch_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
   const bool pl = a.planes != nullptr;
+  const dim3 block(NW * kWave);
   switch (mode) {
     // projections read pre-split rows; the lm_heads (rows gathered per head)
     // split in the kernel
     case kAdd:
       if (!pl) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, true>), grid, dim3(kGT), 0, s, a);
+      hipLaunchKernelGGL((bgemm_kernel<kAdd, FM, FN, NORM, true, NW>), grid, block, 0, s, a);
       break;
     case kSwiGLU:
       if (!pl) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, true>), grid, dim3(kGT), 0, s, a);
+      hipLaunchKernelGGL((bgemm_kernel<kSwiGLU, FM, FN, NORM, true, NW>), grid, block, 0, s, a);
       break;
     case kQKV:
       if (!pl) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, true>), grid, dim3(kGT), 0, s, a);
+      hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, true, NW>), grid, block, 0, s, a);
       break;
     case kHead:
       if (pl) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false>), grid, dim3(kGT), 0, s, a);
+      hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false, NW>), grid, block, 0, s, a);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -771,9 +794,11 @@ hipError_t launch_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
 }
 
 template <int FM, int FN>
-hipError_t launch_f(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
-  return a.norm_g != nullptr ? launch_t<FM, FN, true>(mode, a, grid, s)
-                             : launch_t<FM, FN, false>(mode, a, grid, s);
+hipError_t launch_f(int mode, int nw, const GemvArgs& a, dim3 grid, hipStream_t s) {
+  const bool norm = a.norm_g != nullptr;
+  if (nw == 4) return norm ? launch_t<FM, FN, true, 4>(mode, a, grid, s) : launch_t<FM, FN, false, 4>(mode, a, grid, s);
+  if (nw == 8) return norm ? launch_t<FM, FN, true, 8>(mode, a, grid, s) : launch_t<FM, FN, false, 8>(mode, a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 // Split pass: rows [0, M) of X (times g when set) into two fp16 planes in
@@ -869,13 +894,14 @@ __global__ __launch_bounds__(kBlock) void absmax_bf16_kernel(const uint16_t* W, 
 
 // bf16 weights only (packed by pack_fragments); fp32 weights keep the fp32
 // kernels of mfma_impl.h.
-hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, const GemvArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, int nw, const GemvArgs& a, dim3 grid, hipStream_t s) {
   if (wdtype != CP_SPEC_BF16) return hipErrorInvalidValue;
-  if (fm == 2 && fn == 2) return launch_f<2, 2>(mode, a, grid, s);
-  if (fm == 2 && fn == 4) return launch_f<2, 4>(mode, a, grid, s);
-  if (fm == 2 && fn == 8) return launch_f<2, 8>(mode, a, grid, s);
-  if (fm == 4 && fn == 4) return launch_f<4, 4>(mode, a, grid, s);
-  if (fm == 4 && fn == 6) return launch_f<4, 6>(mode, a, grid, s);
+  if (a.K % (64 * nw)) return hipErrorInvalidValue;  // an even number of chunks per wave
+  if (fm == 2 && fn == 2) return launch_f<2, 2>(mode, nw, a, grid, s);
+  if (fm == 2 && fn == 4) return launch_f<2, 4>(mode, nw, a, grid, s);
+  if (fm == 2 && fn == 8) return launch_f<2, 8>(mode, nw, a, grid, s);
+  if (fm == 4 && fn == 4) return launch_f<4, 4>(mode, nw, a, grid, s);
+  if (fm == 4 && fn == 6) return launch_f<4, 6>(mode, nw, a, grid, s);
   return hipErrorInvalidValue;
 }
 

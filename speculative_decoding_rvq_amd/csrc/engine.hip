@@ -174,6 +174,10 @@ constexpr int kMfmaMinStreams = 8;
 constexpr int kMfmaMinRows = 32;
 constexpr int kFillBlocks = 256;  // one block per compute unit
 
+// Waves per K-split block for a grid of `blocks` blocks with work: eight
+// below one block per compute unit, four from there on.
+int bgemm_waves(long blocks) { return blocks >= kFillBlocks ? 4 : 8; }
+
 // bf16 weights in MFMA fragment order for the batched path: only when many
 // rows can occur and every matrix tiles (N % 16, K % 128).
 bool packs_weights(const Shape& s) {
@@ -384,7 +388,8 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
       CPS_HIP(launch_bgemm_lds(mode, a.norm_g != nullptr, a, s));
       return CP_SPEC_OK;
     }
-    CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, fn, a, dim3(cols / (16 * fn), (a.M + 16 * fm - 1) / (16 * fm)), s));
+    const dim3 grid(cols / (16 * fn), (a.M + 16 * fm - 1) / (16 * fm));
+    CPS_HIP(launch_bgemm(h->sh.wdt, mode, fm, fn, bgemm_waves(static_cast<long>(grid.x) * grid.y), a, grid, s));
     return CP_SPEC_OK;
   }
   if (!head_mode && a.M >= kMfmaMinRows && mfma_fits(mode, a)) {
@@ -579,7 +584,8 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
     const int slices = (per_head + 31) / 32;
     const int avg = (M + a.n_heads - 1) / a.n_heads;
     const int fn = a.N % 128 == 0 && a.N / 128 * ((avg + 31) / 32) * a.n_heads >= kFillBlocks ? 8 : 4;
-    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, fn, a, dim3(a.N / (16 * fn), slices, a.n_heads), s));
+    const long busy = static_cast<long>(a.N / (16 * fn)) * ((avg + 31) / 32) * a.n_heads;  // blocks with rows
+    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, fn, bgemm_waves(busy), a, dim3(a.N / (16 * fn), slices, a.n_heads), s));
     return CP_SPEC_OK;
   }
   if (per_head > 0 && mfma_fits(kHead, a)) {

@@ -584,8 +584,11 @@ int head_logits(const cp_spec* h, hipStream_t s, int M, const float* X, int xdiv
     const int slices = (per_head + 31) / 32;
     const int avg = (M + a.n_heads - 1) / a.n_heads;
     const int fn = a.N % 128 == 0 && a.N / 128 * ((avg + 31) / 32) * a.n_heads >= kFillBlocks ? 8 : 4;
+    // four waves only for the wide tiles on a full grid (measured: the
+    // 32 x 64 tiles keep eight, whose in-kernel split is latency-bound)
     const long busy = static_cast<long>(a.N / (16 * fn)) * ((avg + 31) / 32) * a.n_heads;  // blocks with rows
-    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, fn, bgemm_waves(busy), a, dim3(a.N / (16 * fn), slices, a.n_heads), s));
+    const int nw = fn == 8 ? bgemm_waves(busy) : 8;
+    CPS_HIP(launch_bgemm(h->sh.wdt, kHead, 2, fn, nw, a, dim3(a.N / (16 * fn), slices, a.n_heads), s));
     return CP_SPEC_OK;
   }
   if (per_head > 0 && mfma_fits(kHead, a)) {

@@ -171,7 +171,10 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   __syncthreads();
 
   // ---- phase 3: four output dimensions of one pair per thread (fp32
-  // rows, or their split pieces for the O projection) ----
+  // rows, or their split pieces for the O projection).  Every row's weights
+  // are zero past its own position, so all threads run the block's np
+  // positions: a uniform trip count, unrolled, its LDS reads in flight
+  // together ----
   constexpr int D4 = D / 4;
   for (int idx = threadIdx.x; idx < npair * D4; idx += kBlock) {
     const int pr = idx / D4, i4 = (idx % D4) * 4;
@@ -180,10 +183,14 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
     if (pp < 0) continue;
     const float* srow = S + pr * 32;
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p = 0; p <= pp; ++p) {
+#pragma unroll 8
+    for (int p = 0; p < np; ++p) {
       const float w = srow[p];
       const float4 v = *reinterpret_cast<const float4*>(Vs + p * D + i4);
-      o[0] += w * v.x; o[1] += w * v.y; o[2] += w * v.z; o[3] += w * v.w;
+      o[0] = fmaf(w, v.x, o[0]);
+      o[1] = fmaf(w, v.y, o[1]);
+      o[2] = fmaf(w, v.z, o[2]);
+      o[3] = fmaf(w, v.w, o[3]);
     }
     const int row = b * R + r, k = (g * group + j) * D + i4;
     if (a.planes != nullptr) {

@@ -99,9 +99,27 @@ __device__ __forceinline__ void block_tile(int* bx, int* by) {
 // ob are the output columns of the two fragments (32 adjacent columns for
 // the residual add).  pp: the row's position (Q/K/V).  Lanes 16 apart hold
 // the same row (the residual add's sums of squares fold over them).
+// The residual add's operands that do not depend on the products: the old
+// values at columns oa / ob and the next projection's gains there.
+struct AddOps {
+  floatx4 ya, yb, ga, gb;
+};
+__device__ __forceinline__ AddOps add_operands(const GemvArgs& a, int row, int oa, int ob) {
+  AddOps o;
+  o.ya = *reinterpret_cast<const floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + oa);
+  o.yb = *reinterpret_cast<const floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + ob);
+  if (a.out_planes != nullptr && a.out_g != nullptr) {
+    o.ga = *reinterpret_cast<const floatx4*>(a.out_g + oa);
+    o.gb = *reinterpret_cast<const floatx4*>(a.out_g + ob);
+  } else {
+    o.ga = o.gb = floatx4{1.0f, 1.0f, 1.0f, 1.0f};
+  }
+  return o;
+}
+// ops: the residual add's operands when loaded earlier (else loaded here).
 template <int MODE>
 __device__ __forceinline__ void finish_pair(const GemvArgs& a, int row, int pp, int lg, const float (&va)[4],
-                                            const float (&vb)[4], int oa, int ob) {
+                                            const float (&vb)[4], int oa, int ob, const AddOps* ops = nullptr) {
   if (MODE == kSwiGLU) {
     float y[4];
 #pragma unroll
@@ -114,37 +132,28 @@ __device__ __forceinline__ void finish_pair(const GemvArgs& a, int row, int pp, 
     return;
   }
   if (MODE == kAdd) {
-    float* ya = a.Y + static_cast<size_t>(row) * a.ldy + oa;
-    float* yb = a.Y + static_cast<size_t>(row) * a.ldy + ob;
-    const floatx4 pa = *reinterpret_cast<const floatx4*>(ya), pb = *reinterpret_cast<const floatx4*>(yb);
+    const AddOps o = ops != nullptr ? *ops : add_operands(a, row, oa, ob);
     float xa[4], xb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xa[i] = pa[i] + va[i];
-      xb[i] = pb[i] + vb[i];
+      xa[i] = o.ya[i] + va[i];
+      xb[i] = o.yb[i] + vb[i];
     }
-    *reinterpret_cast<floatx4*>(ya) = floatx4{xa[0], xa[1], xa[2], xa[3]};
-    *reinterpret_cast<floatx4*>(yb) = floatx4{xb[0], xb[1], xb[2], xb[3]};
+    *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + oa) = floatx4{xa[0], xa[1], xa[2], xa[3]};
+    *reinterpret_cast<floatx4*>(a.Y + static_cast<size_t>(row) * a.ldy + ob) = floatx4{xb[0], xb[1], xb[2], xb[3]};
     if (a.out_planes != nullptr) {
       // the next normed projection's input: x * g split, and the row's sum
       // of squares over these 32 columns (four lanes of the row)
-      float ga[4] = {1.0f, 1.0f, 1.0f, 1.0f}, gb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (a.out_g != nullptr) {
-        const floatx4 g0 = *reinterpret_cast<const floatx4*>(a.out_g + oa);
-        const floatx4 g1 = *reinterpret_cast<const floatx4*>(a.out_g + ob);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ga[i] = g0[i], gb[i] = g1[i];
-      }
       float ya4[4], yb4[4], ssr = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ssr = fmaf(xa[i], xa[i], ssr);
-        ya4[i] = xa[i] * ga[i];
+        ya4[i] = xa[i] * o.ga[i];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ssr = fmaf(xb[i], xb[i], ssr);
-        yb4[i] = xb[i] * gb[i];
+        yb4[i] = xb[i] * o.gb[i];
       }
       bool bad = split_store4(a.out_planes, a.out_ptiles, row, oa, ya4);
       bad |= split_store4(a.out_planes, a.out_ptiles, row, ob, yb4);
@@ -277,6 +286,49 @@ __global__ __launch_bounds__(NW * kWave) void bgemm_kernel(const GemvArgs a) {
   float ss[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) ss[i] = 0.0f;
+
+  // Epilogue operands that do not depend on the products.  Pre-split
+  // RMSNorm rows' sums of squares per 32-wide K chunk (TPR neighbouring
+  // threads read a row's, each a contiguous run) and the Q/K/V rows'
+  // positions are loaded after the K loop; the residual add's old values and
+  // next gains of the pairs this wave finishes go out after the first chunks
+  // and stay in flight during the K loop.
+  constexpr int TPR = kGT / TM;
+  constexpr int kRun = 8;
+  constexpr int U = FM * (FN / 2);          // fragment pairs of the tile
+  constexpr int UPW = (U + NW - 1) / NW;    // ... finished per wave
+  const int np = a.K / 32, per = np / TPR;
+  const int srow = rows_s[tid / TPR];
+  const float* sp = (PL && NORM) ? a.ssp + static_cast<size_t>(srow >= 0 ? srow : 0) * np + (tid % TPR) * per
+                                 : nullptr;
+  float sv[kRun];
+  int pv = -1;
+  // (not for the widest tile at eight waves, whose registers are full)
+  constexpr bool kPreAdd = MODE == kAdd && (NW == 4 || FM * FN <= 16);
+  AddOps pre[kPreAdd ? UPW : 1];
+  const int n0col = bx * TN;
+  const int c4 = 4 * lg;
+  // pair u: fragments (f, na) and (f, nb), na = j and nb = j + FN / 2 for
+  // SwiGLU (a gate tile and its up tile), na = 2 j and nb = 2 j + 1
+  // otherwise (32 adjacent columns)
+  auto pair_of = [&](int u, int& f, int& j, int& na, int& nb) {
+    f = u / (FN / 2);
+    j = u % (FN / 2);
+    na = MODE == kSwiGLU ? j : 2 * j;
+    nb = MODE == kSwiGLU ? j + FN / 2 : 2 * j + 1;
+  };
+  auto epilogue_loads = [&]() __attribute__((always_inline)) {
+    if constexpr (kPreAdd) {
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int u = wave + NW * i;
+        int f, j, na, nb;
+        pair_of(u < U ? u : 0, f, j, na, nb);
+        const int row = rows_s[16 * f + li];
+        if (u < U && row >= 0) pre[i] = add_operands(a, row, n0col + 16 * na + c4, n0col + 16 * nb + c4);
+      }
+    }
+  };
   if constexpr (PL) {
     // activations pre-split: plane p of row tile t, chunk c is the 1 KB
     // fragment at ((c * T + t) * 2 + p) * 512 fp16 (T row tiles)
@@ -313,6 +365,8 @@ __global__ __launch_bounds__(NW * kWave) void bgemm_kernel(const GemvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     PFrag pa1 = fetch_p(1);
     BFrag pb1 = fetch_b(1);
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue_loads();
     __builtin_amdgcn_sched_barrier(0);
     for (int c = 0; c + 2 < cw; c += 2) {
       mma_p(pa0, pb0);
@@ -442,32 +496,23 @@ __global__ __launch_bounds__(NW * kWave) void bgemm_kernel(const GemvArgs a) {
 
   }
 
-  // RMSNorm of pre-split rows: the producer left per-row sums of squares per
-  // 32-wide K chunk.  TPR neighbouring threads read a row's, each a
-  // contiguous run, all loads at once (they stay in flight during the tile
-  // exchange below); each run is summed in order and the TPR sums folded by
-  // a butterfly, the same on every run.
-  constexpr int TPR = kGT / TM;
-  constexpr int kRun = 8;
-  const int np = a.K / 32, per = np / TPR;
-  const int srow = rows_s[tid / TPR];
-  const float* sp = (PL && NORM) ? a.ssp + static_cast<size_t>(srow >= 0 ? srow : 0) * np + (tid % TPR) * per
-                                 : nullptr;
-  float sv[kRun];
-  if constexpr (PL && NORM) {
-#pragma unroll
-    for (int i = 0; i < kRun; ++i) sv[i] = (srow >= 0 && i < per) ? sp[i] : 0.0f;
-  }
-  int pv = -1;  // Q/K/V: the row's position, loaded with them
-  if (MODE == kQKV && tid < TM && rows_s[tid] >= 0) pv = a.pos[rows_s[tid]];
-
   // ---- the partial tiles meet in LDS in a fixed order.  Eight waves:
   // waves 4-7 hand theirs to waves 0-3 (w + w+4), which store the four
   // sums; four waves store their own.  One more barrier and every wave reads
   // the four sums of the fragments it finishes as (s0 + s1) + (s2 + s3).
   // Entries are 16 bytes per lane, in lane order: no bank conflicts.  The
   // rows' partial sums of squares go along. ----
-  __syncthreads();  // every wave is past its last stage read (stage and part share LDS)
+  // every wave past its last stage read (stage and part share LDS; the
+  // pre-split path at four waves never touches the stage)
+  // the rows' sums of squares and positions: all loads at once, in flight
+  // during the tile exchange (issued during the K loop instead they slowed
+  // gate/up and Q/K/V)
+  if constexpr (PL && NORM) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) sv[i] = (srow >= 0 && i < per) ? sp[i] : 0.0f;
+  }
+  if (MODE == kQKV && tid < TM && rows_s[tid] >= 0) pv = a.pos[rows_s[tid]];
+  if (!PL || NW == 8) __syncthreads();
   if (NORM && !PL) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -542,17 +587,15 @@ __global__ __launch_bounds__(NW * kWave) void bgemm_kernel(const GemvArgs a) {
     }
   }
 
-  // ---- each wave finishes fragment pairs u = wave, wave + 8, ...: (f, n0)
-  // and (f, n1), n0 = j and n1 = j + FN / 2 for SwiGLU (a gate tile and its
-  // up tile), n0 = 2 j and n1 = 2 j + 1 otherwise (32 adjacent columns).
+  // ---- each wave finishes fragment pairs u = wave, wave + NW, ... (pair_of).
   // Lane l holds row 16 f + l % 16 and, of each fragment, the four columns
   // 4 (l / 16) .. +3, so every store writes 16 (fp32) or 8 (fp16) bytes. ----
-  const int n0col = bx * TN;
-  constexpr int U = FM * (FN / 2);
-  const int c4 = 4 * lg;
-  for (int u = wave; u < U; u += NW) {
-    const int f = u / (FN / 2), j = u % (FN / 2);
-    const int na = MODE == kSwiGLU ? j : 2 * j, nb = MODE == kSwiGLU ? j + FN / 2 : 2 * j + 1;
+#pragma unroll
+  for (int i = 0; i < UPW; ++i) {
+    const int u = wave + NW * i;
+    if (u >= U) break;
+    int f, j, na, nb;
+    pair_of(u, f, j, na, nb);
     const int r = 16 * f + li;
     const int row = rows_s[r];
     const float rs = NORM ? rinv_of(r) : 1.0f;
@@ -574,7 +617,7 @@ __global__ __launch_bounds__(NW * kWave) void bgemm_kernel(const GemvArgs a) {
       finish_pair<MODE>(a, row, -1, lg, va, vb, bx * (TN / 2) + 16 * j + c4, 0);
     else
       finish_pair<MODE>(a, row, MODE == kQKV ? pos_s[r] : -1, lg, va, vb, n0col + 16 * na + c4,
-                        n0col + 16 * nb + c4);
+                        n0col + 16 * nb + c4, kPreAdd ? &pre[i] : nullptr);
   }
 }
 
@@ -784,10 +827,14 @@ hipError_t launch_t(int mode, const GemvArgs& a, dim3 grid, hipStream_t s) {
       if (!pl) return hipErrorInvalidValue;
       hipLaunchKernelGGL((bgemm_kernel<kQKV, FM, FN, NORM, true, NW>), grid, block, 0, s, a);
       break;
-    case kHead:
-      if (pl) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false, NW>), grid, block, 0, s, a);
-      break;
+    case kHead:  // 32-row tiles (rows gathered per head)
+      if constexpr (FM == 2) {
+        if (pl) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bgemm_kernel<kHead, FM, FN, NORM, false, NW>), grid, block, 0, s, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

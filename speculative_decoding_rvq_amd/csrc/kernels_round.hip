@@ -868,8 +868,11 @@ __device__ __forceinline__ void count_flags(uint32_t f, cp_spec_stats* cnt) {
 // whose output is h_s) becomes the round's drafts (codes, flags and dense
 // distributions, as the draft kernel leaves them), the verify rows E_s[c_s]
 // and E_{s+t}[d_t] are gathered, and the rows' heads for the next heads
-// launch are set.  Every thread of the block calls it.
-__device__ void fused_next_round(const RoundArgs& r, int b, int s, int gamma, int hrow, int last) {
+// launch are set.  cc / cf: that row's candidate codes and flags, already
+// read (so the gather's loads go out at once).  Every thread of the block
+// calls it.
+__device__ void fused_next_round(const RoundArgs& r, int b, int s, int gamma, int hrow, int last, const int* cc,
+                                 const uint32_t* cf) {
   const int tid = threadIdx.x;
   const size_t cb = (static_cast<size_t>(b) * r.R + hrow) * r.W;
   const int V4 = r.V / 4;
@@ -877,14 +880,14 @@ __device__ void fused_next_round(const RoundArgs& r, int b, int s, int gamma, in
   float4* dst = reinterpret_cast<float4*>(r.q + static_cast<size_t>(b) * r.W * r.V);
   for (int i = tid; i < gamma * V4; i += kBlock) dst[i] = src[i];
   if (tid < gamma) {
-    r.dcode[static_cast<size_t>(b) * r.W + tid] = r.ccode[cb + tid];
-    r.dflags[static_cast<size_t>(b) * r.W + tid] = r.cflags[cb + tid];
+    r.dcode[static_cast<size_t>(b) * r.W + tid] = cc[tid];
+    r.dflags[static_cast<size_t>(b) * r.W + tid] = cf[tid];
   }
   // the gamma + 1 verify rows side by side, a group of threads each
   const int nrow = gamma + 1, per = kBlock / nrow;
   const int k = tid / per;
   if (k < nrow) {
-    const int code = k == 0 ? last : r.ccode[cb + k - 1];
+    const int code = k == 0 ? last : cc[k - 1];
     embed_row_span(r, s + k, code, r.X + (static_cast<size_t>(b) * r.R + k) * r.H, tid - k * per, per);
   }
   const int W1 = r.W + 1;
@@ -914,6 +917,9 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
   __shared__ cp_spec_stats cnt_s;
   __shared__ int tcode_s[CP_SPEC_MAX_WINDOW], dcode_s[CP_SPEC_MAX_WINDOW];
   __shared__ uint32_t tflags_s[CP_SPEC_MAX_WINDOW], dflags_s[CP_SPEC_MAX_WINDOW];
+  // fused drafts: every verify row's candidate codes and flags
+  __shared__ int ccode_s[CP_SPEC_MAX_WINDOW * CP_SPEC_MAX_WINDOW];
+  __shared__ uint32_t cflags_s[CP_SPEC_MAX_WINDOW * CP_SPEC_MAX_WINDOW];
   __shared__ int sh_n, sh_hrow;
   constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
   constexpr int kCntW = sizeof(cp_spec_stats) / 8;
@@ -934,6 +940,9 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
   } else if (tid >= 112 && tid < 112 + r.W) {
     dcode_s[tid - 112] = r.dcode[static_cast<size_t>(b) * r.W + tid - 112];
     dflags_s[tid - 112] = r.dflags[static_cast<size_t>(b) * r.W + tid - 112];
+  } else if (r.fused && tid >= 128 && tid < 128 + r.R * r.W) {
+    ccode_s[tid - 128] = r.ccode[rb * r.W + tid - 128];
+    cflags_s[tid - 128] = r.cflags[rb * r.W + tid - 128];
   }
   const int H4 = r.H / 4;
   const int nf4 = r.R * H4;
@@ -1080,7 +1089,8 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
       r.thead[rb + tid] = tid <= gamma ? s + 1 + tid : 0;
     }
     if (tid < r.W) r.dhead[static_cast<size_t>(b) * r.W + tid] = tid + 1 <= gamma ? s + tid + 1 : 0;
-    if (r.fused) fused_next_round(r, b, s, gamma, sh_hrow, st.last);
+    if (r.fused)
+      fused_next_round(r, b, s, gamma, sh_hrow, st.last, ccode_s + sh_hrow * r.W, cflags_s + sh_hrow * r.W);
   }
   if (tid == 0) r.st[b] = st;
 }

@@ -79,7 +79,7 @@ __device__ int walk_step(const RowLds& L, int total, int V, int nk, XF x, UAF ua
   return -1;
 }
 
-// The outcome of a chain round from its rows' steps (one thread).
+// The outcome of a chain round from its rows' steps.
 //   dcode[t-1]         draft of offset t = 1..gamma;
 //   tcode[r], tflags[r] row r's step: greedy, its argmax (and kFlagArgmax);
 //                      sampled, the tested draft when kRowAccepted, else the
@@ -96,20 +96,22 @@ struct ChainOutcome {
   uint32_t accept, cdf;
 };
 
-__device__ __forceinline__ ChainOutcome chain_outcome(int gamma, bool greedy, const int* dcode, const int* tcode,
-                                                      const uint32_t* tflags, int* codes) {
+// One wave decides: lane l holds draft l + 1 (dc, l < gamma) and row l's
+// step (tc, tf, l <= gamma); every lane of the wave calls it, and lane l
+// gets the code it commits in *code (valid for l <= n_acc).
+__device__ __forceinline__ ChainOutcome chain_outcome(int gamma, bool greedy, int dc, int tc, uint32_t tf,
+                                                      int* code) {
+  const int l = static_cast<int>(threadIdx.x % kWave);
+  const bool kept = l < gamma && (greedy ? dc == tc : (tf & kRowAccepted) != 0u);
   ChainOutcome o{0, 0u, 0u};
-  if (greedy) {
-    while (o.n_acc < gamma && dcode[o.n_acc] == tcode[o.n_acc]) ++o.n_acc;
-  } else {
-    while (o.n_acc < gamma && (tflags[o.n_acc] & kRowAccepted)) ++o.n_acc;
+  // the first lane not kept (lanes from gamma on never are): n_acc <= gamma
+  o.n_acc = __builtin_ctzll(static_cast<unsigned long long>(__ballot(!kept)));
+  if (!greedy) {
     const int tested = min(o.n_acc + 1, gamma);
-    for (int t = 1; t <= tested; ++t)
-      if (tflags[t - 1] & kFlagAccept) o.accept |= 1u << (t - 1);
-    if (tflags[o.n_acc] & kFlagCdf) o.cdf = 1u << o.n_acc;
+    o.accept = static_cast<uint32_t>(__ballot(l < tested && (tf & kFlagAccept) != 0u));
+    o.cdf = static_cast<uint32_t>(__ballot(l == o.n_acc && (tf & kFlagCdf) != 0u));
   }
-  for (int t = 0; t < o.n_acc; ++t) codes[t] = dcode[t];
-  codes[o.n_acc] = tcode[o.n_acc];
+  *code = l < o.n_acc ? dc : tc;
   return o;
 }
 

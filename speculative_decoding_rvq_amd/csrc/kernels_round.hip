@@ -388,30 +388,32 @@ __global__ __launch_bounds__(kBlock) void accept_rows_kernel(const AcceptArgs a)
   });
 }
 
-// One thread per stream: the round's outcome from its rows (chain_outcome).
+// One wave per stream: the round's outcome from its rows (chain_outcome).
 __global__ __launch_bounds__(kBlock) void accept_outcome_kernel(const AcceptArgs a) {
-  const int b = blockIdx.x * kBlock + threadIdx.x;
-  if (b >= a.B) return;
+  const int b = blockIdx.x * (kBlock / kWave) + static_cast<int>(threadIdx.x / kWave);
+  if (b >= a.B) return;  // the whole wave
+  const int l = static_cast<int>(threadIdx.x % kWave);
   const int W = a.W;
   const int gamma = min(max(a.gamma[b], 0), W);
-  int dc[CP_SPEC_MAX_WINDOW], tc[CP_SPEC_MAX_WINDOW], codes[CP_SPEC_MAX_WINDOW];
-  uint32_t tf[CP_SPEC_MAX_WINDOW];
-  for (int t = 0; t < gamma; ++t) dc[t] = a.draft[static_cast<size_t>(b) * W + t];
-  for (int i = 0; i <= gamma; ++i) {
-    tc[i] = a.tcode[static_cast<size_t>(b) * (W + 1) + i];
-    tf[i] = a.tflags[static_cast<size_t>(b) * (W + 1) + i];
-  }
-  const ChainOutcome o = chain_outcome(gamma, a.greedy != 0, dc, tc, tf, codes);
+  const int dc = l < gamma ? a.draft[static_cast<size_t>(b) * W + l] : 0;
+  const int tc = l <= gamma ? a.tcode[static_cast<size_t>(b) * (W + 1) + l] : 0;
+  const uint32_t tf = l <= gamma ? a.tflags[static_cast<size_t>(b) * (W + 1) + l] : 0u;
+  int code;
+  const ChainOutcome o = chain_outcome(gamma, a.greedy != 0, dc, tc, tf, &code);
   const int n = o.n_acc + 1;
-  a.n_out[b] = n;
-  for (int i = 0; i <= W; ++i) a.codes_out[static_cast<size_t>(b) * (W + 1) + i] = i < n ? codes[i] : -1;
-  if (a.flags_out) a.flags_out[b] = o.accept | o.cdf;
+  if (l <= W) a.codes_out[static_cast<size_t>(b) * (W + 1) + l] = l < n ? code : -1;
+  if (l == 0) {
+    a.n_out[b] = n;
+    if (a.flags_out) a.flags_out[b] = o.accept | o.cdf;
+  }
 }
 
 hipError_t launch_accept_rows(const AcceptArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   hipLaunchKernelGGL(accept_rows_kernel, dim3(a.W + 1, a.B), dim3(kBlock), row_lds_bytes(a.V, true), s, a);
-  hipLaunchKernelGGL(accept_outcome_kernel, dim3((a.B + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+  constexpr int kStreamsPerBlock = kBlock / kWave;
+  hipLaunchKernelGGL(accept_outcome_kernel, dim3((a.B + kStreamsPerBlock - 1) / kStreamsPerBlock), dim3(kBlock), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -963,59 +965,65 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
   const size_t fb = static_cast<size_t>(st.f) * c.B + b;
   int* out = c.out_codes + fb * r.G;
 
-  // ---- the decision (one thread) ----
-  if (tid == 0) {
+  // ---- the decision (wave 0; lane l holds draft l + 1 and row l) ----
+  if (tid < kWave) {
     cp_spec_stats& cnt = cnt_s;
+    const int l = tid;
     if (st.mode == kModePrefill) {
-      const uint32_t f = tflags_s[1] & ~kRowAccepted;
-      count_flags(f, &cnt);
-      if (f) st_s.flags |= 1u << 1;
-      out[1] = st_s.last = tcode_s[1];
-      ++cnt.prefill_passes;
-      sh_n = 1;
-      sh_hrow = 1;
-      st_s.s = 1;
+      if (l == 0) {
+        const uint32_t f = tflags_s[1] & ~kRowAccepted;
+        count_flags(f, &cnt);
+        if (f) st_s.flags |= 1u << 1;
+        out[1] = st_s.last = tcode_s[1];
+        ++cnt.prefill_passes;
+        sh_n = 1;
+        sh_hrow = 1;
+        st_s.s = 1;
+      }
     } else {
       const int s = st.s, gamma = st.gamma;
-      uint32_t fl = st.flags;
-      int codes[CP_SPEC_MAX_WINDOW];
-      const ChainOutcome o = chain_outcome(gamma, r.greedy != 0, dcode_s, tcode_s, tflags_s, codes);
+      const int dc = l < gamma ? dcode_s[l] : 0;
+      const uint32_t df = l < gamma ? dflags_s[l] : 0u;
+      const int tc = l <= gamma ? tcode_s[l] : 0;
+      const uint32_t tf = l <= gamma ? tflags_s[l] : 0u;
+      int code;
+      const ChainOutcome o = chain_outcome(gamma, r.greedy != 0, dc, tc, tf, &code);
       const int n_acc = o.n_acc, n = n_acc + 1;
       // near ties of the decisions the outcome used: drafts 1..n_acc + 1
-      // (the last one tested), rows 0..n_acc
-      for (int t = 1; t <= min(n_acc + 1, gamma); ++t) {
-        const uint32_t f = dflags_s[t - 1];
-        count_flags(f, &cnt);
-        if (f) fl |= 1u << (s + t);
+      // (the last one tested), rows 0..n_acc; draft l + 1 and row l both
+      // mark depth s + 1 + l
+      const uint32_t dfu = l < min(n_acc + 1, gamma) ? df : 0u;
+      const uint32_t rfu = l <= n_acc ? (tf & (kFlagTopk | kFlagArgmax)) : 0u;
+      const uint32_t marked = static_cast<uint32_t>(__ballot(dfu != 0u || rfu != 0u));
+      auto both = [&](uint32_t bit) {
+        return __popcll(__ballot((dfu & bit) != 0u)) + __popcll(__ballot((rfu & bit) != 0u));
+      };
+      const int n_topk = both(kFlagTopk), n_argmax = both(kFlagArgmax);
+      const int n_cdf = both(kFlagCdf) + (o.cdf != 0u ? 1 : 0);
+      const int n_accept = both(kFlagAccept) + __popc(o.accept);
+      const int last = __shfl(code, n_acc);
+      if (l <= n_acc) out[s + 1 + l] = code;
+      if (l < gamma) {  // one counter word per lane
+        ++cnt.proposed[l];
+        if (l < n_acc) ++cnt.accepted[l];
       }
-      for (int i = 0; i <= n_acc; ++i) {
-        const uint32_t f = tflags_s[i] & (kFlagTopk | kFlagArgmax);
-        count_flags(f, &cnt);
-        if (f) fl |= 1u << (s + 1 + i);
+      if (l == 0) {
+        cnt.near_tie_topk += n_topk;
+        cnt.near_tie_argmax += n_argmax;
+        cnt.near_tie_cdf += n_cdf;
+        cnt.near_tie_accept += n_accept;
+        uint32_t fl = st.flags | (marked << (s + 1)) | (o.accept << (s + 1));
+        if (o.cdf) fl |= 1u << (s + n);
+        st_s.last = last;
+        ++cnt.rounds;
+        if (n_acc == gamma) ++cnt.bonus;
+        st_s.flags = fl;
+        st_s.s = s + n;
+        sh_n = n;
+        sh_hrow = n - 1;
       }
-      for (int t = 1; t <= gamma; ++t)
-        if (o.accept & (1u << (t - 1))) {
-          ++cnt.near_tie_accept;
-          fl |= 1u << (s + t);
-        }
-      if (o.cdf) {
-        ++cnt.near_tie_cdf;
-        fl |= 1u << (s + n);
-      }
-      for (int t = 0; t < n; ++t) out[s + 1 + t] = codes[t];
-      st_s.last = codes[n_acc];
-      ++cnt.rounds;
-      for (int t = 1; t <= gamma; ++t) {
-        ++cnt.proposed[t - 1];
-        if (t <= n_acc) ++cnt.accepted[t - 1];
-      }
-      if (n_acc == gamma) ++cnt.bonus;
-      st_s.flags = fl;
-      st_s.s = s + n;
-      sh_n = n;
-      sh_hrow = n - 1;
     }
-    if (st_s.s >= r.G - 1) {  // frame complete
+    if (l == 0 && st_s.s >= r.G - 1) {  // frame complete
       if (c.out_flags) c.out_flags[fb] = st_s.flags;
       ++cnt.frames;
       cnt.codes += r.G - 1;

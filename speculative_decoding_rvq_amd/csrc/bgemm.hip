@@ -844,7 +844,9 @@ template <int FM, int FN>
 hipError_t launch_f(int mode, int nw, const GemvArgs& a, dim3 grid, hipStream_t s) {
   const bool norm = a.norm_g != nullptr;
   if (nw == 4) return norm ? launch_t<FM, FN, true, 4>(mode, a, grid, s) : launch_t<FM, FN, false, 4>(mode, a, grid, s);
-  if (nw == 8) return norm ? launch_t<FM, FN, true, 8>(mode, a, grid, s) : launch_t<FM, FN, false, 8>(mode, a, grid, s);
+  if constexpr (FM * FN <= 24) {  // the 64 x 128 tile at eight waves would spill
+    if (nw == 8) return norm ? launch_t<FM, FN, true, 8>(mode, a, grid, s) : launch_t<FM, FN, false, 8>(mode, a, grid, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -949,6 +951,7 @@ hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, int nw, const Gemv
   if (fm == 2 && fn == 8) return launch_f<2, 8>(mode, nw, a, grid, s);
   if (fm == 4 && fn == 4) return launch_f<4, 4>(mode, nw, a, grid, s);
   if (fm == 4 && fn == 6) return launch_f<4, 6>(mode, nw, a, grid, s);
+  if (fm == 4 && fn == 8) return launch_f<4, 8>(mode, nw, a, grid, s);
   return hipErrorInvalidValue;
 }
 

@@ -337,13 +337,17 @@ bool mfma_fits(int mode, const GemvArgs& a) {
 // Block tile (16 fm) x (16 fn) of the packed bf16 kernel for M rows: the
 // largest that still gives every compute unit a block, else the one with the
 // most blocks; false when no tile divides the columns or K is not a
-// multiple of 512 (eight waves, each an even number of 32-wide chunks).
+// multiple of 512 (up to eight waves, each an even number of 32-wide
+// chunks).  64 x 128 only for the residual adds, always at four waves: it
+// cut the O and down projections' L2-to-CU bytes per compute unit by a third
+// at 1024 rows (Q/K/V ran slower on it than on 64 x 96).
 bool bgemm_tile(int mode, int N, int K, int M, int* fm_out, int* fn_out) {
-  static const int kTiles[4][2] = {{4, 6}, {4, 4}, {2, 4}, {2, 2}};
+  static const int kTiles[5][2] = {{4, 8}, {4, 6}, {4, 4}, {2, 4}, {2, 2}};
   if (K % 512) return false;
   int best = -1, best_blocks = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     const int fm = kTiles[i][0], fn = kTiles[i][1];
+    if (fn == 8 && mode != kAdd) continue;
     const bool fits = mode == kSwiGLU ? N % (8 * fn) == 0 : N % (16 * fn) == 0;
     if (!fits) continue;
     const int cols = mode == kSwiGLU ? 2 * N : N;
@@ -352,6 +356,7 @@ bool bgemm_tile(int mode, int N, int K, int M, int* fm_out, int* fn_out) {
       best = i;
       break;
     }
+    if (fn == 8) continue;  // not below a full grid (its blocks take four waves)
     if (blocks > best_blocks) best = i, best_blocks = blocks;
   }
   if (best < 0) return false;

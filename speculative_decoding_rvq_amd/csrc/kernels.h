@@ -230,8 +230,8 @@ enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };
 hipError_t launch_mfma(int wdtype, int mode, int tile, const GemvArgs& a, dim3 grid, hipStream_t s);
 // Matrix-core projections with in-block split-K over fragment-packed bf16
 // weights (W0 / W1 packed by pack_fragments): block tile (16 fm) x (16 fn),
-// (fm, fn) in {(2, 2), (2, 4), (2, 8), (4, 4), (4, 6)}, K a multiple of 512;
-// nw waves per block (4 or 8, each taking K / nw); grid
+// (fm, fn) in {(2, 2), (2, 4), (2, 8), (4, 4), (4, 6), (4, 8)}, K a multiple
+// of 512; nw waves per block (4 or 8, each taking K / nw; (4, 8) only 4); grid
 // (columns / tile, rows / tile) or, lm_heads, (V / tile, row tiles, heads).
 hipError_t launch_bgemm(int wdtype, int mode, int fm, int fn, int nw, const GemvArgs& a, dim3 grid, hipStream_t s);
 // Large batches (kLdsMinRows rows or more): 128 x 192 block tiles staged in

@@ -24,11 +24,12 @@
 //    fragment entry, split in registers and written as whole entries to a
 //    small XOR-swizzled LDS stage private to the wave (no block barrier in
 //    the K loop, no bank conflicts on either side).
-// Tiling: a block owns (16 FM) x (16 FN) outputs; its eight wave64s (two a
-// SIMD, so one's MFMAs cover the other's waits) split K in eighths and keep
-// the next two chunks' loads in flight.  The partial tiles (and the rows'
-// partial sums of squares) meet in LDS and are added in a fixed order: the
-// result does not depend on timing.
+// Tiling: a block owns (16 FM) x (16 FN) outputs; its wave64s split K: four
+// (one a SIMD) once the grid has a block per compute unit, eight (two a
+// SIMD, so one's MFMAs cover the other's waits) on smaller grids.  Each wave
+// keeps its next two chunks' loads in flight.  The partial tiles (and the
+// rows' partial sums of squares) meet in LDS and are added in a fixed order:
+// the result does not depend on timing.
 //
 // RMSNorm: x * g is split; the rows' sums of squares are accumulated on the
 // way and 1/sqrt(mean + eps) scales the outputs.  Epilogues: residual add,

@@ -50,7 +50,8 @@ struct Shape {
 
 struct Layout {
   size_t st, call, sstats, dhead, thead, pos, hstate, dX, X, Hout, ncode, Q, attn, act, kv, dlogits, q, dcode, dflags,
-      tlogits, p, tcode, tflags, rope, packed, planes, ssp, fhead, cq, ccode, cflags, hb, ovf, total;
+      tlogits, p, tcode, tflags, rope, packed, planes, ssp, fhead, cq, ccode, cflags, hb, st2, dcode2, dflags2, ovf,
+      total;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -233,6 +234,11 @@ Layout make_layout(const Shape& s) {
   l.ccode = take(s.fd ? B * R * W * i4 : 0);
   l.cflags = take(s.fd ? B * R * W * i4 : 0);
   l.hb = take(s.fd && s.K > 0 ? static_cast<size_t>(s.G - 1) * s.K * s.V * f4 : 0);
+  // the accept step folded into the next pass's first projection: staging
+  // copies of the stream state and drafts
+  l.st2 = take(s.fd ? B * sizeof(StreamState) : 0);
+  l.dcode2 = take(s.fd ? B * W * i4 : 0);
+  l.dflags2 = take(s.fd ? B * W * i4 : 0);
   l.p = take(B * R * s.V * f4);
   // (also the component accept's per-row scratch, [B][width + 1])
   const size_t Rt = std::max<size_t>(R, CP_SPEC_MAX_WINDOW);
@@ -273,6 +279,7 @@ struct cp_spec {
   hipGraphExec_t graph = nullptr;
   int graph_B = -1;
   bool use_graph = true;
+  bool use_fold = true;
 
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
   long long kv_sb() const { return static_cast<long long>(sh.L) * 2 * sh.Gk * sh.kvdim; }
@@ -314,7 +321,21 @@ struct cp_spec {
     r.p = at<float>(lo.p);
     r.tcode = at<int>(lo.tcode);
     r.tflags = at<uint32_t>(lo.tflags);
+    r.st_out = r.st;
+    r.dcode_out = r.dcode;
+    r.dflags_out = r.dflags;
+    if (fold_accept(B)) {
+      r.fold = 1;
+      r.st_out = at<StreamState>(lo.st2);
+      r.dcode_out = at<int>(lo.dcode2);
+      r.dflags_out = at<uint32_t>(lo.dflags2);
+    }
     return r;
+  }
+  // Whether the round's accept step runs inside the next pass's first
+  // projection (fused drafts, chain window, layer 0's Q/K/V on the GEMV).
+  bool fold_accept(int B) const {
+    return sh.fd && sh.tn == 0 && sh.R >= 2 && B * sh.R < kMfmaMinRows && use_fold;
   }
 };
 
@@ -368,8 +389,9 @@ bool bgemm_tile(int mode, int N, int K, int M, int* fm_out, int* fn_out) {
 // One skinny projection: Y (op) W . rows(X).  Many rows: matrix-core tiles
 // (bf16: over the fragment-packed copies pk0 / pk1 of W0 / W1).
 int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* pk0 = nullptr,
-         const uint16_t* pk1 = nullptr) {
+         const uint16_t* pk1 = nullptr, const RoundArgs* fold = nullptr) {
   if (a.M <= 0) return CP_SPEC_OK;
+  if (fold != nullptr && a.M >= kMfmaMinRows) return fail(CP_SPEC_EINVAL, "folded accept step off the GEMV path");
   int fm, fn;
   if (a.planes != nullptr && !bgemm_tile(mode, a.N, a.K, a.M, &fm, &fn))
     return fail(CP_SPEC_EINVAL, "pre-split rows without a matrix-core tile");
@@ -435,6 +457,11 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
     mt = mt_for(a.M, spt, vec);
     gy = (a.M + mt - 1) / mt;
   }
+  if (fold != nullptr) {
+    if (mode != kQKV) return fail(CP_SPEC_EINVAL, "folded accept step outside the Q/K/V GEMV");
+    CPS_HIP(launch_gemv_fold(h->sh.wdt, mt, a, *fold, gx, gy, s));
+    return CP_SPEC_OK;
+  }
   CPS_HIP(launch_gemv(h->sh.wdt, mode, mt, a, gx, gy, s));
   return CP_SPEC_OK;
 }
@@ -456,8 +483,10 @@ bool fused_planes(const cp_spec* h, int M) {
 
 // One decoder kernel of layer l over B*R rows of X at positions `pos`
 // (fused: see fused_planes; layer 0's Q/K/V input is split by the caller).
+// fold: layer 0 of a round whose previous accept step runs inside its Q/K/V
+// launch.
 int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R, float* X,
-                 const int* pos, float* kv, bool fused = false) {
+                 const int* pos, float* kv, bool fused = false, const RoundArgs* fold = nullptr) {
   const Shape& sh = h->sh;
   const int M = B * R;
   float* Q = h->at<float>(h->lo.Q);
@@ -492,7 +521,7 @@ int layer_kernel(const cp_spec* h, hipStream_t s, int kind, int l, int B, int R,
       a.kv_vo = kv_vo; a.rows_per_stream = R; a.pos = pos; a.kv_positions = sh.Gk;
       if (fused) a.planes = P0, a.ptiles = T, a.ssp = S;
       a.wscale0 = sc(0);
-      return gemv(h, s, kQKV, a, pw(0));
+      return gemv(h, s, kQKV, a, pw(0), nullptr, fold);
     case CP_SPEC_KERNEL_ATTENTION: {
       AttnArgs at{};
       at.Q = Q; at.out = attn; at.kv = kvl; at.kv_sb = h->kv_sb(); at.kv_vo = kv_vo; at.pos = pos;
@@ -547,14 +576,16 @@ const int kLayerKinds[5] = {CP_SPEC_KERNEL_QKV, CP_SPEC_KERNEL_ATTENTION, CP_SPE
                             CP_SPEC_KERNEL_GATE_UP, CP_SPEC_KERNEL_DOWN};
 
 // All decoder layers over B*R rows of X at positions `pos`, cache `kv`.
-int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const int* pos, float* kv) {
+int run_layers(const cp_spec* h, hipStream_t s, int B, int R, float* X, const int* pos, float* kv,
+               const RoundArgs* fold = nullptr) {
   const bool fused = fused_planes(h, B * R);
+  if (fold != nullptr && fused) return fail(CP_SPEC_EINVAL, "folded accept step with pre-split rows");
   if (fused)  // layer 0's Q/K/V input: the rows as the round left them
     CPS_HIP(launch_split_rows(X, h->sh.H, B * R, h->sh.H, static_cast<const float*>(h->layers[0][0]),
                               h->at<uint16_t>(h->lo.planes), h->at<float>(h->lo.ssp), h->at<int>(h->lo.ovf), pos, s));
   for (int l = 0; l < h->sh.L; ++l)
     for (int kind : kLayerKinds) {
-      const int rc = layer_kernel(h, s, kind, l, B, R, X, pos, kv, fused);
+      const int rc = layer_kernel(h, s, kind, l, B, R, X, pos, kv, fused, l == 0 ? fold : nullptr);
       if (rc) return rc;
     }
   return CP_SPEC_OK;
@@ -629,14 +660,15 @@ int enqueue_round(const cp_spec* h, hipStream_t s, int B) {
     // next ones: rows (stream, verify row r, k) with k = 0 the target head
     // and k = 1..W row r's candidate drafts (at most R rows of a stream per
     // head)
-    if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv)))) return rc;
+    // with the fold, layer 0's Q/K/V launch also commits the previous round
+    if ((rc = run_layers(h, s, B, sh.R, r.X, r.pos, h->at<float>(h->lo.kv), r.fold ? &r : nullptr))) return rc;
     const int W1 = sh.W + 1;
     if ((rc = head_logits(h, s, B * sh.R * W1, r.X, W1, r.fhead, h->fnorm, r.Hout, r.tlogits,
                           per_head > 0 ? B * sh.R : 0, B * sh.R,
                           sh.K > 0 ? h->at<float>(h->lo.hb) : nullptr)))
       return rc;
     CPS_HIP(launch_target_topk(r, s));
-    CPS_HIP(launch_round_accept(r, s));
+    if (!r.fold) CPS_HIP(launch_round_accept(r, s));
     return CP_SPEC_OK;
   }
   if (sh.N >= 2) {
@@ -685,7 +717,9 @@ long long rounds_lower_bound(const Shape& sh, const StreamState& st, int F) {
   const int nw = std::max(sh.N, 1);
   const long long per_frame = 1 + (sh.G - 2 + nw - 1) / nw;
   if (st.mode == kModeDone) return 0;
-  if (st.mode == kModePrefill) return static_cast<long long>(F - st.f) * per_frame;
+  // (with the accept step folded into the next pass, a state is the round
+  // just verified, not yet committed: still at least one pass)
+  if (st.mode == kModePrefill || st.mode == kModeFresh) return static_cast<long long>(F - st.f) * per_frame;
   return (sh.G - 1 - st.s + nw - 1) / nw + static_cast<long long>(F - st.f - 1) * per_frame;
 }
 

@@ -59,10 +59,25 @@ __device__ __forceinline__ const WT* weight_row(const GemvArgs& a, const WT* W0,
   return W0 + static_cast<size_t>(o) * a.K;
 }
 
-// WT weight type, MODE epilogue, MT activation rows per tile, SPT 16-byte
-// chunks per thread per row.
-template <typename WT, int MODE, int MT, int SPT>
-__global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
+// Where a block's activation rows come from.  The default reads row m / xdiv
+// of a.X and a K/V append's position from a.pos; a custom source (kCustom)
+// provides prepare() (called by every thread once the first weights are in
+// flight), load(m, k, x): the VEC values of the block's row m from column k,
+// and pos(m), for the rows m0 .. m0 + MT - 1 of a launch with one row tile
+// per block row.
+struct XRows {
+  static constexpr bool kCustom = false;
+  __device__ void prepare() const {}
+  template <int VEC>
+  __device__ void load(int, int, float4 (&)[VEC / 4]) const {}
+  __device__ int pos(int) const { return -1; }
+};
+
+// One block of the GEMV: block (bx, by) of a grid gdx blocks wide (after any
+// remapping).  WT weight type, MODE epilogue, MT activation rows per tile,
+// SPT 16-byte chunks per thread per row.
+template <typename WT, int MODE, int MT, int SPT, typename Rows>
+__device__ __forceinline__ void gemv_block(const GemvArgs& a, int bx, int by, int gdx, const Rows& rows) {
   using C = Chunk<WT>;
   using VT = typename C::T;
   constexpr int VEC = C::N;
@@ -77,17 +92,6 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   const int tid = threadIdx.x;
   const int rg = tid / KT, kt = tid % KT;
   const int lane = tid % kWave;
-  // Several row tiles read the same weight rows.  Blocks go to the eight
-  // XCDs in turn (linear id modulo 8): the row tiles of one weight slice are
-  // given to consecutive blocks of one XCD, so all but the first read the
-  // slice from that XCD's L2.
-  int bx = blockIdx.x, by = blockIdx.y;
-  if (MODE != kHeadG && gridDim.y > 1 && gridDim.x % 8 == 0) {
-    const int L = blockIdx.x + gridDim.x * blockIdx.y;
-    const int i = L / 8;
-    by = i % gridDim.y;
-    bx = (i / gridDim.y) * 8 + L % 8;
-  }
   const int m0 = MODE == kHeadG ? 0 : by * MT;
   if (MODE != kHeadG && a.M - m0 <= 0) return;
 
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   // activation row m of the block
   auto row_of = [&](int m) { return MODE == kHeadG ? rows_s[m] : m0 + m; };
   const int Mloc = MODE == kHeadG ? Mg : min(MT, a.M - m0);
-  const int stride = gridDim.x * RG;
+  const int stride = gdx * RG;
   int ubase = bx * RG;
 
   // ---- the activation rows first, then the first unit's weights: the rows
@@ -122,17 +126,55 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
   // read once per chunk, not once per row: every vector memory instruction
   // counts at one stream, more than the bytes it moves. ----
   const bool norm = a.norm_g != nullptr;
+  VT wv[RPG][SPT];
+  auto load_first_weights = [&]() __attribute__((always_inline)) {
+    const int u = min(ubase + rg, a.units - 1);
+#pragma unroll
+    for (int rp = 0; rp < RPG; ++rp) {
+      const WT* wr = weight_row<WT, MODE, RPG>(a, W0, u * RPG + rp);
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) wv[rp][j] = *reinterpret_cast<const VT*>(wr + (kt + KT * j) * VEC);
+    }
+  };
+  if constexpr (Rows::kCustom) {
+    // a custom source finds its rows first (prepare: loads and a barrier),
+    // so the weights go out before it
+    load_first_weights();
+    __builtin_amdgcn_sched_barrier(0);
+    rows.prepare();
+  }
   float4 xv[MT][SPT][VEC / 4];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4)
-        xv[m][j][e / 4] =
-            m < Mloc ? *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row_of(m) / a.xdiv) * a.ldx +
-                                                        (kt + KT * j) * VEC + e)
-                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int e = 0; e < VEC; e += 4) {
+        if constexpr (Rows::kCustom) {
+          if (e == 0) rows.template load<VEC>(m, (kt + KT * j) * VEC, xv[m][j]);
+        } else {
+          xv[m][j][e / 4] =
+              m < Mloc ? *reinterpret_cast<const float4*>(a.X + static_cast<size_t>(row_of(m) / a.xdiv) * a.ldx +
+                                                          (kt + KT * j) * VEC + e)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+      }
+  if constexpr (Rows::kCustom) {
+    // block column 0 also leaves the rows in a.X (the round's row buffer:
+    // the residual stream the later projections add to)
+    if (bx == 0 && rg == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < Mloc) {
+#pragma unroll
+          for (int j = 0; j < SPT; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+              *reinterpret_cast<float4*>(const_cast<float*>(a.X) + static_cast<size_t>(m0 + m) * a.ldx +
+                                         (kt + KT * j) * VEC + e) = xv[m][j][e / 4];
+        }
+    }
+  }
   float4 gv[SPT][VEC / 4];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
@@ -141,16 +183,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
       gv[j][e / 4] = norm ? *reinterpret_cast<const float4*>(a.norm_g + (kt + KT * j) * VEC + e)
                           : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
   __builtin_amdgcn_sched_barrier(0);
-  VT wv[RPG][SPT];
-  {
-    const int u = min(ubase + rg, a.units - 1);
-#pragma unroll
-    for (int rp = 0; rp < RPG; ++rp) {
-      const WT* wr = weight_row<WT, MODE, RPG>(a, W0, u * RPG + rp);
-#pragma unroll
-      for (int j = 0; j < SPT; ++j) wv[rp][j] = *reinterpret_cast<const VT*>(wr + (kt + KT * j) * VEC);
-    }
-  }
+  if constexpr (!Rows::kCustom) load_first_weights();
   __builtin_amdgcn_sched_barrier(0);
   float xr[MT][SPT][VEC];
   float ss[MT];
@@ -185,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
     if (!owner || u >= a.units || m >= Mloc) return;
     const int row = m0 + m;
     if (MODE == kAdd) y = a.Y[static_cast<size_t>(row) * a.ldy + u * RPG + rp];
-    if (MODE == kQKV) pp = a.pos[row];
+    if (MODE == kQKV) pp = Rows::kCustom ? rows.pos(m) : a.pos[row];
   };
   epi_load(ubase, yold, ppos);
 
@@ -306,6 +339,22 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
     yold = yold_n, ppos = ppos_n;
     if (nb < a.units) __syncthreads();  // part[] is rewritten by the next unit
   }
+}
+
+template <typename WT, int MODE, int MT, int SPT>
+__global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvArgs a) {
+  // Several row tiles read the same weight rows.  Blocks go to the eight
+  // XCDs in turn (linear id modulo 8): the row tiles of one weight slice are
+  // given to consecutive blocks of one XCD, so all but the first read the
+  // slice from that XCD's L2.
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (MODE != kHeadG && gridDim.y > 1 && gridDim.x % 8 == 0) {
+    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    const int i = L / 8;
+    by = i % gridDim.y;
+    bx = (i / gridDim.y) * 8 + L % 8;
+  }
+  gemv_block<WT, MODE, MT, SPT>(a, bx, by, gridDim.x, XRows{});
 }
 
 // Host-side dispatch for one weight type: MT in {1, 2, 4, 8}, SPT in 1..4.

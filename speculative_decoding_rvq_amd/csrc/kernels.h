@@ -156,12 +156,14 @@ struct StreamState {
   int f;       // frame being decoded
   int s;       // committed depth (c_0..c_s committed, c_s not yet fed)
   int gamma;   // drafts in the coming round
-  int mode;    // kModePrefill / kModeSpec / kModeDone
+  int mode;    // kModePrefill / kModeSpec / kModeDone / kModeFresh
   uint32_t flags;
   int last;                   // c_s, the last committed code
   uint32_t seed_lo, seed_hi;  // the frame's Philox key
 };
-enum { kModePrefill = 0, kModeSpec = 1, kModeDone = 2 };
+// kModeFresh (accept folded into the first projection): the call's first
+// pass, whose rows are frame f's prefill and which has no outcome to commit
+enum { kModePrefill = 0, kModeSpec = 1, kModeDone = 2, kModeFresh = 3 };
 
 // Arguments of one decode call, written on device by the init kernel so the
 // captured round graph can be replayed for any call.
@@ -219,11 +221,28 @@ struct RoundArgs {
   uint32_t* cflags;  // [B][R][W]
   int* tcode;      // [B][R]
   uint32_t* tflags;  // [B][R]
+  // where the accept step writes the stream state and the next round's
+  // drafts: st / dcode / dflags themselves, or, with the accept step folded
+  // into the next pass's first projection (fold), staging copies: the
+  // projection's other blocks still read the old ones; the target softmax
+  // launch reads the staged ones and moves them into place
+  int fold;
+  StreamState* st_out;
+  int* dcode_out;
+  uint32_t* dflags_out;
 };
 
 // Launchers.  All asynchronous on `s`.
 hipError_t launch_gemv(int wdtype, int mode, int mt, const GemvArgs& a, int grid_x, int grid_y,
                        hipStream_t s);
+// Layer 0's Q/K/V GEMV with the previous round's accept step folded in
+// (r.fold): r.B extra blocks run the accept step (into r.st_out /
+// r.dcode_out / r.dflags_out), and the GEMV blocks take the same outcome from
+// r.st, r.tcode / r.tflags, r.dcode and r.ccode and read their rows from the
+// embedding tables or h_frame directly.  Grid gx x gy GEMV blocks as for
+// launch_gemv, plus the accept blocks.
+hipError_t launch_gemv_fold(int wdtype, int mt, const GemvArgs& a, const RoundArgs& r, int gx, int gy,
+                            hipStream_t s);
 // tile: kTile64 (64 x 64, LDS-staged), kTile32 / kTile16 (split-K over the
 // block's four waves; K a multiple of 128).
 enum MfmaTile { kTile64 = 0, kTile32 = 1, kTile16 = 2 };

@@ -5,6 +5,7 @@
 
 #include "dev_common.h"
 #include "kernels.h"
+#include "gemv_impl.h"
 #include "topk_impl.h"
 #include "accept_impl.h"
 
@@ -572,7 +573,10 @@ __device__ void setup_prefill(const RoundArgs& r, const CallDesc& c, int b, int 
   float* x = r.X + static_cast<size_t>(b) * r.R * r.H;
   const float* hf = c.h_frame + (static_cast<size_t>(f) * c.B + b) * r.H;
   const int c0 = c.c0[static_cast<size_t>(f) * c.B + b];
-  if (r.H > kBlock) {
+  if (r.fold) {
+    // (the rows: the folded Q/K/V launch reads them itself and leaves them
+    // in X)
+  } else if (r.H > kBlock) {
     if ((r.H & 3) == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(hf)) & 15u) == 0) {
       const int step = kBlock * 4;
       for (int i = threadIdx.x * 4; i < r.H; i += kGatherRun * step) {
@@ -620,7 +624,7 @@ __global__ __launch_bounds__(kBlock) void round_init_kernel(const RoundArgs r, c
   StreamState st{};
   if (c.F > 0) {
     setup_prefill(r, c, b, 0);
-    st.mode = kModePrefill;
+    st.mode = r.fold ? kModeFresh : kModePrefill;
     set_frame_seed(st, c.seeds[b]);
   } else {
     st.mode = kModeDone;
@@ -730,7 +734,7 @@ __device__ void candidate_draft(const RoundArgs& r, int b, int rr, int k, SelSme
                                 uint64_t* red64, uint32_t* red32) {
   const size_t frow = (static_cast<size_t>(b) * r.R + rr) * (r.W + 1) + k;
   const int head = r.fhead[frow];
-  const StreamState st = r.st[b];
+  const StreamState st = r.fold ? r.st_out[b] : r.st[b];  // (fold: the staged state is this round's)
   float zv[VPT];
   load_row<VPT>(r.tlogits + frow * r.V, zv);
   if (head <= 0 || st.mode == kModeDone) return;
@@ -766,6 +770,20 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
   const int W1 = r.fused ? r.W + 1 : 1;
   const int rr = blockIdx.x / W1, kc = blockIdx.x % W1, b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * r.R + rr;
+  if (r.fold && blockIdx.x == 0) {
+    // the accept step folded into this pass's first projection left the
+    // stream's state and drafts in staging copies, which this launch reads;
+    // the next pass's first projection reads them in place
+    constexpr int kStW = sizeof(StreamState) / 4;
+    const int t = threadIdx.x;
+    if (t < kStW) {
+      reinterpret_cast<int*>(r.st + b)[t] = reinterpret_cast<const int*>(r.st_out + b)[t];
+    } else if (t >= kWave && t < kWave + r.W) {
+      const size_t i = static_cast<size_t>(b) * r.W + (t - kWave);
+      r.dcode[i] = r.dcode_out[i];
+      r.dflags[i] = r.dflags_out[i];
+    }
+  }
   dispatch_vpt(r.V, [&](auto vpt) {
     constexpr int VPT = decltype(vpt)::value;
     if (kc > 0) {
@@ -780,7 +798,7 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
     // chain's row rr tests draft offset rr + 1, which exists for rr < W; a
     // tree row tests the children of its node, drafted at depth dep[rr] + 1)
     const int head = r.thead[row];
-    const StreamState st = r.st[b];
+    const StreamState st = r.fold ? r.st_out[b] : r.st[b];  // (fold: the staged state is this round's)
     float zv[VPT];
     load_row<VPT>(r.tlogits + row * W1 * r.V, zv);
     const int qi = r.tnodes > 0 ? r.dep[rr] : rr;
@@ -791,7 +809,7 @@ __global__ __launch_bounds__(kBlock) void target_topk_kernel(const RoundArgs r) 
       const float* qrow = r.q + (static_cast<size_t>(b) * r.W + qi) * r.V;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) qv[j] = qrow[base + j];
-      if (r.tnodes == 0) dd = r.dcode[static_cast<size_t>(b) * r.W + rr];
+      if (r.tnodes == 0) dd = (r.fold ? r.dcode_out : r.dcode)[static_cast<size_t>(b) * r.W + rr];
     }
     // (a finished stream's heads are zero already; testing its mode here keeps
     // the state load ahead of this branch)
@@ -882,13 +900,15 @@ __device__ void fused_next_round(const RoundArgs& r, int b, int s, int gamma, in
   float4* dst = reinterpret_cast<float4*>(r.q + static_cast<size_t>(b) * r.W * r.V);
   for (int i = tid; i < gamma * V4; i += kBlock) dst[i] = src[i];
   if (tid < gamma) {
-    r.dcode[static_cast<size_t>(b) * r.W + tid] = cc[tid];
-    r.dflags[static_cast<size_t>(b) * r.W + tid] = cf[tid];
+    r.dcode_out[static_cast<size_t>(b) * r.W + tid] = cc[tid];
+    r.dflags_out[static_cast<size_t>(b) * r.W + tid] = cf[tid];
   }
-  // the gamma + 1 verify rows side by side, a group of threads each
+  // the gamma + 1 verify rows side by side, a group of threads each (with
+  // the fold, the next pass's Q/K/V launch reads them itself and leaves
+  // them in X)
   const int nrow = gamma + 1, per = kBlock / nrow;
   const int k = tid / per;
-  if (k < nrow) {
+  if (k < nrow && !r.fold) {
     const int code = k == 0 ? last : cc[k - 1];
     embed_row_span(r, s + k, code, r.X + (static_cast<size_t>(b) * r.R + k) * r.H, tid - k * per, per);
   }
@@ -913,7 +933,10 @@ constexpr int kHrowF4 = 8;
 // output rows, one of which becomes h_{s+n}); one thread then decides, and
 // the block writes.  Counters stay per stream (no device-wide atomics inside
 // the round); they are added to the caller's totals once per call.
-__global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) {
+// The accept step of stream b, by one block of kBlock threads.  It reads the
+// round's state from r.st / r.dcode / r.dflags and writes the next round's to
+// r.st_out / r.dcode_out / r.dflags_out.
+__device__ void accept_step(const RoundArgs& r, int b) {
   __shared__ StreamState st_s;
   __shared__ CallDesc c_s;
   __shared__ cp_spec_stats cnt_s;
@@ -926,7 +949,7 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
   constexpr int kStW = sizeof(StreamState) / 4, kCallW = sizeof(CallDesc) / 4;
   constexpr int kCntW = sizeof(cp_spec_stats) / 8;
   static_assert(kStW <= 32 && kCallW <= 32 && kCntW <= 32, "state words");
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const size_t rb = static_cast<size_t>(b) * r.R;
 
   // ---- every independent load at once ----
@@ -960,7 +983,15 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
   }
   __syncthreads();
   StreamState st = st_s;
-  if (st.mode == kModeDone) return;
+  if (st.mode == kModeDone || st.mode == kModeFresh) {
+    // nothing to commit: a finished stream, or a call's first pass (the
+    // init kernel set up its rows)
+    if (tid == 0 && r.st_out != r.st) {
+      if (st.mode == kModeFresh) st.mode = kModePrefill;
+      r.st_out[b] = st;
+    }
+    return;
+  }
   const CallDesc& c = c_s;
   const size_t fb = static_cast<size_t>(st.f) * c.B + b;
   int* out = c.out_codes + fb * r.G;
@@ -1100,12 +1131,204 @@ __global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r)
     if (r.fused)
       fused_next_round(r, b, s, gamma, sh_hrow, st.last, ccode_s + sh_hrow * r.W, cflags_s + sh_hrow * r.W);
   }
-  if (tid == 0) r.st[b] = st;
+  if (tid == 0) r.st_out[b] = st;
 }
+
+__global__ __launch_bounds__(kBlock) void round_accept_kernel(const RoundArgs r) { accept_step(r, blockIdx.x); }
 
 hipError_t launch_round_accept(const RoundArgs& r, hipStream_t s) {
   hipLaunchKernelGGL(round_accept_kernel, dim3(r.B), dim3(kBlock), 0, s, r);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The accept step folded into the next pass's first projection.
+//
+// A row of the fold's Q/K/V launch: where its values come from (null: a zero
+// row; fp32 or the tables' type) and its position (-1: inactive).
+struct FoldRow {
+  const void* p;
+  int bf16;
+  int pos;
+};
+
+template <int MT>
+__device__ void fold_rows(const RoundArgs& r, int m0, int M, FoldRow* out);
+
+// The GEMV's custom row source: the block's FoldRows (LDS), found by
+// fold_rows in prepare().
+template <int MT>
+struct FoldRows {
+  static constexpr bool kCustom = true;
+  const RoundArgs& r;
+  int m0, M;
+  FoldRow* rows;
+  __device__ void prepare() const { fold_rows<MT>(r, m0, M, rows); }
+  template <int VEC>
+  __device__ void load(int m, int k, float4 (&x)[VEC / 4]) const {
+    const FoldRow fr = rows[m];
+    if (fr.p == nullptr) {
+#pragma unroll
+      for (int i = 0; i < VEC / 4; ++i) x[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      return;
+    }
+    if (fr.bf16) {
+      const uint16_t* e = static_cast<const uint16_t*>(fr.p) + k;
+      if ((reinterpret_cast<uintptr_t>(e) & 7u) == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+          const uint2 v = *reinterpret_cast<const uint2*>(e + 4 * i);
+          x[i] = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i)
+          x[i] = make_float4(bf16_to_f32(e[4 * i]), bf16_to_f32(e[4 * i + 1]), bf16_to_f32(e[4 * i + 2]),
+                             bf16_to_f32(e[4 * i + 3]));
+      }
+    } else {
+      const float* f = static_cast<const float*>(fr.p) + k;
+      if ((reinterpret_cast<uintptr_t>(f) & 15u) == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) x[i] = *reinterpret_cast<const float4*>(f + 4 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) x[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+      }
+    }
+  }
+  __device__ int pos(int m) const { return rows[m].pos; }
+};
+
+// Rows m0 .. m0 + MT - 1 (of M) of the fold's Q/K/V launch.  For each stream
+// with rows there, the outcome of the round the last pass verified, as the
+// accept step takes it (chain_outcome on the rows' steps; a prefill commits
+// row 1's code), then the next round's input rows and positions: E_s[c_s] and
+// E_{s+t}[d_t] with the drafts of the row that ended the round, or, after a
+// frame, the next frame's prefill rows [h_frame, E_0[c_0]].  Wave w takes the
+// block's w-th stream (R >= 2 and MT <= 8: at most four).  Every thread of
+// the block calls it.
+template <int MT>
+__device__ void fold_rows(const RoundArgs& r, int m0, int M, FoldRow* out) {
+  // rows past M (and rows no stream claims) stay zero rows
+  if (threadIdx.x < MT) out[threadIdx.x] = FoldRow{nullptr, 0, -1};
+  __syncthreads();
+  const int w = static_cast<int>(threadIdx.x) / kWave, l = static_cast<int>(threadIdx.x) % kWave;
+  const int b = m0 / r.R + w;
+  if (w < 4 && b < r.B && b * r.R < m0 + MT) {
+    // every load that does not depend on the outcome at once: the state, the
+    // rows' steps (lane l: row l), the drafts (lane l: d_{l+1}) and every
+    // row's candidate codes (lane l: entry l of [R][W])
+    const size_t rb = static_cast<size_t>(b) * r.R;
+    const StreamState st = r.st[b];
+    const CallDesc* c = r.call;
+    const int cF = c->F, cB = c->B;
+    const float* hframe = c->h_frame;
+    const int* c0 = c->c0;
+    const int tc = l < r.R ? r.tcode[rb + l] : 0;
+    const uint32_t tf = l < r.R ? r.tflags[rb + l] : 0u;
+    const int dc = l < r.W ? r.dcode[static_cast<size_t>(b) * r.W + l] : 0;
+    const int cc = l < r.R * r.W ? r.ccode[rb * r.W + l] : 0;
+    int mode = st.mode, f = st.f, s = st.s, last = st.last, hrow = 0;
+    bool pre = mode == kModeFresh;  // the next rows are frame f's prefill
+    if (mode == kModePrefill || mode == kModeSpec) {
+      int n = 1;
+      if (mode == kModePrefill) {
+        hrow = 1;
+        last = __shfl(tc, 1);
+      } else {
+        const int gamma = st.gamma;
+        int code;
+        const ChainOutcome o = chain_outcome(gamma, r.greedy != 0, l < gamma ? dc : 0, l <= gamma ? tc : 0,
+                                             l <= gamma ? tf : 0u, &code);
+        n = o.n_acc + 1;
+        hrow = n - 1;
+        last = __shfl(code, o.n_acc);
+      }
+      s = (mode == kModePrefill ? 0 : s) + n;
+      mode = kModeSpec;
+      if (s >= r.G - 1) {  // frame complete
+        f += 1;
+        mode = f >= cF ? kModeDone : kModePrefill;
+        pre = mode == kModePrefill;
+      }
+    }
+    const int gamma = mode == kModeSpec ? (r.N == 0 ? 0 : min(r.N - 1, r.G - 2 - s)) : 0;
+    // lane l: row l's draft code, d_l of the row that ended the round
+    const int ccl = __shfl(cc, min(max(hrow * r.W + l - 1, 0), kWave - 1));
+    const int rr = l, row = b * r.R + rr, m = row - m0;
+    if (rr < r.R && m >= 0 && m < MT) {
+      FoldRow fr{nullptr, 0, -1};
+      if (row < M && mode != kModeDone) {
+        const size_t fb = static_cast<size_t>(f) * cB + b;
+        int table = -1, code = 0;
+        if (pre) {
+          if (rr == 0) fr = FoldRow{hframe + fb * r.H, 0, 0};
+          if (rr == 1) table = 0, code = c0[fb], fr.pos = 1;
+        } else if (rr <= gamma) {
+          table = s + rr;
+          code = rr == 0 ? last : ccl;
+          fr.pos = s + 1 + rr;
+        }
+        if (table >= 0) {
+          code = min(max(code, 0), r.V - 1);  // codes come from [0, V); never index outside
+          const size_t off = (static_cast<size_t>(table) * r.V + code) * r.H;
+          fr.p = r.wbf16 ? static_cast<const void*>(static_cast<const uint16_t*>(r.embed) + off)
+                         : static_cast<const void*>(static_cast<const float*>(r.embed) + off);
+          fr.bf16 = r.wbf16;
+        }
+      }
+      out[m] = fr;
+    }
+  }
+  __syncthreads();
+}
+
+// Grid: r.B accept blocks, then gdx x gdy GEMV blocks (one-dimensional).
+template <typename WT, int MT, int SPT>
+__global__ __launch_bounds__(kBlock) void gemv_fold_kernel(const GemvArgs a, const RoundArgs r, int gdx, int gdy) {
+  const int L = blockIdx.x;
+  if (L < r.B) {
+    accept_step(r, L);
+    return;
+  }
+  // as gemv_kernel's: the row tiles of one weight slice on one XCD
+  const int Lg = L - r.B;
+  int bx = Lg % gdx, by = Lg / gdx;
+  if (gdy > 1 && gdx % 8 == 0) {
+    const int i = Lg / 8;
+    by = i % gdy;
+    bx = (i / gdy) * 8 + Lg % 8;
+  }
+  __shared__ FoldRow rows_s[MT];
+  gemv_block<WT, kQKV, MT, SPT>(a, bx, by, gdx, FoldRows<MT>{r, by * MT, a.M, rows_s});
+}
+
+template <typename WT>
+hipError_t launch_gemv_fold_t(int mt, const GemvArgs& a, const RoundArgs& r, int gx, int gy, hipStream_t s) {
+  constexpr int VEC = Chunk<WT>::N;
+  const int spt = a.K / (VEC * a.kt);
+  if (r.R < 2 || a.rows_per_stream != r.R || a.M != r.B * r.R) return hipErrorInvalidValue;
+  const dim3 grid(r.B + gx * gy), block(kBlock);
+#define CPS_FOLD_CASE(MT_, SPT_)                                                                \
+  if (mt == MT_ && spt == SPT_) {                                                               \
+    hipLaunchKernelGGL((gemv_fold_kernel<WT, MT_, SPT_>), grid, block, 0, s, a, r, gx, gy);    \
+    return hipGetLastError();                                                                   \
+  }
+#define CPS_FOLD_MT(MT_) CPS_FOLD_CASE(MT_, 1) CPS_FOLD_CASE(MT_, 2) CPS_FOLD_CASE(MT_, 3) CPS_FOLD_CASE(MT_, 4)
+  CPS_FOLD_MT(1)
+  CPS_FOLD_MT(2)
+  CPS_FOLD_MT(4)
+  CPS_FOLD_MT(8)
+#undef CPS_FOLD_MT
+#undef CPS_FOLD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_fold(int wdtype, int mt, const GemvArgs& a, const RoundArgs& r, int gx, int gy,
+                            hipStream_t s) {
+  return wdtype == CP_SPEC_BF16 ? launch_gemv_fold_t<uint16_t>(mt, a, r, gx, gy, s)
+                                : launch_gemv_fold_t<float>(mt, a, r, gx, gy, s);
 }
 
 // ---------------------------------------------------------------------------

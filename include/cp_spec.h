@@ -95,7 +95,9 @@ typedef struct cp_spec_cfg {
    * row 1) also scores the heads of the depths after it, with the offsets
    * when draft_offsets > 0, in the same lm_head launch as the target rows;
    * their drafts are drawn in the target softmax launch, and the accept
-   * step keeps the set of the row that ends the round.  The drafts and the
+   * step keeps the set of the row that ends the round.  Below 32 verify rows
+   * the accept step runs inside the next pass's first (Q/K/V) launch, whose
+   * projection blocks read the next rows from the tables themselves.  The drafts and the
    * committed codes are those of fused_draft 0; the separate draft GEMV and
    * draft softmax launches are gone, the heads launch scores up to
    * max(N, 2) x N rows per stream instead of max(N, 2).  Chain windows only
@@ -245,8 +247,8 @@ int cp_spec_topk_sample(cp_spec* h, void* stream, int32_t n_rows,
  *   d_flags out [B] u32 nullable (bit t-1: near tie at offset t, either the
  *   accept test of a tested offset or the CDF of the committed draw).
  * Every row is decided in parallel by the step the decode round's target
- * kernel takes (one child per row), then the outcome scan of its accept
- * kernel; the rows' steps go through the workspace.
+ * kernel takes (one child per row), then the outcome scan its accept step
+ * runs (one wave per stream); the rows' steps go through the workspace.
  * Errors: EINVAL for n_streams outside 0..max_streams, width outside 0..7,
  * null pointers. */
 int cp_spec_accept(cp_spec* h, void* stream, int32_t n_streams, int32_t width,

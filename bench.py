@@ -22,6 +22,18 @@ METRIC = "committed RVQ codes/sec + accepted codes/verify pass, 1 & 64 streams, 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense, MI355X
 REALTIME_FPS = 12.5
+# The next round's drafts formed in this round's verify tail (RVQ section
+# 2.2, Figure 3) on every workload where it measured faster on this GPU
+# (codes/s against separate draft launches: tiny 1.19x, tiny greedy 1.15x,
+# tiny at 64 streams 1.09x, qwen3tts 1.05x, qwen3tts at 64 streams 1.01x);
+# the wide decoder at 256 streams keeps separate draft launches (0.91x: its
+# R*W extra candidate rows per stream cost more head work than the launches
+# saved).  The fused_draft section of the output measures both again.
+UNFUSED_WORKLOADS = ("wide-256",)
+
+
+def fused_for(workload):
+    return 0 if workload in UNFUSED_WORKLOADS else 1
 
 
 def _inputs(c, torch, np):
@@ -205,14 +217,14 @@ def verify_sweep(cid, Ns=(2, 3, 4, 5, 6, 7, 8), frames=None, steps=2):
     import synth
     from speculative_decoding_rvq_amd import binding
     from speculative_decoding_rvq_amd.calibrate import calibrate_window
-    c = synth.config(cid, **({"frames": frames} if frames else {}))
+    c = synth.config(cid, fused_draft=fused_for(cid), **({"frames": frames} if frames else {}))
     wdev = binding.weights_to_device(synth.make_weights(c))
     dh, dc, ds, *_ = _inputs(c, torch, np)
     cal = calibrate_window(c, wdev, dh, dc, ds, sizes=Ns, repeats=steps)
     del wdev
     torch.cuda.empty_cache()
     return {"workload": cid, "frames": c["frames"], "streams": c["streams"],
-            "best_verify_size": cal["measured_best"],
+            "fused_draft": c["fused_draft"], "best_verify_size": cal["measured_best"],
             "calibrated_verify_size": cal["verify_size"],
             "accepted_share_by_offset": cal["accepted_share_by_offset"],
             "by_verify_size": {str(n): {k: round(v, 4) for k, v in r.items()}
@@ -335,7 +347,8 @@ def _leg(r, c, steps, warmup):
             "realtime_factor_vs_12.5fps": r["frames_per_s_per_stream"] / REALTIME_FPS,
             "codes_per_verify_pass": r["codes_per_verify_pass"],
             "codes_per_decoder_pass": r["codes_per_decoder_pass"],
-            "acceptance_by_offset": r["acceptance_by_offset"]}
+            "acceptance_by_offset": r["acceptance_by_offset"],
+            "fused_draft": c.get("fused_draft", 0)}
 
 
 def baseline_configs(main_line, s64, c64):
@@ -346,13 +359,13 @@ def baseline_configs(main_line, s64, c64):
     roofline (its 1.0 GB of decoder and head weights exceed the 256 MB
     Infinity Cache, so its weight traffic comes from HBM)."""
     out = {}
-    r1, c1 = run_workload("tiny", 5, 2)
+    r1, c1 = run_workload("tiny", 5, 2, fused_draft=fused_for("tiny"))
     out["1"] = _leg(r1, c1, 5, 2)
     out["1"]["cpu_oracle_codes_per_s"] = oracle_rate("tiny", 30)
     out["2"] = {"workload": main_line["config"]["workload"], "see": "value / roofline"}
     sweep = {}
     for N in range(2, 9):
-        r3, c3 = run_workload("tiny-greedy", 3, 1, verify_size=N)
+        r3, c3 = run_workload("tiny-greedy", 3, 1, verify_size=N, fused_draft=fused_for("tiny-greedy"))
         leg = _leg(r3, c3, 3, 1)
         sweep[str(N)] = {k: leg[k] for k in ("codes_per_s", "ms_per_step", "codes_per_verify_pass",
                                                "codes_per_decoder_pass", "acceptance_by_offset")}
@@ -361,7 +374,7 @@ def baseline_configs(main_line, s64, c64):
                             "to G - 2 - s drafts)",
                 "by_verify_size": sweep}
     out["4"] = _leg(s64, c64, 1, 1)
-    r5, c5 = run_workload("wide-256", 1, 1, kernels=True)
+    r5, c5 = run_workload("wide-256", 1, 1, kernels=True, fused_draft=fused_for("wide-256"))
     out["5"] = _leg(r5, c5, 1, 1)
     k5 = r5["kernels"]
     out["5"]["roofline"] = roofline(k5, c5["dtype"], "wide-256")
@@ -408,11 +421,7 @@ def main():
         print(json.dumps({"copy_mib": args.copy_mb, "launches": 8}), flush=True)
         return
 
-    # one stream: the next round's drafts formed in this round's verify tail
-    # (RVQ section 2.2, Figure 3; 2-3 % faster there), separate draft
-    # launches for batched streams (faster there)
-    import synth
-    fd = 1 if synth.config(args.workload)["streams"] == 1 else 0
+    fd = fused_for(args.workload)
     main_res, c = run_workload(args.workload, args.steps, args.warmup,
                                frames=args.frames, kernels=True, fused_draft=fd)
     line = {
@@ -454,7 +463,7 @@ def main():
         line["ar_baseline"] = {"codes_per_s": ar["codes_per_s"],
                                "ms_per_step": ar["ms_per_step"],
                                "speedup": main_res["codes_per_s"] / ar["codes_per_s"]}
-        s64, c64 = run_workload("tiny-64", 1, 1, kernels=True)
+        s64, c64 = run_workload("tiny-64", 1, 1, kernels=True, fused_draft=fused_for("tiny-64"))
         line["streams64"] = {k: s64[k] for k in (
             "codes_per_s", "frames_per_s", "ms_per_step",
             "codes_per_verify_pass", "codes_per_decoder_pass",
@@ -462,7 +471,8 @@ def main():
         line["streams64"]["roofline"] = roofline(s64["kernels"], c64["dtype"], "tiny-64")
         # the qwen3tts shape at 64 streams: weights large enough for the
         # batched projections' roofline to mean something
-        q64, cq64 = run_workload("qwen3tts-64", 1, 1, kernels=True)
+        q64, cq64 = run_workload("qwen3tts-64", 1, 1, kernels=True,
+                                 fused_draft=fused_for("qwen3tts-64"))
         line["streams64_qwen3tts"] = {k: q64[k] for k in (
             "codes_per_s", "frames_per_s", "ms_per_step",
             "codes_per_verify_pass", "codes_per_decoder_pass")}
@@ -475,10 +485,12 @@ def main():
         # draft heads reading h_s + b_t; untrained offsets, so only the cost
         # and the changed acceptance are meaningful
         line["draft_offsets"] = {}
+        offs = {}
         for wl, steps in ((args.workload, args.steps), ("qwen3tts-64", 1)):
             ref = main_res if wl == args.workload else q64
             o, co = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
-                                 offsets=(3, 0.1), fused_draft=fd if wl == args.workload else 0)
+                                 offsets=(3, 0.1), fused_draft=fused_for(wl))
+            offs[wl] = o
             line["draft_offsets"][wl] = {
                 "K": co["draft_offsets"], "scale": co["offset_scale"],
                 "codes_per_s": o["codes_per_s"], "ms_per_step": o["ms_per_step"],
@@ -489,26 +501,30 @@ def main():
                                                     (ref["ms_per_step"] / ref["stats"]["rounds"]),
             }
         # the next round's drafts formed in this round's verify tail (one
-        # heads launch and one softmax launch per round instead of two each)
+        # heads launch and one softmax launch per round instead of two each),
+        # against separate draft launches: each workload's leg above ran in
+        # its chosen mode, the other mode runs here
         line["fused_draft"] = {}
-        for wl, steps, fused, ref, off in ((args.workload, args.steps, main_res if fd else None,
-                                            None if fd else main_res, None),
-                                           ("qwen3tts-64", 1, None, q64, None),
-                                           (args.workload, args.steps, None, None, (3, 0.1))):
-            fr = fused or run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
-                                       offsets=off, fused_draft=1)[0]
-            if ref is None:
-                ref = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
-                                   offsets=off)[0]
-            key = wl + (f" K={off[0]}" if off else "")
+
+        def per_pass_us(r):  # one stream's verify or prefill pass
+            return 1e3 * r["ms_per_step"] / ((r["stats"]["rounds"] + r["stats"]["prefill_passes"]) / r["streams"])
+
+        for key, wl, steps, off, have in ((args.workload, args.workload, args.steps, None, main_res),
+                                          ("tiny-64", "tiny-64", 1, None, s64),
+                                          ("qwen3tts-64", "qwen3tts-64", 1, None, q64),
+                                          (args.workload + " K=3", args.workload, args.steps, (3, 0.1),
+                                           offs[args.workload])):
+            other = run_workload(wl, steps, 1, frames=args.frames if wl == args.workload else None,
+                                 offsets=off, fused_draft=1 - fused_for(wl))[0]
+            fr, ref = (have, other) if fused_for(wl) else (other, have)
             line["fused_draft"][key] = {
                 "codes_per_s": fr["codes_per_s"], "ms_per_step": fr["ms_per_step"],
                 "codes_per_verify_pass": fr["codes_per_verify_pass"],
                 "unfused_codes_per_s": ref["codes_per_s"],
                 "throughput_vs_unfused": fr["codes_per_s"] / ref["codes_per_s"],
-                "us_per_pass": 1e3 * fr["ms_per_step"] / (fr["stats"]["rounds"] + fr["stats"]["prefill_passes"]),
-                "unfused_us_per_pass": 1e3 * ref["ms_per_step"] /
-                                       (ref["stats"]["rounds"] + ref["stats"]["prefill_passes"]),
+                "us_per_pass": per_pass_us(fr),
+                "unfused_us_per_pass": per_pass_us(ref),
+                "used_by_the_legs_above": bool(fused_for(wl)),
             }
         # the verify window chosen on this device (acceptance saturates while
         # a wider window costs more rows per pass)

@@ -122,12 +122,14 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 2: scores and softmax.  A 16-lane row per pair (pairs in
-  // groups of 16 per block); lane l scores positions l and l + 16, the
-  // row's max and sum fold by DPP rotations (no LDS permutes) ----
+  // ---- phase 2: scores and softmax.  32 lanes per pair (eight pairs per
+  // block pass): lane l scores positions l % 16 and l % 16 + 16 over one
+  // half of the head dimensions, the two halves meet by a lane exchange;
+  // the row's max and sum fold by DPP rotations within each 16-lane row ----
   {
-    const int l16 = threadIdx.x & 15, prow = threadIdx.x >> 4;
-    for (int pr0 = 0; pr0 < npair; pr0 += kBlock / 16) {
+    const int l32 = threadIdx.x & 31, prow = threadIdx.x >> 5;
+    const int l16 = l32 & 15, hd = l32 >> 4;
+    for (int pr0 = 0; pr0 < npair; pr0 += kBlock / 32) {
       const int pr = pr0 + prow;
       const bool live_pair = pr < npair;
       const int pp = live_pair ? pos_s[pr / group] : -1;
@@ -135,21 +137,24 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int p = l16 + 16 * h;
-        sc[h] = -INFINITY;
+        float part = 0.0f;
         if (p <= pp) {
-          const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D);
-          const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS);
+          const float4* q4 = reinterpret_cast<const float4*>(Qs + pr * D + hd * half);
+          const float4* k4 = reinterpret_cast<const float4*>(Ks + p * KS + hd * half);
           float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int i = 0; i < D / 4; ++i) {
+          for (int i = 0; i < H4; ++i) {
             const float4 x = q4[i], y = k4[i];
             acc[0] = fmaf(x.x, y.x, acc[0]);
             acc[1] = fmaf(x.y, y.y, acc[1]);
             acc[2] = fmaf(x.z, y.z, acc[2]);
             acc[3] = fmaf(x.w, y.w, acc[3]);
           }
-          sc[h] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale;
+          part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         }
+        // lanes l and l ^ 16 hold the two halves of one score (same p, pp)
+        const float other = __shfl_xor(part, 16);
+        sc[h] = p <= pp ? (hd == 0 ? part + other : other + part) * a.scale : -INFINITY;
       }
       float mx = fmaxf(sc[0], sc[1]);
       mx = fmaxf(mx, dpp_f<kRor8>(mx));
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void attention_kernel(const AttnArgs a) {
       sum += dpp_f<kRor4>(sum);
       sum += dpp_f<kRor2>(sum);
       sum += dpp_f<kRor1>(sum);
-      if (live_pair && pp >= 0) {
+      if (live_pair && pp >= 0 && hd == 0) {
         S[pr * 32 + l16] = e0 / sum;  // zero past the row's own position
         S[pr * 32 + l16 + 16] = e1 / sum;
       }

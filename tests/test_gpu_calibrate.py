@@ -14,8 +14,8 @@ torch = pytest.importorskip("torch")
 
 
 def test_calibrate_window_tiny():
-    from speculative_decoding_rvq_amd.calibrate import choose_window, expected_codes_per_round
-    from speculative_decoding_rvq_amd.calibrate import calibrate_window
+    from speculative_decoding_rvq_amd.calibrate import (calibrate_window, choose_window, expected_codes_per_round,
+                                                         expected_passes_per_frame)
     c = synth.config("tiny", frames=40)
     hf, c0, seeds = synth.make_inputs(c)
     dh = torch.from_numpy(np.ascontiguousarray(hf)).cuda()
@@ -34,7 +34,11 @@ def test_calibrate_window_tiny():
         assert r["us_per_pass"] > 0.0 and r["codes_per_s"] > 0.0
         assert 1.0 <= r["codes_per_verify_pass"] <= n
         assert r["expected_codes_per_round"] == pytest.approx(expected_codes_per_round(share, n))
-    assert cal["verify_size"] == choose_window(share, {n: r["us_per_pass"] for n, r in rows.items()})
+    for n, r in rows.items():
+        assert r["expected_passes_per_frame"] == pytest.approx(expected_passes_per_frame(share, n, c["groups"]))
+        log(f"N={n}: passes per frame {r['passes_per_frame']:.3f} measured, "
+            f"{r['expected_passes_per_frame']:.3f} expected")
+    assert cal["verify_size"] == choose_window(share, {n: r["us_per_pass"] for n, r in rows.items()}, c["groups"])
     assert cal["measured_best"] in sizes
 
 

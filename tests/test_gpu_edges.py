@@ -1,8 +1,9 @@
 """GPU parity at the edges of the method: the fewest code groups (G = 3: every
 round is a single target draw; G = 2: the autoregressive fallback), the full
 vocabulary as top-k set, top-k 1 (the deterministic chain), very low and very
-high temperature, and one handle decoding different stream counts in turn
-(GEMV and matrix-core paths, a new graph per count).  Same frame rule as the
+high temperature, the most code groups (G = 32: attention over positions
+16..31, heads up to 31), and one handle decoding different stream counts in
+turn (GEMV and matrix-core paths, a new graph per count).  Same frame rule as the
 other decode tests: equal codes, or the oracle re-run with one near-tie
 decision taken the other way reproduces the GPU's codes.
 """
@@ -89,6 +90,25 @@ def test_temperature_extremes(T):
     log(f"decode T={T} F=30")
     got = decode_gpu(h, hf, c0, seeds)
     _check(f"T={T}", c, m, got, hf, c0, seeds, [(f, 0) for f in range(30)])
+
+
+@pytest.mark.parametrize("B,fused,dtype", [(1, 0, synth.F32), (1, 1, synth.F32), (12, 1, synth.F32),
+                                           (1, 1, synth.BF16), (12, 0, synth.BF16)])
+def test_thirty_two_groups(B, fused, dtype):
+    """G = 32, the most the library takes: a frame's positions reach 31, so
+    the attention's scores take their second 16-position half, and the heads
+    run up to 31; one stream (GEMV path, the folded accept step with fused
+    drafts) and 12 streams (48 rows: matrix-core path), fp32 and bf16
+    weights."""
+    kw = dict(hidden=512, q_heads=8, ffn=1024) if dtype == synth.BF16 else {}
+    c, h, m = _setup(max_streams=B, groups=32, verify_size=4, top_k=50, frames=6 if B == 1 else 2,
+                     streams=B, fused_draft=fused, dtype=dtype, **kw)
+    hf, c0, seeds = synth.make_inputs(c)
+    F = c["frames"]
+    log(f"decode G=32 B={B} fused={fused} {'bf16' if dtype == synth.BF16 else 'fp32'} F={F}")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == F * B and got[2]["codes"] == F * B * 31
+    _check(f"G32 B={B} fused={fused}", c, m, got, hf, c0, seeds, [(f, b) for f in range(F) for b in range(B)])
 
 
 def test_one_handle_different_stream_counts():

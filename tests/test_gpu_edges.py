@@ -2,7 +2,7 @@
 round is a single target draw; G = 2: the autoregressive fallback), the full
 vocabulary as top-k set, top-k 1 (the deterministic chain), very low and very
 high temperature, the most code groups (G = 32: attention over positions
-16..31, heads up to 31), and one handle decoding different stream counts in
+16..31, heads up to 31), head dims 16 and 32, and one handle decoding different stream counts in
 turn (GEMV and matrix-core paths, a new graph per count).  Same frame rule as the
 other decode tests: equal codes, or the oracle re-run with one near-tie
 decision taken the other way reproduces the GPU's codes.
@@ -109,6 +109,20 @@ def test_thirty_two_groups(B, fused, dtype):
     got = decode_gpu(h, hf, c0, seeds)
     assert got[2]["frames"] == F * B and got[2]["codes"] == F * B * 31
     _check(f"G32 B={B} fused={fused}", c, m, got, hf, c0, seeds, [(f, b) for f in range(F) for b in range(B)])
+
+
+@pytest.mark.parametrize("d,B", [(16, 1), (32, 1), (16, 12), (32, 12)])
+def test_small_head_dims(d, B):
+    """Head dims 16 and 32 (16 and 8 query heads over a 256-wide model, two
+    per KV head): the attention kernel's other instantiations, one stream
+    and 12 streams."""
+    c, h, m = _setup(max_streams=B, groups=8, verify_size=4, top_k=50, frames=8 if B == 1 else 2, streams=B,
+                     head_dim=d, q_heads=256 // d, kv_heads=128 // d)
+    hf, c0, seeds = synth.make_inputs(c)
+    F = c["frames"]
+    log(f"decode d={d} B={B} F={F}")
+    got = decode_gpu(h, hf, c0, seeds)
+    _check(f"d={d} B={B}", c, m, got, hf, c0, seeds, [(f, b) for f in range(F) for b in range(B)])
 
 
 def test_one_handle_different_stream_counts():

@@ -76,6 +76,23 @@ def test_tree_tiny_all_frames(parents):
     _check("tiny", c, oracle_model("tiny"), parents, got, hf, c0, seeds, [(f, 0) for f in range(60)])
 
 
+@pytest.mark.parametrize("parents", [T15, T63], ids=["15", "63"])
+def test_tree_thirty_two_groups(parents):
+    """G = 32 (the most the library takes): the committed prefix reaches
+    position 31, so the tree attention keys on up to 32 + 63 positions and
+    nodes; the tiny decoder's shape with its own 32-group weights."""
+    from oracle import decoder
+    from speculative_decoding_rvq_amd import binding
+    c = synth.config("tiny", groups=32, tree=list(parents), frames=8)
+    w = synth.make_weights(c)
+    h = binding.Handle(c, binding.weights_to_device(w))
+    hf, c0, seeds = synth.make_inputs(c)
+    log(f"decode tiny G=32 tree of {len(parents)} nodes F=8")
+    got = decode_gpu(h, hf, c0, seeds)
+    assert got[2]["frames"] == 8 and got[2]["codes"] == 8 * 31
+    _check("tiny G=32", c, decoder.Model(c, w), parents, got, hf, c0, seeds, [(f, 0) for f in range(8)])
+
+
 def test_one_child_tree_equals_gpu_chain():
     c, h = _tree_handle("tiny", [0, 1, 2], frames=60)
     hf, c0, seeds = synth.make_inputs(c)

@@ -148,6 +148,20 @@ def test_wide_256_streams_sampled():
     _check("wide-256", c, hf, c0, seeds, pairs, gc, gf, gst, dparams(c), False)
 
 
+@pytest.mark.parametrize("fused", [0, 1])
+def test_wide_one_stream(fused):
+    """The wide decoder (H 2048, V 4096, K 6144 for the down projection) at
+    one stream: the GEMV path with 256 threads per weight row, 16 codes per
+    thread in the top-k and sampling kernels, separate or fused drafts."""
+    c = synth.config("wide-256", frames=4, streams=1, fused_draft=fused)
+    hf, c0, seeds = synth.make_inputs(c)
+    h = handle("wide-256", max_streams=1, fused_draft=fused)
+    log(f"decode wide B=1 F=4 fused={fused}")
+    gc, gf, gst = decode_gpu(h, hf, c0, seeds)
+    assert gst["frames"] == 4
+    _check("wide-256", c, hf, c0, seeds, [(f, 0) for f in range(4)], gc, gf, gst, dparams(c), True)
+
+
 def test_wide_256_streams_full_sampled():
     """The wide workload at full size: 256 streams x 200 frames (8 layers,
     H 2048, V 4096, correlated heads, top-k 100), sampled frames."""

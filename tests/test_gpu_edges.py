@@ -2,7 +2,7 @@
 round is a single target draw; G = 2: the autoregressive fallback), the full
 vocabulary as top-k set, top-k 1 (the deterministic chain), very low and very
 high temperature, the most code groups (G = 32: attention over positions
-16..31, heads up to 31), head dims 16 and 32, vocabularies of 512 and 1024 codes, and one handle decoding different stream counts in
+16..31, heads up to 31), head dims 16 and 32, vocabularies of 512, 1024 and 4096 codes, and one handle decoding different stream counts in
 turn (GEMV and matrix-core paths, a new graph per count).  Same frame rule as the
 other decode tests: equal codes, or the oracle re-run with one near-tie
 decision taken the other way reproduces the GPU's codes.
@@ -125,10 +125,11 @@ def test_small_head_dims(d, B):
     _check(f"d={d} B={B}", c, m, got, hf, c0, seeds, [(f, b) for f in range(F) for b in range(B)])
 
 
-@pytest.mark.parametrize("V,B,greedy", [(512, 1, False), (1024, 1, False), (1024, 12, False), (512, 1, True)])
+@pytest.mark.parametrize("V,B,greedy", [(512, 1, False), (1024, 1, False), (1024, 12, False), (512, 1, True),
+                                        (4096, 1, False), (4096, 1, True)])
 def test_vocabulary_sizes(V, B, greedy):
-    """Vocabularies of 512 and 1024 codes (two and four codes per thread in
-    the top-k and sampling kernels), sampled and greedy."""
+    """Vocabularies of 512, 1024 and 4096 codes (two, four and sixteen codes
+    per thread in the top-k and sampling kernels), sampled and greedy."""
     c, h, m = _setup(max_streams=B, groups=8, verify_size=4, top_k=1 if greedy else 50, greedy=greedy,
                      vocab=V, frames=8 if B == 1 else 2, streams=B)
     hf, c0, seeds = synth.make_inputs(c)

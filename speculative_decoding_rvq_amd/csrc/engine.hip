@@ -445,26 +445,29 @@ int gemv(const cp_spec* h, hipStream_t s, int mode, GemvArgs a, const uint16_t* 
     mt = 1;
     gy = a.M;
   } else if (mode == kHeadG) {
-    // a head's rows share its weights in one block (up to 8, within the
-    // activation registers); a.hslices comes in as the most rows one head
-    // can have and leaves as the slices per head
+    // a head's rows in slices of two per block: the slices of one weight
+    // slice run on one XCD (block columns keep their XCD across the grid's
+    // rows), so all but the first read it from that XCD's L2.  Measured at
+    // one stream with fused drafts against up to 8 rows per block: 0.6 us
+    // per pass faster at N = 4, 4 us at N = 8.  a.hslices comes in as the
+    // most rows one head can have and leaves as the slices per head
     const int rph = std::max(a.hslices, 1);
-    mt = rph <= 2 ? 2 : (rph <= 4 ? 4 : 8);
-    while (mt > 2 && mt * spt * vec > 96) mt >>= 1;
+    mt = 2;
     a.hslices = (rph + mt - 1) / mt;
     gy = a.n_heads * a.hslices;
   } else {
     mt = mt_for(a.M, spt, vec);
-    // residual adds and the Q/K/V launch that runs the accept step: two rows
-    // per block at most.  A thread loads two fp32 activation vectors per
-    // 16-byte weight chunk and row, so four rows make the activation loads
-    // twice the weight loads; with two rows per block the second row tile
-    // reads the same weight slice from its XCD's L2 (gemv_kernel's block
-    // order).  Measured at one stream: down 4.54 -> 4.03 us, O 3.41 -> 3.35,
-    // 2.5-4.5 % more codes/s on every one-stream workload; the SwiGLU
-    // projection (5.4 -> 5.7 us) and the plain Q/K/V at eight rows (6.1 ->
-    // 7.0) keep their wider tiles.
-    if (mode == kAdd || fold != nullptr) mt = std::min(mt, 2);
+    // residual adds, the Q/K/V launch that runs the accept step, and Q/K/V
+    // over at most four rows: two rows per block at most.  A thread loads two
+    // fp32 activation vectors per 16-byte weight chunk and row, so four rows
+    // make the activation loads twice the weight loads; with two rows per
+    // block the second row tile reads the same weight slice from its XCD's
+    // L2 (gemv_kernel's block order).  Measured at one stream: down 4.54 ->
+    // 4.03 us, O 3.41 -> 3.35, 2.5-4.5 % more codes/s on every one-stream
+    // workload; the SwiGLU projection (5.4 -> 5.7 us) keeps its wider tiles,
+    // and so does the plain Q/K/V at eight rows (6.1 -> 7.0 us; 2 us per
+    // pass slower at N = 8).
+    if (mode == kAdd || fold != nullptr || (mode == kQKV && a.M <= 4)) mt = std::min(mt, 2);
     gy = (a.M + mt - 1) / mt;
   }
   if (fold != nullptr) {
